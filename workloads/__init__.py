@@ -1,0 +1,181 @@
+"""Seeded synthetic workloads shared by the oracle checks, the GPU tests and the benchmark.
+
+This module only draws random inputs; it computes nothing the method computes
+(no softmax, no acceptance test, no scheduling, no Markov scores). Every array is
+produced by numpy's PCG64 from a fixed seed, so both sides of a parity check see
+identical bytes.
+
+Shapes follow the workloads the source pages describe: block 7 offline and
+block 16 (DSpark study notes, sections 7-8; PCTree article), Qwen3's 151,936
+vocabulary and DeepSeek-V4's 129,280, concurrency up to 256 with mixed easy and
+hard streams (SGLang article). The public benchmarks those pages evaluate on are
+not used; these synthetic logits stand in for them.
+
+Recipes (N(m, s) = normal with mean m and standard deviation s):
+
+* tiny verify (C1): R=4, K=7, V=1024, fp32 target t ~ N(0, 2) of shape [R, K+1, V];
+  draft d_{i,k} = t_{i,k-1} + N(0, 0.5); confidence sigmoid(N(1, 1)).
+* dense-vocab verify (C2): R=64, K=7, V=151,936, bf16; t ~ N(0, 3) plus 8 on an
+  i.i.d. 1% of entries; d_{i,k} = t_{i,k-1} + sigma * eps with eps ~ N(0, 1) and
+  sigma from ``calibration.json`` (chosen by a committed oracle script so the
+  mean one-token acceptance is about 0.8).
+* scheduled ragged verify (C3): R=256, K=16, V=151,936, bf16; t as C2; a noise
+  scale sigma_i ~ U(0.2, 2.0) per request (easy and hard streams);
+  d = t + sigma_i * eps; confidence c_{i,k} = sigmoid(4 - 2.5 sigma_i + 0.25 eta),
+  eta ~ N(0, 1) (a logistic model of the draft-target gap); additive cost table
+  c(n) = 1.0 + 0.05 n.
+* Markov chain (C4): R=256, B=16, V=151,936, rank 256; L ~ N(0, 3) bf16;
+  U [V, r], W [r, V] ~ N(0, 0.02) bf16; anchors uniform over the vocabulary.
+* PCTree + tree verify (C5): R=128, D=16, V=129,280, rank 256, k=4, F=16, N=64;
+  L, U, W as C4; target logits for the root and each tree node ~ N(0, 3) bf16.
+
+Draft tokens x_{i,k} are the synthetic draft model's samples from softmax(d/T)
+(Gumbel-max with this module's own noise), or argmax d when T = 0.
+"""
+import json
+import os
+
+import numpy as np
+
+V_QWEN3 = 151936
+V_DSV4 = 129280
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 to bfloat16 (round to nearest even); returns the uint16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((b + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """Exact float32 values of bfloat16 bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def calibration():
+    with open(os.path.join(_HERE, "calibration.json")) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _store(x32, dtype):
+    return f32_to_bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, np.float32)
+
+
+def values(arr, dtype):
+    """Float32 view of stored logits (bf16 bits are widened exactly)."""
+    return bf16_bits_to_f32(arr) if dtype == "bf16" else np.asarray(arr, np.float32)
+
+
+def _draw_tokens(rng, d32, temperature):
+    if temperature == 0.0:
+        return np.argmax(d32, axis=-1).astype(np.int32)
+    g = -np.log(-np.log(rng.random(d32.shape, dtype=np.float64).clip(1e-300, None)))
+    return np.argmax(d32.astype(np.float64) / temperature + g, axis=-1).astype(np.int32)
+
+
+def verify_case(R, K, V, dtype="bf16", seed=0, t_sigma=3.0, boost_p=0.0, boost=8.0,
+                d_sigma=0.5, temperature=1.0):
+    """Dense target [R, K+1, V] and draft [R, K, V] logits plus draft tokens [R, K].
+
+    d_sigma: scalar or per-request array of draft noise scales.
+    """
+    rng = _rng(seed)
+    d_sig = np.broadcast_to(np.asarray(d_sigma, dtype=np.float32), (R,))
+    t_store = np.empty((R, K + 1, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    d_store = np.empty((R, K, V), dtype=t_store.dtype)
+    x = np.empty((R, K), dtype=np.int32)
+    for i in range(R):
+        t = rng.standard_normal((K + 1, V), dtype=np.float32) * np.float32(t_sigma)
+        if boost_p > 0:
+            t += np.float32(boost) * (rng.random((K + 1, V), dtype=np.float32) < boost_p)
+        t_store[i] = _store(t, dtype)
+        tv = values(t_store[i], dtype)
+        eps = rng.standard_normal((K, V), dtype=np.float32)
+        d_store[i] = _store(tv[:K] + d_sig[i] * eps, dtype)
+        x[i] = _draw_tokens(rng, values(d_store[i], dtype), temperature)
+    return dict(t=t_store, d=d_store, x=x, dtype=dtype, R=R, K=K, V=V, temperature=temperature)
+
+
+def confidences(rng, R, K, mean=1.0, std=1.0):
+    return (1.0 / (1.0 + np.exp(-(mean + std * rng.standard_normal((R, K)))))).astype(np.float32)
+
+
+def c1():
+    """Tiny verify: 4 requests, K=7, V=1024, fp32, Philox seed 0."""
+    c = verify_case(4, 7, 1024, dtype="f32", seed=1001, t_sigma=2.0, d_sigma=0.5)
+    c["conf"] = confidences(_rng(2001), 4, 7)
+    c["anchors"] = _rng(3001).integers(0, 1024, size=4).astype(np.int32)
+    c["cost"] = 1.0 + 0.05 * np.arange(4 * 7 + 1, dtype=np.float64)
+    return c
+
+
+def c2(sigma=None):
+    """Dense-vocab verify: 64 requests, K=7, V=151,936, bf16, full-block windows."""
+    if sigma is None:
+        sigma = calibration()["c2_sigma"]
+    c = verify_case(64, 7, V_QWEN3, dtype="bf16", seed=1002, t_sigma=3.0, boost_p=0.01,
+                    boost=8.0, d_sigma=sigma)
+    c["conf"] = confidences(_rng(2002), 64, 7)
+    c["anchors"] = _rng(3002).integers(0, V_QWEN3, size=64).astype(np.int32)
+    # flat step-time table: every candidate with nonzero survival raises throughput,
+    # so the scheduler returns full-block windows
+    c["cost"] = np.ones(64 * 7 + 1, dtype=np.float64)
+    c["sigma"] = sigma
+    return c
+
+
+def c3(R=256, K=16, V=V_QWEN3):
+    """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table."""
+    rng = _rng(2003)
+    sig = rng.uniform(0.2, 2.0, size=R).astype(np.float32)
+    c = verify_case(R, K, V, dtype="bf16", seed=1003, t_sigma=3.0, boost_p=0.01, boost=8.0,
+                    d_sigma=sig)
+    eta = rng.standard_normal((R, K))
+    z = 4.0 - 2.5 * sig[:, None].astype(np.float64) + 0.25 * eta
+    c["conf"] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    c["anchors"] = _rng(3003).integers(0, V, size=R).astype(np.int32)
+    c["cost"] = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
+    c["sigma_i"] = sig
+    return c
+
+
+def markov_case(R, B, V, rank=256, seed=1004, l_sigma=3.0, w_sigma=0.02):
+    """Base logits L [R, B, V], factors U [V, r], W [r, V] (bf16 bits) and anchors [R]."""
+    rng = _rng(seed)
+    L = np.empty((R, B, V), dtype=np.uint16)
+    for i in range(R):
+        L[i] = f32_to_bf16_bits(rng.standard_normal((B, V), dtype=np.float32) * np.float32(l_sigma))
+    U = f32_to_bf16_bits(rng.standard_normal((V, rank), dtype=np.float32) * np.float32(w_sigma))
+    W = f32_to_bf16_bits(rng.standard_normal((rank, V), dtype=np.float32) * np.float32(w_sigma))
+    anchors = rng.integers(0, V, size=R).astype(np.int32)
+    return dict(L=L, U=U, W=W, anchors=anchors, R=R, B=B, V=V, rank=rank)
+
+
+def c4():
+    """Markov chain: 256 requests, 16 steps, V=151,936, rank 256."""
+    return markov_case(256, 16, V_QWEN3, 256, seed=1004)
+
+
+def tree_target(R, n_rows, V, seed, sigma=3.0):
+    """Target logits [R, n_rows, V] bf16 for the root and each tree node."""
+    rng = _rng(seed)
+    out = np.empty((R, n_rows, V), dtype=np.uint16)
+    for i in range(R):
+        out[i] = f32_to_bf16_bits(rng.standard_normal((n_rows, V), dtype=np.float32) * np.float32(sigma))
+    return out
+
+
+def c5():
+    """PCTree + tree verify: 128 requests, depth 16, V=129,280, k=4, F=16, N=64."""
+    c = markov_case(128, 16, V_DSV4, 256, seed=1005)
+    c.update(topk=4, frontier=16, topN=64)
+    c["target"] = tree_target(128, 65, V_DSV4, seed=2005)
+    return c
