@@ -1,0 +1,313 @@
+"""MI355X (gfx950) hot path of confidence-scheduled speculative decoding.
+
+Thin torch-tensor binding of libdsp's C ABI (include/dsp.h). Every function
+here only checks and marshals arguments (device pointers, strides, the current
+HIP stream, a workspace from torch's allocator); all arithmetic runs in the HIP
+kernels of libdsp.so. The library must be built first
+(``python -m block_drafting_verification_amd.build``); nothing here falls back
+to another implementation.
+
+Calls (same names as the C entry points without the ``dsp_`` prefix):
+  schedule_windows   -- survival products + hardware-aware prefix scheduler
+  pack_ragged        -- front-packed cu_seqlens verify buffer
+  verify_rejection   -- batched ragged rejection / greedy / tree verify
+  draft_markov_step  -- Markov-head greedy chain
+  tree_expand        -- PCTree expansion
+  philox_uniforms    -- the counter-based uniforms the verify step draws
+"""
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DSP_STATUS_NONFINITE,
+                   DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE, DspError, KERNELS)
+
+__all__ = ["PreparedCall", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step", "tree_expand",
+           "philox_uniforms", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
+           "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_STATUS_TOKEN_RANGE",
+           "DSP_STATUS_WINDOW_RANGE", "DSP_STATUS_NONFINITE"]
+
+
+def lib():
+    return _abi.load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return DSP_BF16
+    if t.dtype == torch.float32:
+        return DSP_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None:
+            _need(t.is_cuda, "tensors must live on the GPU")
+
+
+def _take(o, key, make):
+    t = o.get(key)
+    return make() if t is None else t
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes, device, private=False):
+    """A device byte buffer of at least nbytes.
+
+    Shared per device for one-shot calls (calls on one stream run in order);
+    private for prepared calls, which keep their buffer for their lifetime.
+    """
+    if private:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < max(nbytes, 1):
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+class PreparedCall:
+    """A libdsp call whose arguments were checked and marshalled once.
+
+    Calling it issues exactly one C ABI call on the stream captured at
+    preparation time, with the same device buffers (results land in
+    ``outputs``). Suitable for tight loops and HIP graph capture.
+    """
+
+    def __init__(self, fn, args, keep, outputs):
+        self._fn = fn
+        self._args = tuple(args)
+        self._keep = keep
+        self.outputs = outputs
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _abi.check(rc)
+        return self.outputs
+
+
+def _finish(fn, args, outputs, prepare, keep):
+    if prepare:
+        return PreparedCall(fn, args, keep, outputs)
+    _abi.check(fn(*args))
+    return outputs
+
+
+def philox_uniforms(ctr, seed, stream=None):
+    """ctr: uint64-valued int64 tensor [n, 4] on the GPU -> float64 [n, 4] uniforms."""
+    _on_gpu(ctr)
+    _need(ctr.dim() == 2 and ctr.shape[1] == 4 and ctr.is_contiguous(), "ctr must be contiguous [n, 4]")
+    out = torch.empty(ctr.shape, dtype=torch.float64, device=ctr.device)
+    _abi.check(lib().dsp_philox_uniforms(_ptr(ctr), ctr.shape[0], seed, _ptr(out), _stream(stream)))
+    return out
+
+
+def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, want_survival=True,
+                     out=None, stream=None, prepare=False):
+    """conf: float32 [R, K]; cost: float64 [>= R*K+1] (both on the GPU).
+
+    Returns dict(windows int32 [R], survival float64 [R, K] or None, stats float64 [4]).
+    """
+    _on_gpu(conf, cost)
+    _need(conf.dtype == torch.float32 and conf.dim() == 2 and conf.is_contiguous(), "conf: contiguous float32 [R, K]")
+    _need(cost.dtype == torch.float64 and cost.is_contiguous(), "cost: contiguous float64")
+    R, K = conf.shape
+    dev = conf.device
+    o = out or {}
+    windows = _take(o, "windows", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    survival = _take(o, "survival", lambda: torch.empty(R, K, dtype=torch.float64, device=dev)) if want_survival else None
+    stats = _take(o, "stats", lambda: torch.empty(4, dtype=torch.float64, device=dev))
+    ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare)
+    args = (_ptr(conf), R, K, _ptr(cost), cost.numel(), mode, max_tokens, _ptr(windows), _ptr(survival),
+            _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
+    res = dict(windows=windows, survival=survival, stats=stats)
+    return _finish(lib().dsp_schedule_windows, args, res, prepare, (conf, cost, ws))
+
+
+def pack_ragged(windows, anchors, drafts, tiers=None, out=None, status=None, stream=None, prepare=False):
+    """windows int32 [R], anchors int32 [R], drafts int32 [R, K] (GPU); tiers: host list.
+
+    Returns dict(cu_seqlens [R+1], tokens/row_req/row_pos [R*(K+1)], total_and_tier [2], status [1]).
+    """
+    _on_gpu(windows, anchors, drafts)
+    for t in (windows, anchors, drafts):
+        _need(t.dtype == torch.int32, "pack_ragged takes int32 tensors")
+    _need(drafts.dim() == 2 and drafts.stride(1) == 1, "drafts: [R, K] with unit inner stride")
+    R, K = drafts.shape
+    dev = drafts.device
+    o = out or {}
+    cu = _take(o, "cu_seqlens", lambda: torch.empty(R + 1, dtype=torch.int32, device=dev))
+    tokens = _take(o, "tokens", lambda: torch.empty(R * (K + 1), dtype=torch.int32, device=dev))
+    row_req = _take(o, "row_req", lambda: torch.empty(R * (K + 1), dtype=torch.int32, device=dev))
+    row_pos = _take(o, "row_pos", lambda: torch.empty(R * (K + 1), dtype=torch.int32, device=dev))
+    tt = _take(o, "total_and_tier", lambda: torch.empty(2, dtype=torch.int32, device=dev))
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    tl = list(tiers or [])
+    arr = (ctypes.c_int32 * max(len(tl), 1))(*tl) if tl else None
+    args = (_ptr(windows), _ptr(anchors), _ptr(drafts), drafts.stride(0), R, K,
+            ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, len(tl),
+            _ptr(cu), _ptr(tokens), _ptr(row_req), _ptr(row_pos), _ptr(tt), _ptr(status), _stream(stream))
+    res = dict(cu_seqlens=cu, tokens=tokens, row_req=row_req, row_pos=row_pos, total_and_tier=tt, status=status)
+    return _finish(lib().dsp_pack_ragged, args, res, prepare, (windows, anchors, drafts, arr))
+
+
+def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,
+                     round=0, req_id=None, max_rows=0, want_probs=True, out=None, status=None,
+                     stream=None, round_dev=None, prepare=False):
+    """Batched ragged verify.
+
+    tgt: packed target logits [T_rows, V] (bf16/fp32, unit inner stride);
+    cu_seqlens: int32 [R+1]; draft_tok: int32 [R, K]; drf: draft logits [R, K, V]
+    (T > 0); parent: int32 [R, K] selects the greedy tree walk (T must be 0).
+    Returns dict(accepted_len, out_tokens [R, K+1], stop_pos, p_x, q_x, status).
+    """
+    _on_gpu(tgt, cu_seqlens, draft_tok, drf, parent, req_id, round_dev)
+    if round_dev is not None:
+        _need(round_dev.dtype == torch.int64 and round_dev.numel() == 1, "round_dev: one int64 on the GPU")
+    _need(tgt.dim() == 2 and tgt.stride(1) == 1, "tgt: [rows, V] with unit inner stride")
+    _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous(), "cu_seqlens: contiguous int32")
+    _need(draft_tok.dtype == torch.int32 and draft_tok.dim() == 2 and draft_tok.stride(1) == 1,
+          "draft_tok: int32 [R, K] with unit inner stride")
+    R, K = draft_tok.shape
+    V = tgt.shape[1]
+    _need(cu_seqlens.numel() == R + 1, "cu_seqlens must have R+1 entries")
+    t_dt = _dtype_code(tgt)
+    greedy = float(temperature) == 0.0
+    d_dt, ld_dr, ld_dk = DSP_BF16, 0, 0
+    if drf is not None:
+        _need(drf.dim() == 3 and drf.shape[0] == R and drf.shape[1] >= K and drf.shape[2] == V and drf.stride(2) == 1,
+              "drf: [R, >=K, V] with unit inner stride")
+        d_dt, ld_dr, ld_dk = _dtype_code(drf), drf.stride(0), drf.stride(1)
+    else:
+        _need(greedy, "draft logits are required when temperature > 0")
+    if parent is not None:
+        _need(parent.dtype == torch.int32 and parent.shape == draft_tok.shape and parent.stride() == draft_tok.stride(),
+              "parent: int32 with the layout of draft_tok")
+    if req_id is not None:
+        _need(req_id.dtype == torch.int64 and req_id.numel() == R and req_id.is_contiguous(), "req_id: int64 [R]")
+    dev = tgt.device
+    o = out or {}
+    acc = _take(o, "accepted_len", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    toks = _take(o, "out_tokens", lambda: torch.empty(R, K + 1, dtype=torch.int32, device=dev))
+    stop = _take(o, "stop_pos", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    p_x = _take(o, "p_x", lambda: torch.empty(R, K, dtype=torch.float32, device=dev)) if want_probs else None
+    q_x = _take(o, "q_x", lambda: torch.empty(R, K, dtype=torch.float32, device=dev)) if want_probs else None
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    # bound the rows the device may read by what the target tensor holds
+    rows_cap = min(R * (K + 1), tgt.shape[0])
+    max_rows = rows_cap if not max_rows else min(int(max_rows), rows_cap)
+    nbytes = lib().dsp_verify_rejection_workspace_size(R, K, V, max_rows, t_dt, d_dt)
+    ws = _workspace(nbytes, dev, prepare)
+    args = (_ptr(tgt), t_dt, tgt.stride(0), _ptr(cu_seqlens), _ptr(drf), d_dt, ld_dr, ld_dk,
+            _ptr(draft_tok), draft_tok.stride(0), _ptr(parent), R, K, V, max_rows, float(temperature),
+            int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x),
+            _ptr(q_x), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+    res = dict(accepted_len=acc, out_tokens=toks, stop_pos=stop, p_x=p_x, q_x=q_x, status=status)
+    return _finish(lib().dsp_verify_rejection, args, res, prepare,
+                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, ws))
+
+
+def _check_markov(L, U, Wt):
+    _on_gpu(L, U, Wt)
+    _need(L.dtype == torch.bfloat16 and L.dim() == 3 and L.stride(2) == 1, "L: bf16 [R, B, V], unit inner stride")
+    _need(U.dtype == torch.bfloat16 and U.dim() == 2 and U.is_contiguous(), "U: contiguous bf16 [V, rank]")
+    _need(Wt.dtype == torch.bfloat16 and Wt.shape == U.shape and Wt.is_contiguous(),
+          "Wt: contiguous bf16 [V, rank] (the second factor stored vocab-major)")
+
+
+def draft_markov_step(L, U, Wt, prev_tok, n_steps=None, want_logq=False, out=None, status=None, stream=None,
+                      prepare=False):
+    """Greedy Markov chain. L: bf16 [R, B, V]; U, Wt: bf16 [V, rank]; prev_tok: int32 [R].
+
+    Returns dict(y int32 [R, n], logq float32 [R, n] or None, status).
+    """
+    _check_markov(L, U, Wt)
+    R, B, V = L.shape
+    n = B if n_steps is None else int(n_steps)
+    _need(1 <= n <= B, "n_steps must be in [1, B]")
+    rank = U.shape[1]
+    _need(prev_tok.dtype == torch.int32 and prev_tok.numel() == R and prev_tok.is_contiguous(), "prev_tok: int32 [R]")
+    dev = L.device
+    o = out or {}
+    y = _take(o, "y", lambda: torch.empty(R, n, dtype=torch.int32, device=dev))
+    logq = _take(o, "logq", lambda: torch.empty(R, n, dtype=torch.float32, device=dev)) if want_logq else None
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().dsp_draft_markov_step_workspace_size(R, V, rank, n, int(want_logq)), dev, prepare)
+    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
+            _ptr(y), y.stride(0), _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+    return _finish(lib().dsp_draft_markov_step, args, dict(y=y, logq=logq, status=status), prepare,
+                   (L, U, Wt, prev_tok, ws))
+
+
+def tree_expand(L, U, Wt, anchor, topk, frontier, topN, out=None, status=None, stream=None, prepare=False):
+    """PCTree expansion. Returns dict(node_token, node_parent, node_depth [R, topN] int32,
+    node_score float64 [R, topN], n_nodes int32 [R], status)."""
+    _check_markov(L, U, Wt)
+    R, D, V = L.shape
+    rank = U.shape[1]
+    _need(anchor.dtype == torch.int32 and anchor.numel() == R and anchor.is_contiguous(), "anchor: int32 [R]")
+    dev = L.device
+    o = out or {}
+    tok = _take(o, "node_token", lambda: torch.empty(R, topN, dtype=torch.int32, device=dev))
+    par = _take(o, "node_parent", lambda: torch.empty(R, topN, dtype=torch.int32, device=dev))
+    dep = _take(o, "node_depth", lambda: torch.empty(R, topN, dtype=torch.int32, device=dev))
+    sc = _take(o, "node_score", lambda: torch.empty(R, topN, dtype=torch.float64, device=dev))
+    nn = _take(o, "n_nodes", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = lib().dsp_tree_expand_workspace_size(R, D, V, rank, topk, frontier, topN)
+    ws = _workspace(nbytes, dev, prepare)
+    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(anchor), R, D, topk,
+            frontier, topN, _ptr(tok), _ptr(par), _ptr(dep), _ptr(sc), _ptr(nn), _ptr(status), _ptr(ws),
+            ws.numel(), _stream(stream))
+    res = dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, n_nodes=nn, status=status)
+    return _finish(lib().dsp_tree_expand, args, res, prepare, (L, U, Wt, anchor, ws))
+
+
+def prof_enable(on=True, kernels=None):
+    """Time every kernel (on=True), none (False), or only the named kernels."""
+    if not on:
+        mask = 0
+    elif kernels is None:
+        mask = -1
+    else:
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNELS.index(k)
+    _abi.check(lib().dsp_prof_enable(mask))
+
+
+def prof_reset():
+    _abi.check(lib().dsp_prof_reset())
+
+
+def prof_query(kernel):
+    """(total milliseconds, launches) recorded for a kernel name from KERNELS since the last reset."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _abi.check(lib().dsp_prof_query(KERNELS.index(kernel), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,919 @@
+// Batched ragged verify for gfx950.
+//
+// Operation (DSpark study notes, section 1 and Figure 1; SGLang article,
+// "three verify modes" and "Ragged verify"; PCTree article for the greedy tree
+// walk): per request, accept draft k with probability min(1, p_k(x_k)/q_k(x_k))
+// left to right, stop at the first rejection and draw the corrected token from
+// norm(max(0, p_k - q_k)), or draw the bonus token from p_{n+1} when the whole
+// window is accepted. T = 0 is greedy matching; a parent array selects the
+// greedy walk of a draft tree.
+//
+// Sampled path (T > 0), two launches on the caller's stream:
+//   1. stats -- one streaming pass over every packed target row and every
+//      windowed draft row. A workgroup owns a (row, chunk) item: up to 2048
+//      16-byte loads in flight, the chunk maximum, then the sum of
+//      exp2(x*c - ref) with ref = max*c (c = log2(e)/T): fp32 per element, fp64
+//      across vectors. Grid-stride over items, so ragged totals known only on
+//      the device need no host synchronisation.
+//   2. decide+sample -- one workgroup per request. Its first wavefront (lane
+//      k-1 = position k) merges the chunk statistics into log-sum-exp (fp64),
+//      forms ratio = exp2(lp2 - lq2) in fp64 with the Philox uniforms, finds the
+//      first rejection by ballot and writes the accepted tokens; then the whole
+//      workgroup draws the corrected token from max(0, p - q) (or the bonus from
+//      p) by inverse CDF: per-chunk fp64 sums, then a rescan of the chunk that
+//      holds u' * total with contiguous per-thread ranges and an fp64
+//      exclusive scan.
+// No workgroup waits on another inside a kernel: on this chip the L2 is per
+// XCD, and publishing data between workgroups would need an L2 write-back per
+// hand-off, so every dependency is a kernel boundary instead.
+//
+// Greedy and tree paths: an arg-max streaming pass (lowest index on ties),
+// then one wavefront per request for matching or the tree walk.
+#include <math.h>
+
+#include "dsp_internal.h"
+
+namespace dsp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVpt = 8;                      // 16-byte vectors per thread per chunk
+constexpr int kChunkVecs = kThreads * kVpt;  // 2048 vectors = 32 KiB per chunk
+constexpr int kCuLds = 2048;                 // cu_seqlens entries staged in LDS
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct StatSlot {
+  float ref;      // chunk max times c (fp32), or -inf for an empty chunk
+  uint32_t flag;  // 1: chunk max not finite
+  double sum;     // sum over the chunk of exp2(x*c - ref)
+};
+static_assert(sizeof(StatSlot) == 16, "slot size");
+
+enum : int32_t { JOB_NONE = 0, JOB_RESID = 1, JOB_BONUS = 2 };
+
+struct Job {
+  int32_t mode;
+  int32_t kstop;     // 1-based position whose token is drawn
+  int32_t trow;      // packed target row of p
+  int32_t drow;      // k-1 of the draft row of q (residual)
+  double lse_t;      // log2-sum-exp2 of target row times c
+  double lse_d;      // same for the draft row
+  double us;         // sampling uniform u'
+  double pad;
+};
+static_assert(sizeof(Job) == 48, "job size");
+
+__host__ __device__ inline int esize_of(int dtype) { return dtype == DSP_BF16 ? 2 : 4; }
+
+// Chunks per row so that one chunk is at most kChunkVecs 16-byte vectors.
+__host__ __device__ inline int stat_chunks(int V, int esize) {
+  const long pv = 16 / esize;
+  const long nvec = (V + pv - 1) / pv;
+  const long n = (nvec + kChunkVecs - 1) / kChunkVecs;
+  return n < 1 ? 1 : (int)n;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int kPerVec = 8;
+  __device__ static float val(const uint16_t* p, long i) { return bf16_val(p[i]); }
+  __device__ static void unpack(u32x4 w, float* x) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[2 * q] = bf16_lo(w[q]);
+      x[2 * q + 1] = bf16_hi(w[q]);
+    }
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int kPerVec = 4;
+  __device__ static float val(const float* p, long i) { return p[i]; }
+  __device__ static void unpack(u32x4 w, float* x) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(w[q]);
+  }
+};
+
+// Row split: [0, head) scalar, [head, tail) as 16-byte vectors, [tail, V) scalar.
+struct RowGeom {
+  int head, nvec, tail;
+};
+template <typename T> __device__ __forceinline__ RowGeom row_geom(const T* p, int V) {
+  constexpr int PV = Elem<T>::kPerVec;
+  const uintptr_t a = (uintptr_t)p;
+  int head = (int)(((16u - (uint32_t)(a & 15u)) & 15u) / sizeof(T));
+  if (head > V) head = V;
+  const int nvec = (V - head) / PV;
+  return {head, nvec, head + nvec * PV};
+}
+
+// One (row, chunk) of the sampled statistics pass.
+template <typename T>
+__device__ __forceinline__ void chunk_stats(const T* __restrict__ row, int V, int nch, int c,
+                                            float cl, StatSlot* __restrict__ out, float* smf,
+                                            double* smd) {
+  constexpr int PV = Elem<T>::kPerVec;
+  const RowGeom g = row_geom(row, V);
+  const int cv = (g.nvec + nch - 1) / nch;
+  const int v0 = c * cv;
+  const int v1 = min(g.nvec, v0 + cv);
+  const u32x4* vp = (const u32x4*)(row + g.head);
+  const int tid = threadIdx.x;
+
+  u32x4 buf[kVpt];
+#pragma unroll
+  for (int j = 0; j < kVpt; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    if (v < v1) buf[j] = __builtin_nontemporal_load(vp + v);
+  }
+  // this thread's scalar elements: one of the unaligned head, one of the tail
+  float sh = -INFINITY, st = -INFINITY;
+  if (c == 0 && tid < g.head) sh = Elem<T>::val(row, tid);
+  if (c == nch - 1 && tid < V - g.tail) st = Elem<T>::val(row, g.tail + tid);
+
+  float m = fmaxf(sh, st);
+#pragma unroll
+  for (int j = 0; j < kVpt; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    if (v < v1) {
+      float x[PV];
+      Elem<T>::unpack(buf[j], x);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) m = fmaxf(m, x[e]);
+    }
+  }
+  const float M = block_max<kThreads / 64>(m, smf);
+  const float ref = M * cl;
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < kVpt; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    if (v < v1) {
+      float x[PV];
+      Elem<T>::unpack(buf[j], x);
+      float e8[PV];
+#pragma unroll
+      for (int e = 0; e < PV; ++e) e8[e] = fast_exp2(__builtin_fmaf(x[e], cl, -ref));
+      // pairwise within the vector, fp64 across vectors
+#pragma unroll
+      for (int w = PV / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; ++e) e8[e] += e8[e + w];
+      s += (double)e8[0];
+    }
+  }
+  if (sh != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(sh, cl, -ref));
+  if (st != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(st, cl, -ref));
+  const double S = block_sum<kThreads / 64>(s, smd);
+  if (tid == 0) {
+    out->ref = ref;
+    out->flag = (M == INFINITY || M != M) ? 1u : 0u;
+    out->sum = S;
+  }
+}
+
+// One (row, chunk) of the greedy pass: (max value, lowest index) as a 64-bit key.
+template <typename T>
+__device__ __forceinline__ void chunk_argmax(const T* __restrict__ row, int V, int nch, int c,
+                                             uint64_t* __restrict__ out, uint64_t* smk) {
+  constexpr int PV = Elem<T>::kPerVec;
+  const RowGeom g = row_geom(row, V);
+  const int cv = (g.nvec + nch - 1) / nch;
+  const int v0 = c * cv;
+  const int v1 = min(g.nvec, v0 + cv);
+  const u32x4* vp = (const u32x4*)(row + g.head);
+  const int tid = threadIdx.x;
+
+  u32x4 buf[kVpt];
+#pragma unroll
+  for (int j = 0; j < kVpt; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    if (v < v1) buf[j] = __builtin_nontemporal_load(vp + v);
+  }
+  float best = -INFINITY;
+  int bidx = -1;
+  if (c == 0 && tid < g.head) {
+    best = Elem<T>::val(row, tid);
+    bidx = tid;
+  }
+  // visit in increasing token order; strict '>' keeps the lowest index of equal values
+#pragma unroll
+  for (int j = 0; j < kVpt; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    if (v < v1) {
+      float x[PV];
+      Elem<T>::unpack(buf[j], x);
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const bool gt = x[e] > best || bidx < 0;
+        best = gt ? x[e] : best;
+        bidx = gt ? g.head + v * PV + e : bidx;
+      }
+    }
+  }
+  if (c == nch - 1 && tid < V - g.tail) {
+    const float x = Elem<T>::val(row, g.tail + tid);
+    if (x > best || bidx < 0) {
+      best = x;
+      bidx = g.tail + tid;
+    }
+  }
+  const uint64_t key = bidx < 0 ? 0ull : amax_key(best, (uint32_t)bidx);
+  const uint64_t K = block_max<kThreads / 64>(key, smk);
+  if (tid == 0) *out = K;
+}
+
+struct StatsArgs {
+  const void* tgt;
+  int64_t ld_t;
+  const void* drf;
+  int64_t ld_d_r, ld_d_k;
+  const int32_t* cu;
+  int32_t R, K, V, max_rows;
+  int32_t ncht, nchd;
+  float cl;
+  StatSlot* tstats;
+  StatSlot* dstats;
+  uint64_t* round_dev;  // sampled path: advanced once per call here, read by the decisions
+};
+
+template <typename TT>
+__global__ __launch_bounds__(kThreads) void verify_argmax_kernel(StatsArgs a) {
+  __shared__ uint64_t smk[kThreads / 64];
+  const int tot = a.cu[a.R];
+  const int T_rows = tot < 0 ? 0 : (tot > a.max_rows ? a.max_rows : tot);
+  const long items = (long)T_rows * a.ncht;
+  uint64_t* keys = (uint64_t*)a.tstats;
+  for (long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int row = (int)(it / a.ncht), c = (int)(it % a.ncht);
+    const TT* p = (const TT*)a.tgt + (size_t)row * a.ld_t;
+    chunk_argmax<TT>(p, a.V, a.ncht, c, keys + 2 * it, smk);
+  }
+}
+
+// log2-sum-exp2 of a row from its chunk slots (fp64). Sets *bad for non-finite rows.
+__device__ __forceinline__ double merge_lse(const StatSlot* s, int nch, bool* bad) {
+  float H = -INFINITY;
+  bool f = false;
+  for (int c = 0; c < nch; ++c) {
+    H = fmaxf(H, s[c].ref);
+    f |= s[c].flag != 0;
+  }
+  double S = 0.0;
+  for (int c = 0; c < nch; ++c)
+    if (s[c].ref != -INFINITY) S += s[c].sum * exp2((double)s[c].ref - (double)H);
+  const double L = (double)H + log2(S);
+  if (f || !(L == L) || L == INFINITY || L == -INFINITY) *bad = true;
+  return L;
+}
+
+__device__ __forceinline__ uint32_t merge_argmax(const StatSlot* s, int nch) {
+  const uint64_t* k = (const uint64_t*)s;
+  uint64_t b = 0;
+  for (int c = 0; c < nch; ++c) b = k[2 * c] > b ? k[2 * c] : b;
+  return amax_index(b);
+}
+
+template <typename T> __device__ __forceinline__ float load_elem(const void* base, size_t off) {
+  return Elem<T>::val((const T*)base, (long)off);
+}
+struct DecideArgs {
+  const void* tgt;
+  int t_dtype;
+  int64_t ld_t;
+  const void* drf;
+  int d_dtype;
+  int64_t ld_d_r, ld_d_k;
+  const int32_t* cu;
+  const int32_t* x;
+  int64_t ld_x;
+  const int32_t* parent;
+  int32_t R, K, V, max_rows;
+  int32_t ncht, nchd;
+  float cl;
+  uint64_t seed, round;
+  const int64_t* req_id;
+  const StatSlot* tstats;
+  const StatSlot* dstats;
+  int32_t* acc_len;
+  int32_t* out;
+  int32_t* stop;
+  float* p_x;
+  float* q_x;
+  int32_t* status;
+  const uint64_t* round_dev;  // when set, the round is read from device memory
+};
+
+__device__ __forceinline__ float load_t(const DecideArgs& a, int row, int v) {
+  const size_t off = (size_t)row * a.ld_t + v;
+  return a.t_dtype == DSP_BF16 ? load_elem<uint16_t>(a.tgt, off) : load_elem<float>(a.tgt, off);
+}
+__device__ __forceinline__ float load_d(const DecideArgs& a, int i, int k0, int v) {
+  const size_t off = (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k + v;
+  return a.d_dtype == DSP_BF16 ? load_elem<uint16_t>(a.drf, off) : load_elem<float>(a.drf, off);
+}
+
+// Writes the all -1 fault record of request i (one wavefront).
+__device__ void fault_request(const DecideArgs& a, int i, int bits) {
+  const int lane = threadIdx.x & 63;
+  for (int j = lane; j <= a.K; j += 64) a.out[(size_t)i * (a.K + 1) + j] = -1;
+  if (a.p_x)
+    for (int j = lane; j < a.K; j += 64) {
+      a.p_x[(size_t)i * a.K + j] = 0.f;
+      a.q_x[(size_t)i * a.K + j] = 0.f;
+    }
+  if (lane == 0) {
+    a.acc_len[i] = -1;
+    a.stop[i] = -1;
+    atomicOr(a.status, bits);
+  }
+}
+
+// Sampled decision of request i, run by one wavefront once all row statistics exist.
+// The sampling job (residual at the first rejection, or the bonus row) goes to *jout.
+template <typename TT, typename TD>
+__device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
+  const int lane = threadIdx.x & 63;
+  const int base = a.cu[i];
+  const int n = a.cu[i + 1] - base - 1;
+  const uint64_t rid = a.req_id ? (uint64_t)a.req_id[i] : (uint64_t)i;
+  const uint64_t rnd = a.round_dev ? *a.round_dev : a.round;
+  const int k = lane + 1;
+  const bool pos = k <= n;     // a draft position of the window
+  const bool bon = lane == n;  // prepares the bonus row (n < 64)
+  int x = 0;
+  if (pos) x = a.x[(size_t)i * a.ld_x + lane];
+  const bool tokbad = pos && (x < 0 || x >= a.V);
+  bool bad = false;
+  double lse_t = 0.0, lse_d = 0.0;
+  if (pos || bon) lse_t = merge_lse(a.tstats + (size_t)(base + lane) * a.ncht, a.ncht, &bad);
+  if (pos) lse_d = merge_lse(a.dstats + ((size_t)i * a.K + lane) * a.nchd, a.nchd, &bad);
+  float tx = 0.f, dx = 0.f;
+  if (pos && !tokbad) {
+    tx = load_elem<TT>(a.tgt, (size_t)(base + lane) * a.ld_t + x);
+    dx = load_elem<TD>(a.drf, (size_t)i * a.ld_d_r + (size_t)lane * a.ld_d_k + x);
+  }
+  uint64_t c[4] = {rnd, rid, (uint64_t)k, 0ull};
+  philox4x64_10(c, a.seed, 0ull);
+  const double u = unit_double(c[0]);
+  const double us = unit_double(c[1]);
+  double lp2 = 0.0, lq2 = 0.0;
+  bool acc = true;
+  if (pos && !tokbad) {
+    const double cl = (double)a.cl;
+    lp2 = (double)tx * cl - lse_t;
+    lq2 = (double)dx * cl - lse_d;
+    acc = u < exp2(lp2 - lq2);
+  }
+  if (__ballot(tokbad)) {
+    fault_request(a, i, DSP_STATUS_TOKEN_RANGE);
+    if (lane == 0) jout->mode = JOB_NONE;
+    return;
+  }
+  if (__ballot(pos && bad)) {
+    fault_request(a, i, DSP_STATUS_NONFINITE);
+    if (lane == 0) jout->mode = JOB_NONE;
+    return;
+  }
+  const uint64_t rej = __ballot(pos && !acc);
+  const int kstop = rej ? __ffsll((unsigned long long)rej) : n + 1;
+  const int accepted = kstop - 1;
+  if (a.p_x && lane < a.K) {
+    a.p_x[(size_t)i * a.K + lane] = pos ? (float)exp2(lp2) : 0.f;
+    a.q_x[(size_t)i * a.K + lane] = pos ? (float)exp2(lq2) : 0.f;
+  }
+  int32_t* orow = a.out + (size_t)i * (a.K + 1);
+  if (lane < accepted) orow[lane] = x;
+  else if (lane > accepted && lane <= a.K) orow[lane] = -1;
+  if (a.K == 64 && lane == 0 && accepted < 64) orow[64] = -1;
+  Job j;
+  j.pad = 0.0;
+  if (kstop <= n) {
+    if (k == kstop) {
+      j.mode = JOB_RESID;
+      j.kstop = kstop;
+      j.trow = base + lane;
+      j.drow = lane;
+      j.lse_t = lse_t;
+      j.lse_d = lse_d;
+      j.us = us;
+      *jout = j;
+    }
+  } else {
+    // whole window accepted: bonus from the row after the last draft
+    bool writer = n < 64 ? bon : lane == 0;
+    if (writer) {
+      double lt = lse_t, ub = us;
+      bool b2 = bad;
+      if (n >= 64) {
+        b2 = false;
+        lt = merge_lse(a.tstats + (size_t)(base + n) * a.ncht, a.ncht, &b2);
+        uint64_t c2[4] = {rnd, rid, (uint64_t)(n + 1), 0ull};
+        philox4x64_10(c2, a.seed, 0ull);
+        ub = unit_double(c2[1]);
+      }
+      j.mode = b2 ? JOB_NONE : JOB_BONUS;
+      j.kstop = n + 1;
+      j.trow = base + n;
+      j.drow = -1;
+      j.lse_t = lt;
+      j.lse_d = 0.0;
+      j.us = ub;
+      *jout = j;
+      if (b2) {
+        orow[n] = -1;
+        atomicOr(a.status, DSP_STATUS_NONFINITE);
+      }
+    }
+  }
+  if (lane == 0) {
+    a.acc_len[i] = accepted;
+    a.stop[i] = kstop;
+  }
+}
+
+// Statistics pass (T > 0): every packed target row and every windowed draft row.
+template <typename TT, typename TD>
+__global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a) {
+  __shared__ float smf[kThreads / 64];
+  __shared__ double smd[kThreads / 64];
+  if (a.round_dev && blockIdx.x == 0 && threadIdx.x == 0) *a.round_dev += 1;
+  const int tot = a.cu[a.R];
+  const int T_rows = tot < 0 ? 0 : (tot > a.max_rows ? a.max_rows : tot);
+  const long items_t = (long)T_rows * a.ncht;
+  const long items = items_t + (long)a.R * a.K * a.nchd;
+  for (long it = blockIdx.x; it < items; it += gridDim.x) {
+    if (it < items_t) {
+      const int row = (int)(it / a.ncht), c = (int)(it % a.ncht);
+      const TT* p = (const TT*)a.tgt + (size_t)row * a.ld_t;
+      chunk_stats<TT>(p, a.V, a.ncht, c, a.cl, a.tstats + it, smf, smd);
+    } else {
+      const long j = it - items_t;
+      const int rk = (int)(j / a.nchd), c = (int)(j % a.nchd);
+      const int i = rk / a.K, k0 = rk % a.K;
+      const int n = a.cu[i + 1] - a.cu[i] - 1;
+      if (k0 >= n) continue;  // uniform over the workgroup
+      const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
+      chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + j, smf, smd);
+    }
+  }
+}
+
+// Chain decision, greedy (T == 0).
+__global__ __launch_bounds__(64) void verify_decide_greedy(DecideArgs a) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  const int base = a.cu[i], end = a.cu[i + 1];
+  const int n = end - base - 1;
+  if (n < 0 || n > a.K || base < 0 || end > a.max_rows) {
+    fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
+    return;
+  }
+  const int k = lane + 1;
+  const bool active = k <= n;
+  bool acc = true, tokbad = false;
+  int x = -1, am = -1;
+  if (active) {
+    x = a.x[(size_t)i * a.ld_x + lane];
+    tokbad = x < 0 || x >= a.V;
+    am = (int)merge_argmax(a.tstats + (size_t)(base + lane) * a.ncht, a.ncht);
+    acc = x == am;
+  }
+  if (__ballot(tokbad)) {
+    fault_request(a, i, DSP_STATUS_TOKEN_RANGE);
+    return;
+  }
+  const uint64_t rej = __ballot(active && !acc);
+  const int kstop = rej ? __ffsll((unsigned long long)rej) : n + 1;
+  const int accepted = kstop - 1;
+  int32_t* orow = a.out + (size_t)i * (a.K + 1);
+  if (lane < accepted) orow[lane] = x;
+  else if (lane > accepted && lane <= a.K) orow[lane] = -1;
+  if (a.K == 64 && lane == 0 && accepted < 64) orow[64] = -1;
+  if (kstop <= n) {
+    if (k == kstop) orow[lane] = am;
+  } else if (lane == 0) {
+    orow[n] = (int)merge_argmax(a.tstats + (size_t)(base + n) * a.ncht, a.ncht);
+  }
+  if (a.p_x && lane < a.K) {
+    a.p_x[(size_t)i * a.K + lane] = 0.f;
+    a.q_x[(size_t)i * a.K + lane] = 0.f;
+  }
+  if (lane == 0) {
+    a.acc_len[i] = accepted;
+    a.stop[i] = kstop;
+  }
+}
+
+// Greedy walk of a draft tree; lane j holds node j.
+__global__ __launch_bounds__(64) void verify_decide_tree(DecideArgs a) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  const int base = a.cu[i], end = a.cu[i + 1];
+  const int nn = end - base - 1;
+  if (nn < 0 || nn > a.K || base < 0 || end > a.max_rows) {
+    fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
+    return;
+  }
+  int tok = -1, par = -2;
+  if (lane < nn) {
+    tok = a.x[(size_t)i * a.ld_x + lane];
+    par = a.parent[(size_t)i * a.ld_x + lane];
+  }
+  if (__ballot(lane < nn && (tok < 0 || tok >= a.V))) {
+    fault_request(a, i, DSP_STATUS_TOKEN_RANGE);
+    return;
+  }
+  int32_t* orow = a.out + (size_t)i * (a.K + 1);
+  int cur = -1, depth = 0;
+  int am = 0;
+  while (true) {
+    am = (int)merge_argmax(a.tstats + (size_t)(base + 1 + cur) * a.ncht, a.ncht);
+    const uint64_t m = __ballot(lane < nn && par == cur && tok == am);
+    if (!m || depth >= a.K) break;
+    const int j = __ffsll((unsigned long long)m) - 1;
+    const int tj = __shfl(tok, j, 64);
+    if (lane == 0) orow[depth] = tj;
+    cur = j;
+    ++depth;
+  }
+  for (int j = depth + 1 + lane; j <= a.K; j += 64) orow[j] = -1;
+  if (lane == 0) {
+    orow[depth] = am;
+    a.acc_len[i] = depth;
+    a.stop[i] = cur;
+  }
+}
+
+struct JobFrame {
+  float t_hi, t_lo, d_hi, d_lo, cl;
+  bool resid;
+};
+__device__ __forceinline__ JobFrame job_frame(const Job& j, float cl, bool resid) {
+  JobFrame f;
+  f.t_hi = (float)j.lse_t;
+  f.t_lo = (float)(j.lse_t - (double)f.t_hi);
+  f.d_hi = (float)j.lse_d;
+  f.d_lo = (float)(j.lse_d - (double)f.d_hi);
+  f.cl = cl;
+  f.resid = resid;
+  return f;
+}
+__device__ __forceinline__ float job_weight(const JobFrame& f, float t, float d) {
+  const float p = fast_exp2(__builtin_fmaf(t, f.cl, -f.t_hi) - f.t_lo);
+  if (!f.resid) return p;
+  const float q = fast_exp2(__builtin_fmaf(d, f.cl, -f.d_hi) - f.d_lo);
+  return fmaxf(p - q, 0.f);
+}
+
+template <typename T> __device__ __forceinline__ void load8(const T* p, bool vec, float* x) {
+  if (vec) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 w = *(const u32x4*)p;
+      Elem<uint16_t>::unpack(w, x);
+    } else {
+      const u32x4 w0 = *(const u32x4*)p;
+      const u32x4 w1 = *((const u32x4*)p + 1);
+      Elem<float>::unpack(w0, x);
+      Elem<float>::unpack(w1, x + 4);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = Elem<T>::val(p, e);
+  }
+}
+
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleMaxChunks = 32;
+constexpr int kSampleVec = kSampleThreads * 8;  // elements covered by one 8-wide step of the workgroup
+
+// Weights of 8 consecutive elements starting at e (16-byte loads when aligned, guarded tail).
+// Eight consecutive logits as raw 16-byte vectors (one for bf16, two for fp32).
+template <typename T> struct Raw8 {
+  u32x4 w[sizeof(T) / 2];
+  __device__ __forceinline__ void load(const T* p) {
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(T) / 2); ++q) w[q] = __builtin_nontemporal_load((const u32x4*)p + q);
+  }
+  __device__ __forceinline__ void unpack(float* x) const {
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(T) / 2); ++q) Elem<T>::unpack(w[q], x + q * Elem<T>::kPerVec);
+  }
+};
+
+template <typename TT, typename TD>
+__device__ __forceinline__ float job_weight8(const JobFrame& f, const TT* tp, const TD* dp, bool t_al, bool d_al,
+                                             int e, int V) {
+  float t[8], d[8];
+  float w = 0.f;
+  if (e + 8 <= V) {
+    load8<TT>(tp + e, t_al, t);
+    if (f.resid) load8<TD>(dp + e, d_al, d);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w += job_weight(f, t[q], f.resid ? d[q] : 0.f);
+  } else {
+    for (int q = 0; e + q < V; ++q)
+      w += job_weight(f, Elem<TT>::val(tp, e + q), f.resid ? Elem<TD>::val(dp, e + q) : 0.f);
+  }
+  return w;
+}
+
+// K2: one workgroup per request. Wavefront 0 takes the accept/reject decisions;
+// then the whole workgroup draws the corrected or bonus token by inverse CDF:
+// pass 1 sums the weights of up to 32 contiguous chunks (fp64), pass 2 rescans
+// the chunk holding u' * total with one 8-element range per thread and an fp64
+// exclusive scan, and the owning thread walks its range to the first element
+// whose cumulative weight exceeds the target.
+template <typename TT, typename TD>
+__global__ __launch_bounds__(kSampleThreads) void verify_decide_sample_kernel(DecideArgs a) {
+  __shared__ Job s_job;
+  __shared__ double s_part[kSampleThreads / 64][kSampleMaxChunks];
+  __shared__ double s_csum[kSampleMaxChunks];
+  __shared__ double s_wtot[kSampleThreads / 64];
+  __shared__ int s_chunk;
+  __shared__ double s_tau;
+  __shared__ int s_found;
+  __shared__ int s_lastp[kSampleThreads / 64];
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < 64) {
+    const int base = a.cu[i], end = a.cu[i + 1];
+    const int n = end - base - 1;
+    if (n < 0 || n > a.K || base < 0 || end > a.max_rows) {
+      fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
+      if (lane == 0) s_job.mode = JOB_NONE;
+    } else {
+      decide_sampled<TT, TD>(a, i, &s_job);
+    }
+  }
+  __syncthreads();
+  const Job jb = s_job;
+  if (jb.mode == JOB_NONE) return;  // uniform over the workgroup
+  const int V = a.V;
+  bool resid = jb.mode == JOB_RESID;
+  const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
+  const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
+  const bool t_al = (((uintptr_t)tp) & 15u) == 0;
+  const bool d_al = !resid || (((uintptr_t)dp) & 15u) == 0;
+  // chunking: nc chunks of ce elements (ce a multiple of one workgroup step)
+  int nc = (V + kSampleVec - 1) / kSampleVec;
+  if (nc > kSampleMaxChunks) nc = kSampleMaxChunks;
+  const int steps = (V + nc * kSampleVec - 1) / (nc * kSampleVec);
+  const int ce = steps * kSampleVec;
+  JobFrame f = job_frame(jb, a.cl, resid);
+  double total = 0.0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    // pass 1: per-chunk sums. Vector vi of this thread covers 8 elements of chunk vi / steps;
+    // a batch of kBatch vectors (both rows) is loaded before any is used.
+    constexpr int kBatch = (sizeof(TT) == 2 && sizeof(TD) == 2) ? 8 : 4;
+    const int nvec = nc * steps;
+    for (int q = tid; q < (kSampleThreads / 64) * kSampleMaxChunks; q += kSampleThreads)
+      (&s_part[0][0])[q] = 0.0;
+    __syncthreads();
+    for (int vb = 0; vb < nvec; vb += kBatch) {
+      Raw8<TT> rt[kBatch];
+      Raw8<TD> rd[kBatch];
+      bool fast[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int vi = vb + b;
+        const int e = (vi / steps) * ce + (vi % steps) * kSampleVec + tid * 8;
+        fast[b] = vi < nvec && e + 8 <= V && t_al && d_al;
+        if (fast[b]) {
+          rt[b].load(tp + e);
+          if (f.resid) rd[b].load(dp + e);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int vi = vb + b;
+        if (vi >= nvec) break;  // uniform
+        const int e = (vi / steps) * ce + (vi % steps) * kSampleVec + tid * 8;
+        float wsum = 0.f;
+        if (fast[b]) {
+          float t[8], d[8];
+          rt[b].unpack(t);
+          if (f.resid) rd[b].unpack(d);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) wsum += job_weight(f, t[q], f.resid ? d[q] : 0.f);
+        } else if (e < V) {
+          wsum = job_weight8<TT, TD>(f, tp, dp, false, false, e, V);
+        }
+        const double ws = wave_sum((double)wsum);
+        if (lane == 0) s_part[w][vi / steps] += ws;
+      }
+    }
+    __syncthreads();
+    if (tid < nc) {
+      double cs = 0.0;
+      for (int q = 0; q < kSampleThreads / 64; ++q) cs += s_part[q][tid];
+      s_csum[tid] = cs;
+    }
+    __syncthreads();
+    total = 0.0;
+    for (int c = 0; c < nc; ++c) total += s_csum[c];
+    if (!resid || total > 0.0) break;
+    // empty residual (p <= q everywhere after rounding): draw from p instead
+    resid = false;
+    f = job_frame(jb, a.cl, false);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double target = jb.us * total;
+    double acc = 0.0;
+    int cs = -1;
+    for (int c = 0; c < nc; ++c) {
+      if (acc + s_csum[c] > target) {
+        cs = c;
+        break;
+      }
+      acc += s_csum[c];
+    }
+    double tau = target - acc;
+    if (cs < 0) {  // rounding left no chunk: take the last chunk with weight
+      for (int c = nc - 1; c >= 0; --c)
+        if (s_csum[c] > 0.0) {
+          cs = c;
+          break;
+        }
+      tau = INFINITY;
+    }
+    s_chunk = cs;
+    s_tau = tau;
+    s_found = 0x7fffffff;
+  }
+  __syncthreads();
+  const int cs = s_chunk;
+  const double tau = s_tau;
+  int32_t* dst = a.out + (size_t)i * (a.K + 1) + jb.kstop - 1;
+  if (cs < 0) {
+    if (tid == 0) *dst = -1;
+    return;
+  }
+  // pass 2: contiguous per-thread ranges of the chosen chunk
+  const int e0 = cs * ce;
+  const int per = steps * 8;
+  const int r0 = min(V, e0 + tid * per), r1 = min(V, r0 + per);
+  double s = 0.0;
+  for (int e = r0; e < r1; e += 8) s += (double)job_weight8<TT, TD>(f, tp, dp, t_al, d_al, e, r1);
+  double inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_wtot[w] = inc;
+  __syncthreads();
+  double off = 0.0;
+  for (int q = 0; q < w; ++q) off += s_wtot[q];
+  const double E = off + inc - s;
+  if (E <= tau && tau < E + s) {
+    double run = E;
+    for (int e = r0; e < r1; ++e) {
+      run += (double)job_weight(f, Elem<TT>::val(tp, e), resid ? Elem<TD>::val(dp, e) : 0.f);
+      if (run > tau) {
+        atomicMin(&s_found, e);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (s_found == 0x7fffffff) {
+    // rounding put the target past the rescanned total: last token with weight in the chunk
+    int last_pos = -1;
+    for (int e = r1 - 1; e >= r0 && last_pos < 0; --e)
+      if (job_weight(f, Elem<TT>::val(tp, e), resid ? Elem<TD>::val(dp, e) : 0.f) > 0.f) last_pos = e;
+    const int lp = block_max<kSampleThreads / 64>(last_pos, s_lastp);
+    if (tid == 0) s_found = lp;
+    __syncthreads();
+  }
+  if (tid == 0) *dst = s_found;
+}
+
+int g_cus = 0;
+int num_cus() {
+  if (g_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_cus = n;
+    else
+      g_cus = 256;
+  }
+  return g_cus;
+}
+
+struct VerifyLayout {
+  int ncht, nchd, max_rows;
+  size_t off_t, off_d, total;
+};
+
+VerifyLayout verify_layout(int R, int K, int V, int max_rows, int t_dtype, int d_dtype) {
+  VerifyLayout L;
+  L.max_rows = max_rows > 0 ? max_rows : R * (K + 1);
+  L.ncht = stat_chunks(V, esize_of(t_dtype));
+  L.nchd = stat_chunks(V, esize_of(d_dtype));
+  size_t off = 0;
+  L.off_t = off;
+  off = align_up(off + (size_t)L.max_rows * L.ncht * sizeof(StatSlot), 256);
+  L.off_d = off;
+  off = align_up(off + (size_t)R * K * L.nchd * sizeof(StatSlot), 256);
+  L.total = off;
+  return L;
+}
+
+template <typename TT, typename TD>
+void launch_sampled(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items) {
+  const int cus = num_cus();
+  long g = max_items < (long)cus * 8 ? max_items : (long)cus * 8;
+  if (g < 1) g = 1;
+  prof_begin(DSP_K_VERIFY_STATS, s);
+  hipLaunchKernelGGL((verify_stats_kernel<TT, TD>), dim3((unsigned)g), dim3(kThreads), 0, s, sa);
+  prof_end(DSP_K_VERIFY_STATS, s);
+  prof_begin(DSP_K_VERIFY_SAMPLE, s);
+  hipLaunchKernelGGL((verify_decide_sample_kernel<TT, TD>), dim3(da.R), dim3(kSampleThreads), 0, s, da);
+  prof_end(DSP_K_VERIFY_SAMPLE, s);
+}
+
+template <typename TT>
+void launch_greedy(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items, bool tree) {
+  const int cus = num_cus();
+  long g = max_items < (long)cus * 8 ? max_items : (long)cus * 8;
+  if (g < 1) g = 1;
+  prof_begin(DSP_K_VERIFY_STATS, s);
+  hipLaunchKernelGGL((verify_argmax_kernel<TT>), dim3((unsigned)g), dim3(kThreads), 0, s, sa);
+  prof_end(DSP_K_VERIFY_STATS, s);
+  prof_begin(DSP_K_VERIFY_DECIDE, s);
+  if (tree)
+    hipLaunchKernelGGL(verify_decide_tree, dim3(da.R), dim3(64), 0, s, da);
+  else
+    hipLaunchKernelGGL(verify_decide_greedy, dim3(da.R), dim3(64), 0, s, da);
+  prof_end(DSP_K_VERIFY_DECIDE, s);
+}
+
+}  // namespace
+}  // namespace dsp
+using namespace dsp;
+
+extern "C" size_t dsp_verify_rejection_workspace_size(int32_t R, int32_t K, int32_t V, int32_t max_rows,
+                                                      int32_t t_dtype, int32_t d_dtype) {
+  if (R < 1 || K < 1 || V < 1 || max_rows < 0) return 0;
+  return verify_layout(R, K, V, max_rows, t_dtype, d_dtype).total;
+}
+
+extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
+                                        const int32_t* cu_seqlens, const void* drf, int32_t d_dtype,
+                                        int64_t ld_d_r, int64_t ld_d_k, const int32_t* draft_tok,
+                                        int64_t ld_x, const int32_t* parent, int32_t R, int32_t K,
+                                        int32_t V, int32_t max_rows, float temperature, uint64_t seed,
+                                        uint64_t round, uint64_t* round_dev, const int64_t* req_id,
+                                        int32_t* accepted_len,
+                                        int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x,
+                                        int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (R < 1 || K < 1 || K > 64 || V < 1)
+    return fail(DSP_ERR_SHAPE, "need R >= 1, 1 <= K <= 64, V >= 1 (R=%d K=%d V=%d)", R, K, V);
+  if (t_dtype != DSP_F32 && t_dtype != DSP_BF16) return fail(DSP_ERR_DTYPE, "bad target dtype %d", t_dtype);
+  if (!(temperature >= 0.f) || temperature == INFINITY)
+    return fail(DSP_ERR_SHAPE, "temperature must be finite and >= 0");
+  const bool greedy = temperature == 0.f;
+  const bool tree = parent != nullptr;
+  if (tree && !greedy) return fail(DSP_ERR_UNSUPPORTED, "tree verify supports temperature 0 only");
+  if (!greedy && d_dtype != DSP_F32 && d_dtype != DSP_BF16)
+    return fail(DSP_ERR_DTYPE, "bad draft dtype %d", d_dtype);
+  if (!tgt || !cu_seqlens || !draft_tok || !accepted_len || !out_tokens || !stop_pos || !status)
+    return fail(DSP_ERR_NULL, "required pointer is NULL");
+  if (!greedy && !drf) return fail(DSP_ERR_NULL, "draft logits required for temperature > 0");
+  if ((p_x == nullptr) != (q_x == nullptr)) return fail(DSP_ERR_NULL, "p_x and q_x go together");
+  if (ld_t < V || ld_x < K) return fail(DSP_ERR_SHAPE, "strides too small");
+  if (!greedy && (ld_d_k < V || ld_d_r < (int64_t)K * ld_d_k))
+    return fail(DSP_ERR_SHAPE, "draft strides too small");
+  if (max_rows < 0 || max_rows > R * (K + 1)) return fail(DSP_ERR_SHAPE, "max_rows out of range");
+  if (((uintptr_t)tgt) % esize_of(t_dtype) || (!greedy && ((uintptr_t)drf) % esize_of(d_dtype)))
+    return fail(DSP_ERR_ALIGN, "logits must be aligned to their element size");
+  const int ddt = greedy ? DSP_BF16 : d_dtype;
+  const VerifyLayout L = verify_layout(R, K, V, max_rows, t_dtype, ddt);
+  if (!ws || ws_bytes < L.total) return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+
+  StatSlot* tstats = (StatSlot*)((uintptr_t)ws + L.off_t);
+  StatSlot* dstats = (StatSlot*)((uintptr_t)ws + L.off_d);
+  const float cl = greedy ? 0.f : (float)(1.4426950408889634074 / (double)temperature);
+  hipStream_t s = (hipStream_t)stream;
+
+  StatsArgs sa{tgt, ld_t, drf, ld_d_r, ld_d_k, cu_seqlens, R, K, V, L.max_rows, L.ncht, L.nchd, cl,
+               tstats, dstats, greedy ? nullptr : round_dev};
+  DecideArgs da{tgt, t_dtype, ld_t, drf, ddt, ld_d_r, ld_d_k, cu_seqlens, draft_tok, ld_x, parent,
+                R, K, V, L.max_rows, L.ncht, L.nchd, cl, seed, round, req_id, tstats, dstats,
+                accepted_len, out_tokens, stop_pos, p_x, q_x, status, round_dev};
+  if (greedy) {
+    const long max_items = (long)L.max_rows * L.ncht;
+    if (t_dtype == DSP_BF16) launch_greedy<uint16_t>(sa, da, s, max_items, tree);
+    else launch_greedy<float>(sa, da, s, max_items, tree);
+  } else {
+    const long max_items = (long)L.max_rows * L.ncht + (long)R * K * L.nchd;
+    if (t_dtype == DSP_BF16 && d_dtype == DSP_BF16) launch_sampled<uint16_t, uint16_t>(sa, da, s, max_items);
+    else if (t_dtype == DSP_BF16) launch_sampled<uint16_t, float>(sa, da, s, max_items);
+    else if (d_dtype == DSP_BF16) launch_sampled<float, uint16_t>(sa, da, s, max_items);
+    else launch_sampled<float, float>(sa, da, s, max_items);
+  }
+  return hip_check(hipGetLastError(), "verify launch");
+}

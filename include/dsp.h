@@ -1,0 +1,262 @@
+/*
+ * dsp.h -- C ABI of the MI355X (gfx950) library for confidence-scheduled
+ * speculative decoding: Markov-head drafting (greedy chain and PCTree tree
+ * expansion), the confidence scheduler, ragged packing and batched verify.
+ *
+ * Sources of the operations (web pages on DSpark and PCTree):
+ *   [N]  DSpark study notes, pages.layerx.co.jp ("DSpark: Confidence-Scheduled
+ *        Speculative Decoding with Semi-Autoregressive Generation"), sections 1-9.
+ *   [P]  PCTree article, qiita.com ("Parent-Conditioned Drafting Tree").
+ *   [S]  SGLang integration article, winzheng.jp ("DSpark in SGLang").
+ *
+ * Conventions shared by every call
+ *   - All pointers are DEVICE pointers unless a parameter says "host".
+ *     The library never allocates device memory: every call that needs
+ *     scratch space takes (ws, ws_bytes) sized by its *_workspace_size query.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream) and deterministic: identical inputs give identical bits.
+ *   - Inputs are read only; outputs must not alias inputs or each other.
+ *   - Return value: DSP_OK (0) or a negative DSP_ERR_* code. Argument checks
+ *     run on the host before any HIP call, so an error return means nothing
+ *     was launched. dsp_last_error() gives a message (thread local).
+ *   - Data-dependent faults that only the device can see (a token id outside
+ *     [0, V), a window outside [0, K], non-finite logits) are OR-ed into the
+ *     device word `*status` as DSP_STATUS_* bits; the caller zeroes it before
+ *     the call and reads it after synchronising. The affected request's
+ *     outputs are set to -1.
+ *   - Logit rows: element (row r, token v) lives at base + r*ld + v, with ld
+ *     in elements, ld >= V. dtype is DSP_F32 or DSP_BF16 (bfloat16 bits).
+ *   - Calls on the same stream may be issued back to back; concurrent calls
+ *     must use distinct workspaces.
+ */
+#ifndef DSP_H
+#define DSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSP_OK                 0
+#define DSP_ERR_NULL          -1  /* a required pointer is NULL */
+#define DSP_ERR_SHAPE         -2  /* a size or stride is out of range */
+#define DSP_ERR_DTYPE         -3  /* unknown dtype code */
+#define DSP_ERR_ALIGN         -4  /* pointer alignment requirement not met */
+#define DSP_ERR_WORKSPACE     -5  /* workspace NULL or smaller than the query */
+#define DSP_ERR_UNSUPPORTED   -6  /* valid but unsupported combination */
+#define DSP_ERR_HIP           -7  /* a HIP runtime call failed */
+
+#define DSP_F32   0
+#define DSP_BF16  1
+
+#define DSP_STATUS_TOKEN_RANGE   1  /* a token id outside [0, V) */
+#define DSP_STATUS_WINDOW_RANGE  2  /* cu_seqlens / windows inconsistent with K or max_rows */
+#define DSP_STATUS_NONFINITE     4  /* a logits row whose maximum is not finite */
+
+#define DSP_SCHED_EARLY_STOP  0
+#define DSP_SCHED_ARGMAX      1
+
+/* Library version, (major << 16) | minor. */
+int32_t dsp_version(void);
+
+/* Message describing the last error returned on this thread ("" if none). */
+const char* dsp_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Counter-based uniforms.                                                   */
+/*                                                                          */
+/* Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As   */
+/* Easy as 1, 2, 3", SC'11) keyed by (seed, 0). For n counters given as      */
+/* ctr[4*j .. 4*j+3] (uint64, device), writes the four output words of each   */
+/* block mapped to doubles in [0, 1) as (w >> 11) * 2^-53 into out[4*j ..].   */
+/* This is the generator the verify call uses at counter (round, request id, */
+/* position k, 0): word 0 is the accept uniform u_k, word 1 the sampling      */
+/* uniform u'_k.                                                             */
+/* ------------------------------------------------------------------------ */
+int32_t dsp_philox_uniforms(const uint64_t* ctr, int64_t n, uint64_t seed, double* out,
+                            void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Survival products and window selection  ([N] 5.1-5.2, [S] "SPS cost table") */
+/*                                                                          */
+/* conf [R, K] float32 row-major: c_{i,k}, the probability that draft k of    */
+/* request i survives given that drafts 1..k-1 did ([N] 5.1).                 */
+/* Survival S_{i,k} = prod_{j<=k} c_{i,j} (fp64, left to right). Candidates   */
+/* (i, k) are ranked by S descending (ties: i, then k ascending); with E_j the*/
+/* sum of the first j survivals and cost[j] the step time when j draft tokens */
+/* are verified, candidate j is taken iff E_j / cost[j] > E_{j-1} / cost[j-1] */
+/* (throughput strictly rises), stopping at the first candidate that fails    */
+/* (DSP_SCHED_EARLY_STOP, the non-anticipating rule of [N] 5.2), or the       */
+/* smallest j maximising E_j / cost[j] (DSP_SCHED_ARGMAX, the SPS-argmax      */
+/* budget of [S] / global search of [N] 9.2; cost must then be > 0).          */
+/* Survivals are summed as exact integers on a 2^-Q grid,                     */
+/* Q = min(40, 53 - ceil(log2(R*K))), so the windows are bit-reproducible.    */
+/*   cost      [n_cost] fp64, n_cost >= R*K + 1 (device).                     */
+/*   max_tokens  cap on N = sum_i n_i (< 0: none).                             */
+/* Outputs: windows [R] int32 (n_i in [0, K]); survival [R, K] fp64 (nullable);*/
+/* stats [4] fp64 (nullable): N, E (in probability units), J = E / cost[N], Q. */
+/* Limits: 1 <= K <= 128, 1 <= R, R*K <= 8192.                                 */
+/* ------------------------------------------------------------------------ */
+size_t dsp_schedule_windows_workspace_size(int32_t R, int32_t K);
+int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
+                             int32_t n_cost, int32_t mode, int32_t max_tokens,
+                             int32_t* windows, double* survival, double* stats,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Ragged pack  ([S] "Ragged verify")                                         */
+/*                                                                          */
+/* Request i contributes its anchor then its first windows[i] drafts, front  */
+/* packed in request order: cu_seqlens[0] = 0,                               */
+/* cu_seqlens[i+1] = cu_seqlens[i] + windows[i] + 1; tokens[cu_seqlens[i]+k] */
+/* is the anchor (k = 0) or drafts[i*ld_drafts + k-1]; row_req / row_pos give */
+/* (i, k) for every packed row. total_and_tier[0] = T = cu_seqlens[R];       */
+/* total_and_tier[1] = the smallest tiers[t] >= T (tiers ascending, host      */
+/* NULL / n_tiers = 0: T itself; -1 if none is large enough).                */
+/* Buffers tokens/row_req/row_pos hold R*(K+1) entries; entries >= T are     */
+/* left untouched. windows outside [0, K] set DSP_STATUS_WINDOW_RANGE.       */
+/* Limits: 1 <= R <= 65536, 1 <= K <= 4096, n_tiers <= 64.                   */
+/* ------------------------------------------------------------------------ */
+int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const int32_t* drafts,
+                        int64_t ld_drafts, int32_t R, int32_t K, const int32_t* tiers_host,
+                        int32_t n_tiers, int32_t* cu_seqlens, int32_t* tokens, int32_t* row_req,
+                        int32_t* row_pos, int32_t* total_and_tier, int32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Batched ragged verify  ([N] 1, 3 / Figure 1; [S] "three verify modes",     */
+/* "Ragged verify"; [P] greedy tree verification)                            */
+/*                                                                          */
+/* Target logits are PACKED: request i owns rows cu_seqlens[i] ..            */
+/* cu_seqlens[i+1]-1 of tgt; row cu_seqlens[i] + k predicts draft position   */
+/* k+1. Its window is n_i = cu_seqlens[i+1] - cu_seqlens[i] - 1 (0..K).       */
+/* Draft logits are dense: position k (1-based) of request i is row           */
+/* drf + i*ld_d_r + (k-1)*ld_d_k. Draft tokens x_{i,k} at                    */
+/* draft_tok[i*ld_x + k-1].                                                  */
+/*                                                                          */
+/* Chain mode (parent == NULL), temperature T > 0: for k = 1..n_i,            */
+/* p_k = softmax(t_{k-1}/T), q_k = softmax(d_k/T); accept x_k iff             */
+/* u_k < p_k(x_k)/q_k(x_k), left to right; at the first rejection the token  */
+/* is drawn from norm(max(0, p_k - q_k)) with u'_k by inverse CDF over        */
+/* ascending token id; if all n_i are accepted the bonus is drawn from        */
+/* p_{n_i+1} with u'_{n_i+1}. u_k, u'_k: Philox4x64-10, key (seed, 0),        */
+/* counter (round, req_id[i] or i, k, 0), words 0 and 1. round_dev (device,  */
+/* nullable, in/out) replaces `round` with a device counter: each sampled call */
+/* increments *round_dev once and uses the new value, so the replays of a     */
+/* captured HIP graph draw fresh uniforms without any host update.           */
+/* T == 0: greedy; x_k accepted iff it equals argmax t_{k-1} (lowest id on    */
+/* ties), the stop token is that argmax; drf may be NULL.                     */
+/* Tree mode (parent != NULL, T must be 0): draft_tok / parent are the        */
+/* node tokens and parent indices [R, K] (-1 = root, parent[j] < j) of up to  */
+/* K nodes; request i owns rows cu_seqlens[i] (root) and cu_seqlens[i]+1+j    */
+/* (node j), n_nodes_i = cu_seqlens[i+1]-cu_seqlens[i]-1. From the root, move */
+/* to the child whose token equals argmax of the current row; the bonus is    */
+/* that argmax where no child matches.                                       */
+/*                                                                          */
+/* Outputs (device):                                                         */
+/*   accepted_len [R] int32    accepted drafts (-1 if the request faulted)    */
+/*   out_tokens [R, K+1] int32 accepted drafts then the corrected / bonus     */
+/*                             token; -1 after it                            */
+/*   stop_pos [R] int32        chain: position of the sampled token           */
+/*                             (accepted_len + 1); tree: last accepted node   */
+/*                             (-1 = root)                                   */
+/*   p_x, q_x [R, K] float32   (nullable; chain, T > 0) p_k(x_k), q_k(x_k)    */
+/*                             for every window position, 0 elsewhere        */
+/* max_rows: host-known bound on cu_seqlens[R] (0 = R*(K+1)); tgt must hold    */
+/* at least that many rows. Rows past min(cu_seqlens[R], max_rows) are never  */
+/* read, and a request whose rows end past max_rows is a window fault.        */
+/* Limits: 1 <= K <= 64, 1 <= V < 2^31, ld >= V.                             */
+/* ------------------------------------------------------------------------ */
+size_t dsp_verify_rejection_workspace_size(int32_t R, int32_t K, int32_t V, int32_t max_rows,
+                                           int32_t t_dtype, int32_t d_dtype);
+int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
+                             const int32_t* cu_seqlens,
+                             const void* drf, int32_t d_dtype, int64_t ld_d_r, int64_t ld_d_k,
+                             const int32_t* draft_tok, int64_t ld_x, const int32_t* parent,
+                             int32_t R, int32_t K, int32_t V, int32_t max_rows,
+                             float temperature, uint64_t seed, uint64_t round,
+                             uint64_t* round_dev, const int64_t* req_id,
+                             int32_t* accepted_len, int32_t* out_tokens, int32_t* stop_pos,
+                             float* p_x, float* q_x, int32_t* status,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Markov-head sequential stage, greedy chain  ([N] 4; [P] z_d = L_d +        */
+/* Markov(y_{d-1}))                                                          */
+/*                                                                          */
+/* For d = 1..n_steps and every request i:                                   */
+/*   z_d = L[i, d-1, :] + U[y_{d-1}, :] . W,   y_d = argmax_v z_d (fp32 z,    */
+/*   lowest id on ties),  y_0 = prev_tok[i];                                  */
+/*   logq[i, d-1] = z_d[y_d] - logsumexp(z_d)  (if logq != NULL).             */
+/* L: bf16, element (i, d, v) at L + i*ldL_r + d*ldL_d + v.                   */
+/* U: bf16 [V, rank] row-major (row y = the first factor's row of token y).   */
+/* Wt: bf16 [V, rank] row-major = the second factor W [rank, V] stored        */
+/*     vocab-major (Wt[v*rank + j] = W[j][v]).                               */
+/* y [R, n_steps] int32 with row stride ld_y; logq float32 same layout.       */
+/* Limits: rank % 32 == 0, 32 <= rank <= 512, 1 <= n_steps, V >= 1.          */
+/* ------------------------------------------------------------------------ */
+size_t dsp_draft_markov_step_workspace_size(int32_t R, int32_t V, int32_t rank, int32_t n_steps,
+                                            int32_t want_logq);
+int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
+                              const void* U, const void* Wt, int32_t V, int32_t rank,
+                              const int32_t* prev_tok, int32_t R, int32_t n_steps,
+                              int32_t* y, int64_t ld_y, float* logq, int32_t* status,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* PCTree expansion  ([P] "the chain becomes a tree")                         */
+/*                                                                          */
+/* Per request, root = anchor with score 0. For depth d = 1..D and every      */
+/* parent p of frontier F_{d-1}: z = L[i, d-1, :] + U[tok(p)] . W (one batched */
+/* Markov call for all parents); children = top-k tokens by (fp32 z desc, id  */
+/* asc); child score s = s(p) + z_v - logsumexp(z) (fp64). F_d = top-F        */
+/* children by (s desc, parent slot asc, child rank asc). The tree is the     */
+/* top-N of all frontier nodes of all depths by (s desc, depth asc, slot asc),*/
+/* parents re-indexed into that order (parent[j] < j, -1 = root).             */
+/* Outputs [R, topN] (row stride topN): node_token, node_parent, node_depth   */
+/* (int32), node_score (fp64); n_nodes [R] = nodes written (rest: -1 / 0).    */
+/* L, U, Wt layouts as dsp_draft_markov_step.                                 */
+/* Limits: 1 <= topk <= min(4, V), 1 <= frontier <= 64, topk*frontier <= 256,  */
+/* 1 <= topN <= 1024, D*frontier <= 1024, rank as above.                      */
+/* ------------------------------------------------------------------------ */
+size_t dsp_tree_expand_workspace_size(int32_t R, int32_t D, int32_t V, int32_t rank,
+                                      int32_t topk, int32_t frontier, int32_t topN);
+int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
+                        const void* U, const void* Wt, int32_t V, int32_t rank,
+                        const int32_t* anchor, int32_t R, int32_t D, int32_t topk,
+                        int32_t frontier, int32_t topN,
+                        int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
+                        double* node_score, int32_t* n_nodes, int32_t* status,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (observability).                                            */
+/*                                                                          */
+/* dsp_prof_enable(mask): bit k set = bracket each launch of kernel k below  */
+/* with HIP events on its launch stream (mask 0 = off, -1 = all).            */
+/* dsp_prof_query synchronises on the recorded events and returns the summed */
+/* duration and launch count since the last reset. Not thread safe, and not  */
+/* to be used while a stream is being captured into a graph.                 */
+/* ------------------------------------------------------------------------ */
+#define DSP_K_VERIFY_STATS     0  /* row statistics / arg-max streaming pass */
+#define DSP_K_VERIFY_DECIDE    1  /* greedy matching / tree walk */
+#define DSP_K_VERIFY_RESIDUAL  2  /* reserved */
+#define DSP_K_VERIFY_SAMPLE    3  /* sampled: decisions + residual / bonus draw */
+#define DSP_K_SCHEDULE         4
+#define DSP_K_PACK             5
+#define DSP_K_MARKOV_GEMM      6
+#define DSP_K_MARKOV_MERGE     7
+#define DSP_K_TREE_GEMM        8
+#define DSP_K_TREE_MERGE       9
+#define DSP_K_TREE_FINAL      10
+#define DSP_K_COUNT           11
+int32_t dsp_prof_enable(int32_t mask);
+int32_t dsp_prof_reset(void);
+int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSP_H */

@@ -1,0 +1,92 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_drafting_verification_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsp.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("dsp_draft_markov_step", "dsp_tree_expand", "dsp_schedule_windows", "dsp_pack_ragged",
+              "dsp_verify_rejection"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _abi.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_error_string():
+    lib = _abi.load()
+    assert lib.dsp_version() >> 16 >= 1
+    assert isinstance(lib.dsp_last_error(), bytes)
+
+
+def _err(rc):
+    return rc, _abi.load().dsp_last_error().decode()
+
+
+def test_host_validation_codes():
+    lib = _abi.load()
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    # verify: K out of range, bad dtype, missing pointers, negative temperature, small workspace
+    rc, msg = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 65, 100, 0, 1.0, 0, 0,
+                                            None, None, p, p, p, None, None, p, p, 1 << 30, None))
+    assert rc == -2 and "K" in msg
+    rc, _ = _err(lib.dsp_verify_rejection(p, 5, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
+                                          None, None, p, p, p, None, None, p, p, 1 << 30, None))
+    assert rc == -3
+    rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, None, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
+                                          None, None, p, p, p, None, None, p, p, 1 << 30, None))
+    assert rc == -1
+    rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, -1.0, 0, 0,
+                                          None, None, p, p, p, None, None, p, p, 1 << 30, None))
+    assert rc == -2
+    rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, p, 4, 7, 100, 0, 1.0, 0, 0,
+                                          None, None, p, p, p, None, None, p, p, 1 << 30, None))
+    assert rc == -6  # tree verify needs temperature 0
+    rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
+                                          None, None, p, p, p, None, None, p, p, 16, None))
+    assert rc == -5
+    # schedule: too many candidates, short cost table, unknown mode
+    assert lib.dsp_schedule_windows(p, 9000, 1, p, 9001, 0, -1, p, None, None, None, 0, None) == -2
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 16, 0, -1, p, None, None, None, 0, None) == -2
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 3, -1, p, None, None, None, 0, None) == -6
+    # pack: descending tiers, too many tiers
+    tiers = (ctypes.c_int32 * 2)(8, 4)
+    assert lib.dsp_pack_ragged(p, p, p, 4, 3, 4, ctypes.cast(tiers, ctypes.c_void_p), 2, p, p, p, p, p, p,
+                               None) == -2
+    assert lib.dsp_pack_ragged(p, p, p, 4, 3, 4, None, 65, p, p, p, p, p, p, None) == -2
+    # markov: rank not a multiple of 32, misaligned factors
+    assert lib.dsp_draft_markov_step(p, 1, 1000, 100, p, p, 100, 48, p, 2, 4, p, 4, None, p, p, 1 << 30,
+                                     None) == -2
+    assert lib.dsp_draft_markov_step(p, 1, 1000, 100, ctypes.c_void_p(18), p, 100, 64, p, 2, 4, p, 4, None,
+                                     p, p, 1 << 30, None) == -4
+    # tree: top-k above 4
+    assert lib.dsp_tree_expand(p, 1, 1000, 100, p, p, 100, 64, p, 2, 4, 5, 4, 8, p, p, p, p, p, p, p,
+                               1 << 30, None) == -2
+
+
+def test_workspace_queries_are_pure_functions():
+    lib = _abi.load()
+    a = lib.dsp_verify_rejection_workspace_size(64, 7, 151936, 0, 1, 1)
+    assert a == lib.dsp_verify_rejection_workspace_size(64, 7, 151936, 0, 1, 1) and a > 0
+    assert lib.dsp_verify_rejection_workspace_size(0, 7, 10, 0, 1, 1) == 0
+    assert lib.dsp_tree_expand_workspace_size(128, 16, 129280, 256, 4, 16, 64) > 0
+    assert lib.dsp_draft_markov_step_workspace_size(256, 151936, 256, 16, 0) > 0

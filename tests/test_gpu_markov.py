@@ -1,0 +1,174 @@
+"""GPU parity of the Markov-head chain and PCTree expansion against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_verification_amd as dsp
+import workloads
+from oracle import markov as om
+from oracle import pctree as opt
+from oracle import verify as ov
+from parity import ARGMAX_BAND, TieCounter, host, to_gpu, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_inputs(c):
+    Wt = np.ascontiguousarray(c["W"].T)  # second factor stored vocab-major
+    return (to_gpu_bf16(c["L"]), to_gpu_bf16(c["U"]), to_gpu_bf16(Wt),
+            to_gpu(c["anchors"].astype(np.int32)))
+
+
+def _f32(c):
+    return (workloads.bf16_bits_to_f32(c["L"]), workloads.bf16_bits_to_f32(c["U"]),
+            workloads.bf16_bits_to_f32(c["W"]))
+
+
+def _check_chain(c, requests=None, want_logq=True, w_boost=1.0):
+    L, U, W = _f32(c)
+    if w_boost != 1.0:
+        Wb = workloads.f32_to_bf16_bits(W * np.float32(w_boost))
+        c = dict(c, W=Wb)
+        L, U, W = _f32(c)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    print(f"chain R={c['R']} B={c['B']} V={c['V']} rank={c['rank']}", flush=True)
+    g = dsp.draft_markov_step(Lg, Ug, Wtg, ag, want_logq=want_logq)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    y = host(g["y"]).astype(np.int64)
+    sel = np.arange(c["R"]) if requests is None else np.asarray(requests)
+    orc = om.chain(L[sel], U, W, c["anchors"][sel], forced=y[sel])
+    ties = TieCounter()
+    ties.decisions += y[sel].size
+    mism = np.argwhere(orc["y"] != y[sel])
+    for ii, d in mism:
+        i = sel[ii]
+        prev = c["anchors"][i] if d == 0 else y[i, d - 1]
+        z = om.markov_logits(L[i, d][None], U, W, [prev])[0]
+        gap = z[orc["y"][ii, d]] - z[y[i, d]]
+        assert gap < ARGMAX_BAND * max(1.0, abs(z[orc["y"][ii, d]])), (i, d, gap)
+        ties.near += 1
+    ties.check()
+    if want_logq:
+        lq = host(g["logq"]).astype(np.float64)[sel]
+        np.testing.assert_allclose(lq, orc["logq_forced"], rtol=1e-5, atol=1e-5)
+    return y
+
+
+@pytest.mark.parametrize("R,B,V,rank", [(5, 4, 1000, 32), (130, 3, 4099, 64), (7, 5, 30000, 256),
+                                        (300, 2, 129, 96)])
+def test_chain_small(R, B, V, rank):
+    c = workloads.markov_case(R, B, V, rank=rank, seed=R + V)
+    _check_chain(c, w_boost=300.0)  # a Markov term large enough to change choices
+    _check_chain(c)
+
+
+def test_chain_of_course_fixture():
+    import json, os
+    gpath = os.path.join(os.path.dirname(__file__), "golden", "of_course_markov.json")
+    g = json.load(open(gpath))
+    V, r = g["vocab"], 32
+    L = np.array(g["L"], np.float32)[None]
+    U = np.zeros((V, r), np.float32)
+    U[:, :2] = np.array(g["U"], np.float32)
+    W = np.zeros((r, V), np.float32)
+    W[:2] = np.array(g["W"], np.float32)
+    c = dict(L=workloads.f32_to_bf16_bits(L), U=workloads.f32_to_bf16_bits(U), W=workloads.f32_to_bf16_bits(W),
+             anchors=np.array([g["tokens"]["anchor"]], np.int32), R=1, B=2, V=V, rank=r)
+    y = _check_chain(c)
+    inv = {v: k for k, v in g["tokens"].items()}
+    assert [inv[int(t)] for t in y[0]] == g["expected_with_markov"]
+
+
+def test_chain_c4_full():
+    """256 requests x 16 steps, V=151,936, rank 256; every request checked with replay."""
+    c = workloads.c4()
+    _check_chain(c, want_logq=True)
+
+
+def _check_tree(c, topk, F, N, requests=None, w_boost=1.0):
+    L, U, W = _f32(c)
+    if w_boost != 1.0:
+        c = dict(c, W=workloads.f32_to_bf16_bits(W * np.float32(w_boost)))
+        L, U, W = _f32(c)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    print(f"tree R={c['R']} D={c['B']} V={c['V']} k={topk} F={F} N={N}", flush=True)
+    g = dsp.tree_expand(Lg, Ug, Wtg, ag, topk, F, N)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    sel = list(range(c["R"])) if requests is None else list(requests)
+    o = opt.tree_expand(L, U, W, c["anchors"], topk, F, N, requests=sel)
+    ties = TieCounter()
+    gt, gp, gd, gs, gn = (host(g[k]) for k in ("node_token", "node_parent", "node_depth", "node_score", "n_nodes"))
+    for i in sel:
+        ties.decisions += int(o["n_nodes"][i]) * 2
+        same = (gn[i] == o["n_nodes"][i] and np.array_equal(gt[i], o["node_token"][i]) and
+                np.array_equal(gp[i], o["node_parent"][i]) and np.array_equal(gd[i], o["node_depth"][i]))
+        if not same:
+            assert o["min_gap"][i] < ARGMAX_BAND, (i, o["min_gap"][i])
+            ties.near += 1
+            continue
+        n = gn[i]
+        np.testing.assert_allclose(gs[i, :n], o["node_score"][i, :n], rtol=1e-5, atol=1e-5)
+    ties.check()
+    return g
+
+
+@pytest.mark.parametrize("R,D,V,k,F,N,rank", [(3, 4, 700, 2, 3, 8, 32), (9, 6, 5003, 4, 16, 64, 64),
+                                              (2, 3, 40000, 4, 16, 20, 256), (140, 2, 300, 3, 5, 7, 32)])
+def test_tree_small(R, D, V, k, F, N, rank):
+    c = workloads.markov_case(R, D, V, rank=rank, seed=7 * R + V)
+    _check_tree(c, k, F, N, w_boost=200.0)
+    _check_tree(c, k, F, N)
+
+
+def test_tree_k1_f1_is_chain():
+    c = workloads.markov_case(4, 5, 3000, rank=64, seed=99)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    t = dsp.tree_expand(Lg, Ug, Wtg, ag, 1, 1, 5)
+    ch = dsp.draft_markov_step(Lg, Ug, Wtg, ag)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(t["node_token"]), host(ch["y"]))
+    np.testing.assert_array_equal(host(t["node_parent"]), np.tile(np.arange(-1, 4), (4, 1)))
+
+
+def test_tree_c5_sampled_requests():
+    """128 requests, depth 16, V=129,280, k=4, F=16, N=64: 6 requests checked against the oracle."""
+    c = workloads.markov_case(128, 16, workloads.V_DSV4, 256, seed=1005)
+    g = _check_tree(c, 4, 16, 64, requests=[0, 1, 37, 64, 100, 127])
+    n = host(g["n_nodes"])
+    assert np.all(n == 64)
+
+
+def test_tree_verify_c5_shape_planted_paths():
+    """Tree verify on C5-shaped targets with a planted accepted path per request."""
+    c = workloads.markov_case(8, 16, workloads.V_DSV4, 256, seed=1005)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    t = dsp.tree_expand(Lg, Ug, Wtg, ag, 4, 16, 64)
+    torch.cuda.synchronize()
+    tok, par = host(t["node_token"]), host(t["node_parent"])
+    R, N, V = 8, 64, workloads.V_DSV4
+    tgt = workloads.tree_target(R, N + 1, V, seed=77)
+    tgt32 = workloads.bf16_bits_to_f32(tgt).copy()
+    rng = np.random.Generator(np.random.PCG64(5))
+    planted = []
+    for i in range(R):
+        depth = int(rng.integers(0, 8))
+        cur, n = -1, 0
+        while n < depth:
+            kids = np.flatnonzero(par[i] == cur)
+            if kids.size == 0:
+                break
+            j = int(kids[0])
+            tgt32[i, 1 + cur, tok[i, j]] = 50.0
+            cur = j
+            n += 1
+        planted.append(n)
+    tb = workloads.f32_to_bf16_bits(tgt32).reshape(R * (N + 1), V)
+    cu = (np.arange(R + 1) * (N + 1)).astype(np.int32)
+    g = dsp.verify_rejection(to_gpu_bf16(tb), to_gpu(cu), t["node_token"], parent=t["node_parent"], temperature=0.0)
+    torch.cuda.synchronize()
+    o = ov.verify_tree_greedy(workloads.bf16_bits_to_f32(tb), cu, tok, par)
+    np.testing.assert_array_equal(host(g["accepted_len"]), o["accepted_len"])
+    np.testing.assert_array_equal(host(g["out_tokens"]), o["out_tokens"])
+    assert np.all(o["accepted_len"] >= np.array(planted))

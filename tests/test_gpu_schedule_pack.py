@@ -1,0 +1,88 @@
+"""GPU parity of the confidence scheduler and the ragged pack (bit-exact against the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_verification_amd as dsp
+import workloads
+from oracle import pack as opack
+from oracle import schedule as osch
+from parity import host, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sched(conf, cost, mode=0, cap=-1):
+    print(f"schedule R={conf.shape[0]} K={conf.shape[1]} mode={mode} cap={cap}", flush=True)
+    g = dsp.schedule_windows(to_gpu(conf), to_gpu(cost), mode=mode, max_tokens=cap)
+    torch.cuda.synchronize()
+    o = osch.schedule_windows(conf, cost, mode=mode, max_tokens=cap)
+    np.testing.assert_array_equal(host(g["windows"]), o["windows"])
+    np.testing.assert_array_equal(host(g["survival"]), o["survival"])
+    st = host(g["stats"])
+    assert st[0] == o["N"] and st[1] == o["E"] and st[3] == o["Q"]
+    assert st[2] == o["J"]
+    return o
+
+
+@pytest.mark.parametrize("R,K", [(1, 1), (3, 2), (7, 16), (64, 7), (256, 16), (100, 33), (8192, 1), (64, 128)])
+def test_schedule_random(R, K):
+    rng = np.random.Generator(np.random.PCG64(R * 1000 + K))
+    conf = rng.uniform(0.0, 1.0, size=(R, K)).astype(np.float32)
+    conf[rng.random((R, K)) < 0.05] = 1.0
+    for a, b in [(1.0, 0.05), (1.0, 0.0), (0.3, 0.2)]:
+        cost = osch.additive_cost(a, b, R * K)
+        for mode in (osch.MODE_EARLY_STOP, osch.MODE_ARGMAX):
+            _sched(conf, cost, mode)
+    _sched(conf, osch.additive_cost(1.0, 0.01, R * K), 0, cap=max(1, R * K // 3))
+    # non-smooth measured table (random positive steps)
+    cost = np.cumsum(rng.uniform(0.0, 0.2, size=R * K + 1)) + 1.0
+    cost[rng.random(R * K + 1) < 0.1] += 0.5
+    _sched(conf, cost, 0)
+    _sched(conf, cost, 1)
+
+
+def test_schedule_special_cases():
+    R, K = 16, 8
+    cost = osch.additive_cost(1.0, 0.05, R * K)
+    o = _sched(np.ones((R, K), np.float32), cost)
+    assert np.all(o["windows"] == K)
+    o = _sched(np.zeros((R, K), np.float32), cost)
+    assert np.all(o["windows"] == 0)
+    o = _sched(np.zeros((R, K), np.float32), np.zeros(R * K + 1))
+    assert np.all(o["windows"] == 0)
+
+
+def test_schedule_c3_workload():
+    c = workloads.c3_schedule_inputs()
+    o = _sched(c["conf"], c["cost"])
+    print("C3 scheduled N =", o["N"], "of", 256 * 16)
+    assert 0 < o["N"] < 256 * 16
+
+
+@pytest.mark.parametrize("R,K", [(1, 1), (5, 3), (256, 16), (4000, 7)])
+def test_pack_random(R, K):
+    rng = np.random.Generator(np.random.PCG64(R + K))
+    w = rng.integers(0, K + 1, size=R).astype(np.int32)
+    anchors = rng.integers(0, 10**6, size=R).astype(np.int32)
+    drafts = rng.integers(0, 10**6, size=(R, K)).astype(np.int32)
+    tiers = sorted(set(rng.integers(R, R * (K + 1) + 2, size=8).tolist()))
+    print(f"pack R={R} K={K}", flush=True)
+    for tl in (None, tiers):
+        g = dsp.pack_ragged(to_gpu(w), to_gpu(anchors), to_gpu(drafts), tiers=tl)
+        torch.cuda.synchronize()
+        o = opack.pack_ragged(w, anchors, drafts, tiers=tl)
+        T = o["total"]
+        np.testing.assert_array_equal(host(g["cu_seqlens"]), o["cu_seqlens"])
+        np.testing.assert_array_equal(host(g["tokens"])[:T], o["tokens"])
+        np.testing.assert_array_equal(host(g["row_req"])[:T], o["row_req"])
+        np.testing.assert_array_equal(host(g["row_pos"])[:T], o["row_pos"])
+        assert host(g["total_and_tier"]).tolist() == [T, o["tier"]]
+        assert int(host(g["status"])[0]) == 0
+
+
+def test_pack_flags_bad_window():
+    w = np.array([2, 9, 1], np.int32)
+    g = dsp.pack_ragged(to_gpu(w), to_gpu(np.zeros(3, np.int32)), to_gpu(np.zeros((3, 4), np.int32)))
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) & dsp.DSP_STATUS_WINDOW_RANGE

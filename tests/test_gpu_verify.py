@@ -1,0 +1,220 @@
+"""GPU parity of the batched ragged verify (C ABI dsp_verify_rejection) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_verification_amd as dsp
+import workloads
+from oracle import philox as ophilox
+from oracle import verify as ov
+from parity import (TieCounter, compare_chain_verify, cu_from_windows, dev, host, logits_to_gpu,
+                    packed_from_dense, to_gpu, values)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_case(case, windows, temperature, seed=0, rnd=0, req_id=None, ld_pad=0, want_probs=True):
+    R, K, V, dt = case["R"], case["K"], case["V"], case["dtype"]
+    tp = packed_from_dense(case["t"], windows)
+    if ld_pad:
+        tp = np.concatenate([tp, np.zeros((tp.shape[0], ld_pad), dtype=tp.dtype)], axis=1)
+    cu = cu_from_windows(windows)
+    tg = logits_to_gpu(tp, dt)[:, :V]
+    dg = logits_to_gpu(case["d"], dt)
+    xg = to_gpu(case["x"].astype(np.int32))
+    rid = None if req_id is None else to_gpu(np.asarray(req_id, dtype=np.int64))
+    print(f"verify case R={R} K={K} V={V} dtype={dt} T={temperature} ld={tg.stride(0)}", flush=True)
+    g = dsp.verify_rejection(tg, to_gpu(cu), xg, drf=dg, temperature=temperature, seed=seed, round=rnd,
+                             req_id=rid, want_probs=want_probs)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    tv = values(tp[:, :V], dt).astype(np.float64)
+    dv = values(case["d"], dt).astype(np.float64)
+
+    def orc(forced):
+        return ov.verify_chain(tv, cu, dv, case["x"], temperature, seed=seed, rnd=rnd, req_id=req_id,
+                               forced_len=forced)
+    return g, orc
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1024, 4099, 40000])
+def test_sampled_small(dt, V):
+    R, K = 6, 5
+    case = workloads.verify_case(R, K, V, dtype=dt, seed=V + (dt == "bf16"), t_sigma=2.0, d_sigma=0.4)
+    windows = np.array([5, 0, 3, 5, 1, 4])
+    ties = TieCounter()
+    for T in (1.0, 0.7):
+        g, orc = _run_case(case, windows, T, seed=11, rnd=2)
+        compare_chain_verify(g, orc, R, K, windows, ties)
+    ties.check()
+
+
+def test_tiny_verify_c1():
+    """4 requests, K=7, V=1024, fp32, Philox seed 0, full windows and a scheduled run."""
+    c = workloads.c1()
+    ties = TieCounter()
+    g, orc = _run_case(c, np.full(4, 7), 1.0, seed=0)
+    compare_chain_verify(g, orc, 4, 7, np.full(4, 7), ties)
+    sch = dsp.schedule_windows(to_gpu(c["conf"]), to_gpu(c["cost"]))
+    w = host(sch["windows"])
+    g, orc = _run_case(c, w, 1.0, seed=0)
+    compare_chain_verify(g, orc, 4, 7, w, ties)
+    ties.check()
+
+
+def test_unaligned_rows_and_request_ids():
+    R, K, V = 5, 4, 3001
+    case = workloads.verify_case(R, K, V, dtype="bf16", seed=5, t_sigma=2.0, d_sigma=0.3)
+    windows = np.array([4, 2, 0, 4, 3])
+    ties = TieCounter()
+    g, orc = _run_case(case, windows, 1.0, seed=3, rnd=9, req_id=[100, 7, 55, 2**40, 3], ld_pad=3)
+    compare_chain_verify(g, orc, R, K, windows, ties)
+    ties.check()
+
+
+def test_identical_rows_accept_everything():
+    R, K, V = 8, 7, 20000
+    case = workloads.verify_case(R, K, V, dtype="bf16", seed=8, t_sigma=3.0, d_sigma=0.0)
+    assert np.array_equal(case["d"], case["t"][:, :K])
+    g, orc = _run_case(case, np.full(R, K), 1.0, seed=4)
+    np.testing.assert_array_equal(host(g["accepted_len"]), K)
+    np.testing.assert_array_equal(host(g["out_tokens"])[:, :K], case["x"])
+    ties = TieCounter()
+    compare_chain_verify(g, orc, R, K, np.full(R, K), ties)
+    assert ties.near == 0
+
+
+def test_greedy_matches_argmax_prefix():
+    R, K, V = 12, 6, 30011
+    rng = np.random.Generator(np.random.PCG64(3))
+    case = workloads.verify_case(R, K, V, dtype="bf16", seed=21, t_sigma=3.0, d_sigma=0.5, temperature=0.0)
+    tv = values(case["t"], "bf16")
+    am = np.argmax(tv, axis=-1)
+    lead = rng.integers(0, K + 1, size=R)
+    x = case["x"].copy()
+    for i in range(R):
+        x[i, :lead[i]] = am[i, :lead[i]]
+        if lead[i] < K and x[i, lead[i]] == am[i, lead[i]]:
+            x[i, lead[i]] = (x[i, lead[i]] + 1) % V
+    case["x"] = x
+    windows = np.array([6, 6, 0, 3, 6, 2, 6, 6, 1, 6, 5, 6])
+    tp = packed_from_dense(case["t"], windows)
+    cu = cu_from_windows(windows)
+    g = dsp.verify_rejection(logits_to_gpu(tp, "bf16"), to_gpu(cu), to_gpu(x.astype(np.int32)), temperature=0.0)
+    torch.cuda.synchronize()
+    o = ov.verify_chain(values(tp, "bf16"), cu, None, x, 0.0)
+    np.testing.assert_array_equal(host(g["accepted_len"]), o["accepted_len"])
+    np.testing.assert_array_equal(host(g["out_tokens"]), o["out_tokens"])
+    np.testing.assert_array_equal(host(g["accepted_len"]), np.minimum(lead, windows))
+
+
+def test_greedy_ties_lowest_token_and_signed_zero():
+    V = 9000
+    t = np.full((1, 2, V), -5.0, dtype=np.float32)
+    t[0, 0, [4000, 17, 8999]] = 3.0
+    t[0, 1, :] = -0.0
+    t[0, 1, 5] = 0.0
+    tb = workloads.f32_to_bf16_bits(t)
+    g = dsp.verify_rejection(to_gpu_bf16_rows(tb[0]), to_gpu(np.array([0, 2], np.int32)),
+                             to_gpu(np.array([[17]], np.int32)), temperature=0.0)
+    torch.cuda.synchronize()
+    assert host(g["accepted_len"])[0] == 1
+    assert host(g["out_tokens"])[0].tolist() == [17, 0]
+
+
+def to_gpu_bf16_rows(bits):
+    from parity import to_gpu_bf16
+    return to_gpu_bf16(bits)
+
+
+def test_tree_walk_matches_oracle():
+    rng = np.random.Generator(np.random.PCG64(31))
+    R, N, V = 6, 20, 5003
+    tok = np.zeros((R, N), np.int32)
+    par = np.zeros((R, N), np.int32)
+    rows = []
+    nn = rng.integers(1, N + 1, size=R)
+    for i in range(R):
+        for j in range(N):
+            par[i, j] = -1 if j < 3 else rng.integers(-1, j)
+        # distinct sibling tokens
+        for j in range(N):
+            tok[i, j] = rng.integers(0, V)
+        r = rng.standard_normal((nn[i] + 1, V)).astype(np.float32) * 3
+        # plant a path root -> ... following argmax
+        cur = -1
+        for _ in range(4):
+            kids = [j for j in range(nn[i]) if par[i, j] == cur]
+            if not kids:
+                break
+            j = kids[rng.integers(0, len(kids))]
+            sib = [s for s in range(nn[i]) if par[i, s] == cur and s != j]
+            while tok[i, j] in tok[i, sib]:
+                tok[i, j] = (tok[i, j] + 1) % V
+            r[1 + cur, tok[i, j]] = 20.0
+            cur = j
+        rows.append(workloads.f32_to_bf16_bits(r))
+    tp = np.concatenate(rows)
+    cu = np.concatenate([[0], np.cumsum(nn + 1)]).astype(np.int32)
+    from parity import to_gpu_bf16
+    g = dsp.verify_rejection(to_gpu_bf16(tp), to_gpu(cu), to_gpu(tok), parent=to_gpu(par), temperature=0.0)
+    torch.cuda.synchronize()
+    o = ov.verify_tree_greedy(values(tp, "bf16"), cu, tok, par)
+    np.testing.assert_array_equal(host(g["accepted_len"]), o["accepted_len"])
+    np.testing.assert_array_equal(host(g["out_tokens"]), o["out_tokens"])
+    np.testing.assert_array_equal(host(g["stop_pos"]), o["stop_node"])
+    assert np.all(o["accepted_len"] >= 1)
+
+
+def test_fault_bits_from_bad_tokens_and_windows():
+    R, K, V = 3, 4, 2048
+    case = workloads.verify_case(R, K, V, dtype="bf16", seed=41)
+    x = case["x"].copy()
+    x[1, 2] = V + 5
+    windows = np.full(R, K)
+    tp = packed_from_dense(case["t"], windows)
+    g = dsp.verify_rejection(logits_to_gpu(tp, "bf16"), to_gpu(cu_from_windows(windows)), to_gpu(x),
+                             drf=logits_to_gpu(case["d"], "bf16"), temperature=1.0)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) & dsp.DSP_STATUS_TOKEN_RANGE
+    acc = host(g["accepted_len"])
+    assert acc[1] == -1 and acc[0] >= 0 and acc[2] >= 0
+    # a window larger than K
+    cu = np.array([0, 5, 10, 16], np.int32)  # last request claims 5 drafts with K = 4
+    g = dsp.verify_rejection(logits_to_gpu(tp, "bf16"), to_gpu(cu), to_gpu(case["x"]),
+                             drf=logits_to_gpu(case["d"], "bf16"), temperature=1.0)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) & dsp.DSP_STATUS_WINDOW_RANGE
+    assert host(g["accepted_len"])[2] == -1
+
+
+def test_max_window_64():
+    R, K, V = 3, 64, 3000
+    case = workloads.verify_case(R, K, V, dtype="bf16", seed=51, t_sigma=1.0, d_sigma=0.05)
+    windows = np.array([64, 63, 10])
+    ties = TieCounter()
+    g, orc = _run_case(case, windows, 1.0, seed=1)
+    compare_chain_verify(g, orc, R, K, windows, ties)
+    ties.check()
+
+
+def test_dense_vocab_verify_c2_full():
+    """64 requests x K=7 x V=151,936 bf16, full-block windows, T=1: every request checked."""
+    c = workloads.c2()
+    R, K = c["R"], c["K"]
+    ties = TieCounter()
+    g, orc = _run_case(c, np.full(R, K), 1.0, seed=0)
+    compare_chain_verify(g, orc, R, K, np.full(R, K), ties)
+    ties.check()
+    acc = host(g["accepted_len"])
+    print("C2 mean accepted", acc.mean(), "near ties", ties.near, "of", ties.decisions)
+
+
+def test_philox_uniforms_bitwise():
+    rng = np.random.Generator(np.random.PCG64(77))
+    ctr = rng.integers(0, 2**63, size=(5000, 4), dtype=np.uint64)
+    ctr[:100] = np.stack([np.full(100, 3), np.arange(100), np.arange(1, 101), np.zeros(100)], axis=1)
+    ref = np.stack([ophilox.to_unit_double(w) for w in ophilox.philox4x64_10(ctr, np.array([9, 0], np.uint64)).T], axis=1)
+    got = host(dsp.philox_uniforms(to_gpu(ctr.view(np.int64)), 9))
+    np.testing.assert_array_equal(got, ref)

@@ -132,18 +132,24 @@ def c2(sigma=None):
     return c
 
 
-def c3(R=256, K=16, V=V_QWEN3):
-    """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table."""
+def c3_schedule_inputs(R=256, K=16, V=V_QWEN3):
+    """Confidences, cost table and per-request noise scales of C3 (no logits)."""
     rng = _rng(2003)
     sig = rng.uniform(0.2, 2.0, size=R).astype(np.float32)
-    c = verify_case(R, K, V, dtype="bf16", seed=1003, t_sigma=3.0, boost_p=0.01, boost=8.0,
-                    d_sigma=sig)
     eta = rng.standard_normal((R, K))
     z = 4.0 - 2.5 * sig[:, None].astype(np.float64) + 0.25 * eta
-    c["conf"] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
-    c["anchors"] = _rng(3003).integers(0, V, size=R).astype(np.int32)
-    c["cost"] = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
-    c["sigma_i"] = sig
+    conf = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    cost = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
+    return dict(conf=conf, cost=cost, sigma_i=sig,
+                anchors=_rng(3003).integers(0, V, size=R).astype(np.int32))
+
+
+def c3(R=256, K=16, V=V_QWEN3):
+    """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table."""
+    s = c3_schedule_inputs(R, K, V)
+    c = verify_case(R, K, V, dtype="bf16", seed=1003, t_sigma=3.0, boost_p=0.01, boost=8.0,
+                    d_sigma=s["sigma_i"])
+    c.update(s)
     return c
 
 
