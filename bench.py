@@ -168,7 +168,8 @@ def bench_verify(args, which):
         sch = dsp.schedule_windows(conf, cost, want_survival=False, stream=stream, prepare=True)
         pk = dsp.pack_ragged(sch.outputs["windows"], anchors, x, stream=stream, prepare=True)
         ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=0,
-                                   round_dev=rnd, max_rows=max_rows, stream=stream, prepare=True)
+                                   round_dev=rnd, max_rows=max_rows, row_req=pk.outputs["row_req"],
+                                   row_pos=pk.outputs["row_pos"], stream=stream, prepare=True)
         ops.update(sch=sch, pk=pk, ver=ver)
 
         def step():  # the verify call advances the device-side Philox round itself

@@ -175,15 +175,19 @@ def pack_ragged(windows, anchors, drafts, tiers=None, out=None, status=None, str
 
 def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,
                      round=0, req_id=None, max_rows=0, want_probs=True, out=None, status=None,
-                     stream=None, round_dev=None, prepare=False):
+                     stream=None, round_dev=None, row_req=None, row_pos=None, prepare=False):
     """Batched ragged verify.
 
     tgt: packed target logits [T_rows, V] (bf16/fp32, unit inner stride);
     cu_seqlens: int32 [R+1]; draft_tok: int32 [R, K]; drf: draft logits [R, K, V]
     (T > 0); parent: int32 [R, K] selects the greedy tree walk (T must be 0).
+    row_req/row_pos: the pack's packed-row maps (optional; locate draft rows directly).
     Returns dict(accepted_len, out_tokens [R, K+1], stop_pos, p_x, q_x, status).
     """
-    _on_gpu(tgt, cu_seqlens, draft_tok, drf, parent, req_id, round_dev)
+    _on_gpu(tgt, cu_seqlens, draft_tok, drf, parent, req_id, round_dev, row_req, row_pos)
+    if row_req is not None or row_pos is not None:
+        _need(row_req is not None and row_pos is not None and row_req.dtype == torch.int32 and
+              row_pos.dtype == torch.int32, "row_req and row_pos: int32, together")
     if round_dev is not None:
         _need(round_dev.dtype == torch.int64 and round_dev.numel() == 1, "round_dev: one int64 on the GPU")
     _need(tgt.dim() == 2 and tgt.stride(1) == 1, "tgt: [rows, V] with unit inner stride")
@@ -223,11 +227,11 @@ def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperat
     ws = _workspace(nbytes, dev, prepare)
     args = (_ptr(tgt), t_dt, tgt.stride(0), _ptr(cu_seqlens), _ptr(drf), d_dt, ld_dr, ld_dk,
             _ptr(draft_tok), draft_tok.stride(0), _ptr(parent), R, K, V, max_rows, float(temperature),
-            int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x),
+            int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(row_req), _ptr(row_pos), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x),
             _ptr(q_x), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     res = dict(accepted_len=acc, out_tokens=toks, stop_pos=stop, p_x=p_x, q_x=q_x, status=status)
     return _finish(lib().dsp_verify_rejection, args, res, prepare,
-                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, ws))
+                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, ws))
 
 
 def _check_markov(L, U, Wt):

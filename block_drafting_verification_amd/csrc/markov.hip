@@ -16,9 +16,10 @@
 // parent rows without any cross-lane traffic per tile; lanes, waves and column
 // groups are merged once at the end.
 //
-// Workgroup (256 threads, 4 waves as 2 x 2): one block of 128 parent rows and a
-// strided set of 128-token vocabulary tiles (tile g, g+G, ...). The gathered
-// U rows of its parents (128 x rank bf16) stay in LDS for all tiles; Wt is
+// Workgroup (512 threads, 8 waves as 2 vocab x 4 rows): one block of 256 parent
+// rows and a strided set of 128-token vocabulary tiles (tile g, g+G, ...), so a
+// Markov step over up to 256 requests streams Wt exactly once. The gathered
+// U rows of its parents (256 x rank bf16) stay in LDS for all tiles; Wt is
 // streamed through two 128 x 32 LDS chunks (double buffered). LDS rows are
 // XOR-swizzled at 16-byte granularity so the 32 rows read by one MFMA fragment
 // load hit distinct banks. Partial results per (column group, row) go to the
@@ -33,12 +34,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTV = 128;  // vocabulary entries per tile
-constexpr int kTR = 128;  // parent rows per workgroup
+constexpr int kWR = 4;            // wavefronts along the parent-row axis
+constexpr int kTR = 64 * kWR;     // parent rows per workgroup (256)
+constexpr int kGT = 128 * kWR;    // threads per workgroup: 2 (vocab) x kWR (rows) wavefronts
 constexpr int kKC = 32;   // rank chunk staged per step
 constexpr int kTopK = 4;  // children tracked per parent
-constexpr int kTargetWGs = 512;
+constexpr int kTargetWGs = 256;  // one 512-thread workgroup per CU
 
 enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2 };
 
@@ -115,7 +119,7 @@ __device__ __forceinline__ void merge_top4(float* va, int* ia, const float* vb, 
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave & 1, wr = wave >> 1;
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   // gather U rows of this block's parents
-  for (int e = tid; e < kTR * nvu; e += 256) {
+  for (int e = tid; e < kTR * nvu; e += kGT) {
     const int rr = e / nvu, kv = e % nvu;
     const int r = r0 + rr;
     u32x4 val = zero4;
@@ -175,13 +179,14 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) l_al[j] = (((uintptr_t)Lrow[j]) & 7u) == 0;
 
-  // Wt chunk of step st: 128 tokens x 32 rank values, two 16-byte vectors per thread
+  // Wt chunk of step st: 128 tokens x 32 rank values = 512 16-byte vectors over the workgroup
+  constexpr int kWQ = (kTV * 4) / kGT;  // vectors per thread (1)
   auto load_w = [&](int st, u32x4* r) {
     const int t = st / nkc, kc = st - t * nkc;
     const int v0 = (g + t * a.G) * kTV;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid + q * 256;
+    for (int q = 0; q < kWQ; ++q) {
+      const int e = tid + q * kGT;
       const int vv = e >> 2, kv = e & 3;
       const int v = v0 + vv;
       r[q] = v < a.V ? *(const u32x4*)(a.Wt + (size_t)v * a.rank + kc * kKC + kv * 8) : zero4;
@@ -189,8 +194,8 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
   };
   auto store_w = [&](int buf, const u32x4* r) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid + q * 256;
+    for (int q = 0; q < kWQ; ++q) {
+      const int e = tid + q * kGT;
       const int vv = e >> 2, kv = e & 3;
       Ws[buf * kTV * 4 + vv * 4 + (kv ^ ((vv >> 1) & 3))] = r[q];
     }
@@ -209,7 +214,10 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
           uint2 w = {0u, 0u};
           if (rvalid[j]) {
             if (full && l_al[j]) {
-              w = *(const uint2*)(Lrow[j] + v);
+              // L is read once per call: non-temporal, so the Wt lines re-read every step keep the cache
+              const u32x2 nt = __builtin_nontemporal_load((const u32x2*)(Lrow[j] + v));
+              w.x = nt.x;
+              w.y = nt.y;
             } else {
               uint32_t e[4];
 #pragma unroll
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
   };
 
   constexpr int kRing = MODE == MODE_ARGMAX ? 4 : 2;  // Wt chunks in flight per thread
-  u32x4 wring[kRing][2];
+  u32x4 wring[kRing][kWQ];
 #pragma unroll
   for (int p = 0; p < kRing; ++p)
     if (p < nsteps) load_w(p, wring[p]);
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
             const float zz = acc[i][j][4 * h + l] + ((l & 1) ? bf16_hi(w) : bf16_lo(w));
             ts += v < a.V ? fast_exp2(__builtin_fmaf(zz, kLog2e, -nref)) : 0.f;
           }
-          const double scale = lref[j] == -INFINITY ? 0.0 : exp2((double)lref[j] - (double)nref);
+          const double scale = lref[j] == -INFINITY ? 0.0 : (double)fast_exp2(lref[j] - nref);
           lsum[j] = lsum[j] * scale + (double)ts;
           lref[j] = nref;
         }
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void markov_gemm_kernel(GemmArgs a) {
   // merge the two vocabulary waves (wv = 0, 1) through LDS, then write partials
   __syncthreads();
   if (MODE == MODE_TREE) {
-    TreePart* xs = (TreePart*)lds;  // [2 (wr)][64 rows]
+    TreePart* xs = (TreePart*)lds;  // [kWR (wr)][64 rows]
     if (wv == 1 && lane < 32) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -651,6 +659,7 @@ __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
 }
 
 size_t gemm_lds_bytes(int rank) { return (size_t)(kTR * (rank / 8) + 2 * kTV * 4) * 16; }
+static_assert((kTV * 4) % kGT == 0, "Wt chunk must split evenly over the workgroup");
 
 int pick_groups(int rows, int V) {
   const int nrb = (rows + kTR - 1) / kTR;
@@ -671,7 +680,7 @@ int32_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     attr_set = true;
   }
   dim3 grid(a.G, (a.rows + kTR - 1) / kTR);
-  hipLaunchKernelGGL(markov_gemm_kernel<MODE>, grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL(markov_gemm_kernel<MODE>, grid, dim3(kGT), lds, s, a);
   return hip_check(hipGetLastError(), "markov gemm launch");
 }
 

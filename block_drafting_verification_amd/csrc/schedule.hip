@@ -10,7 +10,8 @@
 //     a 2^-Q grid and packed into a unique 64-bit key
 //     ((2^41-1-Sq) << 23 | i << 7 | k-1) so ascending key order is
 //     (S desc, i asc, k asc) and any correct sort gives the same order;
-//   - bitonic sort in LDS; exact uint64 prefix sums of Sq;
+//   - bitonic sort (registers / wave shuffles / LDS by stride); exact uint64
+//     prefix sums of Sq;
 //   - the throughput test per candidate as two separate fp64 products
 //     (E_j * c[j-1] > E_{j-1} * c[j]) and a block minimum for the first failure;
 //   - window of request i = how many of its keys precede the first rejected key
@@ -61,6 +62,67 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* wsum) {
   return wsum[w] + inc - v;
 }
 
+// Ascending bitonic sort of keys[0..P) (P a power of two, P <= 1024 * E) by a
+// 1024-thread block holding E consecutive keys per thread: strides below E are
+// swapped in registers, strides below 64*E through wave shuffles, and only the
+// wider strides through LDS, so most of the log2(P)(log2(P)+1)/2 stages need no barrier.
+template <int E>
+__device__ void bitonic_keys(uint64_t* keys, int P) {
+  const int tid = threadIdx.x;
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = tid * E + e;
+    v[e] = idx < P ? keys[idx] : ~0ull;
+  }
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int ep = e ^ stride;
+          if (ep > e) {
+            const bool up = ((tid * E + e) & size) == 0;
+            const uint64_t a = v[e], b = v[ep];
+            if ((a > b) == up) {
+              v[e] = b;
+              v[ep] = a;
+            }
+          }
+        }
+        continue;
+      }
+      const int ts = stride / E;  // distance in threads
+      uint64_t o[E];
+      if (ts < 64) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = __shfl_xor(v[e], ts, 64);
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) keys[tid * E + e] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = keys[(tid ^ ts) * E + e];
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int idx = tid * E + e;
+        const bool up = (idx & size) == 0;
+        const bool low = (idx & stride) == 0;
+        v[e] = (low == up) ? (o[e] < v[e] ? o[e] : v[e]) : (o[e] > v[e] ? o[e] : v[e]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = tid * E + e;
+    if (idx < P) keys[idx] = v[e];
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     const float* __restrict__ conf, int R, int K, const double* __restrict__ cost, int mode, int M,
     int Q, int32_t* __restrict__ windows, double* __restrict__ survival, double* __restrict__ stats) {
@@ -91,21 +153,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   __syncthreads();
 
   // bitonic sort, ascending
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < P / 2; t += kSchedThreads) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t a = keys[lo], b = keys[hi];
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
+  if (P <= 1024) bitonic_keys<1>(keys, P);
+  else if (P == 2048) bitonic_keys<2>(keys, P);
+  else if (P == 4096) bitonic_keys<4>(keys, P);
+  else bitonic_keys<8>(keys, P);
 
   // exact prefix sums over the first M sorted candidates; thread t owns [t*C, t*C + C)
   const int C = (M + kSchedThreads - 1) / kSchedThreads;

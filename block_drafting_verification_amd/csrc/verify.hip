@@ -36,10 +36,15 @@
 namespace dsp {
 namespace {
 
+#ifndef DSP_STATS_VPT
+#define DSP_STATS_VPT 8
+#endif
+#ifndef DSP_STATS_WG_PER_CU
+#define DSP_STATS_WG_PER_CU 0  // persistent grid: workgroups per CU (0: one item per workgroup)
+#endif
 constexpr int kThreads = 256;
-constexpr int kVpt = 8;                      // 16-byte vectors per thread per chunk
-constexpr int kChunkVecs = kThreads * kVpt;  // 2048 vectors = 32 KiB per chunk
-constexpr int kCuLds = 2048;                 // cu_seqlens entries staged in LDS
+constexpr int kVpt = DSP_STATS_VPT;          // 16-byte vectors per thread per chunk
+constexpr int kChunkVecs = kThreads * kVpt;  // vectors per chunk (2048 = 32 KiB of bf16)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -236,6 +241,8 @@ struct StatsArgs {
   StatSlot* tstats;
   StatSlot* dstats;
   uint64_t* round_dev;  // sampled path: advanced once per call here, read by the decisions
+  const int32_t* row_req;  // optional packed-row maps (request, position) from the ragged pack
+  const int32_t* row_pos;
 };
 
 template <typename TT>
@@ -254,15 +261,41 @@ __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(StatsArgs a) {
 
 // log2-sum-exp2 of a row from its chunk slots (fp64). Sets *bad for non-finite rows.
 __device__ __forceinline__ double merge_lse(const StatSlot* s, int nch, bool* bad) {
+  // slots are read 16 at a time, all loads issued before any is used (one memory
+  // latency per batch instead of one per chunk), then merged online in fp64
+  constexpr int B = 16;
   float H = -INFINITY;
-  bool f = false;
-  for (int c = 0; c < nch; ++c) {
-    H = fmaxf(H, s[c].ref);
-    f |= s[c].flag != 0;
-  }
   double S = 0.0;
-  for (int c = 0; c < nch; ++c)
-    if (s[c].ref != -INFINITY) S += s[c].sum * exp2((double)s[c].ref - (double)H);
+  bool f = false;
+  for (int c0 = 0; c0 < nch; c0 += B) {
+    float ref[B];
+    double sum[B];
+    uint32_t flag[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      ref[q] = -INFINITY;
+      sum[q] = 0.0;
+      flag[q] = 0u;
+      if (c0 + q < nch) {
+        ref[q] = s[c0 + q].ref;
+        flag[q] = s[c0 + q].flag;
+        sum[q] = s[c0 + q].sum;
+      }
+    }
+    float Hb = H;
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      Hb = fmaxf(Hb, ref[q]);
+      f |= flag[q] != 0u;
+    }
+    // chunk factors 2^(ref - max) <= 1 in fp32 (one v_exp_f32 each), products and sums in fp64
+    double Sb = H == -INFINITY ? 0.0 : S * (double)fast_exp2(H - Hb);
+#pragma unroll
+    for (int q = 0; q < B; ++q)
+      if (ref[q] != -INFINITY) Sb += sum[q] * (double)fast_exp2(ref[q] - Hb);
+    H = Hb;
+    S = Sb;
+  }
   const double L = (double)H + log2(S);
   if (f || !(L == L) || L == INFINITY || L == -INFINITY) *bad = true;
   return L;
@@ -270,8 +303,15 @@ __device__ __forceinline__ double merge_lse(const StatSlot* s, int nch, bool* ba
 
 __device__ __forceinline__ uint32_t merge_argmax(const StatSlot* s, int nch) {
   const uint64_t* k = (const uint64_t*)s;
+  constexpr int B = 16;
   uint64_t b = 0;
-  for (int c = 0; c < nch; ++c) b = k[2 * c] > b ? k[2 * c] : b;
+  for (int c0 = 0; c0 < nch; c0 += B) {
+    uint64_t v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) v[q] = c0 + q < nch ? k[2 * (c0 + q)] : 0ull;
+#pragma unroll
+    for (int q = 0; q < B; ++q) b = v[q] > b ? v[q] : b;
+  }
   return amax_index(b);
 }
 
@@ -433,30 +473,66 @@ __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
   }
 }
 
-// Statistics pass (T > 0): every packed target row and every windowed draft row.
+// Request owning packed row p: largest i with cu[i] <= p (cu ascending).
+__device__ __forceinline__ int find_request(const int32_t* cu, int R, int p) {
+  int lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int kCuLds = 2048;  // requests whose offsets are staged in LDS for the row search
+
+// Statistics pass (T > 0): every packed target row, and the draft row of every packed
+// row that is not an anchor (so windows shorter than K cost no work). One workgroup
+// item is one (row, chunk): target items first, then draft items in packed-row order.
+// A draft item finds its (request, position) in the pack's row maps when the caller
+// passes them, else by a binary search of cu_seqlens staged in LDS.
 template <typename TT, typename TD>
 __global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a) {
   __shared__ float smf[kThreads / 64];
   __shared__ double smd[kThreads / 64];
+  __shared__ int32_t s_cu[kCuLds + 1];
   if (a.round_dev && blockIdx.x == 0 && threadIdx.x == 0) *a.round_dev += 1;
   const int tot = a.cu[a.R];
   const int T_rows = tot < 0 ? 0 : (tot > a.max_rows ? a.max_rows : tot);
   const long items_t = (long)T_rows * a.ncht;
-  const long items = items_t + (long)a.R * a.K * a.nchd;
+  const long items = items_t + (long)T_rows * a.nchd;
+  bool staged = false;
   for (long it = blockIdx.x; it < items; it += gridDim.x) {
     if (it < items_t) {
       const int row = (int)(it / a.ncht), c = (int)(it % a.ncht);
       const TT* p = (const TT*)a.tgt + (size_t)row * a.ld_t;
       chunk_stats<TT>(p, a.V, a.ncht, c, a.cl, a.tstats + it, smf, smd);
-    } else {
-      const long j = it - items_t;
-      const int rk = (int)(j / a.nchd), c = (int)(j % a.nchd);
-      const int i = rk / a.K, k0 = rk % a.K;
-      const int n = a.cu[i + 1] - a.cu[i] - 1;
-      if (k0 >= n) continue;  // uniform over the workgroup
-      const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
-      chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + j, smf, smd);
+      continue;
     }
+    const long j = it - items_t;
+    const int row = (int)(j / a.nchd), c = (int)(j % a.nchd);
+    int i = -1, k0 = -1;
+    if (a.row_req) {
+      i = a.row_req[row];
+      k0 = a.row_pos[row] - 1;
+      if (i < 0 || i >= a.R || a.cu[i] + k0 + 1 != row) {  // maps disagree with cu_seqlens: search
+        i = find_request(a.cu, a.R, row);
+        k0 = row - a.cu[i] - 1;
+      }
+    } else {
+      const bool cu_lds = a.R <= kCuLds;
+      if (cu_lds && !staged) {
+        for (int q = threadIdx.x; q <= a.R; q += kThreads) s_cu[q] = a.cu[q];
+        __syncthreads();
+        staged = true;
+      }
+      const int32_t* cu = cu_lds ? s_cu : a.cu;
+      i = find_request(cu, a.R, row);
+      k0 = row - cu[i] - 1;  // draft position - 1 (-1: the anchor row)
+    }
+    if (k0 < 0 || k0 >= a.K) continue;  // uniform over the workgroup
+    const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
+    chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + c, smf, smd);
   }
 }
 
@@ -583,11 +659,6 @@ template <typename T> __device__ __forceinline__ void load8(const T* p, bool vec
 }
 
 
-constexpr int kSampleThreads = 1024;
-constexpr int kSampleMaxChunks = 32;
-constexpr int kSampleVec = kSampleThreads * 8;  // elements covered by one 8-wide step of the workgroup
-
-// Weights of 8 consecutive elements starting at e (16-byte loads when aligned, guarded tail).
 // Eight consecutive logits as raw 16-byte vectors (one for bf16, two for fp32).
 template <typename T> struct Raw8 {
   u32x4 w[sizeof(T) / 2];
@@ -601,6 +672,26 @@ template <typename T> struct Raw8 {
   }
 };
 
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleGrain = kSampleThreads * 8;  // chunk granularity: one 8-element vector per sample thread
+
+// Residual / bonus chunking: R * nch2 items of ce elements (ce a multiple of kSampleGrain).
+struct SampleGeom {
+  int nch2, ce;
+};
+__host__ __device__ inline SampleGeom sample_geom(int R, int V) {
+  int n = (2048 + R - 1) / R;
+  if (n > 64) n = 64;
+  if (n < 1) n = 1;
+  int ce = (V + n - 1) / n;
+  ce = (ce + kSampleGrain - 1) / kSampleGrain * kSampleGrain;
+  SampleGeom g;
+  g.ce = ce;
+  g.nch2 = (V + ce - 1) / ce;
+  return g;
+}
+
+// Weights of 8 consecutive elements starting at e (16-byte loads when aligned, guarded tail).
 template <typename TT, typename TD>
 __device__ __forceinline__ float job_weight8(const JobFrame& f, const TT* tp, const TD* dp, bool t_al, bool d_al,
                                              int e, int V) {
@@ -618,110 +709,137 @@ __device__ __forceinline__ float job_weight8(const JobFrame& f, const TT* tp, co
   return w;
 }
 
-// K2: one workgroup per request. Wavefront 0 takes the accept/reject decisions;
-// then the whole workgroup draws the corrected or bonus token by inverse CDF:
-// pass 1 sums the weights of up to 32 contiguous chunks (fp64), pass 2 rescans
-// the chunk holding u' * total with one 8-element range per thread and an fp64
-// exclusive scan, and the owning thread walks its range to the first element
-// whose cumulative weight exceeds the target.
+// Sum of the job's weights over [e0, e0 + len) with 256 threads x 8 elements per step;
+// up to kBatch steps of loads are issued before any is used.
 template <typename TT, typename TD>
-__global__ __launch_bounds__(kSampleThreads) void verify_decide_sample_kernel(DecideArgs a) {
-  __shared__ Job s_job;
-  __shared__ double s_part[kSampleThreads / 64][kSampleMaxChunks];
-  __shared__ double s_csum[kSampleMaxChunks];
+__device__ __forceinline__ double job_chunk_sum(const JobFrame& f, const TT* tp, const TD* dp, int e0, int len,
+                                                int V) {
+  constexpr int kBatch = (sizeof(TT) == 2 && sizeof(TD) == 2) ? 4 : 2;
+  const bool t_al = (((uintptr_t)tp) & 15u) == 0;
+  const bool d_al = !f.resid || (((uintptr_t)dp) & 15u) == 0;
+  const int e1 = min(V, e0 + len);
+  double s = 0.0;
+  for (int eb = e0 + threadIdx.x * 8; eb < e1; eb += kBatch * kThreads * 8) {
+    Raw8<TT> rt[kBatch];
+    Raw8<TD> rd[kBatch];
+    bool fast[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = eb + b * kThreads * 8;
+      fast[b] = e + 8 <= e1 && t_al && d_al;
+      if (fast[b]) {
+        rt[b].load(tp + e);
+        if (f.resid) rd[b].load(dp + e);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = eb + b * kThreads * 8;
+      float w = 0.f;
+      if (fast[b]) {
+        float t[8], d[8];
+        rt[b].unpack(t);
+        if (f.resid) rd[b].unpack(d);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) w += job_weight(f, t[q], f.resid ? d[q] : 0.f);
+      } else if (e < e1) {
+        w = job_weight8<TT, TD>(f, tp, dp, false, false, e, e1);
+      }
+      s += (double)w;
+    }
+  }
+  return s;
+}
+
+// Decisions: one wavefront per request; writes the request's sampling job.
+template <typename TT, typename TD>
+__global__ __launch_bounds__(64) void verify_decide_kernel(DecideArgs a, Job* __restrict__ jobs) {
+  const int i = blockIdx.x;
+  const int base = a.cu[i], end = a.cu[i + 1];
+  const int n = end - base - 1;
+  if (n < 0 || n > a.K || base < 0 || end > a.max_rows) {
+    fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
+    if (threadIdx.x == 0) jobs[i].mode = JOB_NONE;
+    return;
+  }
+  decide_sampled<TT, TD>(a, i, jobs + i);
+}
+
+struct SampleArgs {
+  const void* tgt;
+  int64_t ld_t;
+  const void* drf;
+  int64_t ld_d_r, ld_d_k;
+  int32_t R, K, V, nch2, ce;
+  float cl;
+  const Job* jobs;
+  double* rsum;
+  int32_t* out;
+};
+
+// Residual / bonus weight sums per (request, chunk), grid-stride over items.
+template <typename TT, typename TD>
+__global__ __launch_bounds__(kThreads) void verify_residual_kernel(SampleArgs a) {
+  __shared__ double smd[kThreads / 64];
+  const long items = (long)a.R * a.nch2;
+  for (long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int i = (int)(it / a.nch2), c = (int)(it % a.nch2);
+    const Job jb = a.jobs[i];
+    if (jb.mode == JOB_NONE) continue;  // uniform over the workgroup
+    const bool resid = jb.mode == JOB_RESID;
+    const JobFrame f = job_frame(jb, a.cl, resid);
+    const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
+    const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
+    const double S = block_sum<kThreads / 64>(job_chunk_sum<TT, TD>(f, tp, dp, c * a.ce, a.ce, a.V), smd);
+    if (threadIdx.x == 0) a.rsum[it] = S;
+  }
+}
+
+// Inverse-CDF draw, one workgroup per request: locate the chunk holding u' * total from
+// the chunk sums, rescan it with contiguous per-thread ranges and an fp64 exclusive scan,
+// and let the owning thread walk its range to the first element past the target.
+template <typename TT, typename TD>
+__global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArgs a) {
+  __shared__ double s_csum[64];
   __shared__ double s_wtot[kSampleThreads / 64];
   __shared__ int s_chunk;
   __shared__ double s_tau;
   __shared__ int s_found;
   __shared__ int s_lastp[kSampleThreads / 64];
   const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid < 64) {
-    const int base = a.cu[i], end = a.cu[i + 1];
-    const int n = end - base - 1;
-    if (n < 0 || n > a.K || base < 0 || end > a.max_rows) {
-      fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
-      if (lane == 0) s_job.mode = JOB_NONE;
-    } else {
-      decide_sampled<TT, TD>(a, i, &s_job);
-    }
-  }
-  __syncthreads();
-  const Job jb = s_job;
-  if (jb.mode == JOB_NONE) return;  // uniform over the workgroup
-  const int V = a.V;
+  const Job jb = a.jobs[i];
+  if (jb.mode == JOB_NONE) return;
   bool resid = jb.mode == JOB_RESID;
   const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
   const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
-  const bool t_al = (((uintptr_t)tp) & 15u) == 0;
-  const bool d_al = !resid || (((uintptr_t)dp) & 15u) == 0;
-  // chunking: nc chunks of ce elements (ce a multiple of one workgroup step)
-  int nc = (V + kSampleVec - 1) / kSampleVec;
-  if (nc > kSampleMaxChunks) nc = kSampleMaxChunks;
-  const int steps = (V + nc * kSampleVec - 1) / (nc * kSampleVec);
-  const int ce = steps * kSampleVec;
-  JobFrame f = job_frame(jb, a.cl, resid);
+  if (tid < 64) s_csum[tid] = tid < a.nch2 ? a.rsum[(size_t)i * a.nch2 + tid] : 0.0;
+  __syncthreads();
   double total = 0.0;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    // pass 1: per-chunk sums. Vector vi of this thread covers 8 elements of chunk vi / steps;
-    // a batch of kBatch vectors (both rows) is loaded before any is used.
-    constexpr int kBatch = (sizeof(TT) == 2 && sizeof(TD) == 2) ? 8 : 4;
-    const int nvec = nc * steps;
-    for (int q = tid; q < (kSampleThreads / 64) * kSampleMaxChunks; q += kSampleThreads)
-      (&s_part[0][0])[q] = 0.0;
-    __syncthreads();
-    for (int vb = 0; vb < nvec; vb += kBatch) {
-      Raw8<TT> rt[kBatch];
-      Raw8<TD> rd[kBatch];
-      bool fast[kBatch];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int vi = vb + b;
-        const int e = (vi / steps) * ce + (vi % steps) * kSampleVec + tid * 8;
-        fast[b] = vi < nvec && e + 8 <= V && t_al && d_al;
-        if (fast[b]) {
-          rt[b].load(tp + e);
-          if (f.resid) rd[b].load(dp + e);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int vi = vb + b;
-        if (vi >= nvec) break;  // uniform
-        const int e = (vi / steps) * ce + (vi % steps) * kSampleVec + tid * 8;
-        float wsum = 0.f;
-        if (fast[b]) {
-          float t[8], d[8];
-          rt[b].unpack(t);
-          if (f.resid) rd[b].unpack(d);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) wsum += job_weight(f, t[q], f.resid ? d[q] : 0.f);
-        } else if (e < V) {
-          wsum = job_weight8<TT, TD>(f, tp, dp, false, false, e, V);
-        }
-        const double ws = wave_sum((double)wsum);
-        if (lane == 0) s_part[w][vi / steps] += ws;
-      }
-    }
-    __syncthreads();
-    if (tid < nc) {
-      double cs = 0.0;
-      for (int q = 0; q < kSampleThreads / 64; ++q) cs += s_part[q][tid];
-      s_csum[tid] = cs;
-    }
-    __syncthreads();
-    total = 0.0;
-    for (int c = 0; c < nc; ++c) total += s_csum[c];
-    if (!resid || total > 0.0) break;
+  for (int c = 0; c < a.nch2; ++c) total += s_csum[c];
+  if (resid && !(total > 0.0)) {
     // empty residual (p <= q everywhere after rounding): draw from p instead
     resid = false;
-    f = job_frame(jb, a.cl, false);
-    __syncthreads();
+    const JobFrame fp = job_frame(jb, a.cl, false);
+    const bool t_al0 = (((uintptr_t)tp) & 15u) == 0;
+    for (int c = 0; c < a.nch2; ++c) {
+      double s0 = 0.0;
+      const int c1 = min(a.V, (c + 1) * a.ce);
+      for (int e = c * a.ce + tid * 8; e < c1; e += kSampleThreads * 8)
+        s0 += (double)job_weight8<TT, TD>(fp, tp, nullptr, t_al0, true, e, c1);
+      const double S = block_sum<kSampleThreads / 64>(s0, s_wtot);
+      __syncthreads();
+      if (tid == 0) s_csum[c] = S;
+      __syncthreads();
+    }
+    total = 0.0;
+    for (int c = 0; c < a.nch2; ++c) total += s_csum[c];
   }
+  const JobFrame f = job_frame(jb, a.cl, resid);
   if (tid == 0) {
     const double target = jb.us * total;
     double acc = 0.0;
     int cs = -1;
-    for (int c = 0; c < nc; ++c) {
+    for (int c = 0; c < a.nch2; ++c) {
       if (acc + s_csum[c] > target) {
         cs = c;
         break;
@@ -730,7 +848,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_decide_sample_kernel(De
     }
     double tau = target - acc;
     if (cs < 0) {  // rounding left no chunk: take the last chunk with weight
-      for (int c = nc - 1; c >= 0; --c)
+      for (int c = a.nch2 - 1; c >= 0; --c)
         if (s_csum[c] > 0.0) {
           cs = c;
           break;
@@ -749,10 +867,11 @@ __global__ __launch_bounds__(kSampleThreads) void verify_decide_sample_kernel(De
     if (tid == 0) *dst = -1;
     return;
   }
-  // pass 2: contiguous per-thread ranges of the chosen chunk
-  const int e0 = cs * ce;
-  const int per = steps * 8;
-  const int r0 = min(V, e0 + tid * per), r1 = min(V, r0 + per);
+  const int e0 = cs * a.ce;
+  const int per = a.ce / kSampleThreads;  // a multiple of 8
+  const int r0 = min(a.V, e0 + tid * per), r1 = min(a.V, r0 + per);
+  const bool t_al = (((uintptr_t)tp) & 15u) == 0;
+  const bool d_al = !resid || (((uintptr_t)dp) & 15u) == 0;
   double s = 0.0;
   for (int e = r0; e < r1; e += 8) s += (double)job_weight8<TT, TD>(f, tp, dp, t_al, d_al, e, r1);
   double inc = s;
@@ -804,7 +923,8 @@ int num_cus() {
 
 struct VerifyLayout {
   int ncht, nchd, max_rows;
-  size_t off_t, off_d, total;
+  SampleGeom sg;
+  size_t off_t, off_d, off_j, off_r, total;
 };
 
 VerifyLayout verify_layout(int R, int K, int V, int max_rows, int t_dtype, int d_dtype) {
@@ -812,33 +932,50 @@ VerifyLayout verify_layout(int R, int K, int V, int max_rows, int t_dtype, int d
   L.max_rows = max_rows > 0 ? max_rows : R * (K + 1);
   L.ncht = stat_chunks(V, esize_of(t_dtype));
   L.nchd = stat_chunks(V, esize_of(d_dtype));
+  L.sg = sample_geom(R, V);
   size_t off = 0;
   L.off_t = off;
   off = align_up(off + (size_t)L.max_rows * L.ncht * sizeof(StatSlot), 256);
   L.off_d = off;
   off = align_up(off + (size_t)R * K * L.nchd * sizeof(StatSlot), 256);
+  L.off_j = off;
+  off = align_up(off + (size_t)R * sizeof(Job), 256);
+  L.off_r = off;
+  off = align_up(off + (size_t)R * L.sg.nch2 * sizeof(double), 256);
   L.total = off;
   return L;
 }
 
+long stats_grid(long max_items) {
+  const long cap = DSP_STATS_WG_PER_CU > 0 ? (long)num_cus() * DSP_STATS_WG_PER_CU : 1l << 20;
+  long g = max_items < cap ? max_items : cap;
+  return g < 1 ? 1 : g;
+}
+
 template <typename TT, typename TD>
-void launch_sampled(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items) {
+void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs& pa, hipStream_t s,
+                    long max_items) {
   const int cus = num_cus();
-  long g = max_items < (long)cus * 8 ? max_items : (long)cus * 8;
-  if (g < 1) g = 1;
+  const long g = stats_grid(max_items);
   prof_begin(DSP_K_VERIFY_STATS, s);
   hipLaunchKernelGGL((verify_stats_kernel<TT, TD>), dim3((unsigned)g), dim3(kThreads), 0, s, sa);
   prof_end(DSP_K_VERIFY_STATS, s);
+  prof_begin(DSP_K_VERIFY_DECIDE, s);
+  hipLaunchKernelGGL((verify_decide_kernel<TT, TD>), dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
+  prof_end(DSP_K_VERIFY_DECIDE, s);
+  const long ri = (long)pa.R * pa.nch2;
+  const long g2 = ri < (long)cus * 8 ? ri : (long)cus * 8;
+  prof_begin(DSP_K_VERIFY_RESIDUAL, s);
+  hipLaunchKernelGGL((verify_residual_kernel<TT, TD>), dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
+  prof_end(DSP_K_VERIFY_RESIDUAL, s);
   prof_begin(DSP_K_VERIFY_SAMPLE, s);
-  hipLaunchKernelGGL((verify_decide_sample_kernel<TT, TD>), dim3(da.R), dim3(kSampleThreads), 0, s, da);
+  hipLaunchKernelGGL((verify_sample_kernel<TT, TD>), dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
   prof_end(DSP_K_VERIFY_SAMPLE, s);
 }
 
 template <typename TT>
 void launch_greedy(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items, bool tree) {
-  const int cus = num_cus();
-  long g = max_items < (long)cus * 8 ? max_items : (long)cus * 8;
-  if (g < 1) g = 1;
+  const long g = stats_grid(max_items);
   prof_begin(DSP_K_VERIFY_STATS, s);
   hipLaunchKernelGGL((verify_argmax_kernel<TT>), dim3((unsigned)g), dim3(kThreads), 0, s, sa);
   prof_end(DSP_K_VERIFY_STATS, s);
@@ -866,6 +1003,7 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
                                         int64_t ld_x, const int32_t* parent, int32_t R, int32_t K,
                                         int32_t V, int32_t max_rows, float temperature, uint64_t seed,
                                         uint64_t round, uint64_t* round_dev, const int64_t* req_id,
+                                        const int32_t* row_req, const int32_t* row_pos,
                                         int32_t* accepted_len,
                                         int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x,
                                         int32_t* status, void* ws, size_t ws_bytes, void* stream) {
@@ -884,6 +1022,7 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
     return fail(DSP_ERR_NULL, "required pointer is NULL");
   if (!greedy && !drf) return fail(DSP_ERR_NULL, "draft logits required for temperature > 0");
   if ((p_x == nullptr) != (q_x == nullptr)) return fail(DSP_ERR_NULL, "p_x and q_x go together");
+  if ((row_req == nullptr) != (row_pos == nullptr)) return fail(DSP_ERR_NULL, "row_req and row_pos go together");
   if (ld_t < V || ld_x < K) return fail(DSP_ERR_SHAPE, "strides too small");
   if (!greedy && (ld_d_k < V || ld_d_r < (int64_t)K * ld_d_k))
     return fail(DSP_ERR_SHAPE, "draft strides too small");
@@ -896,11 +1035,13 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
 
   StatSlot* tstats = (StatSlot*)((uintptr_t)ws + L.off_t);
   StatSlot* dstats = (StatSlot*)((uintptr_t)ws + L.off_d);
+  Job* jobs = (Job*)((uintptr_t)ws + L.off_j);
+  double* rsum = (double*)((uintptr_t)ws + L.off_r);
   const float cl = greedy ? 0.f : (float)(1.4426950408889634074 / (double)temperature);
   hipStream_t s = (hipStream_t)stream;
 
   StatsArgs sa{tgt, ld_t, drf, ld_d_r, ld_d_k, cu_seqlens, R, K, V, L.max_rows, L.ncht, L.nchd, cl,
-               tstats, dstats, greedy ? nullptr : round_dev};
+               tstats, dstats, greedy ? nullptr : round_dev, row_req, row_pos};
   DecideArgs da{tgt, t_dtype, ld_t, drf, ddt, ld_d_r, ld_d_k, cu_seqlens, draft_tok, ld_x, parent,
                 R, K, V, L.max_rows, L.ncht, L.nchd, cl, seed, round, req_id, tstats, dstats,
                 accepted_len, out_tokens, stop_pos, p_x, q_x, status, round_dev};
@@ -909,11 +1050,12 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
     if (t_dtype == DSP_BF16) launch_greedy<uint16_t>(sa, da, s, max_items, tree);
     else launch_greedy<float>(sa, da, s, max_items, tree);
   } else {
-    const long max_items = (long)L.max_rows * L.ncht + (long)R * K * L.nchd;
-    if (t_dtype == DSP_BF16 && d_dtype == DSP_BF16) launch_sampled<uint16_t, uint16_t>(sa, da, s, max_items);
-    else if (t_dtype == DSP_BF16) launch_sampled<uint16_t, float>(sa, da, s, max_items);
-    else if (d_dtype == DSP_BF16) launch_sampled<float, uint16_t>(sa, da, s, max_items);
-    else launch_sampled<float, float>(sa, da, s, max_items);
+    SampleArgs pa{tgt, ld_t, drf, ld_d_r, ld_d_k, R, K, V, L.sg.nch2, L.sg.ce, cl, jobs, rsum, out_tokens};
+    const long max_items = (long)L.max_rows * (L.ncht + L.nchd);
+    if (t_dtype == DSP_BF16 && d_dtype == DSP_BF16) launch_sampled<uint16_t, uint16_t>(sa, da, pa, s, max_items);
+    else if (t_dtype == DSP_BF16) launch_sampled<uint16_t, float>(sa, da, pa, s, max_items);
+    else if (d_dtype == DSP_BF16) launch_sampled<float, uint16_t>(sa, da, pa, s, max_items);
+    else launch_sampled<float, float>(sa, da, pa, s, max_items);
   }
   return hip_check(hipGetLastError(), "verify launch");
 }

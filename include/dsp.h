@@ -163,6 +163,10 @@ int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const in
 /*                             (-1 = root)                                   */
 /*   p_x, q_x [R, K] float32   (nullable; chain, T > 0) p_k(x_k), q_k(x_k)    */
 /*                             for every window position, 0 elsewhere        */
+/* row_req, row_pos (nullable, together): the request and position of every  */
+/* packed row, as written by dsp_pack_ragged; when given, draft rows are      */
+/* located from them instead of by searching cu_seqlens (a row whose maps do */
+/* not match cu_seqlens falls back to the search).                           */
 /* max_rows: host-known bound on cu_seqlens[R] (0 = R*(K+1)); tgt must hold    */
 /* at least that many rows. Rows past min(cu_seqlens[R], max_rows) are never  */
 /* read, and a request whose rows end past max_rows is a window fault.        */
@@ -177,6 +181,7 @@ int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
                              int32_t R, int32_t K, int32_t V, int32_t max_rows,
                              float temperature, uint64_t seed, uint64_t round,
                              uint64_t* round_dev, const int64_t* req_id,
+                             const int32_t* row_req, const int32_t* row_pos,
                              int32_t* accepted_len, int32_t* out_tokens, int32_t* stop_pos,
                              float* p_x, float* q_x, int32_t* status,
                              void* ws, size_t ws_bytes, void* stream);

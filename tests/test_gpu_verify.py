@@ -13,7 +13,15 @@ from parity import (TieCounter, compare_chain_verify, cu_from_windows, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def _run_case(case, windows, temperature, seed=0, rnd=0, req_id=None, ld_pad=0, want_probs=True):
+def _row_maps(windows):
+    """The pack's packed-row maps (request, position) for the given windows."""
+    req = np.concatenate([np.full(w + 1, i, np.int32) for i, w in enumerate(windows)])
+    pos = np.concatenate([np.arange(w + 1, dtype=np.int32) for w in windows])
+    return to_gpu(req), to_gpu(pos)
+
+
+def _run_case(case, windows, temperature, seed=0, rnd=0, req_id=None, ld_pad=0, want_probs=True,
+              row_maps=False):
     R, K, V, dt = case["R"], case["K"], case["V"], case["dtype"]
     tp = packed_from_dense(case["t"], windows)
     if ld_pad:
@@ -23,9 +31,11 @@ def _run_case(case, windows, temperature, seed=0, rnd=0, req_id=None, ld_pad=0, 
     dg = logits_to_gpu(case["d"], dt)
     xg = to_gpu(case["x"].astype(np.int32))
     rid = None if req_id is None else to_gpu(np.asarray(req_id, dtype=np.int64))
-    print(f"verify case R={R} K={K} V={V} dtype={dt} T={temperature} ld={tg.stride(0)}", flush=True)
+    rq, rp = _row_maps(windows) if row_maps else (None, None)
+    print(f"verify case R={R} K={K} V={V} dtype={dt} T={temperature} ld={tg.stride(0)} maps={row_maps}",
+          flush=True)
     g = dsp.verify_rejection(tg, to_gpu(cu), xg, drf=dg, temperature=temperature, seed=seed, round=rnd,
-                             req_id=rid, want_probs=want_probs)
+                             req_id=rid, want_probs=want_probs, row_req=rq, row_pos=rp)
     torch.cuda.synchronize()
     assert int(host(g["status"])[0]) == 0
     tv = values(tp[:, :V], dt).astype(np.float64)
@@ -44,8 +54,8 @@ def test_sampled_small(dt, V):
     case = workloads.verify_case(R, K, V, dtype=dt, seed=V + (dt == "bf16"), t_sigma=2.0, d_sigma=0.4)
     windows = np.array([5, 0, 3, 5, 1, 4])
     ties = TieCounter()
-    for T in (1.0, 0.7):
-        g, orc = _run_case(case, windows, T, seed=11, rnd=2)
+    for T, maps in ((1.0, False), (0.7, False), (1.0, True)):
+        g, orc = _run_case(case, windows, T, seed=11, rnd=2, row_maps=maps)
         compare_chain_verify(g, orc, R, K, windows, ties)
     ties.check()
 
@@ -68,8 +78,10 @@ def test_unaligned_rows_and_request_ids():
     case = workloads.verify_case(R, K, V, dtype="bf16", seed=5, t_sigma=2.0, d_sigma=0.3)
     windows = np.array([4, 2, 0, 4, 3])
     ties = TieCounter()
-    g, orc = _run_case(case, windows, 1.0, seed=3, rnd=9, req_id=[100, 7, 55, 2**40, 3], ld_pad=3)
-    compare_chain_verify(g, orc, R, K, windows, ties)
+    for maps in (False, True):
+        g, orc = _run_case(case, windows, 1.0, seed=3, rnd=9, req_id=[100, 7, 55, 2**40, 3], ld_pad=3,
+                           row_maps=maps)
+        compare_chain_verify(g, orc, R, K, windows, ties)
     ties.check()
 
 
@@ -204,7 +216,7 @@ def test_dense_vocab_verify_c2_full():
     c = workloads.c2()
     R, K = c["R"], c["K"]
     ties = TieCounter()
-    g, orc = _run_case(c, np.full(R, K), 1.0, seed=0)
+    g, orc = _run_case(c, np.full(R, K), 1.0, seed=0, row_maps=True)
     compare_chain_verify(g, orc, R, K, np.full(R, K), ties)
     ties.check()
     acc = host(g["accepted_len"])
