@@ -11,9 +11,10 @@ from fixed seeds, copied to HBM before timing, and reused for every step (the
 Philox round changes per step).
 
 Other workloads (--workload):
-  c3  confidence-scheduled ragged verify (256 x 16, mixed easy/hard streams)
-  c4  Markov-head greedy chain (256 requests x 16 steps, rank 256)
-  c5  PCTree expansion (128 x depth 16, k=4, F=16, N=64) + greedy tree verify
+  scheduled-verify  confidence-scheduled ragged verify (256 x 16, mixed easy/hard streams)
+  markov-chain      Markov-head greedy chain (256 requests x 16 steps, rank 256)
+  pctree            PCTree expansion (128 x depth 16, k=4, F=16, N=64) + greedy tree verify
+  copy              1 GiB device copy (reference for scaling HBM counters)
 
 Prints ONE JSON line. `roofline` covers the dominant kernel of the workload,
 timed with HIP events recorded by libdsp on the launch stream during the timed
@@ -39,7 +40,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5", "copy"])
+    ap.add_argument("--workload", default="dense-verify",
+                    choices=["dense-verify", "scheduled-verify", "markov-chain", "pctree", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prof-all", action="store_true", help="time every kernel with events (diagnostic)")
@@ -142,7 +144,7 @@ def bench_verify(args, which):
     import workloads
 
     dev = torch.device("cuda", 0)
-    c = workloads.c2() if which == "c2" else workloads.c3()
+    c = workloads.dense_verify() if which == "dense-verify" else workloads.scheduled_verify()
     R, K, V = c["R"], c["K"], c["V"]
 
     def gpu(a):
@@ -156,7 +158,7 @@ def bench_verify(args, which):
     # windows are a deterministic function of the confidences: compute them once to lay out the
     # packed target logits (they stand in for the target forward over the packed buffer)
     w0 = dsp.schedule_windows(conf, cost)["windows"].cpu().numpy()
-    if which == "c2":
+    if which == "dense-verify":
         tgt = bf16(c["t"].reshape(R * (K + 1), V))
     else:
         tgt = bf16(np.concatenate([c["t"][i, :w0[i] + 1] for i in range(R)]))
@@ -199,7 +201,7 @@ def bench_verify(args, which):
         higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic (seeded N(0,3) logits with 1% +8 boosts; draft = target + Gaussian noise)",
         config=dict(workload=("dense-vocab verify: 64 requests, K=7, V=151936, bf16, full-block windows, T=1"
-                              if which == "c2" else
+                              if which == "dense-verify" else
                               "confidence-scheduled ragged verify: 256 requests, K=16, V=151936, bf16, "
                               "additive cost 1+0.05n, compact windows, T=1"),
                     requests=R, block=K, vocab=V, verified_drafts_per_step=N, packed_rows=T_rows,
@@ -223,7 +225,7 @@ def bench_markov(args):
     import workloads
 
     dev = torch.device("cuda", 0)
-    c = workloads.c4()
+    c = workloads.markov_chain()
     R, B, V, r = c["R"], c["B"], c["V"], c["rank"]
 
     def bf16(bits):
@@ -238,7 +240,8 @@ def bench_markov(args):
                                     args.prof_all)
     elapsed = min(eager, graph)
     g = kern["MARKOV_GEMM"]["avg_us"]
-    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 / B
+    # one launch reads the step's base logits L, the previous tokens' rows of U and all of Wt
+    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2
     flops_launch = 2.0 * R * r * V
     res = dict(
         metric="drafted tokens/sec", value=R * B * args.steps / elapsed, unit="tokens/s", n_gpus=1,
@@ -247,7 +250,7 @@ def bench_markov(args):
         config=dict(workload="Markov-head greedy chain: 256 requests, 16 steps, V=151936, rank 256"),
         roofline=dict(kernel="markov_gemm", bound="hbm", achieved=bytes_launch / (g * 1e-6) / 1e9,
                       peak=PEAK_HBM_GBS, unit="GB/s", frac=bytes_launch / (g * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                      traffic=traffic_from_profiles("markov.hip", "markov_gemm", "c4"),
+                      traffic=traffic_from_profiles("markov.hip", "markov_gemm", "markov-chain"),
                       mfma_tflops=flops_launch / (g * 1e-6) / 1e12,
                       mfma_frac=flops_launch / (g * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, avg_us=g),
         kernels=kern,
@@ -273,7 +276,7 @@ def bench_tree(args):
     import workloads
 
     dev = torch.device("cuda", 0)
-    c = workloads.c5()
+    c = workloads.pctree()
     R, D, V, r = c["R"], c["B"], c["V"], c["rank"]
     k, F, N = c["topk"], c["frontier"], c["topN"]
 
@@ -353,9 +356,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.workload == "copy":
         res = bench_copy(args)
-    elif args.workload in ("c2", "c3"):
+    elif args.workload in ("dense-verify", "scheduled-verify"):
         res = bench_verify(args, args.workload)
-    elif args.workload == "c4":
+    elif args.workload == "markov-chain":
         res = bench_markov(args)
     else:
         res = bench_tree(args)

@@ -35,7 +35,6 @@ struct ProfRec {
 static int32_t g_prof_mask = 0;
 static std::vector<ProfRec> g_prof_recs;
 static std::vector<hipEvent_t> g_prof_pool;
-static hipEvent_t g_prof_open[DSP_K_COUNT];
 
 static hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -48,22 +47,21 @@ static hipEvent_t prof_event() {
   return e;
 }
 
-void prof_begin(int kernel, hipStream_t s) {
-  if (!(g_prof_mask & (1 << kernel))) return;
-  hipEvent_t e = prof_event();
-  if (!e) return;
-  hipEventRecord(e, s);
-  g_prof_open[kernel] = e;
+bool prof_events(int kernel, hipEvent_t* start, hipEvent_t* stop) {
+  if (!(g_prof_mask & (1 << kernel))) return false;
+  hipEvent_t a = prof_event();
+  if (!a) return false;
+  hipEvent_t b = prof_event();
+  if (!b) {
+    g_prof_pool.push_back(a);
+    return false;
+  }
+  *start = a;
+  *stop = b;
+  return true;
 }
 
-void prof_end(int kernel, hipStream_t s) {
-  if (!(g_prof_mask & (1 << kernel)) || !g_prof_open[kernel]) return;
-  hipEvent_t e = prof_event();
-  if (!e) return;
-  hipEventRecord(e, s);
-  g_prof_recs.push_back({kernel, g_prof_open[kernel], e});
-  g_prof_open[kernel] = nullptr;
-}
+void prof_commit(int kernel, hipEvent_t start, hipEvent_t stop) { g_prof_recs.push_back({kernel, start, stop}); }
 
 // ---------------------------------------------------------------- philox utility
 __global__ void philox_uniforms_kernel(const uint64_t* __restrict__ ctr, int64_t n, uint64_t seed,
@@ -93,8 +91,7 @@ extern "C" int32_t dsp_philox_uniforms(const uint64_t* ctr, int64_t n, uint64_t 
   if (!ctr || !out) return fail(DSP_ERR_NULL, "ctr and out are required");
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(philox_uniforms_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)stream, ctr, n, seed, out);
+  philox_uniforms_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(ctr, n, seed, out);
   return hip_check(hipGetLastError(), "philox_uniforms launch");
 }
 

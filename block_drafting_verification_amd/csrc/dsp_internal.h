@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP translation units of libdsp (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -14,9 +15,26 @@ int32_t fail(int32_t code, const char* fmt, ...);   // records dsp_last_error, r
 void clear_error();
 int32_t hip_check(hipError_t e, const char* what);  // DSP_OK or DSP_ERR_HIP
 
-// Kernel timing hooks (no-ops unless dsp_prof_enable(1)).
-void prof_begin(int kernel, hipStream_t s);
-void prof_end(int kernel, hipStream_t s);
+// Kernel timing (off unless dsp_prof_enable selects the kernel id): prof_events hands out
+// a start/stop event pair when the id is selected, prof_commit files the pair for
+// dsp_prof_query once the launch carrying them is enqueued.
+bool prof_events(int kernel, hipEvent_t* start, hipEvent_t* stop);
+void prof_commit(int kernel, hipEvent_t start, hipEvent_t stop);
+
+// Launch `kernel` on stream s. When its id is being timed, the events ride on the
+// dispatch packet itself (hipExtLaunchKernelGGL), so they bracket the kernel's own
+// execution rather than the host's launch gap.
+template <typename... KArgs, typename... Args>
+inline void launch(int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                   Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (prof_events(kid, &e0, &e1)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, (KArgs)args...);
+    prof_commit(kid, e0, e1);
+  } else {
+    kernel<<<grid, block, shmem, s>>>((KArgs)args...);
+  }
+}
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -34,7 +34,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTV = 128;  // vocabulary entries per tile
 constexpr int kWR = 4;            // wavefronts along the parent-row axis
@@ -214,10 +213,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
           uint2 w = {0u, 0u};
           if (rvalid[j]) {
             if (full && l_al[j]) {
-              // L is read once per call: non-temporal, so the Wt lines re-read every step keep the cache
-              const u32x2 nt = __builtin_nontemporal_load((const u32x2*)(Lrow[j] + v));
-              w.x = nt.x;
-              w.y = nt.y;
+              w = *(const uint2*)(Lrow[j] + v);
             } else {
               uint32_t e[4];
 #pragma unroll
@@ -671,7 +667,7 @@ int pick_groups(int rows, int V) {
 }
 
 template <int MODE>
-int32_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
   const size_t lds = gemm_lds_bytes(a.rank);
   static bool attr_set = false;
   if (!attr_set) {
@@ -680,7 +676,7 @@ int32_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     attr_set = true;
   }
   dim3 grid(a.G, (a.rows + kTR - 1) / kTR);
-  hipLaunchKernelGGL(markov_gemm_kernel<MODE>, grid, dim3(kGT), lds, s, a);
+  launch(kid, markov_gemm_kernel<MODE>, grid, dim3(kGT), (uint32_t)lds, s, a);
   return hip_check(hipGetLastError(), "markov gemm launch");
 }
 
@@ -768,14 +764,11 @@ extern "C" int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t
     GemmArgs ga{(const uint16_t*)U, (const uint16_t*)Wt, V, rank,
                 d == 0 ? prev_tok : y + (d - 1), d == 0 ? 1 : ld_y,
                 (const uint16_t*)L, ldL_r, ldL_d, d, R, 1, G, ws, status};
-    prof_begin(DSP_K_MARKOV_GEMM, s);
-    rc = logq ? launch_gemm<MODE_ARGMAX_LSE>(ga, s) : launch_gemm<MODE_ARGMAX>(ga, s);
-    prof_end(DSP_K_MARKOV_GEMM, s);
+    rc = logq ? launch_gemm<MODE_ARGMAX_LSE>(DSP_K_MARKOV_GEMM, ga, s)
+              : launch_gemm<MODE_ARGMAX>(DSP_K_MARKOV_GEMM, ga, s);
     if (rc) return rc;
     ChainMergeArgs ma{(const ChainPart*)ws, G, R, d, y, ld_y, logq};
-    prof_begin(DSP_K_MARKOV_MERGE, s);
-    hipLaunchKernelGGL(chain_merge_kernel, dim3(R), dim3(64), 0, s, ma);
-    prof_end(DSP_K_MARKOV_MERGE, s);
+    launch(DSP_K_MARKOV_MERGE, chain_merge_kernel, dim3(R), dim3(64), 0, s, ma);
     rc = hip_check(hipGetLastError(), "chain merge launch");
     if (rc) return rc;
   }
@@ -824,25 +817,19 @@ extern "C" int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r
     const int32_t* ptok = d == 1 ? anchor : tok[d & 1];
     GemmArgs ga{(const uint16_t*)U, (const uint16_t*)Wt, V, rank, ptok, 1, (const uint16_t*)L, ldL_r,
                 ldL_d, d - 1, rows, fp, G, part, status};
-    prof_begin(DSP_K_TREE_GEMM, s);
-    rc = launch_gemm<MODE_TREE>(ga, s);
-    prof_end(DSP_K_TREE_GEMM, s);
+    rc = launch_gemm<MODE_TREE>(DSP_K_TREE_GEMM, ga, s);
     if (rc) return rc;
     const int fn = f[d - 1];
     TreeMergeArgs ma{part, G, d, fp, fn, topk, frontier, R, V, rank, ptok, d == 1 ? nullptr : sc[d & 1],
                      tok[(d + 1) & 1], sc[(d + 1) & 1], kept, T.kept_stride, (const uint16_t*)L, ldL_r,
                      ldL_d, (const uint16_t*)U, (const uint16_t*)Wt, status};
-    prof_begin(DSP_K_TREE_MERGE, s);
-    hipLaunchKernelGGL(tree_merge_kernel, dim3(R), dim3(256), 0, s, ma);
-    prof_end(DSP_K_TREE_MERGE, s);
+    launch(DSP_K_TREE_MERGE, tree_merge_kernel, dim3(R), dim3(256), 0, s, ma);
     rc = hip_check(hipGetLastError(), "tree merge launch");
     if (rc) return rc;
     fp = fn;
   }
   TreeFinalArgs fa{kept, T.kept_stride, D, frontier, topk, topN, R, node_token, node_parent, node_depth,
                    node_score, n_nodes};
-  prof_begin(DSP_K_TREE_FINAL, s);
-  hipLaunchKernelGGL(tree_final_kernel, dim3(R), dim3(256), 0, s, fa);
-  prof_end(DSP_K_TREE_FINAL, s);
+    launch(DSP_K_TREE_FINAL, tree_final_kernel, dim3(R), dim3(256), 0, s, fa);
   return hip_check(hipGetLastError(), "tree final launch");
 }

@@ -333,10 +333,8 @@ extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K,
     return fail(DSP_ERR_UNSUPPORTED, "unknown scheduler mode %d", mode);
   if (!conf || !cost || !windows) return fail(DSP_ERR_NULL, "conf, cost and windows are required");
   const int M = max_tokens < 0 ? R * K : (max_tokens < R * K ? max_tokens : R * K);
-  prof_begin(DSP_K_SCHEDULE, (hipStream_t)stream);
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, (hipStream_t)stream, conf, R, K,
-                     cost, mode, M, quant_bits(R, K), windows, survival, stats);
-  prof_end(DSP_K_SCHEDULE, (hipStream_t)stream);
+  launch(DSP_K_SCHEDULE, schedule_kernel, dim3(1), dim3(kSchedThreads), 0, (hipStream_t)stream, conf, R, K,
+         cost, mode, M, quant_bits(R, K), windows, survival, stats);
   return hip_check(hipGetLastError(), "schedule launch");
 }
 
@@ -358,9 +356,7 @@ extern "C" int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchor
   for (int j = 0; j < 64; ++j) t.v[j] = j < n_tiers ? tiers_host[j] : 0;
   for (int j = 1; j < n_tiers; ++j)
     if (t.v[j] < t.v[j - 1]) return fail(DSP_ERR_SHAPE, "tiers must be ascending");
-  prof_begin(DSP_K_PACK, (hipStream_t)stream);
-  hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, windows, anchors, drafts,
-                     ld_drafts, R, K, t, cu_seqlens, tokens, row_req, row_pos, total_and_tier, status);
-  prof_end(DSP_K_PACK, (hipStream_t)stream);
+  launch(DSP_K_PACK, pack_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, windows, anchors, drafts,
+         ld_drafts, R, K, t, cu_seqlens, tokens, row_req, row_pos, total_and_tier, status);
   return hip_check(hipGetLastError(), "pack launch");
 }

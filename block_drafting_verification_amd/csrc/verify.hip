@@ -957,34 +957,20 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
                     long max_items) {
   const int cus = num_cus();
   const long g = stats_grid(max_items);
-  prof_begin(DSP_K_VERIFY_STATS, s);
-  hipLaunchKernelGGL((verify_stats_kernel<TT, TD>), dim3((unsigned)g), dim3(kThreads), 0, s, sa);
-  prof_end(DSP_K_VERIFY_STATS, s);
-  prof_begin(DSP_K_VERIFY_DECIDE, s);
-  hipLaunchKernelGGL((verify_decide_kernel<TT, TD>), dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
-  prof_end(DSP_K_VERIFY_DECIDE, s);
+  launch(DSP_K_VERIFY_STATS, verify_stats_kernel<TT, TD>, dim3((unsigned)g), dim3(kThreads), 0, s, sa);
+  launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
   const long ri = (long)pa.R * pa.nch2;
   const long g2 = ri < (long)cus * 8 ? ri : (long)cus * 8;
-  prof_begin(DSP_K_VERIFY_RESIDUAL, s);
-  hipLaunchKernelGGL((verify_residual_kernel<TT, TD>), dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
-  prof_end(DSP_K_VERIFY_RESIDUAL, s);
-  prof_begin(DSP_K_VERIFY_SAMPLE, s);
-  hipLaunchKernelGGL((verify_sample_kernel<TT, TD>), dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
-  prof_end(DSP_K_VERIFY_SAMPLE, s);
+  launch(DSP_K_VERIFY_RESIDUAL, verify_residual_kernel<TT, TD>, dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
+  launch(DSP_K_VERIFY_SAMPLE, verify_sample_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
 }
 
 template <typename TT>
 void launch_greedy(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items, bool tree) {
   const long g = stats_grid(max_items);
-  prof_begin(DSP_K_VERIFY_STATS, s);
-  hipLaunchKernelGGL((verify_argmax_kernel<TT>), dim3((unsigned)g), dim3(kThreads), 0, s, sa);
-  prof_end(DSP_K_VERIFY_STATS, s);
-  prof_begin(DSP_K_VERIFY_DECIDE, s);
-  if (tree)
-    hipLaunchKernelGGL(verify_decide_tree, dim3(da.R), dim3(64), 0, s, da);
-  else
-    hipLaunchKernelGGL(verify_decide_greedy, dim3(da.R), dim3(64), 0, s, da);
-  prof_end(DSP_K_VERIFY_DECIDE, s);
+  launch(DSP_K_VERIFY_STATS, verify_argmax_kernel<TT>, dim3((unsigned)g), dim3(kThreads), 0, s, sa);
+  launch(DSP_K_VERIFY_DECIDE, tree ? verify_decide_tree : verify_decide_greedy, dim3(da.R), dim3(64), 0, s,
+         da);
 }
 
 }  // namespace

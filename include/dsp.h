@@ -238,16 +238,18 @@ int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t l
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (observability).                                            */
 /*                                                                          */
-/* dsp_prof_enable(mask): bit k set = bracket each launch of kernel k below  */
-/* with HIP events on its launch stream (mask 0 = off, -1 = all).            */
+/* dsp_prof_enable(mask): bit k set = time each launch of kernel k below     */
+/* with a start/stop HIP event pair attached to the kernel's own dispatch on */
+/* its launch stream (hipExtLaunchKernelGGL), so the interval is the kernel's */
+/* execution, not host launch gaps (mask 0 = off, -1 = all).                 */
 /* dsp_prof_query synchronises on the recorded events and returns the summed */
 /* duration and launch count since the last reset. Not thread safe, and not  */
 /* to be used while a stream is being captured into a graph.                 */
 /* ------------------------------------------------------------------------ */
 #define DSP_K_VERIFY_STATS     0  /* row statistics / arg-max streaming pass */
-#define DSP_K_VERIFY_DECIDE    1  /* greedy matching / tree walk */
-#define DSP_K_VERIFY_RESIDUAL  2  /* reserved */
-#define DSP_K_VERIFY_SAMPLE    3  /* sampled: decisions + residual / bonus draw */
+#define DSP_K_VERIFY_DECIDE    1  /* accept/reject decisions; greedy matching; tree walk */
+#define DSP_K_VERIFY_RESIDUAL  2  /* sampled: per-chunk mass of the residual / bonus row */
+#define DSP_K_VERIFY_SAMPLE    3  /* sampled: inverse-CDF draw of the correction token */
 #define DSP_K_SCHEDULE         4
 #define DSP_K_PACK             5
 #define DSP_K_MARKOV_GEMM      6

@@ -9,7 +9,7 @@ that rate over all R*K position pairs of the workload is within 0.005 of 0.8,
 using the oracle's fp64 log-softmax, and writes the result to
 workloads/calibration.json. It calls only the oracle and the seeded generator.
 
-    python -m oracle.calibrate_c2
+    python -m oracle.calibrate_dense_verify
 """
 import json
 import os
@@ -50,7 +50,7 @@ def main():
             hi = mid
     out = os.path.join(os.path.dirname(workloads.__file__), "calibration.json")
     with open(out, "w") as f:
-        json.dump({"c2_sigma": round(mid, 6), "c2_mean_acceptance": round(a, 6),
+        json.dump({"dense_verify_sigma": round(mid, 6), "dense_verify_mean_acceptance": round(a, 6),
                    "method": "bisection of sigma on [0.01, 5] for mean sum_v min(p, q) = 0.80 +- 0.005 "
                              "over the 448 (target, draft) row pairs, oracle fp64 softmax"}, f, indent=1)
         f.write("\n")

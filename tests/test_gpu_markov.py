@@ -82,7 +82,7 @@ def test_chain_of_course_fixture():
 
 def test_chain_c4_full():
     """256 requests x 16 steps, V=151,936, rank 256; every request checked with replay."""
-    c = workloads.c4()
+    c = workloads.markov_chain()
     _check_chain(c, want_logq=True)
 
 
@@ -141,7 +141,7 @@ def test_tree_c5_sampled_requests():
 
 
 def test_tree_verify_c5_shape_planted_paths():
-    """Tree verify on C5-shaped targets with a planted accepted path per request."""
+    """Tree verify on targets shaped like the PCTree workload with a planted accepted path per request."""
     c = workloads.markov_case(8, 16, workloads.V_DSV4, 256, seed=1005)
     Lg, Ug, Wtg, ag = _gpu_inputs(c)
     t = dsp.tree_expand(Lg, Ug, Wtg, ag, 4, 16, 64)

@@ -54,9 +54,9 @@ def test_schedule_special_cases():
 
 
 def test_schedule_c3_workload():
-    c = workloads.c3_schedule_inputs()
+    c = workloads.scheduled_verify_inputs()
     o = _sched(c["conf"], c["cost"])
-    print("C3 scheduled N =", o["N"], "of", 256 * 16)
+    print("scheduled verify: N =", o["N"], "of", 256 * 16)
     assert 0 < o["N"] < 256 * 16
 
 

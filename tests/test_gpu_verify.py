@@ -60,9 +60,9 @@ def test_sampled_small(dt, V):
     ties.check()
 
 
-def test_tiny_verify_c1():
+def test_tiny_verify():
     """4 requests, K=7, V=1024, fp32, Philox seed 0, full windows and a scheduled run."""
-    c = workloads.c1()
+    c = workloads.tiny_verify()
     ties = TieCounter()
     g, orc = _run_case(c, np.full(4, 7), 1.0, seed=0)
     compare_chain_verify(g, orc, 4, 7, np.full(4, 7), ties)
@@ -211,16 +211,16 @@ def test_max_window_64():
     ties.check()
 
 
-def test_dense_vocab_verify_c2_full():
+def test_dense_vocab_verify_full():
     """64 requests x K=7 x V=151,936 bf16, full-block windows, T=1: every request checked."""
-    c = workloads.c2()
+    c = workloads.dense_verify()
     R, K = c["R"], c["K"]
     ties = TieCounter()
     g, orc = _run_case(c, np.full(R, K), 1.0, seed=0, row_maps=True)
     compare_chain_verify(g, orc, R, K, np.full(R, K), ties)
     ties.check()
     acc = host(g["accepted_len"])
-    print("C2 mean accepted", acc.mean(), "near ties", ties.near, "of", ties.decisions)
+    print("dense verify: mean accepted", acc.mean(), "near ties", ties.near, "of", ties.decisions)
 
 
 def test_philox_uniforms_bitwise():

@@ -13,21 +13,21 @@ not used; these synthetic logits stand in for them.
 
 Recipes (N(m, s) = normal with mean m and standard deviation s):
 
-* tiny verify (C1): R=4, K=7, V=1024, fp32 target t ~ N(0, 2) of shape [R, K+1, V];
+* tiny verify: R=4, K=7, V=1024, fp32 target t ~ N(0, 2) of shape [R, K+1, V];
   draft d_{i,k} = t_{i,k-1} + N(0, 0.5); confidence sigmoid(N(1, 1)).
-* dense-vocab verify (C2): R=64, K=7, V=151,936, bf16; t ~ N(0, 3) plus 8 on an
+* dense-vocab verify: R=64, K=7, V=151,936, bf16; t ~ N(0, 3) plus 8 on an
   i.i.d. 1% of entries; d_{i,k} = t_{i,k-1} + sigma * eps with eps ~ N(0, 1) and
   sigma from ``calibration.json`` (chosen by a committed oracle script so the
   mean one-token acceptance is about 0.8).
-* scheduled ragged verify (C3): R=256, K=16, V=151,936, bf16; t as C2; a noise
+* scheduled ragged verify: R=256, K=16, V=151,936, bf16; t as the dense-vocab verify; a noise
   scale sigma_i ~ U(0.2, 2.0) per request (easy and hard streams);
   d = t + sigma_i * eps; confidence c_{i,k} = sigmoid(4 - 2.5 sigma_i + 0.25 eta),
   eta ~ N(0, 1) (a logistic model of the draft-target gap); additive cost table
   c(n) = 1.0 + 0.05 n.
-* Markov chain (C4): R=256, B=16, V=151,936, rank 256; L ~ N(0, 3) bf16;
+* Markov chain: R=256, B=16, V=151,936, rank 256; L ~ N(0, 3) bf16;
   U [V, r], W [r, V] ~ N(0, 0.02) bf16; anchors uniform over the vocabulary.
-* PCTree + tree verify (C5): R=128, D=16, V=129,280, rank 256, k=4, F=16, N=64;
-  L, U, W as C4; target logits for the root and each tree node ~ N(0, 3) bf16.
+* PCTree + tree verify: R=128, D=16, V=129,280, rank 256, k=4, F=16, N=64;
+  L, U, W as the Markov chain; target logits for the root and each tree node ~ N(0, 3) bf16.
 
 Draft tokens x_{i,k} are the synthetic draft model's samples from softmax(d/T)
 (Gumbel-max with this module's own noise), or argmax d when T = 0.
@@ -108,7 +108,7 @@ def confidences(rng, R, K, mean=1.0, std=1.0):
     return (1.0 / (1.0 + np.exp(-(mean + std * rng.standard_normal((R, K)))))).astype(np.float32)
 
 
-def c1():
+def tiny_verify():
     """Tiny verify: 4 requests, K=7, V=1024, fp32, Philox seed 0."""
     c = verify_case(4, 7, 1024, dtype="f32", seed=1001, t_sigma=2.0, d_sigma=0.5)
     c["conf"] = confidences(_rng(2001), 4, 7)
@@ -117,10 +117,10 @@ def c1():
     return c
 
 
-def c2(sigma=None):
+def dense_verify(sigma=None):
     """Dense-vocab verify: 64 requests, K=7, V=151,936, bf16, full-block windows."""
     if sigma is None:
-        sigma = calibration()["c2_sigma"]
+        sigma = calibration()["dense_verify_sigma"]
     c = verify_case(64, 7, V_QWEN3, dtype="bf16", seed=1002, t_sigma=3.0, boost_p=0.01,
                     boost=8.0, d_sigma=sigma)
     c["conf"] = confidences(_rng(2002), 64, 7)
@@ -132,8 +132,8 @@ def c2(sigma=None):
     return c
 
 
-def c3_schedule_inputs(R=256, K=16, V=V_QWEN3):
-    """Confidences, cost table and per-request noise scales of C3 (no logits)."""
+def scheduled_verify_inputs(R=256, K=16, V=V_QWEN3):
+    """Confidences, cost table and per-request noise scales of the scheduled verify (no logits)."""
     rng = _rng(2003)
     sig = rng.uniform(0.2, 2.0, size=R).astype(np.float32)
     eta = rng.standard_normal((R, K))
@@ -144,9 +144,9 @@ def c3_schedule_inputs(R=256, K=16, V=V_QWEN3):
                 anchors=_rng(3003).integers(0, V, size=R).astype(np.int32))
 
 
-def c3(R=256, K=16, V=V_QWEN3):
+def scheduled_verify(R=256, K=16, V=V_QWEN3):
     """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table."""
-    s = c3_schedule_inputs(R, K, V)
+    s = scheduled_verify_inputs(R, K, V)
     c = verify_case(R, K, V, dtype="bf16", seed=1003, t_sigma=3.0, boost_p=0.01, boost=8.0,
                     d_sigma=s["sigma_i"])
     c.update(s)
@@ -165,7 +165,7 @@ def markov_case(R, B, V, rank=256, seed=1004, l_sigma=3.0, w_sigma=0.02):
     return dict(L=L, U=U, W=W, anchors=anchors, R=R, B=B, V=V, rank=rank)
 
 
-def c4():
+def markov_chain():
     """Markov chain: 256 requests, 16 steps, V=151,936, rank 256."""
     return markov_case(256, 16, V_QWEN3, 256, seed=1004)
 
@@ -179,7 +179,7 @@ def tree_target(R, n_rows, V, seed, sigma=3.0):
     return out
 
 
-def c5():
+def pctree():
     """PCTree + tree verify: 128 requests, depth 16, V=129,280, k=4, F=16, N=64."""
     c = markov_case(128, 16, V_DSV4, 256, seed=1005)
     c.update(topk=4, frontier=16, topN=64)
