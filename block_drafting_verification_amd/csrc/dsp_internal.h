@@ -6,7 +6,7 @@
 #include <stdint.h>
 #include <stddef.h>
 
-#include "../../include/dsp.h"
+#include "dsp.h"
 
 namespace dsp {
 

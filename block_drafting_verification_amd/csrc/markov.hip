@@ -16,13 +16,17 @@
 // parent rows without any cross-lane traffic per tile; lanes, waves and column
 // groups are merged once at the end.
 //
-// Workgroup (512 threads, 8 waves as 2 vocab x 4 rows): one block of 256 parent
-// rows and a strided set of 128-token vocabulary tiles (tile g, g+G, ...), so a
-// Markov step over up to 256 requests streams Wt exactly once. The gathered
-// U rows of its parents (256 x rank bf16) stay in LDS for all tiles; Wt is
-// streamed through two 128 x 32 LDS chunks (double buffered). LDS rows are
-// XOR-swizzled at 16-byte granularity so the 32 rows read by one MFMA fragment
-// load hit distinct banks. Partial results per (column group, row) go to the
+// Workgroup (512 threads, 8 waves): 256 parent rows, one 32-row MFMA column
+// block per wave, and a contiguous range of 32-token vocabulary stages. Each
+// lane keeps its parent row's U fragments (the MFMA B operand) in registers for
+// the whole launch. Wt rows and the matching L entries of a stage arrive with
+// coalesced 16-byte loads into a ring of register buffers four stages deep, are
+// written to one of two LDS stage buffers and read back as MFMA A fragments
+// (Wt, XOR-swizzled at 16-byte granularity so the 8 rows of a fragment read hit
+// distinct bank groups) and as the epilogue's L values. One barrier per stage.
+// With more than 256 parent rows (the tree), the row blocks that share a
+// vocabulary range are placed on one XCD so the range's Wt is fetched into that
+// XCD's L2 once. Partial results per (vocabulary range, row) go to the
 // workspace; small merge kernels combine them.
 #include <math.h>
 
@@ -35,13 +39,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTV = 128;  // vocabulary entries per tile
-constexpr int kWR = 4;            // wavefronts along the parent-row axis
-constexpr int kTR = 64 * kWR;     // parent rows per workgroup (256)
-constexpr int kGT = 128 * kWR;    // threads per workgroup: 2 (vocab) x kWR (rows) wavefronts
-constexpr int kKC = 32;   // rank chunk staged per step
-constexpr int kTopK = 4;  // children tracked per parent
-constexpr int kTargetWGs = 256;  // one 512-thread workgroup per CU
+constexpr int kWaves = 8;
+constexpr int kGT = 64 * kWaves;  // threads per workgroup
+constexpr int kTR = 32 * kWaves;  // parent rows per workgroup: one 32-row MFMA column block per wave
+constexpr int kTS = 32;           // vocabulary entries per pipeline stage (one 32-row MFMA block)
+constexpr int kTopK = 4;          // children tracked per parent
+constexpr int kTargetWGs = 256;   // one workgroup per CU
 
 enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2 };
 
@@ -73,6 +76,8 @@ struct GemmArgs {
   int32_t rows, rows_per_req, G;
   void* part;              // ChainPart or TreePart [rows][G]
   int32_t* status;
+  int32_t nrb;             // row blocks of kTR rows
+  int32_t xcd_map;         // 1: row blocks of a slice share an XCD (G % 8 == 0)
 };
 
 // 16-byte slot of (row, vector) in a swizzled LDS tile whose rows hold `nv` vectors
@@ -117,323 +122,264 @@ __device__ __forceinline__ void merge_top4(float* va, int* ia, const float* vb, 
   }
 }
 
-template <int MODE>
+template <int MODE, int KS>
 __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
-  extern __shared__ u32x4 lds[];
+  constexpr int NV = 2 * KS;                  // 16-byte vectors per staged Wt row (rank padded to 16*KS)
+  constexpr int WST = kTS * NV;               // Wt vectors per stage
+  constexpr int WQ = (WST + kGT - 1) / kGT;   // Wt vectors loaded per thread per stage
+  constexpr int LST = kTR * 4;                // L vectors per stage: 256 rows x 32 tokens
+  constexpr int LQ = LST / kGT;               // L vectors loaded per thread per stage
+  constexpr int NR = KS <= 16 ? 4 : 2;        // stages in flight per thread (register ring)
+  static_assert(LST % kGT == 0, "L stage must split evenly over the workgroup");
+  extern __shared__ u32x4 lds[];              // [2][WST + LST]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave & 1, wr = wave >> 1;
-  const int g = blockIdx.x, rb = blockIdx.y;
-  const int r0 = rb * kTR;
-  const int nvu = a.rank / 8;     // 16-byte vectors per U row
-  u32x4* Us = lds;                // [kTR][nvu] swizzled
-  u32x4* Ws = lds + kTR * nvu;    // [2][kTV][4] swizzled
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // gather U rows of this block's parents
-  for (int e = tid; e < kTR * nvu; e += kGT) {
-    const int rr = e / nvu, kv = e % nvu;
-    const int r = r0 + rr;
-    u32x4 val = zero4;
-    if (r < a.rows) {
-      int tok = a.row_tok[(size_t)r * a.ld_tok];
+  // workgroup -> (vocabulary slice g, row block rb). With several row blocks, the
+  // blocks sharing a slice get ids congruent mod 8 (one XCD) and adjacent in dispatch
+  // order, so the slice's Wt lines are fetched once into that XCD's L2.
+  int g, rb;
+  {
+    const int id = blockIdx.x;
+    if (a.xcd_map) {
+      const int j = id >> 3;
+      g = (j / a.nrb) * 8 + (id & 7);
+      rb = j % a.nrb;
+    } else {
+      g = id % a.G;
+      rb = id / a.G;
+    }
+  }
+  const int r0 = rb * kTR;
+  const int nst_all = (a.V + kTS - 1) / kTS;
+  const int s_begin = (int)(((long)g * nst_all) / a.G);
+  const int nst = (int)(((long)(g + 1) * nst_all) / a.G) - s_begin;
+
+  // B operand: this lane's parent row (one per lane pair) and its U row, held in
+  // registers for the whole launch: k-step ks covers rank 16ks + 8*(lane/32) .. +8
+  const int nloc = wave * 32 + (lane & 31);
+  const int row = r0 + nloc;
+  const bool rvalid = row < a.rows;
+  bf16x8 ufr[KS];
+  {
+    int tok = 0;
+    if (rvalid) {
+      tok = a.row_tok[(size_t)row * a.ld_tok];
       if (tok < 0 || tok >= a.V) {
-        if (kv == 0 && g == 0) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+        if (g == 0 && lane < 32) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
         tok = 0;
       }
-      val = *(const u32x4*)(a.U + (size_t)tok * a.rank + kv * 8);
     }
-    Us[swz(rr, kv, nvu)] = val;
+    const uint16_t* up = a.U + (size_t)tok * a.rank + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = zero4;
+      if (rvalid && 16 * ks + 8 * (lane >> 5) < a.rank) v = *(const u32x4*)(up + 16 * ks);
+      ufr[ks] = __builtin_bit_cast(bf16x8, v);
+    }
   }
 
-  // per-lane state for parent rows j = 0, 1 (row r0 + wr*64 + j*32 + lane%32)
-  float best[2] = {-INFINITY, -INFINITY};
-  int bidx[2] = {0x7fffffff, 0x7fffffff};
-  float tv[2][kTopK];
-  int ti[2][kTopK];
-  float lref[2] = {-INFINITY, -INFINITY};
-  double lsum[2] = {0.0, 0.0};
+  // rows whose L vectors this thread stages: row (tid + q*kGT) / 4, 16-byte column tid % 4
+  const uint16_t* lrow[LQ];
+  bool lok[LQ], lal[LQ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int q = 0; q < kTopK; ++q) {
-      tv[j][q] = -INFINITY;
-      ti[j][q] = 0x7fffffff;
-    }
-
-  const uint16_t* Lrow[2];
-  bool rvalid[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = r0 + wr * 64 + j * 32 + (lane & 31);
-    rvalid[j] = r < a.rows;
-    const int req = rvalid[j] ? r / a.rows_per_req : 0;
-    Lrow[j] = a.L + (size_t)req * a.ldL_r + (size_t)a.d * a.ldL_d;
+  for (int q = 0; q < LQ; ++q) {
+    const int rr = r0 + ((tid + q * kGT) >> 2);
+    lok[q] = rr < a.rows;
+    const int req = lok[q] ? rr / a.rows_per_req : 0;
+    lrow[q] = a.L + (size_t)req * a.ldL_r + (size_t)a.d * a.ldL_d;
+    lal[q] = (((uintptr_t)lrow[q]) & 15u) == 0;
   }
-
-  const int ncb = (a.V + kTV - 1) / kTV;
-  const int nkc = a.rank / kKC;
-  const int my_tiles = g < ncb ? (ncb - g + a.G - 1) / a.G : 0;
-  const int nsteps = my_tiles * nkc;  // (tile, rank chunk) pairs streamed by this workgroup
-  bool l_al[2];
+  auto load_stage = [&](int s, u32x4* rw, u32x4* rl) {
+    const int v0 = (s_begin + s) * kTS;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) l_al[j] = (((uintptr_t)Lrow[j]) & 7u) == 0;
-
-  // Wt chunk of step st: 128 tokens x 32 rank values = 512 16-byte vectors over the workgroup
-  constexpr int kWQ = (kTV * 4) / kGT;  // vectors per thread (1)
-  auto load_w = [&](int st, u32x4* r) {
-    const int t = st / nkc, kc = st - t * nkc;
-    const int v0 = (g + t * a.G) * kTV;
-#pragma unroll
-    for (int q = 0; q < kWQ; ++q) {
+    for (int q = 0; q < WQ; ++q) {
       const int e = tid + q * kGT;
-      const int vv = e >> 2, kv = e & 3;
+      const int vv = e / NV, kv = e % NV;
       const int v = v0 + vv;
-      r[q] = v < a.V ? *(const u32x4*)(a.Wt + (size_t)v * a.rank + kc * kKC + kv * 8) : zero4;
+      rw[q] = (e < WST && v < a.V && kv * 8 < a.rank) ? *(const u32x4*)(a.Wt + (size_t)v * a.rank + kv * 8)
+                                                     : zero4;
     }
-  };
-  auto store_w = [&](int buf, const u32x4* r) {
 #pragma unroll
-    for (int q = 0; q < kWQ; ++q) {
-      const int e = tid + q * kGT;
-      const int vv = e >> 2, kv = e & 3;
-      Ws[buf * kTV * 4 + vv * 4 + (kv ^ ((vv >> 1) & 3))] = r[q];
-    }
-  };
-  // L values of this lane for tile v0, as bf16 pairs: [row j][vocab block i][group h]
-  uint2 lpre[2][2][4];
-  auto load_l = [&](int v0) {
-    const bool full = v0 + kTV <= a.V;
+    for (int q = 0; q < LQ; ++q) {
+      const int v = v0 + 8 * (tid & 3);
+      u32x4 w = zero4;
+      if (lok[q]) {
+        if (lal[q] && v + 8 <= a.V) {
+          w = *(const u32x4*)(lrow[q] + v);
+        } else {
+          uint32_t e[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int v = v0 + wv * 64 + i * 32 + 8 * h + 4 * (lane >> 5);
-          uint2 w = {0u, 0u};
-          if (rvalid[j]) {
-            if (full && l_al[j]) {
-              w = *(const uint2*)(Lrow[j] + v);
-            } else {
-              uint32_t e[4];
-#pragma unroll
-              for (int l = 0; l < 4; ++l) e[l] = v + l < a.V ? (uint32_t)Lrow[j][v + l] : 0u;
-              w.x = e[0] | (e[1] << 16);
-              w.y = e[2] | (e[3] << 16);
-            }
-          }
-          lpre[j][i][h] = w;
+          for (int l = 0; l < 8; ++l) e[l] = v + l < a.V ? (uint32_t)lrow[q][v + l] : 0u;
+          w.x = e[0] | (e[1] << 16);
+          w.y = e[2] | (e[3] << 16);
+          w.z = e[4] | (e[5] << 16);
+          w.w = e[6] | (e[7] << 16);
         }
+      }
+      rl[q] = w;
+    }
+  };
+  // LDS layouts. Wt stage: token row m holds NV vectors, vector kv at m*NV + swz_w(m, kv);
+  // the 8 rows read together by one MFMA fragment load land on 8 distinct 16-byte
+  // bank groups. L stage: row n holds 4 vectors, vector c at n*4 + (c ^ ((n >> 1) & 3)).
+  auto swz_w = [](int m, int kv) {
+    return NV >= 8 ? ((kv & ~7) | ((kv ^ m) & 7)) : ((kv & ~3) | ((kv ^ (m >> 1)) & 3));
+  };
+  auto store_stage = [&](int b, const u32x4* rw, const u32x4* rl) {
+    u32x4* Ws = lds + b * (WST + LST);
+    u32x4* Ls = Ws + WST;
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
+      const int e = tid + q * kGT;
+      if (e < WST) {
+        const int vv = e / NV, kv = e % NV;
+        Ws[vv * NV + swz_w(vv, kv)] = rw[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) {
+      const int n = (tid + q * kGT) >> 2, c = tid & 3;
+      Ls[n * 4 + (c ^ ((n >> 1) & 3))] = rl[q];
     }
   };
 
-  constexpr int kRing = MODE == MODE_ARGMAX ? 4 : 2;  // Wt chunks in flight per thread
-  u32x4 wring[kRing][kWQ];
+  // per-lane running state of this lane's parent row
+  float best = -INFINITY;
+  int bidx = 0x7fffffff;
+  float tv[kTopK];
+  int ti[kTopK];
 #pragma unroll
-  for (int p = 0; p < kRing; ++p)
-    if (p < nsteps) load_w(p, wring[p]);
-  f32x16 acc[2][2];
-  for (int base = 0; base < nsteps; base += kRing) {
+  for (int q = 0; q < kTopK; ++q) {
+    tv[q] = -INFINITY;
+    ti[q] = 0x7fffffff;
+  }
+  float lref = -INFINITY;
+  double lsum = 0.0;
+
+  u32x4 ringw[NR][WQ], ringl[NR][LQ];
 #pragma unroll
-    for (int p = 0; p < kRing; ++p) {
-      const int st = base + p;
-      if (st >= nsteps) break;  // uniform over the workgroup
-      const int t = st / nkc, kc = st - t * nkc;
-      const int v0 = (g + t * a.G) * kTV;
-      if (kc == 0) {
+  for (int p = 0; p < NR; ++p)
+    if (p < nst) load_stage(p, ringw[p], ringl[p]);
+
+  for (int base = 0; base < nst; base += NR) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-        load_l(v0);
-      }
-      // buffer st&1 was last read two steps ago, before the previous barrier
-      store_w(st & 1, wring[p]);
+    for (int p = 0; p < NR; ++p) {
+      const int s = base + p;
+      if (s >= nst) break;  // uniform over the workgroup
+      const int b = p & 1;  // NR is even, so s & 1 == p & 1
+      // buffer b was last read two stages ago, before the previous barrier
+      store_stage(b, ringw[p], ringl[p]);
       __syncthreads();
-      if (st + kRing < nsteps) load_w(st + kRing, wring[p]);
-      const u32x4* Wb = Ws + (st & 1) * kTV * 4;
+      if (s + NR < nst) load_stage(s + NR, ringw[p], ringl[p]);
+      const u32x4* Ws = lds + b * (WST + LST);
+      const u32x4* Ls = Ws + WST;
+      f32x16 acc;
 #pragma unroll
-      for (int ks = 0; ks < kKC / 16; ++ks) {
-        bf16x8 af[2], bu[2];
+      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int vv = wv * 64 + i * 32 + (lane & 31);
-          const int kv = ks * 2 + (lane >> 5);
-          u32x4 tw = Wb[vv * 4 + (kv ^ ((vv >> 1) & 3))];
-          af[i] = __builtin_bit_cast(bf16x8, tw);
-          const int rr = wr * 64 + i * 32 + (lane & 31);
-          u32x4 tu = Us[swz(rr, kc * (kKC / 8) + kv, nvu)];
-          bu[i] = __builtin_bit_cast(bf16x8, tu);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bu[j], acc[i][j], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int m = lane & 31, kv = 2 * ks + (lane >> 5);
+        const bf16x8 af = __builtin_bit_cast(bf16x8, Ws[m * NV + swz_w(m, kv)]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ufr[ks], acc, 0, 0, 0);
       }
-      if (kc != nkc - 1) continue;
-      // epilogue: lane holds, for parent row j, tokens v0 + wv*64 + i*32 + 8*h + 4*(lane/32) + l,
-      // visited in increasing token order; z = acc + L is formed on the fly (twice when the
-      // log-sum-exp is needed) instead of being kept in registers
+      if (!rvalid) continue;
+      // accumulator a of this lane is token v0 + 8*(a/4) + 4*(lane/32) + a%4 of its row:
+      // visited in increasing token order; z = acc + L
+      const int v0 = (s_begin + s) * kTS;
+      const char* lb = (const char*)(Ls + nloc * 4) + 8 * (lane >> 5);
+      float z[16];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!rvalid[j]) continue;
-        float tmax = -INFINITY;
+      for (int h = 0; h < 4; ++h) {
+        const uint2 w = *(const uint2*)(lb + 16 * (h ^ ((nloc >> 1) & 3)));
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-          const int i = q >> 4, h = (q >> 2) & 3, l = q & 3;
-          const int v = v0 + wv * 64 + i * 32 + 8 * h + 4 * (lane >> 5) + l;
-          const uint32_t w = l < 2 ? lpre[j][i][h].x : lpre[j][i][h].y;
-          const float zz = v < a.V ? acc[i][j][4 * h + l] + ((l & 1) ? bf16_hi(w) : bf16_lo(w)) : -INFINITY;
-          tmax = fmaxf(tmax, zz);
-          if (MODE == MODE_TREE) {
-            if (zz > tv[j][kTopK - 1]) {
-              tv[j][kTopK - 1] = zz;
-              ti[j][kTopK - 1] = v;
+        for (int l = 0; l < 4; ++l) {
+          const int v = v0 + 8 * h + 4 * (lane >> 5) + l;
+          const uint32_t ww = l < 2 ? w.x : w.y;
+          z[4 * h + l] = v < a.V ? acc[4 * h + l] + ((l & 1) ? bf16_hi(ww) : bf16_lo(ww)) : -INFINITY;
+        }
+      }
+      float tmax = -INFINITY;
 #pragma unroll
-              for (int p = kTopK - 1; p > 0; --p) {
-                if (tv[j][p] > tv[j][p - 1]) {
-                  const float fv = tv[j][p]; tv[j][p] = tv[j][p - 1]; tv[j][p - 1] = fv;
-                  const int iv = ti[j][p]; ti[j][p] = ti[j][p - 1]; ti[j][p - 1] = iv;
-                }
+      for (int q = 0; q < 16; ++q) {
+        const int v = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        tmax = fmaxf(tmax, z[q]);
+        if (MODE == MODE_TREE) {
+          if (z[q] > tv[kTopK - 1]) {
+            tv[kTopK - 1] = z[q];
+            ti[kTopK - 1] = v;
+#pragma unroll
+            for (int p2 = kTopK - 1; p2 > 0; --p2) {
+              if (tv[p2] > tv[p2 - 1]) {
+                const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
+                const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
               }
             }
-          } else if (zz > best[j]) {
-            best[j] = zz;
-            bidx[j] = v;
           }
+        } else if (z[q] > best) {
+          best = z[q];
+          bidx = v;
         }
-        if (MODE != MODE_ARGMAX && tmax != -INFINITY) {
-          const float nref = fmaxf(lref[j], tmax * kLog2e);
-          float ts = 0.f;
+      }
+      if (MODE != MODE_ARGMAX && tmax != -INFINITY) {
+        const float nref = fmaxf(lref, tmax * kLog2e);
+        float ts = 0.f;
 #pragma unroll
-          for (int q = 0; q < 32; ++q) {
-            const int i = q >> 4, h = (q >> 2) & 3, l = q & 3;
-            const int v = v0 + wv * 64 + i * 32 + 8 * h + 4 * (lane >> 5) + l;
-            const uint32_t w = l < 2 ? lpre[j][i][h].x : lpre[j][i][h].y;
-            const float zz = acc[i][j][4 * h + l] + ((l & 1) ? bf16_hi(w) : bf16_lo(w));
-            ts += v < a.V ? fast_exp2(__builtin_fmaf(zz, kLog2e, -nref)) : 0.f;
-          }
-          const double scale = lref[j] == -INFINITY ? 0.0 : (double)fast_exp2(lref[j] - nref);
-          lsum[j] = lsum[j] * scale + (double)ts;
-          lref[j] = nref;
-        }
+        for (int q = 0; q < 16; ++q) ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));  // exp2(-inf) = 0
+        const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
+        lsum = lsum * scale + (double)ts;
+        lref = nref;
       }
     }
   }
 
-  // merge lane pairs (lane, lane ^ 32 hold the same parent rows)
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (MODE == MODE_TREE) {
-      float ov[kTopK];
-      int oi[kTopK];
-#pragma unroll
-      for (int q = 0; q < kTopK; ++q) {
-        ov[q] = __shfl_xor(tv[j][q], 32, 64);
-        oi[q] = __shfl_xor(ti[j][q], 32, 64);
-      }
-      merge_top4(tv[j], ti[j], ov, oi);
-    } else {
-      const float ob = __shfl_xor(best[j], 32, 64);
-      const int oi = __shfl_xor(bidx[j], 32, 64);
-      if (ob > best[j] || (ob == best[j] && oi < bidx[j])) {
-        best[j] = ob;
-        bidx[j] = oi;
-      }
-    }
-    if (MODE != MODE_ARGMAX) {
-      const float oref = __shfl_xor(lref[j], 32, 64);
-      const double osum = __shfl_xor(lsum[j], 32, 64);
-      const float nref = fmaxf(lref[j], oref);
-      double s = 0.0;
-      if (lref[j] != -INFINITY) s += lsum[j] * exp2((double)lref[j] - (double)nref);
-      if (oref != -INFINITY) s += osum * exp2((double)oref - (double)nref);
-      lref[j] = nref;
-      lsum[j] = s;
-    }
-  }
-
-  // merge the two vocabulary waves (wv = 0, 1) through LDS, then write partials
-  __syncthreads();
+  // merge lane pairs (lane, lane ^ 32 hold the same parent row), then lanes < 32 write
   if (MODE == MODE_TREE) {
-    TreePart* xs = (TreePart*)lds;  // [kWR (wr)][64 rows]
-    if (wv == 1 && lane < 32) {
+    float ov[kTopK];
+    int oi[kTopK];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        TreePart p;
-#pragma unroll
-        for (int q = 0; q < kTopK; ++q) {
-          p.val[q] = tv[j][q];
-          p.idx[q] = ti[j][q];
-        }
-        p.ref = lref[j];
-        p.pad = 0.f;
-        p.sum = lsum[j];
-        xs[wr * 64 + j * 32 + lane] = p;
-      }
+    for (int q = 0; q < kTopK; ++q) {
+      ov[q] = __shfl_xor(tv[q], 32, 64);
+      oi[q] = __shfl_xor(ti[q], 32, 64);
     }
-    __syncthreads();
-    if (wv == 0 && lane < 32) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = r0 + wr * 64 + j * 32 + lane;
-        if (r >= a.rows) continue;
-        const TreePart o = xs[wr * 64 + j * 32 + lane];
-        TreePart p;
-        merge_top4(tv[j], ti[j], o.val, o.idx);
-#pragma unroll
-        for (int q = 0; q < kTopK; ++q) {
-          p.val[q] = tv[j][q];
-          p.idx[q] = ti[j][q];
-        }
-        const float nref = fmaxf(lref[j], o.ref);
-        double s = 0.0;
-        if (lref[j] != -INFINITY) s += lsum[j] * exp2((double)lref[j] - (double)nref);
-        if (o.ref != -INFINITY) s += o.sum * exp2((double)o.ref - (double)nref);
-        p.ref = nref;
-        p.pad = 0.f;
-        p.sum = s;
-        ((TreePart*)a.part)[(size_t)r * a.G + g] = p;
-      }
-    }
+    merge_top4(tv, ti, ov, oi);
   } else {
-    ChainPart* xs = (ChainPart*)lds;
-    if (wv == 1 && lane < 32) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        ChainPart p;
-        p.key = bidx[j] == 0x7fffffff ? 0ull : amax_key(best[j], (uint32_t)bidx[j]);
-        p.ref = lref[j];
-        p.pad = 0.f;
-        p.sum = lsum[j];
-        xs[wr * 64 + j * 32 + lane] = p;
-      }
+    const float ob = __shfl_xor(best, 32, 64);
+    const int oi = __shfl_xor(bidx, 32, 64);
+    if (ob > best || (ob == best && oi < bidx)) {
+      best = ob;
+      bidx = oi;
     }
-    __syncthreads();
-    if (wv == 0 && lane < 32) {
+  }
+  if (MODE != MODE_ARGMAX) {
+    const float oref = __shfl_xor(lref, 32, 64);
+    const double osum = __shfl_xor(lsum, 32, 64);
+    const float nref = fmaxf(lref, oref);
+    double s = 0.0;
+    if (lref != -INFINITY) s += lsum * exp2((double)lref - (double)nref);
+    if (oref != -INFINITY) s += osum * exp2((double)oref - (double)nref);
+    lref = nref;
+    lsum = s;
+  }
+  if (lane >= 32 || !rvalid) return;
+  if (MODE == MODE_TREE) {
+    TreePart p;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = r0 + wr * 64 + j * 32 + lane;
-        if (r >= a.rows) continue;
-        const ChainPart o = xs[wr * 64 + j * 32 + lane];
-        ChainPart p;
-        const uint64_t k0 = bidx[j] == 0x7fffffff ? 0ull : amax_key(best[j], (uint32_t)bidx[j]);
-        p.key = k0 > o.key ? k0 : o.key;
-        const float nref = fmaxf(lref[j], o.ref);
-        double s = 0.0;
-        if (MODE != MODE_ARGMAX) {
-          if (lref[j] != -INFINITY) s += lsum[j] * exp2((double)lref[j] - (double)nref);
-          if (o.ref != -INFINITY) s += o.sum * exp2((double)o.ref - (double)nref);
-        }
-        p.ref = nref;
-        p.pad = 0.f;
-        p.sum = s;
-        ((ChainPart*)a.part)[(size_t)r * a.G + g] = p;
-      }
+    for (int q = 0; q < kTopK; ++q) {
+      p.val[q] = tv[q];
+      p.idx[q] = ti[q];
     }
+    p.ref = lref;
+    p.pad = 0.f;
+    p.sum = lsum;
+    ((TreePart*)a.part)[(size_t)row * a.G + g] = p;
+  } else {
+    ChainPart p;
+    p.key = bidx == 0x7fffffff ? 0ull : amax_key(best, (uint32_t)bidx);
+    p.ref = lref;
+    p.pad = 0.f;
+    p.sum = MODE == MODE_ARGMAX ? 0.0 : lsum;
+    ((ChainPart*)a.part)[(size_t)row * a.G + g] = p;
   }
 }
 
@@ -654,30 +600,49 @@ __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
   if (tid == 0) a.n_nodes[i] = nout;
 }
 
-size_t gemm_lds_bytes(int rank) { return (size_t)(kTR * (rank / 8) + 2 * kTV * 4) * 16; }
-static_assert((kTV * 4) % kGT == 0, "Wt chunk must split evenly over the workgroup");
+// k-steps of 16 for a rank (rank padded with zeros to a power of two >= 32)
+int ksteps(int rank) {
+  int ks = 2;
+  while (16 * ks < rank) ks *= 2;
+  return ks;
+}
+
+size_t gemm_lds_bytes(int ks) { return (size_t)2 * (kTS * 2 * ks + kTR * 4) * 16; }
 
 int pick_groups(int rows, int V) {
   const int nrb = (rows + kTR - 1) / kTR;
-  const int ncb = (V + kTV - 1) / kTV;
+  const int nst = (V + kTS - 1) / kTS;
   int G = (kTargetWGs + nrb - 1) / nrb;
-  if (G > ncb) G = ncb;
+  if (nrb > 1 && G >= 8) G = G / 8 * 8;
+  if (G > nst) G = nst;
   if (G < 1) G = 1;
   return G;
 }
 
-template <int MODE>
-int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
-  const size_t lds = gemm_lds_bytes(a.rank);
+template <int MODE, int KS>
+int32_t launch_gemm_ks(int kid, GemmArgs a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)markov_gemm_kernel<MODE>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)markov_gemm_kernel<MODE, KS>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  dim3 grid(a.G, (a.rows + kTR - 1) / kTR);
-  launch(kid, markov_gemm_kernel<MODE>, grid, dim3(kGT), (uint32_t)lds, s, a);
+  a.nrb = (a.rows + kTR - 1) / kTR;
+  a.xcd_map = a.nrb > 1 && a.G % 8 == 0;
+  launch(kid, markov_gemm_kernel<MODE, KS>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT),
+         (uint32_t)gemm_lds_bytes(KS), s, a);
   return hip_check(hipGetLastError(), "markov gemm launch");
+}
+
+template <int MODE>
+int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
+  switch (ksteps(a.rank)) {
+    case 2: return launch_gemm_ks<MODE, 2>(kid, a, s);
+    case 4: return launch_gemm_ks<MODE, 4>(kid, a, s);
+    case 8: return launch_gemm_ks<MODE, 8>(kid, a, s);
+    case 16: return launch_gemm_ks<MODE, 16>(kid, a, s);
+    default: return launch_gemm_ks<MODE, 32>(kid, a, s);
+  }
 }
 
 int32_t check_markov_common(const void* L, int32_t l_dtype, const void* U, const void* Wt, int32_t V,

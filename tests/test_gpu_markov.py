@@ -56,7 +56,7 @@ def _check_chain(c, requests=None, want_logq=True, w_boost=1.0):
 
 
 @pytest.mark.parametrize("R,B,V,rank", [(5, 4, 1000, 32), (130, 3, 4099, 64), (7, 5, 30000, 256),
-                                        (300, 2, 129, 96)])
+                                        (300, 2, 129, 96), (3, 2, 2000, 512), (600, 2, 9000, 128)])
 def test_chain_small(R, B, V, rank):
     c = workloads.markov_case(R, B, V, rank=rank, seed=R + V)
     _check_chain(c, w_boost=300.0)  # a Markov term large enough to change choices
@@ -115,7 +115,8 @@ def _check_tree(c, topk, F, N, requests=None, w_boost=1.0):
 
 
 @pytest.mark.parametrize("R,D,V,k,F,N,rank", [(3, 4, 700, 2, 3, 8, 32), (9, 6, 5003, 4, 16, 64, 64),
-                                              (2, 3, 40000, 4, 16, 20, 256), (140, 2, 300, 3, 5, 7, 32)])
+                                              (2, 3, 40000, 4, 16, 20, 256), (140, 2, 300, 3, 5, 7, 32),
+                                              (20, 3, 40000, 4, 16, 30, 64)])
 def test_tree_small(R, D, V, k, F, N, rank):
     c = workloads.markov_case(R, D, V, rank=rank, seed=7 * R + V)
     _check_tree(c, k, F, N, w_boost=200.0)
