@@ -11,6 +11,7 @@ instructions are disabled.
 import concurrent.futures
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -30,14 +31,38 @@ FLAGS = [
 ]
 
 
+# Kernels whose streaming loads are issued asynchronously from inline assembly must not
+# spill registers (a spill could copy a register before its load lands): the Markov GEMM
+# instantiations with rank up to 256 (k-steps 2..16).
+ASYNC_KERNELS = re.compile(r"markov_gemm_kernelILi\dELi(2|4|8|16)ELb[01]E")
+
+
+def _spills(stderr):
+    """(function, vgpr spills + scratch bytes per lane) from hipcc's kernel-resource-usage
+    remarks: either means values may live in memory instead of registers."""
+    out, name = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            out.setdefault(name, 0)
+        m = re.search(r"(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and name:
+            out[name] += int(m.group(2))
+    return list(out.items())
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "remark:")
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    bad = [(n, c) for n, c in _spills(r.stderr or "") if c and ASYNC_KERNELS.search(n)]
+    if bad:
+        raise RuntimeError(f"{src}: kernels with asynchronous loads spill or use scratch: {bad}")
     return obj, err
 
 

@@ -102,7 +102,7 @@ extern "C" int32_t dsp_prof_enable(int32_t mask) {
 
 extern "C" int32_t dsp_prof_reset(void) {
   for (auto& r : g_prof_recs) {
-    hipEventSynchronize(r.b);
+    (void)hipEventSynchronize(r.b);
     g_prof_pool.push_back(r.a);
     g_prof_pool.push_back(r.b);
   }

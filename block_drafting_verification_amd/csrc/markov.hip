@@ -20,7 +20,7 @@
 // block per wave, and a contiguous range of 32-token vocabulary stages. Each
 // lane keeps its parent row's U fragments (the MFMA B operand) in registers for
 // the whole launch. Wt rows and the matching L entries of a stage arrive with
-// coalesced 16-byte loads into a ring of register buffers four stages deep, are
+// bounds-checked 16-byte buffer loads into a ring of register buffers three stages deep, are
 // written to one of two LDS stage buffers and read back as MFMA A fragments
 // (Wt, XOR-swizzled at 16-byte granularity so the 8 rows of a fragment read hit
 // distinct bank groups) and as the epilogue's L values. One barrier per stage.
@@ -47,6 +47,55 @@ constexpr int kTopK = 4;          // children tracked per parent
 constexpr int kTargetWGs = 256;   // one workgroup per CU
 
 enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2 };
+
+// ---------------------------------------------------------------- streaming loads
+// The stage ring is fed by raw buffer loads issued from inline assembly with explicit
+// s_waitcnt vmcnt(N): the compiler's own wait insertion cannot follow loads carried
+// around a loop in a register ring and drains every load in flight at the loop edge,
+// which turns a 4-deep pipeline into a stop-and-go one. A buffer descriptor holds a
+// base and a byte extent; the hardware returns zero for any offset at or past the
+// extent, so out-of-range lanes take an offset past every extent and need no branch.
+typedef uint32_t s32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;  // past every extent (extents are < 2^31 bytes)
+
+__device__ __forceinline__ s32x4 make_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  s32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);  // stride 0
+  d.z = __builtin_amdgcn_readfirstlane(bytes);
+  d.w = 0x00020000u;  // 32-bit data format, as for every gfx9 buffer access
+  return d;
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(const s32x4& d) {
+  void* base = (void*)(((uint64_t)d.y << 32) | d.x);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)d.z, (int)d.w);
+}
+// ASYNC: the inline-assembly form, whose result must not be read before a vm_wait that
+// covers it. Otherwise the compiler's own buffer load (it waits where needed). Kernels
+// that spill registers must use the latter: a spill could copy a register whose load
+// has not landed.
+// The destination is a read-write operand: the register then stays bound to its ring
+// slot for the whole loop, so the compiler never hands it to another value while a
+// load into it is still in flight.
+template <bool ASYNC>
+__device__ __forceinline__ void buf_load_x4(u32x4& v, const s32x4& d, uint32_t off) {
+  if (ASYNC)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "+v"(v) : "v"(off), "s"(d) : "memory");
+  else
+    v = __builtin_amdgcn_raw_buffer_load_b128(as_rsrc(d), off, 0, 0);
+}
+template <bool ASYNC>
+__device__ __forceinline__ void buf_load_u16(uint32_t& v, const s32x4& d, uint32_t off) {
+  if (ASYNC)
+    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "+v"(v) : "v"(off), "s"(d) : "memory");
+  else
+    v = __builtin_amdgcn_raw_buffer_load_b16(as_rsrc(d), off, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 struct ChainPart {  // per (group, row)
   uint64_t key;     // arg-max key of z (fp32), lowest id on ties
@@ -122,18 +171,20 @@ __device__ __forceinline__ void merge_top4(float* va, int* ia, const float* vb, 
   }
 }
 
-template <int MODE, int KS>
+template <int MODE, int KS, bool LAL>
 __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   constexpr int NV = 2 * KS;                  // 16-byte vectors per staged Wt row (rank padded to 16*KS)
   constexpr int WST = kTS * NV;               // Wt vectors per stage
   constexpr int WQ = (WST + kGT - 1) / kGT;   // Wt vectors loaded per thread per stage
   constexpr int LST = kTR * 4;                // L vectors per stage: 256 rows x 32 tokens
   constexpr int LQ = LST / kGT;               // L vectors loaded per thread per stage
-  constexpr int NR = KS <= 16 ? 4 : 2;        // stages in flight per thread (register ring)
+  constexpr int NR = KS <= 16 && LAL ? 3 : 2;  // stages in flight per thread (register ring)
+  constexpr int NU = NR % 2 ? 2 * NR : NR;     // stages per unrolled loop body (ring slot and
+                                               // buffer parity both static)
+  constexpr bool AS = KS <= 16;               // asynchronous ring loads (kernels that do not spill)
   static_assert(LST % kGT == 0, "L stage must split evenly over the workgroup");
   extern __shared__ u32x4 lds[];              // [2][WST + LST]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   // workgroup -> (vocabulary slice g, row block rb). With several row blocks, the
   // blocks sharing a slice get ids congruent mod 8 (one XCD) and adjacent in dispatch
@@ -160,6 +211,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   const int nloc = wave * 32 + (lane & 31);
   const int row = r0 + nloc;
   const bool rvalid = row < a.rows;
+  const bool all_rows = r0 + kTR <= a.rows;  // every row of the block is a parent row
   bf16x8 ufr[KS];
   {
     int tok = 0;
@@ -170,63 +222,77 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         tok = 0;
       }
     }
-    const uint16_t* up = a.U + (size_t)tok * a.rank + 8 * (lane >> 5);
+    // issued like the ring's loads (the compiler would otherwise keep them "pending" around
+    // the stage loop and drain the ring for them); the first stage's wait covers them
+    const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)a.V * a.rank * 2));
+    const uint32_t ubase = (uint32_t)(((size_t)tok * a.rank + 8 * (lane >> 5)) * 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = zero4;
-      if (rvalid && 16 * ks + 8 * (lane >> 5) < a.rank) v = *(const u32x4*)(up + 16 * ks);
-      ufr[ks] = __builtin_bit_cast(bf16x8, v);
+      const bool ok = rvalid && 16 * ks + 8 * (lane >> 5) < a.rank;
+      u32x4 u = {0u, 0u, 0u, 0u};
+      buf_load_x4<AS>(u, udesc, ok ? ubase + 32 * ks : kOOB);
+      ufr[ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
 
-  // rows whose L vectors this thread stages: row (tid + q*kGT) / 4, 16-byte column tid % 4
-  const uint16_t* lrow[LQ];
-  bool lok[LQ], lal[LQ];
+  // L rows staged by this thread: row (tid + q*kGT) / 4, 16-byte column tid % 4, addressed
+  // from the first request of this row block (spans checked on the host)
+  const s32x4 wdesc = make_desc(a.Wt, (uint32_t)((size_t)a.V * a.rank * 2));
+  const int req0 = r0 / a.rows_per_req;
+  const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
+  const s32x4 ldesc = make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
+                                (uint32_t)(((size_t)(rlast / a.rows_per_req - req0) * a.ldL_r + a.V) * 2));
+  // Byte offsets of this thread's loads, less a per-stage term that is uniform over the
+  // workgroup. Entries that are never valid (rank padding, spare threads, rows past the
+  // block) start at kOOB; a stage past the range gets the term kOOB. Either way the sum
+  // lies past the extent (extents and live terms are below 2^31) and the load reads zero,
+  // as does a live stage's entry whose token is past V (offset past the Wt extent), while
+  // an L entry past V of a row reads the next row's start or zero: masked at use.
+  uint32_t wofs[WQ], lofs[LQ];
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int e = tid + q * kGT;
+    const int vv = e / NV, kv = e % NV;
+    wofs[q] = e < WST && kv * 8 < a.rank ? (uint32_t)((vv * a.rank + kv * 8) * 2) : kOOB;
+  }
 #pragma unroll
   for (int q = 0; q < LQ; ++q) {
     const int rr = r0 + ((tid + q * kGT) >> 2);
-    lok[q] = rr < a.rows;
-    const int req = lok[q] ? rr / a.rows_per_req : 0;
-    lrow[q] = a.L + (size_t)req * a.ldL_r + (size_t)a.d * a.ldL_d;
-    lal[q] = (((uintptr_t)lrow[q]) & 15u) == 0;
+    lofs[q] = rr < a.rows ? (uint32_t)(((size_t)(rr / a.rows_per_req - req0) * a.ldL_r + 8 * (tid & 3)) * 2)
+                          : kOOB;
   }
-  auto load_stage = [&](int s, u32x4* rw, u32x4* rl) {
-    const int v0 = (s_begin + s) * kTS;
+  // Every thread issues the same LPS loads for every stage, including the stages past
+  // its range: the count of loads in flight is then a constant the ring's waits can name.
+  constexpr int LPS = WQ + LQ * (LAL ? 1 : 8);  // loads per stage per thread
+  auto load_stage = [&](int s, u32x4* rw, u32x4* rl, uint32_t (*ru)[8]) {
+    const bool live = s < nst;
+    const uint32_t tw = live ? (uint32_t)((size_t)(s_begin + s) * kTS * a.rank * 2) : kOOB;
+    const uint32_t tl = live ? (uint32_t)((s_begin + s) * kTS * 2) : kOOB;
 #pragma unroll
-    for (int q = 0; q < WQ; ++q) {
-      const int e = tid + q * kGT;
-      const int vv = e / NV, kv = e % NV;
-      const int v = v0 + vv;
-      rw[q] = (e < WST && v < a.V && kv * 8 < a.rank) ? *(const u32x4*)(a.Wt + (size_t)v * a.rank + kv * 8)
-                                                     : zero4;
-    }
+    for (int q = 0; q < WQ; ++q) buf_load_x4<AS>(rw[q], wdesc, wofs[q] + tw);
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
-      const int v = v0 + 8 * (tid & 3);
-      u32x4 w = zero4;
-      if (lok[q]) {
-        if (lal[q] && v + 8 <= a.V) {
-          w = *(const u32x4*)(lrow[q] + v);
-        } else {
-          uint32_t e[8];
+      if (LAL) {
+        buf_load_x4<AS>(rl[q], ldesc, lofs[q] + tl);
+      } else {
+        // unaligned rows: one 2-byte load per entry, packed only after the stage's wait
 #pragma unroll
-          for (int l = 0; l < 8; ++l) e[l] = v + l < a.V ? (uint32_t)lrow[q][v + l] : 0u;
-          w.x = e[0] | (e[1] << 16);
-          w.y = e[2] | (e[3] << 16);
-          w.z = e[4] | (e[5] << 16);
-          w.w = e[6] | (e[7] << 16);
-        }
+        for (int l = 0; l < 8; ++l) buf_load_u16<AS>(ru[q][l], ldesc, lofs[q] + tl + 2 * l);
       }
-      rl[q] = w;
     }
   };
-  // LDS layouts. Wt stage: token row m holds NV vectors, vector kv at m*NV + swz_w(m, kv);
-  // the 8 rows read together by one MFMA fragment load land on 8 distinct 16-byte
-  // bank groups. L stage: row n holds 4 vectors, vector c at n*4 + (c ^ ((n >> 1) & 3)).
+  // LDS layouts. Wt stage: token row m holds NV vectors, vector kv at m*NV + swz_w(m, kv).
+  // A 16-byte read by 64 lanes is served 16 lanes (256 bytes, all 64 banks) at a time,
+  // so the 16 rows read together must fall on 16 distinct 16-byte slots of a 256-byte
+  // window: XOR the vector index with the row within aligned groups of W = min(NV, 16)
+  // vectors, R = 16 / W rows sharing a window. L stage: row n holds 4 vectors, vector c
+  // at n*4 + (c ^ ((n >> 2) & 3)), so the epilogue's 8-byte reads of 16 consecutive rows
+  // hit 16 distinct slots.
   auto swz_w = [](int m, int kv) {
-    return NV >= 8 ? ((kv & ~7) | ((kv ^ m) & 7)) : ((kv & ~3) | ((kv ^ (m >> 1)) & 3));
+    constexpr int W = NV < 16 ? NV : 16, R = 16 / W;
+    return (kv & ~(W - 1)) | ((kv ^ (m / R)) & (W - 1));
   };
-  auto store_stage = [&](int b, const u32x4* rw, const u32x4* rl) {
+  auto store_stage = [&](int b, const u32x4* rw, const u32x4* rl, const uint32_t (*ru)[8]) {
     u32x4* Ws = lds + b * (WST + LST);
     u32x4* Ls = Ws + WST;
 #pragma unroll
@@ -240,13 +306,23 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
       const int n = (tid + q * kGT) >> 2, c = tid & 3;
-      Ls[n * 4 + (c ^ ((n >> 1) & 3))] = rl[q];
+      u32x4 w;
+      if (LAL) {
+        w = rl[q];
+      } else {
+        w.x = ru[q][0] | (ru[q][1] << 16);
+        w.y = ru[q][2] | (ru[q][3] << 16);
+        w.z = ru[q][4] | (ru[q][5] << 16);
+        w.w = ru[q][6] | (ru[q][7] << 16);
+      }
+      Ls[n * 4 + (c ^ ((n >> 2) & 3))] = w;
     }
   };
 
   // per-lane running state of this lane's parent row
   float best = -INFINITY;
   int bidx = 0x7fffffff;
+  int bcode = -1;  // chain: 16 * stage + value index of best
   float tv[kTopK];
   int ti[kTopK];
 #pragma unroll
@@ -257,82 +333,141 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   float lref = -INFINITY;
   double lsum = 0.0;
 
-  u32x4 ringw[NR][WQ], ringl[NR][LQ];
+  u32x4 ringw[NR][WQ] = {}, ringl[NR][LQ] = {};
+  uint32_t ringu[NR][LAL ? 1 : LQ][8] = {};
 #pragma unroll
-  for (int p = 0; p < NR; ++p)
-    if (p < nst) load_stage(p, ringw[p], ringl[p]);
+  for (int p = 0; p < NR; ++p) load_stage(p, ringw[p], ringl[p], ringu[p]);
 
-  for (int base = 0; base < nst; base += NR) {
+  // Accumulator a of this lane is token v0 + 8*(a/4) + 4*(lane/32) + a%4 of its row, so
+  // the 16 values are visited in increasing token order. The accumulator starts from
+  // L (or -inf for a token past V or a row past the block), so the MFMAs leave z itself.
+  auto init_from_l = [&](int s, const u32x4* Ls, f32x16& acc) {
+    const int v0 = (s_begin + s) * kTS;
+    const char* lb = (const char*)(Ls + nloc * 4) + 8 * (lane >> 5);
+    uint2 w[4];
 #pragma unroll
-    for (int p = 0; p < NR; ++p) {
+    for (int h = 0; h < 4; ++h) w[h] = *(const uint2*)(lb + 16 * (h ^ ((nloc >> 2) & 3)));
+    if (v0 + kTS <= a.V && all_rows) {  // uniform: nothing to mask
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t ww = (q & 3) < 2 ? w[q >> 2].x : w[q >> 2].y;
+        acc[q] = (q & 1) ? bf16_hi(ww) : bf16_lo(ww);
+      }
+    } else {
+      const int vb = v0 + 4 * (lane >> 5);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t ww = (q & 3) < 2 ? w[q >> 2].x : w[q >> 2].y;
+        const bool ok = rvalid & (vb + 8 * (q >> 2) + (q & 3) < a.V);
+        acc[q] = ok ? ((q & 1) ? bf16_hi(ww) : bf16_lo(ww)) : -INFINITY;
+      }
+    }
+  };
+  // epilogue of one stage for the log-sum-exp and tree modes (z = acc)
+  auto epilogue = [&](int s, const f32x16& z) {
+    const int v0 = (s_begin + s) * kTS;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int v = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      tmax = fmaxf(tmax, z[q]);
+      if (MODE == MODE_TREE) {
+        if (z[q] > tv[kTopK - 1]) {
+          tv[kTopK - 1] = z[q];
+          ti[kTopK - 1] = v;
+#pragma unroll
+          for (int p2 = kTopK - 1; p2 > 0; --p2) {
+            if (tv[p2] > tv[p2 - 1]) {
+              const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
+              const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
+            }
+          }
+        }
+      } else if (z[q] > best) {
+        best = z[q];
+        bidx = v;
+      }
+    }
+    if (tmax != -INFINITY) {
+      const float nref = fmaxf(lref, tmax * kLog2e);
+      float ts = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));  // exp2(-inf) = 0
+      const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
+      lsum = lsum * scale + (double)ts;
+      lref = nref;
+    }
+  };
+
+  // Stages are software-pipelined inside each wave: the MFMAs of stage s are issued
+  // first, then the epilogue of stage s-1 runs on the other accumulator (for the chain,
+  // one value per MFMA, in program order between them).
+  f32x16 acc[2];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[1][q] = -INFINITY;  // "stage -1": updates nothing
+  for (int base = 0; base < nst; base += NU) {
+#pragma unroll
+    for (int p = 0; p < NU; ++p) {
       const int s = base + p;
       if (s >= nst) break;  // uniform over the workgroup
-      const int b = p & 1;  // NR is even, so s & 1 == p & 1
+      const int b = p & 1;  // NU is even, so s & 1 == p & 1
+      const int rp = p % NR;
+      // stage s is the oldest of the NR stages in flight: wait for its loads only
+      vm_wait<(NR - 1) * LPS>();
       // buffer b was last read two stages ago, before the previous barrier
-      store_stage(b, ringw[p], ringl[p]);
+      store_stage(b, ringw[rp], ringl[rp], ringu[rp]);
       __syncthreads();
-      if (s + NR < nst) load_stage(s + NR, ringw[p], ringl[p]);
+      load_stage(s + NR, ringw[rp], ringl[rp], ringu[rp]);
       const u32x4* Ws = lds + b * (WST + LST);
-      const u32x4* Ls = Ws + WST;
-      f32x16 acc;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+      init_from_l(s, Ws + WST, acc[b]);
+      const int code0 = 16 * (s - 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int m = lane & 31, kv = 2 * ks + (lane >> 5);
         const bf16x8 af = __builtin_bit_cast(bf16x8, Ws[m * NV + swz_w(m, kv)]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ufr[ks], acc, 0, 0, 0);
-      }
-      if (!rvalid) continue;
-      // accumulator a of this lane is token v0 + 8*(a/4) + 4*(lane/32) + a%4 of its row:
-      // visited in increasing token order; z = acc + L
-      const int v0 = (s_begin + s) * kTS;
-      const char* lb = (const char*)(Ls + nloc * 4) + 8 * (lane >> 5);
-      float z[16];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const uint2 w = *(const uint2*)(lb + 16 * (h ^ ((nloc >> 1) & 3)));
-#pragma unroll
-        for (int l = 0; l < 4; ++l) {
-          const int v = v0 + 8 * h + 4 * (lane >> 5) + l;
-          const uint32_t ww = l < 2 ? w.x : w.y;
-          z[4 * h + l] = v < a.V ? acc[4 * h + l] + ((l & 1) ? bf16_hi(ww) : bf16_lo(ww)) : -INFINITY;
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ufr[ks], acc[b], 0, 0, 0);
+        if (MODE == MODE_ARGMAX && ks < 16 && acc[b ^ 1][ks] > best) {
+          best = acc[b ^ 1][ks];
+          bcode = code0 + ks;
         }
       }
-      float tmax = -INFINITY;
+      if (MODE == MODE_ARGMAX) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int v = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        tmax = fmaxf(tmax, z[q]);
-        if (MODE == MODE_TREE) {
-          if (z[q] > tv[kTopK - 1]) {
-            tv[kTopK - 1] = z[q];
-            ti[kTopK - 1] = v;
-#pragma unroll
-            for (int p2 = kTopK - 1; p2 > 0; --p2) {
-              if (tv[p2] > tv[p2 - 1]) {
-                const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
-                const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
-              }
-            }
+        for (int q = KS; q < 16; ++q)  // ranks below 256: the remaining values
+          if (acc[b ^ 1][q] > best) {
+            best = acc[b ^ 1][q];
+            bcode = code0 + q;
           }
-        } else if (z[q] > best) {
-          best = z[q];
-          bidx = v;
-        }
-      }
-      if (MODE != MODE_ARGMAX && tmax != -INFINITY) {
-        const float nref = fmaxf(lref, tmax * kLog2e);
-        float ts = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));  // exp2(-inf) = 0
-        const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
-        lsum = lsum * scale + (double)ts;
-        lref = nref;
+      } else if (s > 0) {
+        epilogue(s - 1, acc[b ^ 1]);
       }
     }
   }
+  // the last stage's epilogue (accumulator picked by two static paths: indexing the
+  // pair with a run-time value would move it to scratch memory)
+  auto finish = [&](const f32x16& last) {
+    if (MODE == MODE_ARGMAX) {
+      const int code0 = 16 * (nst - 1);
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (last[q] > best) {
+          best = last[q];
+          bcode = code0 + q;
+        }
+    } else {
+      epilogue(nst - 1, last);
+    }
+  };
+  if (nst > 0) {
+    if ((nst - 1) & 1) finish(acc[1]);
+    else finish(acc[0]);
+  }
+  if (MODE == MODE_ARGMAX && bcode >= 0) {
+    const int q = bcode & 15;
+    bidx = (s_begin + (bcode >> 4)) * kTS + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+  }
 
+  vm_wait<0>();  // the ring's trailing loads (all out of range) land before the wave ends
   // merge lane pairs (lane, lane ^ 32 hold the same parent row), then lanes < 32 write
   if (MODE == MODE_TREE) {
     float ov[kTopK];
@@ -619,30 +754,42 @@ int pick_groups(int rows, int V) {
   return G;
 }
 
-template <int MODE, int KS>
+template <int MODE, int KS, bool LAL>
 int32_t launch_gemm_ks(int kid, GemmArgs a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)markov_gemm_kernel<MODE, KS>,
+    (void)hipFuncSetAttribute((const void*)markov_gemm_kernel<MODE, KS, LAL>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
   a.nrb = (a.rows + kTR - 1) / kTR;
   a.xcd_map = a.nrb > 1 && a.G % 8 == 0;
-  launch(kid, markov_gemm_kernel<MODE, KS>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT),
+  launch(kid, markov_gemm_kernel<MODE, KS, LAL>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT),
          (uint32_t)gemm_lds_bytes(KS), s, a);
   return hip_check(hipGetLastError(), "markov gemm launch");
 }
 
+template <int MODE, bool LAL>
+int32_t launch_gemm_al(int kid, const GemmArgs& a, hipStream_t s) {
+  switch (ksteps(a.rank)) {
+    case 2: return launch_gemm_ks<MODE, 2, LAL>(kid, a, s);
+    case 4: return launch_gemm_ks<MODE, 4, LAL>(kid, a, s);
+    case 8: return launch_gemm_ks<MODE, 8, LAL>(kid, a, s);
+    case 16: return launch_gemm_ks<MODE, 16, LAL>(kid, a, s);
+    default: return launch_gemm_ks<MODE, 32, LAL>(kid, a, s);
+  }
+}
+
+// L rows 16-byte aligned (base and both strides) take the vector-load kernel
 template <int MODE>
 int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
-  switch (ksteps(a.rank)) {
-    case 2: return launch_gemm_ks<MODE, 2>(kid, a, s);
-    case 4: return launch_gemm_ks<MODE, 4>(kid, a, s);
-    case 8: return launch_gemm_ks<MODE, 8>(kid, a, s);
-    case 16: return launch_gemm_ks<MODE, 16>(kid, a, s);
-    default: return launch_gemm_ks<MODE, 32>(kid, a, s);
-  }
+  if ((size_t)a.V * a.rank * 2 >= kOOB)
+    return fail(DSP_ERR_SHAPE, "Wt must span less than 2 GiB (V * rank * 2 bytes)");
+  const size_t reqs = (size_t)(kTR + a.rows_per_req - 1) / a.rows_per_req + 1;  // requests a row block touches
+  if ((reqs * (size_t)a.ldL_r + (size_t)a.V) * 2 >= kOOB)
+    return fail(DSP_ERR_SHAPE, "the L rows of %d parent rows must span less than 2 GiB", kTR);
+  const bool al = ((uintptr_t)a.L) % 16 == 0 && a.ldL_r % 8 == 0 && a.ldL_d % 8 == 0;
+  return al ? launch_gemm_al<MODE, true>(kid, a, s) : launch_gemm_al<MODE, false>(kid, a, s);
 }
 
 int32_t check_markov_common(const void* L, int32_t l_dtype, const void* U, const void* Wt, int32_t V,
