@@ -8,21 +8,24 @@
 // window is accepted. T = 0 is greedy matching; a parent array selects the
 // greedy walk of a draft tree.
 //
-// Sampled path (T > 0), two launches on the caller's stream:
+// Sampled path (T > 0), four launches on the caller's stream:
 //   1. stats -- one streaming pass over every packed target row and every
 //      windowed draft row. A workgroup owns a (row, chunk) item: up to 2048
 //      16-byte loads in flight, the chunk maximum, then the sum of
 //      exp2(x*c - ref) with ref = max*c (c = log2(e)/T): fp32 per element, fp64
-//      across vectors. Grid-stride over items, so ragged totals known only on
-//      the device need no host synchronisation.
-//   2. decide+sample -- one workgroup per request. Its first wavefront (lane
-//      k-1 = position k) merges the chunk statistics into log-sum-exp (fp64),
-//      forms ratio = exp2(lp2 - lq2) in fp64 with the Philox uniforms, finds the
-//      first rejection by ballot and writes the accepted tokens; then the whole
-//      workgroup draws the corrected token from max(0, p - q) (or the bonus from
-//      p) by inverse CDF: per-chunk fp64 sums, then a rescan of the chunk that
-//      holds u' * total with contiguous per-thread ranges and an fp64
-//      exclusive scan.
+//      across vectors. Items past the device-side packed total exit at once, so
+//      ragged totals known only on the device need no host synchronisation.
+//   2. decide -- one wavefront per request (lane k-1 = position k): merges the
+//      chunk statistics into log-sum-exp (fp64), forms ratio = exp2(lp2 - lq2)
+//      in fp64 with the Philox uniforms, finds the first rejection by ballot,
+//      writes the accepted tokens and leaves a job (row, both log-sum-exps,
+//      uniform) for the correction draw.
+//   3. residual -- per (request, chunk): the fp64 mass of max(0, p - q) (or of
+//      p for a bonus draw) over the chunk.
+//   4. sample -- one workgroup per request: picks the chunk that holds
+//      u' * total, rescans it with contiguous per-thread ranges and an fp64
+//      exclusive scan, and writes the smallest token whose running sum exceeds
+//      the target (the last positive entry if rounding leaves none).
 // No workgroup waits on another inside a kernel: on this chip the L2 is per
 // XCD, and publishing data between workgroups would need an L2 write-back per
 // hand-off, so every dependency is a kernel boundary instead.
