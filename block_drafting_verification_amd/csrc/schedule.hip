@@ -62,64 +62,101 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* wsum) {
   return wsum[w] + inc - v;
 }
 
-// Ascending bitonic sort of keys[0..P) (P a power of two, P <= 1024 * E) by a
-// 1024-thread block holding E consecutive keys per thread: strides below E are
-// swapped in registers, strides below 64*E through wave shuffles, and only the
-// wider strides through LDS, so most of the log2(P)(log2(P)+1)/2 stages need no barrier.
+// Lane exchange at xor distance TS (1..32) inside a wavefront, with fixed patterns:
+// DPP quad permutes for 1 and 2, ds_swizzle xor masks for 4, 8 and 16 (no LDS memory
+// access), ds_bpermute only for 32.
+template <int TS>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  if (TS == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  if (TS == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  if (TS == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x101F);  // and 31, xor 4
+  if (TS == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x201F);
+  if (TS == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ 32) << 2), (int)x);
+}
+template <int TS, int E>
+__device__ __forceinline__ void xor_lanes(const uint64_t* v, uint64_t* o) {
+  uint32_t lo[E], hi[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    lo[e] = xor_lane<TS>((uint32_t)v[e]);
+    hi[e] = xor_lane<TS>((uint32_t)(v[e] >> 32));
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = ((uint64_t)hi[e] << 32) | lo[e];
+}
+
+// Ascending bitonic sort of keys[0..P) (P a power of two, 64 * E <= P <= 1024 * E) by
+// the first P / E threads of a 1024-thread block, E consecutive keys per thread:
+// strides below E are compare-exchanges in registers, strides below 64*E go through
+// lane exchanges inside a wavefront (fixed patterns when E > 1), and only wider
+// strides through LDS, so
+// most of the log2(P)(log2(P)+1)/2 stages need neither memory nor a barrier.
 template <int E>
 __device__ void bitonic_keys(uint64_t* keys, int P) {
   const int tid = threadIdx.x;
+  const bool act = tid * E < P;
   uint64_t v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = tid * E + e;
-    v[e] = idx < P ? keys[idx] : ~0ull;
-  }
+  for (int e = 0; e < E; ++e) v[e] = act ? keys[tid * E + e] : ~0ull;
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride < E) {
+        // partner in the same thread: element e ^ stride (stride in {1, 2, 4})
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int ep = e ^ stride;
-          if (ep > e) {
+        for (int sb = 1; sb < E; sb <<= 1) {
+          if (sb != stride) continue;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if (e & sb) continue;
             const bool up = ((tid * E + e) & size) == 0;
-            const uint64_t a = v[e], b = v[ep];
-            if ((a > b) == up) {
-              v[e] = b;
-              v[ep] = a;
-            }
+            const uint64_t a = v[e], b = v[e | sb];
+            const bool sw = (a > b) == up;
+            v[e] = sw ? b : a;
+            v[e | sb] = sw ? a : b;
           }
         }
         continue;
       }
       const int ts = stride / E;  // distance in threads
       uint64_t o[E];
-      if (ts < 64) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = __shfl_xor(v[e], ts, 64);
+      if (ts < 64 && E == 1) {
+        // one key per thread: a single lane permute costs less than a branch per stage
+        o[0] = __shfl_xor(v[0], ts, 64);
+      } else if (ts < 64) {
+        // one uniform branch per stage, then straight-line fixed-pattern exchanges
+        switch (ts) {
+          case 1: xor_lanes<1, E>(v, o); break;
+          case 2: xor_lanes<2, E>(v, o); break;
+          case 4: xor_lanes<4, E>(v, o); break;
+          case 8: xor_lanes<8, E>(v, o); break;
+          case 16: xor_lanes<16, E>(v, o); break;
+          default: xor_lanes<32, E>(v, o); break;
+        }
       } else {
         __syncthreads();
+        if (act)
 #pragma unroll
-        for (int e = 0; e < E; ++e) keys[tid * E + e] = v[e];
+          for (int e = 0; e < E; ++e) keys[tid * E + e] = v[e];
         __syncthreads();
+        if (act)
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = keys[(tid ^ ts) * E + e];
+          for (int e = 0; e < E; ++e) o[e] = keys[(tid ^ ts) * E + e];
       }
+      const bool up = ((tid * E) & size) == 0;     // size > stride >= E: same for all e
+      const bool low = ((tid * E) & stride) == 0;  // likewise
+      const bool keep_min = low == up;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int idx = tid * E + e;
-        const bool up = (idx & size) == 0;
-        const bool low = (idx & stride) == 0;
-        v[e] = (low == up) ? (o[e] < v[e] ? o[e] : v[e]) : (o[e] > v[e] ? o[e] : v[e]);
+        const bool lt = o[e] < v[e];
+        v[e] = lt == keep_min ? o[e] : v[e];
       }
     }
   }
   __syncthreads();
+  if (act)
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = tid * E + e;
-    if (idx < P) keys[idx] = v[e];
-  }
+    for (int e = 0; e < E; ++e) keys[tid * E + e] = v[e];
   __syncthreads();
 }
 
@@ -149,14 +186,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
       keys[i * K + k] = sched_key(quantise(s, scale), i, k);
     }
   }
-  for (int j = n + tid; j < P; j += kSchedThreads) keys[j] = ~0ull;
+  for (int j = n + tid; j < (P < 64 ? 64 : P); j += kSchedThreads) keys[j] = ~0ull;
   __syncthreads();
 
-  // bitonic sort, ascending
-  if (P <= 1024) bitonic_keys<1>(keys, P);
-  else if (P == 2048) bitonic_keys<2>(keys, P);
-  else if (P == 4096) bitonic_keys<4>(keys, P);
-  else bitonic_keys<8>(keys, P);
+  // bitonic sort, ascending, over at least one full wavefront of slots (padding keys
+  // are ~0 and sort last), with as many threads as the size allows
+  const int PS = P < 64 ? 64 : P;
+  if (PS <= 1024) bitonic_keys<1>(keys, PS);
+  else if (PS == 2048) bitonic_keys<2>(keys, PS);
+  else if (PS == 4096) bitonic_keys<4>(keys, PS);
+  else bitonic_keys<8>(keys, PS);
 
   // exact prefix sums over the first M sorted candidates; thread t owns [t*C, t*C + C)
   const int C = (M + kSchedThreads - 1) / kSchedThreads;
