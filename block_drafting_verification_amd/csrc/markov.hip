@@ -212,28 +212,27 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   const int row = r0 + nloc;
   const bool rvalid = row < a.rows;
   const bool all_rows = r0 + kTR <= a.rows;  // every row of the block is a parent row
-  bf16x8 ufr[KS];
-  {
-    int tok = 0;
-    if (rvalid) {
-      tok = a.row_tok[(size_t)row * a.ld_tok];
-      if (tok < 0 || tok >= a.V) {
-        if (g == 0 && lane < 32) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
-        tok = 0;
-      }
+  // the row's token; its U row is fetched after the first stage's loads are issued
+  int tok = 0;
+  if (rvalid) {
+    tok = a.row_tok[(size_t)row * a.ld_tok];
+    if (tok < 0 || tok >= a.V) {
+      if (g == 0 && lane < 32) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+      tok = 0;
     }
-    // issued like the ring's loads (the compiler would otherwise keep them "pending" around
-    // the stage loop and drain the ring for them); the first stage's wait covers them
+  }
+  u32x4 ufr[KS] = {};  // B fragments, loaded straight into their registers
+  // issued like the ring's loads (the compiler would otherwise keep them "pending" around
+  // the stage loop and drain the ring for them); the first stage's wait covers them
+  auto load_u = [&]() {
     const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)a.V * a.rank * 2));
     const uint32_t ubase = (uint32_t)(((size_t)tok * a.rank + 8 * (lane >> 5)) * 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bool ok = rvalid && 16 * ks + 8 * (lane >> 5) < a.rank;
-      u32x4 u = {0u, 0u, 0u, 0u};
-      buf_load_x4<AS>(u, udesc, ok ? ubase + 32 * ks : kOOB);
-      ufr[ks] = __builtin_bit_cast(bf16x8, u);
+      buf_load_x4<AS>(ufr[ks], udesc, ok ? ubase + 32 * ks : kOOB);
     }
-  }
+  };
 
   // L rows staged by this thread: row (tid + q*kGT) / 4, 16-byte column tid % 4, addressed
   // from the first request of this row block (spans checked on the host)
@@ -335,8 +334,12 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
 
   u32x4 ringw[NR][WQ] = {}, ringl[NR][LQ] = {};
   uint32_t ringu[NR][LAL ? 1 : LQ][8] = {};
+  // prologue: stage 0, then the U rows (which wait on the token load), then the rest of
+  // the ring; the first stage's wait then covers stage 0 and the U rows only
+  load_stage(0, ringw[0], ringl[0], ringu[0]);
+  load_u();
 #pragma unroll
-  for (int p = 0; p < NR; ++p) load_stage(p, ringw[p], ringl[p], ringu[p]);
+  for (int p = 1; p < NR; ++p) load_stage(p, ringw[p], ringl[p], ringu[p]);
 
   // Accumulator a of this lane is token v0 + 8*(a/4) + 4*(lane/32) + a%4 of its row, so
   // the 16 values are visited in increasing token order. The accumulator starts from
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       for (int ks = 0; ks < KS; ++ks) {
         const int m = lane & 31, kv = 2 * ks + (lane >> 5);
         const bf16x8 af = __builtin_bit_cast(bf16x8, Ws[m * NV + swz_w(m, kv)]);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ufr[ks], acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, ufr[ks]), acc[b], 0, 0, 0);
         if (MODE == MODE_ARGMAX && ks < 16 && acc[b ^ 1][ks] > best) {
           best = acc[b ^ 1][ks];
           bcode = code0 + ks;
