@@ -581,19 +581,22 @@ struct TreeMergeArgs {
   int32_t* status;
 };
 
-// One workgroup per request: merge the column-group partials of its parents
-// (one wavefront per parent), score every candidate child in fp64 (one
-// wavefront per candidate, lanes splitting the rank), keep the top-F by
-// (s desc, parent slot, child rank).
+// One workgroup per request: merge the column-group partials of its parents (16
+// lanes per parent), score every candidate child in fp64 (4 lanes per candidate,
+// each a quarter of the rank, every load issued before any is used), keep the top-F
+// by (s desc, parent slot, child rank).
 __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
   __shared__ double c_score[256];
   __shared__ int32_t c_tok[256];
   __shared__ double p_lse[64];
   __shared__ int32_t p_top[64][kTopK];
-  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = blockIdx.x, tid = threadIdx.x;
   const int nc = a.fp * a.topk;
-  for (int p = w; p < a.fp; p += 4) {
-    const TreePart* pr = a.part + (size_t)(i * a.fp + p) * a.G;
+  // parents: 16 lanes each (aligned groups inside a wavefront), 16 parents per pass
+  for (int pb = 0; pb < a.fp; pb += 16) {
+    const int p = pb + (tid >> 4), j = tid & 15;
+    const bool pv = p < a.fp;
+    const TreePart* pr = a.part + (size_t)(i * a.fp + (pv ? p : 0)) * a.G;
     float tv[kTopK];
     int ti[kTopK];
 #pragma unroll
@@ -602,12 +605,13 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
       ti[q] = 0x7fffffff;
     }
     float H = -INFINITY;
-    for (int g = lane; g < a.G; g += 64) {
-      merge_top4(tv, ti, pr[g].val, pr[g].idx);
-      H = fmaxf(H, pr[g].ref);
-    }
+    if (pv)
+      for (int g = j; g < a.G; g += 16) {
+        merge_top4(tv, ti, pr[g].val, pr[g].idx);
+        H = fmaxf(H, pr[g].ref);
+      }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
+    for (int o = 8; o > 0; o >>= 1) {
       float ov[kTopK];
       int oi[kTopK];
 #pragma unroll
@@ -616,34 +620,55 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
         oi[q] = __shfl_xor(ti[q], o, 64);
       }
       merge_top4(tv, ti, ov, oi);
+      H = fmaxf(H, __shfl_xor(H, o, 64));
     }
-    H = wave_max(H);
     double S = 0.0;
-    for (int g = lane; g < a.G; g += 64)
-      if (pr[g].ref != -INFINITY) S += pr[g].sum * exp2((double)pr[g].ref - (double)H);
-    S = wave_sum(S);
-    if (lane == 0) {
+    if (pv)
+      for (int g = j; g < a.G; g += 16)
+        if (pr[g].ref != -INFINITY) S += pr[g].sum * exp2((double)pr[g].ref - (double)H);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
+    if (pv && j == 0) {
       p_lse[p] = ((double)H + log2(S)) * kLn2d;
 #pragma unroll
       for (int q = 0; q < kTopK; ++q) p_top[p][q] = ti[q];
     }
   }
   __syncthreads();
-  for (int c = w; c < nc; c += 4) {
-    const int p = c / a.topk, rk = c % a.topk;
+  // candidates: 4 lanes each, lane quarter r covers rank [r*rank/4, (r+1)*rank/4)
+  for (int cb = 0; cb < nc; cb += 64) {
+    const int c = cb + (tid >> 2), r = tid & 3;
+    const bool cv = c < nc;
+    const int p = cv ? c / a.topk : 0, rk = cv ? c % a.topk : 0;
     int v = p_top[p][rk];
-    if (v < 0 || v >= a.V) {  // only reachable with non-finite scores
-      if (lane == 0) atomicOr(a.status, DSP_STATUS_NONFINITE);
-      v = 0;
+    if (cv && (v < 0 || v >= a.V)) {  // only reachable with non-finite scores
+      if (r == 0) atomicOr(a.status, DSP_STATUS_NONFINITE);
     }
+    if (v < 0 || v >= a.V) v = 0;
     const int ptoken = a.ptok[i * a.fp + p];
-    // z_v recomputed in fp64 for the score: lanes split the rank
-    const uint16_t* ur = a.U + (size_t)ptoken * a.rank;
-    const uint16_t* wr = a.Wt + (size_t)v * a.rank;
+    const int qn = a.rank / 4;  // a multiple of 8
+    const u32x4* ur = (const u32x4*)(a.U + (size_t)ptoken * a.rank + r * qn);
+    const u32x4* wr = (const u32x4*)(a.Wt + (size_t)v * a.rank + r * qn);
     double m = 0.0;
-    for (int j = lane; j < a.rank; j += 64) m += (double)bf16_val(ur[j]) * (double)bf16_val(wr[j]);
-    m = wave_sum(m);
-    if (lane == 0) {
+    for (int j0 = 0; j0 < qn / 8; j0 += 8) {  // 8 vector pairs in flight
+      u32x4 uu[8], ww[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const bool ok = j0 + t < qn / 8;
+        uu[t] = ok ? ur[j0 + t] : u32x4{0u, 0u, 0u, 0u};
+        ww[t] = ok ? wr[j0 + t] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          m += (double)bf16_lo(uu[t][h]) * (double)bf16_lo(ww[t][h]);
+          m += (double)bf16_hi(uu[t][h]) * (double)bf16_hi(ww[t][h]);
+        }
+    }
+    m += __shfl_xor(m, 1, 64);
+    m += __shfl_xor(m, 2, 64);
+    if (cv && r == 0) {
       const double z = (double)bf16_val(a.L[(size_t)i * a.ldL_r + (size_t)(a.d - 1) * a.ldL_d + v]) + m;
       const double ps = a.pscore ? a.pscore[i * a.fp + p] : 0.0;
       c_score[c] = ps + fmin(0.0, z - p_lse[p]);
@@ -705,13 +730,28 @@ __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
     s_out[e] = -1;
   }
   __syncthreads();
-  // rank by (score desc, depth asc, slot asc) == (score desc, kept id asc)
+  // rank by (score desc, depth asc, slot asc) == (score desc, kept id asc). Each
+  // depth's frontier is already in that order (slot = rank of the pruning), so the
+  // rank of a node is its slot plus, for every other depth, a binary-search count of
+  // the nodes there that precede it: score >= s at shallower depths (they win ties),
+  // score > s at deeper ones.
   for (int e = tid; e < nk; e += 256) {
     if (!s_valid[e]) continue;
     const double s = s_score[e];
-    int rank = 0;
-    for (int o = 0; o < nk; ++o)
-      rank += (s_valid[o] && (s_score[o] > s || (s_score[o] == s && o < e))) ? 1 : 0;
+    const int de = e / a.F;
+    int rank = e % a.F;
+    for (int d = 0; d < a.D; ++d) {
+      if (d == de) continue;
+      const double* ls = s_score + d * a.F;
+      int lo = 0, hi = fsz[d];  // first slot that does not precede e
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const bool pre = d < de ? ls[mid] >= s : ls[mid] > s;
+        if (pre) lo = mid + 1;
+        else hi = mid;
+      }
+      rank += lo;
+    }
     if (rank < a.topN) s_out[e] = rank;
   }
   __syncthreads();
