@@ -39,6 +39,8 @@ import numpy as np
 
 MODE_EARLY_STOP = 0
 MODE_ARGMAX = 1
+MODE_TOP_M = 2
+MODE_THRESHOLD = 3
 
 
 def quant_bits(R, K):
@@ -80,11 +82,19 @@ def sorted_candidates(Sq):
     return ii[order], kk[order], sq[order]
 
 
-def schedule_windows(conf, cost, mode=MODE_EARLY_STOP, max_tokens=-1):
+def schedule_windows(conf, cost, mode=MODE_EARLY_STOP, max_tokens=-1, threshold=0.0):
     """Per-request verify windows n_i chosen by the prefix scheduler (notes 5.2).
 
     conf: [R, K] float32 confidences; cost: fp64 table, cost[n] = step time when
     n draft tokens are verified (len >= R*K + 1).
+    Modes besides the early stop and the global argmax (notes 9.2):
+      MODE_TOP_M -- a capacity fixed in advance (notes 9.2: the verify capacity comes
+        from confidences two steps old, the ranking from the current survivals): the
+        first min(max_tokens, R*K) candidates of the current order (max_tokens < 0:
+        all of them);
+      MODE_THRESHOLD -- the conventional fixed threshold (notes 5.2 and 8.3,
+        threshold 0 = verify the full block): n_i = #{k : S_{i,k} >= threshold},
+        compared on the fp64 survival.
     Returns dict(windows [R] int32, survival [R, K] fp64, N, E, J, Q).
     """
     conf = np.asarray(conf, dtype=np.float32)
@@ -117,6 +127,15 @@ def schedule_windows(conf, cost, mode=MODE_EARLY_STOP, max_tokens=-1):
             Jj = float(E[j]) / float(cost[j])
             if Jj > best:
                 best, N = Jj, j
+    elif mode == MODE_TOP_M:
+        N = M
+    elif mode == MODE_THRESHOLD:
+        windows = np.array([sum(1 for k in range(K) if S[i, k] >= threshold) for i in range(R)], dtype=np.int32)
+        N = int(windows.sum())
+        En = sum(int(Sq[i, k]) for i in range(R) for k in range(int(windows[i])))
+        E_real = float(En) * (2.0 ** -Q)
+        J = E_real / float(cost[N]) if cost[N] != 0 else (0.0 if E_real == 0 else math.inf)
+        return dict(windows=windows, survival=S, N=N, E=E_real, J=J, Q=Q, order=(ci[:M], ck[:M]))
     else:
         raise ValueError("unknown mode")
     windows = np.zeros(R, dtype=np.int32)

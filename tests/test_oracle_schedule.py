@@ -141,3 +141,72 @@ def test_figure1_window():
     cost = osch.additive_cost(g["cost_a"], g["cost_b"], 4)
     for mode in (osch.MODE_EARLY_STOP, osch.MODE_ARGMAX):
         assert osch.schedule_windows(conf, cost, mode)["windows"][0] == g["expected_window"]
+
+
+# ---- scheduler variants: fixed capacity from an older step (top-M) and fixed threshold
+
+
+def test_threshold_zero_is_full_block():
+    """Notes 8.3, Figure 5: threshold 0 is the conventional verify-everything block."""
+    rng = np.random.default_rng(3)
+    conf = rng.uniform(0.0, 1.0, size=(9, 7)).astype(np.float32)
+    r = osch.schedule_windows(conf, np.ones(64), mode=osch.MODE_THRESHOLD, threshold=0.0)
+    assert np.array_equal(r["windows"], np.full(9, 7))
+    assert r["N"] == 63
+
+
+def test_threshold_hand_case():
+    # survivals (float32 confidences multiplied in fp64): row 0: 0.9, 0.72, 0.36; row 1: 0.5, 0.45, 0.405
+    conf = np.array([[0.9, 0.8, 0.5], [0.5, 0.9, 0.9]], np.float32)
+    cost = np.ones(7)
+    for th, want in [(0.3, [3, 3]), (0.4, [2, 3]), (0.42, [2, 2]), (0.46, [2, 1]), (0.6, [2, 0]), (0.8, [1, 0]),
+                     (0.95, [0, 0])]:
+        r = osch.schedule_windows(conf, cost, mode=osch.MODE_THRESHOLD, threshold=th)
+        assert r["windows"].tolist() == want, th
+        assert r["N"] == sum(want)
+
+
+def test_threshold_monotone_and_prefix():
+    rng = np.random.default_rng(4)
+    conf = rng.uniform(0.3, 1.0, size=(20, 9)).astype(np.float32)
+    prev = None
+    for th in np.linspace(0.0, 1.0, 21):
+        w = osch.schedule_windows(conf, np.ones(181), mode=osch.MODE_THRESHOLD, threshold=th)["windows"]
+        S = np.cumprod(conf.astype(np.float64), axis=1)
+        assert np.array_equal(w, (S >= th).sum(axis=1))  # S is non-increasing, so a prefix
+        if prev is not None:
+            assert np.all(w <= prev)
+        prev = w
+
+
+def _exact_order(conf):
+    """Candidates by exact fp64 survival descending, ties by request then position."""
+    S = np.cumprod(conf.astype(np.float64), axis=1)
+    R, K = S.shape
+    return sorted(((i, k) for i in range(R) for k in range(K)), key=lambda t: (-S[t], t[0], t[1]))
+
+
+def test_top_m_takes_the_m_best_candidates():
+    rng = np.random.default_rng(5)
+    conf = rng.uniform(0.2, 1.0, size=(11, 6)).astype(np.float32)
+    order = _exact_order(conf)
+    for M in (0, 1, 7, 30, 65, 66):
+        r = osch.schedule_windows(conf, np.ones(67), mode=osch.MODE_TOP_M, max_tokens=M)
+        want = np.zeros(11, np.int32)
+        for i, _ in order[:M]:
+            want[i] += 1
+        assert np.array_equal(r["windows"], want), M
+        assert r["N"] == M
+
+
+def test_top_m_at_the_early_stop_capacity_reproduces_it():
+    """With the capacity the early stop would choose, the ranking from the same
+    survivals gives the same windows (the async rule only delays the capacity)."""
+    rng = np.random.default_rng(6)
+    conf = rng.uniform(0.1, 1.0, size=(16, 8)).astype(np.float32)
+    cost = osch.additive_cost(1.0, 0.05, 128)
+    es = osch.schedule_windows(conf, cost)
+    tm = osch.schedule_windows(conf, cost, mode=osch.MODE_TOP_M, max_tokens=es["N"])
+    assert np.array_equal(es["windows"], tm["windows"])
+    small = osch.schedule_windows(conf, cost, mode=osch.MODE_TOP_M, max_tokens=es["N"] // 2)
+    assert np.all(small["windows"] <= es["windows"])
