@@ -20,12 +20,14 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DSP_STATUS_NONFINITE,
-                   DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE, DspError, KERNELS)
+from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DSP_SCHED_THRESHOLD,
+                   DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE,
+                   DspError, KERNELS)
 
 __all__ = ["PreparedCall", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step", "tree_expand",
            "philox_uniforms", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
-           "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_STATUS_TOKEN_RANGE",
+           "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
+           "DSP_STATUS_TOKEN_RANGE",
            "DSP_STATUS_WINDOW_RANGE", "DSP_STATUS_NONFINITE"]
 
 
@@ -123,9 +125,12 @@ def philox_uniforms(ctr, seed, stream=None):
     return out
 
 
-def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, want_survival=True,
+def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, threshold=0.0, want_survival=True,
                      out=None, stream=None, prepare=False):
     """conf: float32 [R, K]; cost: float64 [>= R*K+1] (both on the GPU).
+
+    mode: DSP_SCHED_EARLY_STOP, DSP_SCHED_ARGMAX, DSP_SCHED_TOP_M (capacity max_tokens)
+    or DSP_SCHED_THRESHOLD (survival >= threshold).
 
     Returns dict(windows int32 [R], survival float64 [R, K] or None, stats float64 [4]).
     """
@@ -139,7 +144,8 @@ def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, want_
     survival = _take(o, "survival", lambda: torch.empty(R, K, dtype=torch.float64, device=dev)) if want_survival else None
     stats = _take(o, "stats", lambda: torch.empty(4, dtype=torch.float64, device=dev))
     ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare)
-    args = (_ptr(conf), R, K, _ptr(cost), cost.numel(), mode, max_tokens, _ptr(windows), _ptr(survival),
+    args = (_ptr(conf), R, K, _ptr(cost), cost.numel(), mode, max_tokens, float(threshold), _ptr(windows),
+            _ptr(survival),
             _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
     res = dict(windows=windows, survival=survival, stats=stats)
     return _finish(lib().dsp_schedule_windows, args, res, prepare, (conf, cost, ws))

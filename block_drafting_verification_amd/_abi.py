@@ -12,6 +12,8 @@ DSP_STATUS_WINDOW_RANGE = 2
 DSP_STATUS_NONFINITE = 4
 DSP_SCHED_EARLY_STOP = 0
 DSP_SCHED_ARGMAX = 1
+DSP_SCHED_TOP_M = 2
+DSP_SCHED_THRESHOLD = 3
 
 KERNELS = ["VERIFY_STATS", "VERIFY_DECIDE", "VERIFY_RESIDUAL", "VERIFY_SAMPLE", "SCHEDULE", "PACK",
            "MARKOV_GEMM", "MARKOV_MERGE", "TREE_GEMM", "TREE_MERGE", "TREE_FINAL"]
@@ -28,7 +30,8 @@ SIGNATURES = {
     "dsp_last_error": (ctypes.c_char_p, []),
     "dsp_philox_uniforms": (_i32, [_p, _i64, _u64, _p, _p]),
     "dsp_schedule_windows_workspace_size": (_sz, [_i32, _i32]),
-    "dsp_schedule_windows": (_i32, [_p, _i32, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]),
+    "dsp_schedule_windows": (_i32, [_p, _i32, _i32, _p, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _p, _sz,
+                                    _p]),
     "dsp_pack_ragged": (_i32, [_p, _p, _p, _i64, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "dsp_verify_rejection_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "dsp_verify_rejection": (_i32, [_p, _i32, _i64, _p, _p, _i32, _i64, _i64, _p, _i64, _p,

@@ -162,7 +162,8 @@ __device__ void bitonic_keys(uint64_t* keys, int P) {
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     const float* __restrict__ conf, int R, int K, const double* __restrict__ cost, int mode, int M,
-    int Q, int32_t* __restrict__ windows, double* __restrict__ survival, double* __restrict__ stats) {
+    double threshold, int Q, int32_t* __restrict__ windows, double* __restrict__ survival,
+    double* __restrict__ stats) {
   __shared__ uint64_t keys[kMaxCand];
   __shared__ float s_conf[kMaxCand];
   __shared__ uint64_t wsum[kSchedThreads / 64];
@@ -189,6 +190,35 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   for (int j = n + tid; j < (P < 64 ? 64 : P); j += kSchedThreads) keys[j] = ~0ull;
   __syncthreads();
 
+  if (mode == DSP_SCHED_THRESHOLD) {
+    // n_i = #{k : S_{i,k} >= threshold} on the fp64 survival; no ranking needed
+    uint64_t esum = 0;
+    int cnt_all = 0;
+    for (int i = tid; i < R; i += kSchedThreads) {
+      double s = 1.0;
+      int cnt = 0;
+      for (int k = 0; k < K; ++k) {
+        s = __dmul_rn(s, (double)s_conf[i * K + k]);
+        if (s >= threshold) {
+          ++cnt;
+          esum += quantise(s, scale);
+        }
+      }
+      windows[i] = cnt;
+      cnt_all += cnt;
+    }
+    const int Nt = block_sum<kSchedThreads / 64>(cnt_all, smi);
+    const uint64_t Et = block_exclusive_scan_u64(esum, wsum) + esum;  // inclusive; the last thread holds the total
+    if (stats && tid == kSchedThreads - 1) {
+      const double E = ldexp((double)Et, -Q);
+      stats[0] = (double)Nt;
+      stats[1] = E;
+      stats[2] = cost[Nt] != 0.0 ? __ddiv_rn(E, cost[Nt]) : (E == 0.0 ? 0.0 : INFINITY);
+      stats[3] = (double)Q;
+    }
+    return;
+  }
+
   // bitonic sort, ascending, over at least one full wavefront of slots (padding keys
   // are ~0 and sort last), with as many threads as the size allows
   const int PS = P < 64 ? 64 : P;
@@ -205,7 +235,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   const uint64_t ex = block_exclusive_scan_u64(local, wsum);
 
   int N;
-  if (mode == DSP_SCHED_EARLY_STOP) {
+  if (mode == DSP_SCHED_TOP_M) {
+    N = M;  // a capacity decided earlier: the first M candidates of the current order
+  } else if (mode == DSP_SCHED_EARLY_STOP) {
     int first_fail = 0x7fffffff;
     uint64_t run = ex;
     for (int p = p0; p < p1; ++p) {
@@ -359,7 +391,7 @@ extern "C" size_t dsp_schedule_windows_workspace_size(int32_t R, int32_t K) {
 }
 
 extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
-                                        int32_t n_cost, int32_t mode, int32_t max_tokens,
+                                        int32_t n_cost, int32_t mode, int32_t max_tokens, double threshold,
                                         int32_t* windows, double* survival, double* stats, void* ws,
                                         size_t ws_bytes, void* stream) {
   clear_error();
@@ -368,12 +400,15 @@ extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K,
   if (R < 1 || K < 1 || K > 128 || (long)R * K > kMaxCand)
     return fail(DSP_ERR_SHAPE, "need R >= 1, 1 <= K <= 128, R*K <= %d (R=%d K=%d)", kMaxCand, R, K);
   if (n_cost < R * K + 1) return fail(DSP_ERR_SHAPE, "cost table needs R*K+1 = %d entries", R * K + 1);
-  if (mode != DSP_SCHED_EARLY_STOP && mode != DSP_SCHED_ARGMAX)
+  if (mode != DSP_SCHED_EARLY_STOP && mode != DSP_SCHED_ARGMAX && mode != DSP_SCHED_TOP_M &&
+      mode != DSP_SCHED_THRESHOLD)
     return fail(DSP_ERR_UNSUPPORTED, "unknown scheduler mode %d", mode);
+  if (mode == DSP_SCHED_THRESHOLD && !(threshold == threshold))
+    return fail(DSP_ERR_SHAPE, "threshold must not be NaN");
   if (!conf || !cost || !windows) return fail(DSP_ERR_NULL, "conf, cost and windows are required");
   const int M = max_tokens < 0 ? R * K : (max_tokens < R * K ? max_tokens : R * K);
   launch(DSP_K_SCHEDULE, schedule_kernel, dim3(1), dim3(kSchedThreads), 0, (hipStream_t)stream, conf, R, K,
-         cost, mode, M, quant_bits(R, K), windows, survival, stats);
+         cost, mode, M, threshold, quant_bits(R, K), windows, survival, stats);
   return hip_check(hipGetLastError(), "schedule launch");
 }
 

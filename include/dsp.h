@@ -57,6 +57,8 @@ extern "C" {
 
 #define DSP_SCHED_EARLY_STOP  0
 #define DSP_SCHED_ARGMAX      1
+#define DSP_SCHED_TOP_M       2
+#define DSP_SCHED_THRESHOLD   3
 
 /* Library version, (major << 16) | minor. */
 int32_t dsp_version(void);
@@ -91,17 +93,24 @@ int32_t dsp_philox_uniforms(const uint64_t* ctr, int64_t n, uint64_t seed, doubl
 /* (DSP_SCHED_EARLY_STOP, the non-anticipating rule of [N] 5.2), or the       */
 /* smallest j maximising E_j / cost[j] (DSP_SCHED_ARGMAX, the SPS-argmax      */
 /* budget of [S] / global search of [N] 9.2; cost must then be > 0).          */
+/* DSP_SCHED_TOP_M takes the first max_tokens candidates of that order: a     */
+/* verify capacity decided earlier (from confidences two steps old, [N] 9.2)  */
+/* with the ranking from the current survivals. DSP_SCHED_THRESHOLD is the    */
+/* conventional fixed threshold ([N] 5.2, 8.3): n_i = #{k : S_{i,k} >=        */
+/* threshold} on the fp64 survival; threshold 0 verifies the full block.      */
 /* Survivals are summed as exact integers on a 2^-Q grid,                     */
 /* Q = min(40, 53 - ceil(log2(R*K))), so the windows are bit-reproducible.    */
 /*   cost      [n_cost] fp64, n_cost >= R*K + 1 (device).                     */
-/*   max_tokens  cap on N = sum_i n_i (< 0: none).                             */
+/*   max_tokens  cap on N = sum_i n_i (< 0: none); the capacity in TOP_M mode.  */
+/*   threshold   survival threshold of DSP_SCHED_THRESHOLD (ignored otherwise;  */
+/*               NaN is rejected).                                             */
 /* Outputs: windows [R] int32 (n_i in [0, K]); survival [R, K] fp64 (nullable);*/
 /* stats [4] fp64 (nullable): N, E (in probability units), J = E / cost[N], Q. */
 /* Limits: 1 <= K <= 128, 1 <= R, R*K <= 8192.                                 */
 /* ------------------------------------------------------------------------ */
 size_t dsp_schedule_windows_workspace_size(int32_t R, int32_t K);
 int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
-                             int32_t n_cost, int32_t mode, int32_t max_tokens,
+                             int32_t n_cost, int32_t mode, int32_t max_tokens, double threshold,
                              int32_t* windows, double* survival, double* stats,
                              void* ws, size_t ws_bytes, void* stream);
 

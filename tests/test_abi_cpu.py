@@ -65,9 +65,10 @@ def test_host_validation_codes():
                                           None, None, None, None, p, p, p, None, None, p, p, 16, None))
     assert rc == -5
     # schedule: too many candidates, short cost table, unknown mode
-    assert lib.dsp_schedule_windows(p, 9000, 1, p, 9001, 0, -1, p, None, None, None, 0, None) == -2
-    assert lib.dsp_schedule_windows(p, 4, 4, p, 16, 0, -1, p, None, None, None, 0, None) == -2
-    assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 3, -1, p, None, None, None, 0, None) == -6
+    assert lib.dsp_schedule_windows(p, 9000, 1, p, 9001, 0, -1, 0.0, p, None, None, None, 0, None) == -2
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 16, 0, -1, 0.0, p, None, None, None, 0, None) == -2
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 4, -1, 0.0, p, None, None, None, 0, None) == -6
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 3, -1, float('nan'), p, None, None, None, 0, None) == -2
     # pack: descending tiers, too many tiers
     tiers = (ctypes.c_int32 * 2)(8, 4)
     assert lib.dsp_pack_ragged(p, p, p, 4, 3, 4, ctypes.cast(tiers, ctypes.c_void_p), 2, p, p, p, p, p, p,

@@ -12,11 +12,11 @@ from parity import host, to_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _sched(conf, cost, mode=0, cap=-1):
-    print(f"schedule R={conf.shape[0]} K={conf.shape[1]} mode={mode} cap={cap}", flush=True)
-    g = dsp.schedule_windows(to_gpu(conf), to_gpu(cost), mode=mode, max_tokens=cap)
+def _sched(conf, cost, mode=0, cap=-1, threshold=0.0):
+    print(f"schedule R={conf.shape[0]} K={conf.shape[1]} mode={mode} cap={cap} th={threshold}", flush=True)
+    g = dsp.schedule_windows(to_gpu(conf), to_gpu(cost), mode=mode, max_tokens=cap, threshold=threshold)
     torch.cuda.synchronize()
-    o = osch.schedule_windows(conf, cost, mode=mode, max_tokens=cap)
+    o = osch.schedule_windows(conf, cost, mode=mode, max_tokens=cap, threshold=threshold)
     np.testing.assert_array_equal(host(g["windows"]), o["windows"])
     np.testing.assert_array_equal(host(g["survival"]), o["survival"])
     st = host(g["stats"])
@@ -53,9 +53,24 @@ def test_schedule_special_cases():
     assert np.all(o["windows"] == 0)
 
 
+@pytest.mark.parametrize("R,K", [(1, 1), (7, 16), (64, 7), (256, 16), (8192, 1), (64, 128)])
+def test_schedule_top_m_and_threshold(R, K):
+    rng = np.random.Generator(np.random.PCG64(R * 7 + K))
+    conf = rng.uniform(0.0, 1.0, size=(R, K)).astype(np.float32)
+    conf[rng.random((R, K)) < 0.05] = 1.0
+    cost = osch.additive_cost(1.0, 0.05, R * K)
+    for M in sorted({0, 1, R * K // 5, R * K // 2, R * K}):
+        _sched(conf, cost, osch.MODE_TOP_M, cap=M)
+    for th in (0.0, 1e-6, 0.1, 0.5, 0.9, 1.0, 1.5):
+        _sched(conf, cost, osch.MODE_THRESHOLD, threshold=th)
+
+
 def test_schedule_c3_workload():
     c = workloads.scheduled_verify_inputs()
+    for th in (0.3, 0.6):
+        _sched(c["conf"], c["cost"], osch.MODE_THRESHOLD, threshold=th)
     o = _sched(c["conf"], c["cost"])
+    _sched(c["conf"], c["cost"], osch.MODE_TOP_M, cap=o["N"])
     print("scheduled verify: N =", o["N"], "of", 256 * 16)
     assert 0 < o["N"] < 256 * 16
 
