@@ -83,19 +83,27 @@ def _sample(p_row, q_row, u):
 
 
 def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, req_id=None,
-                 forced_len=None):
+                 forced_len=None, cap=None):
     """Chain verify over a packed target buffer.
 
     tgt: [T_rows, V] logits (exact float values of the stored dtype);
     drf: [R, K, V]; draft_tok: [R, K]; cu_seqlens: [R+1].
     forced_len: optional [R]; when given, request i follows accept for
     k <= forced_len[i] and reject at forced_len[i] + 1 (replay of another
-    implementation's decisions); ``agree`` then tells where that differs from
-    the oracle's own decision.
+    implementation's decisions over the whole packed window); ``agree`` then
+    tells where that differs from the oracle's own decision.
+    cap: optional [R] commit windows (the SGLang article's cap-accept mode):
+    the decisions run over the whole packed window n_i, ``ceiling`` reports how
+    many drafts that full verify accepts, and only the first c_i = min(cap_i, n_i)
+    positions are committed: a rejection at k <= c_i stops there as usual; if the
+    first c_i drafts are all accepted, the bonus is drawn from p_{c_i+1} with the
+    sampling uniform of position c_i + 1 -- exactly what verifying the window c_i
+    alone commits (compact mode), while the full block exposes the ceiling.
 
     Returns dict(accepted_len [R], out_tokens [R, K+1] (-1 padded), stop_pos [R],
-    p_x, q_x [R, K] (every window position; 0 beyond the window and under greedy), accept_margin [R, K] (|u - ratio|,
-    +inf where not decided), sample_margin [R], agree [R] bool).
+    ceiling [R] (drafts accepted over the whole window), p_x, q_x [R, K] (every
+    window position; 0 beyond the window and under greedy), accept_margin [R, K]
+    (|u - ratio|, +inf where not decided), sample_margin [R], agree [R] bool).
     """
     tgt = np.asarray(tgt)
     drf = np.asarray(drf)
@@ -108,6 +116,7 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
     acc_len = np.zeros(R, dtype=np.int32)
     out = np.full((R, K + 1), -1, dtype=np.int32)
     stop = np.zeros(R, dtype=np.int32)
+    ceiling = np.zeros(R, dtype=np.int32)
     p_x = np.zeros((R, K), dtype=np.float64)
     q_x = np.zeros((R, K), dtype=np.float64)
     acc_margin = np.full((R, K), np.inf)
@@ -139,7 +148,6 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
             if take != own:
                 agree[i] = False
             if take:
-                out[i, k - 1] = x
                 continue
             stopped_at = k
             break
@@ -149,17 +157,24 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
                 agree[i] = False
         else:
             k = stopped_at
+        ceiling[i] = k - 1
+        c = n if cap is None else max(0, min(int(cap[i]), n))
+        if k > c + 1:  # the first c drafts are all accepted: commit them and draw the bonus after them
+            k = c + 1
+        for j in range(1, k):
+            out[i, j - 1] = int(draft_tok[i, j - 1])
         acc_len[i] = k - 1
         stop[i] = k
         if greedy:
             out[i, k - 1] = argmax_lowest(tgt[base + k - 1])
         else:
             p = np.exp(log_softmax(tgt[base + k - 1], temperature))
-            q = np.exp(log_softmax(drf[i, k - 1], temperature)) if k <= n else None
+            rejected = ceiling[i] + 1 <= c  # a rejection inside the commit window: residual draw
+            q = np.exp(log_softmax(drf[i, k - 1], temperature)) if rejected else None
             v, mg = _sample(p, q, u_smp[i, k - 1])
             out[i, k - 1] = v
             smp_margin[i] = mg
-    return dict(accepted_len=acc_len, out_tokens=out, stop_pos=stop, p_x=p_x, q_x=q_x,
+    return dict(accepted_len=acc_len, out_tokens=out, stop_pos=stop, ceiling=ceiling, p_x=p_x, q_x=q_x,
                 accept_margin=acc_margin, sample_margin=smp_margin, agree=agree)
 
 

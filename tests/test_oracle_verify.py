@@ -250,3 +250,49 @@ def test_tree_walk_planted_path():
     assert res["accepted_len"][0] == 4
     assert list(res["out_tokens"][0, :4]) == [token[j] for j in planted]
     assert res["out_tokens"][0, 4] == 0 and res["stop_node"][0] == 10
+
+
+# ---- cap-accept (SGLang article, "three verify modes" and "observability")
+
+
+def _cap_case(seed, R=12, K=6, V=29, T=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    t = rng.standard_normal((R, K + 1, V)) * 2.0
+    d = np.concatenate([t[:, :K] + rng.standard_normal((R, K, V)) * 0.6], axis=0)
+    Td = T if T > 0 else 1.0  # draft tokens drawn from softmax(d) (argmax-free at T = 0 too)
+    x = np.array([[rng.choice(V, p=np.exp(ov.log_softmax(d[i, k], Td))) for k in range(K)] for i in range(R)])
+    cap = rng.integers(0, K + 2, size=R)  # includes caps beyond the block
+    return t, d, x, cap
+
+
+@pytest.mark.parametrize("seed,T", [(1, 1.0), (2, 0.7), (3, 0.0), (4, 1.0)])
+def test_cap_accept_commits_what_compact_commits(seed, T):
+    """The committed result equals verifying only the window (compact): the same
+    uniforms, keyed by request and position, make every committed decision and
+    the draw identical; only the packing differs."""
+    t, d, x, cap = _cap_case(seed, T=T)
+    R, K1, V = t.shape
+    K = K1 - 1
+    tp, cu = _packed(t)
+    full = ov.verify_chain(tp, cu, d, x, T, seed=9, rnd=3, cap=cap)
+    c = np.minimum(cap, K)
+    tpc = np.concatenate([t[i, :c[i] + 1] for i in range(R)])
+    cuc = np.concatenate([[0], np.cumsum(c + 1)]).astype(np.int32)
+    compact = ov.verify_chain(tpc, cuc, d, x, T, seed=9, rnd=3)
+    for key in ("accepted_len", "out_tokens", "stop_pos"):
+        np.testing.assert_array_equal(full[key], compact[key])
+
+
+@pytest.mark.parametrize("seed,T", [(5, 1.0), (6, 0.0)])
+def test_cap_accept_ceiling_is_the_full_block_verify(seed, T):
+    t, d, x, cap = _cap_case(seed, T=T)
+    tp, cu = _packed(t)
+    full = ov.verify_chain(tp, cu, d, x, T, seed=2, rnd=1, cap=cap)
+    static = ov.verify_chain(tp, cu, d, x, T, seed=2, rnd=1)
+    np.testing.assert_array_equal(full["ceiling"], static["accepted_len"])
+    np.testing.assert_array_equal(static["ceiling"], static["accepted_len"])
+    assert np.all(full["accepted_len"] == np.minimum(full["ceiling"], np.minimum(cap, t.shape[1] - 1)))
+    # a cap at or beyond the block is the static verify itself
+    wide = ov.verify_chain(tp, cu, d, x, T, seed=2, rnd=1, cap=np.full(len(cap), 99))
+    for key in ("accepted_len", "out_tokens", "stop_pos"):
+        np.testing.assert_array_equal(wide[key], static[key])
