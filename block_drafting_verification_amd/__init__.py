@@ -181,16 +181,19 @@ def pack_ragged(windows, anchors, drafts, tiers=None, out=None, status=None, str
 
 def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,
                      round=0, req_id=None, max_rows=0, want_probs=True, out=None, status=None,
-                     stream=None, round_dev=None, row_req=None, row_pos=None, prepare=False):
+                     stream=None, round_dev=None, row_req=None, row_pos=None, cap=None, want_ceiling=False,
+                     prepare=False):
     """Batched ragged verify.
 
     tgt: packed target logits [T_rows, V] (bf16/fp32, unit inner stride);
     cu_seqlens: int32 [R+1]; draft_tok: int32 [R, K]; drf: draft logits [R, K, V]
     (T > 0); parent: int32 [R, K] selects the greedy tree walk (T must be 0).
     row_req/row_pos: the pack's packed-row maps (optional; locate draft rows directly).
-    Returns dict(accepted_len, out_tokens [R, K+1], stop_pos, p_x, q_x, status).
+    cap: int32 [R] cap-accept commit windows (chain only); want_ceiling (implied by cap)
+    adds 'ceiling' [R], the drafts accepted over the whole packed window.
+    Returns dict(accepted_len, out_tokens [R, K+1], stop_pos, p_x, q_x, status[, ceiling]).
     """
-    _on_gpu(tgt, cu_seqlens, draft_tok, drf, parent, req_id, round_dev, row_req, row_pos)
+    _on_gpu(tgt, cu_seqlens, draft_tok, drf, parent, req_id, round_dev, row_req, row_pos, cap)
     if row_req is not None or row_pos is not None:
         _need(row_req is not None and row_pos is not None and row_req.dtype == torch.int32 and
               row_pos.dtype == torch.int32, "row_req and row_pos: int32, together")
@@ -224,6 +227,10 @@ def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperat
     stop = _take(o, "stop_pos", lambda: torch.empty(R, dtype=torch.int32, device=dev))
     p_x = _take(o, "p_x", lambda: torch.empty(R, K, dtype=torch.float32, device=dev)) if want_probs else None
     q_x = _take(o, "q_x", lambda: torch.empty(R, K, dtype=torch.float32, device=dev)) if want_probs else None
+    if cap is not None:
+        _need(cap.dtype == torch.int32 and cap.numel() == R and cap.is_contiguous(), "cap: int32 [R]")
+    ceiling = _take(o, "ceiling", lambda: torch.empty(R, dtype=torch.int32, device=dev)) \
+        if (cap is not None or want_ceiling) else None
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     # bound the rows the device may read by what the target tensor holds
@@ -233,11 +240,14 @@ def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperat
     ws = _workspace(nbytes, dev, prepare)
     args = (_ptr(tgt), t_dt, tgt.stride(0), _ptr(cu_seqlens), _ptr(drf), d_dt, ld_dr, ld_dk,
             _ptr(draft_tok), draft_tok.stride(0), _ptr(parent), R, K, V, max_rows, float(temperature),
-            int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(row_req), _ptr(row_pos), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x),
-            _ptr(q_x), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+            int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(row_req), _ptr(row_pos), _ptr(cap),
+            _ptr(ceiling), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x), _ptr(q_x), _ptr(status), _ptr(ws),
+            ws.numel(), _stream(stream))
     res = dict(accepted_len=acc, out_tokens=toks, stop_pos=stop, p_x=p_x, q_x=q_x, status=status)
+    if ceiling is not None:
+        res["ceiling"] = ceiling
     return _finish(lib().dsp_verify_rejection, args, res, prepare,
-                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, ws))
+                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, cap, ws))
 
 
 def _check_markov(L, U, Wt):

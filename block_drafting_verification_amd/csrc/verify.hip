@@ -346,7 +346,24 @@ struct DecideArgs {
   float* q_x;
   int32_t* status;
   const uint64_t* round_dev;  // when set, the round is read from device memory
+  const int32_t* cap;         // cap-accept commit windows (nullable)
+  int32_t* ceiling;           // drafts accepted over the whole window (nullable)
 };
+
+// Cap-accept: the decisions cover the whole packed window n; only the first
+// c = min(cap_i, n) positions are committed. Returns the committed stop position
+// (first rejection if it lies inside the commit window, else c + 1, whose draw is
+// then the bonus from p_{c+1}) and reports the full-window acceptance.
+__device__ __forceinline__ int commit_stop(const DecideArgs& a, int i, int n, int kfull, int* cw) {
+  int c = n;
+  if (a.cap) {
+    c = a.cap[i];
+    c = c < 0 ? 0 : (c > n ? n : c);
+  }
+  *cw = c;
+  if (a.ceiling && (threadIdx.x & 63) == 0) a.ceiling[i] = kfull - 1;
+  return kfull <= c ? kfull : c + 1;
+}
 
 __device__ __forceinline__ float load_t(const DecideArgs& a, int row, int v) {
   const size_t off = (size_t)row * a.ld_t + v;
@@ -420,7 +437,8 @@ __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
     return;
   }
   const uint64_t rej = __ballot(pos && !acc);
-  const int kstop = rej ? __ffsll((unsigned long long)rej) : n + 1;
+  int cw;
+  const int kstop = commit_stop(a, i, n, rej ? __ffsll((unsigned long long)rej) : n + 1, &cw);
   const int accepted = kstop - 1;
   if (a.p_x && lane < a.K) {
     a.p_x[(size_t)i * a.K + lane] = pos ? (float)exp2(lp2) : 0.f;
@@ -432,7 +450,7 @@ __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
   if (a.K == 64 && lane == 0 && accepted < 64) orow[64] = -1;
   Job j;
   j.pad = 0.0;
-  if (kstop <= n) {
+  if (kstop <= cw) {
     if (k == kstop) {
       j.mode = JOB_RESID;
       j.kstop = kstop;
@@ -444,28 +462,29 @@ __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
       *jout = j;
     }
   } else {
-    // whole window accepted: bonus from the row after the last draft
-    bool writer = n < 64 ? bon : lane == 0;
+    // whole commit window accepted: bonus from the row after its last draft (lane cw
+    // holds that row's statistics and the sampling uniform of position cw + 1)
+    bool writer = cw < 64 ? lane == cw : lane == 0;
     if (writer) {
       double lt = lse_t, ub = us;
       bool b2 = bad;
-      if (n >= 64) {
+      if (cw >= 64) {
         b2 = false;
-        lt = merge_lse(a.tstats + (size_t)(base + n) * a.ncht, a.ncht, &b2);
-        uint64_t c2[4] = {rnd, rid, (uint64_t)(n + 1), 0ull};
+        lt = merge_lse(a.tstats + (size_t)(base + cw) * a.ncht, a.ncht, &b2);
+        uint64_t c2[4] = {rnd, rid, (uint64_t)(cw + 1), 0ull};
         philox4x64_10(c2, a.seed, 0ull);
         ub = unit_double(c2[1]);
       }
       j.mode = b2 ? JOB_NONE : JOB_BONUS;
-      j.kstop = n + 1;
-      j.trow = base + n;
+      j.kstop = cw + 1;
+      j.trow = base + cw;
       j.drow = -1;
       j.lse_t = lt;
       j.lse_d = 0.0;
       j.us = ub;
       *jout = j;
       if (b2) {
-        orow[n] = -1;
+        orow[cw] = -1;
         atomicOr(a.status, DSP_STATUS_NONFINITE);
       }
     }
@@ -563,16 +582,17 @@ __global__ __launch_bounds__(64) void verify_decide_greedy(DecideArgs a) {
     return;
   }
   const uint64_t rej = __ballot(active && !acc);
-  const int kstop = rej ? __ffsll((unsigned long long)rej) : n + 1;
+  int cw;
+  const int kstop = commit_stop(a, i, n, rej ? __ffsll((unsigned long long)rej) : n + 1, &cw);
   const int accepted = kstop - 1;
   int32_t* orow = a.out + (size_t)i * (a.K + 1);
   if (lane < accepted) orow[lane] = x;
   else if (lane > accepted && lane <= a.K) orow[lane] = -1;
   if (a.K == 64 && lane == 0 && accepted < 64) orow[64] = -1;
-  if (kstop <= n) {
+  if (kstop <= cw) {
     if (k == kstop) orow[lane] = am;
   } else if (lane == 0) {
-    orow[n] = (int)merge_argmax(a.tstats + (size_t)(base + n) * a.ncht, a.ncht);
+    orow[cw] = (int)merge_argmax(a.tstats + (size_t)(base + cw) * a.ncht, a.ncht);
   }
   if (a.p_x && lane < a.K) {
     a.p_x[(size_t)i * a.K + lane] = 0.f;
@@ -993,7 +1013,7 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
                                         int32_t V, int32_t max_rows, float temperature, uint64_t seed,
                                         uint64_t round, uint64_t* round_dev, const int64_t* req_id,
                                         const int32_t* row_req, const int32_t* row_pos,
-                                        int32_t* accepted_len,
+                                        const int32_t* cap, int32_t* ceiling, int32_t* accepted_len,
                                         int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x,
                                         int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
@@ -1004,6 +1024,7 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
     return fail(DSP_ERR_SHAPE, "temperature must be finite and >= 0");
   const bool greedy = temperature == 0.f;
   const bool tree = parent != nullptr;
+  if (tree && (cap || ceiling)) return fail(DSP_ERR_UNSUPPORTED, "cap-accept applies to chain verify only");
   if (tree && !greedy) return fail(DSP_ERR_UNSUPPORTED, "tree verify supports temperature 0 only");
   if (!greedy && d_dtype != DSP_F32 && d_dtype != DSP_BF16)
     return fail(DSP_ERR_DTYPE, "bad draft dtype %d", d_dtype);
@@ -1033,7 +1054,7 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
                tstats, dstats, greedy ? nullptr : round_dev, row_req, row_pos};
   DecideArgs da{tgt, t_dtype, ld_t, drf, ddt, ld_d_r, ld_d_k, cu_seqlens, draft_tok, ld_x, parent,
                 R, K, V, L.max_rows, L.ncht, L.nchd, cl, seed, round, req_id, tstats, dstats,
-                accepted_len, out_tokens, stop_pos, p_x, q_x, status, round_dev};
+                accepted_len, out_tokens, stop_pos, p_x, q_x, status, round_dev, cap, ceiling};
   if (greedy) {
     const long max_items = (long)L.max_rows * L.ncht;
     if (t_dtype == DSP_BF16) launch_greedy<uint16_t>(sa, da, s, max_items, tree);

@@ -176,6 +176,14 @@ int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const in
 /* packed row, as written by dsp_pack_ragged; when given, draft rows are      */
 /* located from them instead of by searching cu_seqlens (a row whose maps do */
 /* not match cu_seqlens falls back to the search).                           */
+/* cap (nullable, chain only): cap-accept commit windows [R] int32 ([S]       */
+/* "three verify modes"): the decisions cover the whole packed window n_i,    */
+/* but only the first c_i = min(max(cap_i, 0), n_i) positions are committed:  */
+/* a rejection at k <= c_i stops there; otherwise the c_i drafts are kept and */
+/* the bonus is drawn from p_{c_i+1} with the uniform of position c_i + 1 --  */
+/* the result of verifying the window c_i alone (compact).                    */
+/* ceiling (nullable, chain only): [R] int32, drafts accepted over the whole  */
+/* packed window (the acceptance ceiling that trimming hides, [S]).           */
 /* max_rows: host-known bound on cu_seqlens[R] (0 = R*(K+1)); tgt must hold    */
 /* at least that many rows. Rows past min(cu_seqlens[R], max_rows) are never  */
 /* read, and a request whose rows end past max_rows is a window fault.        */
@@ -191,6 +199,7 @@ int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
                              float temperature, uint64_t seed, uint64_t round,
                              uint64_t* round_dev, const int64_t* req_id,
                              const int32_t* row_req, const int32_t* row_pos,
+                             const int32_t* cap, int32_t* ceiling,
                              int32_t* accepted_len, int32_t* out_tokens, int32_t* stop_pos,
                              float* p_x, float* q_x, int32_t* status,
                              void* ws, size_t ws_bytes, void* stream);

@@ -47,22 +47,25 @@ def test_host_validation_codes():
     p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
     # verify: K out of range, bad dtype, missing pointers, negative temperature, small workspace
     rc, msg = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 65, 100, 0, 1.0, 0, 0,
-                                            None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
+                                            None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
     assert rc == -2 and "K" in msg
     rc, _ = _err(lib.dsp_verify_rejection(p, 5, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
-                                          None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
+                                          None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
     assert rc == -3
     rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, None, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
-                                          None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
+                                          None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
     assert rc == -1
     rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, -1.0, 0, 0,
-                                          None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
+                                          None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
     assert rc == -2
     rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, p, 4, 7, 100, 0, 1.0, 0, 0,
-                                          None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
+                                          None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30, None))
     assert rc == -6  # tree verify needs temperature 0
+    rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, p, 4, 7, 100, 0, 0.0, 0, 0,
+                                          None, None, None, None, p, None, p, p, p, None, None, p, p, 1 << 30, None))
+    assert rc == -6  # cap-accept is chain-only
     rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
-                                          None, None, None, None, p, p, p, None, None, p, p, 16, None))
+                                          None, None, None, None, None, None, p, p, p, None, None, p, p, 16, None))
     assert rc == -5
     # schedule: too many candidates, short cost table, unknown mode
     assert lib.dsp_schedule_windows(p, 9000, 1, p, 9001, 0, -1, 0.0, p, None, None, None, 0, None) == -2

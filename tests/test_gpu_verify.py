@@ -230,3 +230,51 @@ def test_philox_uniforms_bitwise():
     ref = np.stack([ophilox.to_unit_double(w) for w in ophilox.philox4x64_10(ctr, np.array([9, 0], np.uint64)).T], axis=1)
     got = host(dsp.philox_uniforms(to_gpu(ctr.view(np.int64)), 9))
     np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("T,dt,V", [(1.0, "bf16", 4099), (0.7, "f32", 1024), (0.0, "bf16", 40000)])
+def test_cap_accept(T, dt, V):
+    """Cap-accept on the full-block packing: the ceiling is the full verify, the committed
+    tokens are the compact verify of the cap window (oracle, and the GPU's own compact run)."""
+    R, K = 9, 6
+    case = workloads.verify_case(R, K, V, dtype=dt, seed=77 + V, t_sigma=2.0, d_sigma=0.4)
+    rng = np.random.Generator(np.random.PCG64(V))
+    cap = rng.integers(0, K + 2, size=R).astype(np.int32)
+    full = np.full(R, K)
+    tp = packed_from_dense(case["t"], full)
+    cu = cu_from_windows(full)
+    tg, dg, xg = logits_to_gpu(tp, dt)[:, :V], logits_to_gpu(case["d"], dt), to_gpu(case["x"].astype(np.int32))
+    print(f"cap-accept R={R} K={K} V={V} dtype={dt} T={T}", flush=True)
+    g = dsp.verify_rejection(tg, to_gpu(cu), xg, drf=dg, temperature=T, seed=4, round=2, cap=to_gpu(cap))
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    tv = values(tp[:, :V], dt).astype(np.float64)
+    dv = values(case["d"], dt).astype(np.float64)
+    ceil_g = host(g["ceiling"]).astype(np.int64)
+    own = ov.verify_chain(tv, cu, dv, case["x"], T, seed=4, rnd=2, cap=cap)
+    ties = TieCounter()
+    for i in np.nonzero(ceil_g != own["ceiling"])[0]:
+        k = int(min(ceil_g[i], own["ceiling"][i])) + 1
+        assert own["accept_margin"][i, k - 1] < 1e-6, (i, ceil_g[i], own["ceiling"][i])
+        ties.near += 1
+    rep = own if ties.near == 0 else ov.verify_chain(tv, cu, dv, case["x"], T, seed=4, rnd=2, cap=cap,
+                                                     forced_len=ceil_g)
+    ties.decisions += int(own["ceiling"].sum()) + R
+    acc, toks = host(g["accepted_len"]).astype(np.int64), host(g["out_tokens"]).astype(np.int64)
+    np.testing.assert_array_equal(acc, rep["accepted_len"])
+    np.testing.assert_array_equal(acc, np.minimum(ceil_g, np.minimum(cap, K)))
+    for i in range(R):
+        np.testing.assert_array_equal(toks[i, :acc[i]], rep["out_tokens"][i, :acc[i]])
+        if toks[i, acc[i]] != rep["out_tokens"][i, acc[i]]:
+            assert rep["sample_margin"][i] < 1e-6
+            ties.near += 1
+        assert np.all(toks[i, acc[i] + 1:] == -1)
+    ties.check()
+    # the GPU's own compact verify of the cap window commits the same tokens
+    c = np.minimum(cap, K)
+    tpc = packed_from_dense(case["t"], c)
+    gc = dsp.verify_rejection(logits_to_gpu(tpc, dt)[:, :V], to_gpu(cu_from_windows(c)), xg, drf=dg, temperature=T,
+                              seed=4, round=2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(gc["accepted_len"]), host(g["accepted_len"]))
+    np.testing.assert_array_equal(host(gc["out_tokens"]), host(g["out_tokens"]))
