@@ -27,7 +27,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-I", os.path.join(ROOT, "include"), "-Wno-unused-result",
+    "-I", os.path.join(ROOT, "include"), "-Wno-unused-result", "-Werror=return-type",
 ]
 
 

@@ -91,6 +91,19 @@ __device__ __forceinline__ double unit_double(uint64_t w) {
   return (double)(w >> 11) * 0x1.0p-53;
 }
 
+// Lane exchange at xor distance TS (1..32) inside a wavefront, with fixed patterns:
+// DPP quad permutes for 1 and 2, ds_swizzle xor masks for 4, 8 and 16 (no LDS memory
+// access), ds_bpermute only for 32.
+template <int TS>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  if (TS == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  if (TS == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  if (TS == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x101F);  // and 31, xor 4
+  if (TS == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x201F);
+  if (TS == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ 32) << 2), (int)x);
+}
+
 // Wave (64 lanes) reductions; deterministic butterfly order.
 template <typename T> __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

@@ -4,18 +4,18 @@
 // table"): block survival S_{i,k} = prod_{j<=k} c_{i,j}; all candidates are
 // ranked by S descending and taken greedily while expected throughput
 // E / cost(N) strictly rises (non-anticipating early stop), or the smallest N
-// maximising it (argmax mode). One workgroup of 1024 threads holds every
-// candidate in LDS:
-//   - survival in fp64 (one thread per request, left to right), quantised to
-//     a 2^-Q grid and packed into a unique 64-bit key
-//     ((2^41-1-Sq) << 23 | i << 7 | k-1) so ascending key order is
-//     (S desc, i asc, k asc) and any correct sort gives the same order;
-//   - bitonic sort (registers / wave shuffles / LDS by stride); exact uint64
-//     prefix sums of Sq;
-//   - the throughput test per candidate as two separate fp64 products
-//     (E_j * c[j-1] > E_{j-1} * c[j]) and a block minimum for the first failure;
-//   - window of request i = how many of its keys precede the first rejected key
-//     (prefix closure makes this the count of taken candidates).
+// maximising it (argmax mode). Two launches:
+//   - ranking, over many workgroups: each builds every candidate key in LDS --
+//     survival in fp64 (one thread per request, left to right), quantised to a
+//     2^-Q grid and packed into a unique 64-bit key ((2^41-1-Sq) << 23 | i << 7
+//     | k-1), so ascending key order is (S desc, i asc, k asc) -- and places a
+//     few of them at their rank (the number of smaller keys, counted by brute
+//     force: n^2 compares spread over the chip cost less than any sort in one
+//     workgroup);
+//   - selection, one workgroup of 1024 threads: exact uint64 prefix sums of Sq,
+//     the throughput test per candidate as two separate fp64 products
+//     (E_j * c[j-1] > E_{j-1} * c[j]) with a block minimum for the first
+//     failure, and window of request i = how many of its candidates are taken.
 //
 // Pack (SGLang article, "Ragged verify"): exclusive scan of n_i + 1, then each
 // request writes its anchor and first n_i drafts front to back.
@@ -62,150 +62,115 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* wsum) {
   return wsum[w] + inc - v;
 }
 
-// Lane exchange at xor distance TS (1..32) inside a wavefront, with fixed patterns:
-// DPP quad permutes for 1 and 2, ds_swizzle xor masks for 4, 8 and 16 (no LDS memory
-// access), ds_bpermute only for 32.
-template <int TS>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
-  if (TS == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-  if (TS == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
-  if (TS == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x101F);  // and 31, xor 4
-  if (TS == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x201F);
-  if (TS == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
-  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ 32) << 2), (int)x);
-}
-template <int TS, int E>
-__device__ __forceinline__ void xor_lanes(const uint64_t* v, uint64_t* o) {
-  uint32_t lo[E], hi[E];
+// Candidate keys of every (request, position): survival in fp64, one thread per
+// request multiplying left to right, quantised and packed (optionally also written
+// out as the survival table).
+__device__ void candidate_keys(const float* __restrict__ conf, int R, int K, double scale,
+                               float* s_conf, uint64_t* keys, double* survival) {
+  const int n = R * K;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) s_conf[j] = conf[j];
+  __syncthreads();
+  for (int i = threadIdx.x; i < R; i += blockDim.x) {
+    double s = 1.0;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      float cf[8];  // eight reads in flight, then the products in order
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    lo[e] = xor_lane<TS>((uint32_t)v[e]);
-    hi[e] = xor_lane<TS>((uint32_t)(v[e] >> 32));
-  }
+      for (int q = 0; q < 8; ++q) cf[q] = k0 + q < K ? s_conf[i * K + k0 + q] : 1.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = ((uint64_t)hi[e] << 32) | lo[e];
-}
-
-// Ascending bitonic sort of keys[0..P) (P a power of two, 64 * E <= P <= 1024 * E) by
-// the first P / E threads of a 1024-thread block, E consecutive keys per thread:
-// strides below E are compare-exchanges in registers, strides below 64*E go through
-// lane exchanges inside a wavefront (fixed patterns when E > 1), and only wider
-// strides through LDS, so
-// most of the log2(P)(log2(P)+1)/2 stages need neither memory nor a barrier.
-template <int E>
-__device__ void bitonic_keys(uint64_t* keys, int P) {
-  const int tid = threadIdx.x;
-  const bool act = tid * E < P;
-  uint64_t v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = act ? keys[tid * E + e] : ~0ull;
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < E) {
-        // partner in the same thread: element e ^ stride (stride in {1, 2, 4})
-#pragma unroll
-        for (int sb = 1; sb < E; sb <<= 1) {
-          if (sb != stride) continue;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            if (e & sb) continue;
-            const bool up = ((tid * E + e) & size) == 0;
-            const uint64_t a = v[e], b = v[e | sb];
-            const bool sw = (a > b) == up;
-            v[e] = sw ? b : a;
-            v[e | sb] = sw ? a : b;
-          }
+      for (int q = 0; q < 8; ++q) {
+        const int k = k0 + q;
+        if (k < K) {
+          s = __dmul_rn(s, (double)cf[q]);
+          if (survival) survival[(size_t)i * K + k] = s;
+          keys[i * K + k] = sched_key(quantise(s, scale), i, k);
         }
-        continue;
-      }
-      const int ts = stride / E;  // distance in threads
-      uint64_t o[E];
-      if (ts < 64 && E == 1) {
-        // one key per thread: a single lane permute costs less than a branch per stage
-        o[0] = __shfl_xor(v[0], ts, 64);
-      } else if (ts < 64) {
-        // one uniform branch per stage, then straight-line fixed-pattern exchanges
-        switch (ts) {
-          case 1: xor_lanes<1, E>(v, o); break;
-          case 2: xor_lanes<2, E>(v, o); break;
-          case 4: xor_lanes<4, E>(v, o); break;
-          case 8: xor_lanes<8, E>(v, o); break;
-          case 16: xor_lanes<16, E>(v, o); break;
-          default: xor_lanes<32, E>(v, o); break;
-        }
-      } else {
-        __syncthreads();
-        if (act)
-#pragma unroll
-          for (int e = 0; e < E; ++e) keys[tid * E + e] = v[e];
-        __syncthreads();
-        if (act)
-#pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = keys[(tid ^ ts) * E + e];
-      }
-      const bool up = ((tid * E) & size) == 0;     // size > stride >= E: same for all e
-      const bool low = ((tid * E) & stride) == 0;  // likewise
-      const bool keep_min = low == up;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool lt = o[e] < v[e];
-        v[e] = lt == keep_min ? o[e] : v[e];
       }
     }
   }
-  __syncthreads();
-  if (act)
-#pragma unroll
-    for (int e = 0; e < E; ++e) keys[tid * E + e] = v[e];
+  // padding keys (never below a real key) up to a whole number of 128-key strips
+  for (int j = n + threadIdx.x; j < ((n + 127) & ~127); j += blockDim.x) keys[j] = ~0ull;
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
-    const float* __restrict__ conf, int R, int K, const double* __restrict__ cost, int mode, int M,
-    double threshold, int Q, int32_t* __restrict__ windows, double* __restrict__ survival,
-    double* __restrict__ stats) {
-  __shared__ uint64_t keys[kMaxCand];
+// Ranking, spread over many workgroups: each workgroup builds every key in LDS and
+// ranks kRankCand of them by counting the keys below each (keys are unique, so the
+// counts are a permutation of 0..n-1), 16 lanes per candidate over interleaved
+// slices of the keys: slice s reads key pairs (2s, 2s+1) of every 32-key strip
+// (lanes of one slice read the same LDS words: a broadcast), four strips per step.
+// The sorted keys go to sorted[rank].
+constexpr int kRankThreads = 256;
+constexpr int kSelPer = kMaxCand / kSchedThreads;  // ranks per thread in the selection
+constexpr int kRankCand = 16;
+constexpr int kRankSlices = kRankThreads / kRankCand;
+
+__global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(const float* __restrict__ conf, int R,
+                                                                     int K, int Q, double* __restrict__ survival,
+                                                                     uint64_t* __restrict__ sorted) {
+  __shared__ __align__(16) uint64_t keys[kMaxCand];
   __shared__ float s_conf[kMaxCand];
+  __shared__ int part[kRankThreads];
+  const int tid = threadIdx.x;
+  const int n = R * K;
+  candidate_keys(conf, R, K, ldexp(1.0, Q), s_conf, keys, blockIdx.x == 0 ? survival : nullptr);
+  const int cl = tid % kRankCand, sl = tid / kRankCand;
+  const int c = blockIdx.x * kRankCand + cl;
+  const uint64_t x = c < n ? keys[c] : 0ull;
+  int cnt = 0;
+  const int np = (n + 127) & ~127;  // padded with keys above every real one
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  for (int j = 2 * sl; j < np; j += 128) {
+    u64x2 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *(const u64x2*)&keys[j + 32 * q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += (v[q].x < x ? 1 : 0) + (v[q].y < x ? 1 : 0);
+  }
+  part[tid] = cnt;
+  __syncthreads();
+  if (sl == 0 && c < n) {
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < kRankSlices; ++q) r += part[q * kRankCand + cl];
+    sorted[r] = x;
+  }
+}
+
+// Selection over the ranked keys (one workgroup): exact prefix sums of Sq, the
+// throughput test, E at N, and the windows; or the fixed-threshold rule straight
+// from the survivals (then no ranking is needed and sorted is unused).
+__global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
+    const float* __restrict__ conf, int R, int K, const double* __restrict__ cost, int mode, int M,
+    double threshold, int Q, const uint64_t* __restrict__ sorted, int32_t* __restrict__ windows,
+    double* __restrict__ survival, double* __restrict__ stats) {
+  __shared__ float s_conf[kMaxCand];  // threshold mode
+  __shared__ int cnt[kMaxCand];
   __shared__ uint64_t wsum[kSchedThreads / 64];
   __shared__ double smd[kSchedThreads / 64];
   __shared__ int smi[kSchedThreads / 64];
   __shared__ uint64_t e_at_n;
   const int tid = threadIdx.x;
   const int n = R * K;
-  int P = 1;
-  while (P < n) P <<= 1;
   const double scale = ldexp(1.0, Q);
-
-  // confidences staged in LDS with coalesced loads, then survival products and keys
-  for (int j = tid; j < n; j += kSchedThreads) s_conf[j] = conf[j];
-  __syncthreads();
-  for (int i = tid; i < R; i += kSchedThreads) {
-    double s = 1.0;
-    for (int k = 0; k < K; ++k) {
-      s = __dmul_rn(s, (double)s_conf[i * K + k]);
-      if (survival) survival[(size_t)i * K + k] = s;
-      keys[i * K + k] = sched_key(quantise(s, scale), i, k);
-    }
-  }
-  for (int j = n + tid; j < (P < 64 ? 64 : P); j += kSchedThreads) keys[j] = ~0ull;
-  __syncthreads();
 
   if (mode == DSP_SCHED_THRESHOLD) {
     // n_i = #{k : S_{i,k} >= threshold} on the fp64 survival; no ranking needed
+    for (int j = tid; j < n; j += kSchedThreads) s_conf[j] = conf[j];
+    __syncthreads();
     uint64_t esum = 0;
     int cnt_all = 0;
     for (int i = tid; i < R; i += kSchedThreads) {
       double s = 1.0;
-      int cnt = 0;
+      int c = 0;
       for (int k = 0; k < K; ++k) {
         s = __dmul_rn(s, (double)s_conf[i * K + k]);
+        if (survival) survival[(size_t)i * K + k] = s;
         if (s >= threshold) {
-          ++cnt;
+          ++c;
           esum += quantise(s, scale);
         }
       }
-      windows[i] = cnt;
-      cnt_all += cnt;
+      windows[i] = c;
+      cnt_all += c;
     }
     const int Nt = block_sum<kSchedThreads / 64>(cnt_all, smi);
     const uint64_t Et = block_exclusive_scan_u64(esum, wsum) + esum;  // inclusive; the last thread holds the total
@@ -219,19 +184,22 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     return;
   }
 
-  // bitonic sort, ascending, over at least one full wavefront of slots (padding keys
-  // are ~0 and sort last), with as many threads as the size allows
-  const int PS = P < 64 ? 64 : P;
-  if (PS <= 1024) bitonic_keys<1>(keys, PS);
-  else if (PS == 2048) bitonic_keys<2>(keys, PS);
-  else if (PS == 4096) bitonic_keys<4>(keys, PS);
-  else bitonic_keys<8>(keys, PS);
-
-  // exact prefix sums over the first M sorted candidates; thread t owns [t*C, t*C + C)
+  // thread t owns ranks [t*C, t*C + C) of the first M (C <= kSelPer): its keys and the
+  // cost entries it needs are loaded straight into registers, all in one round trip
   const int C = (M + kSchedThreads - 1) / kSchedThreads;
   const int p0 = min(M, tid * C), p1 = min(M, p0 + C);
+  uint64_t kq[kSelPer];
+  double cq[kSelPer + 1];
+#pragma unroll
+  for (int q = 0; q < kSelPer; ++q) kq[q] = p0 + q < p1 ? sorted[p0 + q] : 0ull;
+#pragma unroll
+  for (int q = 0; q <= kSelPer; ++q) cq[q] = p0 + q <= p1 ? cost[p0 + q] : 0.0;
+  for (int i = tid; i < R; i += kSchedThreads) cnt[i] = 0;
+
+  // exact prefix sums of the quantised survivals in rank order
   uint64_t local = 0;
-  for (int p = p0; p < p1; ++p) local += key_sq(keys[p]);
+#pragma unroll
+  for (int q = 0; q < kSelPer; ++q) local += p0 + q < p1 ? key_sq(kq[q]) : 0ull;
   const uint64_t ex = block_exclusive_scan_u64(local, wsum);
 
   int N;
@@ -240,16 +208,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   } else if (mode == DSP_SCHED_EARLY_STOP) {
     int first_fail = 0x7fffffff;
     uint64_t run = ex;
-    for (int p = p0; p < p1; ++p) {
-      const int j = p + 1;
-      const uint64_t Ej = run + key_sq(keys[p]);
-      const double lhs = __dmul_rn((double)Ej, cost[j - 1]);
-      const double rhs = __dmul_rn((double)run, cost[j]);
-      if (!(lhs > rhs)) {
-        first_fail = j;
-        break;
+#pragma unroll
+    for (int q = 0; q < kSelPer; ++q) {
+      if (p0 + q < p1 && first_fail == 0x7fffffff) {
+        const int j = p0 + q + 1;
+        const uint64_t Ej = run + key_sq(kq[q]);
+        const double lhs = __dmul_rn((double)Ej, cq[q]);       // E_j * c[j-1]
+        const double rhs = __dmul_rn((double)run, cq[q + 1]);  // E_{j-1} * c[j]
+        if (!(lhs > rhs)) first_fail = j;
+        run = Ej;
       }
-      run = Ej;
     }
     const int ff = block_min<kSchedThreads / 64>(first_fail, smi);
     N = ff == 0x7fffffff ? M : ff - 1;
@@ -257,17 +225,20 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     double best = -1.0;
     int bj = 0x7fffffff;
     if (tid == 0) {
-      best = __ddiv_rn(0.0, cost[0]);
+      best = __ddiv_rn(0.0, cq[0]);
       bj = 0;
     }
     uint64_t run = ex;
-    for (int p = p0; p < p1; ++p) {
-      const int j = p + 1;
-      run += key_sq(keys[p]);
-      const double J = __ddiv_rn((double)run, cost[j]);
-      if (J > best) {
-        best = J;
-        bj = j;
+#pragma unroll
+    for (int q = 0; q < kSelPer; ++q) {
+      if (p0 + q < p1) {
+        const int j = p0 + q + 1;
+        run += key_sq(kq[q]);
+        const double J = __ddiv_rn((double)run, cq[q + 1]);
+        if (J > best) {
+          best = J;
+          bj = j;
+        }
       }
     }
     const double Jm = block_max<kSchedThreads / 64>(best, smd);
@@ -275,27 +246,21 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     N = jm;
   }
 
-  // E at N (sum of the first N quantised survivals)
-  if (tid == 0) e_at_n = 0;
-  __syncthreads();
+  // E at N (sum of the first N quantised survivals), and the window of request i: how
+  // many of its candidates are among the first N (its taken candidates are its leading
+  // positions whenever the survival does not grow along k)
   if (N > 0 && N - 1 >= p0 && N - 1 < p1) {
     uint64_t run = ex;
-    for (int p = p0; p < N; ++p) run += key_sq(keys[p]);
+#pragma unroll
+    for (int q = 0; q < kSelPer; ++q) run += p0 + q < N ? key_sq(kq[q]) : 0ull;  // N <= p1 here
     e_at_n = run;
   }
+  if (N == 0 && tid == 0) e_at_n = 0;
+#pragma unroll
+  for (int q = 0; q < kSelPer; ++q)
+    if (p0 + q < p1 && p0 + q < N) atomicAdd(&cnt[(int)((kq[q] >> 7) & 0xFFFFu)], 1);
   __syncthreads();
-  const uint64_t thr = N < n ? keys[N] : ~0ull;
-
-  // window of request i: its candidates ranked before the first untaken one
-  for (int i = tid; i < R; i += kSchedThreads) {
-    double s = 1.0;
-    int cnt = 0;
-    for (int k = 0; k < K; ++k) {
-      s = __dmul_rn(s, (double)s_conf[i * K + k]);
-      cnt += sched_key(quantise(s, scale), i, k) < thr ? 1 : 0;
-    }
-    windows[i] = cnt;
-  }
+  for (int i = tid; i < R; i += kSchedThreads) windows[i] = cnt[i];
   if (stats && tid == 0) {
     const double E = ldexp((double)e_at_n, -Q);
     stats[0] = (double)N;
@@ -385,9 +350,8 @@ int quant_bits(int R, int K) {
 using namespace dsp;
 
 extern "C" size_t dsp_schedule_windows_workspace_size(int32_t R, int32_t K) {
-  (void)R;
-  (void)K;
-  return 0;
+  if (R < 1 || K < 1) return 0;
+  return ((size_t)R * K * sizeof(uint64_t) + 255) & ~(size_t)255;  // the ranked keys
 }
 
 extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
@@ -395,8 +359,6 @@ extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K,
                                         int32_t* windows, double* survival, double* stats, void* ws,
                                         size_t ws_bytes, void* stream) {
   clear_error();
-  (void)ws;
-  (void)ws_bytes;
   if (R < 1 || K < 1 || K > 128 || (long)R * K > kMaxCand)
     return fail(DSP_ERR_SHAPE, "need R >= 1, 1 <= K <= 128, R*K <= %d (R=%d K=%d)", kMaxCand, R, K);
   if (n_cost < R * K + 1) return fail(DSP_ERR_SHAPE, "cost table needs R*K+1 = %d entries", R * K + 1);
@@ -406,9 +368,19 @@ extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K,
   if (mode == DSP_SCHED_THRESHOLD && !(threshold == threshold))
     return fail(DSP_ERR_SHAPE, "threshold must not be NaN");
   if (!conf || !cost || !windows) return fail(DSP_ERR_NULL, "conf, cost and windows are required");
+  if (!ws || ws_bytes < dsp_schedule_windows_workspace_size(R, K))
+    return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", dsp_schedule_windows_workspace_size(R, K));
   const int M = max_tokens < 0 ? R * K : (max_tokens < R * K ? max_tokens : R * K);
-  launch(DSP_K_SCHEDULE, schedule_kernel, dim3(1), dim3(kSchedThreads), 0, (hipStream_t)stream, conf, R, K,
-         cost, mode, M, threshold, quant_bits(R, K), windows, survival, stats);
+  const int Q = quant_bits(R, K);
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* sorted = (uint64_t*)ws;
+  if (mode != DSP_SCHED_THRESHOLD) {
+    const int g = (R * K + kRankCand - 1) / kRankCand;
+    launch(DSP_K_SCHEDULE_RANK, schedule_rank_kernel, dim3(g), dim3(kRankThreads), 0, s, conf, R, K, Q, survival,
+           sorted);
+  }
+  launch(DSP_K_SCHEDULE, schedule_select_kernel, dim3(1), dim3(kSchedThreads), 0, s, conf, R, K, cost, mode, M,
+         threshold, Q, (const uint64_t*)sorted, windows, survival, stats);
   return hip_check(hipGetLastError(), "schedule launch");
 }
 

@@ -116,11 +116,44 @@ template <typename T> __device__ __forceinline__ RowGeom row_geom(const T* p, in
   return {head, nvec, head + nvec * PV};
 }
 
-// One (row, chunk) of the sampled statistics pass.
+// Partial log2-sum-exp2 of a set of logits times c: the set's sum of 2^(x c - ref),
+// with ref the set's maximum times c (-inf and 0 for an empty set).
+struct LsePart {
+  float ref;
+  float pad;
+  double sum;
+};
+
+// Merge of two partials: factors 2^(ref - max) <= 1 in fp32, products and sum in fp64.
+// Symmetric bit for bit (fp contraction is off), so both lanes of a butterfly pair end
+// with the same value.
+__device__ __forceinline__ void lse_merge(float& r, double& s, float r2, double s2) {
+  const float H = fmaxf(r, r2);
+  if (H != -INFINITY) {
+    const double a = s * (double)fast_exp2(r - H);
+    const double b = s2 * (double)fast_exp2(r2 - H);
+    s = a + b;
+  }
+  r = H;
+}
+template <int TS> __device__ __forceinline__ void lse_xor_step(float& r, double& s) {
+  const uint64_t sb = (uint64_t)__double_as_longlong(s);
+  const float r2 = __uint_as_float(xor_lane<TS>(__float_as_uint(r)));
+  const uint32_t lo = xor_lane<TS>((uint32_t)sb), hi = xor_lane<TS>((uint32_t)(sb >> 32));
+  lse_merge(r, s, r2, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+}
+
+// One (row, chunk) of the sampled statistics pass: each thread reduces its own
+// elements against its own maximum, then one butterfly merge per wavefront and one
+// LDS exchange between wavefronts (double-buffered by *phase, so a workgroup that
+// loops over items needs a single barrier per item).
+// The slot is written only if chk is null or *chk == chk_val (read after the row's
+// loads are issued, so its latency overlaps them); returns whether it was.
 template <typename T>
-__device__ __forceinline__ void chunk_stats(const T* __restrict__ row, int V, int nch, int c,
-                                            float cl, StatSlot* __restrict__ out, float* smf,
-                                            double* smd) {
+__device__ __forceinline__ bool chunk_stats(const T* __restrict__ row, int V, int nch, int c,
+                                            float cl, StatSlot* __restrict__ out,
+                                            LsePart (*sml)[kThreads / 64], int* phase,
+                                            const int32_t* chk = nullptr, int chk_val = 0) {
   constexpr int PV = Elem<T>::kPerVec;
   const RowGeom g = row_geom(row, V);
   const int cv = (g.nvec + nch - 1) / nch;
@@ -129,6 +162,7 @@ __device__ __forceinline__ void chunk_stats(const T* __restrict__ row, int V, in
   const u32x4* vp = (const u32x4*)(row + g.head);
   const int tid = threadIdx.x;
 
+  int chk_got = chk ? *chk : chk_val;
   u32x4 buf[kVpt];
 #pragma unroll
   for (int j = 0; j < kVpt; ++j) {
@@ -139,6 +173,8 @@ __device__ __forceinline__ void chunk_stats(const T* __restrict__ row, int V, in
   float sh = -INFINITY, st = -INFINITY;
   if (c == 0 && tid < g.head) sh = Elem<T>::val(row, tid);
   if (c == nch - 1 && tid < V - g.tail) st = Elem<T>::val(row, g.tail + tid);
+  asm volatile("" : "+v"(chk_got));  // the check lands here, while the row is in flight
+  const bool ok = chk_got == chk_val;
 
   float m = fmaxf(sh, st);
 #pragma unroll
@@ -151,34 +187,53 @@ __device__ __forceinline__ void chunk_stats(const T* __restrict__ row, int V, in
       for (int e = 0; e < PV; ++e) m = fmaxf(m, x[e]);
     }
   }
-  const float M = block_max<kThreads / 64>(m, smf);
-  const float ref = M * cl;
+  // unpack again below instead of keeping every element live as a float
+#pragma unroll
+  for (int j = 0; j < kVpt; ++j) asm volatile("" : "+v"(buf[j]));
+  float ref = m * cl;
   double s = 0.0;
+  if (m != -INFINITY) {
 #pragma unroll
-  for (int j = 0; j < kVpt; ++j) {
-    const int v = v0 + tid + j * kThreads;
-    if (v < v1) {
-      float x[PV];
-      Elem<T>::unpack(buf[j], x);
-      float e8[PV];
+    for (int j = 0; j < kVpt; ++j) {
+      const int v = v0 + tid + j * kThreads;
+      if (v < v1) {
+        float x[PV];
+        Elem<T>::unpack(buf[j], x);
+        float e8[PV];
 #pragma unroll
-      for (int e = 0; e < PV; ++e) e8[e] = fast_exp2(__builtin_fmaf(x[e], cl, -ref));
-      // pairwise within the vector, fp64 across vectors
+        for (int e = 0; e < PV; ++e) e8[e] = fast_exp2(__builtin_fmaf(x[e], cl, -ref));
+        // pairwise within the vector, fp64 across vectors
 #pragma unroll
-      for (int w = PV / 2; w > 0; w >>= 1)
+        for (int w = PV / 2; w > 0; w >>= 1)
 #pragma unroll
-        for (int e = 0; e < w; ++e) e8[e] += e8[e + w];
-      s += (double)e8[0];
+          for (int e = 0; e < w; ++e) e8[e] += e8[e + w];
+        s += (double)e8[0];
+      }
     }
+    if (sh != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(sh, cl, -ref));
+    if (st != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(st, cl, -ref));
   }
-  if (sh != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(sh, cl, -ref));
-  if (st != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(st, cl, -ref));
-  const double S = block_sum<kThreads / 64>(s, smd);
+  lse_xor_step<1>(ref, s);
+  lse_xor_step<2>(ref, s);
+  lse_xor_step<4>(ref, s);
+  lse_xor_step<8>(ref, s);
+  lse_xor_step<16>(ref, s);
+  lse_xor_step<32>(ref, s);
+  LsePart* buf2 = sml[*phase];
+  *phase ^= 1;
+  if ((tid & 63) == 0) buf2[tid >> 6] = LsePart{ref, 0.f, s};
+  __syncthreads();
+  if (!ok) return false;
   if (tid == 0) {
-    out->ref = ref;
-    out->flag = (M == INFINITY || M != M) ? 1u : 0u;
+    float R = buf2[0].ref;
+    double S = buf2[0].sum;
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) lse_merge(R, S, buf2[w].ref, buf2[w].sum);
+    out->ref = R;
+    out->flag = (R == INFINITY || R != R) ? 1u : 0u;
     out->sum = S;
   }
+  return true;
 }
 
 // One (row, chunk) of the greedy pass: (max value, lowest index) as a 64-bit key.
@@ -514,47 +569,76 @@ constexpr int kCuLds = 2048;  // requests whose offsets are staged in LDS for th
 // A draft item finds its (request, position) in the pack's row maps when the caller
 // passes them, else by a binary search of cu_seqlens staged in LDS.
 template <typename TT, typename TD>
-__global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a) {
-  __shared__ float smf[kThreads / 64];
-  __shared__ double smd[kThreads / 64];
+__global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a, const int32_t* __restrict__ cu_,
+                                                                 const int32_t* __restrict__ rq_,
+                                                                 const int32_t* __restrict__ rp_) {
+  // cu_seqlens and the row maps are only read here; as restrict-qualified parameters their
+  // workgroup-uniform reads go through the scalar cache instead of one vector request per
+  // wavefront to the same few lines
+  __shared__ LsePart sml[2][kThreads / 64];
   __shared__ int32_t s_cu[kCuLds + 1];
+  int phase = 0;
   if (a.round_dev && blockIdx.x == 0 && threadIdx.x == 0) *a.round_dev += 1;
-  const int tot = a.cu[a.R];
-  const int T_rows = tot < 0 ? 0 : (tot > a.max_rows ? a.max_rows : tot);
-  const long items_t = (long)T_rows * a.ncht;
-  const long items = items_t + (long)T_rows * a.nchd;
+  // items are numbered against max_rows, so a workgroup knows its row before cu_seqlens
+  // arrives; rows at or past the packed total are skipped. The packed total is read in
+  // each item together with the item's other metadata (one memory round trip).
+  const long items_t = (long)a.max_rows * a.ncht;
+  const long items = items_t + (long)a.max_rows * a.nchd;
+  const int max_packed = (int)min((long)a.max_rows, (long)a.R * (a.K + 1));
   bool staged = false;
   for (long it = blockIdx.x; it < items; it += gridDim.x) {
     if (it < items_t) {
       const int row = (int)(it / a.ncht), c = (int)(it % a.ncht);
+      if (row >= min(cu_[a.R], a.max_rows)) continue;  // uniform over the workgroup
       const TT* p = (const TT*)a.tgt + (size_t)row * a.ld_t;
-      chunk_stats<TT>(p, a.V, a.ncht, c, a.cl, a.tstats + it, smf, smd);
+      chunk_stats<TT>(p, a.V, a.ncht, c, a.cl, a.tstats + it, sml, &phase);
       continue;
     }
     const long j = it - items_t;
     const int row = (int)(j / a.nchd), c = (int)(j % a.nchd);
-    int i = -1, k0 = -1;
-    if (a.row_req) {
-      i = a.row_req[row];
-      k0 = a.row_pos[row] - 1;
-      if (i < 0 || i >= a.R || a.cu[i] + k0 + 1 != row) {  // maps disagree with cu_seqlens: search
-        i = find_request(a.cu, a.R, row);
-        k0 = row - a.cu[i] - 1;
+    if (row >= max_packed) continue;
+    if (rq_) {
+      // the maps are read together with the packed total; their agreement with
+      // cu_seqlens is checked while the row streams in, and a disagreeing pair falls
+      // back to the search
+      // (no branch between the three loads, so they are issued together)
+      const int i = rq_[row];
+      const int k0 = rp_[row] - 1;
+      const int tot = cu_[a.R];
+      asm volatile("" ::"v"(i), "v"(k0), "v"(tot));  // keep the three loads ahead of any branch
+      const bool in_req = (i >= 0) & (i < a.R);
+      const bool drafted = in_req & (k0 >= 0) & (k0 < a.K);
+      if (row >= tot) continue;
+      if (drafted) {
+        const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
+        if (chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + c, sml,
+                            &phase, cu_ + i, row - k0 - 1))
+          continue;
+      } else if (in_req && k0 == -1 && cu_[i] == row) {
+        continue;  // anchor row: no draft logits
       }
-    } else {
-      const bool cu_lds = a.R <= kCuLds;
-      if (cu_lds && !staged) {
-        for (int q = threadIdx.x; q <= a.R; q += kThreads) s_cu[q] = a.cu[q];
-        __syncthreads();
-        staged = true;
-      }
-      const int32_t* cu = cu_lds ? s_cu : a.cu;
-      i = find_request(cu, a.R, row);
-      k0 = row - cu[i] - 1;  // draft position - 1 (-1: the anchor row)
+      const int i2 = find_request(cu_, a.R, row);
+      const int k2 = row - cu_[i2] - 1;
+      if (k2 < 0 || k2 >= a.K) continue;
+      const TD* p = (const TD*)a.drf + (size_t)i2 * a.ld_d_r + (size_t)k2 * a.ld_d_k;
+      chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i2 * a.K + k2) * a.nchd + c, sml,
+                      &phase);
+      continue;
     }
+    if (row >= cu_[a.R]) continue;
+    const bool cu_lds = a.R <= kCuLds;
+    if (cu_lds && !staged) {
+      for (int q = threadIdx.x; q <= a.R; q += kThreads) s_cu[q] = cu_[q];
+      __syncthreads();
+      staged = true;
+    }
+    const int32_t* cu = cu_lds ? s_cu : cu_;
+    const int i = find_request(cu, a.R, row);
+    const int k0 = row - cu[i] - 1;  // draft position - 1 (-1: the anchor row)
     if (k0 < 0 || k0 >= a.K) continue;  // uniform over the workgroup
     const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
-    chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + c, smf, smd);
+    chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + c, sml,
+                    &phase);
   }
 }
 
@@ -980,7 +1064,8 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
                     long max_items) {
   const int cus = num_cus();
   const long g = stats_grid(max_items);
-  launch(DSP_K_VERIFY_STATS, verify_stats_kernel<TT, TD>, dim3((unsigned)g), dim3(kThreads), 0, s, sa);
+  launch(DSP_K_VERIFY_STATS, verify_stats_kernel<TT, TD>, dim3((unsigned)g), dim3(kThreads), 0, s, sa, sa.cu,
+         sa.row_req, sa.row_pos);
   launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
   const long ri = (long)pa.R * pa.nch2;
   const long g2 = ri < (long)cus * 8 ? ri : (long)cus * 8;

@@ -107,6 +107,8 @@ int32_t dsp_philox_uniforms(const uint64_t* ctr, int64_t n, uint64_t seed, doubl
 /* Outputs: windows [R] int32 (n_i in [0, K]); survival [R, K] fp64 (nullable);*/
 /* stats [4] fp64 (nullable): N, E (in probability units), J = E / cost[N], Q. */
 /* Limits: 1 <= K <= 128, 1 <= R, R*K <= 8192.                                 */
+/* Workspace: dsp_schedule_windows_workspace_size(R, K) bytes (the ranked     */
+/* keys), required in every mode.                                            */
 /* ------------------------------------------------------------------------ */
 size_t dsp_schedule_windows_workspace_size(int32_t R, int32_t K);
 int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
@@ -173,7 +175,9 @@ int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const in
 /*   p_x, q_x [R, K] float32   (nullable; chain, T > 0) p_k(x_k), q_k(x_k)    */
 /*                             for every window position, 0 elsewhere        */
 /* row_req, row_pos (nullable, together): the request and position of every  */
-/* packed row, as written by dsp_pack_ragged; when given, draft rows are      */
+/* packed row, as written by dsp_pack_ragged (min(max_rows, R*(K+1)) entries */
+/* each, read whether or not the row is below the packed total, so both must */
+/* be that long); when given, draft rows are                                 */
 /* located from them instead of by searching cu_seqlens (a row whose maps do */
 /* not match cu_seqlens falls back to the search).                           */
 /* cap (nullable, chain only): cap-accept commit windows [R] int32 ([S]       */
@@ -268,14 +272,15 @@ int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t l
 #define DSP_K_VERIFY_DECIDE    1  /* accept/reject decisions; greedy matching; tree walk */
 #define DSP_K_VERIFY_RESIDUAL  2  /* sampled: per-chunk mass of the residual / bonus row */
 #define DSP_K_VERIFY_SAMPLE    3  /* sampled: inverse-CDF draw of the correction token */
-#define DSP_K_SCHEDULE         4
+#define DSP_K_SCHEDULE         4  /* scheduler: prefix sums, throughput test, windows */
 #define DSP_K_PACK             5
 #define DSP_K_MARKOV_GEMM      6
 #define DSP_K_MARKOV_MERGE     7
 #define DSP_K_TREE_GEMM        8
 #define DSP_K_TREE_MERGE       9
 #define DSP_K_TREE_FINAL      10
-#define DSP_K_COUNT           11
+#define DSP_K_SCHEDULE_RANK   11  /* scheduler: ranking of the candidate keys */
+#define DSP_K_COUNT           12
 int32_t dsp_prof_enable(int32_t mask);
 int32_t dsp_prof_reset(void);
 int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);

@@ -72,6 +72,11 @@ def test_host_validation_codes():
     assert lib.dsp_schedule_windows(p, 4, 4, p, 16, 0, -1, 0.0, p, None, None, None, 0, None) == -2
     assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 4, -1, 0.0, p, None, None, None, 0, None) == -6
     assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 3, -1, float('nan'), p, None, None, None, 0, None) == -2
+    # schedule: the ranked keys need the queried workspace (in every mode)
+    need = lib.dsp_schedule_windows_workspace_size(4, 4)
+    assert need >= 4 * 4 * 8
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 0, -1, 0.0, p, None, None, None, 0, None) == -5
+    assert lib.dsp_schedule_windows(p, 4, 4, p, 17, 3, -1, 0.5, p, None, None, p, need - 1, None) == -5
     # pack: descending tiers, too many tiers
     tiers = (ctypes.c_int32 * 2)(8, 4)
     assert lib.dsp_pack_ragged(p, p, p, 4, 3, 4, ctypes.cast(tiers, ctypes.c_void_p), 2, p, p, p, p, p, p,

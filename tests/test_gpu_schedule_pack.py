@@ -42,6 +42,20 @@ def test_schedule_random(R, K):
     _sched(conf, cost, 1)
 
 
+@pytest.mark.parametrize("R,K", [(3, 5), (64, 7), (256, 16)])
+def test_schedule_nonmonotone_survival(R, K):
+    """Confidences above 1 let a survival grow along k, so a request's candidates are no
+    longer ranked in position order: the kernel must see it and sort every key."""
+    rng = np.random.Generator(np.random.PCG64(77 + R * K))
+    S = rng.uniform(0.05, 1.0, size=(R, K))
+    prev = np.concatenate([np.ones((R, 1)), S[:, :-1]], axis=1)
+    conf = (S / prev).astype(np.float32)
+    assert np.any(conf > 1.0)
+    for mode in (osch.MODE_EARLY_STOP, osch.MODE_ARGMAX):
+        _sched(conf, osch.additive_cost(1.0, 0.05, R * K), mode)
+    _sched(conf, osch.additive_cost(1.0, 0.05, R * K), osch.MODE_TOP_M, cap=R * K // 2)
+
+
 def test_schedule_special_cases():
     R, K = 16, 8
     cost = osch.additive_cost(1.0, 0.05, R * K)

@@ -13,10 +13,21 @@ from parity import (TieCounter, compare_chain_verify, cu_from_windows, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def _row_maps(windows):
-    """The pack's packed-row maps (request, position) for the given windows."""
+def _row_maps(windows, bad=False):
+    """The pack's packed-row maps (request, position) for the given windows; with bad=True
+    some entries disagree with cu_seqlens (another request, a draft row labelled as an
+    anchor, an anchor labelled as a draft row, a request out of range), which the verify
+    must detect and resolve by searching cu_seqlens."""
     req = np.concatenate([np.full(w + 1, i, np.int32) for i, w in enumerate(windows)])
     pos = np.concatenate([np.arange(w + 1, dtype=np.int32) for w in windows])
+    if bad:
+        cu = cu_from_windows(windows)
+        drafts = [r for r in range(len(req)) if pos[r] > 0]
+        anchors = [int(c) for c in cu[:-1]]
+        req[drafts[0]] = (req[drafts[0]] + 1) % len(windows)
+        pos[drafts[1]] = 0
+        pos[anchors[1]] = 2
+        req[drafts[-1]] = -5
     return to_gpu(req), to_gpu(pos)
 
 
@@ -31,7 +42,7 @@ def _run_case(case, windows, temperature, seed=0, rnd=0, req_id=None, ld_pad=0, 
     dg = logits_to_gpu(case["d"], dt)
     xg = to_gpu(case["x"].astype(np.int32))
     rid = None if req_id is None else to_gpu(np.asarray(req_id, dtype=np.int64))
-    rq, rp = _row_maps(windows) if row_maps else (None, None)
+    rq, rp = _row_maps(windows, bad=row_maps == "bad") if row_maps else (None, None)
     print(f"verify case R={R} K={K} V={V} dtype={dt} T={temperature} ld={tg.stride(0)} maps={row_maps}",
           flush=True)
     g = dsp.verify_rejection(tg, to_gpu(cu), xg, drf=dg, temperature=temperature, seed=seed, round=rnd,
@@ -78,7 +89,7 @@ def test_unaligned_rows_and_request_ids():
     case = workloads.verify_case(R, K, V, dtype="bf16", seed=5, t_sigma=2.0, d_sigma=0.3)
     windows = np.array([4, 2, 0, 4, 3])
     ties = TieCounter()
-    for maps in (False, True):
+    for maps in (False, True, "bad"):
         g, orc = _run_case(case, windows, 1.0, seed=3, rnd=9, req_id=[100, 7, 55, 2**40, 3], ld_pad=3,
                            row_maps=maps)
         compare_chain_verify(g, orc, R, K, windows, ties)
