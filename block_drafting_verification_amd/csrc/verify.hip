@@ -136,16 +136,28 @@ __device__ __forceinline__ void lse_merge(float& r, double& s, float r2, double 
   }
   r = H;
 }
-template <int TS> __device__ __forceinline__ void lse_xor_step(float& r, double& s) {
-  const uint64_t sb = (uint64_t)__double_as_longlong(s);
-  const float r2 = __uint_as_float(xor_lane<TS>(__float_as_uint(r)));
-  const uint32_t lo = xor_lane<TS>((uint32_t)sb), hi = xor_lane<TS>((uint32_t)(sb >> 32));
-  lse_merge(r, s, r2, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+// Sum over the wavefront by xor butterflies; fp64 addition commutes, so every lane ends
+// with the same bits.
+template <int TS> __device__ __forceinline__ double sum_xor_step(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = xor_lane<TS>((uint32_t)b), hi = xor_lane<TS>((uint32_t)(b >> 32));
+  return v + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum_xor(double s) {
+  s = sum_xor_step<1>(s);
+  s = sum_xor_step<2>(s);
+  s = sum_xor_step<4>(s);
+  s = sum_xor_step<8>(s);
+  s = sum_xor_step<16>(s);
+  return sum_xor_step<32>(s);
+}
+template <int TS> __device__ __forceinline__ float max_xor_step(float v) {
+  return fmaxf(v, __uint_as_float(xor_lane<TS>(__float_as_uint(v))));
 }
 
-// One (row, chunk) of the sampled statistics pass: each thread reduces its own
-// elements against its own maximum, then one butterfly merge per wavefront and one
-// LDS exchange between wavefronts (double-buffered by *phase, so a workgroup that
+// One (row, chunk) of the sampled statistics pass: the wavefront's maximum is the
+// reference of all its lanes' exp2 sums, which are then added by butterflies, and one
+// LDS exchange merges the wavefronts (double-buffered by *phase, so a workgroup that
 // loops over items needs a single barrier per item).
 // The slot is written only if chk is null or *chk == chk_val (read after the row's
 // loads are issued, so its latency overlaps them); returns whether it was.
@@ -187,9 +199,17 @@ __device__ __forceinline__ bool chunk_stats(const T* __restrict__ row, int V, in
       for (int e = 0; e < PV; ++e) m = fmaxf(m, x[e]);
     }
   }
-  // unpack again below instead of keeping every element live as a float
+  // the exp pass converts the raw vectors again: keeping 8 fp32 values per vector live
+  // instead would cost registers and therefore occupancy
 #pragma unroll
   for (int j = 0; j < kVpt; ++j) asm volatile("" : "+v"(buf[j]));
+  // one reference per wavefront (its maximum), so the lane sums need no rescaling
+  m = max_xor_step<1>(m);
+  m = max_xor_step<2>(m);
+  m = max_xor_step<4>(m);
+  m = max_xor_step<8>(m);
+  m = max_xor_step<16>(m);
+  m = max_xor_step<32>(m);
   float ref = m * cl;
   double s = 0.0;
   if (m != -INFINITY) {
@@ -197,9 +217,9 @@ __device__ __forceinline__ bool chunk_stats(const T* __restrict__ row, int V, in
     for (int j = 0; j < kVpt; ++j) {
       const int v = v0 + tid + j * kThreads;
       if (v < v1) {
+        float e8[PV];
         float x[PV];
         Elem<T>::unpack(buf[j], x);
-        float e8[PV];
 #pragma unroll
         for (int e = 0; e < PV; ++e) e8[e] = fast_exp2(__builtin_fmaf(x[e], cl, -ref));
         // pairwise within the vector, fp64 across vectors
@@ -213,12 +233,7 @@ __device__ __forceinline__ bool chunk_stats(const T* __restrict__ row, int V, in
     if (sh != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(sh, cl, -ref));
     if (st != -INFINITY) s += (double)fast_exp2(__builtin_fmaf(st, cl, -ref));
   }
-  lse_xor_step<1>(ref, s);
-  lse_xor_step<2>(ref, s);
-  lse_xor_step<4>(ref, s);
-  lse_xor_step<8>(ref, s);
-  lse_xor_step<16>(ref, s);
-  lse_xor_step<32>(ref, s);
+  s = wave_sum_xor(s);
   LsePart* buf2 = sml[*phase];
   *phase ^= 1;
   if ((tid & 63) == 0) buf2[tid >> 6] = LsePart{ref, 0.f, s};
