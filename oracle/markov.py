@@ -19,12 +19,28 @@ the PCTree article states; the rank is a parameter (256 in the workloads). z is
 computed in fp64; the argmax decision is taken on z rounded to fp32, the
 precision the GPU path decides in, lowest token id on ties.
 
+Sampled chain (the draft side of the full draft -> schedule -> pack -> verify
+cycle; SGLang article, "Ragged verify", and the notes' section 1: the verifier
+needs the draft distribution q of every drafted position): the step's logits are
+emitted as bf16, ẑ_d = bf16(z_d) (round to nearest, ties to even, from the exact
+value), q_d = softmax(ẑ_d / T), and y_d is the inverse-CDF draw from q_d over
+ascending token ids with the Philox uniform of (round, request id, d, stream 1).
+Drawing from the emitted bf16 rows makes the verify step's q exactly the law the
+token came from, which rejection sampling needs.
+
 Pinned by: W = 0 reduces each step to numpy's argmax of L_d; the rank-r term
 equals an independent fp64 dot-product evaluation; the "of course / no problem"
 fixture of the notes' section 2 and Figure 2 (a tie in L_2 resolved toward the
-token the previous choice boosts); logq normalisation (tests/test_oracle_markov.py).
+token the previous choice boosts); logq normalisation; for the sampled chain,
+bf16 rounding equal to the integer rounding of float32 inputs and to the nearer
+of the two enumerated bf16 neighbours of fp64 inputs, the two-token logistic
+law of the draw, and the T -> 0 limit equal to the argmax of the rounded row
+(tests/test_oracle_markov.py).
 """
 import numpy as np
+
+from . import philox
+from .verify import inverse_cdf
 
 
 def markov_logits(L_row, U, W, prev_tok):
@@ -83,3 +99,80 @@ def chain(L, U, W, anchor, n_steps=None, forced=None, want_margin=False):
     if want_margin:
         res.update(margin=margin, zmax=zmax)
     return res
+
+
+def round_bf16(z):
+    """Round fp64 values to the nearest bfloat16 value (ties to even).
+
+    Returns (values as fp64, distance of each input to the nearest rounding
+    midpoint, one bf16 unit in the last place at each input). bfloat16 keeps 8
+    significant bits: with z = m * 2^e, 0.5 <= |m| < 1, the kept significand is
+    m * 2^8 rounded to an integer.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    assert np.all(np.isfinite(z))
+    m, e = np.frexp(z)
+    s = m * 256.0
+    r = np.rint(s)  # nearest integer, ties to even
+    out = np.ldexp(r / 256.0, e)
+    a = np.abs(s)
+    mid_gap = np.ldexp(np.abs((a - np.floor(a)) - 0.5) / 256.0, e)
+    ulp = np.ldexp(np.full_like(z, 1.0 / 256.0), e)
+    return out, mid_gap, ulp
+
+
+# a bf16 rounding whose input lies this close to a midpoint (relative to max(1, |z|)) may
+# round the other way in fp32 arithmetic: counted as a near-tie of the emitted row
+ROUND_BAND = 1e-5
+
+
+def chain_sampled(L, U, W, anchor, temperature, seed=0, rnd=0, req_id=None, n_steps=None, forced=None):
+    """Sampled Markov chain: L [R, B, V]; step d draws y_d from softmax(bf16(z_d) / T).
+
+    forced: optional [R, n] tokens to condition on (replay of another
+    implementation's draws), as in ``chain``.
+    Returns dict(y [R, n], logq [R, n] (of the oracle's own draw), logq_forced,
+    zhat [R, n, V] fp64 values of the emitted bf16 rows, round_tie [R, n, V] bool
+    (inputs within ROUND_BAND of a rounding midpoint), sample_margin [R, n]
+    (distance of u * total to the nearest CDF boundary over the total), tie_shift
+    [R, n] (bound on how far the CDF can move if the near-midpoint entries round
+    the other way, relative to the total)).
+    """
+    L = np.asarray(L)
+    R, B, V = L.shape
+    n = B if n_steps is None else int(n_steps)
+    T = float(temperature)
+    assert T > 0
+    rid = np.arange(R) if req_id is None else np.asarray(req_id, dtype=np.int64)
+    y = np.zeros((R, n), dtype=np.int64)
+    logq = np.zeros((R, n))
+    logq_forced = np.zeros((R, n))
+    zhat = np.zeros((R, n, V))
+    round_tie = np.zeros((R, n, V), dtype=bool)
+    margin = np.zeros((R, n))
+    shift = np.zeros((R, n))
+    prev = np.asarray(anchor, dtype=np.int64).copy()
+    for d in range(n):
+        z = markov_logits(L[:, d, :], U, W, prev)
+        zh, gap, ulp = round_bf16(z)
+        zhat[:, d] = zh
+        tie = gap < ROUND_BAND * np.maximum(1.0, np.abs(z))
+        round_tie[:, d] = tie
+        u = philox.draft_uniforms(seed, rnd, rid, d + 1)
+        for i in range(R):
+            s = zh[i] / T
+            mx = np.max(s)
+            w = np.exp(s - mx)
+            lse = mx + np.log(np.sum(w))
+            v, mg = inverse_cdf(w, u[i])
+            y[i, d] = v
+            margin[i, d] = mg
+            logq[i, d] = s[v] - lse
+            q = w / np.sum(w)
+            shift[i, d] = 2.0 * float(np.sum(q[tie[i]] * np.expm1(ulp[i, tie[i]] / T)))
+        prev = y[:, d] if forced is None else np.asarray(forced, dtype=np.int64)[:, d]
+        logq_forced[:, d] = zh[np.arange(R), prev] / T - (
+            np.max(zh / T, axis=-1) + np.log(np.sum(np.exp(zh / T - np.max(zh / T, axis=-1, keepdims=True)),
+                                                   axis=-1)))
+    return dict(y=y, logq=logq, logq_forced=logq_forced, zhat=zhat, round_tie=round_tie,
+                sample_margin=margin, tie_shift=shift)

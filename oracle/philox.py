@@ -24,10 +24,12 @@ W1 = np.uint64(0xBB67AE8584CAA73B)
 _LO32 = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
-# Word layout used by the verify step: counter = (round, request id, position, stream).
+# Word layout: counter = (round, request id, position, stream).
 STREAM_VERIFY = 0
 WORD_ACCEPT = 0      # uniform u_k compared with min(1, p/q)
 WORD_SAMPLE = 1      # uniform u'_k for the residual (rejection at k) or bonus (k = n+1)
+STREAM_DRAFT = 1     # the sampled Markov draft: word 0 draws the token of position d
+WORD_DRAW = 0
 
 
 def _mulhilo(a, b):
@@ -90,3 +92,19 @@ def verify_uniforms(seed, rnd, req_ids, kmax):
     key = np.array([np.uint64(seed), np.uint64(0)], dtype=np.uint64)
     out = philox4x64_10(ctr, key)
     return to_unit_double(out[..., WORD_ACCEPT]), to_unit_double(out[..., WORD_SAMPLE])
+
+
+def draft_uniforms(seed, rnd, req_ids, d):
+    """Uniform of the sampled draft's token draw at position d (1-based) for each request.
+
+    Counter (round, request id, d, STREAM_DRAFT), word 0; the verify step's
+    counters use stream 0, so the two never share a block.
+    """
+    req_ids = np.asarray(req_ids, dtype=np.uint64)
+    ctr = np.zeros((req_ids.shape[0], 4), dtype=np.uint64)
+    ctr[:, 0] = np.uint64(rnd)
+    ctr[:, 1] = req_ids
+    ctr[:, 2] = np.uint64(d)
+    ctr[:, 3] = np.uint64(STREAM_DRAFT)
+    key = np.array([np.uint64(seed), np.uint64(0)], dtype=np.uint64)
+    return to_unit_double(philox4x64_10(ctr, key)[:, WORD_DRAW])

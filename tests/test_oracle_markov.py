@@ -86,3 +86,84 @@ def test_forced_replay_is_step_local():
     np.testing.assert_array_equal(rep["y"][:, :2], own[:, :2])
     z = om.markov_logits(L[:, 2], U, W, forced[:, 1])
     np.testing.assert_array_equal(rep["y"][:, 2], np.argmax(z.astype(np.float32), -1))
+
+
+# ---------------------------------------------------------------- sampled chain
+
+def test_round_bf16_equals_integer_rounding_of_float32():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    x = np.concatenate([x, np.float32([0.0, 1.0, -1.0, 3.0, 1.00390625, 1.01171875])])
+    got, _, _ = om.round_bf16(x.astype(np.float64))
+    ref = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(x)).astype(np.float64)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_round_bf16_picks_nearest_enumerated_neighbour():
+    """fp64 inputs (not representable in fp32) against every positive finite bf16 value."""
+    allb = np.sort(workloads.bf16_bits_to_f32(np.arange(1, 0x7F80, dtype=np.uint16)).astype(np.float64))
+    rng = np.random.default_rng(8)
+    z = rng.uniform(0.01, 100.0, 20000) * (1 + 1e-12 * rng.standard_normal(20000))
+    got, gap, ulp = om.round_bf16(z)
+    j = np.searchsorted(allb, z)
+    lo, hi = allb[j - 1], allb[j]
+    dlo, dhi = z - lo, hi - z
+    bits_lo = workloads.f32_to_bf16_bits(lo.astype(np.float32))
+    even_lo = (bits_lo & 1) == 0
+    want = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(even_lo, lo, hi)))
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_allclose(gap, np.abs(dlo - dhi) / 2, rtol=1e-9, atol=1e-300)
+    np.testing.assert_allclose(ulp, hi - lo, rtol=0)
+
+
+def test_sampled_two_token_law_is_logistic():
+    """V = 2, no Markov term: P(y = 1) = 1 / (1 + exp(-(l1 - l0) / T)) (closed form)."""
+    for beta, T in ((0.5, 1.0), (-1.5, 0.7)):
+        R = 400
+        L = np.zeros((R, 1, 2), dtype=np.float32)
+        L[:, 0, 1] = beta
+        U = np.zeros((2, 32), dtype=np.float32)
+        W = np.zeros((32, 2), dtype=np.float32)
+        ones = 0
+        N = 0
+        for rnd in range(60):
+            res = om.chain_sampled(L, U, W, np.zeros(R, dtype=np.int64), T, seed=11, rnd=rnd)
+            ones += int(res["y"].sum())
+            N += R
+        a = 1.0 / (1.0 + math.exp(-beta / T))
+        assert abs(ones / N - a) < 5 * math.sqrt(a * (1 - a) / N), (beta, T, ones / N, a)
+
+
+def test_sampled_low_temperature_is_argmax_of_rounded_row():
+    L, U, W, anchors = _small(R=8, B=3, V=300, r=32, seed=9)
+    W = W * 300
+    res = om.chain_sampled(L, U, W, anchors, 1e-3, seed=2)
+    prev = anchors
+    checked = 0
+    for d in range(3):
+        zh, _, _ = om.round_bf16(om.markov_logits(L[:, d], U, W, prev))
+        top = -np.sort(-zh, axis=-1)
+        for i in range(8):
+            if top[i, 0] - top[i, 1] > 0.1:
+                assert res["y"][i, d] == int(np.argmax(zh[i]))
+                checked += 1
+        prev = res["y"][:, d]
+    assert checked >= 12
+
+
+def test_sampled_replay_is_step_local():
+    L, U, W, anchors = _small(R=4, B=4, V=120, r=32, seed=10)
+    W = W * 300
+    own = om.chain_sampled(L, U, W, anchors, 1.0, seed=5, rnd=3)
+    forced = own["y"].copy()
+    forced[:, 1] = (forced[:, 1] + 7) % 120
+    rep = om.chain_sampled(L, U, W, anchors, 1.0, seed=5, rnd=3, forced=forced)
+    np.testing.assert_array_equal(rep["y"][:, :2], own["y"][:, :2])
+    np.testing.assert_array_equal(rep["zhat"][:, :2], own["zhat"][:, :2])
+    z3 = om.round_bf16(om.markov_logits(L[:, 2], U, W, forced[:, 1]))[0]
+    np.testing.assert_array_equal(rep["zhat"][:, 2], z3)
+    np.testing.assert_allclose(np.exp(own["logq"]).sum() > 0, True)
+    # logq_forced is the log-probability of the forced token under the step's rounded row
+    s = z3 / 1.0
+    lse = s.max(-1) + np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1))
+    np.testing.assert_allclose(rep["logq_forced"][:, 2], s[np.arange(4), forced[:, 2]] - lse, rtol=1e-12)
