@@ -12,6 +12,7 @@ Calls (same names as the C entry points without the ``dsp_`` prefix):
   pack_ragged        -- front-packed cu_seqlens verify buffer
   verify_rejection   -- batched ragged rejection / greedy / tree verify
   draft_markov_step  -- Markov-head greedy chain
+  draft_markov_sample -- Markov-head sampled chain emitting its bf16 draft logits
   tree_expand        -- PCTree expansion
   philox_uniforms    -- the counter-based uniforms the verify step draws
 """
@@ -24,7 +25,8 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
                    DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE,
                    DspError, KERNELS)
 
-__all__ = ["PreparedCall", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step", "tree_expand",
+__all__ = ["PreparedCall", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step",
+           "draft_markov_sample", "tree_expand",
            "philox_uniforms", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
            "DSP_STATUS_TOKEN_RANGE",
@@ -281,6 +283,41 @@ def draft_markov_step(L, U, Wt, prev_tok, n_steps=None, want_logq=False, out=Non
             _ptr(y), y.stride(0), _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_markov_step, args, dict(y=y, logq=logq, status=status), prepare,
                    (L, U, Wt, prev_tok, ws))
+
+
+def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_dev=None, req_id=None,
+                        n_steps=None, want_logq=True, out=None, status=None, stream=None, prepare=False):
+    """Sampled Markov chain. L: bf16 [R, B, V]; U, Wt: bf16 [V, rank]; prev_tok: int32 [R].
+
+    Returns dict(y int32 [R, n], logq float32 [R, n] or None, z bf16 [R, n, V] (the
+    emitted draft logits), status).
+    """
+    _check_markov(L, U, Wt)
+    R, B, V = L.shape
+    n = B if n_steps is None else int(n_steps)
+    _need(1 <= n <= B, "n_steps must be in [1, B]")
+    rank = U.shape[1]
+    _need(prev_tok.dtype == torch.int32 and prev_tok.numel() == R and prev_tok.is_contiguous(), "prev_tok: int32 [R]")
+    _on_gpu(round_dev, req_id)
+    _need(round_dev is None or (round_dev.dtype == torch.int64 and round_dev.numel() == 1),
+          "round_dev: int64 [1]")
+    _need(req_id is None or (req_id.dtype == torch.int64 and req_id.numel() == R and req_id.is_contiguous()),
+          "req_id: int64 [R]")
+    dev = L.device
+    o = out or {}
+    y = _take(o, "y", lambda: torch.empty(R, n, dtype=torch.int32, device=dev))
+    logq = _take(o, "logq", lambda: torch.empty(R, n, dtype=torch.float32, device=dev)) if want_logq else None
+    vpad = (V + 7) // 8 * 8
+    z = _take(o, "z", lambda: torch.empty(R, n, vpad, dtype=torch.bfloat16, device=dev)[..., :V])
+    _need(z.dtype == torch.bfloat16 and z.dim() == 3 and z.stride(2) == 1, "z: bf16 [R, n, V] with unit stride")
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().dsp_draft_markov_sample_workspace_size(R, V, rank, n), dev, prepare)
+    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
+            float(temperature), int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(y), y.stride(0),
+            _ptr(logq), _ptr(z), z.stride(0), z.stride(1), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+    return _finish(lib().dsp_draft_markov_sample, args, dict(y=y, logq=logq, z=z, status=status), prepare,
+                   (L, U, Wt, prev_tok, round_dev, req_id, ws))
 
 
 def tree_expand(L, U, Wt, anchor, topk, frontier, topN, out=None, status=None, stream=None, prepare=False):

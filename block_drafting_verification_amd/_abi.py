@@ -40,6 +40,9 @@ SIGNATURES = {
     "dsp_draft_markov_step_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "dsp_draft_markov_step": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _p, _i32, _i32,
                                      _p, _i64, _p, _p, _p, _sz, _p]),
+    "dsp_draft_markov_sample_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "dsp_draft_markov_sample": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _p, _i32, _i32, _f32, _u64, _u64,
+                                       _p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _sz, _p]),
     "dsp_tree_expand_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "dsp_tree_expand": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _p, _i32, _i32, _i32,
                                _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),

@@ -46,7 +46,7 @@ constexpr int kTS = 32;           // vocabulary entries per pipeline stage (one 
 constexpr int kTopK = 4;          // children tracked per parent
 constexpr int kTargetWGs = 256;   // one workgroup per CU
 
-enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2 };
+enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2, MODE_SAMPLE = 3 };
 
 // ---------------------------------------------------------------- streaming loads
 // The stage ring is fed by raw buffer loads issued from inline assembly with explicit
@@ -127,6 +127,12 @@ struct GemmArgs {
   int32_t* status;
   int32_t nrb;             // row blocks of kTR rows
   int32_t xcd_map;         // 1: row blocks of a slice share an XCD (G % 8 == 0)
+  // sampled chain: the step's logits rounded to bf16 go to zout (element (row, v) at
+  // zout + row*ldz_r + d*ldz_d + v), and the log-sum-exp partials are of those rounded
+  // values times cz = log2(e) / T
+  uint16_t* zout;
+  int64_t ldz_r, ldz_d;
+  float cz;
 };
 
 // 16-byte slot of (row, vector) in a swizzled LDS tile whose rows hold `nv` vectors
@@ -181,7 +187,11 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   constexpr int NR = KS <= 16 && LAL ? 3 : 2;  // stages in flight per thread (register ring)
   constexpr int NU = NR % 2 ? 2 * NR : NR;     // stages per unrolled loop body (ring slot and
                                                // buffer parity both static)
-  constexpr bool AS = KS <= 16;               // asynchronous ring loads (kernels that do not spill)
+  // asynchronous ring loads (kernels that do not spill). Not with global stores in the
+  // loop (the sampled chain's rows): stores share the vector memory counter with the
+  // loads and may complete out of order with them, so counted waits would not cover the
+  // ring; the compiler's own waits do.
+  constexpr bool AS = KS <= 16 && MODE != MODE_SAMPLE;
   static_assert(LST % kGT == 0, "L stage must split evenly over the workgroup");
   extern __shared__ u32x4 lds[];              // [2][WST + LST]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -366,9 +376,41 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       }
     }
   };
-  // epilogue of one stage for the log-sum-exp and tree modes (z = acc)
-  auto epilogue = [&](int s, const f32x16& z) {
+  // epilogue of one stage for the log-sum-exp, tree and sampled modes (z = acc)
+  const float cz = MODE == MODE_SAMPLE ? a.cz : kLog2e;
+  auto epilogue = [&](int s, const f32x16& zacc) {
     const int v0 = (s_begin + s) * kTS;
+    f32x16 z = zacc;
+    if (MODE == MODE_SAMPLE) {
+      // round to bf16 (nearest, ties to even; infinities stay infinite), emit the row
+      // entries of this stage (four runs of four consecutive tokens), and continue
+      // with the rounded values
+      uint32_t hb[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t u = __float_as_uint(z[q]);
+        hb[q] = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        z[q] = __uint_as_float(hb[q] << 16);
+      }
+      if (rvalid) {
+        uint16_t* zr = a.zout + (size_t)row * a.ldz_r + (size_t)a.d * a.ldz_d;
+        const int vb = v0 + 4 * (lane >> 5);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int v = vb + 8 * h;
+          if (v + 4 <= a.V) {
+            uint2 w;
+            w.x = hb[4 * h] | (hb[4 * h + 1] << 16);
+            w.y = hb[4 * h + 2] | (hb[4 * h + 3] << 16);
+            *(uint2*)(zr + v) = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (v + e < a.V) zr[v + e] = (uint16_t)hb[4 * h + e];
+          }
+        }
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -386,16 +428,16 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
             }
           }
         }
-      } else if (z[q] > best) {
+      } else if (MODE == MODE_ARGMAX_LSE && z[q] > best) {
         best = z[q];
         bidx = v;
       }
     }
     if (tmax != -INFINITY) {
-      const float nref = fmaxf(lref, tmax * kLog2e);
+      const float nref = fmaxf(lref, tmax * cz);
       float ts = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));  // exp2(-inf) = 0
+      for (int q = 0; q < 16; ++q) ts += fast_exp2(__builtin_fmaf(z[q], cz, -nref));  // exp2(-inf) = 0
       const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
       lsum = lsum * scale + (double)ts;
       lref = nref;
@@ -552,6 +594,159 @@ __global__ __launch_bounds__(64) void chain_merge_kernel(ChainMergeArgs a) {
       const double zy = (double)amax_value(best);
       a.logq[(size_t)r * a.ld_y + a.d] = (float)((zy * kLog2ed - lse2) * kLn2d);
     }
+  }
+}
+
+// ---------------------------------------------------------------- sampled chain draw
+struct ChainSampleArgs {
+  const ChainPart* part;  // [R][G] log-sum-exp partials of the rounded row per vocabulary slice
+  int32_t G, R, d, V;
+  const uint16_t* z;      // the emitted bf16 rows
+  int64_t ldz_r, ldz_d;
+  float cz;               // log2(e) / T
+  uint64_t seed, round;
+  const uint64_t* round_dev;
+  const int64_t* req_id;
+  int32_t* y;
+  int64_t ld_y;
+  float* logq;
+  int32_t* status;
+};
+
+// Inclusive prefix sum over the wavefront (fixed Hillis-Steele order, fp64).
+__device__ __forceinline__ double wave_scan_incl(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double w = __shfl_up(v, o, 64);
+    if (lane >= o) v += w;
+  }
+  return v;
+}
+
+// Inverse-CDF draw of step d for row r, one wavefront per row: the vocabulary slices'
+// masses (from the GEMM partials) locate the slice that holds u * total, then that
+// slice of the emitted bf16 row is rescanned in ascending token order, lane by lane
+// over contiguous ranges, to the first token whose running mass exceeds the target
+// (the last token with mass if rounding leaves none). Slices are the GEMM's: slice g
+// covers 32-token stages [g*nst/G, (g+1)*nst/G).
+__global__ __launch_bounds__(64) void chain_sample_kernel(ChainSampleArgs a) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const ChainPart* pr = a.part + (size_t)r * a.G;
+  const int gpl = (a.G + 63) / 64;  // slices per lane (G <= 256)
+  float ref[4];
+  double sum[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = lane * gpl + q;
+    ref[q] = -INFINITY;
+    sum[q] = 0.0;
+    if (q < gpl && g < a.G) {
+      ref[q] = pr[g].ref;
+      sum[q] = pr[g].sum;
+    }
+  }
+  float H = fmaxf(fmaxf(ref[0], ref[1]), fmaxf(ref[2], ref[3]));
+  H = wave_max(H);
+  double w[4], lsum = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[q] = ref[q] == -INFINITY ? 0.0 : sum[q] * (double)fast_exp2(ref[q] - H);
+    lsum += w[q];
+  }
+  const double incl = wave_scan_incl(lsum);
+  const double total = __shfl(incl, 63, 64);
+  int32_t* yo = a.y + (size_t)r * a.ld_y + a.d;
+  if (!(total > 0.0) || !(H < INFINITY) || total == INFINITY) {
+    if (lane == 0) {
+      *yo = -1;
+      if (a.logq) a.logq[(size_t)r * a.ld_y + a.d] = NAN;
+      atomicOr(a.status, DSP_STATUS_NONFINITE);
+    }
+    return;
+  }
+  const uint64_t rid = a.req_id ? (uint64_t)a.req_id[r] : (uint64_t)r;
+  const uint64_t rnd = a.round_dev ? *a.round_dev : a.round;
+  uint64_t c[4] = {rnd, rid, (uint64_t)(a.d + 1), 1ull};  // stream 1: the draft's draws
+  philox4x64_10(c, a.seed, 0ull);
+  const double tau = unit_double(c[0]) * total;
+  // the slice holding tau (else the last slice with mass)
+  const double excl = incl - lsum;
+  const uint64_t hit = __ballot(lsum > 0.0 && excl <= tau && tau < incl);
+  int gs = -1;
+  double tin = INFINITY;  // target inside the slice; +inf: take its last token with mass
+  if (hit) {
+    const int l = __ffsll((unsigned long long)hit) - 1;
+    if (lane == l) {
+      double acc = excl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (gs < 0 && w[q] > 0.0 && tau < acc + w[q]) {
+          gs = lane * gpl + q;
+          tin = tau - acc;
+        }
+        acc += w[q];
+      }
+      if (gs < 0) {  // rounding between the per-slice and the lane sums: last slice with mass
+        for (int q = 3; q >= 0; --q)
+          if (gs < 0 && w[q] > 0.0) gs = lane * gpl + q;
+      }
+    }
+    gs = __shfl(gs, l, 64);
+    tin = __shfl(tin, l, 64);
+  } else {
+    const uint64_t any = __ballot(lsum > 0.0);
+    const int l = 63 - __clzll((long long)any);
+    if (lane == l)
+      for (int q = 3; q >= 0; --q)
+        if (gs < 0 && w[q] > 0.0) gs = lane * gpl + q;
+    gs = __shfl(gs, l, 64);
+  }
+  const int nst_all = (a.V + 31) / 32;
+  const int t0 = (int)(((long)gs * nst_all) / a.G) * 32;
+  const int t1 = min(a.V, (int)(((long)(gs + 1) * nst_all) / a.G) * 32);
+  const int per = (t1 - t0 + 63) / 64;
+  const int v0 = min(t1, t0 + lane * per), v1 = min(t1, v0 + per);
+  const uint16_t* zr = a.z + (size_t)r * a.ldz_r + (size_t)a.d * a.ldz_d;
+  double ms = 0.0;
+  for (int v = v0; v < v1; ++v) ms += (double)fast_exp2(__builtin_fmaf(bf16_val(zr[v]), a.cz, -H));
+  const double mi = wave_scan_incl(ms);
+  const double me = mi - ms;
+  const uint64_t hit2 = __ballot(ms > 0.0 && me <= tin && tin < mi);
+  int tok = -1;
+  if (hit2) {
+    const int l = __ffsll((unsigned long long)hit2) - 1;
+    if (lane == l) {
+      double acc = me;
+      for (int v = v0; v < v1 && tok < 0; ++v) {
+        const double wv = (double)fast_exp2(__builtin_fmaf(bf16_val(zr[v]), a.cz, -H));
+        if (wv > 0.0 && tin < acc + wv) tok = v;
+        acc += wv;
+      }
+      if (tok < 0)  // rounding inside the lane: its last token with mass
+        for (int v = v1 - 1; v >= v0 && tok < 0; --v)
+          if (fast_exp2(__builtin_fmaf(bf16_val(zr[v]), a.cz, -H)) > 0.f) tok = v;
+    }
+    tok = __shfl(tok, l, 64);
+  }
+  if (tok < 0) {
+    const uint64_t any = __ballot(ms > 0.0);
+    if (any) {
+      const int l = 63 - __clzll((long long)any);
+      if (lane == l)
+        for (int v = v1 - 1; v >= v0 && tok < 0; --v)
+          if (fast_exp2(__builtin_fmaf(bf16_val(zr[v]), a.cz, -H)) > 0.f) tok = v;
+      tok = __shfl(tok, l, 64);
+    }
+  }
+  if (lane == 0) {
+    *yo = tok;
+    if (a.logq) {
+      const double lse2 = (double)H + log2(total);
+      const float lq = tok < 0 ? NAN : (float)(((double)bf16_val(zr[tok]) * (double)a.cz - lse2) * kLn2d);
+      a.logq[(size_t)r * a.ld_y + a.d] = lq;
+    }
+    if (tok < 0) atomicOr(a.status, DSP_STATUS_NONFINITE);
   }
 }
 
@@ -925,6 +1120,56 @@ extern "C" int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t
     ChainMergeArgs ma{(const ChainPart*)ws, G, R, d, y, ld_y, logq};
     launch(DSP_K_MARKOV_MERGE, chain_merge_kernel, dim3(R), dim3(64), 0, s, ma);
     rc = hip_check(hipGetLastError(), "chain merge launch");
+    if (rc) return rc;
+  }
+  return DSP_OK;
+}
+
+extern "C" size_t dsp_draft_markov_sample_workspace_size(int32_t R, int32_t V, int32_t rank, int32_t n_steps) {
+  (void)rank;
+  (void)n_steps;
+  if (R < 1 || V < 1) return 0;
+  return align_up((size_t)pick_groups(R, V) * R * sizeof(ChainPart), 256);
+}
+
+extern "C" int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
+                                           const void* U, const void* Wt, int32_t V, int32_t rank,
+                                           const int32_t* prev_tok, int32_t R, int32_t n_steps,
+                                           float temperature, uint64_t seed, uint64_t round,
+                                           const uint64_t* round_dev, const int64_t* req_id, int32_t* y,
+                                           int64_t ld_y, float* logq, void* z, int64_t ldz_r, int64_t ldz_d,
+                                           int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int32_t rc = check_markov_common(L, l_dtype, U, Wt, V, rank);
+  if (rc) return rc;
+  if (R < 1 || n_steps < 1) return fail(DSP_ERR_SHAPE, "need R >= 1 and n_steps >= 1");
+  if (!(temperature > 0.f) || temperature == INFINITY)
+    return fail(DSP_ERR_SHAPE, "temperature must be finite and > 0 (use the greedy chain for T = 0)");
+  if (!prev_tok || !y || !z || !status) return fail(DSP_ERR_NULL, "prev_tok, y, z and status are required");
+  if (ld_y < n_steps) return fail(DSP_ERR_SHAPE, "ld_y < n_steps");
+  if (ldL_d < V || ldL_r < (int64_t)(n_steps - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
+  if (ldz_d < V || ldz_r < (int64_t)(n_steps - 1) * ldz_d + V) return fail(DSP_ERR_SHAPE, "z strides too small");
+  if (((uintptr_t)z) % 16 || ldz_d % 8 || ldz_r % 8)
+    return fail(DSP_ERR_ALIGN, "z must be 16-byte aligned with strides that are multiples of 8 elements");
+  const size_t need = dsp_draft_markov_sample_workspace_size(R, V, rank, n_steps);
+  if (!ws || ws_bytes < need) return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  hipStream_t s = (hipStream_t)stream;
+  const int G = pick_groups(R, V);
+  const float cz = (float)(1.4426950408889634074 / (double)temperature);
+  for (int d = 0; d < n_steps; ++d) {
+    GemmArgs ga{(const uint16_t*)U, (const uint16_t*)Wt, V, rank,
+                d == 0 ? prev_tok : y + (d - 1), d == 0 ? 1 : ld_y,
+                (const uint16_t*)L, ldL_r, ldL_d, d, R, 1, G, ws, status};
+    ga.zout = (uint16_t*)z;
+    ga.ldz_r = ldz_r;
+    ga.ldz_d = ldz_d;
+    ga.cz = cz;
+    rc = launch_gemm<MODE_SAMPLE>(DSP_K_MARKOV_GEMM, ga, s);
+    if (rc) return rc;
+    ChainSampleArgs sa{(const ChainPart*)ws, G, R, d, V, (const uint16_t*)z, ldz_r, ldz_d, cz,
+                       seed, round, round_dev, req_id, y, ld_y, logq, status};
+    launch(DSP_K_MARKOV_MERGE, chain_sample_kernel, dim3(R), dim3(64), 0, s, sa);
+    rc = hip_check(hipGetLastError(), "chain sample launch");
     if (rc) return rc;
   }
   return DSP_OK;

@@ -232,6 +232,40 @@ int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t ldL_r, int
                               void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Markov-head sequential stage, sampled chain  ([N] 1, 4; [S] "Ragged       */
+/* verify": the draft side of the draft -> schedule -> pack -> verify cycle) */
+/*                                                                          */
+/* For d = 1..n_steps and every request i:                                   */
+/*   z_d = L[i, d-1, :] + U[y_{d-1}, :] . W (fp32), y_0 = prev_tok[i];         */
+/*   zh_d = bf16(z_d), round to nearest even, written to                     */
+/*          z[i*ldz_r + (d-1)*ldz_d + v] (these rows are the draft logits    */
+/*          that dsp_verify_rejection takes as drf, so q there is exactly the */
+/*          law the token was drawn from);                                   */
+/*   q_d = softmax(zh_d / T);  y_d = smallest v with                         */
+/*          sum_{w<=v} q_d(w) > u_d (inverse CDF over ascending token ids;   */
+/*          the last token with mass if rounding leaves none);              */
+/*   logq[i, d-1] = log q_d(y_d) (if logq != NULL).                          */
+/* u_d: Philox4x64-10, key (seed, 0), counter (round, req_id[i] or i, d, 1),  */
+/* word 0 mapped to [0, 1) as (w >> 11) * 2^-53; stream 1 keeps the draft's   */
+/* draws apart from the verify step's (stream 0). round_dev (device,         */
+/* nullable) replaces `round` with *round_dev, read and not advanced (the    */
+/* verify call advances it), so a captured cycle draws fresh uniforms.       */
+/* L, U, Wt as dsp_draft_markov_step; z: bf16, 16-byte aligned, ldz_d and    */
+/* ldz_r multiples of 8 elements, ldz_d >= V; y and logq [R, n_steps] with   */
+/* row stride ld_y. temperature must be finite and > 0 (the greedy chain is  */
+/* dsp_draft_markov_step). A row whose mass is not finite sets               */
+/* DSP_STATUS_NONFINITE and writes y = -1.                                   */
+/* ------------------------------------------------------------------------ */
+size_t dsp_draft_markov_sample_workspace_size(int32_t R, int32_t V, int32_t rank, int32_t n_steps);
+int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
+                                const void* U, const void* Wt, int32_t V, int32_t rank,
+                                const int32_t* prev_tok, int32_t R, int32_t n_steps, float temperature,
+                                uint64_t seed, uint64_t round, const uint64_t* round_dev,
+                                const int64_t* req_id, int32_t* y, int64_t ld_y, float* logq, void* z,
+                                int64_t ldz_r, int64_t ldz_d, int32_t* status, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* PCTree expansion  ([P] "the chain becomes a tree")                         */
 /*                                                                          */
 /* Per request, root = anchor with score 0. For depth d = 1..D and every      */

@@ -135,8 +135,9 @@ def chain_sampled(L, U, W, anchor, temperature, seed=0, rnd=0, req_id=None, n_st
     zhat [R, n, V] fp64 values of the emitted bf16 rows, round_tie [R, n, V] bool
     (inputs within ROUND_BAND of a rounding midpoint), sample_margin [R, n]
     (distance of u * total to the nearest CDF boundary over the total), tie_shift
-    [R, n] (bound on how far the CDF can move if the near-midpoint entries round
-    the other way, relative to the total)).
+    [R, n] (bound on how far the CDF can move if the near-midpoint entries land
+    on another bf16 value -- up to one unit plus ROUND_BAND * max(1, |z|) away --
+    relative to the total)).
     """
     L = np.asarray(L)
     R, B, V = L.shape
@@ -169,7 +170,9 @@ def chain_sampled(L, U, W, anchor, temperature, seed=0, rnd=0, req_id=None, n_st
             margin[i, d] = mg
             logq[i, d] = s[v] - lse
             q = w / np.sum(w)
-            shift[i, d] = 2.0 * float(np.sum(q[tie[i]] * np.expm1(ulp[i, tie[i]] / T)))
+            # a near-midpoint entry computed in fp32 may land up to one unit plus the band away
+            dev = ulp[i, tie[i]] + ROUND_BAND * np.maximum(1.0, np.abs(z[i, tie[i]]))
+            shift[i, d] = 2.0 * float(np.sum(q[tie[i]] * np.expm1(dev / T)))
         prev = y[:, d] if forced is None else np.asarray(forced, dtype=np.int64)[:, d]
         logq_forced[:, d] = zh[np.arange(R), prev] / T - (
             np.max(zh / T, axis=-1) + np.log(np.sum(np.exp(zh / T - np.max(zh / T, axis=-1, keepdims=True)),

@@ -8,7 +8,7 @@ import workloads
 from oracle import markov as om
 from oracle import pctree as opt
 from oracle import verify as ov
-from parity import ARGMAX_BAND, TieCounter, host, to_gpu, to_gpu_bf16
+from parity import ARGMAX_BAND, SAMPLE_BAND, TieCounter, host, to_gpu, to_gpu_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +173,89 @@ def test_tree_verify_c5_shape_planted_paths():
     np.testing.assert_array_equal(host(g["accepted_len"]), o["accepted_len"])
     np.testing.assert_array_equal(host(g["out_tokens"]), o["out_tokens"])
     assert np.all(o["accepted_len"] >= np.array(planted))
+
+
+# ---------------------------------------------------------------- sampled chain
+
+def _check_sampled(c, T, seed=0, rnd=0, requests=None, w_boost=1.0):
+    """Sampled chain against the oracle with replay of the GPU's draws: the emitted bf16 rows
+    bit-exact except entries the oracle marks as rounding near-ties (then within one bf16
+    unit), the draws exact except counted near-ties, logq within 1e-5."""
+    L, U, W = _f32(c)
+    if w_boost != 1.0:
+        c = dict(c, W=workloads.f32_to_bf16_bits(W * np.float32(w_boost)))
+        L, U, W = _f32(c)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    print(f"sampled chain R={c['R']} B={c['B']} V={c['V']} rank={c['rank']} T={T}", flush=True)
+    g = dsp.draft_markov_sample(Lg, Ug, Wtg, ag, T, seed=seed, round=rnd)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    y = host(g["y"]).astype(np.int64)
+    sel = np.arange(c["R"]) if requests is None else np.asarray(requests)
+    zg = workloads.bf16_bits_to_f32(host(g["z"][sel].contiguous().view(torch.int16)).view(np.uint16))
+    orc = om.chain_sampled(L[sel], U, W, c["anchors"][sel], T, seed=seed, rnd=rnd, req_id=sel, forced=y[sel])
+    # emitted rows
+    diff = zg.astype(np.float64) != orc["zhat"]
+    assert not np.any(diff & ~orc["round_tie"]), np.argwhere(diff & ~orc["round_tie"])[:5]
+    if diff.any():
+        # an fp32 value near a rounding midpoint lands within one unit plus the fp32 band
+        # (near zero, after cancellation, the band spans several units)
+        zo = orc["zhat"][diff]
+        _, _, ulp = om.round_bf16(zo)
+        allow = ulp * 1.0000001 + om.ROUND_BAND * np.maximum(1.0, np.abs(zo))
+        assert np.all(np.abs(zg[diff] - zo) <= allow)
+    # draws
+    ties = TieCounter()
+    ties.decisions += y[sel].size
+    for ii, d in np.argwhere(orc["y"] != y[sel]):
+        band = max(SAMPLE_BAND, orc["tie_shift"][ii, d])
+        assert orc["sample_margin"][ii, d] < band, (sel[ii], d, orc["sample_margin"][ii, d], band)
+        ties.near += 1
+        ties.notes.append((int(sel[ii]), int(d)))
+    ties.check()
+    # logq: 1e-5, widened where a rounding near-tie may have moved the row's normaliser
+    # (tie_shift bounds that move) or the drawn token's own rounded value (one unit / T)
+    lq = host(g["logq"]).astype(np.float64)[sel]
+    ys = y[sel]
+    tok_tie = np.take_along_axis(orc["round_tie"], ys[..., None], axis=2)[..., 0]
+    tok_val = np.take_along_axis(orc["zhat"], ys[..., None], axis=2)[..., 0]
+    _, _, tok_ulp = om.round_bf16(tok_val)
+    tok_dev = tok_ulp + om.ROUND_BAND * np.maximum(1.0, np.abs(tok_val))
+    allow = 1e-5 * np.maximum(1.0, np.abs(orc["logq_forced"])) + orc["tie_shift"] + np.where(tok_tie, tok_dev / T, 0.0)
+    err = np.abs(lq - orc["logq_forced"])
+    assert np.all(err <= allow), (np.argwhere(err > allow)[:5], err.max())
+    return g, y
+
+
+@pytest.mark.parametrize("R,B,V,rank,T", [(5, 4, 1000, 32, 1.0), (130, 3, 4099, 64, 0.7), (7, 3, 30000, 256, 1.3),
+                                          (300, 2, 129, 96, 1.0), (3, 2, 2000, 512, 0.5)])
+def test_chain_sampled_small(R, B, V, rank, T):
+    c = workloads.markov_case(R, B, V, rank=rank, seed=R + V + 1)
+    _check_sampled(c, T, seed=3, rnd=1, w_boost=100.0)
+    _check_sampled(c, T, seed=4, rnd=2)
+
+
+def test_chain_sampled_round_dev_and_req_id():
+    """A device round equals the same host round; request ids move the uniforms."""
+    c = workloads.markov_case(6, 3, 2000, rank=32, seed=12)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    a = dsp.draft_markov_sample(Lg, Ug, Wtg, ag, 1.0, seed=9, round=5)
+    rd = torch.full((1,), 5, dtype=torch.int64, device=Lg.device)
+    b = dsp.draft_markov_sample(Lg, Ug, Wtg, ag, 1.0, seed=9, round=0, round_dev=rd)
+    rid = torch.arange(100, 106, dtype=torch.int64, device=Lg.device)
+    e = dsp.draft_markov_sample(Lg, Ug, Wtg, ag, 1.0, seed=9, round=5, req_id=rid)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(a["y"]), host(b["y"]))
+    assert int(host(rd)[0]) == 5  # read, not advanced
+    L, U, W = _f32(c)
+    o = om.chain_sampled(L, U, W, c["anchors"], 1.0, seed=9, rnd=5, req_id=np.arange(100, 106),
+                         forced=host(e["y"]).astype(np.int64))
+    bad = np.argwhere(o["y"] != host(e["y"]))
+    assert all(o["sample_margin"][i, d] < max(SAMPLE_BAND, o["tie_shift"][i, d]) for i, d in bad)
+
+
+def test_chain_sampled_c4_shape():
+    """The Markov-chain workload's shape (256 x 16, V=151,936, rank 256), sampled at T=1;
+    6 requests checked against the oracle through all 16 steps."""
+    c = workloads.markov_chain()
+    _check_sampled(c, 1.0, seed=0, rnd=0, requests=[0, 1, 77, 128, 200, 255])
