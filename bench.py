@@ -14,6 +14,7 @@ Other workloads (--workload):
   scheduled-verify  confidence-scheduled ragged verify (256 x 16, mixed easy/hard streams)
   markov-chain      Markov-head greedy chain (256 requests x 16 steps, rank 256)
   pctree            PCTree expansion (128 x depth 16, k=4, F=16, N=64) + greedy tree verify
+  cycle             sampled Markov draft (256 x 16, emitting its bf16 rows) -> schedule -> pack -> verify
   copy              1 GiB device copy (reference for scaling HBM counters)
 
 Prints ONE JSON line. `roofline` covers the dominant kernel of the workload,
@@ -41,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense-verify",
-                    choices=["dense-verify", "scheduled-verify", "markov-chain", "pctree", "copy"])
+                    choices=["dense-verify", "scheduled-verify", "markov-chain", "pctree", "cycle", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prof-all", action="store_true", help="time every kernel with events (diagnostic)")
@@ -327,6 +328,84 @@ def bench_tree(args):
     return res
 
 
+def bench_cycle(args):
+    """Draft -> schedule -> pack -> verify, one HIP graph per step (the pages' cycle).
+
+    The Markov head samples 16 positions for 256 requests and emits its bf16 rows (the
+    verify's q); the scheduler picks windows from per-position confidences; the pack lays
+    out the verify buffer; the verify checks the windows against target rows laid out in
+    packed order at setup (they stand in for the target forward, which is not part of the
+    method and is not timed).
+    """
+    import numpy as np
+    import torch
+    import block_drafting_verification_amd as dsp
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    c = workloads.cycle_case(256, 16, workloads.V_QWEN3, 256, seed=1006)
+    R, K, V, r = c["R"], c["K"], c["V"], c["rank"]
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    L, U, Wt = bf16(c["L"]), bf16(c["U"]), bf16(np.ascontiguousarray(c["W"].T))
+    a = torch.from_numpy(c["anchors"]).to(dev)
+    conf = torch.from_numpy(c["conf"]).to(dev)
+    cost = torch.from_numpy(c["cost"]).to(dev)
+    w0 = dsp.schedule_windows(conf, cost)["windows"].cpu().numpy()
+    tgt = bf16(workloads.cycle_target(c, w0))
+    rd = torch.zeros(1, dtype=torch.int64, device=dev)
+    ops = {}
+
+    def make_step(stream):
+        dr = dsp.draft_markov_sample(L, U, Wt, a, 1.0, seed=0, round_dev=rd, stream=stream, prepare=True)
+        sch = dsp.schedule_windows(conf, cost, want_survival=False, stream=stream, prepare=True)
+        pk = dsp.pack_ragged(sch.outputs["windows"], a, dr.outputs["y"], stream=stream, prepare=True)
+        ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], dr.outputs["y"], drf=dr.outputs["z"],
+                                   temperature=1.0, seed=0, round_dev=rd, max_rows=tgt.shape[0],
+                                   row_req=pk.outputs["row_req"], row_pos=pk.outputs["row_pos"],
+                                   want_probs=False, stream=stream, prepare=True)
+        ops.update(dr=dr, sch=sch, pk=pk, ver=ver)
+
+        def step():
+            dr()
+            sch()
+            pk()
+            ver()
+        return step
+
+    eager, graph, kern = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "MARKOV_MERGE",
+                                                                          "VERIFY_STATS"], args.prof_all)
+    elapsed = min(eager, graph)
+    for k in ("dr", "pk", "ver"):
+        assert int(ops[k].outputs["status"].item()) == 0, "device status flagged a fault"
+    win = ops["sch"].outputs["windows"].cpu().numpy()
+    assert np.array_equal(win, w0)
+    N = int(win.sum())
+    acc = ops["ver"].outputs["accepted_len"].cpu().numpy()
+    g = kern["MARKOV_GEMM"]["avg_us"]
+    # one sampled step reads L's rows, the previous tokens' U rows and Wt, and writes the bf16 rows
+    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 + R * V * 2
+    res = dict(
+        metric="verified draft tokens/sec", value=N * args.steps / elapsed, unit="tokens/s", n_gpus=1,
+        steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic (Markov-head inputs; target rows = draft base logits + per-request noise, packed order)",
+        config=dict(workload="draft -> schedule -> pack -> verify cycle: 256 requests, 16 sampled drafts, "
+                             "V=151936, rank 256, T=1, additive cost 1+0.05n",
+                    requests=R, block=K, vocab=V, drafted_per_step=R * K, verified_drafts_per_step=N,
+                    packed_rows=R + N, mean_accepted=float(acc.mean()),
+                    drafted_tokens_per_s=R * K * args.steps / elapsed),
+        roofline=dict(kernel="markov_gemm (sampled, emits bf16 rows)", bound="hbm",
+                      achieved=bytes_launch / (g * 1e-6) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=bytes_launch / (g * 1e-6) / 1e9 / PEAK_HBM_GBS, traffic=None,
+                      algorithmic_bytes=bytes_launch, avg_us=g),
+        kernels=kern,
+        timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps))
+    return res
+
+
 def bench_copy(args):
     """Plain device-to-device copy of a 1 GiB buffer: the reference for scaling HBM counters."""
     import torch
@@ -360,6 +439,8 @@ def main():
         res = bench_verify(args, args.workload)
     elif args.workload == "markov-chain":
         res = bench_markov(args)
+    elif args.workload == "cycle":
+        res = bench_cycle(args)
     else:
         res = bench_tree(args)
     print(json.dumps(res))

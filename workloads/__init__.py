@@ -29,6 +29,14 @@ Recipes (N(m, s) = normal with mean m and standard deviation s):
 * PCTree + tree verify: R=128, D=16, V=129,280, rank 256, k=4, F=16, N=64;
   L, U, W as the Markov chain; target logits for the root and each tree node ~ N(0, 3) bf16.
 
+* draft -> schedule -> pack -> verify cycle: the Markov-chain inputs (L, U, W,
+  anchors) draft K positions per request; a noise scale sigma_i ~ U(0.2, 2.0)
+  per request sets both the confidence sigmoid(4 - 2.5 sigma_i + 0.25 eta) and
+  the target row that predicts draft position k, t_{i,k-1} = L_{i,k-1} +
+  sigma_i * eps (t_{i,K} ~ N(0, 3)); the target rows are laid out in packed
+  order for given windows (standing in for the target forward over the packed
+  buffer); cost c(n) = 1.0 + 0.05 n.
+
 Draft tokens x_{i,k} are the synthetic draft model's samples from softmax(d/T)
 (Gumbel-max with this module's own noise), or argmax d when T = 0.
 """
@@ -185,3 +193,36 @@ def pctree():
     c.update(topk=4, frontier=16, topN=64)
     c["target"] = tree_target(128, 65, V_DSV4, seed=2005)
     return c
+
+
+def cycle_case(R, K, V, rank, seed):
+    """Inputs of the draft -> schedule -> pack -> verify cycle (see the module docstring)."""
+    c = markov_case(R, K, V, rank=rank, seed=seed)
+    rng = _rng(seed + 7)
+    sig = rng.uniform(0.2, 2.0, size=R).astype(np.float32)
+    eta = rng.standard_normal((R, K))
+    c["conf"] = (1.0 / (1.0 + np.exp(-(4.0 - 2.5 * sig[:, None] + 0.25 * eta)))).astype(np.float32)
+    c["cost"] = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
+    c["sigma"] = sig
+    c["K"] = K
+    c["target_seed"] = seed + 11
+    return c
+
+
+def cycle_target(c, windows):
+    """Packed target rows (bf16 bits) for the given windows: request i owns rows for positions
+    0..windows[i]; the row of position k < K is L_{i,k} + sigma_i * eps, that of position K is
+    N(0, 3). Rows are drawn in packed order from one generator, so they depend only on the
+    windows and the case."""
+    rng = _rng(c["target_seed"])
+    L = c["L"]
+    R, K, V = c["R"], c["K"], c["V"]
+    rows = []
+    for i in range(R):
+        for k in range(int(windows[i]) + 1):
+            eps = rng.standard_normal(V, dtype=np.float32)
+            if k < K:
+                rows.append(f32_to_bf16_bits(bf16_bits_to_f32(L[i, k]) + c["sigma"][i] * eps))
+            else:
+                rows.append(f32_to_bf16_bits(np.float32(3.0) * eps))
+    return np.stack(rows)
