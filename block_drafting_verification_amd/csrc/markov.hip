@@ -187,11 +187,13 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   constexpr int NR = KS <= 16 && LAL ? 3 : 2;  // stages in flight per thread (register ring)
   constexpr int NU = NR % 2 ? 2 * NR : NR;     // stages per unrolled loop body (ring slot and
                                                // buffer parity both static)
-  // asynchronous ring loads (kernels that do not spill). Not with global stores in the
-  // loop (the sampled chain's rows): stores share the vector memory counter with the
-  // loads and may complete out of order with them, so counted waits would not cover the
-  // ring; the compiler's own waits do.
-  constexpr bool AS = KS <= 16 && MODE != MODE_SAMPLE;
+  // asynchronous ring loads (kernels that do not spill). The sampled chain's global
+  // stores share the vector memory counter with the ring's loads and may retire in any
+  // order relative to them, but loads return in order among themselves: with at most
+  // (NR-1)*LPS operations outstanding, the loads of the oldest stage cannot still be
+  // pending (every later stage's loads would be too, more than that count), so the
+  // counted waits stay sufficient; stores still in flight only make them wait longer.
+  constexpr bool AS = KS <= 16;
   static_assert(LST % kGT == 0, "L stage must split evenly over the workgroup");
   extern __shared__ u32x4 lds[];              // [2][WST + LST]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -488,6 +490,10 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       }
     }
   }
+  // The ring's trailing loads (past the range: they read zeros) must land before any
+  // code after the loop runs: the ring registers are dead from here on, and the
+  // compiler may hand them to the epilogue below while a load into them is in flight.
+  vm_wait<0>();
   // the last stage's epilogue (accumulator picked by two static paths: indexing the
   // pair with a run-time value would move it to scratch memory)
   auto finish = [&](const f32x16& last) {
@@ -512,7 +518,6 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     bidx = (s_begin + (bcode >> 4)) * kTS + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
   }
 
-  vm_wait<0>();  // the ring's trailing loads (all out of range) land before the wave ends
   // merge lane pairs (lane, lane ^ 32 hold the same parent row), then lanes < 32 write
   if (MODE == MODE_TREE) {
     float ov[kTopK];
