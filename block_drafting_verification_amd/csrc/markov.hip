@@ -45,6 +45,7 @@ constexpr int kTR = 32 * kWaves;  // parent rows per workgroup: one 32-row MFMA 
 constexpr int kTS = 32;           // vocabulary entries per pipeline stage (one 32-row MFMA block)
 constexpr int kTopK = 4;          // children tracked per parent
 constexpr int kTargetWGs = 256;   // one workgroup per CU
+constexpr int kZS = 80;           // bytes per row of a wave's staging tile of emitted logits (64 + pad)
 
 enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2, MODE_SAMPLE = 3 };
 
@@ -394,21 +395,32 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         hb[q] = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
         z[q] = __uint_as_float(hb[q] << 16);
       }
-      if (rvalid) {
-        uint16_t* zr = a.zout + (size_t)row * a.ldz_r + (size_t)a.d * a.ldz_d;
-        const int vb = v0 + 4 * (lane >> 5);
+      // through this wave's private LDS tile (32 rows x 32 tokens, rows kZS bytes
+      // apart): lanes write their runs of four, then read back 16 bytes of one row each,
+      // so every global store writes 16 rows x 64 contiguous bytes
+      char* zt = (char*)(lds + 2 * (WST + LST)) + wave * (32 * kZS);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int v = vb + 8 * h;
-          if (v + 4 <= a.V) {
-            uint2 w;
-            w.x = hb[4 * h] | (hb[4 * h + 1] << 16);
-            w.y = hb[4 * h + 2] | (hb[4 * h + 3] << 16);
-            *(uint2*)(zr + v) = w;
+      for (int h = 0; h < 4; ++h) {
+        uint2 w;
+        w.x = hb[4 * h] | (hb[4 * h + 1] << 16);
+        w.y = hb[4 * h + 2] | (hb[4 * h + 3] << 16);
+        *(uint2*)(zt + (lane & 31) * kZS + 16 * h + 8 * (lane >> 5)) = w;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rl = (lane >> 2) + 16 * j, ch = lane & 3;
+        const uint4 w = *(const uint4*)(zt + rl * kZS + 16 * ch);
+        const int grow = r0 + wave * 32 + rl;
+        const int v = v0 + 8 * ch;
+        if (grow < a.rows) {
+          uint16_t* zp = a.zout + (size_t)grow * a.ldz_r + (size_t)a.d * a.ldz_d + v;
+          if (v + 8 <= a.V) {
+            *(uint4*)zp = w;
           } else {
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (v + e < a.V) zr[v + e] = (uint16_t)hb[4 * h + e];
+            for (int e = 0; e < 8; ++e)
+              if (v + e < a.V) zp[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
           }
         }
       }
@@ -985,7 +997,9 @@ int ksteps(int rank) {
   return ks;
 }
 
-size_t gemm_lds_bytes(int ks) { return (size_t)2 * (kTS * 2 * ks + kTR * 4) * 16; }
+size_t gemm_lds_bytes(int ks, int mode) {
+  return (size_t)2 * (kTS * 2 * ks + kTR * 4) * 16 + (mode == MODE_SAMPLE ? (size_t)kWaves * 32 * kZS : 0);
+}
 
 int pick_groups(int rows, int V) {
   const int nrb = (rows + kTR - 1) / kTR;
@@ -1008,7 +1022,7 @@ int32_t launch_gemm_ks(int kid, GemmArgs a, hipStream_t s) {
   a.nrb = (a.rows + kTR - 1) / kTR;
   a.xcd_map = a.nrb > 1 && a.G % 8 == 0;
   launch(kid, markov_gemm_kernel<MODE, KS, LAL>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT),
-         (uint32_t)gemm_lds_bytes(KS), s, a);
+         (uint32_t)gemm_lds_bytes(KS, MODE), s, a);
   return hip_check(hipGetLastError(), "markov gemm launch");
 }
 
