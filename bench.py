@@ -399,7 +399,8 @@ def bench_cycle(args):
                     drafted_tokens_per_s=R * K * args.steps / elapsed),
         roofline=dict(kernel="markov_gemm (sampled, emits bf16 rows)", bound="hbm",
                       achieved=bytes_launch / (g * 1e-6) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=bytes_launch / (g * 1e-6) / 1e9 / PEAK_HBM_GBS, traffic=None,
+                      frac=bytes_launch / (g * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                      traffic=traffic_from_profiles("markov.hip", "markov_gemm", "cycle"),
                       algorithmic_bytes=bytes_launch, avg_us=g),
         kernels=kern,
         timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps))
