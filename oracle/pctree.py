@@ -26,6 +26,11 @@ top-N ranges over every kept frontier node of every depth, root excluded. Since
 log pi <= 0 a child never outranks its parent, so the depth-ascending tie-break
 keeps the tree ancestor-closed.
 
+The verify's target forward attends tree-causally: node j sees itself and its
+ancestors. ``ancestor_masks`` writes that relation as bit sets, word w of node
+j holding bit (a mod 64) for every ancestor-or-self a with a // 64 == w (the
+root is implicit and not a bit).
+
 Pinned by: k = 1, F = 1 reduces to the greedy Markov chain; with no pruning on
 a tiny vocabulary the tree equals brute-force top-N over all paths by summed
 fp64 log-probability; invariants parent[j] < j, ancestor closure, scores
@@ -118,3 +123,18 @@ def tree_expand(L, U, W, anchor, topk, frontier, topN, requests=None):
             tok[i, j], par[i, j], dep[i, j], sc[i, j] = n["token"], n["parent"], n["depth"], n["score"]
     return dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, n_nodes=nn,
                 min_gap=gaps)
+
+
+def ancestor_masks(node_parent, n_nodes):
+    """[R, N, ceil(N/64)] uint64 ancestor-or-self bit sets of the tree nodes (0 past n_nodes)."""
+    par = np.asarray(node_parent, dtype=np.int64)
+    R, N = par.shape
+    Wd = (N + 63) // 64
+    out = np.zeros((R, N, Wd), dtype=np.uint64)
+    for i in range(R):
+        for j in range(int(n_nodes[i])):
+            a = j
+            while a >= 0:
+                out[i, j, a // 64] |= np.uint64(1) << np.uint64(a % 64)
+                a = int(par[i, a])
+    return out

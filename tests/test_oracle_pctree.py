@@ -88,3 +88,30 @@ def test_tree_invariants(k, F, N):
             assert len(set(sib.tolist())) == len(sib)
         for d in range(1, D + 1):
             assert (dep == d).sum() <= F
+
+
+def test_ancestor_masks_chain_closed_form():
+    """A chain-shaped tree: node j's ancestors-or-self are 0..j, i.e. the low j+1 bits."""
+    N = 130
+    par = np.arange(-1, N - 1)[None]
+    m = opt.ancestor_masks(par, [N])
+    for j in range(N):
+        want = [0, 0, 0]
+        for a in range(j + 1):
+            want[a // 64] |= 1 << (a % 64)
+        assert [int(x) for x in m[0, j]] == want
+
+
+def test_ancestor_masks_popcount_is_depth_and_closed():
+    L, U, W, a = _case(3, 4, 200, seed=6, boost=200)
+    t = opt.tree_expand(L, U, W, a, topk=3, frontier=5, topN=12)
+    m = opt.ancestor_masks(t["node_parent"], t["n_nodes"])
+    for i in range(3):
+        for j in range(int(t["n_nodes"][i])):
+            bits = [b for b in range(12) if (int(m[i, j, 0]) >> b) & 1]
+            assert len(bits) == t["node_depth"][i, j]
+            assert j in bits and max(bits) == j
+            p = t["node_parent"][i, j]
+            if p >= 0:
+                assert int(m[i, j, 0]) == int(m[i, p, 0]) | (1 << j)
+        assert np.all(m[i, int(t["n_nodes"][i]):] == 0)
