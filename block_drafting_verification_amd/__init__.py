@@ -320,9 +320,11 @@ def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_
                    (L, U, Wt, prev_tok, round_dev, req_id, ws))
 
 
-def tree_expand(L, U, Wt, anchor, topk, frontier, topN, out=None, status=None, stream=None, prepare=False):
+def tree_expand(L, U, Wt, anchor, topk, frontier, topN, want_mask=False, out=None, status=None, stream=None,
+                prepare=False):
     """PCTree expansion. Returns dict(node_token, node_parent, node_depth [R, topN] int32,
-    node_score float64 [R, topN], n_nodes int32 [R], status)."""
+    node_score float64 [R, topN], n_nodes int32 [R], anc_mask int64 [R, topN, ceil(topN/64)]
+    (uint64 bit sets: node o's ancestors and itself) or None, status)."""
     _check_markov(L, U, Wt)
     R, D, V = L.shape
     rank = U.shape[1]
@@ -334,14 +336,18 @@ def tree_expand(L, U, Wt, anchor, topk, frontier, topN, out=None, status=None, s
     dep = _take(o, "node_depth", lambda: torch.empty(R, topN, dtype=torch.int32, device=dev))
     sc = _take(o, "node_score", lambda: torch.empty(R, topN, dtype=torch.float64, device=dev))
     nn = _take(o, "n_nodes", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    words = (topN + 63) // 64
+    mask = _take(o, "anc_mask", lambda: torch.empty(R, topN, words, dtype=torch.int64, device=dev)) \
+        if want_mask else None
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     nbytes = lib().dsp_tree_expand_workspace_size(R, D, V, rank, topk, frontier, topN)
     ws = _workspace(nbytes, dev, prepare)
     args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(anchor), R, D, topk,
-            frontier, topN, _ptr(tok), _ptr(par), _ptr(dep), _ptr(sc), _ptr(nn), _ptr(status), _ptr(ws),
-            ws.numel(), _stream(stream))
-    res = dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, n_nodes=nn, status=status)
+            frontier, topN, _ptr(tok), _ptr(par), _ptr(dep), _ptr(sc), _ptr(nn), _ptr(mask), _ptr(status),
+            _ptr(ws), ws.numel(), _stream(stream))
+    res = dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, n_nodes=nn, anc_mask=mask,
+               status=status)
     return _finish(lib().dsp_tree_expand, args, res, prepare, (L, U, Wt, anchor, ws))
 
 

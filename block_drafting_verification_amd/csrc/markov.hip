@@ -916,6 +916,7 @@ struct TreeFinalArgs {
   int32_t* node_depth;
   double* node_score;
   int32_t* n_nodes;
+  uint64_t* anc_mask;  // nullable: [R, topN, W] ancestor-or-self bit sets, W = ceil(topN / 64)
 };
 
 __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
@@ -923,6 +924,7 @@ __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
   __shared__ int32_t s_valid[1024];
   __shared__ int32_t s_out[1024];
   __shared__ int32_t fsz[1024];
+  __shared__ int32_t s_par[1024];  // parent of each output node, in output order
   const int i = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) {
     int prev = 1;  // frontier size after depth d: min(F, topk * previous)
@@ -975,10 +977,12 @@ __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
     if (o < 0) continue;
     const Kept k = kr[e];
     const size_t at = (size_t)i * a.topN + o;
+    const int po = k.parent < 0 ? -1 : s_out[k.parent];
     a.node_token[at] = k.token;
-    a.node_parent[at] = k.parent < 0 ? -1 : s_out[k.parent];
+    a.node_parent[at] = po;
     a.node_depth[at] = e / a.F + 1;
     a.node_score[at] = k.score;
+    s_par[o] = po;
   }
   for (int o = nout + tid; o < a.topN; o += 256) {
     const size_t at = (size_t)i * a.topN + o;
@@ -988,6 +992,23 @@ __global__ __launch_bounds__(256) void tree_final_kernel(TreeFinalArgs a) {
     a.node_score[at] = 0.0;
   }
   if (tid == 0) a.n_nodes[i] = nout;
+  if (a.anc_mask) {
+    // node o sees itself and its ancestors (tree-causal attention in the verify's
+    // target forward): per word, walk the parent chain (parent[o] < o) and collect the
+    // bits that fall in that word
+    __syncthreads();
+    const int W = (a.topN + 63) / 64;
+    for (int o = tid; o < a.topN; o += 256) {
+      uint64_t* mo = a.anc_mask + ((size_t)i * a.topN + o) * W;
+      for (int w = 0; w < W; ++w) {
+        uint64_t m = 0;
+        if (o < nout)
+          for (int c = o; c >= 0 && c >= 64 * w; c = s_par[c])
+            if (c < 64 * (w + 1)) m |= 1ull << (c & 63);
+        mo[w] = m;
+      }
+    }
+  }
 }
 
 // k-steps of 16 for a rank (rank padded with zeros to a power of two >= 32)
@@ -1206,8 +1227,8 @@ extern "C" int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r
                                    const int32_t* anchor, int32_t R, int32_t D, int32_t topk,
                                    int32_t frontier, int32_t topN, int32_t* node_token,
                                    int32_t* node_parent, int32_t* node_depth, double* node_score,
-                                   int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   int32_t* n_nodes, uint64_t* anc_mask, int32_t* status, void* ws,
+                                   size_t ws_bytes, void* stream) {
   clear_error();
   int32_t rc = check_markov_common(L, l_dtype, U, Wt, V, rank);
   if (rc) return rc;
@@ -1248,7 +1269,7 @@ extern "C" int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r
     fp = fn;
   }
   TreeFinalArgs fa{kept, T.kept_stride, D, frontier, topk, topN, R, node_token, node_parent, node_depth,
-                   node_score, n_nodes};
+                   node_score, n_nodes, anc_mask};
     launch(DSP_K_TREE_FINAL, tree_final_kernel, dim3(R), dim3(256), 0, s, fa);
   return hip_check(hipGetLastError(), "tree final launch");
 }

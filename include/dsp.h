@@ -277,6 +277,10 @@ int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, i
 /* parents re-indexed into that order (parent[j] < j, -1 = root).             */
 /* Outputs [R, topN] (row stride topN): node_token, node_parent, node_depth   */
 /* (int32), node_score (fp64); n_nodes [R] = nodes written (rest: -1 / 0).    */
+/* anc_mask (nullable): [R, topN, W] uint64, W = ceil(topN / 64): bit (j % 64) */
+/* of word j / 64 of node o is set iff node j is o or an ancestor of o (the   */
+/* root is implicit) -- the tree-causal attention pattern of the target      */
+/* forward that verifies the tree ([P]); rows past n_nodes are zero.         */
 /* L, U, Wt layouts as dsp_draft_markov_step.                                 */
 /* Limits: 1 <= topk <= min(4, V), 1 <= frontier <= 64, topk*frontier <= 256,  */
 /* 1 <= topN <= 1024, D*frontier <= 1024, rank as above.                      */
@@ -288,7 +292,7 @@ int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t l
                         const int32_t* anchor, int32_t R, int32_t D, int32_t topk,
                         int32_t frontier, int32_t topN,
                         int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
-                        double* node_score, int32_t* n_nodes, int32_t* status,
+                        double* node_score, int32_t* n_nodes, uint64_t* anc_mask, int32_t* status,
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

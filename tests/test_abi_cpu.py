@@ -88,8 +88,13 @@ def test_host_validation_codes():
     assert lib.dsp_draft_markov_step(p, 1, 1000, 100, ctypes.c_void_p(18), p, 100, 64, p, 2, 4, p, 4, None,
                                      p, p, 1 << 30, None) == -4
     # tree: top-k above 4
-    assert lib.dsp_tree_expand(p, 1, 1000, 100, p, p, 100, 64, p, 2, 4, 5, 4, 8, p, p, p, p, p, p, p,
+    assert lib.dsp_tree_expand(p, 1, 1000, 100, p, p, 100, 64, p, 2, 4, 5, 4, 8, p, p, p, p, p, None, p, p,
                                1 << 30, None) == -2
+    # sampled chain: temperature 0 is the greedy entry point's; misaligned emitted rows
+    assert lib.dsp_draft_markov_sample(p, 1, 1000, 100, p, p, 100, 64, p, 2, 4, 0.0, 0, 0, None, None, p, 4,
+                                       None, p, 1000, 100, p, p, 1 << 30, None) == -2
+    assert lib.dsp_draft_markov_sample(p, 1, 1000, 100, p, p, 100, 64, p, 2, 4, 1.0, 0, 0, None, None, p, 4,
+                                       None, ctypes.c_void_p(24), 1000, 104, p, p, 1 << 30, None) == -4
 
 
 def test_workspace_queries_are_pure_functions():

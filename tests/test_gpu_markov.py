@@ -93,11 +93,13 @@ def _check_tree(c, topk, F, N, requests=None, w_boost=1.0):
         L, U, W = _f32(c)
     Lg, Ug, Wtg, ag = _gpu_inputs(c)
     print(f"tree R={c['R']} D={c['B']} V={c['V']} k={topk} F={F} N={N}", flush=True)
-    g = dsp.tree_expand(Lg, Ug, Wtg, ag, topk, F, N)
+    g = dsp.tree_expand(Lg, Ug, Wtg, ag, topk, F, N, want_mask=True)
     torch.cuda.synchronize()
     assert int(host(g["status"])[0]) == 0
+    gm = host(g["anc_mask"]).view(np.uint64)
     sel = list(range(c["R"])) if requests is None else list(requests)
     o = opt.tree_expand(L, U, W, c["anchors"], topk, F, N, requests=sel)
+    om_mask = opt.ancestor_masks(o["node_parent"], o["n_nodes"])
     ties = TieCounter()
     gt, gp, gd, gs, gn = (host(g[k]) for k in ("node_token", "node_parent", "node_depth", "node_score", "n_nodes"))
     for i in sel:
@@ -110,13 +112,14 @@ def _check_tree(c, topk, F, N, requests=None, w_boost=1.0):
             continue
         n = gn[i]
         np.testing.assert_allclose(gs[i, :n], o["node_score"][i, :n], rtol=1e-5, atol=1e-5)
+        np.testing.assert_array_equal(gm[i], om_mask[i])  # tree-causal ancestor masks, exact
     ties.check()
     return g
 
 
 @pytest.mark.parametrize("R,D,V,k,F,N,rank", [(3, 4, 700, 2, 3, 8, 32), (9, 6, 5003, 4, 16, 64, 64),
                                               (2, 3, 40000, 4, 16, 20, 256), (140, 2, 300, 3, 5, 7, 32),
-                                              (20, 3, 40000, 4, 16, 30, 64)])
+                                              (20, 3, 40000, 4, 16, 30, 64), (3, 8, 3000, 4, 16, 100, 32)])
 def test_tree_small(R, D, V, k, F, N, rank):
     c = workloads.markov_case(R, D, V, rank=rank, seed=7 * R + V)
     _check_tree(c, k, F, N, w_boost=200.0)
