@@ -917,25 +917,21 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(SampleArgs a)
   }
 }
 
-// Inverse-CDF draw, one workgroup per request: locate the chunk holding u' * total from
-// the chunk sums, rescan it with contiguous per-thread ranges and an fp64 exclusive scan,
-// and let the owning thread walk its range to the first element past the target.
+// Inverse-CDF draw of request i's job, one workgroup: s_csum (LDS) holds the job's
+// weight per chunk of a.ce elements; locate the chunk holding u' * total, rescan it
+// with contiguous per-thread ranges and an fp64 exclusive scan, and let the owning
+// thread walk its range to the first element past the target.
 template <typename TT, typename TD>
-__global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArgs a) {
-  __shared__ double s_csum[64];
+__device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s_csum) {
   __shared__ double s_wtot[kSampleThreads / 64];
   __shared__ int s_chunk;
   __shared__ double s_tau;
   __shared__ int s_found;
   __shared__ int s_lastp[kSampleThreads / 64];
-  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const Job jb = a.jobs[i];
-  if (jb.mode == JOB_NONE) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   bool resid = jb.mode == JOB_RESID;
   const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
   const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
-  if (tid < 64) s_csum[tid] = tid < a.nch2 ? a.rsum[(size_t)i * a.nch2 + tid] : 0.0;
-  __syncthreads();
   double total = 0.0;
   for (int c = 0; c < a.nch2; ++c) total += s_csum[c];
   if (resid && !(total > 0.0)) {
@@ -1030,6 +1026,103 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArg
   if (tid == 0) *dst = s_found;
 }
 
+template <typename TT, typename TD>
+__global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArgs a) {
+  __shared__ double s_csum[64];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const Job jb = a.jobs[i];
+  if (jb.mode == JOB_NONE) return;
+  if (tid < 64) s_csum[tid] = tid < a.nch2 ? a.rsum[(size_t)i * a.nch2 + tid] : 0.0;
+  __syncthreads();
+  sample_draw<TT, TD>(a, i, jb, s_csum);
+}
+
+// Decisions, residual / bonus mass and the draw of one request in one workgroup of
+// kSampleThreads: the first wavefront decides (accepted prefix, outputs, the job of
+// the draw); all waves then stream the job's row(s) once -- a 16-byte vector of each
+// row per thread per block of kSampleGrain elements, kFinBatch blocks of loads in
+// flight -- adding each thread's weights per chunk of a.ce elements (a multiple of
+// the block, so blocks never straddle chunks); a wavefront sum per chunk goes to LDS,
+// and the draw proceeds from those chunk masses. No other workgroup is involved, so
+// the request needs no hand-off through memory.
+constexpr int kFinBatch = 4;
+template <typename TT, typename TD>
+__global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArgs da, SampleArgs a) {
+  __shared__ Job s_job;
+  __shared__ double s_part[64][kSampleThreads / 64];
+  __shared__ double s_csum[64];
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < 64) {
+    const int base = da.cu[i], end = da.cu[i + 1];
+    const int n = end - base - 1;
+    if (n < 0 || n > da.K || base < 0 || end > da.max_rows) {
+      fault_request(da, i, DSP_STATUS_WINDOW_RANGE);
+      if (tid == 0) s_job.mode = JOB_NONE;
+    } else {
+      decide_sampled<TT, TD>(da, i, &s_job);
+    }
+  }
+  __syncthreads();
+  const Job jb = s_job;
+  if (jb.mode == JOB_NONE) return;  // uniform over the workgroup
+  const bool resid = jb.mode == JOB_RESID;
+  const JobFrame f = job_frame(jb, a.cl, resid);
+  const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
+  const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
+  const bool al = (((uintptr_t)tp) & 15u) == 0 && (!resid || (((uintptr_t)dp) & 15u) == 0);
+  const int nblk = (a.V + kSampleGrain - 1) / kSampleGrain;
+  const int bpc = a.ce / kSampleGrain;  // blocks per chunk
+  double run = 0.0;
+  for (int j0 = 0; j0 < nblk; j0 += kFinBatch) {
+    Raw8<TT> rt[kFinBatch];
+    Raw8<TD> rd[kFinBatch];
+    bool fast[kFinBatch];
+#pragma unroll
+    for (int b = 0; b < kFinBatch; ++b) {
+      const int e = (j0 + b) * kSampleGrain + tid * 8;
+      fast[b] = al && e + 8 <= a.V;
+      if (fast[b]) {
+        rt[b].load(tp + e);
+        if (resid) rd[b].load(dp + e);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kFinBatch; ++b) {
+      const int j = j0 + b;
+      if (j >= nblk) break;  // uniform
+      const int e = j * kSampleGrain + tid * 8;
+      float wsum = 0.f;
+      if (fast[b]) {
+        float t[8], d[8];
+        rt[b].unpack(t);
+        if (resid) rd[b].unpack(d);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wsum += job_weight(f, t[q], resid ? d[q] : 0.f);
+      } else if (e < a.V) {
+        wsum = job_weight8<TT, TD>(f, tp, dp, false, false, e, a.V);
+      }
+      run += (double)wsum;
+      if ((j + 1) % bpc == 0 || j + 1 == nblk) {  // the chunk ends with this block (uniform)
+        double s = run;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0) s_part[j / bpc][w] = s;
+        run = 0.0;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    double c = 0.0;
+    if (tid < a.nch2)
+#pragma unroll
+      for (int q = 0; q < kSampleThreads / 64; ++q) c += s_part[tid][q];
+    s_csum[tid] = c;
+  }
+  __syncthreads();
+  sample_draw<TT, TD>(a, i, jb, s_csum);
+}
+
 int g_cus = 0;
 int num_cus() {
   if (g_cus == 0) {
@@ -1041,6 +1134,18 @@ int num_cus() {
       g_cus = 256;
   }
   return g_cus;
+}
+
+// Chunking of the one-workgroup finish: at most 64 chunks of a multiple of kSampleGrain.
+__host__ __device__ inline SampleGeom finish_geom(int V) {
+  int n = (V + kSampleGrain - 1) / kSampleGrain;
+  if (n > 64) n = 64;
+  int ce = (V + n - 1) / n;
+  ce = (ce + kSampleGrain - 1) / kSampleGrain * kSampleGrain;
+  SampleGeom g;
+  g.ce = ce;
+  g.nch2 = (V + ce - 1) / ce;
+  return g;
 }
 
 struct VerifyLayout {
@@ -1081,11 +1186,23 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
   const long g = stats_grid(max_items);
   launch(DSP_K_VERIFY_STATS, verify_stats_kernel<TT, TD>, dim3((unsigned)g), dim3(kThreads), 0, s, sa, sa.cu,
          sa.row_req, sa.row_pos);
-  launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
-  const long ri = (long)pa.R * pa.nch2;
-  const long g2 = ri < (long)cus * 8 ? ri : (long)cus * 8;
-  launch(DSP_K_VERIFY_RESIDUAL, verify_residual_kernel<TT, TD>, dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
-  launch(DSP_K_VERIFY_SAMPLE, verify_sample_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
+  if (4l * pa.R >= 3l * cus) {
+    // enough requests to give nearly every CU one: decide, stream and draw each request
+    // in its own workgroup (no hand-off between launches)
+    SampleArgs fa = pa;
+    const SampleGeom fg = finish_geom(pa.V);
+    fa.nch2 = fg.nch2;
+    fa.ce = fg.ce;
+    launch(DSP_K_VERIFY_SAMPLE, verify_finish_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, da, fa);
+  } else {
+    // few requests: one CU per request would leave most of the chip idle on the residual
+    // rows (two exponentials per element), so the rows are spread over every CU
+    launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
+    const long ri = (long)pa.R * pa.nch2;
+    const long g2 = ri < (long)cus * 8 ? ri : (long)cus * 8;
+    launch(DSP_K_VERIFY_RESIDUAL, verify_residual_kernel<TT, TD>, dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
+    launch(DSP_K_VERIFY_SAMPLE, verify_sample_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
+  }
 }
 
 template <typename TT>

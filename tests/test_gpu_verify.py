@@ -289,3 +289,31 @@ def test_cap_accept(T, dt, V):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(gc["accepted_len"]), host(g["accepted_len"]))
     np.testing.assert_array_equal(host(gc["out_tokens"]), host(g["out_tokens"]))
+
+
+def test_scheduled_ragged_verify_full():
+    """The confidence-scheduled ragged verify workload: 256 requests x K=16, V=151,936 bf16;
+    scheduler -> pack -> compact verify on the GPU, every request checked against the oracle
+    (256 requests take the one-workgroup-per-request decision and draw)."""
+    c = workloads.scheduled_verify()
+    R, K, V = c["R"], c["K"], c["V"]
+    sch = dsp.schedule_windows(to_gpu(c["conf"]), to_gpu(c["cost"]))
+    xg = to_gpu(c["x"].astype(np.int32))
+    pk = dsp.pack_ragged(sch["windows"], to_gpu(c["anchors"]), xg)
+    w = host(sch["windows"])
+    tp = packed_from_dense(c["t"], w)
+    print(f"scheduled verify R={R} K={K} V={V} packed rows={tp.shape[0]} drafts={int(w.sum())}", flush=True)
+    g = dsp.verify_rejection(logits_to_gpu(tp, "bf16"), pk["cu_seqlens"], xg, drf=logits_to_gpu(c["d"], "bf16"),
+                             temperature=1.0, seed=0, round=3, row_req=pk["row_req"], row_pos=pk["row_pos"])
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    cu = cu_from_windows(w)
+    np.testing.assert_array_equal(host(pk["cu_seqlens"]), cu)
+    tv = values(tp, "bf16").astype(np.float64)
+    dv = values(c["d"], "bf16").astype(np.float64)
+
+    def orc(forced):
+        return ov.verify_chain(tv, cu, dv, c["x"], 1.0, seed=0, rnd=3, forced_len=forced)
+    ties = TieCounter()
+    compare_chain_verify(g, orc, R, K, w, ties)
+    ties.check()
