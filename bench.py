@@ -14,7 +14,8 @@ Other workloads (--workload):
   scheduled-verify  confidence-scheduled ragged verify (256 x 16, mixed easy/hard streams)
   markov-chain      Markov-head greedy chain (256 requests x 16 steps, rank 256)
   pctree            PCTree expansion (128 x depth 16, k=4, F=16, N=64) + greedy tree verify
-  cycle             sampled Markov draft (256 x 16, emitting its bf16 rows) -> schedule -> pack -> verify
+  cycle             sampled Markov draft (256 x 16, emitting its bf16 rows) -> confidence head -> schedule
+                    -> pack -> verify
   copy              1 GiB device copy (reference for scaling HBM counters)
 
 Prints ONE JSON line. `roofline` covers the dominant kernel of the workload,
@@ -329,10 +330,12 @@ def bench_tree(args):
 
 
 def bench_cycle(args):
-    """Draft -> schedule -> pack -> verify, one HIP graph per step (the pages' cycle).
+    """Draft -> confidence head -> schedule -> pack -> verify, one HIP graph per step (the
+    pages' cycle).
 
     The Markov head samples 16 positions for 256 requests and emits its bf16 rows (the
-    verify's q); the scheduler picks windows from per-position confidences; the pack lays
+    verify's q); the confidence head (hidden size 4096, sequential temperatures) gives the
+    per-position confidences from which the scheduler picks windows; the pack lays
     out the verify buffer; the verify checks the windows against target rows laid out in
     packed order at setup (they stand in for the target forward, which is not part of the
     method and is not timed).
@@ -351,25 +354,30 @@ def bench_cycle(args):
 
     L, U, Wt = bf16(c["L"]), bf16(c["U"]), bf16(np.ascontiguousarray(c["W"].T))
     a = torch.from_numpy(c["anchors"]).to(dev)
-    conf = torch.from_numpy(c["conf"]).to(dev)
+    hd = workloads.cycle_head_inputs(c)
+    hh, hw = bf16(hd["h"]), bf16(hd["w"])
+    temps = torch.from_numpy(hd["temps"]).to(dev)
     cost = torch.from_numpy(c["cost"]).to(dev)
-    w0 = dsp.schedule_windows(conf, cost)["windows"].cpu().numpy()
+    conf0 = dsp.confidence_head(hh, hw, hd["bias"], temps)["conf"]
+    w0 = dsp.schedule_windows(conf0, cost)["windows"].cpu().numpy()
     tgt = bf16(workloads.cycle_target(c, w0))
     rd = torch.zeros(1, dtype=torch.int64, device=dev)
     ops = {}
 
     def make_step(stream):
         dr = dsp.draft_markov_sample(L, U, Wt, a, 1.0, seed=0, round_dev=rd, stream=stream, prepare=True)
-        sch = dsp.schedule_windows(conf, cost, want_survival=False, stream=stream, prepare=True)
+        ch = dsp.confidence_head(hh, hw, hd["bias"], temps, stream=stream, prepare=True)
+        sch = dsp.schedule_windows(ch.outputs["conf"], cost, want_survival=False, stream=stream, prepare=True)
         pk = dsp.pack_ragged(sch.outputs["windows"], a, dr.outputs["y"], stream=stream, prepare=True)
         ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], dr.outputs["y"], drf=dr.outputs["z"],
                                    temperature=1.0, seed=0, round_dev=rd, max_rows=tgt.shape[0],
                                    row_req=pk.outputs["row_req"], row_pos=pk.outputs["row_pos"],
                                    want_probs=False, stream=stream, prepare=True)
-        ops.update(dr=dr, sch=sch, pk=pk, ver=ver)
+        ops.update(dr=dr, ch=ch, sch=sch, pk=pk, ver=ver)
 
         def step():
             dr()
+            ch()
             sch()
             pk()
             ver()
@@ -378,7 +386,7 @@ def bench_cycle(args):
     eager, graph, kern = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "MARKOV_MERGE",
                                                                           "VERIFY_STATS"], args.prof_all)
     elapsed = min(eager, graph)
-    for k in ("dr", "pk", "ver"):
+    for k in ("dr", "ch", "pk", "ver"):
         assert int(ops[k].outputs["status"].item()) == 0, "device status flagged a fault"
     win = ops["sch"].outputs["windows"].cpu().numpy()
     assert np.array_equal(win, w0)
@@ -392,8 +400,8 @@ def bench_cycle(args):
         steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic (Markov-head inputs; target rows = draft base logits + per-request noise, packed order)",
-        config=dict(workload="draft -> schedule -> pack -> verify cycle: 256 requests, 16 sampled drafts, "
-                             "V=151936, rank 256, T=1, additive cost 1+0.05n",
+        config=dict(workload="draft -> confidence head -> schedule -> pack -> verify cycle: 256 requests, "
+                             "16 sampled drafts, V=151936, rank 256, hidden 4096, T=1, additive cost 1+0.05n",
                     requests=R, block=K, vocab=V, drafted_per_step=R * K, verified_drafts_per_step=N,
                     packed_rows=R + N, mean_accepted=float(acc.mean()),
                     drafted_tokens_per_s=R * K * args.steps / elapsed),

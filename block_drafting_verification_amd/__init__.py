@@ -8,6 +8,7 @@ kernels of libdsp.so. The library must be built first
 to another implementation.
 
 Calls (same names as the C entry points without the ``dsp_`` prefix):
+  confidence_head    -- per-position confidences (linear projection + sigmoid, STS temperatures)
   schedule_windows   -- survival products + hardware-aware prefix scheduler
   pack_ragged        -- front-packed cu_seqlens verify buffer
   verify_rejection   -- batched ragged rejection / greedy / tree verify
@@ -25,7 +26,7 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
                    DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE,
                    DspError, KERNELS)
 
-__all__ = ["PreparedCall", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step",
+__all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step",
            "draft_markov_sample", "tree_expand",
            "philox_uniforms", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
@@ -125,6 +126,25 @@ def philox_uniforms(ctr, seed, stream=None):
     out = torch.empty(ctr.shape, dtype=torch.float64, device=ctr.device)
     _abi.check(lib().dsp_philox_uniforms(_ptr(ctr), ctr.shape[0], seed, _ptr(out), _stream(stream)))
     return out
+
+
+def confidence_head(h, w, bias, sts_temp=None, out=None, status=None, stream=None, prepare=False):
+    """Confidence head: h [R, K, H] (bf16/fp32, unit inner stride), w [H], scalar bias,
+    sts_temp float32 [K] or None. Returns dict(conf float32 [R, K], status)."""
+    _on_gpu(h, w, sts_temp)
+    _need(h.dim() == 3 and h.stride(2) == 1, "h: [R, K, H] with unit inner stride")
+    R, K, H = h.shape
+    _need(w.dim() == 1 and w.numel() == H and w.is_contiguous(), "w: contiguous [H]")
+    _need(sts_temp is None or (sts_temp.dtype == torch.float32 and sts_temp.numel() == K
+                               and sts_temp.is_contiguous()), "sts_temp: float32 [K]")
+    dev = h.device
+    o = out or {}
+    conf = _take(o, "conf", lambda: torch.empty(R, K, dtype=torch.float32, device=dev))
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    args = (_ptr(h), _dtype_code(h), h.stride(0), h.stride(1), _ptr(w), _dtype_code(w), float(bias),
+            _ptr(sts_temp), R, K, H, _ptr(conf), _ptr(status), _stream(stream))
+    return _finish(lib().dsp_confidence_head, args, dict(conf=conf, status=status), prepare, (h, w, sts_temp))
 
 
 def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, threshold=0.0, want_survival=True,

@@ -81,6 +81,24 @@ int32_t dsp_philox_uniforms(const uint64_t* ctr, int64_t n, uint64_t seed, doubl
                             void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Confidence head with sequential temperature scaling  ([N] 5.1; [S] STS)   */
+/*                                                                          */
+/* conf[i*K + k] = sigmoid((w . h_{i,k} + bias) / T_k): the probability that  */
+/* draft k of request i survives verification given that drafts 1..k-1 did,  */
+/* from a linear projection of the draft's hidden state; T_k (sts_temp[k],   */
+/* device, nullable = all 1) is the position's calibration temperature. The  */
+/* output is the scheduler's conf input.                                     */
+/*   h: [R, K, H] hidden states, element (i, k, j) at h + i*ld_h_r +         */
+/*      k*ld_h_k + j; h_dtype / w_dtype DSP_F32 or DSP_BF16; w: [H].         */
+/*   Dot products in fp32 per 8 elements, summed in fp64; logit, temperature */
+/*   and sigmoid in fp64, output fp32. A NaN result sets                     */
+/*   DSP_STATUS_NONFINITE. No workspace.                                     */
+/* ------------------------------------------------------------------------ */
+int32_t dsp_confidence_head(const void* h, int32_t h_dtype, int64_t ld_h_r, int64_t ld_h_k, const void* w,
+                            int32_t w_dtype, float bias, const float* sts_temp, int32_t R, int32_t K,
+                            int32_t H, float* conf, int32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Survival products and window selection  ([N] 5.1-5.2, [S] "SPS cost table") */
 /*                                                                          */
 /* conf [R, K] float32 row-major: c_{i,k}, the probability that draft k of    */
@@ -318,7 +336,8 @@ int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t l
 #define DSP_K_TREE_MERGE       9
 #define DSP_K_TREE_FINAL      10
 #define DSP_K_SCHEDULE_RANK   11  /* scheduler: ranking of the candidate keys */
-#define DSP_K_COUNT           12
+#define DSP_K_CONFIDENCE      12  /* confidence head */
+#define DSP_K_COUNT           13
 int32_t dsp_prof_enable(int32_t mask);
 int32_t dsp_prof_reset(void);
 int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);

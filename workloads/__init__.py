@@ -37,6 +37,11 @@ Recipes (N(m, s) = normal with mean m and standard deviation s):
   order for given windows (standing in for the target forward over the packed
   buffer); cost c(n) = 1.0 + 0.05 n.
 
+* confidence head (the cycle builds its hidden states so that the head reproduces
+  the cycle's confidences; see cycle_head_inputs): hidden states h [R, K, H] ~ N(0, 1) bf16, weights w [H] ~
+  N(0, 1) / sqrt(H) bf16 (logits of unit scale), bias 1.5, sequential
+  temperatures T_k = 1 + 0.05 k.
+
 Draft tokens x_{i,k} are the synthetic draft model's samples from softmax(d/T)
 (Gumbel-max with this module's own noise), or argmax d when T = 0.
 """
@@ -201,12 +206,34 @@ def cycle_case(R, K, V, rank, seed):
     rng = _rng(seed + 7)
     sig = rng.uniform(0.2, 2.0, size=R).astype(np.float32)
     eta = rng.standard_normal((R, K))
-    c["conf"] = (1.0 / (1.0 + np.exp(-(4.0 - 2.5 * sig[:, None] + 0.25 * eta)))).astype(np.float32)
+    logit = 4.0 - 2.5 * sig[:, None] + 0.25 * eta
+    c["conf"] = (1.0 / (1.0 + np.exp(-logit))).astype(np.float32)
     c["cost"] = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
     c["sigma"] = sig
     c["K"] = K
     c["target_seed"] = seed + 11
+    c["logit"] = logit
     return c
+
+
+def cycle_head_inputs(c, H=4096):
+    """Hidden states and head weights for the cycle whose confidence head reproduces the
+    cycle's confidences: h_{i,k} carries (T_k * logit_{i,k} - bias) / |w|^2 along w plus
+    Gaussian noise orthogonal to w, so sigmoid((w . h + bias) / T_k) ~ conf_{i,k} (up to the
+    bf16 rounding of h)."""
+    rng = _rng(c["target_seed"] + 1)
+    R, K = c["R"], c["K"]
+    w = f32_to_bf16_bits(rng.standard_normal(H, dtype=np.float32) / np.float32(np.sqrt(H)))
+    w64 = bf16_bits_to_f32(w).astype(np.float64)
+    temps = (1.0 + 0.05 * np.arange(K)).astype(np.float32)
+    bias = 1.5
+    along = (temps[None, :].astype(np.float64) * c["logit"] - bias) / float(w64 @ w64)
+    h = np.empty((R, K, H), dtype=np.uint16)
+    for i in range(R):
+        e = rng.standard_normal((K, H))
+        e -= np.outer(e @ w64, w64) / float(w64 @ w64)
+        h[i] = f32_to_bf16_bits((along[i][:, None] * w64[None, :] + e).astype(np.float32))
+    return dict(h=h, w=w, bias=bias, temps=temps, H=H)
 
 
 def cycle_target(c, windows):
@@ -226,3 +253,12 @@ def cycle_target(c, windows):
             else:
                 rows.append(f32_to_bf16_bits(np.float32(3.0) * eps))
     return np.stack(rows)
+
+
+def confidence_case(R, K, H, seed):
+    """Inputs of the confidence head (see the module docstring)."""
+    rng = _rng(seed)
+    h = f32_to_bf16_bits(rng.standard_normal((R, K, H), dtype=np.float32))
+    w = f32_to_bf16_bits(rng.standard_normal(H, dtype=np.float32) / np.float32(np.sqrt(H)))
+    temps = (1.0 + 0.05 * np.arange(K)).astype(np.float32)
+    return dict(h=h, w=w, bias=1.5, temps=temps, R=R, K=K, H=H)
