@@ -45,7 +45,7 @@ constexpr int kTR = 32 * kWaves;  // parent rows per workgroup: one 32-row MFMA 
 constexpr int kTS = 32;           // vocabulary entries per pipeline stage (one 32-row MFMA block)
 constexpr int kTopK = 4;          // children tracked per parent
 constexpr int kTargetWGs = 256;   // one workgroup per CU
-constexpr int kZS = 80;           // bytes per row of a wave's staging tile of emitted logits (64 + pad)
+constexpr int kZS = 144;          // bytes per row of a wave's staging tile of emitted logits (128 + pad)
 
 enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2, MODE_SAMPLE = 3 };
 
@@ -395,32 +395,42 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         hb[q] = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
         z[q] = __uint_as_float(hb[q] << 16);
       }
-      // through this wave's private LDS tile (32 rows x 32 tokens, rows kZS bytes
-      // apart): lanes write their runs of four, then read back 16 bytes of one row each,
-      // so every global store writes 16 rows x 64 contiguous bytes
+      // through this wave's private LDS tile of a stage pair (32 rows x 64 tokens,
+      // rows kZS bytes apart; the pair starts at an even global stage, so its 128
+      // bytes per row are one aligned line): lanes write their runs of four into the
+      // stage's half, and once the pair is complete (or the slice ends) read back 16
+      // bytes each, so every global store writes 8 rows x 128 contiguous bytes. Halves
+      // outside this slice (the first stage of a slice can be a pair's second half,
+      // the last its first half) are not stored.
       char* zt = (char*)(lds + 2 * (WST + LST)) + wave * (32 * kZS);
+      const int half = (s_begin + s) & 1;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         uint2 w;
         w.x = hb[4 * h] | (hb[4 * h + 1] << 16);
         w.y = hb[4 * h + 2] | (hb[4 * h + 3] << 16);
-        *(uint2*)(zt + (lane & 31) * kZS + 16 * h + 8 * (lane >> 5)) = w;
+        *(uint2*)(zt + (lane & 31) * kZS + 64 * half + 16 * h + 8 * (lane >> 5)) = w;
       }
+      if (half == 1 || s == nst - 1) {  // uniform over the workgroup
+        const bool lo_ok = half == 0 || s >= 1;  // the pair's first stage belongs to this slice
+        const bool hi_ok = half == 1;
+        const int vp = v0 - 32 * half;            // the pair's first token
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int rl = (lane >> 2) + 16 * j, ch = lane & 3;
-        const uint4 w = *(const uint4*)(zt + rl * kZS + 16 * ch);
-        const int grow = r0 + wave * 32 + rl;
-        const int v = v0 + 8 * ch;
-        if (grow < a.rows) {
-          uint16_t* zp = a.zout + (size_t)grow * a.ldz_r + (size_t)a.d * a.ldz_d + v;
-          if (v + 8 <= a.V) {
-            *(uint4*)zp = w;
-          } else {
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        for (int j = 0; j < 4; ++j) {
+          const int rl = (lane >> 3) + 8 * j, ch = lane & 7;
+          const uint4 w = *(const uint4*)(zt + rl * kZS + 16 * ch);
+          const int grow = r0 + wave * 32 + rl;
+          const int v = vp + 8 * ch;
+          if (grow < a.rows && ((ch < 4) ? lo_ok : hi_ok)) {
+            uint16_t* zp = a.zout + (size_t)grow * a.ldz_r + (size_t)a.d * a.ldz_d + v;
+            if (v + 8 <= a.V) {
+              *(uint4*)zp = w;
+            } else {
+              const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (v + e < a.V) zp[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+              for (int e = 0; e < 8; ++e)
+                if (v + e < a.V) zp[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
