@@ -26,6 +26,10 @@
 //      u' * total, rescans it with contiguous per-thread ranges and an fp64
 //      exclusive scan, and writes the smallest token whose running sum exceeds
 //      the target (the last positive entry if rounding leaves none).
+// When the requests alone fill the chip (R >= 3/4 of the CUs), launches 2-4 are one
+// launch instead: a 1024-thread workgroup per request decides with its first
+// wavefront, streams the job's row(s) once into per-chunk masses in LDS and draws
+// (one CU per request is then no loss, and no hand-off between launches is needed).
 // No workgroup waits on another inside a kernel: on this chip the L2 is per
 // XCD, and publishing data between workgroups would need an L2 write-back per
 // hand-off, so every dependency is a kernel boundary instead.

@@ -102,3 +102,55 @@ def test_cycle_repeats_draw_fresh_uniforms():
         bad = np.argwhere(o["y"] != y)
         assert all(o["sample_margin"][i, d] < max(SAMPLE_BAND, o["tie_shift"][i, d]) for i, d in bad)
     assert not np.array_equal(ys[0], ys[1])
+
+
+def test_cycle_bench_shape_sampled_requests():
+    """The cycle at the bench's shape (256 requests x 16 sampled drafts, V=151,936, rank 256):
+    windows and pack checked exactly for every request; draws (all 16 steps, replayed) and the
+    verify decisions and drawn tokens checked against the oracle on sampled requests."""
+    c = workloads.cycle_case(256, 16, workloads.V_QWEN3, 256, seed=1006)
+    R, K, V, T, seed = c["R"], c["K"], c["V"], 1.0, 0
+    L, U, W = (workloads.bf16_bits_to_f32(c[k]) for k in ("L", "U", "W"))
+    windows_host = osch.schedule_windows(c["conf"], c["cost"])["windows"]
+    tp = workloads.cycle_target(c, windows_host)
+    print(f"cycle (bench shape) packed rows={tp.shape[0]} drafts={int(windows_host.sum())}", flush=True)
+    Lg, Ug = to_gpu_bf16(c["L"]), to_gpu_bf16(c["U"])
+    Wtg = to_gpu_bf16(np.ascontiguousarray(c["W"].T))
+    ag = to_gpu(c["anchors"].astype(np.int32))
+    rd = torch.zeros(1, dtype=torch.int64, device=Lg.device)
+    dr = dsp.draft_markov_sample(Lg, Ug, Wtg, ag, T, seed=seed, round_dev=rd)
+    sch = dsp.schedule_windows(to_gpu(c["conf"]), to_gpu(c["cost"]))
+    pk = dsp.pack_ragged(sch["windows"], ag, dr["y"])
+    ver = dsp.verify_rejection(to_gpu_bf16(tp), pk["cu_seqlens"], dr["y"], drf=dr["z"], temperature=T,
+                               seed=seed, round_dev=rd, row_req=pk["row_req"], row_pos=pk["row_pos"],
+                               want_probs=False)
+    torch.cuda.synchronize()
+    for st in (dr["status"], pk["status"], ver["status"]):
+        assert int(host(st)[0]) == 0
+    y = host(dr["y"]).astype(np.int64)
+    w = host(sch["windows"])
+    np.testing.assert_array_equal(w, windows_host)
+    op = opack.pack_ragged(w, c["anchors"], y)
+    np.testing.assert_array_equal(host(pk["cu_seqlens"]), op["cu_seqlens"])
+    T_rows = int(op["cu_seqlens"][-1])
+    np.testing.assert_array_equal(host(pk["tokens"])[:T_rows], op["tokens"])
+    sel = np.array([0, 5, 77, 128, 200, 255])
+    od = om.chain_sampled(L[sel], U, W, c["anchors"][sel], T, seed=seed, rnd=0, req_id=sel, forced=y[sel])
+    ties = TieCounter()
+    ties.decisions += y[sel].size
+    for ii, d in np.argwhere(od["y"] != y[sel]):
+        assert od["sample_margin"][ii, d] < max(SAMPLE_BAND, od["tie_shift"][ii, d]), (sel[ii], d)
+        ties.near += 1
+    # verify of the sampled requests: their packed rows and their own draft rows as q
+    cu = op["cu_seqlens"]
+    rows = np.concatenate([tp[cu[i]:cu[i + 1]] for i in sel])
+    cu_s = np.concatenate([[0], np.cumsum([cu[i + 1] - cu[i] for i in sel])]).astype(np.int32)
+    tv = workloads.bf16_bits_to_f32(rows).astype(np.float64)
+
+    def orc(forced):
+        return ov.verify_chain(tv, cu_s, od["zhat"], y[sel], T, seed=seed, rnd=1, req_id=sel, forced_len=forced)
+    sub = {k: ver[k][torch.as_tensor(sel, device=ver[k].device)] for k in ("accepted_len", "out_tokens")}
+    shift = od["tie_shift"]
+    compare_chain_verify(sub, orc, len(sel), K, w[sel], ties, accept_band=4.0 * shift,
+                         sample_band=4.0 * shift.max(axis=1))
+    ties.check()
