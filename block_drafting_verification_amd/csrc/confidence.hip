@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * kConfRows) void confidence_kernel(ConfArgs a) 
   double acc = 0.0;
   int g = lane;
   if (al) {
-    constexpr int B = 4;  // groups per lane in flight
+    constexpr int B = 8;  // groups per lane in flight (a whole 4096-wide bf16 row per wavefront)
     for (; g + 64 * (B - 1) < ng; g += 64 * B) {
       u32x4 hv[B][Vec8<TH>::kVecs], wv[B][Vec8<TW>::kVecs];
 #pragma unroll
