@@ -215,9 +215,33 @@ def bench_verify(args, which):
         timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps,
                     value_from="graph" if graph <= eager else "eager"),
     )
+    res["roofline"]["read_ref"] = read_reference(tgt, drf)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_oracle_verify(c, win, args.cpu_seconds)
     return res
+
+
+def read_reference(*tensors, reps=10):
+    """Achievable read rate on this machine over the same buffers, outside the timed step: the
+    library's streaming-read probe (plain 16-byte loads) over each; a second denominator beside
+    the HBM peak."""
+    import torch
+    import block_drafting_verification_amd as dsp
+    nbytes = sum(t.numel() * t.element_size() for t in tensors)
+    sink = torch.zeros(1, dtype=torch.int32, device=tensors[0].device)
+    for t in tensors:
+        dsp.stream_read(t, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for t in tensors:
+            dsp.stream_read(t, sink)
+    b.record()
+    b.synchronize()
+    sec = a.elapsed_time(b) / 1e3 / reps
+    return dict(GBps=nbytes / sec / 1e9, bytes=nbytes, frac_of_peak=nbytes / sec / 1e9 / PEAK_HBM_GBS,
+                method="streaming-read probe over the same target and draft logits")
 
 
 def bench_markov(args):

@@ -28,7 +28,7 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
 
 __all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step",
            "draft_markov_sample", "tree_expand",
-           "philox_uniforms", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
+           "philox_uniforms", "stream_read", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
            "DSP_STATUS_TOKEN_RANGE",
            "DSP_STATUS_WINDOW_RANGE", "DSP_STATUS_NONFINITE"]
@@ -369,6 +369,17 @@ def tree_expand(L, U, Wt, anchor, topk, frontier, topN, want_mask=False, out=Non
     res = dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, n_nodes=nn, anc_mask=mask,
                status=status)
     return _finish(lib().dsp_tree_expand, args, res, prepare, (L, U, Wt, anchor, ws))
+
+
+def stream_read(t, sink=None, stream=None):
+    """Read every byte of the contiguous GPU tensor t (16-byte aligned, size a multiple of 16)
+    with the library's streaming-read probe; returns the sink word tensor."""
+    _on_gpu(t)
+    _need(t.is_contiguous(), "t must be contiguous")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=t.device)
+    _abi.check(lib().dsp_stream_read(_ptr(t), t.numel() * t.element_size(), _ptr(sink), _stream(stream)))
+    return sink
 
 
 def prof_enable(on=True, kernels=None):

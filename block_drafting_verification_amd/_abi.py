@@ -47,6 +47,7 @@ SIGNATURES = {
     "dsp_tree_expand_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "dsp_tree_expand": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _p, _i32, _i32, _i32,
                                _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "dsp_stream_read": (_i32, [_p, _sz, _p, _p]),
     "dsp_prof_enable": (_i32, [_i32]),
     "dsp_prof_reset": (_i32, []),
     "dsp_prof_query": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),

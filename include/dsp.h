@@ -314,6 +314,17 @@ int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t l
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Read probe (measurement).                                                 */
+/*                                                                          */
+/* Streams `bytes` (a multiple of 16) from the 16-byte aligned device buffer */
+/* p with plain 16-byte loads, eight in flight per thread (*sink, device, is */
+/* written only for one data-dependent value, so the loads stay live): the  */
+/* achievable read rate of the same buffers the streaming kernels read, a    */
+/* second denominator beside the HBM peak.                                   */
+/* ------------------------------------------------------------------------ */
+int32_t dsp_stream_read(const void* p, size_t bytes, uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (observability).                                            */
 /*                                                                          */
 /* dsp_prof_enable(mask): bit k set = time each launch of kernel k below     */
