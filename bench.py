@@ -200,14 +200,15 @@ def bench_verify(args, which):
     res = dict(
         metric="verified draft tokens/sec", value=N * args.steps / elapsed, unit="tokens/s",
         n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps,
-        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
         data="synthetic (seeded N(0,3) logits with 1% +8 boosts; draft = target + Gaussian noise)",
         config=dict(workload=("dense-vocab verify: 64 requests, K=7, V=151936, bf16, full-block windows, T=1"
                               if which == "dense-verify" else
                               "confidence-scheduled ragged verify: 256 requests, K=16, V=151936, bf16, "
                               "additive cost 1+0.05n, compact windows, T=1"),
-                    requests=R, block=K, vocab=V, verified_drafts_per_step=N, packed_rows=T_rows,
-                    mean_accepted=float(acc.mean())),
+                    requests=R, block=K, vocab=V, logits_dtype="bf16",
+                    arithmetic="fp32 per element (exp2), fp64 sums and decisions",
+                    verified_drafts_per_step=N, packed_rows=T_rows, mean_accepted=float(acc.mean())),
         roofline=dict(kernel="verify_stats", bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=achieved / PEAK_HBM_GBS, traffic=traffic, algorithmic_bytes=bytes_stats,
                       avg_us=st),

@@ -43,14 +43,8 @@
 namespace dsp {
 namespace {
 
-#ifndef DSP_STATS_VPT
-#define DSP_STATS_VPT 8
-#endif
-#ifndef DSP_STATS_WG_PER_CU
-#define DSP_STATS_WG_PER_CU 0  // persistent grid: workgroups per CU (0: one item per workgroup)
-#endif
 constexpr int kThreads = 256;
-constexpr int kVpt = DSP_STATS_VPT;          // 16-byte vectors per thread per chunk
+constexpr int kVpt = 8;                      // 16-byte vectors per thread per chunk (4 and 12-16 measured slower)
 constexpr int kChunkVecs = kThreads * kVpt;  // vectors per chunk (2048 = 32 KiB of bf16)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -1177,8 +1171,10 @@ VerifyLayout verify_layout(int R, int K, int V, int max_rows, int t_dtype, int d
   return L;
 }
 
+// One item per workgroup (a persistent grid looping over items measured slower: the
+// hardware's workgroup dispatch overlaps items better), capped for very large batches.
 long stats_grid(long max_items) {
-  const long cap = DSP_STATS_WG_PER_CU > 0 ? (long)num_cus() * DSP_STATS_WG_PER_CU : 1l << 20;
+  const long cap = 1l << 20;
   long g = max_items < cap ? max_items : cap;
   return g < 1 ? 1 : g;
 }
