@@ -107,17 +107,20 @@ def round_bf16(z):
     Returns (values as fp64, distance of each input to the nearest rounding
     midpoint, one bf16 unit in the last place at each input). bfloat16 keeps 8
     significant bits: with z = m * 2^e, 0.5 <= |m| < 1, the kept significand is
-    m * 2^8 rounded to an integer.
+    m * 2^8 rounded to an integer. A masked logit (-inf) rounds to itself, with
+    no midpoint near it (gap +inf) and unit 0.
     """
     z = np.asarray(z, dtype=np.float64)
-    assert np.all(np.isfinite(z))
-    m, e = np.frexp(z)
+    masked = np.isneginf(z)
+    assert np.all(np.isfinite(z) | masked)
+    zf = np.where(masked, 0.0, z)
+    m, e = np.frexp(zf)
     s = m * 256.0
     r = np.rint(s)  # nearest integer, ties to even
-    out = np.ldexp(r / 256.0, e)
+    out = np.where(masked, -np.inf, np.ldexp(r / 256.0, e))
     a = np.abs(s)
-    mid_gap = np.ldexp(np.abs((a - np.floor(a)) - 0.5) / 256.0, e)
-    ulp = np.ldexp(np.full_like(z, 1.0 / 256.0), e)
+    mid_gap = np.where(masked, np.inf, np.ldexp(np.abs((a - np.floor(a)) - 0.5) / 256.0, e))
+    ulp = np.where(masked, 0.0, np.ldexp(np.full_like(zf, 1.0 / 256.0), e))
     return out, mid_gap, ulp
 
 

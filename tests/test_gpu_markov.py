@@ -262,3 +262,21 @@ def test_chain_sampled_c4_shape():
     6 requests checked against the oracle through all 16 steps."""
     c = workloads.markov_chain()
     _check_sampled(c, 1.0, seed=0, rnd=0, requests=[0, 1, 77, 128, 200, 255])
+
+
+def test_chain_and_tree_masked_vocabulary():
+    """-inf base logits (a masked vocabulary): never chosen by the chain, the sampled chain or
+    the tree, and no mass in the log-sum-exp."""
+    c = workloads.markov_case(5, 3, 3001, rank=64, seed=33)
+    rng = np.random.default_rng(5)
+    mask = rng.random(3001) < 0.2
+    L = c["L"].copy()
+    L[..., mask] = 0xFF80
+    c = dict(c, L=L)
+    y = _check_chain(c, want_logq=True)
+    assert not np.any(mask[y])
+    g, ys = _check_sampled(c, 1.0, seed=2, rnd=0)
+    assert not np.any(mask[ys])
+    t = _check_tree(c, 4, 8, 16)
+    nt = host(t["node_token"])
+    assert not np.any(mask[nt[nt >= 0]])

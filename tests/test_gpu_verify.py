@@ -317,3 +317,27 @@ def test_scheduled_ragged_verify_full():
     ties = TieCounter()
     compare_chain_verify(g, orc, R, K, w, ties)
     ties.check()
+
+
+def test_masked_vocabulary_entries():
+    """Rows with -inf entries (a masked or padded vocabulary, same mask for target and draft):
+    the masked tokens carry no probability mass on either side and are never drawn."""
+    R, K, V = 6, 5, 5003
+    case = workloads.verify_case(R, K, V, dtype="bf16", seed=91, t_sigma=2.0, d_sigma=0.4)
+    rng = np.random.default_rng(4)
+    mask = rng.random(V) < 0.15
+    mask[-3:] = True  # a padded tail
+    t, d = case["t"].copy(), case["d"].copy()
+    t[..., mask] = 0xFF80  # bf16 -inf
+    d[..., mask] = 0xFF80
+    d32 = workloads.bf16_bits_to_f32(d)
+    x = np.argmax(d32, axis=-1).astype(np.int32)  # a most likely (unmasked) draft token
+    case = dict(case, t=t, d=d, x=x)
+    windows = np.array([5, 0, 3, 5, 1, 4])
+    ties = TieCounter()
+    for T in (1.0, 0.7):
+        g, orc = _run_case(case, windows, T, seed=13, rnd=1, row_maps=True)
+        compare_chain_verify(g, orc, R, K, windows, ties)
+        toks = host(g["out_tokens"])
+        assert not np.any(mask[toks[toks >= 0]]), "a masked token was drawn"
+    ties.check()

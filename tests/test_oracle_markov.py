@@ -167,3 +167,31 @@ def test_sampled_replay_is_step_local():
     s = z3 / 1.0
     lse = s.max(-1) + np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1))
     np.testing.assert_allclose(rep["logq_forced"][:, 2], s[np.arange(4), forced[:, 2]] - lse, rtol=1e-12)
+
+
+def test_masked_logits_carry_no_mass():
+    """A masked vocabulary entry (-inf base logit) rounds to -inf and is never drawn; with V = 3
+    and token 2 masked the two remaining tokens keep the logistic law (closed form)."""
+    got, gap, ulp = om.round_bf16(np.array([-np.inf, 1.5]))
+    assert got[0] == -np.inf and gap[0] == np.inf and ulp[0] == 0.0 and got[1] == 1.5
+    beta, T, R = 0.8, 1.0, 400
+    L = np.zeros((R, 1, 3), dtype=np.float32)
+    L[:, 0, 1] = beta
+    L[:, 0, 2] = -np.inf
+    U = np.zeros((3, 32), dtype=np.float32)
+    W = np.zeros((32, 3), dtype=np.float32)
+    ones, N = 0, 0
+    for rnd in range(60):
+        res = om.chain_sampled(L, U, W, np.zeros(R, dtype=np.int64), T, seed=12, rnd=rnd)
+        assert not np.any(res["y"] == 2)
+        assert np.all(res["round_tie"][..., 2] == False)  # noqa: E712
+        ones += int(res["y"].sum())
+        N += R
+    a = 1.0 / (1.0 + math.exp(-beta / T))
+    assert abs(ones / N - a) < 5 * math.sqrt(a * (1 - a) / N), (ones / N, a)
+    # greedy chain: the masked token is never the argmax even when the rank term favours it
+    Wg = np.zeros((32, 3), dtype=np.float32)
+    Ug = np.ones((3, 32), dtype=np.float32)
+    Wg[:, 2] = 10.0
+    g = om.chain(L, Ug, Wg, np.zeros(R, dtype=np.int64))
+    assert not np.any(g["y"] == 2)
