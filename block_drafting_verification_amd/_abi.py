@@ -16,7 +16,8 @@ DSP_SCHED_TOP_M = 2
 DSP_SCHED_THRESHOLD = 3
 
 KERNELS = ["VERIFY_STATS", "VERIFY_DECIDE", "VERIFY_RESIDUAL", "VERIFY_SAMPLE", "SCHEDULE", "PACK",
-           "MARKOV_GEMM", "MARKOV_MERGE", "TREE_GEMM", "TREE_MERGE", "TREE_FINAL", "SCHEDULE_RANK", "CONFIDENCE"]
+           "MARKOV_GEMM", "MARKOV_MERGE", "TREE_GEMM", "TREE_MERGE", "TREE_FINAL", "SCHEDULE_RANK", "CONFIDENCE",
+           "TREE_PROBE"]
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32

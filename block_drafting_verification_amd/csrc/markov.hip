@@ -134,6 +134,9 @@ struct GemmArgs {
   uint16_t* zout;
   int64_t ldz_r, ldz_d;
   float cz;
+  // tree: per parent row, a value t with every entry of the row's top 4 strictly above
+  // it (or NULL: no bound); entries at or below t are not offered to the top-4 list
+  const float* theta;
 };
 
 // 16-byte slot of (row, vector) in a swizzled LDS tile whose rows hold `nv` vectors
@@ -344,6 +347,10 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   }
   float lref = -INFINITY;
   double lsum = 0.0;
+  // tree: an entry enters the top-4 list only above thr = max(4th kept value, row bound)
+  float th_row = -INFINITY;
+  if (MODE == MODE_TREE && a.theta && rvalid) th_row = a.theta[row];
+  float thr = th_row;
 
   u32x4 ringw[NR][WQ] = {}, ringl[NR][LQ] = {};
   uint32_t ringu[NR][LAL ? 1 : LQ][8] = {};
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       }
     }
   };
-  // epilogue of one stage for the log-sum-exp, tree and sampled modes (z = acc)
+  // epilogue of one stage for the log-sum-exp and sampled modes (z = acc)
   const float cz = MODE == MODE_SAMPLE ? a.cz : kLog2e;
   auto epilogue = [&](int s, const f32x16& zacc) {
     const int v0 = (s_begin + s) * kTS;
@@ -440,19 +447,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int v = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
       tmax = fmaxf(tmax, z[q]);
-      if (MODE == MODE_TREE) {
-        if (z[q] > tv[kTopK - 1]) {
-          tv[kTopK - 1] = z[q];
-          ti[kTopK - 1] = v;
-#pragma unroll
-          for (int p2 = kTopK - 1; p2 > 0; --p2) {
-            if (tv[p2] > tv[p2 - 1]) {
-              const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
-              const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
-            }
-          }
-        }
-      } else if (MODE == MODE_ARGMAX_LSE && z[q] > best) {
+      if (MODE == MODE_ARGMAX_LSE && z[q] > best) {
         best = z[q];
         bidx = v;
       }
@@ -468,9 +463,49 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     }
   };
 
+  // Tree: the stage maximum tm and ts = sum of exp2(z log2e - lref) are accumulated one
+  // value per MFMA of the next stage, against the reference of the stages before; the
+  // reference is raised only when the stage could exceed it by more than 2^64 (each term
+  // stays finite in fp32), which recomputes the stage's sum (always on a lane's first
+  // non-empty stage). Then the top-4 insertion, skipped unless the stage has an entry
+  // above the threshold.
+  auto tree_stage_end = [&](int s, const f32x16& z, float tm, float ts) {
+    const int v0 = (s_begin + s) * kTS;
+    // the fast path's sum is selected, not branched on, so that the exponentials stay
+    // between the MFMAs (a branch lets the compiler sink them past the whole stage)
+    const bool fast = lref != -INFINITY && tm * kLog2e <= lref + 64.f;
+    lsum += fast ? (double)ts : 0.0;
+    if (!fast && tm != -INFINITY) {
+      const float nref = fmaxf(lref, tm * kLog2e);
+      float t2 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) t2 += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));
+      const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
+      lsum = lsum * scale + (double)t2;
+      lref = nref;
+    }
+    if (tm > thr) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (z[q] > thr) {
+          tv[kTopK - 1] = z[q];
+          ti[kTopK - 1] = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+#pragma unroll
+          for (int p2 = kTopK - 1; p2 > 0; --p2) {
+            if (tv[p2] > tv[p2 - 1]) {
+              const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
+              const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
+            }
+          }
+          thr = fmaxf(tv[kTopK - 1], th_row);
+        }
+      }
+    }
+  };
+
   // Stages are software-pipelined inside each wave: the MFMAs of stage s are issued
-  // first, then the epilogue of stage s-1 runs on the other accumulator (for the chain,
-  // one value per MFMA, in program order between them).
+  // first, then the epilogue of stage s-1 runs on the other accumulator (for the chain
+  // and the tree, one value per MFMA, in program order between them).
   f32x16 acc[2];
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[1][q] = -INFINITY;  // "stage -1": updates nothing
@@ -490,6 +525,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       const u32x4* Ws = lds + b * (WST + LST);
       init_from_l(s, Ws + WST, acc[b]);
       const int code0 = 16 * (s - 1);
+      float tm = -INFINITY, ts = 0.f;  // tree: stage s-1 (discarded for s = 0)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int m = lane & 31, kv = 2 * ks + (lane >> 5);
@@ -499,8 +535,21 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
           best = acc[b ^ 1][ks];
           bcode = code0 + ks;
         }
+        if (MODE == MODE_TREE && ks < 16) {
+          tm = fmaxf(tm, acc[b ^ 1][ks]);
+          ts += fast_exp2(__builtin_fmaf(acc[b ^ 1][ks], kLog2e, -lref));
+        }
       }
-      if (MODE == MODE_ARGMAX) {
+      if (MODE == MODE_TREE) {
+#pragma unroll
+        for (int q = KS; q < 16; ++q) {  // ranks below 256: the remaining values
+          tm = fmaxf(tm, acc[b ^ 1][q]);
+          ts += fast_exp2(__builtin_fmaf(acc[b ^ 1][q], kLog2e, -lref));
+        }
+        // s = 0: the stage before is the -inf sentinel, which changes nothing (its sum is
+        // not selected, its maximum is -inf)
+        tree_stage_end(s - 1, acc[b ^ 1], tm, ts);
+      } else if (MODE == MODE_ARGMAX) {
 #pragma unroll
         for (int q = KS; q < 16; ++q)  // ranks below 256: the remaining values
           if (acc[b ^ 1][q] > best) {
@@ -527,6 +576,14 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
           best = last[q];
           bcode = code0 + q;
         }
+    } else if (MODE == MODE_TREE) {
+      float tm = -INFINITY, ts = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        tm = fmaxf(tm, last[q]);
+        ts += fast_exp2(__builtin_fmaf(last[q], kLog2e, -lref));
+      }
+      tree_stage_end(nst - 1, last, tm, ts);
     } else {
       epilogue(nst - 1, last);
     }
@@ -801,7 +858,80 @@ struct TreeMergeArgs {
   const uint16_t* U;
   const uint16_t* Wt;
   int32_t* status;
+  // row bounds of the next depth (NULL: none): probe tokens [R][D][4] of the L rows,
+  // bounds written to theta[R * fn]
+  const int32_t* probe;
+  float* theta;
+  int32_t D;
 };
+
+// Four probe tokens per (request, L row): probe j is the arg-max of the row over the
+// 256-token blocks b with b % 4 == j (lowest id on ties), or -1 if none is finite.
+// Four distinct tokens, so the smallest of any row's values at them is a lower bound
+// on that row's 4th-largest value. One workgroup per (request, row, j).
+struct ProbeArgs {
+  const uint16_t* L;
+  int64_t ldL_r, ldL_d;
+  int32_t V, D, d0;   // rows d0 .. D-1
+  int32_t* probe;     // [R][D][4]
+};
+__global__ __launch_bounds__(256) void tree_probe_kernel(ProbeArgs a) {
+  __shared__ float s_v[4];
+  __shared__ int32_t s_i[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = blockIdx.x & 3;
+  const int nrow = a.D - a.d0;
+  const int i = (blockIdx.x >> 2) / nrow, d = a.d0 + (blockIdx.x >> 2) % nrow;
+  const uint16_t* row = a.L + (size_t)i * a.ldL_r + (size_t)d * a.ldL_d;
+  const bool al = ((uintptr_t)row & 15) == 0;
+  const int nb = (a.V + 255) / 256;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  // 32 threads per block (8 tokens each), 8 blocks per pass; a thread's tokens increase
+  for (int b = j + 4 * (tid >> 5); b < nb; b += 32) {
+    const int v0 = b * 256 + 8 * (tid & 31);
+    float x[8];
+    if (al && v0 + 8 <= a.V) {
+      const u32x4 w = *(const u32x4*)(row + v0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_lo(w[e]);
+        x[2 * e + 1] = bf16_hi(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = v0 + e < a.V ? bf16_val(row[v0 + e]) : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (x[e] > best) {
+        best = x[e];
+        bi = v0 + e;
+      }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (better(ov, oi, best, bi)) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    s_v[wave] = best;
+    s_i[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(s_v[w], s_i[w], best, bi)) {
+        best = s_v[w];
+        bi = s_i[w];
+      }
+    a.probe[((size_t)i * a.D + d) * 4 + j] = best == -INFINITY ? -1 : bi;
+  }
+}
 
 // One workgroup per request: merge the column-group partials of its parents (16
 // lanes per parent), score every candidate child in fp64 (4 lanes per candidate,
@@ -812,6 +942,7 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
   __shared__ int32_t c_tok[256];
   __shared__ double p_lse[64];
   __shared__ int32_t p_top[64][kTopK];
+  __shared__ int32_t s_ntok[64];
   const int i = blockIdx.x, tid = threadIdx.x;
   const int nc = a.fp * a.topk;
   // parents: 16 lanes each (aligned groups inside a wavefront), 16 parents per pass
@@ -907,6 +1038,7 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
     }
     if (rank < a.fn) {
       const int p = tid / a.topk;
+      s_ntok[rank] = c_tok[tid];
       a.ntok[i * a.fn + rank] = c_tok[tid];
       a.nscore[i * a.fn + rank] = s;
       Kept k;
@@ -914,6 +1046,51 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
       k.parent = a.d == 1 ? -1 : (a.d - 2) * a.F + p;
       k.score = s;
       a.kept[(size_t)i * a.kept_stride + (size_t)(a.d - 1) * a.F + rank] = k;
+    }
+  }
+  if (!a.theta) return;
+  __syncthreads();
+  // Row bounds for the next depth (L row a.d): for new parent r and probe j, z = L + U[tok]
+  // . W exactly (fp64, 4 lanes per pair), less 2^-12 (|L| + sum |u w|), which exceeds
+  // the error of any fp32 evaluation of the 257-term sum; the bound of r is the smallest
+  // over its four probes, rounded down to fp32 and stepped below (entries >= it pass).
+  const int32_t* pr = a.probe + ((size_t)i * a.D + a.d) * 4;
+  for (int pb = 0; pb < a.fn * 4; pb += 64) {
+    const int pj = pb + (tid >> 2), qr = tid & 3;
+    const bool ok = pj < a.fn * 4;
+    const int r = ok ? pj >> 2 : 0;
+    const int v = ok ? pr[pj & 3] : -1;
+    double m = 0.0, am = 0.0;
+    if (v >= 0) {
+      const int qn = a.rank / 4;
+      const u32x4* ur = (const u32x4*)(a.U + (size_t)s_ntok[r] * a.rank + qr * qn);
+      const u32x4* wr = (const u32x4*)(a.Wt + (size_t)v * a.rank + qr * qn);
+      for (int t = 0; t < qn / 8; ++t) {
+        const u32x4 uu = ur[t], ww = wr[t];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const double p0 = (double)bf16_lo(uu[h]) * (double)bf16_lo(ww[h]);
+          const double p1 = (double)bf16_hi(uu[h]) * (double)bf16_hi(ww[h]);
+          m += p0 + p1;
+          am += fabs(p0) + fabs(p1);
+        }
+      }
+    }
+    m += __shfl_xor(m, 1, 64);
+    m += __shfl_xor(m, 2, 64);
+    am += __shfl_xor(am, 1, 64);
+    am += __shfl_xor(am, 2, 64);
+    double bound = -INFINITY;
+    if (v >= 0) {
+      const double l = (double)bf16_val(a.L[(size_t)i * a.ldL_r + (size_t)a.d * a.ldL_d + v]);
+      bound = l + m - 0x1p-12 * (fabs(l) + am);
+    }
+    bound = fmin(bound, __shfl_xor(bound, 4, 64));
+    bound = fmin(bound, __shfl_xor(bound, 8, 64));
+    if (ok && (tid & 15) == 0) {
+      float t = (float)bound;
+      if ((double)t > bound) t = nextafterf(t, -INFINITY);
+      a.theta[i * a.fn + r] = nextafterf(t, -INFINITY);
     }
   }
 }
@@ -1102,7 +1279,7 @@ void frontier_sizes(int D, int topk, int F, int* f) {
 }
 
 struct TreeLayout {
-  size_t off_part, off_tok0, off_tok1, off_sc0, off_sc1, off_kept, total;
+  size_t off_part, off_tok0, off_tok1, off_sc0, off_sc1, off_kept, off_probe, off_theta, total;
   int kept_stride;
 };
 TreeLayout tree_layout(int R, int D, int V, int rank, int topk, int F) {
@@ -1126,6 +1303,8 @@ TreeLayout tree_layout(int R, int D, int V, int rank, int topk, int F) {
   t.off_sc1 = off; off = align_up(off + (size_t)R * F * 8, 256);
   t.kept_stride = D * F;
   t.off_kept = off; off = align_up(off + (size_t)R * D * F * sizeof(Kept), 256);
+  t.off_probe = off; off = align_up(off + (size_t)R * D * 4 * sizeof(int32_t), 256);
+  t.off_theta = off; off = align_up(off + (size_t)R * F * sizeof(float), 256);
   t.total = off;
   return t;
 }
@@ -1258,8 +1437,18 @@ extern "C" int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r
   int32_t* tok[2] = {(int32_t*)(b + T.off_tok0), (int32_t*)(b + T.off_tok1)};
   double* sc[2] = {(double*)(b + T.off_sc0), (double*)(b + T.off_sc1)};
   Kept* kept = (Kept*)(b + T.off_kept);
+  int32_t* probe = (int32_t*)(b + T.off_probe);
+  float* theta = (float*)(b + T.off_theta);
   int f[1024];
   frontier_sizes(D, topk, frontier, f);
+  // probe tokens of the L rows of depths 2..D (row bounds for the top-4 selection)
+  if (D > 1) {
+    ProbeArgs pa{(const uint16_t*)L, ldL_r, ldL_d, V, D, 1, probe};
+    if ((int64_t)R * (D - 1) * 4 >= (int64_t)1 << 31) return fail(DSP_ERR_SHAPE, "R * D too large");
+    launch(DSP_K_TREE_PROBE, tree_probe_kernel, dim3((unsigned)(R * (D - 1) * 4)), dim3(256), 0, s, pa);
+    rc = hip_check(hipGetLastError(), "tree probe launch");
+    if (rc) return rc;
+  }
   int fp = 1;
   for (int d = 1; d <= D; ++d) {
     const int rows = R * fp;
@@ -1267,12 +1456,13 @@ extern "C" int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r
     const int32_t* ptok = d == 1 ? anchor : tok[d & 1];
     GemmArgs ga{(const uint16_t*)U, (const uint16_t*)Wt, V, rank, ptok, 1, (const uint16_t*)L, ldL_r,
                 ldL_d, d - 1, rows, fp, G, part, status};
+    ga.theta = d == 1 ? nullptr : theta;
     rc = launch_gemm<MODE_TREE>(DSP_K_TREE_GEMM, ga, s);
     if (rc) return rc;
     const int fn = f[d - 1];
     TreeMergeArgs ma{part, G, d, fp, fn, topk, frontier, R, V, rank, ptok, d == 1 ? nullptr : sc[d & 1],
                      tok[(d + 1) & 1], sc[(d + 1) & 1], kept, T.kept_stride, (const uint16_t*)L, ldL_r,
-                     ldL_d, (const uint16_t*)U, (const uint16_t*)Wt, status};
+                     ldL_d, (const uint16_t*)U, (const uint16_t*)Wt, status, probe, d < D ? theta : nullptr, D};
     launch(DSP_K_TREE_MERGE, tree_merge_kernel, dim3(R), dim3(256), 0, s, ma);
     rc = hip_check(hipGetLastError(), "tree merge launch");
     if (rc) return rc;

@@ -300,6 +300,9 @@ int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, i
 /* root is implicit) -- the tree-causal attention pattern of the target      */
 /* forward that verifies the tree ([P]); rows past n_nodes are zero.         */
 /* L, U, Wt layouts as dsp_draft_markov_step.                                 */
+/* The selection reads each base-logit row once more up front (R*(D-1) rows) */
+/* to bound every parent row's 4th-largest z from below; entries under the   */
+/* bound cannot be among the top 4, so the outputs do not depend on it.      */
 /* Limits: 1 <= topk <= min(4, V), 1 <= frontier <= 64, topk*frontier <= 256,  */
 /* 1 <= topN <= 1024, D*frontier <= 1024, rank as above.                      */
 /* ------------------------------------------------------------------------ */
@@ -348,7 +351,8 @@ int32_t dsp_stream_read(const void* p, size_t bytes, uint32_t* sink, void* strea
 #define DSP_K_TREE_FINAL      10
 #define DSP_K_SCHEDULE_RANK   11  /* scheduler: ranking of the candidate keys */
 #define DSP_K_CONFIDENCE      12  /* confidence head */
-#define DSP_K_COUNT           13
+#define DSP_K_TREE_PROBE      13  /* PCTree: probe tokens of the base-logit rows */
+#define DSP_K_COUNT           14
 int32_t dsp_prof_enable(int32_t mask);
 int32_t dsp_prof_reset(void);
 int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);

@@ -280,3 +280,53 @@ def test_chain_and_tree_masked_vocabulary():
     t = _check_tree(c, 4, 8, 16)
     nt = host(t["node_token"])
     assert not np.any(mask[nt[nt >= 0]])
+
+
+def _tree_exact(c, topk, F, N):
+    """Tree against the oracle with no near-tie allowance (cases whose ties the order rules
+    settle exactly)."""
+    L, U, W = _f32(c)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    print(f"tree (exact) R={c['R']} D={c['B']} V={c['V']} k={topk} F={F} N={N}", flush=True)
+    g = dsp.tree_expand(Lg, Ug, Wtg, ag, topk, F, N)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    o = opt.tree_expand(L, U, W, c["anchors"], topk, F, N)
+    for k in ("node_token", "node_parent", "node_depth", "n_nodes"):
+        np.testing.assert_array_equal(host(g[k]), o[k], err_msg=k)
+    np.testing.assert_allclose(host(g["node_score"]), o["node_score"], rtol=1e-5, atol=1e-5)
+    return g, o
+
+
+@pytest.mark.parametrize("lval", [0.0, 1.5])
+def test_tree_all_equal_rows(lval):
+    """Every z equal (constant base logits, zero Markov factors): children are the lowest ids,
+    the frontier follows (parent slot, child rank). Every candidate sits exactly on the row
+    bound's probe values, the tightest case for the selection's lower bound."""
+    c = workloads.markov_case(3, 4, 2000, rank=32, seed=41)
+    c["L"][:] = workloads.f32_to_bf16_bits(np.full(c["L"].shape, lval, dtype=np.float32))
+    c["U"][:] = 0
+    c["W"][:] = 0
+    g, o = _tree_exact(c, 4, 8, 20)
+    assert set(host(g["node_token"])[0, :4]) == {0, 1, 2, 3}
+
+
+def test_tree_planted_top4_at_probe_tokens():
+    """Each base-logit row has its four largest values at the probe tokens (one per 256-token
+    block class, 1 block apart), so the children's 4th-largest z equals the row bound's
+    smallest probe value up to the margin."""
+    c = workloads.markov_case(4, 5, 3001, rank=64, seed=42, l_sigma=1.0)
+    Lf = workloads.bf16_bits_to_f32(c["L"])
+    for t, val in ((7, 20.0), (300, 19.0), (600, 18.5), (900, 18.0)):
+        Lf[:, :, t] = val
+    c["L"] = workloads.f32_to_bf16_bits(Lf)
+    g, o = _tree_exact(c, 4, 4, 16)
+    tok, dep = host(g["node_token"]), host(g["node_depth"])
+    for i in range(c["R"]):
+        assert set(tok[i][dep[i] == 1]) == {7, 300, 600, 900}
+
+
+def test_tree_tiny_vocabulary():
+    """V = 5 (one 256-token block: three probe classes empty, no row bound)."""
+    c = workloads.markov_case(3, 3, 5, rank=32, seed=43)
+    _check_tree(c, 4, 4, 12)
