@@ -463,25 +463,34 @@ __device__ void fault_request(const DecideArgs& a, int i, int bits) {
 template <typename TT, typename TD>
 __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
   const int lane = threadIdx.x & 63;
+  // Two rounds of memory latency: first everything addressed by (i, lane) alone (the
+  // window, the draft tokens, the draft rows' statistics of every block position),
+  // then what needs the packed base or the tokens (target statistics, the two logits).
   const int base = a.cu[i];
-  const int n = a.cu[i + 1] - base - 1;
+  const int nxt = a.cu[i + 1];
   const uint64_t rid = a.req_id ? (uint64_t)a.req_id[i] : (uint64_t)i;
   const uint64_t rnd = a.round_dev ? *a.round_dev : a.round;
   const int k = lane + 1;
+  const bool blk = lane < a.K;
+  int x = 0;
+  if (blk) x = a.x[(size_t)i * a.ld_x + lane];
+  bool bad_d = false;
+  double lse_d = 0.0;  // slots past the window hold no statistics: used only for positions
+  if (blk) lse_d = merge_lse(a.dstats + ((size_t)i * a.K + lane) * a.nchd, a.nchd, &bad_d);
+  const int n = nxt - base - 1;
   const bool pos = k <= n;     // a draft position of the window
   const bool bon = lane == n;  // prepares the bonus row (n < 64)
-  int x = 0;
-  if (pos) x = a.x[(size_t)i * a.ld_x + lane];
+  if (!pos) x = 0;
   const bool tokbad = pos && (x < 0 || x >= a.V);
-  bool bad = false;
-  double lse_t = 0.0, lse_d = 0.0;
-  if (pos || bon) lse_t = merge_lse(a.tstats + (size_t)(base + lane) * a.ncht, a.ncht, &bad);
-  if (pos) lse_d = merge_lse(a.dstats + ((size_t)i * a.K + lane) * a.nchd, a.nchd, &bad);
   float tx = 0.f, dx = 0.f;
   if (pos && !tokbad) {
     tx = load_elem<TT>(a.tgt, (size_t)(base + lane) * a.ld_t + x);
     dx = load_elem<TD>(a.drf, (size_t)i * a.ld_d_r + (size_t)lane * a.ld_d_k + x);
   }
+  bool bad = pos && bad_d;
+  double lse_t = 0.0;
+  if (pos || bon) lse_t = merge_lse(a.tstats + (size_t)(base + lane) * a.ncht, a.ncht, &bad);
+  if (!pos) lse_d = 0.0;
   uint64_t c[4] = {rnd, rid, (uint64_t)k, 0ull};
   philox4x64_10(c, a.seed, 0ull);
   const double u = unit_double(c[0]);
