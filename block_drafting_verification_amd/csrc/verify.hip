@@ -333,7 +333,9 @@ __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(StatsArgs a) {
 // log2-sum-exp2 of a row from its chunk slots (fp64). Sets *bad for non-finite rows.
 __device__ __forceinline__ double merge_lse(const StatSlot* s, int nch, bool* bad) {
   // slots are read 16 at a time, all loads issued before any is used (one memory
-  // latency per batch instead of one per chunk), then merged online in fp64
+  // latency per batch instead of one per chunk), then merged online in fp64. The
+  // loads are unconditional (slots past the row repeat its last one and are masked
+  // after): a load under a branch makes the compiler wait for it on the spot.
   constexpr int B = 16;
   float H = -INFINITY;
   double S = 0.0;
@@ -344,14 +346,11 @@ __device__ __forceinline__ double merge_lse(const StatSlot* s, int nch, bool* ba
     uint32_t flag[B];
 #pragma unroll
     for (int q = 0; q < B; ++q) {
-      ref[q] = -INFINITY;
-      sum[q] = 0.0;
-      flag[q] = 0u;
-      if (c0 + q < nch) {
-        ref[q] = s[c0 + q].ref;
-        flag[q] = s[c0 + q].flag;
-        sum[q] = s[c0 + q].sum;
-      }
+      const StatSlot v = s[c0 + q < nch ? c0 + q : nch - 1];
+      const bool in = c0 + q < nch;
+      ref[q] = in ? v.ref : -INFINITY;
+      flag[q] = in ? v.flag : 0u;
+      sum[q] = in ? v.sum : 0.0;
     }
     float Hb = H;
 #pragma unroll
@@ -788,12 +787,30 @@ template <typename T> __device__ __forceinline__ void load8(const T* p, bool vec
 }
 
 
+// A bounded view of one logit row (base and extent made wave-uniform): a 16-byte
+// load at a byte offset at or past the extent returns zeros and touches no memory,
+// so loads can be issued unconditionally (no branch for the compiler to wait at).
+constexpr uint32_t kRowOOB = 0x80000000u;  // past every extent (rows are under 2 GiB)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
 // Eight consecutive logits as raw 16-byte vectors (one for bf16, two for fp32).
 template <typename T> struct Raw8 {
   u32x4 w[sizeof(T) / 2];
   __device__ __forceinline__ void load(const T* p) {
 #pragma unroll
     for (int q = 0; q < (int)(sizeof(T) / 2); ++q) w[q] = __builtin_nontemporal_load((const u32x4*)p + q);
+  }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(T) / 2); ++q)
+      w[q] = __builtin_amdgcn_raw_buffer_load_b128(r, off == kRowOOB ? kRowOOB : off + 16 * q, 0, 0);
   }
   __device__ __forceinline__ void unpack(float* x) const {
 #pragma unroll
@@ -847,6 +864,9 @@ __device__ __forceinline__ double job_chunk_sum(const JobFrame& f, const TT* tp,
   const bool t_al = (((uintptr_t)tp) & 15u) == 0;
   const bool d_al = !f.resid || (((uintptr_t)dp) & 15u) == 0;
   const int e1 = min(V, e0 + len);
+  // unconditional bounded loads (a load under a branch is waited for on the spot)
+  const __amdgpu_buffer_rsrc_t trs = row_rsrc(tp, (uint32_t)((size_t)V * sizeof(TT)));
+  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dp, f.resid ? (uint32_t)((size_t)V * sizeof(TD)) : 0u);
   double s = 0.0;
   for (int eb = e0 + threadIdx.x * 8; eb < e1; eb += kBatch * kThreads * 8) {
     Raw8<TT> rt[kBatch];
@@ -856,10 +876,8 @@ __device__ __forceinline__ double job_chunk_sum(const JobFrame& f, const TT* tp,
     for (int b = 0; b < kBatch; ++b) {
       const int e = eb + b * kThreads * 8;
       fast[b] = e + 8 <= e1 && t_al && d_al;
-      if (fast[b]) {
-        rt[b].load(tp + e);
-        if (f.resid) rd[b].load(dp + e);
-      }
+      rt[b].load_buf(trs, fast[b] ? (uint32_t)(e * sizeof(TT)) : kRowOOB);
+      rd[b].load_buf(drs, fast[b] && f.resid ? (uint32_t)(e * sizeof(TD)) : kRowOOB);
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
@@ -1080,29 +1098,35 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
   const int nblk = (a.V + kSampleGrain - 1) / kSampleGrain;
   const int bpc = a.ce / kSampleGrain;  // blocks per chunk
   double run = 0.0;
-  for (int j0 = 0; j0 < nblk; j0 += kFinBatch) {
-    Raw8<TT> rt[kFinBatch];
-    Raw8<TD> rd[kFinBatch];
-    bool fast[kFinBatch];
+  // two register buffers of FB blocks: the loads of the next batch are in
+  // flight while the current one is weighed (one workgroup per CU has no other
+  // work to cover the memory latency)
+  constexpr int FB = (sizeof(TT) == 2 && sizeof(TD) == 2) ? kFinBatch : kFinBatch / 2;  // fp32: twice the bytes
+  Raw8<TT> rt[2][FB];
+  Raw8<TD> rd[2][FB];
+  bool fast[2][FB];
+  const __amdgpu_buffer_rsrc_t trs = row_rsrc(tp, (uint32_t)((size_t)a.V * sizeof(TT)));
+  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dp, resid ? (uint32_t)((size_t)a.V * sizeof(TD)) : 0u);
+  auto issue = [&](int j0, int p) {
 #pragma unroll
-    for (int b = 0; b < kFinBatch; ++b) {
+    for (int b = 0; b < FB; ++b) {
       const int e = (j0 + b) * kSampleGrain + tid * 8;
-      fast[b] = al && e + 8 <= a.V;
-      if (fast[b]) {
-        rt[b].load(tp + e);
-        if (resid) rd[b].load(dp + e);
-      }
+      fast[p][b] = al && e + 8 <= a.V;
+      rt[p][b].load_buf(trs, fast[p][b] ? (uint32_t)(e * sizeof(TT)) : kRowOOB);
+      rd[p][b].load_buf(drs, fast[p][b] && resid ? (uint32_t)(e * sizeof(TD)) : kRowOOB);
     }
+  };
+  auto weigh = [&](int j0, int p) {
 #pragma unroll
-    for (int b = 0; b < kFinBatch; ++b) {
+    for (int b = 0; b < FB; ++b) {
       const int j = j0 + b;
       if (j >= nblk) break;  // uniform
       const int e = j * kSampleGrain + tid * 8;
       float wsum = 0.f;
-      if (fast[b]) {
+      if (fast[p][b]) {
         float t[8], d[8];
-        rt[b].unpack(t);
-        if (resid) rd[b].unpack(d);
+        rt[p][b].unpack(t);
+        if (resid) rd[p][b].unpack(d);
 #pragma unroll
         for (int q = 0; q < 8; ++q) wsum += job_weight(f, t[q], resid ? d[q] : 0.f);
       } else if (e < a.V) {
@@ -1117,6 +1141,14 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
         run = 0.0;
       }
     }
+  };
+  issue(0, 0);
+  for (int j0 = 0; j0 < nblk; j0 += 2 * FB) {
+    const bool more1 = j0 + FB < nblk, more2 = j0 + 2 * FB < nblk;
+    if (more1) issue(j0 + FB, 1);
+    weigh(j0, 0);
+    if (more2) issue(j0 + 2 * FB, 0);
+    if (more1) weigh(j0 + FB, 1);
   }
   __syncthreads();
   if (tid < 64) {
@@ -1246,6 +1278,7 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
   if (R < 1 || K < 1 || K > 64 || V < 1)
     return fail(DSP_ERR_SHAPE, "need R >= 1, 1 <= K <= 64, V >= 1 (R=%d K=%d V=%d)", R, K, V);
   if (t_dtype != DSP_F32 && t_dtype != DSP_BF16) return fail(DSP_ERR_DTYPE, "bad target dtype %d", t_dtype);
+  if ((int64_t)V * 4 >= ((int64_t)1 << 31)) return fail(DSP_ERR_SHAPE, "V too large: rows must stay under 2 GiB");
   if (!(temperature >= 0.f) || temperature == INFINITY)
     return fail(DSP_ERR_SHAPE, "temperature must be finite and >= 0");
   const bool greedy = temperature == 0.f;

@@ -209,7 +209,7 @@ int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const in
 /* max_rows: host-known bound on cu_seqlens[R] (0 = R*(K+1)); tgt must hold    */
 /* at least that many rows. Rows past min(cu_seqlens[R], max_rows) are never  */
 /* read, and a request whose rows end past max_rows is a window fault.        */
-/* Limits: 1 <= K <= 64, 1 <= V < 2^31, ld >= V.                             */
+/* Limits: 1 <= K <= 64, 1 <= V < 2^29 (rows under 2 GiB), ld >= V.         */
 /* ------------------------------------------------------------------------ */
 size_t dsp_verify_rejection_workspace_size(int32_t R, int32_t K, int32_t V, int32_t max_rows,
                                            int32_t t_dtype, int32_t d_dtype);
