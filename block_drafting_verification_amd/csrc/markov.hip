@@ -720,15 +720,15 @@ __global__ __launch_bounds__(64) void chain_sample_kernel(ChainSampleArgs a) {
   const int gpl = (a.G + 63) / 64;  // slices per lane (G <= 256)
   float ref[4];
   double sum[4];
+  // unconditional loads (clamped index, masked after): a load under a branch is
+  // waited for on the spot
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int g = lane * gpl + q;
-    ref[q] = -INFINITY;
-    sum[q] = 0.0;
-    if (q < gpl && g < a.G) {
-      ref[q] = pr[g].ref;
-      sum[q] = pr[g].sum;
-    }
+    const bool in = q < gpl && g < a.G;
+    const ChainPart pg = pr[in ? g : a.G - 1];
+    ref[q] = in ? pg.ref : -INFINITY;
+    sum[q] = in ? pg.sum : 0.0;
   }
   float H = fmaxf(fmaxf(ref[0], ref[1]), fmaxf(ref[2], ref[3]));
   H = wave_max(H);
@@ -792,8 +792,18 @@ __global__ __launch_bounds__(64) void chain_sample_kernel(ChainSampleArgs a) {
   const int per = (t1 - t0 + 63) / 64;
   const int v0 = min(t1, t0 + lane * per), v1 = min(t1, v0 + per);
   const uint16_t* zr = a.z + (size_t)r * a.ldz_r + (size_t)a.d * a.ldz_d;
+  // the lane's range in batches of kRB entries, all loads of a batch issued first
+  // (clamped to the range, masked after)
+  constexpr int kRB = 16;
   double ms = 0.0;
-  for (int v = v0; v < v1; ++v) ms += (double)fast_exp2(__builtin_fmaf(bf16_val(zr[v]), a.cz, -H));
+  for (int vb = v0; vb < v1; vb += kRB) {
+    uint16_t x[kRB];
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) x[j] = zr[min(vb + j, v1 - 1)];
+#pragma unroll
+    for (int j = 0; j < kRB; ++j)
+      if (vb + j < v1) ms += (double)fast_exp2(__builtin_fmaf(bf16_val(x[j]), a.cz, -H));
+  }
   const double mi = wave_scan_incl(ms);
   const double me = mi - ms;
   const uint64_t hit2 = __ballot(ms > 0.0 && me <= tin && tin < mi);
@@ -802,10 +812,18 @@ __global__ __launch_bounds__(64) void chain_sample_kernel(ChainSampleArgs a) {
     const int l = __ffsll((unsigned long long)hit2) - 1;
     if (lane == l) {
       double acc = me;
-      for (int v = v0; v < v1 && tok < 0; ++v) {
-        const double wv = (double)fast_exp2(__builtin_fmaf(bf16_val(zr[v]), a.cz, -H));
-        if (wv > 0.0 && tin < acc + wv) tok = v;
-        acc += wv;
+      for (int vb = v0; vb < v1 && tok < 0; vb += kRB) {
+        uint16_t x[kRB];
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) x[j] = zr[min(vb + j, v1 - 1)];
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+          if (vb + j < v1 && tok < 0) {
+            const double wv = (double)fast_exp2(__builtin_fmaf(bf16_val(x[j]), a.cz, -H));
+            if (wv > 0.0 && tin < acc + wv) tok = vb + j;
+            acc += wv;
+          }
+        }
       }
       if (tok < 0)  // rounding inside the lane: its last token with mass
         for (int v = v1 - 1; v >= v0 && tok < 0; --v)

@@ -791,6 +791,7 @@ template <typename T> __device__ __forceinline__ void load8(const T* p, bool vec
 // load at a byte offset at or past the extent returns zeros and touches no memory,
 // so loads can be issued unconditionally (no branch for the compiler to wait at).
 constexpr uint32_t kRowOOB = 0x80000000u;  // past every extent (rows are under 2 GiB)
+constexpr int kAuxNT = 2;                   // cache-policy operand of a buffer load: non-temporal
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
@@ -807,10 +808,13 @@ template <typename T> struct Raw8 {
 #pragma unroll
     for (int q = 0; q < (int)(sizeof(T) / 2); ++q) w[q] = __builtin_nontemporal_load((const u32x4*)p + q);
   }
+  // non-temporal, as the plain loads: rows streamed once must not evict what the next
+  // kernels of the step read (without the hint the scheduler and pack of the next step
+  // measured 2-3 us slower)
   __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
     for (int q = 0; q < (int)(sizeof(T) / 2); ++q)
-      w[q] = __builtin_amdgcn_raw_buffer_load_b128(r, off == kRowOOB ? kRowOOB : off + 16 * q, 0, 0);
+      w[q] = __builtin_amdgcn_raw_buffer_load_b128(r, off == kRowOOB ? kRowOOB : off + 16 * q, 0, kAuxNT);
   }
   __device__ __forceinline__ void unpack(float* x) const {
 #pragma unroll
@@ -1098,35 +1102,34 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
   const int nblk = (a.V + kSampleGrain - 1) / kSampleGrain;
   const int bpc = a.ce / kSampleGrain;  // blocks per chunk
   double run = 0.0;
-  // two register buffers of FB blocks: the loads of the next batch are in
-  // flight while the current one is weighed (one workgroup per CU has no other
-  // work to cover the memory latency)
+  // batches of FB blocks, every load of a batch issued before any is used (double
+  // buffering the batches measured no faster)
   constexpr int FB = (sizeof(TT) == 2 && sizeof(TD) == 2) ? kFinBatch : kFinBatch / 2;  // fp32: twice the bytes
-  Raw8<TT> rt[2][FB];
-  Raw8<TD> rd[2][FB];
-  bool fast[2][FB];
+  Raw8<TT> rt[FB];
+  Raw8<TD> rd[FB];
+  bool fast[FB];
   const __amdgpu_buffer_rsrc_t trs = row_rsrc(tp, (uint32_t)((size_t)a.V * sizeof(TT)));
   const __amdgpu_buffer_rsrc_t drs = row_rsrc(dp, resid ? (uint32_t)((size_t)a.V * sizeof(TD)) : 0u);
-  auto issue = [&](int j0, int p) {
+  auto issue = [&](int j0) {
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
       const int e = (j0 + b) * kSampleGrain + tid * 8;
-      fast[p][b] = al && e + 8 <= a.V;
-      rt[p][b].load_buf(trs, fast[p][b] ? (uint32_t)(e * sizeof(TT)) : kRowOOB);
-      rd[p][b].load_buf(drs, fast[p][b] && resid ? (uint32_t)(e * sizeof(TD)) : kRowOOB);
+      fast[b] = al && e + 8 <= a.V;
+      rt[b].load_buf(trs, fast[b] ? (uint32_t)(e * sizeof(TT)) : kRowOOB);
+      rd[b].load_buf(drs, fast[b] && resid ? (uint32_t)(e * sizeof(TD)) : kRowOOB);
     }
   };
-  auto weigh = [&](int j0, int p) {
+  auto weigh = [&](int j0) {
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
       const int j = j0 + b;
       if (j >= nblk) break;  // uniform
       const int e = j * kSampleGrain + tid * 8;
       float wsum = 0.f;
-      if (fast[p][b]) {
+      if (fast[b]) {
         float t[8], d[8];
-        rt[p][b].unpack(t);
-        if (resid) rd[p][b].unpack(d);
+        rt[b].unpack(t);
+        if (resid) rd[b].unpack(d);
 #pragma unroll
         for (int q = 0; q < 8; ++q) wsum += job_weight(f, t[q], resid ? d[q] : 0.f);
       } else if (e < a.V) {
@@ -1142,13 +1145,9 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
       }
     }
   };
-  issue(0, 0);
-  for (int j0 = 0; j0 < nblk; j0 += 2 * FB) {
-    const bool more1 = j0 + FB < nblk, more2 = j0 + 2 * FB < nblk;
-    if (more1) issue(j0 + FB, 1);
-    weigh(j0, 0);
-    if (more2) issue(j0 + 2 * FB, 0);
-    if (more1) weigh(j0 + FB, 1);
+  for (int j0 = 0; j0 < nblk; j0 += FB) {
+    issue(j0);
+    weigh(j0);
   }
   __syncthreads();
   if (tid < 64) {
