@@ -976,11 +976,19 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
       ti[q] = 0x7fffffff;
     }
     float H = -INFINITY;
-    if (pv)
-      for (int g = j; g < a.G; g += 16) {
-        merge_top4(tv, ti, pr[g].val, pr[g].idx);
-        H = fmaxf(H, pr[g].ref);
-      }
+    // four partials per lane per batch, loaded unconditionally (clamped, masked after:
+    // a load under a branch is waited for on the spot)
+    for (int g0 = j; g0 < a.G; g0 += 64) {
+      TreePart tp[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tp[q] = pr[min(g0 + 16 * q, a.G - 1)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (pv && g0 + 16 * q < a.G) {
+          merge_top4(tv, ti, tp[q].val, tp[q].idx);
+          H = fmaxf(H, tp[q].ref);
+        }
+    }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) {
       float ov[kTopK];
@@ -994,9 +1002,19 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
       H = fmaxf(H, __shfl_xor(H, o, 64));
     }
     double S = 0.0;
-    if (pv)
-      for (int g = j; g < a.G; g += 16)
-        if (pr[g].ref != -INFINITY) S += pr[g].sum * exp2((double)pr[g].ref - (double)H);
+    for (int g0 = j; g0 < a.G; g0 += 64) {
+      float rf[4];
+      double sm[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = min(g0 + 16 * q, a.G - 1);
+        rf[q] = pr[g].ref;
+        sm[q] = pr[g].sum;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (pv && g0 + 16 * q < a.G && rf[q] != -INFINITY) S += sm[q] * exp2((double)rf[q] - (double)H);
+    }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
     if (pv && j == 0) {
@@ -1021,21 +1039,22 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
     const u32x4* ur = (const u32x4*)(a.U + (size_t)ptoken * a.rank + r * qn);
     const u32x4* wr = (const u32x4*)(a.Wt + (size_t)v * a.rank + r * qn);
     double m = 0.0;
-    for (int j0 = 0; j0 < qn / 8; j0 += 8) {  // 8 vector pairs in flight
+    for (int j0 = 0; j0 < qn / 8; j0 += 8) {  // 8 vector pairs in flight (clamped, masked after)
       u32x4 uu[8], ww[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const bool ok = j0 + t < qn / 8;
-        uu[t] = ok ? ur[j0 + t] : u32x4{0u, 0u, 0u, 0u};
-        ww[t] = ok ? wr[j0 + t] : u32x4{0u, 0u, 0u, 0u};
+        const int tt = min(j0 + t, qn / 8 - 1);
+        uu[t] = ur[tt];
+        ww[t] = wr[tt];
       }
 #pragma unroll
       for (int t = 0; t < 8; ++t)
+        if (j0 + t < qn / 8)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          m += (double)bf16_lo(uu[t][h]) * (double)bf16_lo(ww[t][h]);
-          m += (double)bf16_hi(uu[t][h]) * (double)bf16_hi(ww[t][h]);
-        }
+          for (int h = 0; h < 4; ++h) {
+            m += (double)bf16_lo(uu[t][h]) * (double)bf16_lo(ww[t][h]);
+            m += (double)bf16_hi(uu[t][h]) * (double)bf16_hi(ww[t][h]);
+          }
     }
     m += __shfl_xor(m, 1, 64);
     m += __shfl_xor(m, 2, 64);
@@ -1079,19 +1098,29 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
     const int r = ok ? pj >> 2 : 0;
     const int v = ok ? pr[pj & 3] : -1;
     double m = 0.0, am = 0.0;
-    if (v >= 0) {
+    {
+      // loads unconditional (token 0 stands in for a missing probe, masked after)
       const int qn = a.rank / 4;
       const u32x4* ur = (const u32x4*)(a.U + (size_t)s_ntok[r] * a.rank + qr * qn);
-      const u32x4* wr = (const u32x4*)(a.Wt + (size_t)v * a.rank + qr * qn);
-      for (int t = 0; t < qn / 8; ++t) {
-        const u32x4 uu = ur[t], ww = wr[t];
+      const u32x4* wr = (const u32x4*)(a.Wt + (size_t)(v >= 0 ? v : 0) * a.rank + qr * qn);
+      for (int j0 = 0; j0 < qn / 8; j0 += 8) {
+        u32x4 uu[8], ww[8];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const double p0 = (double)bf16_lo(uu[h]) * (double)bf16_lo(ww[h]);
-          const double p1 = (double)bf16_hi(uu[h]) * (double)bf16_hi(ww[h]);
-          m += p0 + p1;
-          am += fabs(p0) + fabs(p1);
+        for (int t = 0; t < 8; ++t) {
+          const int tt = min(j0 + t, qn / 8 - 1);
+          uu[t] = ur[tt];
+          ww[t] = wr[tt];
         }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (j0 + t < qn / 8)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const double p0 = (double)bf16_lo(uu[t][h]) * (double)bf16_lo(ww[t][h]);
+              const double p1 = (double)bf16_hi(uu[t][h]) * (double)bf16_hi(ww[t][h]);
+              m += p0 + p1;
+              am += fabs(p0) + fabs(p1);
+            }
       }
     }
     m += __shfl_xor(m, 1, 64);
