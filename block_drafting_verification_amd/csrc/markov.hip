@@ -45,6 +45,7 @@ constexpr int kTR = 32 * kWaves;  // parent rows per workgroup: one 32-row MFMA 
 constexpr int kTS = 32;           // vocabulary entries per pipeline stage (one 32-row MFMA block)
 constexpr int kTopK = 4;          // children tracked per parent
 constexpr int kTargetWGs = 256;   // one workgroup per CU
+static_assert(kTargetWGs <= 256, "the merge kernels read at most four partials per lane (G <= 256)");
 constexpr int kZS = 144;          // bytes per row of a wave's staging tile of emitted logits (128 + pad)
 
 enum { MODE_ARGMAX = 0, MODE_ARGMAX_LSE = 1, MODE_TREE = 2, MODE_SAMPLE = 3 };
@@ -659,19 +660,27 @@ struct ChainMergeArgs {
 __global__ __launch_bounds__(64) void chain_merge_kernel(ChainMergeArgs a) {
   const int r = blockIdx.x, lane = threadIdx.x;
   const ChainPart* pr = a.part + (size_t)r * a.G;
+  // G <= 256: at most four partials per lane, all loaded before any is used (clamped
+  // index, masked after)
+  ChainPart cp[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cp[q] = pr[min(lane + 64 * q, a.G - 1)];
   uint64_t best = 0;
   float H = -INFINITY;
-  for (int g = lane; g < a.G; g += 64) {
-    best = pr[g].key > best ? pr[g].key : best;
-    H = fmaxf(H, pr[g].ref);
-  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (lane + 64 * q < a.G) {
+      best = cp[q].key > best ? cp[q].key : best;
+      H = fmaxf(H, cp[q].ref);
+    }
   best = wave_max(best);
   if (lane == 0) a.y[(size_t)r * a.ld_y + a.d] = (int32_t)amax_index(best);
   if (a.logq) {
     H = wave_max(H);
     double S = 0.0;
-    for (int g = lane; g < a.G; g += 64)
-      if (pr[g].ref != -INFINITY) S += pr[g].sum * exp2((double)pr[g].ref - (double)H);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane + 64 * q < a.G && cp[q].ref != -INFINITY) S += cp[q].sum * exp2((double)cp[q].ref - (double)H);
     S = wave_sum(S);
     if (lane == 0) {
       const double lse2 = (double)H + log2(S);
