@@ -886,16 +886,17 @@ __device__ __forceinline__ double job_chunk_sum(const JobFrame& f, const TT* tp,
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int e = eb + b * kThreads * 8;
-      float w = 0.f;
-      if (fast[b]) {
-        float t[8], d[8];
-        rt[b].unpack(t);
-        if (f.resid) rd[b].unpack(d);
+      // the fast-path weights are computed unconditionally (an out-of-range vector read
+      // zeros and is discarded by the select): a load used only under a branch is sunk
+      // into it by the compiler, which then waits for it there
+      float t[8], d[8];
+      rt[b].unpack(t);
+      rd[b].unpack(d);
+      float wf = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) w += job_weight(f, t[q], f.resid ? d[q] : 0.f);
-      } else if (e < e1) {
-        w = job_weight8<TT, TD>(f, tp, dp, false, false, e, e1);
-      }
+      for (int q = 0; q < 8; ++q) wf += job_weight(f, t[q], f.resid ? d[q] : 0.f);
+      float w = fast[b] ? wf : 0.f;
+      if (!fast[b] && e < e1) w = job_weight8<TT, TD>(f, tp, dp, false, false, e, e1);
       s += (double)w;
     }
   }
@@ -1125,16 +1126,15 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
       const int j = j0 + b;
       if (j >= nblk) break;  // uniform
       const int e = j * kSampleGrain + tid * 8;
-      float wsum = 0.f;
-      if (fast[b]) {
-        float t[8], d[8];
-        rt[b].unpack(t);
-        if (resid) rd[b].unpack(d);
+      // unconditional fast-path weights, selected after (see job_chunk_sum)
+      float t[8], d[8];
+      rt[b].unpack(t);
+      rd[b].unpack(d);
+      float wf = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) wsum += job_weight(f, t[q], resid ? d[q] : 0.f);
-      } else if (e < a.V) {
-        wsum = job_weight8<TT, TD>(f, tp, dp, false, false, e, a.V);
-      }
+      for (int q = 0; q < 8; ++q) wf += job_weight(f, t[q], resid ? d[q] : 0.f);
+      float wsum = fast[b] ? wf : 0.f;
+      if (!fast[b] && e < a.V) wsum = job_weight8<TT, TD>(f, tp, dp, false, false, e, a.V);
       run += (double)wsum;
       if ((j + 1) % bpc == 0 || j + 1 == nblk) {  // the chunk ends with this block (uniform)
         double s = run;
