@@ -859,6 +859,24 @@ __device__ __forceinline__ float job_weight8(const JobFrame& f, const TT* tp, co
   return w;
 }
 
+// The weights of 8 consecutive elements starting at e (zero past V), one per element.
+template <typename TT, typename TD>
+__device__ __forceinline__ void job_weights8(const JobFrame& f, const TT* tp, const TD* dp, bool t_al, bool d_al,
+                                             int e, int V, float* wv) {
+  if (e + 8 <= V) {
+    float t[8], d[8];
+    load8<TT>(tp + e, t_al, t);
+    if (f.resid) load8<TD>(dp + e, d_al, d);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) wv[q] = job_weight(f, t[q], f.resid ? d[q] : 0.f);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      wv[q] = e + q < V ? job_weight(f, Elem<TT>::val(tp, e + q), f.resid ? Elem<TD>::val(dp, e + q) : 0.f)
+                        : 0.f;
+  }
+}
+
 // Sum of the job's weights over [e0, e0 + len) with 256 threads x 8 elements per step;
 // up to kBatch steps of loads are issued before any is used.
 template <typename TT, typename TD>
@@ -1020,8 +1038,19 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
   const int r0 = min(a.V, e0 + tid * per), r1 = min(a.V, r0 + per);
   const bool t_al = (((uintptr_t)tp) & 15u) == 0;
   const bool d_al = !resid || (((uintptr_t)dp) & 15u) == 0;
+  // the thread's weights; with 8 elements per thread (chunks of 8192) they stay in
+  // registers for the walk below
   double s = 0.0;
-  for (int e = r0; e < r1; e += 8) s += (double)job_weight8<TT, TD>(f, tp, dp, t_al, d_al, e, r1);
+  float wv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) wv[q] = 0.f;
+  for (int e = r0; e < r1; e += 8) {
+    job_weights8<TT, TD>(f, tp, dp, t_al, d_al, e, r1, wv);
+    float ws = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ws += wv[q];
+    s += (double)ws;
+  }
   double inc = s;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -1035,11 +1064,28 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
   const double E = off + inc - s;
   if (E <= tau && tau < E + s) {
     double run = E;
-    for (int e = r0; e < r1; ++e) {
-      run += (double)job_weight(f, Elem<TT>::val(tp, e), resid ? Elem<TD>::val(dp, e) : 0.f);
-      if (run > tau) {
-        atomicMin(&s_found, e);
-        break;
+    if (per == 8) {
+      int hit = -1;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        run += (double)wv[q];
+        if (hit < 0 && r0 + q < r1 && run > tau) hit = r0 + q;
+      }
+      if (hit >= 0) atomicMin(&s_found, hit);
+    } else {
+      for (int e = r0; e < r1; e += 8) {
+        float w8[8];
+        job_weights8<TT, TD>(f, tp, dp, t_al, d_al, e, r1, w8);
+        int hit = -1;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          run += (double)w8[q];
+          if (hit < 0 && run > tau) hit = e + q;
+        }
+        if (hit >= 0) {
+          atomicMin(&s_found, hit);
+          break;
+        }
       }
     }
   }
