@@ -67,6 +67,11 @@ def test_host_validation_codes():
     rc, _ = _err(lib.dsp_verify_rejection(p, 1, 100, p, p, 1, 700, 100, p, 7, None, 4, 7, 100, 0, 1.0, 0, 0,
                                           None, None, None, None, None, None, p, p, p, None, None, p, p, 16, None))
     assert rc == -5
+    big = 1 << 29  # a logit row of 2 GiB in fp32: past what the bounded row loads address
+    rc, msg = _err(lib.dsp_verify_rejection(p, 1, big, p, p, 1, 7 * big, big, p, 7, None, 4, 7, big, 0, 1.0, 0, 0,
+                                            None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30,
+                                            None))
+    assert rc == -2 and "2 GiB" in msg
     # schedule: too many candidates, short cost table, unknown mode
     assert lib.dsp_schedule_windows(p, 9000, 1, p, 9001, 0, -1, 0.0, p, None, None, None, 0, None) == -2
     assert lib.dsp_schedule_windows(p, 4, 4, p, 16, 0, -1, 0.0, p, None, None, None, 0, None) == -2
