@@ -169,8 +169,9 @@ def bench_verify(args, which):
     ops = {}
 
     def make_step(stream):
-        sch = dsp.schedule_windows(conf, cost, want_survival=False, stream=stream, prepare=True)
-        pk = dsp.pack_ragged(sch.outputs["windows"], anchors, x, stream=stream, prepare=True)
+        # the scheduler and the pack in one call (one launch: the selection workgroup packs)
+        sch = dsp.schedule_pack(conf, cost, anchors, x, want_survival=False, stream=stream, prepare=True)
+        pk = sch
         ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=0,
                                    round_dev=rnd, max_rows=max_rows, row_req=pk.outputs["row_req"],
                                    row_pos=pk.outputs["row_pos"], stream=stream, prepare=True)
@@ -178,7 +179,6 @@ def bench_verify(args, which):
 
         def step():  # the verify call advances the device-side Philox round itself
             sch()
-            pk()
             ver()
         return step
 
@@ -392,8 +392,9 @@ def bench_cycle(args):
     def make_step(stream):
         dr = dsp.draft_markov_sample(L, U, Wt, a, 1.0, seed=0, round_dev=rd, stream=stream, prepare=True)
         ch = dsp.confidence_head(hh, hw, hd["bias"], temps, stream=stream, prepare=True)
-        sch = dsp.schedule_windows(ch.outputs["conf"], cost, want_survival=False, stream=stream, prepare=True)
-        pk = dsp.pack_ragged(sch.outputs["windows"], a, dr.outputs["y"], stream=stream, prepare=True)
+        sch = dsp.schedule_pack(ch.outputs["conf"], cost, a, dr.outputs["y"], want_survival=False, stream=stream,
+                                prepare=True)
+        pk = sch
         ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], dr.outputs["y"], drf=dr.outputs["z"],
                                    temperature=1.0, seed=0, round_dev=rd, max_rows=tgt.shape[0],
                                    row_req=pk.outputs["row_req"], row_pos=pk.outputs["row_pos"],
@@ -404,7 +405,6 @@ def bench_cycle(args):
             dr()
             ch()
             sch()
-            pk()
             ver()
         return step
 

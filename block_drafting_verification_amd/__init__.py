@@ -27,7 +27,7 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
                    DspError, KERNELS)
 
 __all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step",
-           "draft_markov_sample", "tree_expand",
+           "draft_markov_sample", "tree_expand", "schedule_pack",
            "philox_uniforms", "stream_read", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
            "DSP_STATUS_TOKEN_RANGE",
@@ -199,6 +199,46 @@ def pack_ragged(windows, anchors, drafts, tiers=None, out=None, status=None, str
             _ptr(cu), _ptr(tokens), _ptr(row_req), _ptr(row_pos), _ptr(tt), _ptr(status), _stream(stream))
     res = dict(cu_seqlens=cu, tokens=tokens, row_req=row_req, row_pos=row_pos, total_and_tier=tt, status=status)
     return _finish(lib().dsp_pack_ragged, args, res, prepare, (windows, anchors, drafts, arr))
+
+
+def schedule_pack(conf, cost, anchors, drafts, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, threshold=0.0,
+                  want_survival=True, tiers=None, out=None, status=None, stream=None, prepare=False):
+    """schedule_windows then pack_ragged on its windows, in one call (one launch fewer).
+
+    conf float32 [R, K], cost float64 [>= R*K+1], anchors int32 [R], drafts int32 [R, K] (GPU).
+    Returns the union of both calls' dicts.
+    """
+    _on_gpu(conf, cost, anchors, drafts)
+    _need(conf.dtype == torch.float32 and conf.dim() == 2 and conf.is_contiguous(), "conf: contiguous float32 [R, K]")
+    _need(cost.dtype == torch.float64 and cost.is_contiguous(), "cost: contiguous float64")
+    for t in (anchors, drafts):
+        _need(t.dtype == torch.int32, "anchors and drafts are int32")
+    _need(drafts.dim() == 2 and drafts.stride(1) == 1 and tuple(drafts.shape) == tuple(conf.shape),
+          "drafts: [R, K] like conf, unit inner stride")
+    R, K = conf.shape
+    dev = conf.device
+    o = out or {}
+    windows = _take(o, "windows", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    survival = _take(o, "survival", lambda: torch.empty(R, K, dtype=torch.float64, device=dev)) if want_survival else None
+    stats = _take(o, "stats", lambda: torch.empty(4, dtype=torch.float64, device=dev))
+    cu = _take(o, "cu_seqlens", lambda: torch.empty(R + 1, dtype=torch.int32, device=dev))
+    tokens = _take(o, "tokens", lambda: torch.empty(R * (K + 1), dtype=torch.int32, device=dev))
+    row_req = _take(o, "row_req", lambda: torch.empty(R * (K + 1), dtype=torch.int32, device=dev))
+    row_pos = _take(o, "row_pos", lambda: torch.empty(R * (K + 1), dtype=torch.int32, device=dev))
+    tt = _take(o, "total_and_tier", lambda: torch.empty(2, dtype=torch.int32, device=dev))
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    tl = list(tiers or [])
+    arr = (ctypes.c_int32 * max(len(tl), 1))(*tl) if tl else None
+    ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare)
+    args = (_ptr(conf), R, K, _ptr(cost), cost.numel(), mode, max_tokens, float(threshold), _ptr(windows),
+            _ptr(survival), _ptr(stats), _ptr(anchors), _ptr(drafts), drafts.stride(0),
+            ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, len(tl),
+            _ptr(cu), _ptr(tokens), _ptr(row_req), _ptr(row_pos), _ptr(tt), _ptr(status), _ptr(ws), ws.numel(),
+            _stream(stream))
+    res = dict(windows=windows, survival=survival, stats=stats, cu_seqlens=cu, tokens=tokens, row_req=row_req,
+               row_pos=row_pos, total_and_tier=tt, status=status)
+    return _finish(lib().dsp_schedule_pack, args, res, prepare, (conf, cost, anchors, drafts, ws, arr))
 
 
 def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,

@@ -35,6 +35,8 @@ SIGNATURES = {
     "dsp_schedule_windows": (_i32, [_p, _i32, _i32, _p, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _p, _sz,
                                     _p]),
     "dsp_pack_ragged": (_i32, [_p, _p, _p, _i64, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "dsp_schedule_pack": (_i32, [_p, _i32, _i32, _p, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _p, _p, _i64, _p,
+                                 _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "dsp_verify_rejection_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "dsp_verify_rejection": (_i32, [_p, _i32, _i64, _p, _p, _i32, _i64, _i64, _p, _i64, _p,
                                     _i32, _i32, _i32, _i32, _f32, _u64, _u64, _p, _p, _p, _p, _p, _p,

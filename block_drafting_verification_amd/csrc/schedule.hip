@@ -135,13 +135,92 @@ __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(const float
   }
 }
 
+struct Tiers {
+  int32_t n;
+  int32_t v[64];
+};
+
+// The pack outputs (and its inputs besides the windows).
+struct PackArgs {
+  const int32_t* anchors;
+  const int32_t* drafts;
+  int64_t ld;
+  Tiers tiers;
+  int32_t* cu;
+  int32_t* tokens;
+  int32_t* row_req;
+  int32_t* row_pos;
+  int32_t* total_and_tier;
+  int32_t* status;
+};
+
+// The pack, run by one workgroup of 1024 threads over windows already in memory (wsum:
+// 16 LDS words for the scan).
+__device__ void pack_body(const int32_t* __restrict__ windows, int R, int K, const PackArgs& pa, uint64_t* wsum) {
+  const int tid = threadIdx.x;
+  const int C = (R + 1023) / 1024;
+  const int i0 = min(R, tid * C), i1 = min(R, i0 + C);
+  uint64_t local = 0;
+  bool bad = false;
+  for (int i = i0; i < i1; ++i) {
+    int w = windows[i];
+    if (w < 0 || w > K) {
+      bad = true;
+      w = w < 0 ? 0 : K;
+    }
+    local += (uint64_t)(w + 1);
+  }
+  if (bad) atomicOr(pa.status, DSP_STATUS_WINDOW_RANGE);
+  const uint64_t ex = block_exclusive_scan_u64(local, wsum);
+  // offsets first (each thread its own requests), then one flat copy over (request, position)
+  int pos = (int)ex;
+  if (tid == 0) pa.cu[0] = 0;
+  for (int i = i0; i < i1; ++i) {
+    int w = windows[i];
+    w = w < 0 ? 0 : (w > K ? K : w);
+    pos += w + 1;
+    pa.cu[i + 1] = pos;
+  }
+  if (i1 == R && i0 < i1) {
+    const int T = pos;
+    int tier = T;
+    if (pa.tiers.n > 0) {
+      tier = -1;
+      for (int t = 0; t < pa.tiers.n; ++t)
+        if (pa.tiers.v[t] >= T) {
+          tier = pa.tiers.v[t];
+          break;
+        }
+    }
+    pa.total_and_tier[0] = T;
+    pa.total_and_tier[1] = tier;
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int K1 = K + 1;
+  for (long j = tid; j < (long)R * K1; j += 1024) {
+    const int i = (int)(j / K1), k = (int)(j % K1);
+    const int start = pa.cu[i];
+    if (start + k >= pa.cu[i + 1]) continue;  // beyond this request's window
+    pa.tokens[start + k] = k == 0 ? pa.anchors[i] : pa.drafts[(size_t)i * pa.ld + k - 1];
+    pa.row_req[start + k] = i;
+    pa.row_pos[start + k] = k;
+  }
+}
+
+__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* __restrict__ windows, int R, int K,
+                                                    PackArgs pa) {
+  __shared__ uint64_t wsum[16];
+  pack_body(windows, R, K, pa, wsum);
+}
+
 // Selection over the ranked keys (one workgroup): exact prefix sums of Sq, the
 // throughput test, E at N, and the windows; or the fixed-threshold rule straight
 // from the survivals (then no ranking is needed and sorted is unused).
 __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     const float* __restrict__ conf, int R, int K, const double* __restrict__ cost, int mode, int M,
     double threshold, int Q, const uint64_t* __restrict__ sorted, int32_t* __restrict__ windows,
-    double* __restrict__ survival, double* __restrict__ stats) {
+    double* __restrict__ survival, double* __restrict__ stats, PackArgs pa) {
   __shared__ float s_conf[kMaxCand];  // threshold mode
   __shared__ int cnt[kMaxCand];
   __shared__ uint64_t wsum[kSchedThreads / 64];
@@ -180,6 +259,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
       stats[1] = E;
       stats[2] = cost[Nt] != 0.0 ? __ddiv_rn(E, cost[Nt]) : (E == 0.0 ? 0.0 : INFINITY);
       stats[3] = (double)Q;
+    }
+    if (pa.cu) {  // the pack of these windows, in this workgroup
+      __threadfence_block();
+      __syncthreads();
+      pack_body(windows, R, K, pa, wsum);
     }
     return;
   }
@@ -268,72 +352,37 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     stats[2] = cost[N] != 0.0 ? __ddiv_rn(E, cost[N]) : (E == 0.0 ? 0.0 : INFINITY);
     stats[3] = (double)Q;
   }
+  if (pa.cu) {  // the pack of these windows, in this workgroup
+    __threadfence_block();
+    __syncthreads();
+    pack_body(windows, R, K, pa, wsum);
+  }
 }
 
-struct Tiers {
-  int32_t n;
-  int32_t v[64];
-};
-
-__global__ __launch_bounds__(1024) void pack_kernel(const int32_t* __restrict__ windows,
-                                                    const int32_t* __restrict__ anchors,
-                                                    const int32_t* __restrict__ drafts, int64_t ld,
-                                                    int R, int K, Tiers tiers, int32_t* __restrict__ cu,
-                                                    int32_t* __restrict__ tokens,
-                                                    int32_t* __restrict__ row_req,
-                                                    int32_t* __restrict__ row_pos,
-                                                    int32_t* __restrict__ total_and_tier,
-                                                    int32_t* __restrict__ status) {
-  __shared__ uint64_t wsum[16];
-  const int tid = threadIdx.x;
-  const int C = (R + 1023) / 1024;
-  const int i0 = min(R, tid * C), i1 = min(R, i0 + C);
-  uint64_t local = 0;
-  bool bad = false;
-  for (int i = i0; i < i1; ++i) {
-    int w = windows[i];
-    if (w < 0 || w > K) {
-      bad = true;
-      w = w < 0 ? 0 : K;
-    }
-    local += (uint64_t)(w + 1);
-  }
-  if (bad) atomicOr(status, DSP_STATUS_WINDOW_RANGE);
-  const uint64_t ex = block_exclusive_scan_u64(local, wsum);
-  // offsets first (each thread its own requests), then one flat copy over (request, position)
-  int pos = (int)ex;
-  if (tid == 0) cu[0] = 0;
-  for (int i = i0; i < i1; ++i) {
-    int w = windows[i];
-    w = w < 0 ? 0 : (w > K ? K : w);
-    pos += w + 1;
-    cu[i + 1] = pos;
-  }
-  if (i1 == R && i0 < i1) {
-    const int T = pos;
-    int tier = T;
-    if (tiers.n > 0) {
-      tier = -1;
-      for (int t = 0; t < tiers.n; ++t)
-        if (tiers.v[t] >= T) {
-          tier = tiers.v[t];
-          break;
-        }
-    }
-    total_and_tier[0] = T;
-    total_and_tier[1] = tier;
-  }
-  __threadfence_block();
-  __syncthreads();
-  const int K1 = K + 1;
-  for (long j = tid; j < (long)R * K1; j += 1024) {
-    const int i = (int)(j / K1), k = (int)(j % K1);
-    const int start = cu[i];
-    if (start + k >= cu[i + 1]) continue;  // beyond this request's window
-    tokens[start + k] = k == 0 ? anchors[i] : drafts[(size_t)i * ld + k - 1];
-    row_req[start + k] = i;
-    row_pos[start + k] = k;
-  }
+// Validates the pack's arguments (windows apart) and fills pa; 0 or an error code.
+int32_t pack_args(const int32_t* anchors, const int32_t* drafts, int64_t ld_drafts, int32_t R, int32_t K,
+                  const int32_t* tiers_host, int32_t n_tiers, int32_t* cu_seqlens, int32_t* tokens,
+                  int32_t* row_req, int32_t* row_pos, int32_t* total_and_tier, int32_t* status, PackArgs* pa) {
+  if (R < 1 || R > 65536 || K < 1 || K > 4096) return fail(DSP_ERR_SHAPE, "need 1 <= R <= 65536, 1 <= K <= 4096");
+  if (ld_drafts < K) return fail(DSP_ERR_SHAPE, "ld_drafts < K");
+  if (n_tiers < 0 || n_tiers > 64 || (n_tiers > 0 && !tiers_host))
+    return fail(DSP_ERR_SHAPE, "n_tiers must be in [0, 64] with a host tier array");
+  if (!anchors || !drafts || !cu_seqlens || !tokens || !row_req || !row_pos || !total_and_tier || !status)
+    return fail(DSP_ERR_NULL, "required pointer is NULL");
+  pa->anchors = anchors;
+  pa->drafts = drafts;
+  pa->ld = ld_drafts;
+  pa->tiers.n = n_tiers;
+  for (int j = 0; j < 64; ++j) pa->tiers.v[j] = j < n_tiers ? tiers_host[j] : 0;
+  for (int j = 1; j < n_tiers; ++j)
+    if (pa->tiers.v[j] < pa->tiers.v[j - 1]) return fail(DSP_ERR_SHAPE, "tiers must be ascending");
+  pa->cu = cu_seqlens;
+  pa->tokens = tokens;
+  pa->row_req = row_req;
+  pa->row_pos = row_pos;
+  pa->total_and_tier = total_and_tier;
+  pa->status = status;
+  return DSP_OK;
 }
 
 int quant_bits(int R, int K) {
@@ -354,11 +403,11 @@ extern "C" size_t dsp_schedule_windows_workspace_size(int32_t R, int32_t K) {
   return ((size_t)R * K * sizeof(uint64_t) + 255) & ~(size_t)255;  // the ranked keys
 }
 
-extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
-                                        int32_t n_cost, int32_t mode, int32_t max_tokens, double threshold,
-                                        int32_t* windows, double* survival, double* stats, void* ws,
-                                        size_t ws_bytes, void* stream) {
-  clear_error();
+namespace dsp {
+namespace {
+// Validates the scheduler's arguments; 0 or an error code.
+int32_t schedule_check(const float* conf, int32_t R, int32_t K, const double* cost, int32_t n_cost, int32_t mode,
+                       double threshold, int32_t* windows, void* ws, size_t ws_bytes) {
   if (R < 1 || K < 1 || K > 128 || (long)R * K > kMaxCand)
     return fail(DSP_ERR_SHAPE, "need R >= 1, 1 <= K <= 128, R*K <= %d (R=%d K=%d)", kMaxCand, R, K);
   if (n_cost < R * K + 1) return fail(DSP_ERR_SHAPE, "cost table needs R*K+1 = %d entries", R * K + 1);
@@ -370,9 +419,15 @@ extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K,
   if (!conf || !cost || !windows) return fail(DSP_ERR_NULL, "conf, cost and windows are required");
   if (!ws || ws_bytes < dsp_schedule_windows_workspace_size(R, K))
     return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", dsp_schedule_windows_workspace_size(R, K));
+  return DSP_OK;
+}
+
+// The scheduler's launches; with pa.cu set, the selection workgroup also packs.
+int32_t schedule_launch(const float* conf, int32_t R, int32_t K, const double* cost, int32_t mode,
+                        int32_t max_tokens, double threshold, int32_t* windows, double* survival, double* stats,
+                        void* ws, const PackArgs& pa, hipStream_t s) {
   const int M = max_tokens < 0 ? R * K : (max_tokens < R * K ? max_tokens : R * K);
   const int Q = quant_bits(R, K);
-  hipStream_t s = (hipStream_t)stream;
   uint64_t* sorted = (uint64_t*)ws;
   if (mode != DSP_SCHED_THRESHOLD) {
     const int g = (R * K + kRankCand - 1) / kRankCand;
@@ -380,8 +435,40 @@ extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K,
            sorted);
   }
   launch(DSP_K_SCHEDULE, schedule_select_kernel, dim3(1), dim3(kSchedThreads), 0, s, conf, R, K, cost, mode, M,
-         threshold, Q, (const uint64_t*)sorted, windows, survival, stats);
+         threshold, Q, (const uint64_t*)sorted, windows, survival, stats, pa);
   return hip_check(hipGetLastError(), "schedule launch");
+}
+}  // namespace
+}  // namespace dsp
+
+extern "C" int32_t dsp_schedule_windows(const float* conf, int32_t R, int32_t K, const double* cost,
+                                        int32_t n_cost, int32_t mode, int32_t max_tokens, double threshold,
+                                        int32_t* windows, double* survival, double* stats, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  clear_error();
+  const int32_t rc = schedule_check(conf, R, K, cost, n_cost, mode, threshold, windows, ws, ws_bytes);
+  if (rc) return rc;
+  PackArgs none{};
+  return schedule_launch(conf, R, K, cost, mode, max_tokens, threshold, windows, survival, stats, ws, none,
+                         (hipStream_t)stream);
+}
+
+extern "C" int32_t dsp_schedule_pack(const float* conf, int32_t R, int32_t K, const double* cost, int32_t n_cost,
+                                     int32_t mode, int32_t max_tokens, double threshold, int32_t* windows,
+                                     double* survival, double* stats, const int32_t* anchors,
+                                     const int32_t* drafts, int64_t ld_drafts, const int32_t* tiers_host,
+                                     int32_t n_tiers, int32_t* cu_seqlens, int32_t* tokens, int32_t* row_req,
+                                     int32_t* row_pos, int32_t* total_and_tier, int32_t* status, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  clear_error();
+  int32_t rc = schedule_check(conf, R, K, cost, n_cost, mode, threshold, windows, ws, ws_bytes);
+  if (rc) return rc;
+  PackArgs pa{};
+  rc = pack_args(anchors, drafts, ld_drafts, R, K, tiers_host, n_tiers, cu_seqlens, tokens, row_req, row_pos,
+                 total_and_tier, status, &pa);
+  if (rc) return rc;
+  return schedule_launch(conf, R, K, cost, mode, max_tokens, threshold, windows, survival, stats, ws, pa,
+                         (hipStream_t)stream);
 }
 
 extern "C" int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const int32_t* drafts,
@@ -390,19 +477,11 @@ extern "C" int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchor
                                    int32_t* row_req, int32_t* row_pos, int32_t* total_and_tier,
                                    int32_t* status, void* stream) {
   clear_error();
-  if (R < 1 || R > 65536 || K < 1 || K > 4096) return fail(DSP_ERR_SHAPE, "need 1 <= R <= 65536, 1 <= K <= 4096");
-  if (ld_drafts < K) return fail(DSP_ERR_SHAPE, "ld_drafts < K");
-  if (n_tiers < 0 || n_tiers > 64 || (n_tiers > 0 && !tiers_host))
-    return fail(DSP_ERR_SHAPE, "n_tiers must be in [0, 64] with a host tier array");
-  if (!windows || !anchors || !drafts || !cu_seqlens || !tokens || !row_req || !row_pos ||
-      !total_and_tier || !status)
-    return fail(DSP_ERR_NULL, "required pointer is NULL");
-  Tiers t;
-  t.n = n_tiers;
-  for (int j = 0; j < 64; ++j) t.v[j] = j < n_tiers ? tiers_host[j] : 0;
-  for (int j = 1; j < n_tiers; ++j)
-    if (t.v[j] < t.v[j - 1]) return fail(DSP_ERR_SHAPE, "tiers must be ascending");
-  launch(DSP_K_PACK, pack_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, windows, anchors, drafts,
-         ld_drafts, R, K, t, cu_seqlens, tokens, row_req, row_pos, total_and_tier, status);
+  if (!windows) return fail(DSP_ERR_NULL, "required pointer is NULL");
+  PackArgs pa{};
+  const int32_t rc = pack_args(anchors, drafts, ld_drafts, R, K, tiers_host, n_tiers, cu_seqlens, tokens, row_req,
+                               row_pos, total_and_tier, status, &pa);
+  if (rc) return rc;
+  launch(DSP_K_PACK, pack_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, windows, R, K, pa);
   return hip_check(hipGetLastError(), "pack launch");
 }

@@ -154,6 +154,25 @@ int32_t dsp_pack_ragged(const int32_t* windows, const int32_t* anchors, const in
                         int32_t* row_pos, int32_t* total_and_tier, int32_t* status, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Window selection and ragged pack in one call  ([N] 5.2; [S] "Ragged       */
+/* verify")                                                                  */
+/*                                                                          */
+/* Exactly dsp_schedule_windows followed by dsp_pack_ragged on the windows    */
+/* it wrote (same arguments, same outputs, bit for bit), with the pack run by */
+/* the selection's own workgroup: one launch fewer between the scheduler and */
+/* the verify. Limits and workspace: those of dsp_schedule_windows (which    */
+/* are within the pack's).                                                   */
+/* ------------------------------------------------------------------------ */
+int32_t dsp_schedule_pack(const float* conf, int32_t R, int32_t K, const double* cost,
+                          int32_t n_cost, int32_t mode, int32_t max_tokens, double threshold,
+                          int32_t* windows, double* survival, double* stats,
+                          const int32_t* anchors, const int32_t* drafts, int64_t ld_drafts,
+                          const int32_t* tiers_host, int32_t n_tiers, int32_t* cu_seqlens,
+                          int32_t* tokens, int32_t* row_req, int32_t* row_pos,
+                          int32_t* total_and_tier, int32_t* status, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Batched ragged verify  ([N] 1, 3 / Figure 1; [S] "three verify modes",     */
 /* "Ragged verify"; [P] greedy tree verification)                            */
 /*                                                                          */

@@ -72,6 +72,11 @@ def test_host_validation_codes():
                                             None, None, None, None, None, None, p, p, p, None, None, p, p, 1 << 30,
                                             None))
     assert rc == -2 and "2 GiB" in msg
+    # schedule + pack: the scheduler's limits, then the pack's pointers
+    assert lib.dsp_schedule_pack(p, 9000, 1, p, 9001, 0, -1, 0.0, p, None, None, p, p, 1, None, 0, p, p, p, p, p,
+                                 p, p, 1 << 20, None) == -2
+    assert lib.dsp_schedule_pack(p, 4, 4, p, 17, 0, -1, 0.0, p, None, None, None, p, 4, None, 0, p, p, p, p, p,
+                                 p, p, 1 << 20, None) == -1
     # schedule: too many candidates, short cost table, unknown mode
     assert lib.dsp_schedule_windows(p, 9000, 1, p, 9001, 0, -1, 0.0, p, None, None, None, 0, None) == -2
     assert lib.dsp_schedule_windows(p, 4, 4, p, 16, 0, -1, 0.0, p, None, None, None, 0, None) == -2

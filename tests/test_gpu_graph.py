@@ -110,8 +110,8 @@ def test_graph_cycle_replays_match_eager():
 
 
 def test_graph_dense_verify_replays_match_eager():
-    """Schedule -> pack -> verify, 64 requests x K=7 (decision, residual and draw as three
-    launches), V=40,000, with the round on the device."""
+    """Schedule + pack (one call) -> verify, 64 requests x K=7 (decision, residual and draw as
+    three launches), V=40,000, with the round on the device."""
     dev = torch.device("cuda", 0)
     c = workloads.verify_case(64, 7, 40000, dtype="bf16", seed=31, boost_p=0.01)
     R, K = c["R"], c["K"]
@@ -125,9 +125,9 @@ def test_graph_dense_verify_replays_match_eager():
     rd = torch.zeros(1, dtype=torch.int64, device=dev)
     ops = {}
 
-    def make_step(stream):
-        sch = dsp.schedule_windows(conf, cost, stream=stream, prepare=True)
-        pk = dsp.pack_ragged(sch.outputs["windows"], anchors, x, stream=stream, prepare=True)
+    def make_step(stream):  # the scheduler and the pack in one call, as the bench runs them
+        sch = dsp.schedule_pack(conf, cost, anchors, x, stream=stream, prepare=True)
+        pk = sch
         ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=3,
                                    round_dev=rd, max_rows=tgt.shape[0], row_req=pk.outputs["row_req"],
                                    row_pos=pk.outputs["row_pos"], stream=stream, prepare=True)
@@ -135,7 +135,6 @@ def test_graph_dense_verify_replays_match_eager():
 
         def step():
             sch()
-            pk()
             ver()
         return step
 

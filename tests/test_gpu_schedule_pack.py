@@ -115,3 +115,36 @@ def test_pack_flags_bad_window():
     g = dsp.pack_ragged(to_gpu(w), to_gpu(np.zeros(3, np.int32)), to_gpu(np.zeros((3, 4), np.int32)))
     torch.cuda.synchronize()
     assert int(host(g["status"])[0]) & dsp.DSP_STATUS_WINDOW_RANGE
+
+
+@pytest.mark.parametrize("R,K", [(1, 1), (7, 16), (64, 7), (256, 16), (2000, 4), (64, 128)])
+def test_schedule_pack_one_call(R, K):
+    """dsp_schedule_pack equals dsp_schedule_windows then dsp_pack_ragged, bit for bit, in every
+    scheduler mode, with and without tiers; the windows and pack also against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(R * 7 + K))
+    conf = rng.uniform(0.05, 1.0, size=(R, K)).astype(np.float32)
+    cost = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
+    anchors = rng.integers(0, 10**6, size=R).astype(np.int32)
+    drafts = rng.integers(0, 10**6, size=(R, K)).astype(np.int32)
+    tiers = sorted(set(rng.integers(R, R * (K + 1) + 2, size=6).tolist()))
+    cg, kg, ag, dg = to_gpu(conf), to_gpu(cost), to_gpu(anchors), to_gpu(drafts)
+    for mode, cap, th, tl in ((dsp.DSP_SCHED_EARLY_STOP, -1, 0.0, None), (dsp.DSP_SCHED_ARGMAX, -1, 0.0, tiers),
+                              (dsp.DSP_SCHED_TOP_M, (R * K) // 3, 0.0, None),
+                              (dsp.DSP_SCHED_THRESHOLD, -1, 0.3, tiers)):
+        print(f"schedule+pack R={R} K={K} mode={mode}", flush=True)
+        f = dsp.schedule_pack(cg, kg, ag, dg, mode=mode, max_tokens=cap, threshold=th, tiers=tl)
+        s = dsp.schedule_windows(cg, kg, mode=mode, max_tokens=cap, threshold=th)
+        p = dsp.pack_ragged(s["windows"], ag, dg, tiers=tl)
+        torch.cuda.synchronize()
+        for k in ("windows", "survival", "stats"):
+            assert torch.equal(f[k], s[k]), k
+        T = int(host(p["total_and_tier"])[0])
+        for k in ("cu_seqlens", "total_and_tier", "status"):
+            assert torch.equal(f[k], p[k]), k
+        for k in ("tokens", "row_req", "row_pos"):
+            assert torch.equal(f[k][:T], p[k][:T]), k
+        o = osch.schedule_windows(conf, cost, mode=mode, max_tokens=cap, threshold=th)
+        np.testing.assert_array_equal(host(f["windows"]), o["windows"])
+        op = opack.pack_ragged(o["windows"], anchors, drafts, tiers=tl)
+        np.testing.assert_array_equal(host(f["tokens"])[:T], op["tokens"])
+        assert host(f["total_and_tier"]).tolist() == [op["total"], op["tier"]]
