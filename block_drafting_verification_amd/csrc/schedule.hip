@@ -62,13 +62,26 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* wsum) {
   return wsum[w] + inc - v;
 }
 
+// conf [n] into LDS: eight loads per thread in flight per round (clamped, stored only
+// in range), instead of one round trip per element.
+__device__ __forceinline__ void stage_conf(const float* __restrict__ conf, int n, float* s_conf) {
+  for (int j0 = threadIdx.x; j0 < n; j0 += 8 * blockDim.x) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = conf[min(j0 + q * (int)blockDim.x, n - 1)];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j0 + q * (int)blockDim.x < n) s_conf[j0 + q * blockDim.x] = v[q];
+  }
+}
+
 // Candidate keys of every (request, position): survival in fp64, one thread per
 // request multiplying left to right, quantised and packed (optionally also written
 // out as the survival table).
 __device__ void candidate_keys(const float* __restrict__ conf, int R, int K, double scale,
                                float* s_conf, uint64_t* keys, double* survival) {
   const int n = R * K;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) s_conf[j] = conf[j];
+  stage_conf(conf, n, s_conf);
   __syncthreads();
   for (int i = threadIdx.x; i < R; i += blockDim.x) {
     double s = 1.0;
@@ -233,7 +246,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
 
   if (mode == DSP_SCHED_THRESHOLD) {
     // n_i = #{k : S_{i,k} >= threshold} on the fp64 survival; no ranking needed
-    for (int j = tid; j < n; j += kSchedThreads) s_conf[j] = conf[j];
+    stage_conf(conf, n, s_conf);
     __syncthreads();
     uint64_t esum = 0;
     int cnt_all = 0;
