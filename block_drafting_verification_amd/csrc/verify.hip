@@ -748,6 +748,99 @@ __global__ __launch_bounds__(64) void verify_decide_tree(DecideArgs a) {
   }
 }
 
+// Greedy tree walk, one workgroup of kWalkThreads per request: from the root, the
+// arg-max of the current node's target row (largest value, lowest token id) selects
+// the child carrying that token, until no child does. Only the rows on the walked
+// path are read -- at most D + 1 of the window's rows -- instead of every node's.
+constexpr int kWalkThreads = 1024;
+constexpr int kWalkVpt = 16;  // 16-byte vectors per thread per round
+
+// Arg-max key (amax_key order) of row p over [0, V), all threads of the workgroup.
+template <typename T>
+__device__ uint64_t row_argmax_key(const T* __restrict__ p, int V, uint64_t* smk) {
+  constexpr int PV = Elem<T>::kPerVec;
+  const RowGeom g = row_geom(p, V);
+  const u32x4* vp = (const u32x4*)(p + g.head);
+  const int tid = threadIdx.x;
+  uint64_t best = 0;
+  if (tid < g.head) best = amax_key(Elem<T>::val(p, tid), (uint32_t)tid);
+  if (tid < V - g.tail) {
+    const uint64_t k = amax_key(Elem<T>::val(p, g.tail + tid), (uint32_t)(g.tail + tid));
+    best = k > best ? k : best;
+  }
+  for (int v0 = tid; v0 < g.nvec; v0 += kWalkVpt * kWalkThreads) {
+    u32x4 buf[kWalkVpt];
+#pragma unroll
+    for (int j = 0; j < kWalkVpt; ++j)  // every load issued first (clamped, masked after)
+      buf[j] = __builtin_nontemporal_load(vp + min(v0 + j * kWalkThreads, g.nvec - 1));
+#pragma unroll
+    for (int j = 0; j < kWalkVpt; ++j) {
+      const int v = v0 + j * kWalkThreads;
+      if (v < g.nvec) {
+        float x[PV];
+        Elem<T>::unpack(buf[j], x);
+#pragma unroll
+        for (int e = 0; e < PV; ++e) {
+          const uint64_t k = amax_key(x[e], (uint32_t)(g.head + v * PV + e));
+          best = k > best ? k : best;
+        }
+      }
+    }
+  }
+  return block_max<kWalkThreads / 64>(best, smk);
+}
+
+template <typename TT>
+__global__ __launch_bounds__(kWalkThreads) void verify_tree_walk_kernel(DecideArgs a) {
+  __shared__ uint64_t smk[kWalkThreads / 64];
+  __shared__ int s_next, s_bad;
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int base = a.cu[i], end = a.cu[i + 1];
+  const int nn = end - base - 1;
+  if (nn < 0 || nn > a.K || base < 0 || end > a.max_rows) {  // uniform
+    if (tid < 64) fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
+    return;
+  }
+  // the window's nodes, one per lane of the first wavefront
+  int tok = -1, par = -2;
+  if (tid < 64 && lane < nn) {
+    tok = a.x[(size_t)i * a.ld_x + lane];
+    par = a.parent[(size_t)i * a.ld_x + lane];
+  }
+  if (tid < 64) {
+    const bool bad = __ballot(lane < nn && (tok < 0 || tok >= a.V)) != 0;
+    if (lane == 0) s_bad = bad;
+  }
+  __syncthreads();
+  if (s_bad) {  // uniform
+    if (tid < 64) fault_request(a, i, DSP_STATUS_TOKEN_RANGE);
+    return;
+  }
+  int32_t* orow = a.out + (size_t)i * (a.K + 1);
+  int cur = -1, depth = 0, am = 0;
+  while (true) {
+    const TT* p = (const TT*)a.tgt + (size_t)(base + 1 + cur) * a.ld_t;
+    am = (int)amax_index(row_argmax_key<TT>(p, a.V, smk));
+    if (tid < 64) {
+      const uint64_t m = __ballot(lane < nn && par == cur && tok == am);
+      if (lane == 0) s_next = (m && depth < a.K) ? __ffsll((unsigned long long)m) - 1 : -1;
+    }
+    __syncthreads();
+    const int j = s_next;
+    __syncthreads();  // everyone has read s_next before the next level rewrites it
+    if (j < 0) break;  // uniform
+    if (tid == j) orow[depth] = tok;  // lane j of the first wavefront holds node j
+    cur = j;
+    ++depth;
+  }
+  for (int k = depth + 1 + tid; k <= a.K; k += kWalkThreads) orow[k] = -1;
+  if (tid == 0) {
+    orow[depth] = am;
+    a.acc_len[i] = depth;
+    a.stop[i] = cur;
+  }
+}
+
 struct JobFrame {
   float t_hi, t_lo, d_hi, d_lo, cl;
   bool resid;
@@ -1293,6 +1386,10 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
 
 template <typename TT>
 void launch_greedy(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items, bool tree) {
+  if (tree) {
+    launch(DSP_K_VERIFY_STATS, verify_tree_walk_kernel<TT>, dim3(da.R), dim3(kWalkThreads), 0, s, da);
+    return;
+  }
   const long g = stats_grid(max_items);
   launch(DSP_K_VERIFY_STATS, verify_argmax_kernel<TT>, dim3((unsigned)g), dim3(kThreads), 0, s, sa);
   launch(DSP_K_VERIFY_DECIDE, tree ? verify_decide_tree : verify_decide_greedy, dim3(da.R), dim3(64), 0, s,
