@@ -151,9 +151,10 @@ def to_gpu_bf16_rows(bits):
     return to_gpu_bf16(bits)
 
 
-def test_tree_walk_matches_oracle():
-    rng = np.random.Generator(np.random.PCG64(31))
-    R, N, V = 6, 20, 5003
+@pytest.mark.parametrize("dt,V", [("bf16", 5003), ("f32", 5003), ("bf16", 40)])
+def test_tree_walk_matches_oracle(dt, V):
+    rng = np.random.Generator(np.random.PCG64(31 + V))
+    R, N = 6, 20
     tok = np.zeros((R, N), np.int32)
     par = np.zeros((R, N), np.int32)
     rows = []
@@ -177,17 +178,34 @@ def test_tree_walk_matches_oracle():
                 tok[i, j] = (tok[i, j] + 1) % V
             r[1 + cur, tok[i, j]] = 20.0
             cur = j
-        rows.append(workloads.f32_to_bf16_bits(r))
+        rows.append(workloads.f32_to_bf16_bits(r) if dt == "bf16" else r)
     tp = np.concatenate(rows)
     cu = np.concatenate([[0], np.cumsum(nn + 1)]).astype(np.int32)
-    from parity import to_gpu_bf16
-    g = dsp.verify_rejection(to_gpu_bf16(tp), to_gpu(cu), to_gpu(tok), parent=to_gpu(par), temperature=0.0)
+    print(f"tree walk R={R} N={N} V={V} dtype={dt}", flush=True)
+    g = dsp.verify_rejection(logits_to_gpu(tp, dt), to_gpu(cu), to_gpu(tok), parent=to_gpu(par), temperature=0.0)
+    torch.cuda.synchronize()
+    o = ov.verify_tree_greedy(values(tp, dt), cu, tok, par)
+    np.testing.assert_array_equal(host(g["accepted_len"]), o["accepted_len"])
+    np.testing.assert_array_equal(host(g["out_tokens"]), o["out_tokens"])
+    np.testing.assert_array_equal(host(g["stop_pos"]), o["stop_node"])
+    assert np.all(o["accepted_len"] >= 1)
+
+
+def test_tree_walk_ties_take_the_lowest_token():
+    """Rows of equal values: every arg-max is token 0, so the walk follows the chain of
+    children carrying token 0 (the first such child at each node) and the bonus is 0."""
+    R, N, V = 2, 6, 999
+    par = np.array([[-1, -1, 0, 0, 2, 4], [-1, 0, 1, -1, 3, 4]], np.int32)
+    tok = np.array([[5, 0, 0, 3, 0, 0], [0, 0, 7, 4, 1, 2]], np.int32)
+    tp = workloads.f32_to_bf16_bits(np.full((R * (N + 1), V), 0.25, np.float32))
+    cu = np.array([0, N + 1, 2 * (N + 1)], np.int32)
+    g = dsp.verify_rejection(logits_to_gpu(tp, "bf16"), to_gpu(cu), to_gpu(tok), parent=to_gpu(par), temperature=0.0)
     torch.cuda.synchronize()
     o = ov.verify_tree_greedy(values(tp, "bf16"), cu, tok, par)
     np.testing.assert_array_equal(host(g["accepted_len"]), o["accepted_len"])
     np.testing.assert_array_equal(host(g["out_tokens"]), o["out_tokens"])
     np.testing.assert_array_equal(host(g["stop_pos"]), o["stop_node"])
-    assert np.all(o["accepted_len"] >= 1)
+    assert host(g["accepted_len"]).tolist() == [1, 2]
 
 
 def test_fault_bits_from_bad_tokens_and_windows():
