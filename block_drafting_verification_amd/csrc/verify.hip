@@ -897,11 +897,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uin
 // Eight consecutive logits as raw 16-byte vectors (one for bf16, two for fp32).
 template <typename T> struct Raw8 {
   u32x4 w[sizeof(T) / 2];
-  __device__ __forceinline__ void load(const T* p) {
-#pragma unroll
-    for (int q = 0; q < (int)(sizeof(T) / 2); ++q) w[q] = __builtin_nontemporal_load((const u32x4*)p + q);
-  }
-  // non-temporal, as the plain loads: rows streamed once must not evict what the next
+  // non-temporal: rows streamed once must not evict what the next
   // kernels of the step read (without the hint the scheduler and pack of the next step
   // measured 2-3 us slower)
   __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -1209,7 +1205,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArg
 // Decisions, residual / bonus mass and the draw of one request in one workgroup of
 // kSampleThreads: the first wavefront decides (accepted prefix, outputs, the job of
 // the draw); all waves then stream the job's row(s) once -- a 16-byte vector of each
-// row per thread per block of kSampleGrain elements, kFinBatch blocks of loads in
+// row per thread per block of kSampleGrain elements, kFinBatch blocks (half for fp32) of loads in
 // flight -- adding each thread's weights per chunk of a.ce elements (a multiple of
 // the block, so blocks never straddle chunks); a wavefront sum per chunk goes to LDS,
 // and the draw proceeds from those chunk masses. No other workgroup is involved, so
