@@ -473,6 +473,11 @@ __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
   const bool blk = lane < a.K;
   int x = 0;
   if (blk) x = a.x[(size_t)i * a.ld_x + lane];
+  // the uniforms need only the round and the request id: drawn while the statistics load
+  uint64_t c[4] = {rnd, rid, (uint64_t)k, 0ull};
+  philox4x64_10(c, a.seed, 0ull);
+  const double u = unit_double(c[0]);
+  const double us = unit_double(c[1]);
   bool bad_d = false;
   double lse_d = 0.0;  // slots past the window hold no statistics: used only for positions
   if (blk) lse_d = merge_lse(a.dstats + ((size_t)i * a.K + lane) * a.nchd, a.nchd, &bad_d);
@@ -490,10 +495,6 @@ __device__ void decide_sampled(const DecideArgs& a, int i, Job* jout) {
   double lse_t = 0.0;
   if (pos || bon) lse_t = merge_lse(a.tstats + (size_t)(base + lane) * a.ncht, a.ncht, &bad);
   if (!pos) lse_d = 0.0;
-  uint64_t c[4] = {rnd, rid, (uint64_t)k, 0ull};
-  philox4x64_10(c, a.seed, 0ull);
-  const double u = unit_double(c[0]);
-  const double us = unit_double(c[1]);
   double lp2 = 0.0, lq2 = 0.0;
   bool acc = true;
   if (pos && !tokbad) {
