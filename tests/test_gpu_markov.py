@@ -330,3 +330,10 @@ def test_tree_tiny_vocabulary():
     """V = 5 (one 256-token block: three probe classes empty, no row bound)."""
     c = workloads.markov_case(3, 3, 5, rank=32, seed=43)
     _check_tree(c, 4, 4, 12)
+
+
+def test_tree_depth_one():
+    """D = 1: one expansion of the anchors (no probe pass, no row bound)."""
+    c = workloads.markov_case(5, 1, 4001, rank=64, seed=44)
+    _check_tree(c, 4, 4, 4)
+    _check_tree(c, 3, 2, 2, w_boost=200.0)

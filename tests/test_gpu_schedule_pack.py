@@ -117,7 +117,7 @@ def test_pack_flags_bad_window():
     assert int(host(g["status"])[0]) & dsp.DSP_STATUS_WINDOW_RANGE
 
 
-@pytest.mark.parametrize("R,K", [(1, 1), (7, 16), (64, 7), (256, 16), (2000, 4), (64, 128)])
+@pytest.mark.parametrize("R,K", [(1, 1), (7, 16), (64, 7), (256, 16), (2000, 4), (64, 128), (8192, 1)])
 def test_schedule_pack_one_call(R, K):
     """dsp_schedule_pack equals dsp_schedule_windows then dsp_pack_ragged, bit for bit, in every
     scheduler mode, with and without tiers; the windows and pack also against the oracle."""
