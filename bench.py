@@ -462,8 +462,8 @@ def bench_copy(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
-              "multi-GPU sharding in this build).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path is not "
+              "sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs the GPU"
