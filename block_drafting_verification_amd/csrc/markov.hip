@@ -239,6 +239,12 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     }
   }
   u32x4 ufr[KS] = {};  // B fragments, loaded straight into their registers
+  // the L k-step's B fragment: 1.0 (bf16) at k = this row's request within the block
+  u32x4 onehot = {0u, 0u, 0u, 0u};
+  if (MODE == MODE_TREE && rvalid) {
+    const int j = row / a.rows_per_req - r0 / a.rows_per_req - 8 * (lane >> 5);
+    if (j >= 0 && j < 8) onehot[j >> 1] = 0x3f80u << (16 * (j & 1));
+  }
   // issued like the ring's loads (the compiler would otherwise keep them "pending" around
   // the stage loop and drain the ring for them); the first stage's wait covers them
   auto load_u = [&]() {
@@ -258,6 +264,12 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
   const s32x4 ldesc = make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
                                 (uint32_t)(((size_t)(rlast / a.rows_per_req - req0) * a.ldL_r + a.V) * 2));
+  // Tree blocks spanning at most 16 requests add the base logits through the matrix
+  // cores: one extra k-step (A = the stage's 32 tokens x 16 requests of L, B = each
+  // row's one-hot request), issued first so z keeps its summation order, in place of
+  // unpacking a per-row L tile into the accumulators. The stage's L tile then holds one
+  // row per request, transposed (token-major, 32 bytes per token).
+  const bool lk = MODE == MODE_TREE && LAL && rlast / a.rows_per_req - req0 < 16;
   // Byte offsets of this thread's loads, less a per-stage term that is uniform over the
   // workgroup. Entries that are never valid (rank padding, spare threads, rows past the
   // block) start at kOOB; a stage past the range gets the term kOOB. Either way the sum
@@ -276,6 +288,10 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     const int rr = r0 + ((tid + q * kGT) >> 2);
     lofs[q] = rr < a.rows ? (uint32_t)(((size_t)(rr / a.rows_per_req - req0) * a.ldL_r + 8 * (tid & 3)) * 2)
                           : kOOB;
+    if (lk)  // request tid/4 of the block, 16-byte column tid%4; past the block's requests: zero
+      lofs[q] = q == 0 && tid < 64 && (tid >> 2) <= rlast / a.rows_per_req - req0
+                    ? (uint32_t)(((size_t)(tid >> 2) * a.ldL_r + 8 * (tid & 3)) * 2)
+                    : kOOB;
   }
   // Every thread issues the same LPS loads for every stage, including the stages past
   // its range: the count of loads in flight is then a constant the ring's waits can name.
@@ -318,6 +334,25 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         const int vv = e / NV, kv = e % NV;
         Ws[vv * NV + swz_w(vv, kv)] = rw[q];
       }
+    }
+    if (lk) {
+      // transposed: token t of request j at Lt[t * 16 + j]; every one of the 16 request
+      // columns is written (zeros past the block's requests), so no stale LDS contents
+      // meet the one-hot zeros. A non-finite entry is staged as the largest finite
+      // magnitude of its sign (a masked -inf as -max): a zero weight times an infinity
+      // would make NaN in every other request's sum.
+      if (tid < 64) {
+        uint16_t* Lt = (uint16_t*)Ls;
+        const int j = tid >> 2, c = tid & 3;
+        const u32x4 w = rl[0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint16_t h = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          if ((h & 0x7f80u) == 0x7f80u) h = (h & 0x8000u) || (h & 0x7fu) ? 0xff7fu : 0x7f7fu;
+          Lt[(8 * c + e) * 16 + j] = h;
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
@@ -524,7 +559,14 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       __syncthreads();
       load_stage(s + NR, ringw[rp], ringl[rp], ringu[rp]);
       const u32x4* Ws = lds + b * (WST + LST);
-      init_from_l(s, Ws + WST, acc[b]);
+      if (lk) {  // the base logits as the first k-step (accumulator from zero)
+        const bf16x8 al = __builtin_bit_cast(
+            bf16x8, *((const u32x4*)((const uint16_t*)(Ws + WST) + (lane & 31) * 16) + (lane >> 5)));
+        f32x16 zero = {};
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, __builtin_bit_cast(bf16x8, onehot), zero, 0, 0, 0);
+      } else {
+        init_from_l(s, Ws + WST, acc[b]);
+      }
       const int code0 = 16 * (s - 1);
       float tm = -INFINITY, ts = 0.f;  // tree: stage s-1 (discarded for s = 0)
 #pragma unroll
@@ -542,6 +584,15 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         }
       }
       if (MODE == MODE_TREE) {
+        if (lk) {  // tokens past V and rows past the block: -inf, as the per-row path starts them
+          const int v0 = (s_begin + s) * kTS;
+          if (!(v0 + kTS <= a.V && all_rows)) {  // uniform
+            const int vb = v0 + 4 * (lane >> 5);
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+              if (!(rvalid & (vb + 8 * (q >> 2) + (q & 3) < a.V))) acc[b][q] = -INFINITY;
+          }
+        }
 #pragma unroll
         for (int q = KS; q < 16; ++q) {  // ranks below 256: the remaining values
           tm = fmaxf(tm, acc[b ^ 1][q]);
