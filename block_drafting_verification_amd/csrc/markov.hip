@@ -1080,7 +1080,8 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
     if (pv && j == 0) {
       p_lse[p] = ((double)H + log2(S)) * kLn2d;
 #pragma unroll
-      for (int q = 0; q < kTopK; ++q) p_top[p][q] = ti[q];
+      for (int q = 0; q < kTopK; ++q)  // below -2^127: a masked entry (staged as -max)
+        p_top[p][q] = tv[q] < -0x1p127f ? -1 : ti[q];
     }
   }
   __syncthreads();
@@ -1090,7 +1091,7 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
     const bool cv = c < nc;
     const int p = cv ? c / a.topk : 0, rk = cv ? c % a.topk : 0;
     int v = p_top[p][rk];
-    if (cv && (v < 0 || v >= a.V)) {  // only reachable with non-finite scores
+    if (cv && (v < 0 || v >= a.V)) {  // fewer than topk finite entries, or non-finite scores
       if (r == 0) atomicOr(a.status, DSP_STATUS_NONFINITE);
     }
     if (v < 0 || v >= a.V) v = 0;

@@ -322,6 +322,9 @@ int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, i
 /* The selection reads each base-logit row once more up front (R*(D-1) rows) */
 /* to bound every parent row's 4th-largest z from below; entries under the   */
 /* bound cannot be among the top 4, so the outputs do not depend on it.      */
+/* A parent row with fewer than topk entries above -2^127 (masked -inf base  */
+/* logits count as absent) sets DSP_STATUS_NONFINITE; its children are then  */
+/* unspecified.                                                              */
 /* Limits: 1 <= topk <= min(4, V), 1 <= frontier <= 64, topk*frontier <= 256,  */
 /* 1 <= topN <= 1024, D*frontier <= 1024, rank as above.                      */
 /* ------------------------------------------------------------------------ */

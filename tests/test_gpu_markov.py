@@ -86,7 +86,7 @@ def test_chain_c4_full():
     _check_chain(c, want_logq=True)
 
 
-def _check_tree(c, topk, F, N, requests=None, w_boost=1.0):
+def _check_tree(c, topk, F, N, requests=None, w_boost=1.0, status=0):
     L, U, W = _f32(c)
     if w_boost != 1.0:
         c = dict(c, W=workloads.f32_to_bf16_bits(W * np.float32(w_boost)))
@@ -95,7 +95,7 @@ def _check_tree(c, topk, F, N, requests=None, w_boost=1.0):
     print(f"tree R={c['R']} D={c['B']} V={c['V']} k={topk} F={F} N={N}", flush=True)
     g = dsp.tree_expand(Lg, Ug, Wtg, ag, topk, F, N, want_mask=True)
     torch.cuda.synchronize()
-    assert int(host(g["status"])[0]) == 0
+    assert int(host(g["status"])[0]) == status
     gm = host(g["anc_mask"]).view(np.uint64)
     sel = list(range(c["R"])) if requests is None else list(requests)
     o = opt.tree_expand(L, U, W, c["anchors"], topk, F, N, requests=sel)
@@ -280,6 +280,21 @@ def test_chain_and_tree_masked_vocabulary():
     t = _check_tree(c, 4, 8, 16)
     nt = host(t["node_token"])
     assert not np.any(mask[nt[nt >= 0]])
+
+
+@pytest.mark.parametrize("R,F,depth", [(5, 16, 0), (40, 16, 0), (40, 16, 2), (5, 16, 2)])
+def test_tree_too_few_finite_entries_is_a_fault(R, F, depth):
+    """Request 0's base logits at one depth are masked but for two tokens, fewer than k = 4:
+    a fault (status bit) on both of the GEMM's paths -- blocks of at most 16 requests add the
+    base logits through the matrix cores (R = 5 at depth 1; 16 parents per request at depth
+    3), the others per row. Every other request still matches the oracle."""
+    c = workloads.markov_case(R, 3, 3001, rank=64, seed=100 + R + depth)
+    L = c["L"].copy()
+    keep = np.zeros(3001, dtype=bool)
+    keep[[17, 2900]] = True
+    L[0, depth, ~keep] = 0xFF80
+    c = dict(c, L=L)
+    _check_tree(c, 4, F, 24, requests=range(1, R), status=dsp.DSP_STATUS_NONFINITE)
 
 
 def _tree_exact(c, topk, F, N):
