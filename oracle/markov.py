@@ -16,8 +16,10 @@ and log q_d(y_d) = z_d[y_d] - logsumexp(z_d).
 
 Readings: the selection rule (stripped from the extracted text) is argmax, as
 the PCTree article states; the rank is a parameter (256 in the workloads). z is
-computed in fp64; the argmax decision is taken on z rounded to fp32, the
-precision the GPU path decides in, lowest token id on ties.
+computed in fp64 and the argmax is taken on those fp64 values, lowest token id
+on exact ties. An implementation that decides in lower precision may differ
+only where the winner and the runner-up are closer than its rounding error;
+``top2_margin`` reports that gap so a checker can recognise such near-ties.
 
 Sampled chain (the draft side of the full draft -> schedule -> pack -> verify
 cycle; SGLang article, "Ragged verify", and the notes' section 1: the verifier
@@ -57,9 +59,8 @@ def logsumexp_rows(z):
 
 
 def decide_argmax(z):
-    """argmax of each row of z rounded to fp32, lowest index on ties."""
-    z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
-    return np.argmax(z32, axis=-1)  # numpy returns the first maximal index
+    """argmax of each fp64 row of z, lowest index on ties."""
+    return np.argmax(np.asarray(z, dtype=np.float64), axis=-1)  # numpy returns the first maximal index
 
 
 def top2_margin(z):
@@ -137,10 +138,19 @@ def chain_sampled(L, U, W, anchor, temperature, seed=0, rnd=0, req_id=None, n_st
     Returns dict(y [R, n], logq [R, n] (of the oracle's own draw), logq_forced,
     zhat [R, n, V] fp64 values of the emitted bf16 rows, round_tie [R, n, V] bool
     (inputs within ROUND_BAND of a rounding midpoint), sample_margin [R, n]
-    (distance of u * total to the nearest CDF boundary over the total), tie_shift
-    [R, n] (bound on how far the CDF can move if the near-midpoint entries land
-    on another bf16 value -- up to one unit plus ROUND_BAND * max(1, |z|) away --
-    relative to the total)).
+    (distance of u * total to the nearest CDF boundary over the total), and the
+    bounds a checker needs when another implementation's emitted row differs at
+    those near-midpoint entries, each by at most dev_v = one unit + ROUND_BAND *
+    max(1, |z_v|):
+      eps [R, n]       = sum over tie entries of q_v * expm1(dev_v / T). Every weight
+                         w_v = exp(zhat_v / T) moves by a factor within exp(+-dev_v / T),
+                         so the total S moves by at most eps * S.
+      tie_shift [R, n] = 2 eps / (1 - eps): bound on the move of the normalised CDF at any
+                         point (|C'/S' - C/S| <= (|C' - C| + C |S' - S| / S) / S'), i.e. of
+                         the draw's margin; also bounds the L1 distance sum |q'_v - q_v|.
+      tok_dev [R, n]   = dev of the token the next step conditions on (its own draw, or
+                         the forced one), 0 if that entry is not a near-midpoint one: its
+                         probability moves by a factor within exp(+-(tok_dev / T + log(1/(1-eps)))).
     """
     L = np.asarray(L)
     R, B, V = L.shape
@@ -155,10 +165,13 @@ def chain_sampled(L, U, W, anchor, temperature, seed=0, rnd=0, req_id=None, n_st
     round_tie = np.zeros((R, n, V), dtype=bool)
     margin = np.zeros((R, n))
     shift = np.zeros((R, n))
+    eps = np.zeros((R, n))
+    tok_dev = np.zeros((R, n))
     prev = np.asarray(anchor, dtype=np.int64).copy()
     for d in range(n):
         z = markov_logits(L[:, d, :], U, W, prev)
         zh, gap, ulp = round_bf16(z)
+        devs = []
         zhat[:, d] = zh
         tie = gap < ROUND_BAND * np.maximum(1.0, np.abs(z))
         round_tie[:, d] = tie
@@ -174,11 +187,16 @@ def chain_sampled(L, U, W, anchor, temperature, seed=0, rnd=0, req_id=None, n_st
             logq[i, d] = s[v] - lse
             q = w / np.sum(w)
             # a near-midpoint entry computed in fp32 may land up to one unit plus the band away
-            dev = ulp[i, tie[i]] + ROUND_BAND * np.maximum(1.0, np.abs(z[i, tie[i]]))
-            shift[i, d] = 2.0 * float(np.sum(q[tie[i]] * np.expm1(dev / T)))
+            dev_row = np.where(tie[i], ulp[i] + ROUND_BAND * np.maximum(1.0, np.abs(z[i])), 0.0)
+            e = float(np.sum(q * np.expm1(dev_row / T)))
+            eps[i, d] = e
+            shift[i, d] = 2.0 * e / (1.0 - e) if e < 1.0 else np.inf
+            devs.append(dev_row)
         prev = y[:, d] if forced is None else np.asarray(forced, dtype=np.int64)[:, d]
+        for i in range(R):
+            tok_dev[i, d] = devs[i][prev[i]]
         logq_forced[:, d] = zh[np.arange(R), prev] / T - (
             np.max(zh / T, axis=-1) + np.log(np.sum(np.exp(zh / T - np.max(zh / T, axis=-1, keepdims=True)),
                                                    axis=-1)))
     return dict(y=y, logq=logq, logq_forced=logq_forced, zhat=zhat, round_tie=round_tie,
-                sample_margin=margin, tie_shift=shift)
+                sample_margin=margin, tie_shift=shift, eps=eps, tok_dev=tok_dev)

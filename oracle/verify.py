@@ -102,8 +102,10 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
 
     Returns dict(accepted_len [R], out_tokens [R, K+1] (-1 padded), stop_pos [R],
     ceiling [R] (drafts accepted over the whole window), p_x, q_x [R, K] (every
-    window position; 0 beyond the window and under greedy), accept_margin [R, K]
-    (|u - ratio|, +inf where not decided), sample_margin [R], agree [R] bool).
+    window position; 0 beyond the window and under greedy), ratio [R, K] (p/q at
+    x, 0 where not computed), accept_margin [R, K] (|u - ratio|, +inf where not
+    decided), sample_margin [R], resid_mass [R] (sum of max(0, p - q) at the stop
+    when the token there is a residual draw, 0 for a bonus draw), agree [R] bool).
     """
     tgt = np.asarray(tgt)
     drf = np.asarray(drf)
@@ -119,8 +121,10 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
     ceiling = np.zeros(R, dtype=np.int32)
     p_x = np.zeros((R, K), dtype=np.float64)
     q_x = np.zeros((R, K), dtype=np.float64)
+    ratio_out = np.zeros((R, K), dtype=np.float64)
     acc_margin = np.full((R, K), np.inf)
     smp_margin = np.full(R, np.inf)
+    resid_mass = np.zeros(R, dtype=np.float64)
     agree = np.ones(R, dtype=bool)
     for i in range(R):
         base = int(cu[i])
@@ -136,6 +140,7 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
                 p_x[i, k - 1] = np.exp(lp[x])
                 q_x[i, k - 1] = np.exp(lq[x])
                 ratio[k] = np.exp(lp[x] - lq[x])
+                ratio_out[i, k - 1] = ratio[k]
         stopped_at = None
         for k in range(1, n + 1):
             x = int(draft_tok[i, k - 1])
@@ -171,11 +176,14 @@ def verify_chain(tgt, cu_seqlens, drf, draft_tok, temperature, seed=0, rnd=0, re
             p = np.exp(log_softmax(tgt[base + k - 1], temperature))
             rejected = ceiling[i] + 1 <= c  # a rejection inside the commit window: residual draw
             q = np.exp(log_softmax(drf[i, k - 1], temperature)) if rejected else None
+            if rejected:
+                resid_mass[i] = float(np.sum(np.maximum(0.0, p - q)))
             v, mg = _sample(p, q, u_smp[i, k - 1])
             out[i, k - 1] = v
             smp_margin[i] = mg
     return dict(accepted_len=acc_len, out_tokens=out, stop_pos=stop, ceiling=ceiling, p_x=p_x, q_x=q_x,
-                accept_margin=acc_margin, sample_margin=smp_margin, agree=agree)
+                ratio=ratio_out, accept_margin=acc_margin, sample_margin=smp_margin, resid_mass=resid_mass,
+                agree=agree)
 
 
 def verify_tree_greedy(tgt, cu_seqlens, node_token, node_parent):

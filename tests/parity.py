@@ -58,15 +58,41 @@ class TieCounter:
             assert self.near <= 1, (self.near, self.decisions, self.notes[:5])
 
 
-def compare_chain_verify(gpu, orc_fn, R, K, windows, ties, p_rtol=1e-5, accept_band=None, sample_band=None):
+def rounding_bands(res, eps, tok_dev, T):
+    """Accept and draw bands of a verify whose draft rows may differ from the oracle's at
+    bf16 rounding near-ties (the sampled chain's emitted rows; oracle.markov.chain_sampled
+    gives eps and tok_dev per row and the bound derivations).
+
+    Accept at position k: ratio = p(x)/q(x) and q(x) moves by a factor within exp(+-eta),
+    eta = tok_dev / T + log(1 / (1 - eps)), so |ratio' - ratio| <= ratio * expm1(eta).
+    Residual draw at the stop k: sum_v |q'_v - q_v| <= dq = 2 eps / (1 - eps), hence every
+    residual CDF boundary and the target u' * sum(r) move by at most dq each, and the
+    decision stands while the oracle's relative margin exceeds 2 dq / sum(r).
+    A bonus draw reads the target rows only. The base bands cover the arithmetic itself.
+    Returns (accept_band [R, K], sample_band [R]).
+    """
+    e = np.minimum(np.asarray(eps, dtype=np.float64), 0.5)
+    eta = np.asarray(tok_dev, dtype=np.float64) / T - np.log1p(-e)
+    accept = ACCEPT_BAND + res["ratio"] * np.expm1(eta)
+    dq = 2.0 * e / (1.0 - e)
+    R = dq.shape[0]
+    sample = np.full(R, SAMPLE_BAND)
+    for i in range(R):
+        k = int(res["stop_pos"][i])
+        if res["resid_mass"][i] > 0:
+            sample[i] += 2.0 * dq[i, k - 1] / res["resid_mass"][i]
+    return accept, sample
+
+
+def compare_chain_verify(gpu, orc_fn, R, K, windows, ties, p_rtol=1e-5, draft_bounds=None):
     """Compare a sampled / greedy chain verify result against the oracle with replay.
 
     orc_fn(forced_len) -> oracle result dict. The oracle is first run on its own;
     where the accepted length differs, the disagreement must be a counted accept
     near-tie and the oracle is replayed along the GPU's decisions to check the
-    drawn token. accept_band [R, K] / sample_band [R] (optional) widen the bands
-    per decision where the inputs themselves may differ slightly between the two
-    sides (draft rows with bf16 rounding near-ties).
+    drawn token. draft_bounds = (eps, tok_dev, T) (optional) widens the bands per
+    decision by ``rounding_bands`` where the draft rows themselves may differ
+    slightly between the two sides.
     """
     acc = host(gpu["accepted_len"]).astype(np.int64)
     toks = host(gpu["out_tokens"]).astype(np.int64)
@@ -74,6 +100,11 @@ def compare_chain_verify(gpu, orc_fn, R, K, windows, ties, p_rtol=1e-5, accept_b
     rep = own
     if np.any(acc != own["accepted_len"]):
         rep = orc_fn(acc)
+    if draft_bounds is None:
+        accept_band, sample_band = np.full((R, K), ACCEPT_BAND), np.full(R, SAMPLE_BAND)
+    else:
+        accept_band, _ = rounding_bands(own, *draft_bounds)
+        _, sample_band = rounding_bands(rep, *draft_bounds)
     for i in range(R):
         n = int(windows[i])
         decided = min(n, int(own["accepted_len"][i]) + 1)
@@ -81,7 +112,7 @@ def compare_chain_verify(gpu, orc_fn, R, K, windows, ties, p_rtol=1e-5, accept_b
         if acc[i] != own["accepted_len"][i]:
             k = int(min(acc[i], own["accepted_len"][i])) + 1  # first differing decision
             m = own["accept_margin"][i, k - 1]
-            band = ACCEPT_BAND if accept_band is None else max(ACCEPT_BAND, accept_band[i, k - 1])
+            band = accept_band[i, k - 1]
             assert m < band, f"request {i}: accepted {acc[i]} vs oracle {own['accepted_len'][i]} (margin {m})"
             ties.near += 1
             ties.notes.append(("accept", i, k, m))
@@ -89,7 +120,7 @@ def compare_chain_verify(gpu, orc_fn, R, K, windows, ties, p_rtol=1e-5, accept_b
         np.testing.assert_array_equal(toks[i, :acc[i]], r["out_tokens"][i, :acc[i]])
         if toks[i, acc[i]] != r["out_tokens"][i, acc[i]]:
             m = r["sample_margin"][i]
-            band = SAMPLE_BAND if sample_band is None else max(SAMPLE_BAND, sample_band[i])
+            band = sample_band[i]
             assert m < band, f"request {i}: drawn token {toks[i, acc[i]]} vs {r['out_tokens'][i, acc[i]]} (margin {m})"
             ties.near += 1
             ties.notes.append(("sample", i, m))

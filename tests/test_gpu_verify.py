@@ -359,3 +359,32 @@ def test_masked_vocabulary_entries():
         toks = host(g["out_tokens"])
         assert not np.any(mask[toks[toks >= 0]]), "a masked token was drawn"
     ties.check()
+
+
+def test_scheduled_workload_static_full_windows():
+    """The static run of the scheduled ragged verify workload: 256 requests x 16 full windows,
+    8,448 packed target rows of V=151,936 bf16 (2.567 GB with the draft rows); every request
+    checked against the oracle (float32 values are passed: bf16 widens exactly)."""
+    c = workloads.scheduled_verify()
+    R, K, V = c["R"], c["K"], c["V"]
+    w = np.full(R, K)
+    tp = c["t"].reshape(R * (K + 1), V)
+    cu = cu_from_windows(w)
+    xg = to_gpu(c["x"].astype(np.int32))
+    print(f"static verify R={R} K={K} V={V} packed rows={tp.shape[0]}", flush=True)
+    rq = to_gpu(np.repeat(np.arange(R, dtype=np.int32), K + 1))
+    rp = to_gpu(np.tile(np.arange(K + 1, dtype=np.int32), R))
+    g = dsp.verify_rejection(logits_to_gpu(tp, "bf16"), to_gpu(cu), xg, drf=logits_to_gpu(c["d"], "bf16"),
+                             temperature=1.0, seed=0, round=4, row_req=rq, row_pos=rp)
+    torch.cuda.synchronize()
+    assert int(host(g["status"])[0]) == 0
+    tv = values(tp, "bf16")
+    dv = values(c["d"], "bf16")
+
+    def orc(forced):
+        return ov.verify_chain(tv, cu, dv, c["x"], 1.0, seed=0, rnd=4, forced_len=forced)
+    ties = TieCounter()
+    compare_chain_verify(g, orc, R, K, w, ties)
+    ties.check()
+    acc = host(g["accepted_len"])
+    print("static verify: mean accepted", acc.mean(), "near ties", ties.near, "of", ties.decisions)

@@ -4,6 +4,7 @@ import math
 import os
 
 import numpy as np
+import pytest
 
 import workloads
 from oracle import markov as om
@@ -41,7 +42,7 @@ def test_chain_conditions_on_previous_choice():
     prev = anchors
     for d in range(6):
         z = om.markov_logits(L[:, d], U, W, prev)
-        np.testing.assert_array_equal(np.argmax(z.astype(np.float32), -1), res["y"][:, d])
+        np.testing.assert_array_equal(np.argmax(z, -1), res["y"][:, d])
         prev = res["y"][:, d]
     # and differs from conditioning on the anchor at every step
     z0 = om.markov_logits(L[:, 3], U, W, anchors)
@@ -85,7 +86,7 @@ def test_forced_replay_is_step_local():
     rep = om.chain(L, U, W, anchors, forced=forced)
     np.testing.assert_array_equal(rep["y"][:, :2], own[:, :2])
     z = om.markov_logits(L[:, 2], U, W, forced[:, 1])
-    np.testing.assert_array_equal(rep["y"][:, 2], np.argmax(z.astype(np.float32), -1))
+    np.testing.assert_array_equal(rep["y"][:, 2], np.argmax(z, -1))
 
 
 # ---------------------------------------------------------------- sampled chain
@@ -195,3 +196,117 @@ def test_masked_logits_carry_no_mass():
     Wg[:, 2] = 10.0
     g = om.chain(L, Ug, Wg, np.zeros(R, dtype=np.int64))
     assert not np.any(g["y"] == 2)
+
+
+def test_argmax_decides_on_fp64_values():
+    """Two entries equal in fp32 but not in fp64: the argmax follows the fp64 values."""
+    L = np.zeros((1, 1, 4), dtype=np.float64)
+    L[0, 0, 1] = 1.0
+    L[0, 0, 3] = 1.0 + 2.0 ** -40  # rounds to 1.0 in fp32
+    assert np.float32(L[0, 0, 3]) == np.float32(1.0)
+    U = np.zeros((4, 32))
+    W = np.zeros((32, 4))
+    res = om.chain(L, U, W, np.zeros(1, dtype=np.int64), want_margin=True)
+    assert res["y"][0, 0] == 3
+    assert res["margin"][0, 0] == 2.0 ** -40
+    # exact ties go to the lowest id
+    L[0, 0, 3] = 1.0
+    assert om.chain(L, U, W, np.zeros(1, dtype=np.int64))["y"][0, 0] == 1
+
+
+def _tie_rows(R, V, seed, T, frac=0.5):
+    """Base logits sitting within ROUND_BAND of a bf16 rounding midpoint at a fraction of the
+    entries (the rest ordinary), no Markov term: z = L exactly."""
+    rng = np.random.default_rng(seed)
+    vals = rng.normal(0.0, 2.0, (R, V))
+    zh, _, ulp = om.round_bf16(vals)
+    mid = zh + 0.5 * ulp * np.where(rng.random((R, V)) < 0.5, 1.0, -1.0)
+    off = (rng.random((R, V)) - 0.5) * 1e-6 * np.maximum(1.0, np.abs(mid))
+    near = rng.random((R, V)) < frac
+    L = np.where(near, mid + off, vals)[:, None, :]
+    return L
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_rounding_tie_bounds_hold_under_perturbation(T):
+    """The bounds chain_sampled reports for rows whose near-midpoint entries may land one unit
+    (plus the band) away, checked against explicit perturbations of those entries (random
+    points and the corners of the allowed box): the CDF and L1 moves stay within tie_shift,
+    and the drawn token's log-probability within tok_dev / T + log(1 / (1 - eps))."""
+    R, V = 12, 48
+    L = _tie_rows(R, V, 3, T)
+    U, W = np.zeros((V, 32)), np.zeros((32, V))
+    res = om.chain_sampled(L, U, W, np.zeros(R, dtype=np.int64), T, seed=4)
+    assert res["round_tie"].sum() > R * V // 4
+    z = L[:, 0, :]
+    zh = res["zhat"][:, 0, :]
+    tie = res["round_tie"][:, 0, :]
+    _, _, ulp = om.round_bf16(z)
+    dev = np.where(tie, ulp + om.ROUND_BAND * np.maximum(1.0, np.abs(z)), 0.0)
+    rng = np.random.default_rng(9)
+    worst = 0.0
+    for i in range(R):
+        x = int(res["y"][i, 0])
+        q = np.exp(zh[i] / T - np.max(zh[i] / T))
+        q /= q.sum()
+        F = np.cumsum(q)
+        for trial in range(200):
+            s = rng.choice([-1.0, 1.0], V) if trial % 2 else rng.uniform(-1.0, 1.0, V)
+            zp = zh[i] + s * dev[i]
+            qp = np.exp(zp / T - np.max(zp / T))
+            qp /= qp.sum()
+            cdf_move = np.max(np.abs(np.cumsum(qp) - F))
+            l1 = np.sum(np.abs(qp - q))
+            assert cdf_move <= res["tie_shift"][i, 0] * (1 + 1e-9)
+            assert l1 <= res["tie_shift"][i, 0] * (1 + 1e-9)
+            lq_move = abs(np.log(qp[x]) - np.log(q[x]))
+            assert lq_move <= res["tok_dev"][i, 0] / T - np.log1p(-res["eps"][i, 0]) + 1e-12
+            worst = max(worst, cdf_move / res["tie_shift"][i, 0])
+    assert worst > 0.2  # the bound is not vacuous on these rows
+
+
+def test_verify_bands_keep_decisions_under_draft_rounding_ties():
+    """A verify whose draft rows are perturbed within the rounding-tie box makes the oracle's
+    decisions wherever the oracle's margin exceeds the band derived from eps and tok_dev
+    (accept: ratio * expm1(eta); residual draw: 2 dq / sum(r)); many rounds of uniforms."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from parity import rounding_bands
+    from oracle import verify as ov
+    T, R, K, V = 1.0, 6, 3, 40
+    rng = np.random.default_rng(21)
+    Ld = np.concatenate([_tie_rows(R, V, 30 + k, T, frac=0.1) for k in range(K)], axis=1)  # [R, K, V]
+    U, W = np.zeros((V, 32)), np.zeros((32, V))
+    # per position one sampled chain step over that position's rows (no Markov term)
+    od = [om.chain_sampled(Ld[:, k:k + 1], U, W, np.zeros(R, dtype=np.int64), T, seed=5) for k in range(K)]
+    zhat = np.concatenate([o["zhat"] for o in od], axis=1)
+    x = np.concatenate([o["y"] for o in od], axis=1)
+    eps = np.concatenate([o["eps"] for o in od], axis=1)
+    tok_dev = np.concatenate([o["tok_dev"] for o in od], axis=1)
+    tie = np.concatenate([o["round_tie"] for o in od], axis=1)
+    _, _, ulp = om.round_bf16(Ld)
+    dev = np.where(tie, ulp + om.ROUND_BAND * np.maximum(1.0, np.abs(Ld)), 0.0)
+    # target rows close to the draft's so that acceptance is frequent and residuals small
+    tgt = np.concatenate([np.concatenate([zhat[i] + rng.normal(0, 0.8, (K, V)), rng.normal(0, 2, (1, V))])
+                          for i in range(R)])
+    cu = np.arange(R + 1) * (K + 1)
+    checked, resid = 0, 0
+    for trial in range(6):
+        s = rng.choice([-1.0, 1.0], zhat.shape) if trial % 2 else rng.uniform(-1.0, 1.0, zhat.shape)
+        zp = zhat + s * dev
+        for rnd in range(40):
+            own = ov.verify_chain(tgt, cu, zhat, x, T, seed=1, rnd=rnd)
+            alt = ov.verify_chain(tgt, cu, zp, x, T, seed=1, rnd=rnd)
+            acc_band, _ = rounding_bands(own, eps, tok_dev, T)
+            for i in range(R):
+                a = int(own["accepted_len"][i])
+                decided = range(min(K, a + 1))
+                if all(own["accept_margin"][i, k] >= acc_band[i, k] for k in decided):
+                    assert alt["accepted_len"][i] == a
+                    _, smp_band = rounding_bands(own, eps, tok_dev, T)
+                    if own["sample_margin"][i] >= smp_band[i]:
+                        assert alt["out_tokens"][i, a] == own["out_tokens"][i, a]
+                        checked += 1
+                        resid += int(own["resid_mass"][i] > 0)
+    print("checked", checked, "residual draws", resid)
+    assert checked > 500 and resid > 100

@@ -115,3 +115,98 @@ def test_ancestor_masks_popcount_is_depth_and_closed():
             if p >= 0:
                 assert int(m[i, j, 0]) == int(m[i, p, 0]) | (1 << j)
         assert np.all(m[i, int(t["n_nodes"][i]):] == 0)
+
+
+def _as_prefer(t):
+    return t["node_token"], t["node_parent"], t["n_nodes"]
+
+
+def test_replay_of_own_tree_changes_nothing():
+    L, U, W, a = _case(3, 6, 400, seed=11, boost=200)
+    own = opt.tree_expand(L, U, W, a, 4, 8, 24)
+    rep = opt.tree_expand(L, U, W, a, 4, 8, 24, prefer=_as_prefer(own))
+    for k in ("node_token", "node_parent", "node_depth", "n_nodes"):
+        np.testing.assert_array_equal(rep[k], own[k])
+    np.testing.assert_array_equal(rep["node_score"], own["node_score"])
+    assert np.all(rep["replays"] == 0)
+    assert np.all(rep["decisions"] > 6)
+
+
+def _planted_topk_tie(delta):
+    """One request, depth 3, no Markov term: at depth 1 tokens 5 and 9 sit at the top-2 cut
+    (k = 2) with z differing by delta; token 5 ranks first at every depth otherwise."""
+    V, D = 64, 3
+    rng = np.random.default_rng(3)
+    L = rng.normal(0.0, 1.0, (1, D, V))
+    L[0, 0, 1] = 4.0
+    L[0, 0, 5] = 3.0 + delta
+    L[0, 0, 9] = 3.0
+    U, W = np.zeros((V, 32)), np.zeros((32, V))
+    return L, U, W, np.array([0])
+
+
+def test_replay_takes_the_other_branch_at_a_planted_near_tie():
+    """The oracle keeps token 5 (z larger by 1e-9); a tree built with token 9 instead (the
+    rounding could have gone either way) is reproduced exactly by the replay, one near-tie."""
+    L, U, W, a = _planted_topk_tie(1e-9)
+    own = opt.tree_expand(L, U, W, a, 2, 4, 12)
+    assert 5 in own["node_token"][0, own["node_depth"][0] == 1]
+    L2 = L.copy()
+    L2[0, 0, 5] = 3.0 - 1e-9
+    other = opt.tree_expand(L2, U, W, a, 2, 4, 12)
+    assert 9 in other["node_token"][0, other["node_depth"][0] == 1]
+    rep = opt.tree_expand(L, U, W, a, 2, 4, 12, prefer=_as_prefer(other))
+    for k in ("node_token", "node_parent", "node_depth", "n_nodes"):
+        np.testing.assert_array_equal(rep[k], other[k])
+    np.testing.assert_allclose(rep["node_score"], other["node_score"], atol=1e-8)
+    assert rep["replays"][0] >= 1
+
+
+def test_replay_refuses_a_branch_outside_the_band():
+    """The same plant with a gap of 1e-3: the other tree's choice is no near-tie, so the
+    replay keeps the oracle's own tree (a checker comparing against it then fails)."""
+    L, U, W, a = _planted_topk_tie(1e-3)
+    own = opt.tree_expand(L, U, W, a, 2, 4, 12)
+    L2 = L.copy()
+    L2[0, 0, 5] = 3.0 - 1e-3
+    other = opt.tree_expand(L2, U, W, a, 2, 4, 12)
+    assert not np.array_equal(own["node_token"], other["node_token"])
+    rep = opt.tree_expand(L, U, W, a, 2, 4, 12, prefer=_as_prefer(other))
+    np.testing.assert_array_equal(rep["node_token"], own["node_token"])
+    assert rep["replays"][0] == 0
+
+
+def test_replay_at_a_planted_frontier_near_tie():
+    """k = 3, F = 2: at depth 1 the 2nd and 3rd children's path scores differ by 1e-10 only;
+    the replay follows whichever of the two the preferred tree kept."""
+    V, D = 50, 3
+    rng = np.random.default_rng(8)
+    L = rng.normal(0.0, 1.0, (1, D, V))
+    L[0, 0, 2] = 5.0
+    L[0, 0, 7] = 4.0 + 1e-10
+    L[0, 0, 30] = 4.0
+    U, W = np.zeros((V, 32)), np.zeros((32, V))
+    a = np.array([0])
+    own = opt.tree_expand(L, U, W, a, 3, 2, 6)
+    d1 = set(own["node_token"][0, own["node_depth"][0] == 1].tolist())
+    assert d1 == {2, 7}
+    L2 = L.copy()
+    L2[0, 0, 7] = 4.0 - 1e-10
+    other = opt.tree_expand(L2, U, W, a, 3, 2, 6)
+    assert set(other["node_token"][0, other["node_depth"][0] == 1].tolist()) == {2, 30}
+    rep = opt.tree_expand(L, U, W, a, 3, 2, 6, prefer=_as_prefer(other))
+    for k in ("node_token", "node_parent", "node_depth"):
+        np.testing.assert_array_equal(rep[k], other[k])
+    assert rep["replays"][0] >= 1
+
+
+def test_topk_decides_on_fp64_values():
+    """Two tokens equal in fp32 but not in fp64 at the top-1 cut: the larger fp64 value wins."""
+    z = np.zeros(10)
+    z[3] = 1.0
+    z[8] = 1.0 + 2.0 ** -40
+    top, gap, _ = opt._topk_tokens(z, 1)
+    assert list(top) == [8] and abs(gap - 2.0 ** -40) < 2.0 ** -70
+    z[8] = 1.0
+    top, _, _ = opt._topk_tokens(z, 1)
+    assert list(top) == [3]

@@ -296,3 +296,15 @@ def test_cap_accept_ceiling_is_the_full_block_verify(seed, T):
     wide = ov.verify_chain(tp, cu, d, x, T, seed=2, rnd=1, cap=np.full(len(cap), 99))
     for key in ("accepted_len", "out_tokens", "stop_pos"):
         np.testing.assert_array_equal(wide[key], static[key])
+
+
+def test_scheduled_tv_fixture_is_current():
+    """The stored total-variation distances behind the scheduled workload's confidences match
+    the oracle's fp64 softmax on sampled (request, position) pairs of the current logits."""
+    import workloads
+    from oracle.calibrate_scheduled_verify import tv_table
+    c = workloads.scheduled_verify(R=256, K=16)
+    sub = dict(c, R=3, t=c["t"][[0, 100, 255]], d=c["d"][[0, 100, 255]])
+    tv = tv_table(sub)
+    np.testing.assert_allclose(tv, c["tv"][[0, 100, 255]], atol=1e-6)
+    assert np.all((c["tv"] >= 0) & (c["tv"] <= 1))

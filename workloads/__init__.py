@@ -21,9 +21,11 @@ Recipes (N(m, s) = normal with mean m and standard deviation s):
   mean one-token acceptance is about 0.8).
 * scheduled ragged verify: R=256, K=16, V=151,936, bf16; t as the dense-vocab verify; a noise
   scale sigma_i ~ U(0.2, 2.0) per request (easy and hard streams);
-  d = t + sigma_i * eps; confidence c_{i,k} = sigmoid(4 - 2.5 sigma_i + 0.25 eta),
-  eta ~ N(0, 1) (a logistic model of the draft-target gap); additive cost table
-  c(n) = 1.0 + 0.05 n.
+  d = t + sigma_i * eps; confidence c_{i,k} = sigmoid(4 - 8 TV_{i,k} + 0.25 eta),
+  eta ~ N(0, 1), a logistic model of the draft-target gap measured as the total-variation
+  distance between the target and draft distributions of the position (TV from
+  scheduled_tv.json, written by the oracle's calibration script: this module computes no
+  softmax); additive cost table c(n) = 1.0 + 0.05 n.
 * Markov chain: R=256, B=16, V=151,936, rank 256; L ~ N(0, 3) bf16;
   U [V, r], W [r, V] ~ N(0, 0.02) bf16; anchors uniform over the vocabulary.
 * PCTree + tree verify: R=128, D=16, V=129,280, rank 256, k=4, F=16, N=64;
@@ -45,6 +47,7 @@ Recipes (N(m, s) = normal with mean m and standard deviation s):
 Draft tokens x_{i,k} are the synthetic draft model's samples from softmax(d/T)
 (Gumbel-max with this module's own noise), or argmax d when T = 0.
 """
+import hashlib
 import json
 import os
 
@@ -146,23 +149,46 @@ def dense_verify(sigma=None):
 
 
 def scheduled_verify_inputs(R=256, K=16, V=V_QWEN3):
-    """Confidences, cost table and per-request noise scales of the scheduled verify (no logits)."""
+    """Cost table, per-request noise scales, confidence noise and anchors of the scheduled
+    verify (no logits, no confidences)."""
     rng = _rng(2003)
     sig = rng.uniform(0.2, 2.0, size=R).astype(np.float32)
     eta = rng.standard_normal((R, K))
-    z = 4.0 - 2.5 * sig[:, None].astype(np.float64) + 0.25 * eta
-    conf = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
     cost = 1.0 + 0.05 * np.arange(R * K + 1, dtype=np.float64)
-    return dict(conf=conf, cost=cost, sigma_i=sig,
+    return dict(cost=cost, sigma_i=sig, eta=eta,
                 anchors=_rng(3003).integers(0, V, size=R).astype(np.int32))
 
 
-def scheduled_verify(R=256, K=16, V=V_QWEN3):
-    """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table."""
+def scheduled_logits_hash(c):
+    h = hashlib.sha256()
+    h.update(np.ascontiguousarray(c["t"]).tobytes())
+    h.update(np.ascontiguousarray(c["d"]).tobytes())
+    return h.hexdigest()[:16]
+
+
+def scheduled_confidences(eta, tv):
+    """c_{i,k} = sigmoid(4 - 8 TV_{i,k} + 0.25 eta_{i,k}) as float32."""
+    z = 4.0 - 8.0 * np.asarray(tv, dtype=np.float64) + 0.25 * eta
+    return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+
+
+def scheduled_verify(R=256, K=16, V=V_QWEN3, with_conf=True):
+    """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table.
+
+    The confidences need the total-variation distances of the logits, which this module does
+    not compute: they are read from scheduled_tv.json (written by the oracle's calibration
+    script for exactly these logits; the stored hash is checked)."""
     s = scheduled_verify_inputs(R, K, V)
     c = verify_case(R, K, V, dtype="bf16", seed=1003, t_sigma=3.0, boost_p=0.01, boost=8.0,
                     d_sigma=s["sigma_i"])
     c.update(s)
+    if with_conf:
+        with open(os.path.join(_HERE, "scheduled_tv.json")) as f:
+            tvj = json.load(f)
+        assert (tvj["R"], tvj["K"]) == (R, K) and tvj["logits_sha256"] == scheduled_logits_hash(c), \
+            "scheduled_tv.json was computed for other logits: rerun python -m oracle.calibrate_scheduled_verify"
+        c["tv"] = np.asarray(tvj["tv"], dtype=np.float64)
+        c["conf"] = scheduled_confidences(s["eta"], c["tv"])
     return c
 
 
