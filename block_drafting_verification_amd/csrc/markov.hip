@@ -98,6 +98,14 @@ template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// A register written by an asynchronous load is only tied to the load statement: plain
+// arithmetic that reads it (bit tests, shifts, packing) could legally be scheduled above
+// the vm_wait that covers the load, since the wait names no register. Passing the
+// register through an empty volatile statement right after the wait makes every later
+// reader depend on that statement, and volatile statements keep their program order, so
+// no reader can move above the wait. It emits no instruction.
+__device__ __forceinline__ void landed(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void landed(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 struct ChainPart {  // per (group, row)
   uint64_t key;     // arg-max key of z (fp32), lowest id on ties
@@ -554,6 +562,21 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       const int rp = p % NR;
       // stage s is the oldest of the NR stages in flight: wait for its loads only
       vm_wait<(NR - 1) * LPS>();
+      if constexpr (AS) {  // what this wait covers: stage s of the ring (and, at s = 0, the U rows)
+#pragma unroll
+        for (int q = 0; q < WQ; ++q) landed(ringw[rp][q]);
+#pragma unroll
+        for (int q = 0; q < LQ; ++q) {
+          if constexpr (LAL) {
+            landed(ringl[rp][q]);
+          } else {
+#pragma unroll
+            for (int l = 0; l < 8; ++l) landed(ringu[rp][q][l]);
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) landed(ufr[ks]);
+      }
       // buffer b was last read two stages ago, before the previous barrier
       store_stage(b, ringw[rp], ringl[rp], ringu[rp]);
       __syncthreads();

@@ -1384,7 +1384,7 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
 template <typename TT>
 void launch_greedy(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, long max_items, bool tree) {
   if (tree) {
-    launch(DSP_K_VERIFY_STATS, verify_tree_walk_kernel<TT>, dim3(da.R), dim3(kWalkThreads), 0, s, da);
+    launch(DSP_K_VERIFY_DECIDE, verify_tree_walk_kernel<TT>, dim3(da.R), dim3(kWalkThreads), 0, s, da);
     return;
   }
   const long g = stats_grid(max_items);

@@ -80,7 +80,7 @@ def test_schedule_top_m_and_threshold(R, K):
 
 
 def test_schedule_c3_workload():
-    c = workloads.scheduled_verify_inputs()
+    c = workloads.scheduled_verify_schedule_inputs()
     for th in (0.3, 0.6):
         _sched(c["conf"], c["cost"], osch.MODE_THRESHOLD, threshold=th)
     o = _sched(c["conf"], c["cost"])

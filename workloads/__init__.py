@@ -172,6 +172,18 @@ def scheduled_confidences(eta, tv):
     return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
 
 
+def scheduled_verify_schedule_inputs(R=256, K=16, V=V_QWEN3):
+    """The scheduled verify's scheduler inputs (confidences from the stored TV table, cost
+    table, anchors) without generating its logits; the full loader checks the table's hash."""
+    s = scheduled_verify_inputs(R, K, V)
+    with open(os.path.join(_HERE, "scheduled_tv.json")) as f:
+        tvj = json.load(f)
+    assert (tvj["R"], tvj["K"]) == (R, K)
+    s["tv"] = np.asarray(tvj["tv"], dtype=np.float64)
+    s["conf"] = scheduled_confidences(s["eta"], s["tv"])
+    return s
+
+
 def scheduled_verify(R=256, K=16, V=V_QWEN3, with_conf=True):
     """Confidence-scheduled ragged verify: mixed easy/hard streams, additive cost table.
 
