@@ -1,27 +1,36 @@
 #!/usr/bin/env python3
 """Benchmark of the hot path on one MI355X.
 
-Default workload (the metric's configuration): dense-vocab verify -- 64
-requests, block K=7, vocabulary 151,936, bf16 logits, full-block windows,
-temperature 1. One step is one pass of the whole path over that batch:
-survival products + window selection (a flat step-time table makes every
-window the full block), ragged pack, and the rejection verify (row statistics,
-decisions, residual sums, inverse-CDF draws). Inputs are generated on the host
-from fixed seeds, copied to HBM before timing, and reused for every step (the
-Philox round changes per step).
+Default workload (the largest configuration that fits one GPU): the
+confidence-scheduled ragged verify -- 256 requests, block K=16, vocabulary
+151,936, bf16 logits, per-request draft noise scales from U(0.2, 2.0), per-position
+confidences from a logistic model of the draft-target total-variation distance,
+additive step-time table c(n) = 1 + 0.05 n. One step is one pass of the whole path
+over that batch: survival products, window selection and the ragged pack (one
+launch), then the rejection verify of the packed windows (row statistics,
+decisions, residual sums, inverse-CDF draws). A sub-record times the static run
+of the same data (every window the full block: 8,448 logit rows, 2.567 GB).
 
 Other workloads (--workload):
-  scheduled-verify  confidence-scheduled ragged verify (256 x 16, mixed easy/hard streams)
+  dense-verify      64 requests x K=7 x V=151,936, full-block windows
   markov-chain      Markov-head greedy chain (256 requests x 16 steps, rank 256)
   pctree            PCTree expansion (128 x depth 16, k=4, F=16, N=64) + greedy tree verify
-  cycle             sampled Markov draft (256 x 16, emitting its bf16 rows) -> confidence head -> schedule
-                    -> pack -> verify
+  cycle             sampled Markov draft (256 x 16, emitting its bf16 rows) -> confidence head
+                    -> schedule -> pack -> verify
   copy              1 GiB device copy (reference for scaling HBM counters)
 
-Prints ONE JSON line. `roofline` covers the dominant kernel of the workload,
-timed with HIP events recorded by libdsp on the launch stream during the timed
-region; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-batch (rank 0, N=1 only).
+Timing: inputs are resident in HBM before the timed region. Each timed step is
+preceded (outside its timed interval) by a 512 MiB store pass over a scratch buffer,
+so the 256 MB Infinity Cache and the L2s hold nothing of the step's inputs; the step
+time is the sum of HIP-event intervals around the steps on their stream. The value
+comes from replays of one captured HIP graph per step (or eager launches if faster).
+`roofline` covers the dominant kernel, its per-launch time taken from HIP events
+that libdsp attaches to each dispatch on the launch stream during the eager pass.
+`cpu_baseline` times the CPU oracle (the plain fp64 numpy implementation) on a bounded
+sample of the same batch, over worker processes on the host's cores; it runs before
+the GPU is touched, so the workers are forked from a process with no GPU state.
+
+Prints ONE JSON line.
 """
 import argparse
 import hashlib
@@ -35,6 +44,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FLUSH_BYTES = 512 << 20     # store pass between timed steps (2x the Infinity Cache)
+MAX_CPU_WORKERS = 16        # host cores given to one GPU
 
 
 def parse():
@@ -42,11 +53,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense-verify",
-                    choices=["dense-verify", "scheduled-verify", "markov-chain", "pctree", "cycle", "copy"])
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", default="scheduled-verify",
+                    choices=["scheduled-verify", "dense-verify", "markov-chain", "pctree", "cycle", "copy"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the parallel oracle sample")
+    ap.add_argument("--cpu-single-seconds", type=float, default=4.0, help="wall budget of the 1-core sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prof-all", action="store_true", help="time every kernel with events (diagnostic)")
+    ap.add_argument("--no-flush", action="store_true", help="diagnostic: no cache flush between timed steps")
     return ap.parse_args()
 
 
@@ -70,27 +82,97 @@ def traffic_from_profiles(kernel_file, kernel_name, workload):
     return rec.get("bytes_per_launch")
 
 
-def run_phases(make_step, steps, warmup, dominant, prof_all=False):
-    """Time a step eagerly (HIP events around the dominant kernels only) and as a replayed HIP graph.
+# ---------------------------------------------------------------- CPU baseline (oracle)
+# Worker processes are forked before this process touches the GPU; they inherit the
+# workload arrays and the task function through _CTX and run numpy single-threaded.
+_CTX = {}
 
-    make_step(stream) returns a zero-argument callable issuing one step of
-    prepared libdsp calls on `stream`. Returns (eager_s, graph_s, kernels).
+
+def _worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def _worker_task(i):
+    return _CTX["fn"](i)
+
+
+def cpu_workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_CPU_WORKERS, n))
+
+
+def cpu_baseline(fn, items, budget_s, single_s, unit, sample_desc):
+    """Time fn(item) -> work units over passes of `items` until the wall budget is spent:
+    in parallel over worker processes, then on one core. Returns the cpu_baseline record."""
+    import multiprocessing as mp
+    _CTX["fn"] = fn
+    workers = cpu_workers()
+    ctx = mp.get_context("fork")
+    done_units, done_items, passes = 0.0, 0, 0
+    with ctx.Pool(workers, initializer=_worker_init) as pool:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            for u in pool.imap_unordered(_worker_task, items, chunksize=max(1, len(items) // (4 * workers))):
+                done_units += u
+                done_items += 1
+            passes += 1
+        wall = time.perf_counter() - t0
+    _worker_init()
+    one_units, one_items = 0.0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < single_s:
+        one_units += fn(items[one_items % len(items)])
+        one_items += 1
+    one_wall = time.perf_counter() - t0
+    return dict(value=done_units / wall, unit=unit, cores=workers, kind="oracle",
+                sample=f"{sample_desc}: {done_items} items over {passes} pass(es) of {len(items)} "
+                       f"({done_units:.0f} {unit.split('/')[0]}, {wall:.1f} s wall, {workers} worker processes)",
+                single_core=dict(value=one_units / one_wall, unit=unit, cores=1,
+                                 sample=f"{one_items} items, {one_wall:.1f} s wall"))
+
+
+# ---------------------------------------------------------------- GPU timing
+def run_phases(make_step, steps, warmup, dominant, do_flush=True):
+    """Time a step eagerly (HIP events attached to every libdsp dispatch) and as a replayed
+    HIP graph, each timed step preceded by a cache-flushing store pass outside its interval.
+
+    make_step(stream) returns a zero-argument callable issuing one step of prepared libdsp
+    calls on `stream`. Returns dict(eager_s, graph_s, warm_graph_s, kernels).
     """
     import torch
     import block_drafting_verification_amd as dsp
     s = torch.cuda.Stream()
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    def flush(i):
+        if do_flush:
+            scratch.fill_(i + 1)  # a plain elementwise store kernel (nonzero: no memset path)
+
+    def timed(body):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, b) in enumerate(ev):
+            flush(i)
+            a.record(s)
+            body()
+            b.record(s)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / 1e3
+
     with torch.cuda.stream(s):
         step = make_step(s)
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
         dsp.prof_reset()
-        dsp.prof_enable(True, kernels=None if prof_all else dominant)
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        eager = time.perf_counter() - t0
+        dsp.prof_enable(True)
+        eager = timed(step)
         dsp.prof_enable(False)
         kern = {}
         for name in dsp.KERNELS:
@@ -104,122 +186,34 @@ def run_phases(make_step, steps, warmup, dominant, prof_all=False):
         for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
+        graph = timed(g.replay)
+        # context only: back-to-back replays with no flush (caches warm)
         t0 = time.perf_counter()
         for _ in range(steps):
             g.replay()
         torch.cuda.synchronize()
-        graph = time.perf_counter() - t0
-    return eager, graph, kern
+        warm = time.perf_counter() - t0
+    for k in dominant:
+        assert k in kern, f"no timed launch of {k}"
+    return dict(eager_s=eager, graph_s=graph, warm_graph_s=warm, kernels=kern)
 
 
-def cpu_oracle_verify(c, windows, budget_s, temperature=1.0):
-    """Time the oracle on whole requests of the batch until the budget is spent."""
-    import numpy as np
-    import workloads
-    from oracle import verify as ov
-    R, K = c["R"], c["K"]
-    done_tokens, done_req, passes = 0, 0, 0
-    w0, c0 = time.perf_counter(), time.process_time()
-    while time.perf_counter() - w0 < budget_s:
-        for i in range(R):
-            n = int(windows[i])
-            t = workloads.values(c["t"][i, :n + 1], c["dtype"]).astype(np.float64)
-            d = workloads.values(c["d"][i:i + 1], c["dtype"]).astype(np.float64)
-            ov.verify_chain(t, np.array([0, n + 1]), d, c["x"][i:i + 1], temperature, seed=0, rnd=passes,
-                            req_id=[i])
-            done_tokens += n
-            done_req += 1
-            if time.perf_counter() - w0 > budget_s:
-                break
-        passes += 1
-    wall = time.perf_counter() - w0
-    cpu = time.process_time() - c0
-    return dict(value=done_tokens / wall, unit="verified draft tokens/s", cores=max(1, round(cpu / wall)),
-                kind="oracle", sample=f"{done_req} request-verifies over {passes} pass(es) of the {R}-request "
-                                      f"batch ({done_tokens} verified draft tokens, {wall:.1f} s wall)")
+def timing_record(ph, steps):
+    elapsed = min(ph["eager_s"], ph["graph_s"])
+    return elapsed, dict(graph_ms_per_step=1000.0 * ph["graph_s"] / steps,
+                         eager_ms_per_step=1000.0 * ph["eager_s"] / steps,
+                         warm_graph_ms_per_step=1000.0 * ph["warm_graph_s"] / steps,
+                         value_from="graph" if ph["graph_s"] <= ph["eager_s"] else "eager",
+                         cache_flush=f"{FLUSH_BYTES >> 20} MiB store pass before each timed step")
 
 
-def bench_verify(args, which):
-    import numpy as np
-    import torch
-    import block_drafting_verification_amd as dsp
-    import workloads
-
-    dev = torch.device("cuda", 0)
-    c = workloads.dense_verify() if which == "dense-verify" else workloads.scheduled_verify()
-    R, K, V = c["R"], c["K"], c["V"]
-
-    def gpu(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    conf, cost, anchors, x = gpu(c["conf"]), gpu(c["cost"]), gpu(c["anchors"]), gpu(c["x"])
-    drf = bf16(c["d"])
-    # windows are a deterministic function of the confidences: compute them once to lay out the
-    # packed target logits (they stand in for the target forward over the packed buffer)
-    w0 = dsp.schedule_windows(conf, cost)["windows"].cpu().numpy()
-    if which == "dense-verify":
-        tgt = bf16(c["t"].reshape(R * (K + 1), V))
-    else:
-        tgt = bf16(np.concatenate([c["t"][i, :w0[i] + 1] for i in range(R)]))
-    max_rows = tgt.shape[0]
-    rnd = torch.zeros(1, dtype=torch.int64, device=dev)
-    ops = {}
-
-    def make_step(stream):
-        # the scheduler and the pack in one call (one launch: the selection workgroup packs)
-        sch = dsp.schedule_pack(conf, cost, anchors, x, want_survival=False, stream=stream, prepare=True)
-        pk = sch
-        ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=0,
-                                   round_dev=rnd, max_rows=max_rows, row_req=pk.outputs["row_req"],
-                                   row_pos=pk.outputs["row_pos"], stream=stream, prepare=True)
-        ops.update(sch=sch, pk=pk, ver=ver)
-
-        def step():  # the verify call advances the device-side Philox round itself
-            sch()
-            ver()
-        return step
-
-    eager, graph, kern = run_phases(make_step, args.steps, args.warmup, ["VERIFY_STATS"], args.prof_all)
-    elapsed = min(eager, graph)
-    so = ops["sch"].outputs
-    vo = ops["ver"].outputs
-    assert int(ops["pk"].outputs["status"].item()) == 0 and int(vo["status"].item()) == 0, \
-        "device status flagged a fault"
-    win = so["windows"].cpu().numpy()
-    assert np.array_equal(win, w0)
-    N = int(win.sum())
-    T_rows = R + N
-    acc = vo["accepted_len"].cpu().numpy()
-    bytes_stats = (T_rows + N) * V * 2
-    st = kern["VERIFY_STATS"]["avg_us"]
-    achieved = bytes_stats / (st * 1e-6) / 1e9
-    traffic = traffic_from_profiles("verify.hip", "verify_stats", which)
-    res = dict(
-        metric="verified draft tokens/sec", value=N * args.steps / elapsed, unit="tokens/s",
-        n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps,
-        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
-        data="synthetic (seeded N(0,3) logits with 1% +8 boosts; draft = target + Gaussian noise)",
-        config=dict(workload=("dense-vocab verify: 64 requests, K=7, V=151936, bf16, full-block windows, T=1"
-                              if which == "dense-verify" else
-                              "confidence-scheduled ragged verify: 256 requests, K=16, V=151936, bf16, "
-                              "additive cost 1+0.05n, compact windows, T=1"),
-                    requests=R, block=K, vocab=V, logits_dtype="bf16",
-                    arithmetic="fp32 per element (exp2), fp64 sums and decisions",
-                    verified_drafts_per_step=N, packed_rows=T_rows, mean_accepted=float(acc.mean())),
-        roofline=dict(kernel="verify_stats", bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=achieved / PEAK_HBM_GBS, traffic=traffic, algorithmic_bytes=bytes_stats,
-                      avg_us=st),
-        kernels=kern,
-        timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps,
-                    value_from="graph" if graph <= eager else "eager"),
-    )
-    res["roofline"]["read_ref"] = read_reference(tgt, drf)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_oracle_verify(c, win, args.cpu_seconds)
-    return res
+def hbm_roofline(kernel, algo_bytes, avg_us, traffic):
+    ach = algo_bytes / (avg_us * 1e-6) / 1e9
+    r = dict(kernel=kernel, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS,
+             traffic=traffic, algorithmic_bytes=algo_bytes, avg_us=avg_us)
+    if traffic:
+        r["traffic_over_algorithmic"] = traffic / algo_bytes
+    return r
 
 
 def read_reference(*tensors, reps=10):
@@ -245,90 +239,245 @@ def read_reference(*tensors, reps=10):
                 method="streaming-read probe over the same target and draft logits")
 
 
-def bench_markov(args):
+def _bf16(dev, bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _gpu(dev, a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+# ---------------------------------------------------------------- verify workloads
+def verify_data(which):
+    import numpy as np
+    import workloads
+    from oracle import schedule as osch
+    c = workloads.dense_verify() if which == "dense-verify" else workloads.scheduled_verify()
+    # the windows are a deterministic function of the confidences: the oracle's gives the
+    # layout of the packed target rows (which stand in for the target forward over the buffer)
+    c["w0"] = osch.schedule_windows(c["conf"], c["cost"])["windows"].astype(np.int64)
+    return c
+
+
+def verify_cpu(c, args):
+    import numpy as np
+    import workloads
+    from oracle import verify as ov
+    win = c["w0"]
+
+    def one(i):
+        n = int(win[i])
+        t = workloads.values(c["t"][i, :n + 1], c["dtype"])
+        d = workloads.values(c["d"][i:i + 1], c["dtype"])
+        ov.verify_chain(t, np.array([0, n + 1]), d, c["x"][i:i + 1], 1.0, seed=0, rnd=0, req_id=[i])
+        return n
+    return cpu_baseline(one, list(range(c["R"])), args.cpu_seconds, args.cpu_single_seconds,
+                        "verified draft tokens/s", "oracle verify of whole requests of the batch (its windows)")
+
+
+def bench_verify(args, which, c, cpu):
     import numpy as np
     import torch
     import block_drafting_verification_amd as dsp
-    import workloads
 
     dev = torch.device("cuda", 0)
-    c = workloads.markov_chain()
+    R, K, V = c["R"], c["K"], c["V"]
+    w0 = c["w0"]
+    conf, cost, anchors, x = _gpu(dev, c["conf"]), _gpu(dev, c["cost"]), _gpu(dev, c["anchors"]), _gpu(dev, c["x"])
+    drf = _bf16(dev, c["d"])
+    if which == "dense-verify":
+        tgt = _bf16(dev, c["t"].reshape(R * (K + 1), V))
+    else:
+        tgt = _bf16(dev, np.concatenate([c["t"][i, :w0[i] + 1] for i in range(R)]))
+    max_rows = tgt.shape[0]
+    rnd = torch.zeros(1, dtype=torch.int64, device=dev)
+    ops = {}
+
+    def make_step(stream):
+        # the scheduler and the pack in one call (one launch: the selection workgroup packs)
+        sch = dsp.schedule_pack(conf, cost, anchors, x, want_survival=False, stream=stream, prepare=True)
+        ver = dsp.verify_rejection(tgt, sch.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=0,
+                                   round_dev=rnd, max_rows=max_rows, row_req=sch.outputs["row_req"],
+                                   row_pos=sch.outputs["row_pos"], stream=stream, prepare=True)
+        ops.update(sch=sch, ver=ver)
+
+        def step():  # the verify call advances the device-side Philox round itself
+            sch()
+            ver()
+        return step
+
+    ph = run_phases(make_step, args.steps, args.warmup, ["VERIFY_STATS"], not args.no_flush)
+    elapsed, timing = timing_record(ph, args.steps)
+    kern = ph["kernels"]
+    so, vo = ops["sch"].outputs, ops["ver"].outputs
+    assert int(so["status"].item()) == 0 and int(vo["status"].item()) == 0, "device status flagged a fault"
+    win = so["windows"].cpu().numpy()
+    assert np.array_equal(win, w0)
+    N = int(win.sum())
+    T_rows = R + N
+    acc = vo["accepted_len"].cpu().numpy()
+    bytes_stats = (T_rows + N) * V * 2
+    wl = ("dense-vocab verify: 64 requests, K=7, V=151936, bf16, full-block windows, T=1"
+          if which == "dense-verify" else
+          "confidence-scheduled ragged verify: 256 requests, K=16, V=151936, bf16, TV-logistic confidences, "
+          "additive cost 1+0.05n, compact windows, T=1")
+    res = dict(
+        metric="verified draft tokens/sec", value=N * args.steps / elapsed, unit="tokens/s",
+        n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps,
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+        data="synthetic (seeded N(0,3) logits with 1% +8 boosts; draft = target + Gaussian noise)",
+        config=dict(workload=wl, requests=R, block=K, vocab=V, logits_dtype="bf16",
+                    arithmetic="fp32 per element (exp2), fp64 sums and decisions",
+                    verified_drafts_per_step=N, packed_rows=T_rows, mean_accepted=float(acc.mean()),
+                    window_histogram=np.bincount(win, minlength=K + 1).tolist()),
+        roofline=hbm_roofline("verify_stats", bytes_stats, kern["VERIFY_STATS"]["avg_us"],
+                              traffic_from_profiles("verify.hip", "verify_stats", which)),
+        kernels=kern, timing=timing)
+    res["roofline"]["read_ref"] = read_reference(tgt, drf)
+    if which == "scheduled-verify":
+        res["static"] = bench_static(args, c, dev, drf, x)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    return res
+
+
+def bench_static(args, c, dev, drf, x):
+    """The static run of the scheduled verify's data: every window the full block (no
+    scheduler), 256 x 17 target rows + 256 x 16 draft rows of V = 151,936 bf16."""
+    import numpy as np
+    import torch
+    import block_drafting_verification_amd as dsp
+    R, K, V = c["R"], c["K"], c["V"]
+    tgt = _bf16(dev, c["t"].reshape(R * (K + 1), V))
+    cu = torch.arange(R + 1, dtype=torch.int32, device=dev) * (K + 1)
+    rq = torch.arange(R, dtype=torch.int32, device=dev).repeat_interleave(K + 1)
+    rp = torch.arange(K + 1, dtype=torch.int32, device=dev).repeat(R)
+    rnd = torch.zeros(1, dtype=torch.int64, device=dev)
+    ops = {}
+
+    def make_step(stream):
+        ver = dsp.verify_rejection(tgt, cu, x, drf=drf, temperature=1.0, seed=0, round_dev=rnd, row_req=rq,
+                                   row_pos=rp, want_probs=False, stream=stream, prepare=True)
+        ops["ver"] = ver
+        return ver
+
+    ph = run_phases(make_step, args.steps, args.warmup, ["VERIFY_STATS"], not args.no_flush)
+    elapsed, timing = timing_record(ph, args.steps)
+    assert int(ops["ver"].outputs["status"].item()) == 0, "device status flagged a fault"
+    acc = ops["ver"].outputs["accepted_len"].cpu().numpy()
+    N = R * K
+    rows = R * (K + 1) + N
+    del tgt
+    return dict(workload="static run of the same data: 256 requests x 16 full windows (8,448 rows, 2.567 GB)",
+                value=N * args.steps / elapsed, unit="verified draft tokens/s", ms_per_step=1000.0 * elapsed / args.steps,
+                mean_accepted=float(acc.mean()),
+                roofline=hbm_roofline("verify_stats", rows * V * 2, ph["kernels"]["VERIFY_STATS"]["avg_us"],
+                                      traffic_from_profiles("verify.hip", "verify_stats", "scheduled-verify-static")),
+                kernels=ph["kernels"], timing=timing)
+
+
+# ---------------------------------------------------------------- Markov chain
+def markov_cpu(c, args):
+    import numpy as np
+    import workloads
+    from oracle import markov as om
+    L = c["L"]
+    U64 = workloads.bf16_bits_to_f32(c["U"]).astype(np.float64)
+    W64 = workloads.bf16_bits_to_f32(c["W"]).astype(np.float64)
+
+    def one(i):
+        om.chain(workloads.bf16_bits_to_f32(L[i:i + 1]), U64, W64, c["anchors"][i:i + 1])
+        return c["B"]
+    return cpu_baseline(one, list(range(c["R"])), args.cpu_seconds, args.cpu_single_seconds,
+                        "drafted tokens/s", "oracle greedy chain of whole requests (all 16 steps)")
+
+
+def bench_markov(args, c, cpu):
+    import torch
+    import block_drafting_verification_amd as dsp
+
+    dev = torch.device("cuda", 0)
     R, B, V, r = c["R"], c["B"], c["V"], c["rank"]
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    L, U, Wt = bf16(c["L"]), bf16(c["U"]), bf16(np.ascontiguousarray(c["W"].T))
+    L, U, Wt = _bf16(dev, c["L"]), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
     a = torch.from_numpy(c["anchors"]).to(dev)
+
     def make_step(stream):
         return dsp.draft_markov_step(L, U, Wt, a, stream=stream, prepare=True)
 
-    eager, graph, kern = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "MARKOV_MERGE"],
-                                    args.prof_all)
-    elapsed = min(eager, graph)
+    ph = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "MARKOV_MERGE"], not args.no_flush)
+    elapsed, timing = timing_record(ph, args.steps)
+    kern = ph["kernels"]
     g = kern["MARKOV_GEMM"]["avg_us"]
-    # one launch reads the step's base logits L, the previous tokens' rows of U and all of Wt
-    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2
+    # algorithmic bytes of one launch (one step over every request): the step's L rows, the
+    # previous tokens' U rows, and W counted once per 16-step call (1/16 of it per step)
+    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 // B
     flops_launch = 2.0 * R * r * V
+    roof = hbm_roofline("markov_gemm", bytes_launch, g, traffic_from_profiles("markov.hip", "markov_gemm",
+                                                                              "markov-chain"))
+    roof.update(mfma_tflops=flops_launch / (g * 1e-6) / 1e12,
+                mfma_frac=flops_launch / (g * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                per_call_us=B * (g + kern["MARKOV_MERGE"]["avg_us"]),
+                per_call_target_us_at_70pct=(R * B * V * 2 + R * B * r * 2 + V * r * 2) / (0.7 * PEAK_HBM_GBS * 1e3))
     res = dict(
         metric="drafted tokens/sec", value=R * B * args.steps / elapsed, unit="tokens/s", n_gpus=1,
         steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload="Markov-head greedy chain: 256 requests, 16 steps, V=151936, rank 256"),
-        roofline=dict(kernel="markov_gemm", bound="hbm", achieved=bytes_launch / (g * 1e-6) / 1e9,
-                      peak=PEAK_HBM_GBS, unit="GB/s", frac=bytes_launch / (g * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                      traffic=traffic_from_profiles("markov.hip", "markov_gemm", "markov-chain"),
-                      mfma_tflops=flops_launch / (g * 1e-6) / 1e12,
-                      mfma_frac=flops_launch / (g * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, avg_us=g),
-        kernels=kern,
-        timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps))
-    if not args.no_cpu_baseline:
-        from oracle import markov as om
-        L32 = workloads.bf16_bits_to_f32(c["L"][:4])
-        U32, W32 = workloads.bf16_bits_to_f32(c["U"]), workloads.bf16_bits_to_f32(c["W"])
-        t0 = time.perf_counter()
-        c0 = time.process_time()
-        om.chain(L32, U32, W32, c["anchors"][:4])
-        wall = time.perf_counter() - t0
-        res["cpu_baseline"] = dict(value=4 * B / wall, unit="drafted tokens/s",
-                                   cores=max(1, round((time.process_time() - c0) / wall)), kind="oracle",
-                                   sample=f"4 of {R} requests, all {B} steps")
+        roofline=roof, kernels=kern, timing=timing)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
-def bench_tree(args):
+# ---------------------------------------------------------------- PCTree
+def tree_cpu(c, args):
+    import numpy as np
+    import workloads
+    from oracle import pctree as opt
+    U64 = workloads.bf16_bits_to_f32(c["U"]).astype(np.float64)
+    W64 = workloads.bf16_bits_to_f32(c["W"]).astype(np.float64)
+
+    def one(i):
+        opt.tree_expand(workloads.bf16_bits_to_f32(c["L"][i:i + 1]), U64, W64, c["anchors"][i:i + 1],
+                        c["topk"], c["frontier"], c["topN"])
+        return c["topN"]
+    return cpu_baseline(one, list(range(c["R"])), args.cpu_seconds, args.cpu_single_seconds,
+                        "tree nodes/s", "oracle PCTree expansion of whole requests (16 depths)")
+
+
+def bench_tree(args, c, cpu):
     import numpy as np
     import torch
     import block_drafting_verification_amd as dsp
-    import workloads
 
     dev = torch.device("cuda", 0)
-    c = workloads.pctree()
     R, D, V, r = c["R"], c["B"], c["V"], c["rank"]
     k, F, N = c["topk"], c["frontier"], c["topN"]
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    L, U, Wt = bf16(c["L"]), bf16(c["U"]), bf16(np.ascontiguousarray(c["W"].T))
+    L, U, Wt = _bf16(dev, c["L"]), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
     a = torch.from_numpy(c["anchors"]).to(dev)
-    tgt = bf16(c["target"].reshape(R * (N + 1), V))
+    tgt = _bf16(dev, c["target"].reshape(R * (N + 1), V))
     cu = torch.arange(R + 1, dtype=torch.int32, device=dev) * (N + 1)
+    ops = {}
+
     def make_step(stream):
         te = dsp.tree_expand(L, U, Wt, a, k, F, N, stream=stream, prepare=True)
         tv = dsp.verify_rejection(tgt, cu, te.outputs["node_token"], parent=te.outputs["node_parent"],
                                   temperature=0.0, want_probs=False, stream=stream, prepare=True)
+        ops.update(te=te, tv=tv)
 
         def step():
             te()
             tv()
         return step
 
-    eager, graph, kern = run_phases(make_step, args.steps, args.warmup, ["TREE_GEMM", "VERIFY_STATS"],
-                                    args.prof_all)
-    elapsed = min(eager, graph)
-    f = []
-    prev = 1
+    ph = run_phases(make_step, args.steps, args.warmup, ["TREE_GEMM", "VERIFY_DECIDE"], not args.no_flush)
+    elapsed, timing = timing_record(ph, args.steps)
+    kern = ph["kernels"]
+    f, prev = [], 1
     for _ in range(D):
         prev = min(F, k * prev)
         f.append(prev)
@@ -336,56 +485,87 @@ def bench_tree(args):
     flops = 2.0 * parents * r * V
     g = kern["TREE_GEMM"]
     gemm_total_us = g["avg_us"] * g["launches"] / args.steps
+    acc = ops["tv"].outputs["accepted_len"].cpu().numpy()
+    walked = int((acc + 1).sum())
+    tflops = flops / (gemm_total_us * 1e-6) / 1e12
     res = dict(
         metric="tree nodes/sec", value=R * N * args.steps / elapsed, unit="nodes/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload="PCTree expansion + greedy tree verify: 128 requests, depth 16, V=129280, rank 256, "
-                             "k=4, F=16, N=64"),
-        roofline=dict(kernel="tree_gemm (all depths)", bound="mfma",
-                      achieved=flops / (gemm_total_us * 1e-6) / 1e12, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=flops / (gemm_total_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, traffic=None,
-                      gemm_us_per_step=gemm_total_us),
-        kernels=kern,
-        timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps))
-    vs = kern["VERIFY_STATS"]["avg_us"]
-    res["tree_verify"] = dict(bytes=R * (N + 1) * V * 2, avg_us=vs,
-                              GBps=R * (N + 1) * V * 2 / (vs * 1e-6) / 1e9)
+                             "k=4, F=16, N=64", parent_rows=parents),
+        roofline=dict(kernel="tree_gemm (all depths)", bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS,
+                      unit="TFLOP/s", frac=tflops / PEAK_BF16_TFLOPS,
+                      traffic=traffic_from_profiles("markov.hip", "markov_gemm_tree", "pctree"),
+                      gemm_us_per_step=gemm_total_us, flops_per_step=flops),
+        kernels=kern, timing=timing)
+    # the walk reads the target rows of the visited nodes only (accepted + 1 per request)
+    wk = kern["VERIFY_DECIDE"]["avg_us"]
+    res["tree_verify"] = dict(kernel="verify_tree_walk", avg_us=wk, rows_walked=walked, bytes_walked=walked * V * 2,
+                              GBps_walked=walked * V * 2 / (wk * 1e-6) / 1e9,
+                              note="one workgroup per request walks root to leaf; latency-bound")
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
-def bench_cycle(args):
-    """Draft -> confidence head -> schedule -> pack -> verify, one HIP graph per step (the
-    pages' cycle).
+# ---------------------------------------------------------------- closed cycle
+def cycle_data():
+    import numpy as np
+    import workloads
+    from oracle import schedule as osch
+    c = workloads.cycle_case(256, 16, workloads.V_QWEN3, 256, seed=1006)
+    c["w0"] = osch.schedule_windows(c["conf"], c["cost"])["windows"].astype(np.int64)
+    c["tp"] = workloads.cycle_target(c, c["w0"])
+    return c
 
-    The Markov head samples 16 positions for 256 requests and emits its bf16 rows (the
-    verify's q); the confidence head (hidden size 4096, sequential temperatures) gives the
-    per-position confidences from which the scheduler picks windows; the pack lays
+
+def cycle_cpu(c, args):
+    import numpy as np
+    import workloads
+    from oracle import markov as om
+    from oracle import verify as ov
+    U64 = workloads.bf16_bits_to_f32(c["U"]).astype(np.float64)
+    W64 = workloads.bf16_bits_to_f32(c["W"]).astype(np.float64)
+    cu = np.concatenate([[0], np.cumsum(c["w0"] + 1)])
+
+    def one(i):
+        d = om.chain_sampled(workloads.bf16_bits_to_f32(c["L"][i:i + 1]), U64, W64, c["anchors"][i:i + 1], 1.0,
+                             seed=0, rnd=0, req_id=[i])
+        n = int(c["w0"][i])
+        t = workloads.bf16_bits_to_f32(c["tp"][cu[i]:cu[i + 1]])
+        ov.verify_chain(t, np.array([0, n + 1]), d["zhat"], d["y"], 1.0, seed=0, rnd=1, req_id=[i])
+        return n
+    return cpu_baseline(one, list(range(c["R"])), args.cpu_seconds, args.cpu_single_seconds,
+                        "verified draft tokens/s",
+                        "oracle sampled draft (16 steps) + verify of whole requests (the scheduler's windows)")
+
+
+def bench_cycle(args, c, cpu):
+    """Draft -> confidence head -> schedule -> pack -> verify, one HIP graph per step (the
+    pages' cycle). The Markov head samples 16 positions for 256 requests and emits its bf16
+    rows (the verify's q); the confidence head (hidden size 4096, sequential temperatures)
+    gives the per-position confidences from which the scheduler picks windows; the pack lays
     out the verify buffer; the verify checks the windows against target rows laid out in
     packed order at setup (they stand in for the target forward, which is not part of the
-    method and is not timed).
-    """
+    method and is not timed)."""
     import numpy as np
     import torch
     import block_drafting_verification_amd as dsp
     import workloads
 
     dev = torch.device("cuda", 0)
-    c = workloads.cycle_case(256, 16, workloads.V_QWEN3, 256, seed=1006)
     R, K, V, r = c["R"], c["K"], c["V"], c["rank"]
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    L, U, Wt = bf16(c["L"]), bf16(c["U"]), bf16(np.ascontiguousarray(c["W"].T))
+    L, U, Wt = _bf16(dev, c["L"]), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
     a = torch.from_numpy(c["anchors"]).to(dev)
     hd = workloads.cycle_head_inputs(c)
-    hh, hw = bf16(hd["h"]), bf16(hd["w"])
+    hh, hw = _bf16(dev, hd["h"]), _bf16(dev, hd["w"])
     temps = torch.from_numpy(hd["temps"]).to(dev)
     cost = torch.from_numpy(c["cost"]).to(dev)
     conf0 = dsp.confidence_head(hh, hw, hd["bias"], temps)["conf"]
     w0 = dsp.schedule_windows(conf0, cost)["windows"].cpu().numpy()
-    tgt = bf16(workloads.cycle_target(c, w0))
+    assert np.array_equal(w0, c["w0"]), "the head's confidences give other windows than the workload's"
+    tgt = _bf16(dev, c["tp"])
     rd = torch.zeros(1, dtype=torch.int64, device=dev)
     ops = {}
 
@@ -394,12 +574,11 @@ def bench_cycle(args):
         ch = dsp.confidence_head(hh, hw, hd["bias"], temps, stream=stream, prepare=True)
         sch = dsp.schedule_pack(ch.outputs["conf"], cost, a, dr.outputs["y"], want_survival=False, stream=stream,
                                 prepare=True)
-        pk = sch
-        ver = dsp.verify_rejection(tgt, pk.outputs["cu_seqlens"], dr.outputs["y"], drf=dr.outputs["z"],
+        ver = dsp.verify_rejection(tgt, sch.outputs["cu_seqlens"], dr.outputs["y"], drf=dr.outputs["z"],
                                    temperature=1.0, seed=0, round_dev=rd, max_rows=tgt.shape[0],
-                                   row_req=pk.outputs["row_req"], row_pos=pk.outputs["row_pos"],
+                                   row_req=sch.outputs["row_req"], row_pos=sch.outputs["row_pos"],
                                    want_probs=False, stream=stream, prepare=True)
-        ops.update(dr=dr, ch=ch, sch=sch, pk=pk, ver=ver)
+        ops.update(dr=dr, ch=ch, sch=sch, ver=ver)
 
         def step():
             dr()
@@ -408,18 +587,18 @@ def bench_cycle(args):
             ver()
         return step
 
-    eager, graph, kern = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "MARKOV_MERGE",
-                                                                          "VERIFY_STATS"], args.prof_all)
-    elapsed = min(eager, graph)
-    for k in ("dr", "ch", "pk", "ver"):
+    ph = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "VERIFY_STATS"], not args.no_flush)
+    elapsed, timing = timing_record(ph, args.steps)
+    kern = ph["kernels"]
+    for k in ("dr", "ch", "sch", "ver"):
         assert int(ops[k].outputs["status"].item()) == 0, "device status flagged a fault"
     win = ops["sch"].outputs["windows"].cpu().numpy()
     assert np.array_equal(win, w0)
     N = int(win.sum())
     acc = ops["ver"].outputs["accepted_len"].cpu().numpy()
     g = kern["MARKOV_GEMM"]["avg_us"]
-    # one sampled step reads L's rows, the previous tokens' U rows and Wt, and writes the bf16 rows
-    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 + R * V * 2
+    # one sampled step: L rows, previous tokens' U rows, W once per 16-step call, emitted rows
+    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 // K + R * V * 2
     res = dict(
         metric="verified draft tokens/sec", value=N * args.steps / elapsed, unit="tokens/s", n_gpus=1,
         steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
@@ -430,13 +609,11 @@ def bench_cycle(args):
                     requests=R, block=K, vocab=V, drafted_per_step=R * K, verified_drafts_per_step=N,
                     packed_rows=R + N, mean_accepted=float(acc.mean()),
                     drafted_tokens_per_s=R * K * args.steps / elapsed),
-        roofline=dict(kernel="markov_gemm (sampled, emits bf16 rows)", bound="hbm",
-                      achieved=bytes_launch / (g * 1e-6) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=bytes_launch / (g * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                      traffic=traffic_from_profiles("markov.hip", "markov_gemm", "cycle"),
-                      algorithmic_bytes=bytes_launch, avg_us=g),
-        kernels=kern,
-        timing=dict(graph_ms_per_step=1000.0 * graph / args.steps, eager_ms_per_step=1000.0 * eager / args.steps))
+        roofline=hbm_roofline("markov_gemm (sampled, emits bf16 rows)", bytes_launch, g,
+                              traffic_from_profiles("markov.hip", "markov_gemm", "cycle")),
+        kernels=kern, timing=timing)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
@@ -465,18 +642,35 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path is not "
               "sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
+    want_cpu = not args.no_cpu_baseline
+    # host side first (data, then the CPU oracle sample), before anything touches the GPU
+    w = args.workload
+    if w in ("dense-verify", "scheduled-verify"):
+        c = verify_data(w)
+        cpu = verify_cpu(c, args) if want_cpu else None
+    elif w == "markov-chain":
+        import workloads
+        c = workloads.markov_chain()
+        cpu = markov_cpu(c, args) if want_cpu else None
+    elif w == "pctree":
+        import workloads
+        c = workloads.pctree()
+        cpu = tree_cpu(c, args) if want_cpu else None
+    elif w == "cycle":
+        c = cycle_data()
+        cpu = cycle_cpu(c, args) if want_cpu else None
     import torch
     assert torch.cuda.is_available(), "bench.py needs the GPU"
-    if args.workload == "copy":
+    if w == "copy":
         res = bench_copy(args)
-    elif args.workload in ("dense-verify", "scheduled-verify"):
-        res = bench_verify(args, args.workload)
-    elif args.workload == "markov-chain":
-        res = bench_markov(args)
-    elif args.workload == "cycle":
-        res = bench_cycle(args)
+    elif w in ("dense-verify", "scheduled-verify"):
+        res = bench_verify(args, w, c, cpu)
+    elif w == "markov-chain":
+        res = bench_markov(args, c, cpu)
+    elif w == "cycle":
+        res = bench_cycle(args, c, cpu)
     else:
-        res = bench_tree(args)
+        res = bench_tree(args, c, cpu)
     print(json.dumps(res))
 
 

@@ -12,6 +12,7 @@ Calls (same names as the C entry points without the ``dsp_`` prefix):
   schedule_windows   -- survival products + hardware-aware prefix scheduler
   pack_ragged        -- front-packed cu_seqlens verify buffer
   verify_rejection   -- batched ragged rejection / greedy / tree verify
+  verify_calibration -- ECE of the confidences against a verify's outcomes
   draft_markov_step  -- Markov-head greedy chain
   draft_markov_sample -- Markov-head sampled chain emitting its bf16 draft logits
   tree_expand        -- PCTree expansion
@@ -26,7 +27,8 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
                    DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE,
                    DspError, KERNELS)
 
-__all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection", "draft_markov_step",
+__all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection",
+           "verify_calibration", "draft_markov_step",
            "draft_markov_sample", "tree_expand", "schedule_pack",
            "philox_uniforms", "stream_read", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
@@ -75,15 +77,31 @@ def _take(o, key, make):
 _ws_cache = {}
 
 
-def _workspace(nbytes, device, private=False):
+def _call_stream(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _is_current(stream, device):
+    return stream.cuda_stream == torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes, device, private=False, stream=None):
     """A device byte buffer of at least nbytes.
 
-    Shared per device for one-shot calls (calls on one stream run in order);
-    private for prepared calls, which keep their buffer for their lifetime.
+    Prepared calls get a private buffer, kept for their lifetime. One-shot calls on
+    the current stream share one buffer per (device, stream): calls on one stream run
+    in order, and a grown cache entry is freed on the stream it was allocated on. A
+    one-shot call on another stream gets a buffer of its own, recorded on that stream
+    so the caching allocator does not reuse it before the call's kernels finish.
     """
     if private:
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-    key = (device.index if device.index is not None else torch.cuda.current_device())
+    s = _call_stream(stream)
+    if not _is_current(s, device):
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf.record_stream(s)
+        return buf
+    key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < max(nbytes, 1):
         buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -112,10 +130,16 @@ class PreparedCall:
         return self.outputs
 
 
-def _finish(fn, args, outputs, prepare, keep):
+def _finish(fn, args, outputs, prepare, keep, stream=None):
     if prepare:
         return PreparedCall(fn, args, keep, outputs)
     _abi.check(fn(*args))
+    if stream is not None:
+        # outputs allocated on the current stream but written on another: keep the
+        # allocator from handing their memory out again before that stream is done
+        for t in outputs.values():
+            if isinstance(t, torch.Tensor) and not _is_current(stream, t.device):
+                t.record_stream(stream)
     return outputs
 
 
@@ -144,7 +168,7 @@ def confidence_head(h, w, bias, sts_temp=None, out=None, status=None, stream=Non
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     args = (_ptr(h), _dtype_code(h), h.stride(0), h.stride(1), _ptr(w), _dtype_code(w), float(bias),
             _ptr(sts_temp), R, K, H, _ptr(conf), _ptr(status), _stream(stream))
-    return _finish(lib().dsp_confidence_head, args, dict(conf=conf, status=status), prepare, (h, w, sts_temp))
+    return _finish(lib().dsp_confidence_head, args, dict(conf=conf, status=status), prepare, (h, w, sts_temp), stream=stream)
 
 
 def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, threshold=0.0, want_survival=True,
@@ -165,12 +189,12 @@ def schedule_windows(conf, cost, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, thres
     windows = _take(o, "windows", lambda: torch.empty(R, dtype=torch.int32, device=dev))
     survival = _take(o, "survival", lambda: torch.empty(R, K, dtype=torch.float64, device=dev)) if want_survival else None
     stats = _take(o, "stats", lambda: torch.empty(4, dtype=torch.float64, device=dev))
-    ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare)
+    ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare, stream)
     args = (_ptr(conf), R, K, _ptr(cost), cost.numel(), mode, max_tokens, float(threshold), _ptr(windows),
             _ptr(survival),
             _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
     res = dict(windows=windows, survival=survival, stats=stats)
-    return _finish(lib().dsp_schedule_windows, args, res, prepare, (conf, cost, ws))
+    return _finish(lib().dsp_schedule_windows, args, res, prepare, (conf, cost, ws), stream=stream)
 
 
 def pack_ragged(windows, anchors, drafts, tiers=None, out=None, status=None, stream=None, prepare=False):
@@ -198,7 +222,7 @@ def pack_ragged(windows, anchors, drafts, tiers=None, out=None, status=None, str
             ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, len(tl),
             _ptr(cu), _ptr(tokens), _ptr(row_req), _ptr(row_pos), _ptr(tt), _ptr(status), _stream(stream))
     res = dict(cu_seqlens=cu, tokens=tokens, row_req=row_req, row_pos=row_pos, total_and_tier=tt, status=status)
-    return _finish(lib().dsp_pack_ragged, args, res, prepare, (windows, anchors, drafts, arr))
+    return _finish(lib().dsp_pack_ragged, args, res, prepare, (windows, anchors, drafts, arr), stream=stream)
 
 
 def schedule_pack(conf, cost, anchors, drafts, mode=DSP_SCHED_EARLY_STOP, max_tokens=-1, threshold=0.0,
@@ -230,7 +254,7 @@ def schedule_pack(conf, cost, anchors, drafts, mode=DSP_SCHED_EARLY_STOP, max_to
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     tl = list(tiers or [])
     arr = (ctypes.c_int32 * max(len(tl), 1))(*tl) if tl else None
-    ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare)
+    ws = _workspace(lib().dsp_schedule_windows_workspace_size(R, K), dev, prepare, stream)
     args = (_ptr(conf), R, K, _ptr(cost), cost.numel(), mode, max_tokens, float(threshold), _ptr(windows),
             _ptr(survival), _ptr(stats), _ptr(anchors), _ptr(drafts), drafts.stride(0),
             ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, len(tl),
@@ -238,7 +262,7 @@ def schedule_pack(conf, cost, anchors, drafts, mode=DSP_SCHED_EARLY_STOP, max_to
             _stream(stream))
     res = dict(windows=windows, survival=survival, stats=stats, cu_seqlens=cu, tokens=tokens, row_req=row_req,
                row_pos=row_pos, total_and_tier=tt, status=status)
-    return _finish(lib().dsp_schedule_pack, args, res, prepare, (conf, cost, anchors, drafts, ws, arr))
+    return _finish(lib().dsp_schedule_pack, args, res, prepare, (conf, cost, anchors, drafts, ws, arr), stream=stream)
 
 
 def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,
@@ -299,7 +323,7 @@ def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperat
     rows_cap = min(R * (K + 1), tgt.shape[0])
     max_rows = rows_cap if not max_rows else min(int(max_rows), rows_cap)
     nbytes = lib().dsp_verify_rejection_workspace_size(R, K, V, max_rows, t_dt, d_dt)
-    ws = _workspace(nbytes, dev, prepare)
+    ws = _workspace(nbytes, dev, prepare, stream)
     args = (_ptr(tgt), t_dt, tgt.stride(0), _ptr(cu_seqlens), _ptr(drf), d_dt, ld_dr, ld_dk,
             _ptr(draft_tok), draft_tok.stride(0), _ptr(parent), R, K, V, max_rows, float(temperature),
             int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(row_req), _ptr(row_pos), _ptr(cap),
@@ -309,7 +333,31 @@ def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperat
     if ceiling is not None:
         res["ceiling"] = ceiling
     return _finish(lib().dsp_verify_rejection, args, res, prepare,
-                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, cap, ws))
+                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, cap, ws), stream=stream)
+
+
+def verify_calibration(conf, cu_seqlens, decided, n_bins=10, out=None, stream=None, prepare=False):
+    """ECE of the confidences conf float32 [R, K] against a verify's outcomes: cu_seqlens
+    int32 [R+1] (the packing verified), decided int32 [R] (accepted_len, or the cap-accept
+    ceiling). Returns dict(ece float64 [R], n_obs int32 [R], ece_batch, bin_count, bin_conf,
+    bin_out (float64 [n_bins] each, views of one 'batch' buffer))."""
+    _on_gpu(conf, cu_seqlens, decided)
+    _need(conf.dtype == torch.float32 and conf.dim() == 2 and conf.stride(1) == 1,
+          "conf: float32 [R, K] with unit inner stride")
+    R, K = conf.shape
+    _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.numel() == R + 1 and cu_seqlens.is_contiguous(),
+          "cu_seqlens: contiguous int32 [R+1]")
+    _need(decided.dtype == torch.int32 and decided.numel() == R and decided.is_contiguous(), "decided: int32 [R]")
+    dev = conf.device
+    o = out or {}
+    ece = _take(o, "ece", lambda: torch.empty(R, dtype=torch.float64, device=dev))
+    nobs = _take(o, "n_obs", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    batch = _take(o, "batch", lambda: torch.empty(1 + 3 * n_bins, dtype=torch.float64, device=dev))
+    args = (_ptr(conf), conf.stride(0), _ptr(cu_seqlens), _ptr(decided), R, K, int(n_bins), _ptr(ece), _ptr(nobs),
+            _ptr(batch), _stream(stream))
+    res = dict(ece=ece, n_obs=nobs, batch=batch, ece_batch=batch[0:1], bin_count=batch[1:1 + n_bins],
+               bin_conf=batch[1 + n_bins:1 + 2 * n_bins], bin_out=batch[1 + 2 * n_bins:])
+    return _finish(lib().dsp_verify_calibration, args, res, prepare, (conf, cu_seqlens, decided), stream=stream)
 
 
 def _check_markov(L, U, Wt):
@@ -338,11 +386,11 @@ def draft_markov_step(L, U, Wt, prev_tok, n_steps=None, want_logq=False, out=Non
     logq = _take(o, "logq", lambda: torch.empty(R, n, dtype=torch.float32, device=dev)) if want_logq else None
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = _workspace(lib().dsp_draft_markov_step_workspace_size(R, V, rank, n, int(want_logq)), dev, prepare)
+    ws = _workspace(lib().dsp_draft_markov_step_workspace_size(R, V, rank, n, int(want_logq)), dev, prepare, stream)
     args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
             _ptr(y), y.stride(0), _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_markov_step, args, dict(y=y, logq=logq, status=status), prepare,
-                   (L, U, Wt, prev_tok, ws))
+                   (L, U, Wt, prev_tok, ws), stream=stream)
 
 
 def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_dev=None, req_id=None,
@@ -372,12 +420,12 @@ def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_
     _need(z.dtype == torch.bfloat16 and z.dim() == 3 and z.stride(2) == 1, "z: bf16 [R, n, V] with unit stride")
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = _workspace(lib().dsp_draft_markov_sample_workspace_size(R, V, rank, n), dev, prepare)
+    ws = _workspace(lib().dsp_draft_markov_sample_workspace_size(R, V, rank, n), dev, prepare, stream)
     args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
             float(temperature), int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(y), y.stride(0),
             _ptr(logq), _ptr(z), z.stride(0), z.stride(1), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_markov_sample, args, dict(y=y, logq=logq, z=z, status=status), prepare,
-                   (L, U, Wt, prev_tok, round_dev, req_id, ws))
+                   (L, U, Wt, prev_tok, round_dev, req_id, ws), stream=stream)
 
 
 def tree_expand(L, U, Wt, anchor, topk, frontier, topN, want_mask=False, out=None, status=None, stream=None,
@@ -402,13 +450,13 @@ def tree_expand(L, U, Wt, anchor, topk, frontier, topN, want_mask=False, out=Non
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     nbytes = lib().dsp_tree_expand_workspace_size(R, D, V, rank, topk, frontier, topN)
-    ws = _workspace(nbytes, dev, prepare)
+    ws = _workspace(nbytes, dev, prepare, stream)
     args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(anchor), R, D, topk,
             frontier, topN, _ptr(tok), _ptr(par), _ptr(dep), _ptr(sc), _ptr(nn), _ptr(mask), _ptr(status),
             _ptr(ws), ws.numel(), _stream(stream))
     res = dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, n_nodes=nn, anc_mask=mask,
                status=status)
-    return _finish(lib().dsp_tree_expand, args, res, prepare, (L, U, Wt, anchor, ws))
+    return _finish(lib().dsp_tree_expand, args, res, prepare, (L, U, Wt, anchor, ws), stream=stream)
 
 
 def stream_read(t, sink=None, stream=None):

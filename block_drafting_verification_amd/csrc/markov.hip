@@ -346,19 +346,24 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     if (lk) {
       // transposed: token t of request j at Lt[t * 16 + j]; every one of the 16 request
       // columns is written (zeros past the block's requests), so no stale LDS contents
-      // meet the one-hot zeros. A non-finite entry is staged as the largest finite
-      // magnitude of its sign (a masked -inf as -max): a zero weight times an infinity
-      // would make NaN in every other request's sum.
+      // meet the one-hot zeros. A non-finite entry is staged as -max (a zero weight times
+      // an infinity would make NaN in every other request's sum): for a masked -inf that
+      // ranks and weighs the same; +inf and NaN are faults and set the status bit.
       if (tid < 64) {
         uint16_t* Lt = (uint16_t*)Ls;
         const int j = tid >> 2, c = tid & 3;
         const u32x4 w = rl[0];
+        bool fault = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           uint16_t h = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-          if ((h & 0x7f80u) == 0x7f80u) h = (h & 0x8000u) || (h & 0x7fu) ? 0xff7fu : 0x7f7fu;
+          if ((h & 0x7f80u) == 0x7f80u) {
+            fault |= !(h & 0x8000u) || (h & 0x7fu);
+            h = 0xff7fu;
+          }
           Lt[(8 * c + e) * 16 + j] = h;
         }
+        if (fault) atomicOr(a.status, DSP_STATUS_NONFINITE);
       }
       return;
     }
@@ -1101,6 +1106,9 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
     if (pv && j == 0) {
+      // a +inf or NaN in the row makes the maximum infinite or the sum NaN (the maxima
+      // skip NaN, the exponentials do not): a fault; the children are then unspecified
+      if (H == INFINITY || !(S == S) || S == INFINITY) atomicOr(a.status, DSP_STATUS_NONFINITE);
       p_lse[p] = ((double)H + log2(S)) * kLn2d;
 #pragma unroll
       for (int q = 0; q < kTopK; ++q)  // below -2^127: a masked entry (staged as -max)

@@ -1035,7 +1035,44 @@ struct SampleArgs {
   const Job* jobs;
   double* rsum;
   int32_t* out;
+  const StatSlot* tstats;  // the statistics pass's target row slots
+  int32_t ncht;
 };
+
+// Chunks of a draw: chunk c covers elements [begin(c), begin(c + 1)) of the row.
+//   uniform (ce > 0): begin(c) = min(V, c * ce) -- the residual / streamed layout;
+//   statistics (ce == 0): the statistics pass's chunks of the row, whose masses the
+//   pass already summed: begin(0) = 0, begin(c) = head + min(nvec, c * cv) * PV for
+//   0 < c < n, begin(n) = V (the unaligned head in chunk 0, the tail in the last).
+struct DrawChunks {
+  int n, ce, V, head, nvec, cv, pv;
+  __device__ __forceinline__ int begin(int c) const {
+    if (ce > 0) return min(V, c * ce);
+    if (c <= 0) return 0;
+    if (c >= n) return V;
+    return head + min(nvec, c * cv) * pv;
+  }
+};
+__device__ __forceinline__ DrawChunks uniform_chunks(const SampleArgs& a) {
+  return DrawChunks{a.nch2, a.ce, a.V, 0, 0, 0, 0};
+}
+template <typename TT>
+__device__ __forceinline__ DrawChunks stats_chunks(const SampleArgs& a, const TT* tp) {
+  const RowGeom g = row_geom(tp, a.V);
+  return DrawChunks{a.ncht, 0, a.V, g.head, g.nvec, (g.nvec + a.ncht - 1) / a.ncht, Elem<TT>::kPerVec};
+}
+// A bonus draw (from p) needs no pass over its row: p's mass in each statistics chunk is
+// the chunk's sum of 2^(x c - ref) times 2^(ref - lse). Used while the row has at most 64
+// chunks (the masses stay in one wavefront's lanes and the draw's 64-entry table).
+__device__ __forceinline__ bool bonus_from_stats(const Job& jb, const SampleArgs& a) {
+  return jb.mode == JOB_BONUS && a.ncht <= 64;
+}
+// lanes 0..63 of the first wavefront: the bonus row's per-chunk masses into s_csum
+__device__ __forceinline__ void bonus_masses(const SampleArgs& a, const Job& jb, double* s_csum) {
+  const int c = threadIdx.x;
+  const StatSlot sl = a.tstats[(size_t)jb.trow * a.ncht + min(c, a.ncht - 1)];
+  s_csum[c] = c < a.ncht && sl.ref != -INFINITY ? sl.sum * exp2((double)sl.ref - jb.lse_t) : 0.0;
+}
 
 // Residual / bonus weight sums per (request, chunk), grid-stride over items.
 template <typename TT, typename TD>
@@ -1045,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(SampleArgs a)
   for (long it = blockIdx.x; it < items; it += gridDim.x) {
     const int i = (int)(it / a.nch2), c = (int)(it % a.nch2);
     const Job jb = a.jobs[i];
-    if (jb.mode == JOB_NONE) continue;  // uniform over the workgroup
+    if (jb.mode == JOB_NONE || bonus_from_stats(jb, a)) continue;  // uniform over the workgroup
     const bool resid = jb.mode == JOB_RESID;
     const JobFrame f = job_frame(jb, a.cl, resid);
     const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
@@ -1060,7 +1097,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(SampleArgs a)
 // with contiguous per-thread ranges and an fp64 exclusive scan, and let the owning
 // thread walk its range to the first element past the target.
 template <typename TT, typename TD>
-__device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s_csum) {
+__device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s_csum, const DrawChunks& dc) {
   __shared__ double s_wtot[kSampleThreads / 64];
   __shared__ int s_chunk;
   __shared__ double s_tau;
@@ -1071,16 +1108,16 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
   const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
   const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
   double total = 0.0;
-  for (int c = 0; c < a.nch2; ++c) total += s_csum[c];
+  for (int c = 0; c < dc.n; ++c) total += s_csum[c];
   if (resid && !(total > 0.0)) {
     // empty residual (p <= q everywhere after rounding): draw from p instead
     resid = false;
     const JobFrame fp = job_frame(jb, a.cl, false);
-    const bool t_al0 = (((uintptr_t)tp) & 15u) == 0;
-    for (int c = 0; c < a.nch2; ++c) {
+    for (int c = 0; c < dc.n; ++c) {
       double s0 = 0.0;
-      const int c1 = min(a.V, (c + 1) * a.ce);
-      for (int e = c * a.ce + tid * 8; e < c1; e += kSampleThreads * 8)
+      const int c0 = dc.begin(c), c1 = dc.begin(c + 1);
+      const bool t_al0 = (((uintptr_t)(tp + c0)) & 15u) == 0;
+      for (int e = c0 + tid * 8; e < c1; e += kSampleThreads * 8)
         s0 += (double)job_weight8<TT, TD>(fp, tp, nullptr, t_al0, true, e, c1);
       const double S = block_sum<kSampleThreads / 64>(s0, s_wtot);
       __syncthreads();
@@ -1088,14 +1125,14 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
       __syncthreads();
     }
     total = 0.0;
-    for (int c = 0; c < a.nch2; ++c) total += s_csum[c];
+    for (int c = 0; c < dc.n; ++c) total += s_csum[c];
   }
   const JobFrame f = job_frame(jb, a.cl, resid);
   if (tid == 0) {
     const double target = jb.us * total;
     double acc = 0.0;
     int cs = -1;
-    for (int c = 0; c < a.nch2; ++c) {
+    for (int c = 0; c < dc.n; ++c) {
       if (acc + s_csum[c] > target) {
         cs = c;
         break;
@@ -1104,7 +1141,7 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
     }
     double tau = target - acc;
     if (cs < 0) {  // rounding left no chunk: take the last chunk with weight
-      for (int c = a.nch2 - 1; c >= 0; --c)
+      for (int c = dc.n - 1; c >= 0; --c)
         if (s_csum[c] > 0.0) {
           cs = c;
           break;
@@ -1123,23 +1160,37 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
     if (tid == 0) *dst = -1;
     return;
   }
-  const int e0 = cs * a.ce;
-  const int per = a.ce / kSampleThreads;  // a multiple of 8
-  const int r0 = min(a.V, e0 + tid * per), r1 = min(a.V, r0 + per);
-  const bool t_al = (((uintptr_t)tp) & 15u) == 0;
-  const bool d_al = !resid || (((uintptr_t)dp) & 15u) == 0;
+  const int e0 = dc.begin(cs), e1 = dc.begin(cs + 1);
+  // contiguous per-thread ranges, a multiple of 8 elements each (8 for the uniform chunks)
+  const int per = (e1 - e0 + kSampleGrain - 1) / kSampleGrain * 8;
+  const int r0 = min(e1, e0 + tid * per), r1 = min(e1, r0 + per);
+  // vector loads need 16-byte aligned ranges: the uniform chunks start at multiples of 8
+  // elements; a statistics chunk of an unaligned row may not
+  const bool t_al = (((uintptr_t)(tp + e0)) & 15u) == 0 && (e0 % 8) == 0;
+  const bool d_al = !resid || ((((uintptr_t)dp) & 15u) == 0 && (e0 % 8) == 0);
   // the thread's weights; with 8 elements per thread (chunks of 8192) they stay in
   // registers for the walk below
+  // the thread's weights: up to 16 elements (chunks of at most 16384) stay in registers
+  // for the walk below
   double s = 0.0;
-  float wv[8];
+  float wv[16];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) wv[q] = 0.f;
-  for (int e = r0; e < r1; e += 8) {
-    job_weights8<TT, TD>(f, tp, dp, t_al, d_al, e, r1, wv);
+  for (int q = 0; q < 16; ++q) wv[q] = 0.f;
+  if (per <= 16) {
+    if (r0 < r1) job_weights8<TT, TD>(f, tp, dp, t_al, d_al, r0, r1, wv);
+    if (r0 + 8 < r1) job_weights8<TT, TD>(f, tp, dp, t_al, d_al, r0 + 8, r1, wv + 8);
     float ws = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ws += wv[q];
-    s += (double)ws;
+    for (int q = 0; q < 16; ++q) ws += wv[q];
+    s = (double)ws;
+  } else {
+    for (int e = r0; e < r1; e += 8) {
+      job_weights8<TT, TD>(f, tp, dp, t_al, d_al, e, r1, wv);
+      float ws = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ws += wv[q];
+      s += (double)ws;
+    }
   }
   double inc = s;
 #pragma unroll
@@ -1154,10 +1205,10 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
   const double E = off + inc - s;
   if (E <= tau && tau < E + s) {
     double run = E;
-    if (per == 8) {
+    if (per <= 16) {
       int hit = -1;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < 16; ++q) {
         run += (double)wv[q];
         if (hit < 0 && r0 + q < r1 && run > tau) hit = r0 + q;
       }
@@ -1198,9 +1249,14 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArg
   const int i = blockIdx.x, tid = threadIdx.x;
   const Job jb = a.jobs[i];
   if (jb.mode == JOB_NONE) return;
-  if (tid < 64) s_csum[tid] = tid < a.nch2 ? a.rsum[(size_t)i * a.nch2 + tid] : 0.0;
+  const bool st = bonus_from_stats(jb, a);
+  if (tid < 64) {
+    if (st) bonus_masses(a, jb, s_csum);
+    else s_csum[tid] = tid < a.nch2 ? a.rsum[(size_t)i * a.nch2 + tid] : 0.0;
+  }
   __syncthreads();
-  sample_draw<TT, TD>(a, i, jb, s_csum);
+  const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
+  sample_draw<TT, TD>(a, i, jb, s_csum, st ? stats_chunks<TT>(a, tp) : uniform_chunks(a));
 }
 
 // Decisions, residual / bonus mass and the draw of one request in one workgroup of
@@ -1231,9 +1287,15 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
   __syncthreads();
   const Job jb = s_job;
   if (jb.mode == JOB_NONE) return;  // uniform over the workgroup
+  const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
+  if (bonus_from_stats(jb, a)) {  // uniform: the masses are known, no pass over the row
+    if (tid < 64) bonus_masses(a, jb, s_csum);
+    __syncthreads();
+    sample_draw<TT, TD>(a, i, jb, s_csum, stats_chunks<TT>(a, tp));
+    return;
+  }
   const bool resid = jb.mode == JOB_RESID;
   const JobFrame f = job_frame(jb, a.cl, resid);
-  const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
   const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
   const bool al = (((uintptr_t)tp) & 15u) == 0 && (!resid || (((uintptr_t)dp) & 15u) == 0);
   const int nblk = (a.V + kSampleGrain - 1) / kSampleGrain;
@@ -1294,7 +1356,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArg
     s_csum[tid] = c;
   }
   __syncthreads();
-  sample_draw<TT, TD>(a, i, jb, s_csum);
+  sample_draw<TT, TD>(a, i, jb, s_csum, uniform_chunks(a));
 }
 
 int g_cus = 0;
@@ -1362,7 +1424,7 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
   const long g = stats_grid(max_items);
   launch(DSP_K_VERIFY_STATS, verify_stats_kernel<TT, TD>, dim3((unsigned)g), dim3(kThreads), 0, s, sa, sa.cu,
          sa.row_req, sa.row_pos);
-  if (4l * pa.R >= 3l * cus) {
+  if (4l * pa.R >= 3l * cus && pa.ncht > 64) {
     // enough requests to give nearly every CU one: decide, stream and draw each request
     // in its own workgroup (no hand-off between launches)
     SampleArgs fa = pa;
@@ -1374,8 +1436,11 @@ void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs&
     // few requests: one CU per request would leave most of the chip idle on the residual
     // rows (two exponentials per element), so the rows are spread over every CU
     launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
+    // one workgroup per (request, chunk) item: most items belong to bonus jobs (masses from
+    // the statistics pass) and exit at once, so a grid-stride loop would only chain their
+    // job loads one after another
     const long ri = (long)pa.R * pa.nch2;
-    const long g2 = ri < (long)cus * 8 ? ri : (long)cus * 8;
+    const long g2 = ri < (1l << 20) ? ri : (1l << 20);
     launch(DSP_K_VERIFY_RESIDUAL, verify_residual_kernel<TT, TD>, dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
     launch(DSP_K_VERIFY_SAMPLE, verify_sample_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
   }
@@ -1458,7 +1523,8 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
     if (t_dtype == DSP_BF16) launch_greedy<uint16_t>(sa, da, s, max_items, tree);
     else launch_greedy<float>(sa, da, s, max_items, tree);
   } else {
-    SampleArgs pa{tgt, ld_t, drf, ld_d_r, ld_d_k, R, K, V, L.sg.nch2, L.sg.ce, cl, jobs, rsum, out_tokens};
+    SampleArgs pa{tgt, ld_t, drf, ld_d_r, ld_d_k, R, K, V, L.sg.nch2, L.sg.ce, cl, jobs, rsum, out_tokens,
+                  tstats, L.ncht};
     const long max_items = (long)L.max_rows * (L.ncht + L.nchd);
     if (t_dtype == DSP_BF16 && d_dtype == DSP_BF16) launch_sampled<uint16_t, uint16_t>(sa, da, pa, s, max_items);
     else if (t_dtype == DSP_BF16) launch_sampled<uint16_t, float>(sa, da, pa, s, max_items);

@@ -307,8 +307,9 @@ int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, i
 /*                                                                          */
 /* Per request, root = anchor with score 0. For depth d = 1..D and every      */
 /* parent p of frontier F_{d-1}: z = L[i, d-1, :] + U[tok(p)] . W (one batched */
-/* Markov call for all parents); children = top-k tokens by (fp32 z desc, id  */
-/* asc); child score s = s(p) + z_v - logsumexp(z) (fp64). F_d = top-F        */
+/* Markov call for all parents); children = top-k tokens by (z desc, id asc),*/
+/* decided on fp32 z (ties within its rounding may go either way); child     */
+/* score s = s(p) + z_v - logsumexp(z) (fp64). F_d = top-F                   */
 /* children by (s desc, parent slot asc, child rank asc). The tree is the     */
 /* top-N of all frontier nodes of all depths by (s desc, depth asc, slot asc),*/
 /* parents re-indexed into that order (parent[j] < j, -1 = root).             */
@@ -323,8 +324,8 @@ int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, i
 /* to bound every parent row's 4th-largest z from below; entries under the   */
 /* bound cannot be among the top 4, so the outputs do not depend on it.      */
 /* A parent row with fewer than topk entries above -2^127 (masked -inf base  */
-/* logits count as absent) sets DSP_STATUS_NONFINITE; its children are then  */
-/* unspecified.                                                              */
+/* logits count as absent), or with a +inf or NaN base logit, sets            */
+/* DSP_STATUS_NONFINITE; its children are then unspecified.                  */
 /* Limits: 1 <= topk <= min(4, V), 1 <= frontier <= 64, topk*frontier <= 256,  */
 /* 1 <= topN <= 1024, D*frontier <= 1024, rank as above.                      */
 /* ------------------------------------------------------------------------ */
@@ -337,6 +338,31 @@ int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t l
                         int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
                         double* node_score, int32_t* n_nodes, uint64_t* anc_mask, int32_t* status,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Calibration of the confidences against a verify  ([S] observability:     */
+/* per-request confidences and calibration metrics such as ECE beside the   */
+/* acceptance ceiling; [N] 5.1: c[i,k] is the probability that position k   */
+/* survives given every earlier position was accepted)                      */
+/*                                                                          */
+/* conf [R, K] fp32 (row stride ld_conf >= K): the confidences the scheduler */
+/* used; cu_seqlens [R+1]: the verify's packing (window n_i = cu[i+1] -     */
+/* cu[i] - 1); decided [R]: drafts accepted over the decided window -- the  */
+/* verify's accepted_len, or its ceiling under cap-accept (-1 = a faulted   */
+/* request: nothing observed). Positions 1..m_i are accepted (outcome 1),   */
+/* position m_i + 1 <= n_i is the first rejection (outcome 0), later ones   */
+/* were never decided. With n_bins equal-width bins of [0, 1] (bin          */
+/* floor(c * n_bins) in fp64, clamped to the range):                        */
+/*   ECE = (1/n) sum_b | sum over bin b of (outcome - c) |  (fp64)          */
+/* = sum_b (n_b/n) |mean outcome - mean c|, 0 when nothing was observed.    */
+/* Outputs (device): ece [R] and n_obs [R] per request; batch [1 + 3*n_bins]*/
+/* = batch ECE over every observed position, then per bin the count, the   */
+/* sum of c and the sum of outcomes. Deterministic (fixed reduction order). */
+/* Limits: R >= 1, 1 <= K <= 64, 1 <= n_bins <= 64. One workgroup.          */
+/* ------------------------------------------------------------------------ */
+int32_t dsp_verify_calibration(const float* conf, int64_t ld_conf, const int32_t* cu_seqlens,
+                               const int32_t* decided, int32_t R, int32_t K, int32_t n_bins,
+                               double* ece, int32_t* n_obs, double* batch, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Read probe (measurement).                                                 */
@@ -374,7 +400,8 @@ int32_t dsp_stream_read(const void* p, size_t bytes, uint32_t* sink, void* strea
 #define DSP_K_SCHEDULE_RANK   11  /* scheduler: ranking of the candidate keys */
 #define DSP_K_CONFIDENCE      12  /* confidence head */
 #define DSP_K_TREE_PROBE      13  /* PCTree: probe tokens of the base-logit rows */
-#define DSP_K_COUNT           14
+#define DSP_K_CALIBRATION     14  /* calibration of the confidences against the verify */
+#define DSP_K_COUNT           15
 int32_t dsp_prof_enable(int32_t mask);
 int32_t dsp_prof_reset(void);
 int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);

@@ -401,3 +401,17 @@ def test_tree_verify_on_pctree_workload_target():
     np.testing.assert_array_equal(host(g["stop_pos"]), o["stop_node"])
     assert np.all(o["accepted_len"] >= planted)
     print("planted mean depth", planted.mean(), "accepted mean", o["accepted_len"].mean())
+
+
+@pytest.mark.parametrize("R,depth,bits", [(5, 0, 0x7F80), (40, 0, 0x7F80), (5, 2, 0x7FC0), (40, 0, 0x7FC0),
+                                          (5, 0, 0xFFC1)])
+def test_tree_nonfinite_base_logit_is_a_fault(R, depth, bits):
+    """A +inf or NaN base logit in request 0's row at one depth sets the non-finite status bit
+    on both of the GEMM's paths (blocks of at most 16 requests add the base logits through
+    the matrix cores: R = 5, and 16 parents per request at depth 3; R = 40 at depth 1 runs
+    per row). Every other request still matches the oracle."""
+    c = workloads.markov_case(R, 3, 3001, rank=64, seed=200 + R + depth + bits)
+    L = c["L"].copy()
+    L[0, depth, 17] = bits
+    c = dict(c, L=L)
+    _check_tree(c, 4, 16, 24, requests=range(1, R), status=dsp.DSP_STATUS_NONFINITE)
