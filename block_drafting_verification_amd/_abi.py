@@ -17,7 +17,7 @@ DSP_SCHED_THRESHOLD = 3
 
 KERNELS = ["VERIFY_STATS", "VERIFY_DECIDE", "VERIFY_RESIDUAL", "VERIFY_SAMPLE", "SCHEDULE", "PACK",
            "MARKOV_GEMM", "MARKOV_MERGE", "TREE_GEMM", "TREE_MERGE", "TREE_FINAL", "SCHEDULE_RANK", "CONFIDENCE",
-           "TREE_PROBE"]
+           "TREE_PROBE", "CALIBRATION"]
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -30,6 +30,7 @@ SIGNATURES = {
     "dsp_version": (_i32, []),
     "dsp_last_error": (ctypes.c_char_p, []),
     "dsp_philox_uniforms": (_i32, [_p, _i64, _u64, _p, _p]),
+    "dsp_verify_calibration": (_i32, [_p, _i64, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "dsp_confidence_head": (_i32, [_p, _i32, _i64, _i64, _p, _i32, _f32, _p, _i32, _i32, _i32, _p, _p, _p]),
     "dsp_schedule_windows_workspace_size": (_sz, [_i32, _i32]),
     "dsp_schedule_windows": (_i32, [_p, _i32, _i32, _p, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _p, _sz,
