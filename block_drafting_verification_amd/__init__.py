@@ -12,6 +12,7 @@ Calls (same names as the C entry points without the ``dsp_`` prefix):
   schedule_windows   -- survival products + hardware-aware prefix scheduler
   pack_ragged        -- front-packed cu_seqlens verify buffer
   verify_rejection   -- batched ragged rejection / greedy / tree verify
+  verify_rejection_noalloc -- the same with the library's fixed scratch (allocates nothing)
   verify_calibration -- ECE of the confidences against a verify's outcomes
   draft_markov_step  -- Markov-head greedy chain
   draft_markov_sample -- Markov-head sampled chain emitting its bf16 draft logits
@@ -28,7 +29,7 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
                    DspError, KERNELS)
 
 __all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection",
-           "verify_calibration", "draft_markov_step",
+           "verify_rejection_noalloc", "verify_calibration", "draft_markov_step",
            "draft_markov_sample", "tree_expand", "schedule_pack",
            "philox_uniforms", "stream_read", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
@@ -265,10 +266,23 @@ def schedule_pack(conf, cost, anchors, drafts, mode=DSP_SCHED_EARLY_STOP, max_to
     return _finish(lib().dsp_schedule_pack, args, res, prepare, (conf, cost, anchors, drafts, ws, arr), stream=stream)
 
 
+def verify_rejection_noalloc(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,
+                             round=0, req_id=None, max_rows=0, want_probs=True, out=None, status=None,
+                             stream=None, round_dev=None, row_req=None, row_pos=None, cap=None,
+                             want_ceiling=False, prepare=False):
+    """verify_rejection through the allocation-free entry point: the library's fixed
+    per-GPU scratch replaces the workspace (batches needing more than 8 MiB of it raise
+    DspError). Pass every output in `out` to allocate nothing here either; calls that
+    overlap on one GPU share that scratch and must not be issued."""
+    return verify_rejection(tgt, cu_seqlens, draft_tok, drf, parent, temperature, seed, round, req_id, max_rows,
+                            want_probs, out, status, stream, round_dev, row_req, row_pos, cap, want_ceiling,
+                            prepare, _noalloc=True)
+
+
 def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperature=1.0, seed=0,
                      round=0, req_id=None, max_rows=0, want_probs=True, out=None, status=None,
                      stream=None, round_dev=None, row_req=None, row_pos=None, cap=None, want_ceiling=False,
-                     prepare=False):
+                     prepare=False, _noalloc=False):
     """Batched ragged verify.
 
     tgt: packed target logits [T_rows, V] (bf16/fp32, unit inner stride);
@@ -322,18 +336,21 @@ def verify_rejection(tgt, cu_seqlens, draft_tok, drf=None, parent=None, temperat
     # bound the rows the device may read by what the target tensor holds
     rows_cap = min(R * (K + 1), tgt.shape[0])
     max_rows = rows_cap if not max_rows else min(int(max_rows), rows_cap)
-    nbytes = lib().dsp_verify_rejection_workspace_size(R, K, V, max_rows, t_dt, d_dt)
-    ws = _workspace(nbytes, dev, prepare, stream)
     args = (_ptr(tgt), t_dt, tgt.stride(0), _ptr(cu_seqlens), _ptr(drf), d_dt, ld_dr, ld_dk,
             _ptr(draft_tok), draft_tok.stride(0), _ptr(parent), R, K, V, max_rows, float(temperature),
             int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(row_req), _ptr(row_pos), _ptr(cap),
-            _ptr(ceiling), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x), _ptr(q_x), _ptr(status), _ptr(ws),
-            ws.numel(), _stream(stream))
+            _ptr(ceiling), _ptr(acc), _ptr(toks), _ptr(stop), _ptr(p_x), _ptr(q_x), _ptr(status))
     res = dict(accepted_len=acc, out_tokens=toks, stop_pos=stop, p_x=p_x, q_x=q_x, status=status)
     if ceiling is not None:
         res["ceiling"] = ceiling
-    return _finish(lib().dsp_verify_rejection, args, res, prepare,
-                   (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, cap, ws), stream=stream)
+    keep = (tgt, cu_seqlens, drf, draft_tok, parent, req_id, round_dev, row_req, row_pos, cap)
+    if _noalloc:
+        return _finish(lib().dsp_verify_rejection_noalloc, args + (_stream(stream),), res, prepare, keep,
+                       stream=stream)
+    nbytes = lib().dsp_verify_rejection_workspace_size(R, K, V, max_rows, t_dt, d_dt)
+    ws = _workspace(nbytes, dev, prepare, stream)
+    return _finish(lib().dsp_verify_rejection, args + (_ptr(ws), ws.numel(), _stream(stream)), res, prepare,
+                   keep + (ws,), stream=stream)
 
 
 def verify_calibration(conf, cu_seqlens, decided, n_bins=10, out=None, stream=None, prepare=False):

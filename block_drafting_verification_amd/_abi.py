@@ -42,6 +42,9 @@ SIGNATURES = {
     "dsp_verify_rejection": (_i32, [_p, _i32, _i64, _p, _p, _i32, _i64, _i64, _p, _i64, _p,
                                     _i32, _i32, _i32, _i32, _f32, _u64, _u64, _p, _p, _p, _p, _p, _p,
                                     _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "dsp_verify_rejection_noalloc": (_i32, [_p, _i32, _i64, _p, _p, _i32, _i64, _i64, _p, _i64, _p,
+                                            _i32, _i32, _i32, _i32, _f32, _u64, _u64, _p, _p, _p, _p, _p, _p,
+                                            _p, _p, _p, _p, _p, _p, _p]),
     "dsp_draft_markov_step_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "dsp_draft_markov_step": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _p, _i32, _i32,
                                      _p, _i64, _p, _p, _p, _sz, _p]),

@@ -38,6 +38,8 @@
 // then one wavefront per request for matching or the tree walk.
 #include <math.h>
 
+#include <mutex>
+
 #include "dsp_internal.h"
 
 namespace dsp {
@@ -1468,16 +1470,48 @@ extern "C" size_t dsp_verify_rejection_workspace_size(int32_t R, int32_t K, int3
   return verify_layout(R, K, V, max_rows, t_dtype, d_dtype).total;
 }
 
-extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
-                                        const int32_t* cu_seqlens, const void* drf, int32_t d_dtype,
-                                        int64_t ld_d_r, int64_t ld_d_k, const int32_t* draft_tok,
-                                        int64_t ld_x, const int32_t* parent, int32_t R, int32_t K,
-                                        int32_t V, int32_t max_rows, float temperature, uint64_t seed,
-                                        uint64_t round, uint64_t* round_dev, const int64_t* req_id,
-                                        const int32_t* row_req, const int32_t* row_pos,
-                                        const int32_t* cap, int32_t* ceiling, int32_t* accepted_len,
-                                        int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x,
-                                        int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+// The allocation-free entry point's scratch: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends. Its size bounds the batches that
+// entry point accepts. Host code never uses the array's name as an address (on the host
+// it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int32_t scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e0 = hipGetDevice(&dev);
+  if (e0 != hipSuccess) return hip_check(e0, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSP_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_check(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DSP_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSP_OK;
+}
+}  // namespace
+
+// Shared by both verify entry points: with noalloc the workspace is the current device's
+// `scratch` (ws and ws_bytes are ignored), after the arguments have been checked.
+static int32_t verify_impl(const void* tgt, int32_t t_dtype, int64_t ld_t, const int32_t* cu_seqlens,
+                           const void* drf, int32_t d_dtype, int64_t ld_d_r, int64_t ld_d_k,
+                           const int32_t* draft_tok, int64_t ld_x, const int32_t* parent, int32_t R, int32_t K,
+                           int32_t V, int32_t max_rows, float temperature, uint64_t seed, uint64_t round,
+                           uint64_t* round_dev, const int64_t* req_id, const int32_t* row_req,
+                           const int32_t* row_pos, const int32_t* cap, int32_t* ceiling, int32_t* accepted_len,
+                           int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x, int32_t* status,
+                           void* ws, size_t ws_bytes, bool noalloc, void* stream) {
   clear_error();
   if (R < 1 || K < 1 || K > 64 || V < 1)
     return fail(DSP_ERR_SHAPE, "need R >= 1, 1 <= K <= 64, V >= 1 (R=%d K=%d V=%d)", R, K, V);
@@ -1504,6 +1538,15 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
     return fail(DSP_ERR_ALIGN, "logits must be aligned to their element size");
   const int ddt = greedy ? DSP_BF16 : d_dtype;
   const VerifyLayout L = verify_layout(R, K, V, max_rows, t_dtype, ddt);
+  if (noalloc) {
+    if (L.total > kNoAllocScratchBytes)
+      return fail(DSP_ERR_WORKSPACE,
+                  "this batch needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                  "(use dsp_verify_rejection with a workspace)", L.total, kNoAllocScratchBytes);
+    const int32_t rc = scratch_address(&ws);
+    if (rc != DSP_OK) return rc;
+    ws_bytes = kNoAllocScratchBytes;
+  }
   if (!ws || ws_bytes < L.total) return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
 
   StatSlot* tstats = (StatSlot*)((uintptr_t)ws + L.off_t);
@@ -1532,4 +1575,34 @@ extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_
     else launch_sampled<float, float>(sa, da, pa, s, max_items);
   }
   return hip_check(hipGetLastError(), "verify launch");
+}
+
+extern "C" int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
+                                        const int32_t* cu_seqlens, const void* drf, int32_t d_dtype,
+                                        int64_t ld_d_r, int64_t ld_d_k, const int32_t* draft_tok,
+                                        int64_t ld_x, const int32_t* parent, int32_t R, int32_t K,
+                                        int32_t V, int32_t max_rows, float temperature, uint64_t seed,
+                                        uint64_t round, uint64_t* round_dev, const int64_t* req_id,
+                                        const int32_t* row_req, const int32_t* row_pos,
+                                        const int32_t* cap, int32_t* ceiling, int32_t* accepted_len,
+                                        int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x,
+                                        int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return verify_impl(tgt, t_dtype, ld_t, cu_seqlens, drf, d_dtype, ld_d_r, ld_d_k, draft_tok, ld_x, parent, R, K,
+                     V, max_rows, temperature, seed, round, round_dev, req_id, row_req, row_pos, cap, ceiling,
+                     accepted_len, out_tokens, stop_pos, p_x, q_x, status, ws, ws_bytes, false, stream);
+}
+
+extern "C" int32_t dsp_verify_rejection_noalloc(const void* tgt, int32_t t_dtype, int64_t ld_t,
+                                                const int32_t* cu_seqlens, const void* drf, int32_t d_dtype,
+                                                int64_t ld_d_r, int64_t ld_d_k, const int32_t* draft_tok,
+                                                int64_t ld_x, const int32_t* parent, int32_t R, int32_t K,
+                                                int32_t V, int32_t max_rows, float temperature, uint64_t seed,
+                                                uint64_t round, uint64_t* round_dev, const int64_t* req_id,
+                                                const int32_t* row_req, const int32_t* row_pos,
+                                                const int32_t* cap, int32_t* ceiling, int32_t* accepted_len,
+                                                int32_t* out_tokens, int32_t* stop_pos, float* p_x, float* q_x,
+                                                int32_t* status, void* stream) {
+  return verify_impl(tgt, t_dtype, ld_t, cu_seqlens, drf, d_dtype, ld_d_r, ld_d_k, draft_tok, ld_x, parent, R, K,
+                     V, max_rows, temperature, seed, round, round_dev, req_id, row_req, row_pos, cap, ceiling,
+                     accepted_len, out_tokens, stop_pos, p_x, q_x, status, nullptr, 0, true, stream);
 }

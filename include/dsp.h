@@ -245,6 +245,30 @@ int32_t dsp_verify_rejection(const void* tgt, int32_t t_dtype, int64_t ld_t,
                              float* p_x, float* q_x, int32_t* status,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* The same verify for callers that cannot allocate device memory (code      */
+/* under HIP graph capture, tight serving loops, harnesses that forbid       */
+/* hipMalloc): no workspace argument and no allocation of any kind. The      */
+/* scratch space is a fixed 8 MiB device array inside the library, one per  */
+/* GPU it runs on, held until the process ends; a batch whose               */
+/* dsp_verify_rejection_workspace_size exceeds 8 MiB is rejected with         */
+/* DSP_ERR_WORKSPACE before anything is launched. The first call on a device */
+/* looks the array's address up (hipGetSymbolAddress) with that device       */
+/* current. Every call on one GPU shares that array: calls that overlap on  */
+/* one GPU (different streams, concurrent threads) race and must not be     */
+/* issued. Nothing needs clearing between calls (every entry a call reads,  */
+/* that call wrote first). Arguments, outputs and errors as dsp_verify_rejection. */
+int32_t dsp_verify_rejection_noalloc(const void* tgt, int32_t t_dtype, int64_t ld_t,
+                                     const int32_t* cu_seqlens,
+                                     const void* drf, int32_t d_dtype, int64_t ld_d_r, int64_t ld_d_k,
+                                     const int32_t* draft_tok, int64_t ld_x, const int32_t* parent,
+                                     int32_t R, int32_t K, int32_t V, int32_t max_rows,
+                                     float temperature, uint64_t seed, uint64_t round,
+                                     uint64_t* round_dev, const int64_t* req_id,
+                                     const int32_t* row_req, const int32_t* row_pos,
+                                     const int32_t* cap, int32_t* ceiling,
+                                     int32_t* accepted_len, int32_t* out_tokens, int32_t* stop_pos,
+                                     float* p_x, float* q_x, int32_t* status, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Markov-head sequential stage, greedy chain  ([N] 4; [P] z_d = L_d +        */
 /* Markov(y_{d-1}))                                                          */
