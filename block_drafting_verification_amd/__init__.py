@@ -16,6 +16,7 @@ Calls (same names as the C entry points without the ``dsp_`` prefix):
   verify_calibration -- ECE of the confidences against a verify's outcomes
   draft_markov_step  -- Markov-head greedy chain
   draft_markov_sample -- Markov-head sampled chain emitting its bf16 draft logits
+  draft_rnn_step     -- greedy chain with the RNN sequential head
   tree_expand        -- PCTree expansion
   philox_uniforms    -- the counter-based uniforms the verify step draws
 """
@@ -29,7 +30,7 @@ from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DS
                    DspError, KERNELS)
 
 __all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection",
-           "verify_rejection_noalloc", "verify_calibration", "draft_markov_step",
+           "verify_rejection_noalloc", "verify_calibration", "draft_markov_step", "draft_rnn_step",
            "draft_markov_sample", "tree_expand", "schedule_pack",
            "philox_uniforms", "stream_read", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
@@ -408,6 +409,41 @@ def draft_markov_step(L, U, Wt, prev_tok, n_steps=None, want_logq=False, out=Non
             _ptr(y), y.stride(0), _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_markov_step, args, dict(y=y, logq=logq, status=status), prepare,
                    (L, U, Wt, prev_tok, ws), stream=stream)
+
+
+def draft_rnn_step(L, h, Gt, A, E, Wot, prev_tok, bias=None, n_steps=None, want_logq=False, out=None, status=None,
+                   stream=None, prepare=False):
+    """Greedy chain with the RNN head. L: bf16 [R, B, V]; h: bf16 [R, B, H] backbone states;
+    Gt: bf16 [r, H]; A: bf16 [r, r]; E, Wot: bf16 [V, r]; bias: float32 [r] or None;
+    prev_tok: int32 [R]. Returns dict(y int32 [R, n], logq float32 [R, n] or None, status)."""
+    _on_gpu(L, h, Gt, A, E, Wot, prev_tok, bias)
+    _need(L.dtype == torch.bfloat16 and L.dim() == 3 and L.stride(2) == 1, "L: bf16 [R, B, V], unit inner stride")
+    R, B, V = L.shape
+    _need(h.dtype == torch.bfloat16 and h.dim() == 3 and h.shape[:2] == (R, B) and h.stride(2) == 1,
+          "h: bf16 [R, B, H], unit inner stride")
+    H = h.shape[2]
+    rank = A.shape[0]
+    _need(A.dtype == torch.bfloat16 and A.shape == (rank, rank) and A.is_contiguous(), "A: contiguous bf16 [r, r]")
+    _need(Gt.dtype == torch.bfloat16 and Gt.shape == (rank, H) and Gt.is_contiguous(), "Gt: contiguous bf16 [r, H]")
+    for t, nm in ((E, "E"), (Wot, "Wot")):
+        _need(t.dtype == torch.bfloat16 and t.shape == (V, rank) and t.is_contiguous(), f"{nm}: contiguous bf16 [V, r]")
+    _need(bias is None or (bias.dtype == torch.float32 and bias.numel() == rank and bias.is_contiguous()),
+          "bias: float32 [r]")
+    n = B if n_steps is None else int(n_steps)
+    _need(1 <= n <= B, "n_steps must be in [1, B]")
+    _need(prev_tok.dtype == torch.int32 and prev_tok.numel() == R and prev_tok.is_contiguous(), "prev_tok: int32 [R]")
+    dev = L.device
+    o = out or {}
+    y = _take(o, "y", lambda: torch.empty(R, n, dtype=torch.int32, device=dev))
+    logq = _take(o, "logq", lambda: torch.empty(R, n, dtype=torch.float32, device=dev)) if want_logq else None
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().dsp_draft_rnn_step_workspace_size(R, V, rank, n), dev, prepare, stream)
+    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(h), DSP_BF16, h.stride(0), h.stride(1), H, _ptr(Gt),
+            _ptr(A), _ptr(E), _ptr(bias), _ptr(Wot), V, rank, _ptr(prev_tok), R, n, _ptr(y), y.stride(0),
+            _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+    return _finish(lib().dsp_draft_rnn_step, args, dict(y=y, logq=logq, status=status), prepare,
+                   (L, h, Gt, A, E, Wot, prev_tok, bias, ws), stream=stream)
 
 
 def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_dev=None, req_id=None,

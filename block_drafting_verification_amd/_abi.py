@@ -17,7 +17,7 @@ DSP_SCHED_THRESHOLD = 3
 
 KERNELS = ["VERIFY_STATS", "VERIFY_DECIDE", "VERIFY_RESIDUAL", "VERIFY_SAMPLE", "SCHEDULE", "PACK",
            "MARKOV_GEMM", "MARKOV_MERGE", "TREE_GEMM", "TREE_MERGE", "TREE_FINAL", "SCHEDULE_RANK", "CONFIDENCE",
-           "TREE_PROBE", "CALIBRATION"]
+           "TREE_PROBE", "CALIBRATION", "RNN_MEMO", "RNN_PROJ"]
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -45,6 +45,9 @@ SIGNATURES = {
     "dsp_verify_rejection_noalloc": (_i32, [_p, _i32, _i64, _p, _p, _i32, _i64, _i64, _p, _i64, _p,
                                             _i32, _i32, _i32, _i32, _f32, _u64, _u64, _p, _p, _p, _p, _p, _p,
                                             _p, _p, _p, _p, _p, _p, _p]),
+    "dsp_draft_rnn_step_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "dsp_draft_rnn_step": (_i32, [_p, _i32, _i64, _i64, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _i32,
+                                  _p, _i32, _i32, _p, _i64, _p, _p, _p, _sz, _p]),
     "dsp_draft_markov_step_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "dsp_draft_markov_step": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _p, _i32, _i32,
                                      _p, _i64, _p, _p, _p, _sz, _p]),

@@ -146,6 +146,9 @@ struct GemmArgs {
   // tree: per parent row, a value t with every entry of the row's top 4 strictly above
   // it (or NULL: no bound); entries at or below t are not offered to the top-4 list
   const float* theta;
+  // rows of U the parent rows may name (0: V, the token table). The RNN head passes its
+  // memo rows here (row r of the memo table for parent row r).
+  int32_t u_rows;
 };
 
 // 16-byte slot of (row, vector) in a swizzled LDS tile whose rows hold `nv` vectors
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   int tok = 0;
   if (rvalid) {
     tok = a.row_tok[(size_t)row * a.ld_tok];
-    if (tok < 0 || tok >= a.V) {
+    if (tok < 0 || tok >= (a.u_rows > 0 ? a.u_rows : a.V)) {
       if (g == 0 && lane < 32) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
       tok = 0;
     }
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   // issued like the ring's loads (the compiler would otherwise keep them "pending" around
   // the stage loop and drain the ring for them); the first stage's wait covers them
   auto load_u = [&]() {
-    const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)a.V * a.rank * 2));
+    const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)(a.u_rows > 0 ? a.u_rows : a.V) * a.rank * 2));
     const uint32_t ubase = (uint32_t)(((size_t)tok * a.rank + 8 * (lane >> 5)) * 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -1344,6 +1347,121 @@ int ksteps(int rank) {
   return ks;
 }
 
+// ---------------------------------------------------------------- RNN head
+// The memo update of the RNN sequential head (DSpark study notes, section 4):
+//   s_d = tanh(s_{d-1} A + E[y_{d-1}] + h_d G + b),  s_0 = 0,
+// in fp64 throughout (bf16 inputs widen exactly), so the memo agrees with any other
+// fp64 evaluation to rounding of the last bits; it enters the vocabulary projection
+// rounded to bf16 (nearest, ties to even), through the Markov GEMM with the memo rows
+// as the parent rows' factor rows.
+
+// P[m, j] = sum_k h[m, k] Gt[j, k] for m = (request, position) rows: a fp64 GEMM tile of
+// 64 rows x 64 memo entries per 256-thread workgroup, 4 x 4 per thread, k staged in LDS.
+struct RnnProjArgs {
+  const uint16_t* h;
+  int64_t ldh_r, ldh_k;
+  int32_t H, n;            // hidden size, positions per request
+  const uint16_t* Gt;      // [r, H]
+  int32_t rank, rows;      // rows = R * n
+  double* P;               // [rows, rank]
+};
+constexpr int kPT = 64;    // tile rows / columns
+constexpr int kPK = 32;    // k per LDS stage
+
+__global__ __launch_bounds__(256) void rnn_proj_kernel(RnnProjArgs a) {
+  __shared__ double sh[kPK][kPT + 1];
+  __shared__ double sg[kPK][kPT + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.x * kPT, j0 = blockIdx.y * kPT;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < a.H; k0 += kPK) {
+    // stage 64 rows x 32 k of h and 64 columns x 32 k of Gt (k-major in LDS), zero-padded
+    for (int e = tid; e < kPT * kPK; e += 256) {
+      const int rr = e / kPK, kk = e % kPK, k = k0 + kk;
+      const int m = m0 + rr, j = j0 + rr;
+      double hv = 0.0, gv = 0.0;
+      if (m < a.rows && k < a.H) {
+        const int i = m / a.n, d = m % a.n;
+        hv = (double)bf16_val(a.h[(size_t)i * a.ldh_r + (size_t)d * a.ldh_k + k]);
+      }
+      if (j < a.rank && k < a.H) gv = (double)bf16_val(a.Gt[(size_t)j * a.H + k]);
+      sh[kk][rr] = hv;
+      sg[kk][rr] = gv;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kPK; ++kk) {
+      double hr[4], gc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hr[q] = sh[kk][ty * 4 + q];
+        gc[q] = sg[kk][tx * 4 + q];
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fma(hr[p], gc[q], acc[p][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = m0 + ty * 4 + p, j = j0 + tx * 4 + q;
+      if (m < a.rows && j < a.rank) a.P[(size_t)m * a.rank + j] = acc[p][q];
+    }
+}
+
+struct RnnMemoArgs {
+  const int32_t* prev;     // previous token of each request at prev[i * ld_prev]
+  int64_t ld_prev;
+  const uint16_t* A;       // [r, r]
+  const uint16_t* E;       // [V, r]
+  const float* bias;       // [r] or NULL
+  const double* P;         // [R * n, r]
+  int32_t n, d, rank, V;
+  double* memo;            // [R, r] fp64, updated in place
+  uint16_t* memo_bf;       // [R, r] bf16 bits for the projection
+  int32_t* idx;            // [R]: row i of the memo table for parent row i
+  int32_t* status;
+};
+
+// fp64 -> bf16, nearest with ties to even, in one rounding: round to fp32 toward zero,
+// make it odd if that was inexact (round to odd keeps the two extra bits the final
+// rounding needs), then the usual fp32 -> bf16 nearest-even.
+__device__ __forceinline__ uint16_t bf16_from_double(double x) {
+  float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x) u |= 1u;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void rnn_memo_kernel(RnnMemoArgs a) {
+  extern __shared__ double sprev[];  // [rank]
+  const int i = blockIdx.x, tid = threadIdx.x;
+  double* mrow = a.memo + (size_t)i * a.rank;
+  for (int k = tid; k < a.rank; k += 256) sprev[k] = a.d == 0 ? 0.0 : mrow[k];
+  int tok = a.prev[(size_t)i * a.ld_prev];
+  if (tok < 0 || tok >= a.V) {
+    if (tid == 0) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+    tok = 0;
+  }
+  if (tid == 0) a.idx[i] = i;
+  __syncthreads();
+  const double* prow = a.P + ((size_t)i * a.n + a.d) * a.rank;
+  for (int j = tid; j < a.rank; j += 256) {
+    double pre = 0.0;
+    for (int k = 0; k < a.rank; ++k) pre = __builtin_fma(sprev[k], (double)bf16_val(a.A[(size_t)k * a.rank + j]), pre);
+    pre += (double)bf16_val(a.E[(size_t)tok * a.rank + j]);
+    pre += prow[j];
+    if (a.bias) pre += (double)a.bias[j];
+    const double sj = tanh(pre);
+    mrow[j] = sj;
+    a.memo_bf[(size_t)i * a.rank + j] = bf16_from_double(sj);
+  }
+}
+
 size_t gemm_lds_bytes(int ks, int mode) {
   return (size_t)2 * (kTS * 2 * ks + kTR * 4) * 16 + (mode == MODE_SAMPLE ? (size_t)kWaves * 32 * kZS : 0);
 }
@@ -1487,6 +1605,84 @@ extern "C" int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t
     if (rc) return rc;
     ChainMergeArgs ma{(const ChainPart*)ws, G, R, d, y, ld_y, logq};
     launch(DSP_K_MARKOV_MERGE, chain_merge_kernel, dim3(R), dim3(64), 0, s, ma);
+    rc = hip_check(hipGetLastError(), "chain merge launch");
+    if (rc) return rc;
+  }
+  return DSP_OK;
+}
+
+struct RnnLayout {
+  size_t off_part, off_P, off_memo, off_bf, off_idx, total;
+};
+static RnnLayout rnn_layout(int R, int V, int rank, int n) {
+  RnnLayout L;
+  size_t off = 0;
+  L.off_part = off;
+  off = align_up(off + (size_t)pick_groups(R, V) * R * sizeof(ChainPart), 256);
+  L.off_P = off;
+  off = align_up(off + (size_t)R * n * rank * sizeof(double), 256);
+  L.off_memo = off;
+  off = align_up(off + (size_t)R * rank * sizeof(double), 256);
+  L.off_bf = off;
+  off = align_up(off + (size_t)R * rank * sizeof(uint16_t), 256);
+  L.off_idx = off;
+  off = align_up(off + (size_t)R * sizeof(int32_t), 256);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t dsp_draft_rnn_step_workspace_size(int32_t R, int32_t V, int32_t rank, int32_t n_steps) {
+  if (R < 1 || V < 1 || rank < 1 || n_steps < 1) return 0;
+  return rnn_layout(R, V, rank, n_steps).total;
+}
+
+extern "C" int32_t dsp_draft_rnn_step(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
+                                      const void* h, int32_t h_dtype, int64_t ldh_r, int64_t ldh_k, int32_t H,
+                                      const void* Gt, const void* A, const void* E, const float* bias,
+                                      const void* Wot, int32_t V, int32_t rank, const int32_t* prev_tok,
+                                      int32_t R, int32_t n_steps, int32_t* y, int64_t ld_y, float* logq,
+                                      int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int32_t rc = check_markov_common(L, l_dtype, E, Wot, V, rank);
+  if (rc) return rc;
+  if (h_dtype != DSP_BF16) return fail(DSP_ERR_DTYPE, "h must be bf16");
+  if (!h || !Gt || !A) return fail(DSP_ERR_NULL, "h, Gt and A are required");
+  if (H < 1) return fail(DSP_ERR_SHAPE, "H must be >= 1");
+  if (R < 1 || n_steps < 1) return fail(DSP_ERR_SHAPE, "need R >= 1 and n_steps >= 1");
+  if (!prev_tok || !y || !status) return fail(DSP_ERR_NULL, "prev_tok, y and status are required");
+  if (ld_y < n_steps) return fail(DSP_ERR_SHAPE, "ld_y < n_steps");
+  if (ldL_d < V || ldL_r < (int64_t)(n_steps - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
+  if (ldh_k < H || ldh_r < (int64_t)(n_steps - 1) * ldh_k + H) return fail(DSP_ERR_SHAPE, "h strides too small");
+  if (((uintptr_t)h) % 2 || ((uintptr_t)Gt) % 2 || ((uintptr_t)A) % 2) return fail(DSP_ERR_ALIGN, "h, Gt, A: 2-byte aligned");
+  const RnnLayout lay = rnn_layout(R, V, rank, n_steps);
+  if (!ws || ws_bytes < lay.total) return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", lay.total);
+  hipStream_t s = (hipStream_t)stream;
+  ChainPart* part = (ChainPart*)((uintptr_t)ws + lay.off_part);
+  double* P = (double*)((uintptr_t)ws + lay.off_P);
+  double* memo = (double*)((uintptr_t)ws + lay.off_memo);
+  uint16_t* mbf = (uint16_t*)((uintptr_t)ws + lay.off_bf);
+  int32_t* idx = (int32_t*)((uintptr_t)ws + lay.off_idx);
+  // the backbone states' contribution to every position's update, up front
+  RnnProjArgs pa{(const uint16_t*)h, ldh_r, ldh_k, H, n_steps, (const uint16_t*)Gt, rank, R * n_steps, P};
+  launch(DSP_K_RNN_PROJ, rnn_proj_kernel, dim3((unsigned)((R * n_steps + kPT - 1) / kPT), (unsigned)((rank + kPT - 1) / kPT)),
+         dim3(256), 0, s, pa);
+  rc = hip_check(hipGetLastError(), "rnn projection launch");
+  if (rc) return rc;
+  const int G = pick_groups(R, V);
+  for (int d = 0; d < n_steps; ++d) {
+    RnnMemoArgs ma{d == 0 ? prev_tok : y + (d - 1), d == 0 ? 1 : ld_y, (const uint16_t*)A, (const uint16_t*)E,
+                   bias, P, n_steps, d, rank, V, memo, mbf, idx, status};
+    launch(DSP_K_RNN_MEMO, rnn_memo_kernel, dim3(R), dim3(256), (uint32_t)(rank * sizeof(double)), s, ma);
+    rc = hip_check(hipGetLastError(), "rnn memo launch");
+    if (rc) return rc;
+    GemmArgs ga{mbf, (const uint16_t*)Wot, V, rank, idx, 1, (const uint16_t*)L, ldL_r, ldL_d, d, R, 1, G, part,
+                status};
+    ga.u_rows = R;
+    rc = logq ? launch_gemm<MODE_ARGMAX_LSE>(DSP_K_MARKOV_GEMM, ga, s)
+              : launch_gemm<MODE_ARGMAX>(DSP_K_MARKOV_GEMM, ga, s);
+    if (rc) return rc;
+    ChainMergeArgs mg{part, G, R, d, y, ld_y, logq};
+    launch(DSP_K_MARKOV_MERGE, chain_merge_kernel, dim3(R), dim3(64), 0, s, mg);
     rc = hip_check(hipGetLastError(), "chain merge launch");
     if (rc) return rc;
   }

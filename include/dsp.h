@@ -327,6 +327,35 @@ int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64_t ldL_r, i
                                 void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* RNN sequential head, greedy chain  ([N] 4, "RNN head": a memo that holds  */
+/* the whole draft so far, updated once per position from the previous     */
+/* memo, the previous token and the current backbone state; its correction  */
+/* is added to the base logits as the Markov head's is)                     */
+/*                                                                          */
+/* s_0 = 0; for d = 1..n_steps, with y_0 = prev_tok[i]:                      */
+/*   s_d = tanh(s_{d-1} A + E[y_{d-1}] + h_d G + bias)      (fp64, r entries) */
+/*   z_d = L[i, d-1, :] + bf16(s_d) . W_o                   (MFMA, fp32 acc)  */
+/*   y_d = argmax z_d (lowest id on ties of the fp32 values), logq as the    */
+/*   Markov step. bf16(.) rounds to nearest, ties to even, from fp64.        */
+/* h: bf16 backbone states, element (i, d, k) at h + i*ldh_r + d*ldh_k + k    */
+/* (k < H). Gt: bf16 [r, H] (G transposed: memo entry j's weights over the  */
+/* state contiguous); A: bf16 [r, r] row-major (s A); E: bf16 [V, r] token  */
+/* table (16-byte aligned); bias: fp32 [r] or NULL; Wot: bf16 [V, r] (W_o   */
+/* stored vocab-major, as Wt). L, y, logq, status as dsp_draft_markov_step. */
+/* The state projection h G for every position is computed first, in fp64  */
+/* (exact products, fp64 sums): it costs 2*R*n*H*r flops on the fp64 units. */
+/* A previous token outside [0, V) sets DSP_STATUS_TOKEN_RANGE.             */
+/* Limits: rank a multiple of 32 in [32, 512], H >= 1.                      */
+/* ------------------------------------------------------------------------ */
+size_t dsp_draft_rnn_step_workspace_size(int32_t R, int32_t V, int32_t rank, int32_t n_steps);
+int32_t dsp_draft_rnn_step(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
+                           const void* h, int32_t h_dtype, int64_t ldh_r, int64_t ldh_k, int32_t H,
+                           const void* Gt, const void* A, const void* E, const float* bias,
+                           const void* Wot, int32_t V, int32_t rank, const int32_t* prev_tok,
+                           int32_t R, int32_t n_steps, int32_t* y, int64_t ld_y, float* logq,
+                           int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* PCTree expansion  ([P] "the chain becomes a tree")                         */
 /*                                                                          */
 /* Per request, root = anchor with score 0. For depth d = 1..D and every      */
@@ -425,7 +454,9 @@ int32_t dsp_stream_read(const void* p, size_t bytes, uint32_t* sink, void* strea
 #define DSP_K_CONFIDENCE      12  /* confidence head */
 #define DSP_K_TREE_PROBE      13  /* PCTree: probe tokens of the base-logit rows */
 #define DSP_K_CALIBRATION     14  /* calibration of the confidences against the verify */
-#define DSP_K_COUNT           15
+#define DSP_K_RNN_MEMO        15  /* RNN head: memo update */
+#define DSP_K_RNN_PROJ        16  /* RNN head: projection of the backbone states */
+#define DSP_K_COUNT           17
 int32_t dsp_prof_enable(int32_t mask);
 int32_t dsp_prof_reset(void);
 int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);

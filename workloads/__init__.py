@@ -28,6 +28,9 @@ Recipes (N(m, s) = normal with mean m and standard deviation s):
   softmax); additive cost table c(n) = 1.0 + 0.05 n.
 * Markov chain: R=256, B=16, V=151,936, rank 256; L ~ N(0, 3) bf16;
   U [V, r], W [r, V] ~ N(0, 0.02) bf16; anchors uniform over the vocabulary.
+* RNN sequential head: the Markov case's L, anchors and second factor (as W_o); backbone
+  states h [R, B, H] ~ N(0, 1) bf16; A [r, r] ~ N(0, 1/sqrt(r)), E [V, r] ~ N(0, 0.5),
+  G [H, r] ~ N(0, 0.5/sqrt(H)) (stored transposed), bias ~ N(0, 0.1).
 * PCTree + tree verify: R=128, D=16, V=129,280, rank 256, k=4, F=16, N=64;
   L, U, W as the Markov chain; target logits for the root and each tree node ~ N(0, 3) bf16.
 
@@ -214,6 +217,27 @@ def markov_case(R, B, V, rank=256, seed=1004, l_sigma=3.0, w_sigma=0.02):
     W = f32_to_bf16_bits(rng.standard_normal((rank, V), dtype=np.float32) * np.float32(w_sigma))
     anchors = rng.integers(0, V, size=R).astype(np.int32)
     return dict(L=L, U=U, W=W, anchors=anchors, R=R, B=B, V=V, rank=rank)
+
+
+def rnn_case(R, B, V, rank=256, H=4096, seed=1007, wo_scale=1.0):
+    """Inputs of the RNN sequential head: the Markov case's base logits L, anchors and
+    second factor (as W_o, times wo_scale), plus backbone states h [R, B, H] ~ N(0, 1),
+    memo-to-memo A [r, r] ~ N(0, 1/sqrt(r)), token table E [V, r] ~ N(0, 0.5), state
+    projection G [H, r] ~ N(0, 0.5/sqrt(H)) stored transposed (Gt [r, H]) and a bias
+    [r] ~ N(0, 0.1); all bf16 bits except the float32 bias."""
+    c = markov_case(R, B, V, rank=rank, seed=seed)
+    rng = _rng(seed + 3)
+    Wo = bf16_bits_to_f32(c.pop("W")) * np.float32(wo_scale)
+    c.pop("U")
+    h = np.empty((R, B, H), dtype=np.uint16)
+    for i in range(R):
+        h[i] = f32_to_bf16_bits(rng.standard_normal((B, H), dtype=np.float32))
+    c.update(Wo=f32_to_bf16_bits(Wo), h=h, H=H,
+             A=f32_to_bf16_bits(rng.standard_normal((rank, rank), dtype=np.float32) / np.float32(np.sqrt(rank))),
+             E=f32_to_bf16_bits(rng.standard_normal((V, rank), dtype=np.float32) * np.float32(0.5)),
+             Gt=f32_to_bf16_bits(rng.standard_normal((rank, H), dtype=np.float32) * np.float32(0.5 / np.sqrt(H))),
+             bias=(rng.standard_normal(rank) * 0.1).astype(np.float32))
+    return c
 
 
 def markov_chain():
