@@ -14,6 +14,7 @@ of the same data (every window the full block: 8,448 logit rows, 2.567 GB).
 Other workloads (--workload):
   dense-verify      64 requests x K=7 x V=151,936, full-block windows
   markov-chain      Markov-head greedy chain (256 requests x 16 steps, rank 256)
+  rnn-chain         RNN-head greedy chain (256 x 16, rank 256, backbone hidden size 4096)
   pctree            PCTree expansion (128 x depth 16, k=4, F=16, N=64) + greedy tree verify
   cycle             sampled Markov draft (256 x 16, emitting its bf16 rows) -> confidence head
                     -> schedule -> pack -> verify
@@ -54,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scheduled-verify",
-                    choices=["scheduled-verify", "dense-verify", "markov-chain", "pctree", "cycle", "copy"])
+                    choices=["scheduled-verify", "dense-verify", "markov-chain", "rnn-chain", "pctree", "cycle", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the parallel oracle sample")
     ap.add_argument("--cpu-single-seconds", type=float, default=4.0, help="wall budget of the 1-core sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -433,6 +434,56 @@ def bench_markov(args, c, cpu):
     return res
 
 
+# ---------------------------------------------------------------- RNN head
+def rnn_cpu(c, args):
+    import numpy as np
+    import workloads
+    from oracle import rnn as orn
+    f = workloads.bf16_bits_to_f32
+    A, E, G = f(c["A"]).astype(np.float64), f(c["E"]).astype(np.float64), f(c["Gt"]).astype(np.float64).T
+    Wo, b = f(c["Wo"]).astype(np.float64), c["bias"].astype(np.float64)
+
+    def one(i):
+        orn.rnn_chain(f(c["L"][i:i + 1]), f(c["h"][i:i + 1]), A, E, G, b, Wo, c["anchors"][i:i + 1])
+        return c["B"]
+    return cpu_baseline(one, list(range(c["R"])), args.cpu_seconds, args.cpu_single_seconds,
+                        "drafted tokens/s", "oracle RNN-head chain of whole requests (all 16 steps)")
+
+
+def bench_rnn(args, c, cpu):
+    import torch
+    import block_drafting_verification_amd as dsp
+
+    dev = torch.device("cuda", 0)
+    R, B, V, r, H = c["R"], c["B"], c["V"], c["rank"], c["H"]
+    L, h, Gt, A, E = (_bf16(dev, c[k]) for k in ("L", "h", "Gt", "A", "E"))
+    Wot = _bf16(dev, c["Wo"].T)
+    bias = _gpu(dev, c["bias"])
+    a = torch.from_numpy(c["anchors"]).to(dev)
+
+    def make_step(stream):
+        return dsp.draft_rnn_step(L, h, Gt, A, E, Wot, a, bias=bias, stream=stream, prepare=True)
+
+    ph = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "RNN_MEMO", "RNN_PROJ"], not args.no_flush)
+    elapsed, timing = timing_record(ph, args.steps)
+    kern = ph["kernels"]
+    g = kern["MARKOV_GEMM"]["avg_us"]
+    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 // B
+    roof = hbm_roofline("markov_gemm (memo rows as factor rows)", bytes_launch, g, None)
+    pj = kern["RNN_PROJ"]["avg_us"]
+    roof["state_projection"] = dict(kernel="rnn_proj", avg_us=pj, fp64_tflops=2.0 * R * B * H * r / (pj * 1e-6) / 1e12,
+                                    fp64_peak_tflops=78.6)
+    res = dict(
+        metric="drafted tokens/sec", value=R * B * args.steps / elapsed, unit="tokens/s", n_gpus=1,
+        steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16 (projection), f64 (memo)", data="synthetic",
+        config=dict(workload="RNN-head greedy chain: 256 requests, 16 steps, V=151936, rank 256, hidden 4096"),
+        roofline=roof, kernels=kern, timing=timing)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    return res
+
+
 # ---------------------------------------------------------------- PCTree
 def tree_cpu(c, args):
     import numpy as np
@@ -652,6 +703,10 @@ def main():
         import workloads
         c = workloads.markov_chain()
         cpu = markov_cpu(c, args) if want_cpu else None
+    elif w == "rnn-chain":
+        import workloads
+        c = workloads.rnn_case(256, 16, workloads.V_QWEN3, 256, H=4096, seed=1007)
+        cpu = rnn_cpu(c, args) if want_cpu else None
     elif w == "pctree":
         import workloads
         c = workloads.pctree()
@@ -667,6 +722,8 @@ def main():
         res = bench_verify(args, w, c, cpu)
     elif w == "markov-chain":
         res = bench_markov(args, c, cpu)
+    elif w == "rnn-chain":
+        res = bench_rnn(args, c, cpu)
     elif w == "cycle":
         res = bench_cycle(args, c, cpu)
     else:

@@ -1356,7 +1356,9 @@ int ksteps(int rank) {
 // as the parent rows' factor rows.
 
 // P[m, j] = sum_k h[m, k] Gt[j, k] for m = (request, position) rows: a fp64 GEMM tile of
-// 64 rows x 64 memo entries per 256-thread workgroup, 4 x 4 per thread, k staged in LDS.
+// 64 rows x 64 memo entries per 256-thread workgroup, 4 x 4 outputs per thread. k moves
+// in chunks of 64: each thread fetches its two 16-byte vectors of h and of Gt for the
+// next chunk while the current one (widened to fp32 in LDS, exact for bf16) is used.
 struct RnnProjArgs {
   const uint16_t* h;
   int64_t ldh_r, ldh_k;
@@ -1366,37 +1368,72 @@ struct RnnProjArgs {
   double* P;               // [rows, rank]
 };
 constexpr int kPT = 64;    // tile rows / columns
-constexpr int kPK = 32;    // k per LDS stage
+constexpr int kPK = 64;    // k per chunk
 
 __global__ __launch_bounds__(256) void rnn_proj_kernel(RnnProjArgs a) {
-  __shared__ double sh[kPK][kPT + 1];
-  __shared__ double sg[kPK][kPT + 1];
+  __shared__ float sh[kPK][kPT + 4];
+  __shared__ float sg[kPK][kPT + 4];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int m0 = blockIdx.x * kPT, j0 = blockIdx.y * kPT;
-  double acc[4][4] = {};
-  for (int k0 = 0; k0 < a.H; k0 += kPK) {
-    // stage 64 rows x 32 k of h and 64 columns x 32 k of Gt (k-major in LDS), zero-padded
-    for (int e = tid; e < kPT * kPK; e += 256) {
-      const int rr = e / kPK, kk = e % kPK, k = k0 + kk;
+  // this thread's two (row, 8-k group) slots of each tile: slot e = tid + 256 q covers
+  // row e / 8 and k = 8 (e % 8) .. + 8
+  const bool vec = (a.H % 8) == 0 && (a.ldh_k % 8) == 0 && (a.ldh_r % 8) == 0 &&
+                   ((uintptr_t)a.h % 16) == 0 && ((uintptr_t)a.Gt % 16) == 0;
+  auto fetch = [&](int k0, uint32_t (*hv)[4], uint32_t (*gv)[4]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q, rr = e >> 3, kk = 8 * (e & 7), k = k0 + kk;
       const int m = m0 + rr, j = j0 + rr;
-      double hv = 0.0, gv = 0.0;
-      if (m < a.rows && k < a.H) {
-        const int i = m / a.n, d = m % a.n;
-        hv = (double)bf16_val(a.h[(size_t)i * a.ldh_r + (size_t)d * a.ldh_k + k]);
+      const int i = m / a.n, d = m % a.n;
+      const uint16_t* hp = a.h + (size_t)i * a.ldh_r + (size_t)d * a.ldh_k + k;
+      const uint16_t* gp = a.Gt + (size_t)j * a.H + k;
+      if (vec && m < a.rows && k + 8 <= a.H) {
+        const uint4 w = *(const uint4*)hp;
+        hv[q][0] = w.x; hv[q][1] = w.y; hv[q][2] = w.z; hv[q][3] = w.w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t lo = (m < a.rows && k + 2 * t < a.H) ? hp[2 * t] : 0u;
+          const uint32_t hi = (m < a.rows && k + 2 * t + 1 < a.H) ? hp[2 * t + 1] : 0u;
+          hv[q][t] = lo | (hi << 16);
+        }
       }
-      if (j < a.rank && k < a.H) gv = (double)bf16_val(a.Gt[(size_t)j * a.H + k]);
-      sh[kk][rr] = hv;
-      sg[kk][rr] = gv;
+      if (vec && j < a.rank && k + 8 <= a.H) {
+        const uint4 w = *(const uint4*)gp;
+        gv[q][0] = w.x; gv[q][1] = w.y; gv[q][2] = w.z; gv[q][3] = w.w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t lo = (j < a.rank && k + 2 * t < a.H) ? gp[2 * t] : 0u;
+          const uint32_t hi = (j < a.rank && k + 2 * t + 1 < a.H) ? gp[2 * t + 1] : 0u;
+          gv[q][t] = lo | (hi << 16);
+        }
+      }
+    }
+  };
+  double acc[4][4] = {};
+  uint32_t hv[2][4], gv[2][4];
+  fetch(0, hv, gv);
+  for (int k0 = 0; k0 < a.H; k0 += kPK) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q, rr = e >> 3, kk = 8 * (e & 7);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sh[kk + 2 * t][rr] = bf16_lo(hv[q][t]);
+        sh[kk + 2 * t + 1][rr] = bf16_hi(hv[q][t]);
+        sg[kk + 2 * t][rr] = bf16_lo(gv[q][t]);
+        sg[kk + 2 * t + 1][rr] = bf16_hi(gv[q][t]);
+      }
     }
     __syncthreads();
-#pragma unroll 4
+    if (k0 + kPK < a.H) fetch(k0 + kPK, hv, gv);  // in flight during this chunk's products
+#pragma unroll 8
     for (int kk = 0; kk < kPK; ++kk) {
-      double hr[4], gc[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        hr[q] = sh[kk][ty * 4 + q];
-        gc[q] = sg[kk][tx * 4 + q];
-      }
+      const float4 h4 = *(const float4*)&sh[kk][ty * 4];
+      const float4 g4 = *(const float4*)&sg[kk][tx * 4];
+      const double hr[4] = {(double)h4.x, (double)h4.y, (double)h4.z, (double)h4.w};
+      const double gc[4] = {(double)g4.x, (double)g4.y, (double)g4.z, (double)g4.w};
 #pragma unroll
       for (int p = 0; p < 4; ++p)
 #pragma unroll
@@ -1452,7 +1489,14 @@ __global__ __launch_bounds__(256) void rnn_memo_kernel(RnnMemoArgs a) {
   const double* prow = a.P + ((size_t)i * a.n + a.d) * a.rank;
   for (int j = tid; j < a.rank; j += 256) {
     double pre = 0.0;
-    for (int k = 0; k < a.rank; ++k) pre = __builtin_fma(sprev[k], (double)bf16_val(a.A[(size_t)k * a.rank + j]), pre);
+    // 32 loads of A in flight, then their products in order (rank is a multiple of 32)
+    for (int k0 = 0; k0 < a.rank; k0 += 32) {
+      uint16_t av[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) av[q] = a.A[(size_t)(k0 + q) * a.rank + j];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) pre = __builtin_fma(sprev[k0 + q], (double)bf16_val(av[q]), pre);
+    }
     pre += (double)bf16_val(a.E[(size_t)tok * a.rank + j]);
     pre += prow[j];
     if (a.bias) pre += (double)a.bias[j];
