@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--cpu-single-seconds", type=float, default=4.0, help="wall budget of the 1-core sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="diagnostic: no cache flush between timed steps")
+    ap.add_argument("--chain-persistent", action="store_true",
+                    help="markov-chain: all 16 steps in one persistent launch (default: one launch per step)")
+    ap.add_argument("--l-layout", default="row-major", choices=["row-major", "token-major"],
+                    help="chain workloads: base logits [R, B, V] (row-major) or [B, V, R] (token-major)")
     return ap.parse_args()
 
 
@@ -246,6 +250,14 @@ def _bf16(dev, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def _chain_l(dev, bits, args):
+    """Base logits [R, B, V] on the GPU, row-major or (a [B, V, R] buffer) token-major."""
+    import numpy as np
+    if args.l_layout == "row-major":
+        return _bf16(dev, bits)
+    return _bf16(dev, np.transpose(bits, (1, 2, 0))).permute(2, 0, 1)
+
+
 def _gpu(dev, a):
     import numpy as np
     import torch
@@ -403,31 +415,45 @@ def bench_markov(args, c, cpu):
 
     dev = torch.device("cuda", 0)
     R, B, V, r = c["R"], c["B"], c["V"], c["rank"]
-    L, U, Wt = _bf16(dev, c["L"]), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
+    L, U, Wt = _chain_l(dev, c["L"], args), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
     a = torch.from_numpy(c["anchors"]).to(dev)
 
     def make_step(stream):
         return dsp.draft_markov_step(L, U, Wt, a, stream=stream, prepare=True)
 
-    ph = run_phases(make_step, args.steps, args.warmup, ["MARKOV_GEMM", "MARKOV_MERGE"], not args.no_flush)
+    persistent = args.chain_persistent
+    dsp.set_option("chain_persistent", int(persistent))
+    try:
+        ph = run_phases(make_step, args.steps, args.warmup,
+                        ["CHAIN_PERSIST" if persistent else "MARKOV_GEMM", "MARKOV_MERGE"], not args.no_flush)
+    finally:
+        dsp.set_option("chain_persistent", 0)
     elapsed, timing = timing_record(ph, args.steps)
     kern = ph["kernels"]
-    g = kern["MARKOV_GEMM"]["avg_us"]
-    # algorithmic bytes of one launch (one step over every request): the step's L rows, the
-    # previous tokens' U rows, and W counted once per 16-step call (1/16 of it per step)
-    bytes_launch = R * V * 2 + R * r * 2 + V * r * 2 // B
-    flops_launch = 2.0 * R * r * V
-    roof = hbm_roofline("markov_gemm", bytes_launch, g, traffic_from_profiles("markov.hip", "markov_gemm",
-                                                                              "markov-chain"))
+    call_bytes = R * B * V * 2 + R * B * r * 2 + V * r * 2
+    if persistent:
+        # one launch = the whole 16-step chain: every step's L rows and U rows, W once
+        g = kern["CHAIN_PERSIST"]["avg_us"]
+        bytes_launch, flops_launch, name = call_bytes, 2.0 * R * r * V * B, "chain_persist (all 16 steps)"
+        per_call = g + kern["MARKOV_MERGE"]["avg_us"] * kern["MARKOV_MERGE"]["launches"] / kern["CHAIN_PERSIST"]["launches"]
+    else:
+        # one launch = one step over every request: the step's L rows, the previous tokens'
+        # U rows, and W counted once per 16-step call (1/16 of it per step)
+        g = kern["MARKOV_GEMM"]["avg_us"]
+        bytes_launch, flops_launch, name = R * V * 2 + R * r * 2 + V * r * 2 // B, 2.0 * R * r * V, "markov_gemm"
+        per_call = B * (g + kern["MARKOV_MERGE"]["avg_us"])
+    roof = hbm_roofline(name, bytes_launch, g, traffic_from_profiles(
+        "markov.hip", "chain_persist" if persistent else "markov_gemm", "markov-chain"))
     roof.update(mfma_tflops=flops_launch / (g * 1e-6) / 1e12,
                 mfma_frac=flops_launch / (g * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                per_call_us=B * (g + kern["MARKOV_MERGE"]["avg_us"]),
-                per_call_target_us_at_70pct=(R * B * V * 2 + R * B * r * 2 + V * r * 2) / (0.7 * PEAK_HBM_GBS * 1e3))
+                per_call_us=per_call,
+                per_call_target_us_at_70pct=call_bytes / (0.7 * PEAK_HBM_GBS * 1e3))
     res = dict(
         metric="drafted tokens/sec", value=R * B * args.steps / elapsed, unit="tokens/s", n_gpus=1,
         steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-        config=dict(workload="Markov-head greedy chain: 256 requests, 16 steps, V=151936, rank 256"),
+        config=dict(workload="Markov-head greedy chain: 256 requests, 16 steps, V=151936, rank 256",
+                    l_layout=args.l_layout, launch="persistent" if persistent else "per step"),
         roofline=roof, kernels=kern, timing=timing)
     if cpu is not None:
         res["cpu_baseline"] = cpu
@@ -456,7 +482,8 @@ def bench_rnn(args, c, cpu):
 
     dev = torch.device("cuda", 0)
     R, B, V, r, H = c["R"], c["B"], c["V"], c["rank"], c["H"]
-    L, h, Gt, A, E = (_bf16(dev, c[k]) for k in ("L", "h", "Gt", "A", "E"))
+    h, Gt, A, E = (_bf16(dev, c[k]) for k in ("h", "Gt", "A", "E"))
+    L = _chain_l(dev, c["L"], args)
     Wot = _bf16(dev, c["Wo"].T)
     bias = _gpu(dev, c["bias"])
     a = torch.from_numpy(c["anchors"]).to(dev)
@@ -477,7 +504,8 @@ def bench_rnn(args, c, cpu):
         metric="drafted tokens/sec", value=R * B * args.steps / elapsed, unit="tokens/s", n_gpus=1,
         steps=args.steps, warmup=args.warmup, ms_per_step=1000.0 * elapsed / args.steps, higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16 (projection), f64 (memo)", data="synthetic",
-        config=dict(workload="RNN-head greedy chain: 256 requests, 16 steps, V=151936, rank 256, hidden 4096"),
+        config=dict(workload="RNN-head greedy chain: 256 requests, 16 steps, V=151936, rank 256, hidden 4096",
+                    l_layout=args.l_layout),
         roofline=roof, kernels=kern, timing=timing)
     if cpu is not None:
         res["cpu_baseline"] = cpu
@@ -607,7 +635,7 @@ def bench_cycle(args, c, cpu):
 
     dev = torch.device("cuda", 0)
     R, K, V, r = c["R"], c["K"], c["V"], c["rank"]
-    L, U, Wt = _bf16(dev, c["L"]), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
+    L, U, Wt = _chain_l(dev, c["L"], args), _bf16(dev, c["U"]), _bf16(dev, c["W"].T)
     a = torch.from_numpy(c["anchors"]).to(dev)
     hd = workloads.cycle_head_inputs(c)
     hh, hw = _bf16(dev, hd["h"]), _bf16(dev, hd["w"])
@@ -658,7 +686,7 @@ def bench_cycle(args, c, cpu):
         config=dict(workload="draft -> confidence head -> schedule -> pack -> verify cycle: 256 requests, "
                              "16 sampled drafts, V=151936, rank 256, hidden 4096, T=1, additive cost 1+0.05n",
                     requests=R, block=K, vocab=V, drafted_per_step=R * K, verified_drafts_per_step=N,
-                    packed_rows=R + N, mean_accepted=float(acc.mean()),
+                    packed_rows=R + N, mean_accepted=float(acc.mean()), l_layout=args.l_layout,
                     drafted_tokens_per_s=R * K * args.steps / elapsed),
         roofline=hbm_roofline("markov_gemm (sampled, emits bf16 rows)", bytes_launch, g,
                               traffic_from_profiles("markov.hip", "markov_gemm", "cycle")),

@@ -25,17 +25,18 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (DSP_BF16, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DSP_SCHED_THRESHOLD,
-                   DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TOKEN_RANGE, DSP_STATUS_WINDOW_RANGE,
+from ._abi import (DSP_BF16, DSP_BF16_TOKEN_MAJOR, DSP_F32, DSP_SCHED_ARGMAX, DSP_SCHED_EARLY_STOP, DSP_SCHED_THRESHOLD,
+                   DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TIMEOUT, DSP_STATUS_TOKEN_RANGE,
+                   DSP_STATUS_WINDOW_RANGE,
                    DspError, KERNELS)
 
 __all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection",
            "verify_rejection_noalloc", "verify_calibration", "draft_markov_step", "draft_rnn_step",
            "draft_markov_sample", "tree_expand", "schedule_pack",
-           "philox_uniforms", "stream_read", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
+           "philox_uniforms", "stream_read", "set_option", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",
            "DSP_SCHED_EARLY_STOP", "DSP_SCHED_ARGMAX", "DSP_SCHED_TOP_M", "DSP_SCHED_THRESHOLD",
            "DSP_STATUS_TOKEN_RANGE",
-           "DSP_STATUS_WINDOW_RANGE", "DSP_STATUS_NONFINITE"]
+           "DSP_STATUS_WINDOW_RANGE", "DSP_STATUS_NONFINITE", "DSP_STATUS_TIMEOUT"]
 
 
 def lib():
@@ -378,9 +379,23 @@ def verify_calibration(conf, cu_seqlens, decided, n_bins=10, out=None, stream=No
     return _finish(lib().dsp_verify_calibration, args, res, prepare, (conf, cu_seqlens, decided), stream=stream)
 
 
-def _check_markov(L, U, Wt):
+def _chain_l(L):
+    """Layout code and strides of the chain's base logits L [R, B, V]: row-major (unit
+    stride over the vocabulary) or token-major (unit stride over requests, e.g. a
+    [B, V, R] buffer viewed through permute(2, 0, 1))."""
+    _need(L.dtype == torch.bfloat16 and L.dim() == 3, "L: bf16 [R, B, V]")
+    if L.stride(2) == 1:
+        return DSP_BF16, L.stride(0), L.stride(1)
+    _need(L.stride(0) == 1, "L: unit stride over the vocabulary or over requests")
+    return DSP_BF16_TOKEN_MAJOR, L.stride(2), L.stride(1)
+
+
+def _check_markov(L, U, Wt, chain=False):
     _on_gpu(L, U, Wt)
-    _need(L.dtype == torch.bfloat16 and L.dim() == 3 and L.stride(2) == 1, "L: bf16 [R, B, V], unit inner stride")
+    if chain:
+        _chain_l(L)
+    else:
+        _need(L.dtype == torch.bfloat16 and L.dim() == 3 and L.stride(2) == 1, "L: bf16 [R, B, V], unit inner stride")
     _need(U.dtype == torch.bfloat16 and U.dim() == 2 and U.is_contiguous(), "U: contiguous bf16 [V, rank]")
     _need(Wt.dtype == torch.bfloat16 and Wt.shape == U.shape and Wt.is_contiguous(),
           "Wt: contiguous bf16 [V, rank] (the second factor stored vocab-major)")
@@ -392,7 +407,8 @@ def draft_markov_step(L, U, Wt, prev_tok, n_steps=None, want_logq=False, out=Non
 
     Returns dict(y int32 [R, n], logq float32 [R, n] or None, status).
     """
-    _check_markov(L, U, Wt)
+    _check_markov(L, U, Wt, chain=True)
+    l_dt, ldl_r, ldl_d = _chain_l(L)
     R, B, V = L.shape
     n = B if n_steps is None else int(n_steps)
     _need(1 <= n <= B, "n_steps must be in [1, B]")
@@ -405,7 +421,7 @@ def draft_markov_step(L, U, Wt, prev_tok, n_steps=None, want_logq=False, out=Non
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     ws = _workspace(lib().dsp_draft_markov_step_workspace_size(R, V, rank, n, int(want_logq)), dev, prepare, stream)
-    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
+    args = (_ptr(L), l_dt, ldl_r, ldl_d, _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
             _ptr(y), y.stride(0), _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_markov_step, args, dict(y=y, logq=logq, status=status), prepare,
                    (L, U, Wt, prev_tok, ws), stream=stream)
@@ -417,7 +433,7 @@ def draft_rnn_step(L, h, Gt, A, E, Wot, prev_tok, bias=None, n_steps=None, want_
     Gt: bf16 [r, H]; A: bf16 [r, r]; E, Wot: bf16 [V, r]; bias: float32 [r] or None;
     prev_tok: int32 [R]. Returns dict(y int32 [R, n], logq float32 [R, n] or None, status)."""
     _on_gpu(L, h, Gt, A, E, Wot, prev_tok, bias)
-    _need(L.dtype == torch.bfloat16 and L.dim() == 3 and L.stride(2) == 1, "L: bf16 [R, B, V], unit inner stride")
+    l_dt, ldl_r, ldl_d = _chain_l(L)
     R, B, V = L.shape
     _need(h.dtype == torch.bfloat16 and h.dim() == 3 and h.shape[:2] == (R, B) and h.stride(2) == 1,
           "h: bf16 [R, B, H], unit inner stride")
@@ -439,7 +455,7 @@ def draft_rnn_step(L, h, Gt, A, E, Wot, prev_tok, bias=None, n_steps=None, want_
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     ws = _workspace(lib().dsp_draft_rnn_step_workspace_size(R, V, rank, n), dev, prepare, stream)
-    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(h), DSP_BF16, h.stride(0), h.stride(1), H, _ptr(Gt),
+    args = (_ptr(L), l_dt, ldl_r, ldl_d, _ptr(h), DSP_BF16, h.stride(0), h.stride(1), H, _ptr(Gt),
             _ptr(A), _ptr(E), _ptr(bias), _ptr(Wot), V, rank, _ptr(prev_tok), R, n, _ptr(y), y.stride(0),
             _ptr(logq), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_rnn_step, args, dict(y=y, logq=logq, status=status), prepare,
@@ -453,7 +469,8 @@ def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_
     Returns dict(y int32 [R, n], logq float32 [R, n] or None, z bf16 [R, n, V] (the
     emitted draft logits), status).
     """
-    _check_markov(L, U, Wt)
+    _check_markov(L, U, Wt, chain=True)
+    l_dt, ldl_r, ldl_d = _chain_l(L)
     R, B, V = L.shape
     n = B if n_steps is None else int(n_steps)
     _need(1 <= n <= B, "n_steps must be in [1, B]")
@@ -474,7 +491,7 @@ def draft_markov_sample(L, U, Wt, prev_tok, temperature, seed=0, round=0, round_
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     ws = _workspace(lib().dsp_draft_markov_sample_workspace_size(R, V, rank, n), dev, prepare, stream)
-    args = (_ptr(L), DSP_BF16, L.stride(0), L.stride(1), _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
+    args = (_ptr(L), l_dt, ldl_r, ldl_d, _ptr(U), _ptr(Wt), V, rank, _ptr(prev_tok), R, n,
             float(temperature), int(seed), int(round), _ptr(round_dev), _ptr(req_id), _ptr(y), y.stride(0),
             _ptr(logq), _ptr(z), z.stride(0), z.stride(1), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
     return _finish(lib().dsp_draft_markov_sample, args, dict(y=y, logq=logq, z=z, status=status), prepare,
@@ -521,6 +538,14 @@ def stream_read(t, sink=None, stream=None):
         sink = torch.zeros(1, dtype=torch.int32, device=t.device)
     _abi.check(lib().dsp_stream_read(_ptr(t), t.numel() * t.element_size(), _ptr(sink), _stream(stream)))
     return sink
+
+
+def set_option(option, value):
+    """Set a library option: "chain_persistent" (1 = the greedy chain may run all steps in
+    one persistent launch, 0 = one launch per step, the default) or "spin_limit" (polls of a
+    persistent launch's grid barrier before it gives up with DSP_STATUS_TIMEOUT)."""
+    code = {"chain_persistent": _abi.DSP_OPT_CHAIN_PERSISTENT, "spin_limit": _abi.DSP_OPT_SPIN_LIMIT}[option]
+    _abi.check(lib().dsp_set_option(code, int(value)))
 
 
 def prof_enable(on=True, kernels=None):

@@ -7,9 +7,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsp.so")
 DSP_OK = 0
 DSP_F32 = 0
 DSP_BF16 = 1
+DSP_BF16_TOKEN_MAJOR = 2
 DSP_STATUS_TOKEN_RANGE = 1
 DSP_STATUS_WINDOW_RANGE = 2
 DSP_STATUS_NONFINITE = 4
+DSP_STATUS_TIMEOUT = 8
+DSP_OPT_CHAIN_PERSISTENT = 0
+DSP_OPT_SPIN_LIMIT = 1
 DSP_SCHED_EARLY_STOP = 0
 DSP_SCHED_ARGMAX = 1
 DSP_SCHED_TOP_M = 2
@@ -17,7 +21,7 @@ DSP_SCHED_THRESHOLD = 3
 
 KERNELS = ["VERIFY_STATS", "VERIFY_DECIDE", "VERIFY_RESIDUAL", "VERIFY_SAMPLE", "SCHEDULE", "PACK",
            "MARKOV_GEMM", "MARKOV_MERGE", "TREE_GEMM", "TREE_MERGE", "TREE_FINAL", "SCHEDULE_RANK", "CONFIDENCE",
-           "TREE_PROBE", "CALIBRATION", "RNN_MEMO", "RNN_PROJ"]
+           "TREE_PROBE", "CALIBRATION", "RNN_MEMO", "RNN_PROJ", "CHAIN_PERSIST"]
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -59,6 +63,7 @@ SIGNATURES = {
                                _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "dsp_stream_read": (_i32, [_p, _sz, _p, _p]),
     "dsp_prof_enable": (_i32, [_i32]),
+    "dsp_set_option": (_i32, [_i32, _i64]),
     "dsp_prof_reset": (_i32, []),
     "dsp_prof_query": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }

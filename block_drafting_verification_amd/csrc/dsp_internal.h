@@ -19,6 +19,8 @@ int32_t hip_check(hipError_t e, const char* what);  // DSP_OK or DSP_ERR_HIP
 // a start/stop event pair when the id is selected, prof_commit files the pair for
 // dsp_prof_query once the launch carrying them is enqueued.
 bool prof_events(int kernel, hipEvent_t* start, hipEvent_t* stop);
+// Current value of a DSP_OPT_* option.
+int64_t option(int32_t opt);
 void prof_commit(int kernel, hipEvent_t start, hipEvent_t stop);
 
 // Launch `kernel` on stream s. When its id is being timed, the events ride on the

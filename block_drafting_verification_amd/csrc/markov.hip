@@ -30,6 +30,8 @@
 // workspace; small merge kernels combine them.
 #include <math.h>
 
+#include <type_traits>
+
 #include "dsp_internal.h"
 
 namespace dsp {
@@ -80,19 +82,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(const s32x4& d) {
 // The destination is a read-write operand: the register then stays bound to its ring
 // slot for the whole loop, so the compiler never hands it to another value while a
 // load into it is still in flight.
-template <bool ASYNC>
+// Each load starts with s_nop 4: a vector memory instruction that reads an SGPR written
+// by a VALU instruction (v_readlane / v_readfirstlane, e.g. when the compiler reloads a
+// spilled descriptor) needs 5 wait states in between, which the compiler inserts before
+// its own memory instructions but not before inline assembly. Without them the load can
+// take a stale descriptor.
+template <bool ASYNC, int IMM = 0>
 __device__ __forceinline__ void buf_load_x4(u32x4& v, const s32x4& d, uint32_t off) {
+  static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset");
   if (ASYNC)
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "+v"(v) : "v"(off), "s"(d) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3"
+                 : "+v"(v) : "v"(off), "s"(d), "n"(IMM) : "memory");
   else
-    v = __builtin_amdgcn_raw_buffer_load_b128(as_rsrc(d), off, 0, 0);
+    v = __builtin_amdgcn_raw_buffer_load_b128(as_rsrc(d), off + IMM, 0, 0);
 }
 template <bool ASYNC>
 __device__ __forceinline__ void buf_load_u16(uint32_t& v, const s32x4& d, uint32_t off) {
   if (ASYNC)
-    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "+v"(v) : "v"(off), "s"(d) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_ushort %0, %1, %2, 0 offen" : "+v"(v) : "v"(off), "s"(d) : "memory");
   else
     v = __builtin_amdgcn_raw_buffer_load_b16(as_rsrc(d), off, 0, 0);
+}
+template <bool ASYNC, int IMM = 0>
+__device__ __forceinline__ void buf_load_x1(uint32_t& v, const s32x4& d, uint32_t off) {
+  static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset");
+  if (ASYNC)
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2, 0 offen offset:%3"
+                 : "+v"(v) : "v"(off), "s"(d), "n"(IMM) : "memory");
+  else
+    v = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc(d), off + IMM, 0, 0);
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -149,6 +167,10 @@ struct GemmArgs {
   // rows of U the parent rows may name (0: V, the token table). The RNN head passes its
   // memo rows here (row r of the memo table for parent row r).
   int32_t u_rows;
+  // base logits stored token-major (chain, one row per request): element (request i,
+  // token v) of depth d at L + i + d*ldL_d + v*ldL_r, i.e. ldL_r is then the stride
+  // between tokens; a stage's tile of 32 tokens x 256 requests is one contiguous read
+  int32_t l_tm;
 };
 
 // 16-byte slot of (row, vector) in a swizzled LDS tile whose rows hold `nv` vectors
@@ -193,7 +215,7 @@ __device__ __forceinline__ void merge_top4(float* va, int* ia, const float* vb, 
   }
 }
 
-template <int MODE, int KS, bool LAL>
+template <int MODE, int KS, bool LAL, bool LTM = false>
 __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   constexpr int NV = 2 * KS;                  // 16-byte vectors per staged Wt row (rank padded to 16*KS)
   constexpr int WST = kTS * NV;               // Wt vectors per stage
@@ -273,8 +295,19 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   const s32x4 wdesc = make_desc(a.Wt, (uint32_t)((size_t)a.V * a.rank * 2));
   const int req0 = r0 / a.rows_per_req;
   const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
-  const s32x4 ldesc = make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
-                                (uint32_t)(((size_t)(rlast / a.rows_per_req - req0) * a.ldL_r + a.V) * 2));
+  // token-major: the block's requests r0..rlast of every token (a multiple of 8 of them,
+  // checked on the host), so 16-byte vectors of 8 requests are either all inside or past it
+  // Row-major: up to the block's last row's token V-1. The range check of a buffer load
+  // is per dword, so with V odd the dword holding that last entry would read as zero:
+  // 16-byte loads (LAL: a 16-byte aligned base) extend the extent to the end of that
+  // dword (2 more bytes, in the same dword, so in memory the row's own entries reach);
+  // 2-byte loads keep it exact.
+  const s32x4 ldesc =
+      LTM ? make_desc(a.L + (size_t)r0 + (size_t)a.d * a.ldL_d,
+                      (uint32_t)(((size_t)(a.V - 1) * a.ldL_r + (rlast - r0 + 1)) * 2))
+          : make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
+                      (uint32_t)((((size_t)(rlast / a.rows_per_req - req0) * a.ldL_r + a.V) * 2 + (LAL ? 3 : 0)) &
+                                 ~(size_t)(LAL ? 3 : 0)));
   // Tree blocks spanning at most 16 requests add the base logits through the matrix
   // cores: one extra k-step (A = the stage's 32 tokens x 16 requests of L, B = each
   // row's one-hot request), issued first so z keeps its summation order, in place of
@@ -299,6 +332,10 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     const int rr = r0 + ((tid + q * kGT) >> 2);
     lofs[q] = rr < a.rows ? (uint32_t)(((size_t)(rr / a.rows_per_req - req0) * a.ldL_r + 8 * (tid & 3)) * 2)
                           : kOOB;
+    if (LTM) {  // vector e: token e / 32 of the stage, requests 8 (e % 32) .. + 8
+      const int e = tid + q * kGT, rg = e & 31;
+      lofs[q] = r0 + 8 * rg < a.rows ? (uint32_t)(((size_t)(e >> 5) * a.ldL_r + 8 * rg) * 2) : kOOB;
+    }
     if (lk)  // request tid/4 of the block, 16-byte column tid%4; past the block's requests: zero
       lofs[q] = q == 0 && tid < 64 && (tid >> 2) <= rlast / a.rows_per_req - req0
                     ? (uint32_t)(((size_t)(tid >> 2) * a.ldL_r + 8 * (tid & 3)) * 2)
@@ -310,7 +347,8 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   auto load_stage = [&](int s, u32x4* rw, u32x4* rl, uint32_t (*ru)[8]) {
     const bool live = s < nst;
     const uint32_t tw = live ? (uint32_t)((size_t)(s_begin + s) * kTS * a.rank * 2) : kOOB;
-    const uint32_t tl = live ? (uint32_t)((s_begin + s) * kTS * 2) : kOOB;
+    const uint32_t tl = live ? (uint32_t)((LTM ? (size_t)(s_begin + s) * kTS * a.ldL_r : (size_t)(s_begin + s) * kTS) * 2)
+                             : kOOB;
 #pragma unroll
     for (int q = 0; q < WQ; ++q) buf_load_x4<AS>(rw[q], wdesc, wofs[q] + tw);
 #pragma unroll
@@ -370,6 +408,11 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       }
       return;
     }
+    if (LTM) {  // token-major tile [32 tokens][256 requests], stored as loaded
+#pragma unroll
+      for (int q = 0; q < LQ; ++q) Ls[tid + q * kGT] = rl[q];
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
       const int n = (tid + q * kGT) >> 2, c = tid & 3;
@@ -418,10 +461,22 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   // L (or -inf for a token past V or a row past the block), so the MFMAs leave z itself.
   auto init_from_l = [&](int s, const u32x4* Ls, f32x16& acc) {
     const int v0 = (s_begin + s) * kTS;
-    const char* lb = (const char*)(Ls + nloc * 4) + 8 * (lane >> 5);
     uint2 w[4];
+    if (LTM) {  // this lane's 16 tokens of its request, 2 bytes each from the [token][request] tile
+      const uint16_t* Lt = (const uint16_t*)Ls + nloc;
+      uint32_t hv[16];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) w[h] = *(const uint2*)(lb + 16 * (h ^ ((nloc >> 2) & 3)));
+      for (int q = 0; q < 16; ++q) hv[q] = Lt[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * kTR];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        w[h].x = hv[4 * h] | (hv[4 * h + 1] << 16);
+        w[h].y = hv[4 * h + 2] | (hv[4 * h + 3] << 16);
+      }
+    } else {
+      const char* lb = (const char*)(Ls + nloc * 4) + 8 * (lane >> 5);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) w[h] = *(const uint2*)(lb + 16 * (h ^ ((nloc >> 2) & 3)));
+    }
     if (v0 + kTS <= a.V && all_rows) {  // uniform: nothing to mask
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -739,9 +794,12 @@ struct ChainMergeArgs {
   float* logq;
 };
 
+// One wavefront per (row r, step a.d + blockIdx.y); the partials of step a.d + y start
+// y * R * G entries after a.part.
 __global__ __launch_bounds__(64) void chain_merge_kernel(ChainMergeArgs a) {
   const int r = blockIdx.x, lane = threadIdx.x;
-  const ChainPart* pr = a.part + (size_t)r * a.G;
+  const ChainPart* pr = a.part + ((size_t)blockIdx.y * a.R + r) * a.G;
+  a.d += blockIdx.y;
   // G <= 256: at most four partials per lane, all loaded before any is used (clamped
   // index, masked after)
   ChainPart cp[4];
@@ -770,6 +828,561 @@ __global__ __launch_bounds__(64) void chain_merge_kernel(ChainMergeArgs a) {
       a.logq[(size_t)r * a.ld_y + a.d] = (float)((zy * kLog2ed - lse2) * kLn2d);
     }
   }
+}
+
+// ---------------------------------------------------------------- persistent greedy chain
+// All steps of the greedy chain in one launch, one workgroup per CU. Between steps the
+// chain needs every row's arg-max over the whole vocabulary before any row can fetch its
+// next U row, so the steps are separated by a grid-wide barrier; what the barrier buys
+// is that each workgroup keeps ITS vocabulary slice of Wt on chip for all the steps
+// (rank 256: 16 KB per 32-token tile; up to 19 tiles per workgroup, 3 per wave in
+// registers and the rest in LDS), so a step streams only the base logits L (and 256
+// U rows from L2) instead of L plus all of Wt.
+//
+// Workgroup: 4 waves (one per SIMD, up to 512 registers each). Wave w owns a contiguous
+// run of at most 5 tiles of the workgroup's slice and computes them for every parent row,
+// one 32-row column block at a time: the column block's U rows are staged in LDS (double
+// buffered, fetched during the block before) and read once as the 16 B fragments of
+// the block; each tile then takes 16 MFMAs with its Wt fragments from registers or LDS.
+// Tiles hold the Wt rows in the order tmap(i), so that the 16 accumulators of a lane are
+// 16 consecutive tokens of its row and its L values are two 16-byte loads (row-major L).
+// The arg-max (and log-sum-exp) per row is combined over lanes and waves in LDS, then
+// over workgroups by a 64-bit atomic max of the order key (value, lowest id) into one of
+// 8 copies per row, so that each copy takes the atomics of an eighth of the workgroups;
+// the next step's tokens are the maxima of the 8 copies. The per-workgroup partials also
+// go to the workspace, from which a merge kernel writes y and log q after the launch.
+//
+// The barrier is a counter that every workgroup raises once per step and then polls.
+// It needs every workgroup resident at once (one per CU, which the launch shape and the
+// resource use guarantee on an idle device); the poll is bounded, and a workgroup that
+// waits past the bound sets DSP_STATUS_TIMEOUT and leaves, so the launch always drains.
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPRegTiles = 3;   // Wt tiles per wave in registers
+constexpr int kPWaveTiles = 5;  // tiles per wave at most
+constexpr int kPMaxTiles = 19;  // tiles per workgroup at most (5, 5, 5, 4)
+constexpr int kPLdsSlots = 7;   // Wt tiles in LDS: waves 0..2 two each, wave 3 one
+constexpr int kPMaxR = 256;     // parent rows
+constexpr int kPGroups = 8;     // arg-max key copies per row
+constexpr int kPKeyStride = 16;  // uint64 words between keys: one 128-byte line each, so the
+                                 // atomics of a step spread over the memory channels
+constexpr int kPRowVec = 33;                // 16-byte vectors per LDS tile row: 32 + 1 of padding
+constexpr int kPTileVec = 32 * kPRowVec;     // per LDS tile (32 rows x 512 bytes, padded)
+constexpr int kCachePolicySC1 = 16;          // buffer access cache policy: SC1 (device scope)
+
+struct PMerge {  // a row's partial over some tiles
+  float best;
+  int32_t idx;
+  float ref;
+  float sum;  // of at most a workgroup's 608 terms, each at most 1
+};
+static_assert(sizeof(PMerge) == 16, "persistent merge record");
+constexpr size_t kPOffU = (size_t)kPLdsSlots * kPTileVec * 16;
+constexpr size_t kPOffM = kPOffU + (size_t)2 * kPTileVec * 16;
+constexpr size_t kPOffP = kPOffM + (size_t)2 * kPWaves * 32 * sizeof(PMerge);
+constexpr size_t kPOffT = kPOffP + (size_t)kPMaxR * sizeof(PMerge);
+constexpr size_t kPOffF = kPOffT + (size_t)kPMaxR * 4;
+constexpr size_t kPLds = kPOffF + 16;
+static_assert(kPLds <= 160 * 1024, "persistent chain LDS");
+
+struct PersistArgs {
+  const uint16_t* U;
+  const uint16_t* Wt;
+  const uint16_t* L;
+  int64_t ldL_r, ldL_d;
+  const int32_t* prev_tok;
+  int32_t V, R, n_steps, G;
+  ChainPart* part;    // [n_steps][R][G]
+  uint64_t* keys;     // [n_steps][kPGroups][R], zero on entry
+  uint32_t* bar;      // zero on entry
+  uint32_t spin_limit;
+  int32_t* status;
+};
+
+// MFMA row i of a tile holds token tmap(i): with i = 8j + 4h + k the accumulator q = 4j + k
+// of a lane in half h is token 16h + q.
+__device__ __forceinline__ int ptmap(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+// 16-byte slot of vector kv of row m in an LDS tile: rows are 33 slots apart, so the 16 rows
+// read together by a quarter wavefront start 4 banks apart and cover all 64 banks, and the
+// slots of one lane's 16 fragments are a fixed stride apart (instruction offsets).
+__device__ __forceinline__ int pslot(int m, int kv) { return m * kPRowVec + kv; }
+
+template <bool LSE>
+__device__ __forceinline__ void pmerge(PMerge& a, const PMerge& b) {
+  if (b.best > a.best || (b.best == a.best && b.idx < a.idx)) {
+    a.best = b.best;
+    a.idx = b.idx;
+  }
+  if (!LSE) return;
+  const float nref = fmaxf(a.ref, b.ref);
+  float s = 0.f;
+  if (a.ref != -INFINITY) s += a.sum * fast_exp2(a.ref - nref);
+  if (b.ref != -INFINITY) s += b.sum * fast_exp2(b.ref - nref);
+  a.ref = nref;
+  a.sum = s;
+}
+
+template <bool LSE>
+__global__ __launch_bounds__(kPThreads, 1) void chain_persist_kernel(PersistArgs a) {
+  extern __shared__ u32x4 plds[];
+  u32x4* Wl = plds;
+  u32x4* Ub = plds + kPOffU / 16;
+  PMerge* Mg = (PMerge*)((char*)plds + kPOffM);
+  PMerge* Pt = (PMerge*)((char*)plds + kPOffP);
+  int32_t* Tk = (int32_t*)((char*)plds + kPOffT);
+  int32_t* Fl = (int32_t*)((char*)plds + kPOffF);
+
+  // the wave index as a scalar: what derives from it (this wave's tiles, their count) is
+  // then scalar too, so the per-tile tests are scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+            col = lane & 31;
+  const int g = blockIdx.x, grp = g & (kPGroups - 1);
+  const int V = a.V, R = a.R, nsteps = a.n_steps;
+  const int nst_all = (V + 31) / 32;
+  const int tb = (int)(((long)g * nst_all) / a.G);
+  const int ng = (int)(((long)(g + 1) * nst_all) / a.G) - tb;
+  // tiles of this wave (at most 5, and 4 for the last wave, which has one LDS slot: the
+  // host keeps ng <= 19, and the clamp keeps every index inside the layout regardless)
+  const int nw = min(ng / 4 + (wave < ng % 4 ? 1 : 0), wave == kPWaves - 1 ? kPWaveTiles - 1 : kPWaveTiles);
+  const int tw = tb + wave * (ng / 4) + min(wave, ng % 4);  // this wave's first tile
+  const int nc = (R + 31) / 32;
+
+  const s32x4 wdesc = make_desc(a.Wt, (uint32_t)((size_t)V * 512));
+  const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)V * 512));
+  const s32x4 kdesc = make_desc(a.keys, (uint32_t)((size_t)nsteps * kPGroups * R * kPKeyStride * 8));
+  // extent up to the last (row, step)'s token V-1, rounded up to the end of its dword (the
+  // range check is per dword; the base is 16-byte aligned)
+  const s32x4 ldesc = make_desc(
+      a.L, (uint32_t)((((size_t)(R - 1) * a.ldL_r + (size_t)(nsteps - 1) * a.ldL_d + V) * 2 + 3) & ~(size_t)3));
+
+  // parent tokens of step 0
+  if (tid < R) {
+    int t = a.prev_tok[tid];
+    if (t < 0 || t >= V) {
+      if (g == 0) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+      t = 0;
+    }
+    Tk[tid] = t;
+  }
+  // Wt tiles past the third of this wave: to its LDS slots (loaded through registers)
+#pragma unroll
+  for (int j = kPRegTiles; j < kPWaveTiles; ++j) {
+    if (wave == kPWaves - 1 && j == kPWaveTiles - 1) continue;  // wave 3 has one slot
+    const int slot = 2 * wave + (j - kPRegTiles);
+    u32x4 tmp[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int e = lane + 64 * p, i = e >> 5, kv = e & 31;
+      const int v = (tw + j) * 32 + ptmap(i);
+      buf_load_x4<false>(tmp[p], wdesc, j < nw && v < V ? (uint32_t)(((size_t)v * 256 + 8 * kv) * 2) : kOOB);
+    }
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int e = lane + 64 * p;
+      Wl[slot * kPTileVec + pslot(e >> 5, e & 31)] = tmp[p];
+    }
+  }
+  __syncthreads();  // Tk
+
+  // Wt tiles 0..2 of this wave in registers: fragment ks of tile j = the 16 bytes of rank
+  // 16ks + 8h .. +8 of token tmap(col). These and the first fills of the L ring and the U
+  // staging use the compiler's own loads (it waits for them before any use, including a
+  // register copy); the loads inside the step loop are the asynchronous ones.
+  u32x4 wr[kPRegTiles][16];
+#pragma unroll
+  for (int j = 0; j < kPRegTiles; ++j) {
+    const int v = (tw + j) * 32 + ptmap(col);
+    const bool ok = j < nw && v < V;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      buf_load_x4<false>(wr[j][ks], wdesc, ok ? (uint32_t)(((size_t)v * 256 + 8 * (2 * ks + h)) * 2) : kOOB);
+  }
+  // L ring: slot j holds tile j of the next (step, column block) this wave computes;
+  // lane (col, h) loads tokens 16h .. 16h+15 of row 32c + col
+  u32x4 ring[kPWaveTiles][2];
+  // lane base of the wave's tiles in row 32c + col of step d (tile j at +64j bytes, the
+  // second 16 bytes at +16: instruction offsets); past the steps or rows: kOOB, whose
+  // offsets stay past every extent. A wave with fewer than 5 tiles still loads 5 (the
+  // extra ones are never used), so every wave issues the same count.
+  auto l_base = [&](int d, int c) -> uint32_t {
+    const int r = c * 32 + col;
+    if (d >= nsteps || r >= R) return kOOB;
+    return (uint32_t)(((size_t)r * a.ldL_r + (size_t)d * a.ldL_d + (size_t)tw * 32 + 16 * h) * 2);
+  };
+  auto l_load = [&](auto jc, uint32_t base, bool async) {
+    constexpr int j = decltype(jc)::value;
+    if (async) {
+      buf_load_x4<true, 64 * j>(ring[j][0], ldesc, base);
+      buf_load_x4<true, 64 * j + 16>(ring[j][1], ldesc, base);
+    } else {
+      buf_load_x4<false, 64 * j>(ring[j][0], ldesc, base);
+      buf_load_x4<false, 64 * j + 16>(ring[j][1], ldesc, base);
+    }
+  };
+  {
+    const uint32_t b0 = l_base(0, 0);
+    l_load(std::integral_constant<int, 0>{}, b0, false);
+    l_load(std::integral_constant<int, 1>{}, b0, false);
+    l_load(std::integral_constant<int, 2>{}, b0, false);
+    l_load(std::integral_constant<int, 3>{}, b0, false);
+    l_load(std::integral_constant<int, 4>{}, b0, false);
+  }
+  // U rows of a column block: thread -> row tid/8, vectors 4*(tid%8) .. +4
+  u32x4 ur[4];
+  auto u_offset = [&](int c) -> uint32_t {  // vector e of the thread's four at +16e bytes
+    const int r = c * 32 + (tid >> 3);
+    if (c >= nc || r >= R) return kOOB;
+    return (uint32_t)(((size_t)Tk[r] * 256 + 8 * 4 * (tid & 7)) * 2);
+  };
+  auto load_u = [&](int c) {
+    const uint32_t o = u_offset(c);
+    buf_load_x4<true, 0>(ur[0], udesc, o);
+    buf_load_x4<true, 16>(ur[1], udesc, o);
+    buf_load_x4<true, 32>(ur[2], udesc, o);
+    buf_load_x4<true, 48>(ur[3], udesc, o);
+  };
+  // One dword of each 128-byte line of every parent row's U row (thread r takes row r):
+  // the lines and their translations are then in L2 when the column blocks' U rows are
+  // fetched one block ahead of their use, instead of each block paying a full memory round
+  // trip behind the one before. Issued together with the first block's rows.
+  uint32_t pf[4] = {0u, 0u, 0u, 0u};
+  auto prefetch_u = [&]() {
+    const bool ok = tid < R;
+    const int t = ok ? Tk[tid] : 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) buf_load_x1<true>(pf[e], udesc, ok ? (uint32_t)((size_t)t * 512 + 128 * e) : kOOB);
+  };
+  auto store_u = [&](int buf) {
+    const int j = tid >> 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ub[buf * kPTileVec + pslot(j, 4 * (tid & 7) + e)] = ur[e];
+  };
+  {
+    const uint32_t o = u_offset(0);
+    buf_load_x4<false, 0>(ur[0], udesc, o);
+    buf_load_x4<false, 16>(ur[1], udesc, o);
+    buf_load_x4<false, 32>(ur[2], udesc, o);
+    buf_load_x4<false, 48>(ur[3], udesc, o);
+  }
+  prefetch_u();
+  vm_wait<0>();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) landed(pf[e]);
+  // every value above is waited for here, before the step loop
+  // the register tiles live in the accumulation registers (AGPRs), which the MFMAs read
+  // as their A operand directly; the arch VGPRs stay for everything else
+#pragma unroll
+  for (int j = 0; j < kPRegTiles; ++j)
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(wr[j][ks]));
+#pragma unroll
+  for (int j = 0; j < kPWaveTiles; ++j) {
+    landed(ring[j][0]);
+    landed(ring[j][1]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) landed(ur[e]);
+  store_u(0);
+  __syncthreads();
+
+  for (int d = 0; d < nsteps; ++d) {
+    for (int c = 0; c < nc; ++c) {
+      // this column block's U fragments (B operand): row col, rank 16ks + 8h .. +8
+      u32x4 bf[16];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) bf[ks] = Ub[(c & 1) * kPTileVec + pslot(col, 2 * ks + h)];
+      load_u(c + 1);  // OOB past the last block: zeros, and the wait counts stay fixed
+      const int dn = c + 1 < nc ? d : d + 1, cn = c + 1 < nc ? c + 1 : 0;
+      float best = -INFINITY, lref = -INFINITY;
+      int bq = -1;
+      double lsum = 0.0;
+      auto epi_lse = [&](const f32x16& z) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) tmax = fmaxf(tmax, z[q]);
+        if (tmax != -INFINITY) {
+          const float nref = fmaxf(lref, tmax * kLog2e);
+          float ts = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));
+          const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
+          lsum = lsum * scale + (double)ts;
+          lref = nref;
+        }
+      };
+      const uint32_t lnext = l_base(dn, cn);
+      // The accumulator of tile j starts from its L values (-inf for a token past V, and
+      // for every entry of a tile past this wave's count, whose Wt rows are zero): the
+      // MFMAs then leave z itself, and such entries never win or weigh.
+      auto init = [&](auto jc, f32x16& z) {
+        constexpr int j = decltype(jc)::value;
+        landed(ring[j][0]);
+        landed(ring[j][1]);
+        const int v0 = (tw + j) * 32;
+        if (j < nw && v0 + 32 <= V) {  // uniform
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const uint32_t w = ring[j][q >> 3][(q & 7) >> 1];
+            z[q] = (q & 1) ? bf16_hi(w) : bf16_lo(w);
+          }
+        } else {
+          // entries left in this lane's run of the vocabulary (computed here, so that the
+          // 16 comparisons are not hoisted out of the loops and held as masks)
+          int left = j < nw ? V - v0 - 16 * h : 0;
+          asm volatile("" : "+v"(left));
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const uint32_t w = ring[j][q >> 3][(q & 7) >> 1];
+            const float f = (q & 1) ? bf16_hi(w) : bf16_lo(w);
+            z[q] = q < left ? f : -INFINITY;
+          }
+        }
+        l_load(jc, lnext, true);  // slot j: the same tile of the next (step, block)
+      };
+      auto wfrag = [&](auto jc, int ks) -> bf16x8 {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j < kPRegTiles) return __builtin_bit_cast(bf16x8, wr[j][ks]);
+        else return __builtin_bit_cast(bf16x8, Wl[(2 * wave + j - kPRegTiles) * kPTileVec + pslot(col, 2 * ks + h)]);
+      };
+      auto mfma = [&](const bf16x8& af, int ks, f32x16& z) {
+        z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bf[ks]), z, 0, 0, 0);
+      };
+      auto arg = [&](float z, int code) {  // tokens visited in increasing order
+        if (z > best) {
+          best = z;
+          bq = code;
+        }
+      };
+      // Tiles go two at a time with their MFMA chains interleaved (each MFMA then waits on
+      // the one issued two slots before it, not on its predecessor), and the arg-max of the
+      // two tiles before runs between them, 2 values per k-step in token order.
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      using I4 = std::integral_constant<int, 4>;
+      f32x16 acc[4];
+      // slots 0, 1: after them came slots 2..4 of the block before and this block's U rows
+      vm_wait<2 * 3 + 4>();
+      init(I0{}, acc[0]);
+      init(I1{}, acc[1]);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        mfma(wfrag(I0{}, ks), ks, acc[0]);
+        mfma(wfrag(I1{}, ks), ks, acc[1]);
+      }
+      // slots 2, 3: after them, slot 4 of the block before, the U rows, the refills of 0, 1
+      vm_wait<2 + 4 + 4>();
+      init(I2{}, acc[2]);
+      init(I3{}, acc[3]);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        mfma(wfrag(I2{}, ks), ks, acc[2]);
+        mfma(wfrag(I3{}, ks), ks, acc[3]);
+        arg(ks < 8 ? acc[0][2 * ks] : acc[1][2 * ks - 16], 2 * ks);
+        arg(ks < 8 ? acc[0][2 * ks + 1] : acc[1][2 * ks - 15], 2 * ks + 1);
+      }
+      // instruction order for the scheduler: the LDS-tile fragments are read two k-steps
+      // ahead; per k-step, an MFMA, half of the step's arg-max work, the next read, the
+      // other MFMA, the other half
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (ks < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      // the arg-max of tiles 0, 1 completes here (otherwise the compiler may sink it past
+      // the next tiles' MFMAs, out of the slots between them)
+      asm volatile("" : "+v"(best), "+v"(bq));
+      if (LSE) {
+        epi_lse(acc[0]);
+        epi_lse(acc[1]);
+      }
+      // slot 4: after it, the U rows and the refills of 0..3
+      vm_wait<4 + 8>();
+      init(I4{}, acc[0]);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        mfma(wfrag(I4{}, ks), ks, acc[0]);
+        arg(ks < 8 ? acc[2][2 * ks] : acc[3][2 * ks - 16], 32 + 2 * ks);
+        arg(ks < 8 ? acc[2][2 * ks + 1] : acc[3][2 * ks - 15], 32 + 2 * ks + 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        if (ks < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      asm volatile("" : "+v"(best), "+v"(bq));
+#pragma unroll
+      for (int q = 0; q < 16; ++q) arg(acc[0][q], 64 + q);
+      if (LSE) {
+        epi_lse(acc[2]);
+        epi_lse(acc[3]);
+        epi_lse(acc[0]);
+      }
+      PMerge m;
+      m.best = best;
+      m.idx = bq < 0 ? 0x7fffffff : (tw + (bq >> 4)) * 32 + 16 * h + (bq & 15);
+      m.ref = lref;
+      m.sum = (float)lsum;
+      {
+        PMerge o;
+        o.best = __shfl_xor(m.best, 32, 64);
+        o.idx = __shfl_xor(m.idx, 32, 64);
+        if (LSE) {
+          o.ref = __shfl_xor(m.ref, 32, 64);
+          o.sum = __shfl_xor(m.sum, 32, 64);
+        }
+        pmerge<LSE>(m, o);
+      }
+      if (lane < 32) Mg[((c & 1) * kPWaves + wave) * 32 + lane] = m;
+      // the next column block's U rows: 10 ring loads were issued after them
+      vm_wait<2 * kPWaveTiles>();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) landed(ur[e]);
+      if (c + 1 == nc) {
+        // leaving the column loop: the ring (now the next step's first block) lands
+        // here, so that any register copy the compiler places on the way out of the
+        // loop copies loaded values (the key update below waits for it anyway)
+        vm_wait<0>();
+#pragma unroll
+        for (int j = 0; j < kPWaveTiles; ++j) {
+          landed(ring[j][0]);
+          landed(ring[j][1]);
+        }
+      }
+      if (c + 1 < nc) store_u((c + 1) & 1);
+      __syncthreads();
+      if (wave == 0 && lane < 32 && c * 32 + lane < R) {
+        PMerge p = Mg[(c & 1) * kPWaves * 32 + lane];
+#pragma unroll
+        for (int w = 1; w < kPWaves; ++w) pmerge<LSE>(p, Mg[((c & 1) * kPWaves + w) * 32 + lane]);
+        Pt[c * 32 + lane] = p;
+      }
+    }
+    __syncthreads();  // Pt complete
+    if (tid < R) {
+      const PMerge p = Pt[tid];
+      const uint64_t key = p.idx == 0x7fffffff ? 0ull : amax_key(p.best, (uint32_t)p.idx);
+      __hip_atomic_fetch_max(a.keys + (((size_t)d * kPGroups + grp) * R + tid) * kPKeyStride, key,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (LSE) {  // log q needs every workgroup's log-sum-exp partial; y alone, the keys
+        ChainPart cp;
+        cp.key = key;
+        cp.ref = p.ref;
+        cp.pad = 0.f;
+        cp.sum = (double)p.sum;
+        a.part[((size_t)d * R + tid) * a.G + g] = cp;
+      }
+    }
+    if (d + 1 == nsteps) break;
+    // Every exchange between workgroups is an agent-scope atomic (the key updates, the
+    // counter, the key and counter reads), performed and read at the device's coherence
+    // point, so no cache write-back or invalidation is needed (fences here would write
+    // back and invalidate the L2 of the XCD, per thread and per step). What is needed is
+    // that this workgroup's key updates are performed before its arrival is counted: each
+    // thread waits for its own (vmcnt 0), then the workgroup barrier orders them before
+    // the arrival.
+    vm_wait<0>();
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t target = (uint32_t)(d + 1) * (uint32_t)a.G;
+      uint32_t polls = 0;
+      int ok = 1;
+      while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (++polls > a.spin_limit) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (!ok) atomicOr(a.status, DSP_STATUS_TIMEOUT);
+      Fl[0] = ok;
+    }
+    __syncthreads();
+    if (!Fl[0]) return;  // uniform; every load issued so far has landed (wait above)
+    if (tid < R) {
+      // the 8 copies of the row's key, read at the device's coherence point (SC1: the
+      // updates are atomics performed there) with plain loads, all issued before any
+      // is waited for (one memory round trip, not eight)
+      uint64_t kq[kPGroups];
+#pragma unroll
+      for (int q = 0; q < kPGroups; ++q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+            as_rsrc(kdesc), (uint32_t)((((size_t)d * kPGroups + q) * R + tid) * kPKeyStride * 8), 0,
+            kCachePolicySC1);
+        kq[q] = ((uint64_t)v[1] << 32) | v[0];
+      }
+      uint64_t k = 0;
+#pragma unroll
+      for (int q = 0; q < kPGroups; ++q) k = kq[q] > k ? kq[q] : k;
+      int t = k == 0 ? -1 : (int)amax_index(k);
+      if (t < 0 || t >= V) {  // no finite entry in the row: as the per-step path, U row 0
+        if (g == 0) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+        t = 0;
+      }
+      Tk[tid] = t;
+    }
+    __syncthreads();
+    load_u(0);
+    prefetch_u();
+    vm_wait<0>();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      landed(ur[e]);
+      landed(pf[e]);
+    }
+#pragma unroll
+    for (int j = 0; j < kPWaveTiles; ++j) {
+      landed(ring[j][0]);
+      landed(ring[j][1]);
+    }
+    store_u(0);
+    __syncthreads();
+  }
+  vm_wait<0>();  // the last refills (past the range, zeros) land before the waves end
+#pragma unroll
+  for (int j = 0; j < kPWaveTiles; ++j) {
+    landed(ring[j][0]);
+    landed(ring[j][1]);
+  }
+}
+
+struct PersistInitArgs {
+  uint64_t* keys;
+  size_t n_keys;  // keys (kPKeyStride words apart)
+  uint32_t* bar;
+};
+__global__ __launch_bounds__(256) void chain_persist_init_kernel(PersistInitArgs a) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < a.n_keys) a.keys[i * kPKeyStride] = 0ull;
+  if (i == 0) *a.bar = 0u;
+}
+
+// y of the greedy chain from the persistent launch's keys: row r, step d (one thread each)
+struct PersistYArgs {
+  const uint64_t* keys;
+  int32_t R, n_steps;
+  int32_t* y;
+  int64_t ld_y;
+};
+__global__ __launch_bounds__(256) void chain_persist_y_kernel(PersistYArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.R * a.n_steps) return;
+  const int d = i / a.R, r = i % a.R;
+  uint64_t k = 0;
+#pragma unroll
+  for (int q = 0; q < kPGroups; ++q) {
+    const uint64_t kq = a.keys[(((size_t)d * kPGroups + q) * a.R + r) * kPKeyStride];
+    k = kq > k ? kq : k;
+  }
+  a.y[(size_t)r * a.ld_y + d] = (int32_t)amax_index(k);  // no finite entry: -1, as the merge
 }
 
 // ---------------------------------------------------------------- sampled chain draw
@@ -1520,17 +2133,17 @@ int pick_groups(int rows, int V) {
   return G;
 }
 
-template <int MODE, int KS, bool LAL>
+template <int MODE, int KS, bool LAL, bool LTM = false>
 int32_t launch_gemm_ks(int kid, GemmArgs a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)markov_gemm_kernel<MODE, KS, LAL>,
+    (void)hipFuncSetAttribute((const void*)markov_gemm_kernel<MODE, KS, LAL, LTM>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
   a.nrb = (a.rows + kTR - 1) / kTR;
   a.xcd_map = a.nrb > 1 && a.G % 8 == 0;
-  launch(kid, markov_gemm_kernel<MODE, KS, LAL>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT),
+  launch(kid, markov_gemm_kernel<MODE, KS, LAL, LTM>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT),
          (uint32_t)gemm_lds_bytes(KS, MODE), s, a);
   return hip_check(hipGetLastError(), "markov gemm launch");
 }
@@ -1551,6 +2164,8 @@ template <int MODE>
 int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
   if ((size_t)a.V * a.rank * 2 >= kOOB)
     return fail(DSP_ERR_SHAPE, "Wt must span less than 2 GiB (V * rank * 2 bytes)");
+  // token-major base logits (checked by the entry point: rank 256, aligned, span)
+  if (a.l_tm) return launch_gemm_ks<MODE, 16, true, true>(kid, a, s);
   const size_t reqs = (size_t)(kTR + a.rows_per_req - 1) / a.rows_per_req + 1;  // requests a row block touches
   if ((reqs * (size_t)a.ldL_r + (size_t)a.V) * 2 >= kOOB)
     return fail(DSP_ERR_SHAPE, "the L rows of %d parent rows must span less than 2 GiB", kTR);
@@ -1558,9 +2173,30 @@ int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
   return al ? launch_gemm_al<MODE, true>(kid, a, s) : launch_gemm_al<MODE, false>(kid, a, s);
 }
 
+// Layout of the chain's base logits: row-major (DSP_BF16: element (i, d, v) at
+// L + i*ldL_r + d*ldL_d + v) or token-major (DSP_BF16_TOKEN_MAJOR: at L + i + d*ldL_d +
+// v*ldL_r). Returns DSP_OK or an error; *tm says which.
+int32_t check_l_layout(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d, int32_t V, int32_t R,
+                       int32_t n, int32_t rank, int32_t* tm) {
+  *tm = l_dtype == DSP_BF16_TOKEN_MAJOR;
+  if (!*tm) {
+    if (ldL_d < V || ldL_r < (int64_t)(n - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
+    return DSP_OK;
+  }
+  if (rank != 256) return fail(DSP_ERR_UNSUPPORTED, "token-major L is supported at rank 256");
+  if (R % 8) return fail(DSP_ERR_SHAPE, "token-major L needs R a multiple of 8 (got %d)", R);
+  if (ldL_r < R || ldL_d < (int64_t)(V - 1) * ldL_r + R) return fail(DSP_ERR_SHAPE, "token-major L strides too small");
+  if (((uintptr_t)L) % 16 || ldL_r % 8 || ldL_d % 8)
+    return fail(DSP_ERR_ALIGN, "token-major L: 16-byte aligned base, strides multiples of 8 elements");
+  // the stage loads address one depth's tokens (plus a stage past V) from 32-bit offsets
+  if ((((size_t)V + kTS) * ldL_r + kTR) * 2 >= kOOB)
+    return fail(DSP_ERR_SHAPE, "token-major L of one depth must span less than 2 GiB");
+  return DSP_OK;
+}
+
 int32_t check_markov_common(const void* L, int32_t l_dtype, const void* U, const void* Wt, int32_t V,
                             int32_t rank) {
-  if (l_dtype != DSP_BF16) return fail(DSP_ERR_DTYPE, "L must be bf16");
+  if (l_dtype != DSP_BF16 && l_dtype != DSP_BF16_TOKEN_MAJOR) return fail(DSP_ERR_DTYPE, "L must be bf16");
   if (!L || !U || !Wt) return fail(DSP_ERR_NULL, "L, U and Wt are required");
   if (V < 1) return fail(DSP_ERR_SHAPE, "V must be >= 1");
   if (rank < 32 || rank > 512 || rank % 32) return fail(DSP_ERR_SHAPE, "rank must be a multiple of 32 in [32, 512]");
@@ -1610,6 +2246,88 @@ TreeLayout tree_layout(int R, int D, int V, int rank, int topk, int F) {
   return t;
 }
 
+// ---------------------------------------------------------------- persistent chain (host)
+// Workgroups of the persistent chain on the current device (one per CU, as many as there
+// are 32-token tiles at most), or 0 when the path does not apply: it needs every CU's
+// workgroup resident at once and at most kPMaxTiles tiles per workgroup.
+int persist_groups(int V) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0, fit = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = -1;
+    (void)hipFuncSetAttribute((const void*)chain_persist_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kPLds);
+    (void)hipFuncSetAttribute((const void*)chain_persist_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kPLds);
+    if (n > 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, chain_persist_kernel<true>, kPThreads, kPLds) != hipSuccess)
+      fit = 0;
+    int fit2 = 0;
+    if (n > 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit2, chain_persist_kernel<false>, kPThreads, kPLds) != hipSuccess)
+      fit2 = 0;
+    cus[dev] = n > 0 && fit >= 1 && fit2 >= 1 ? (n < kTargetWGs ? n : kTargetWGs) : -1;
+  }
+  if (cus[dev] < 0) return 0;
+  const int nst = (V + 31) / 32;
+  const int G = nst < cus[dev] ? nst : cus[dev];
+  return (nst + G - 1) / G <= kPMaxTiles ? G : 0;
+}
+
+struct PersistLayout {
+  size_t off_part, off_keys, off_bar, total;
+};
+PersistLayout persist_layout(int R, int n_steps) {
+  PersistLayout l;
+  size_t off = 0;
+  l.off_part = off;
+  off = align_up(off + (size_t)n_steps * R * kTargetWGs * sizeof(ChainPart), 256);
+  l.off_keys = off;
+  off = align_up(off + (size_t)n_steps * kPGroups * R * kPKeyStride * sizeof(uint64_t), 256);
+  l.off_bar = off;
+  off = align_up(off + sizeof(uint32_t), 256);
+  l.total = off;
+  return l;
+}
+
+// Shapes the persistent chain takes (the device-side checks are in persist_groups).
+bool persist_shape_ok(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d, int32_t V, int32_t rank,
+                      int32_t R, int32_t n_steps) {
+  if (l_dtype != DSP_BF16 || rank != 256 || R > kPMaxR) return false;
+  if (((uintptr_t)L) % 16 || ldL_r % 8 || ldL_d % 8) return false;
+  return (((size_t)(R - 1) * ldL_r + (size_t)(n_steps - 1) * ldL_d + V) * 2) < kOOB;
+}
+
+int32_t chain_persistent(int G, const void* L, int64_t ldL_r, int64_t ldL_d, const void* U, const void* Wt,
+                         int32_t V, const int32_t* prev_tok, int32_t R, int32_t n_steps, int32_t* y, int64_t ld_y,
+                         float* logq, int32_t* status, void* ws, hipStream_t s) {
+  const PersistLayout l = persist_layout(R, n_steps);
+  char* base = (char*)ws;
+  PersistInitArgs ia{(uint64_t*)(base + l.off_keys), (size_t)n_steps * kPGroups * R, (uint32_t*)(base + l.off_bar)};
+  launch(DSP_K_MARKOV_MERGE, chain_persist_init_kernel, dim3((unsigned)((ia.n_keys + 255) / 256)), dim3(256), 0, s,
+         ia);
+  int32_t rc = hip_check(hipGetLastError(), "persistent chain init launch");
+  if (rc) return rc;
+  PersistArgs pa{(const uint16_t*)U, (const uint16_t*)Wt, (const uint16_t*)L, ldL_r, ldL_d, prev_tok, V, R,
+                 n_steps, G, (ChainPart*)(base + l.off_part), ia.keys, ia.bar,
+                 (uint32_t)option(DSP_OPT_SPIN_LIMIT), status};
+  if (logq)
+    launch(DSP_K_CHAIN_PERSIST, chain_persist_kernel<true>, dim3((unsigned)G), dim3(kPThreads), (uint32_t)kPLds, s, pa);
+  else
+    launch(DSP_K_CHAIN_PERSIST, chain_persist_kernel<false>, dim3((unsigned)G), dim3(kPThreads), (uint32_t)kPLds, s, pa);
+  rc = hip_check(hipGetLastError(), "persistent chain launch");
+  if (rc) return rc;
+  if (logq) {  // y and log q from the workgroups' partials
+    ChainMergeArgs ma{pa.part, G, R, 0, y, ld_y, logq};
+    launch(DSP_K_MARKOV_MERGE, chain_merge_kernel, dim3((unsigned)R, (unsigned)n_steps), dim3(64), 0, s, ma);
+  } else {    // y from the keys
+    PersistYArgs ya{ia.keys, R, n_steps, y, ld_y};
+    launch(DSP_K_MARKOV_MERGE, chain_persist_y_kernel, dim3((unsigned)((R * n_steps + 255) / 256)), dim3(256), 0,
+           s, ya);
+  }
+  return hip_check(hipGetLastError(), "chain merge launch");
+}
+
 }  // namespace
 }  // namespace dsp
 
@@ -1617,11 +2335,14 @@ using namespace dsp;
 
 extern "C" size_t dsp_draft_markov_step_workspace_size(int32_t R, int32_t V, int32_t rank, int32_t n_steps,
                                                        int32_t want_logq) {
-  (void)rank;
-  (void)n_steps;
   (void)want_logq;
   if (R < 1 || V < 1) return 0;
-  return align_up((size_t)pick_groups(R, V) * R * sizeof(ChainPart), 256);
+  size_t need = align_up((size_t)pick_groups(R, V) * R * sizeof(ChainPart), 256);
+  if (rank == 256 && R <= kPMaxR && n_steps >= 1) {
+    const size_t p = persist_layout(R, n_steps).total;
+    need = p > need ? p : need;
+  }
+  return need;
 }
 
 extern "C" int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t ldL_r, int64_t ldL_d,
@@ -1635,15 +2356,23 @@ extern "C" int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t
   if (R < 1 || n_steps < 1) return fail(DSP_ERR_SHAPE, "need R >= 1 and n_steps >= 1");
   if (!prev_tok || !y || !status) return fail(DSP_ERR_NULL, "prev_tok, y and status are required");
   if (ld_y < n_steps) return fail(DSP_ERR_SHAPE, "ld_y < n_steps");
-  if (ldL_d < V || ldL_r < (int64_t)(n_steps - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
+  int32_t tm = 0;
+  rc = check_l_layout(L, l_dtype, ldL_r, ldL_d, V, R, n_steps, rank, &tm);
+  if (rc) return rc;
   const size_t need = dsp_draft_markov_step_workspace_size(R, V, rank, n_steps, logq != nullptr);
   if (!ws || ws_bytes < need) return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   hipStream_t s = (hipStream_t)stream;
+  if (option(DSP_OPT_CHAIN_PERSISTENT) && persist_shape_ok(L, l_dtype, ldL_r, ldL_d, V, rank, R, n_steps)) {
+    const int Gp = persist_groups(V);
+    if (Gp > 0)
+      return chain_persistent(Gp, L, ldL_r, ldL_d, U, Wt, V, prev_tok, R, n_steps, y, ld_y, logq, status, ws, s);
+  }
   const int G = pick_groups(R, V);
   for (int d = 0; d < n_steps; ++d) {
     GemmArgs ga{(const uint16_t*)U, (const uint16_t*)Wt, V, rank,
                 d == 0 ? prev_tok : y + (d - 1), d == 0 ? 1 : ld_y,
                 (const uint16_t*)L, ldL_r, ldL_d, d, R, 1, G, ws, status};
+    ga.l_tm = tm;
     rc = logq ? launch_gemm<MODE_ARGMAX_LSE>(DSP_K_MARKOV_GEMM, ga, s)
               : launch_gemm<MODE_ARGMAX>(DSP_K_MARKOV_GEMM, ga, s);
     if (rc) return rc;
@@ -1695,7 +2424,9 @@ extern "C" int32_t dsp_draft_rnn_step(const void* L, int32_t l_dtype, int64_t ld
   if (R < 1 || n_steps < 1) return fail(DSP_ERR_SHAPE, "need R >= 1 and n_steps >= 1");
   if (!prev_tok || !y || !status) return fail(DSP_ERR_NULL, "prev_tok, y and status are required");
   if (ld_y < n_steps) return fail(DSP_ERR_SHAPE, "ld_y < n_steps");
-  if (ldL_d < V || ldL_r < (int64_t)(n_steps - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
+  int32_t tm = 0;
+  rc = check_l_layout(L, l_dtype, ldL_r, ldL_d, V, R, n_steps, rank, &tm);
+  if (rc) return rc;
   if (ldh_k < H || ldh_r < (int64_t)(n_steps - 1) * ldh_k + H) return fail(DSP_ERR_SHAPE, "h strides too small");
   if (((uintptr_t)h) % 2 || ((uintptr_t)Gt) % 2 || ((uintptr_t)A) % 2) return fail(DSP_ERR_ALIGN, "h, Gt, A: 2-byte aligned");
   const RnnLayout lay = rnn_layout(R, V, rank, n_steps);
@@ -1722,6 +2453,7 @@ extern "C" int32_t dsp_draft_rnn_step(const void* L, int32_t l_dtype, int64_t ld
     GemmArgs ga{mbf, (const uint16_t*)Wot, V, rank, idx, 1, (const uint16_t*)L, ldL_r, ldL_d, d, R, 1, G, part,
                 status};
     ga.u_rows = R;
+    ga.l_tm = tm;
     rc = logq ? launch_gemm<MODE_ARGMAX_LSE>(DSP_K_MARKOV_GEMM, ga, s)
               : launch_gemm<MODE_ARGMAX>(DSP_K_MARKOV_GEMM, ga, s);
     if (rc) return rc;
@@ -1755,7 +2487,9 @@ extern "C" int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64
     return fail(DSP_ERR_SHAPE, "temperature must be finite and > 0 (use the greedy chain for T = 0)");
   if (!prev_tok || !y || !z || !status) return fail(DSP_ERR_NULL, "prev_tok, y, z and status are required");
   if (ld_y < n_steps) return fail(DSP_ERR_SHAPE, "ld_y < n_steps");
-  if (ldL_d < V || ldL_r < (int64_t)(n_steps - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
+  int32_t tm = 0;
+  rc = check_l_layout(L, l_dtype, ldL_r, ldL_d, V, R, n_steps, rank, &tm);
+  if (rc) return rc;
   if (ldz_d < V || ldz_r < (int64_t)(n_steps - 1) * ldz_d + V) return fail(DSP_ERR_SHAPE, "z strides too small");
   if (((uintptr_t)z) % 16 || ldz_d % 8 || ldz_r % 8)
     return fail(DSP_ERR_ALIGN, "z must be 16-byte aligned with strides that are multiples of 8 elements");
@@ -1768,6 +2502,7 @@ extern "C" int32_t dsp_draft_markov_sample(const void* L, int32_t l_dtype, int64
     GemmArgs ga{(const uint16_t*)U, (const uint16_t*)Wt, V, rank,
                 d == 0 ? prev_tok : y + (d - 1), d == 0 ? 1 : ld_y,
                 (const uint16_t*)L, ldL_r, ldL_d, d, R, 1, G, ws, status};
+    ga.l_tm = tm;
     ga.zout = (uint16_t*)z;
     ga.ldz_r = ldz_r;
     ga.ldz_d = ldz_d;
@@ -1807,6 +2542,7 @@ extern "C" int32_t dsp_tree_expand(const void* L, int32_t l_dtype, int64_t ldL_r
   if (topN < 1 || topN > 1024) return fail(DSP_ERR_SHAPE, "need 1 <= topN <= 1024");
   if (!anchor || !node_token || !node_parent || !node_depth || !node_score || !n_nodes || !status)
     return fail(DSP_ERR_NULL, "required pointer is NULL");
+  if (l_dtype != DSP_BF16) return fail(DSP_ERR_UNSUPPORTED, "the tree takes row-major L");
   if (ldL_d < V || ldL_r < (int64_t)(D - 1) * ldL_d + V) return fail(DSP_ERR_SHAPE, "L strides too small");
   const TreeLayout T = tree_layout(R, D, V, rank, topk, frontier);
   if (!ws || ws_bytes < T.total) return fail(DSP_ERR_WORKSPACE, "workspace needs %zu bytes", T.total);

@@ -50,10 +50,13 @@ extern "C" {
 
 #define DSP_F32   0
 #define DSP_BF16  1
+/* bf16 base logits stored token-major (the chain's L only; see dsp_draft_markov_step) */
+#define DSP_BF16_TOKEN_MAJOR  2
 
 #define DSP_STATUS_TOKEN_RANGE   1  /* a token id outside [0, V) */
 #define DSP_STATUS_WINDOW_RANGE  2  /* cu_seqlens / windows inconsistent with K or max_rows */
 #define DSP_STATUS_NONFINITE     4  /* a logits row whose maximum is not finite */
+#define DSP_STATUS_TIMEOUT       8  /* a persistent launch's grid barrier gave up waiting */
 
 #define DSP_SCHED_EARLY_STOP  0
 #define DSP_SCHED_ARGMAX      1
@@ -277,7 +280,14 @@ int32_t dsp_verify_rejection_noalloc(const void* tgt, int32_t t_dtype, int64_t l
 /*   z_d = L[i, d-1, :] + U[y_{d-1}, :] . W,   y_d = argmax_v z_d (fp32 z,    */
 /*   lowest id on ties),  y_0 = prev_tok[i];                                  */
 /*   logq[i, d-1] = z_d[y_d] - logsumexp(z_d)  (if logq != NULL).             */
-/* L: bf16, element (i, d, v) at L + i*ldL_r + d*ldL_d + v.                   */
+/* L: bf16. l_dtype DSP_BF16: element (i, d, v) at L + i*ldL_r + d*ldL_d + v */
+/*    (ldL_d >= V). l_dtype DSP_BF16_TOKEN_MAJOR: element (i, d, v) at       */
+/*    L + i + d*ldL_d + v*ldL_r, i.e. ldL_r is the stride between tokens     */
+/*    (ldL_r >= R, ldL_d >= (V-1)*ldL_r + R; a [B, V, R] buffer); it needs    */
+/*    rank 256, R a multiple of 8, a 16-byte aligned L and both strides      */
+/*    multiples of 8 (else DSP_ERR_UNSUPPORTED / _SHAPE / _ALIGN). Same       */
+/*    results either way; the token-major tile of a step is one contiguous   */
+/*    read per 32 tokens.                                                    */
 /* U: bf16 [V, rank] row-major (row y = the first factor's row of token y).   */
 /* Wt: bf16 [V, rank] row-major = the second factor W [rank, V] stored        */
 /*     vocab-major (Wt[v*rank + j] = W[j][v]).                               */
@@ -311,7 +321,8 @@ int32_t dsp_draft_markov_step(const void* L, int32_t l_dtype, int64_t ldL_r, int
 /* draws apart from the verify step's (stream 0). round_dev (device,         */
 /* nullable) replaces `round` with *round_dev, read and not advanced (the    */
 /* verify call advances it), so a captured cycle draws fresh uniforms.       */
-/* L, U, Wt as dsp_draft_markov_step; z: bf16, 16-byte aligned, ldz_d and    */
+/* L (either layout), U, Wt as dsp_draft_markov_step; z: bf16, 16-byte       */
+/* aligned, ldz_d and                                                       */
 /* ldz_r multiples of 8 elements, ldz_d >= V; y and logq [R, n_steps] with   */
 /* row stride ld_y. temperature must be finite and > 0 (the greedy chain is  */
 /* dsp_draft_markov_step). A row whose mass is not finite sets               */
@@ -372,7 +383,8 @@ int32_t dsp_draft_rnn_step(const void* L, int32_t l_dtype, int64_t ldL_r, int64_
 /* of word j / 64 of node o is set iff node j is o or an ancestor of o (the   */
 /* root is implicit) -- the tree-causal attention pattern of the target      */
 /* forward that verifies the tree ([P]); rows past n_nodes are zero.         */
-/* L, U, Wt layouts as dsp_draft_markov_step.                                 */
+/* U, Wt layouts as dsp_draft_markov_step; L row-major only (l_dtype          */
+/* DSP_BF16, ldL_d >= V; else DSP_ERR_UNSUPPORTED).                          */
 /* The selection reads each base-logit row once more up front (R*(D-1) rows) */
 /* to bound every parent row's 4th-largest z from below; entries under the   */
 /* bound cannot be among the top 4, so the outputs do not depend on it.      */
@@ -446,7 +458,7 @@ int32_t dsp_stream_read(const void* p, size_t bytes, uint32_t* sink, void* strea
 #define DSP_K_SCHEDULE         4  /* scheduler: prefix sums, throughput test, windows */
 #define DSP_K_PACK             5
 #define DSP_K_MARKOV_GEMM      6
-#define DSP_K_MARKOV_MERGE     7
+#define DSP_K_MARKOV_MERGE     7  /* chain merge (and the persistent chain's key reset) */
 #define DSP_K_TREE_GEMM        8
 #define DSP_K_TREE_MERGE       9
 #define DSP_K_TREE_FINAL      10
@@ -456,10 +468,28 @@ int32_t dsp_stream_read(const void* p, size_t bytes, uint32_t* sink, void* strea
 #define DSP_K_CALIBRATION     14  /* calibration of the confidences against the verify */
 #define DSP_K_RNN_MEMO        15  /* RNN head: memo update */
 #define DSP_K_RNN_PROJ        16  /* RNN head: projection of the backbone states */
-#define DSP_K_COUNT           17
+#define DSP_K_CHAIN_PERSIST   17  /* greedy chain: all steps in one persistent launch */
+#define DSP_K_COUNT           18
 int32_t dsp_prof_enable(int32_t mask);
 int32_t dsp_prof_reset(void);
 int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);
+
+/* ------------------------------------------------------------------------ */
+/* Library options (process-wide; for tests and diagnostics).               */
+/*                                                                          */
+/* DSP_OPT_CHAIN_PERSISTENT: 1 lets dsp_draft_markov_step run all steps in  */
+/*   one persistent launch where that path applies (see there); 0 (default) */
+/*   keeps one launch per step, which measures faster on gfx950. Tokens are  */
+/*   identical either way; log q agrees to fp32 rounding.                    */
+/* DSP_OPT_SPIN_LIMIT: polls a persistent launch's grid barrier makes before */
+/*   it gives up and sets DSP_STATUS_TIMEOUT (default 2^20, about a second); */
+/*   0 makes every wait that is not already satisfied give up at once.       */
+/* Returns DSP_ERR_SHAPE for an unknown option or a negative value. Not      */
+/* thread safe; set before issuing work.                                     */
+/* ------------------------------------------------------------------------ */
+#define DSP_OPT_CHAIN_PERSISTENT  0
+#define DSP_OPT_SPIN_LIMIT        1
+int32_t dsp_set_option(int32_t option, int64_t value);
 
 #ifdef __cplusplus
 }

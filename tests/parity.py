@@ -27,6 +27,12 @@ def to_gpu_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev())
 
 
+def to_gpu_bf16_token_major(bits):
+    """[R, B, V] bfloat16 bits -> a [B, V, R] GPU buffer viewed as [R, B, V] (unit stride
+    over requests: the chain's token-major base-logit layout)."""
+    return to_gpu_bf16(np.ascontiguousarray(np.transpose(bits, (1, 2, 0)))).permute(2, 0, 1)
+
+
 def to_gpu(arr, dtype=None):
     t = torch.from_numpy(np.ascontiguousarray(arr))
     if dtype is not None:

@@ -97,6 +97,28 @@ def test_host_validation_codes():
                                      None) == -2
     assert lib.dsp_draft_markov_step(p, 1, 1000, 100, ctypes.c_void_p(18), p, 100, 64, p, 2, 4, p, 4, None,
                                      p, p, 1 << 30, None) == -4
+    # markov, token-major base logits: rank 256 only, R a multiple of 8, strides and span
+    TM = _abi.DSP_BF16_TOKEN_MAJOR
+    assert lib.dsp_draft_markov_step(p, TM, 16, 16 * 100, p, p, 100, 64, p, 16, 4, p, 4, None, p, p, 1 << 30,
+                                     None) == -6
+    rc, msg = _err(lib.dsp_draft_markov_step(p, TM, 16, 16 * 100, p, p, 100, 256, p, 12, 4, p, 4, None, p, p,
+                                             1 << 30, None))
+    assert rc == -2 and "multiple of 8" in msg
+    assert lib.dsp_draft_markov_step(p, TM, 8, 16 * 100, p, p, 100, 256, p, 16, 4, p, 4, None, p, p, 1 << 30,
+                                     None) == -2  # token stride below R
+    assert lib.dsp_draft_markov_step(p, TM, 16, 99 * 16, p, p, 100, 256, p, 16, 4, p, 4, None, p, p, 1 << 30,
+                                     None) == -2  # depth stride below (V-1)*ldL_r + R
+    assert lib.dsp_draft_markov_step(ctypes.c_void_p(24), TM, 16, 1600, p, p, 100, 256, p, 16, 4, p, 4, None, p,
+                                     p, 1 << 30, None) == -4
+    assert lib.dsp_draft_markov_step(p, TM, 20, 2000, p, p, 100, 256, p, 16, 4, p, 4, None, p, p, 1 << 30,
+                                     None) == -4  # token stride not a multiple of 8
+    rc, msg = _err(lib.dsp_draft_markov_step(p, TM, 1 << 14, 151936 << 14, p, p, 151936, 256, p, 16, 4, p, 4,
+                                             None, p, p, 1 << 30, None))
+    assert rc == -2 and "2 GiB" in msg
+    assert lib.dsp_draft_markov_sample(p, TM, 12, 1200, p, p, 100, 256, p, 12, 4, 1.0, 0, 0, None, None, p, 4,
+                                       None, p, 1000, 104, p, p, 1 << 30, None) == -2
+    assert lib.dsp_tree_expand(p, TM, 16, 1600, p, p, 100, 256, p, 16, 4, 4, 4, 8, p, p, p, p, p, None, p, p,
+                               1 << 30, None) == -6  # the tree takes row-major L
     # tree: top-k above 4
     assert lib.dsp_tree_expand(p, 1, 1000, 100, p, p, 100, 64, p, 2, 4, 5, 4, 8, p, p, p, p, p, None, p, p,
                                1 << 30, None) == -2

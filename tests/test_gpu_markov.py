@@ -8,15 +8,15 @@ import workloads
 from oracle import markov as om
 from oracle import pctree as opt
 from oracle import verify as ov
-from parity import ARGMAX_BAND, SAMPLE_BAND, TieCounter, host, to_gpu, to_gpu_bf16
+from parity import ARGMAX_BAND, SAMPLE_BAND, TieCounter, host, to_gpu, to_gpu_bf16, to_gpu_bf16_token_major
 
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_inputs(c):
+def _gpu_inputs(c, token_major=False):
     Wt = np.ascontiguousarray(c["W"].T)  # second factor stored vocab-major
-    return (to_gpu_bf16(c["L"]), to_gpu_bf16(c["U"]), to_gpu_bf16(Wt),
-            to_gpu(c["anchors"].astype(np.int32)))
+    Lg = to_gpu_bf16_token_major(c["L"]) if token_major else to_gpu_bf16(c["L"])
+    return (Lg, to_gpu_bf16(c["U"]), to_gpu_bf16(Wt), to_gpu(c["anchors"].astype(np.int32)))
 
 
 def _f32(c):
@@ -24,14 +24,14 @@ def _f32(c):
             workloads.bf16_bits_to_f32(c["W"]))
 
 
-def _check_chain(c, requests=None, want_logq=True, w_boost=1.0):
+def _check_chain(c, requests=None, want_logq=True, w_boost=1.0, token_major=False):
     L, U, W = _f32(c)
     if w_boost != 1.0:
         Wb = workloads.f32_to_bf16_bits(W * np.float32(w_boost))
         c = dict(c, W=Wb)
         L, U, W = _f32(c)
-    Lg, Ug, Wtg, ag = _gpu_inputs(c)
-    print(f"chain R={c['R']} B={c['B']} V={c['V']} rank={c['rank']}", flush=True)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c, token_major)
+    print(f"chain R={c['R']} B={c['B']} V={c['V']} rank={c['rank']} token_major={token_major}", flush=True)
     g = dsp.draft_markov_step(Lg, Ug, Wtg, ag, want_logq=want_logq)
     torch.cuda.synchronize()
     assert int(host(g["status"])[0]) == 0
@@ -84,6 +84,124 @@ def test_chain_c4_full():
     """256 requests x 16 steps, V=151,936, rank 256; every request checked with replay."""
     c = workloads.markov_chain()
     _check_chain(c, want_logq=True)
+
+
+@pytest.mark.parametrize("R,B,V", [(8, 4, 1000), (136, 3, 4099), (264, 2, 30011)])
+def test_chain_token_major_layout(R, B, V):
+    """Base logits stored token-major ([B, V, R]): tokens exact against the oracle (counted
+    near-ties), and every output bit-identical to the row-major call's (same arithmetic)."""
+    c = workloads.markov_case(R, B, V, rank=256, seed=R + V + 7)
+    y = _check_chain(c, w_boost=300.0, token_major=True)
+    Lr, Ug, Wtg, ag = _gpu_inputs(c)
+    Lt = _gpu_inputs(c, True)[0]
+    assert Lt.stride(0) == 1
+    a = dsp.draft_markov_step(Lr, Ug, Wtg, ag, want_logq=True)  # both on the per-step kernels
+    b = dsp.draft_markov_step(Lt, Ug, Wtg, ag, want_logq=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(a["y"]), host(b["y"]))
+    np.testing.assert_array_equal(host(a["logq"]).view(np.uint32), host(b["logq"]).view(np.uint32))
+    assert int(host(b["status"])[0]) == 0
+
+
+def test_chain_token_major_c4_full():
+    """The Markov-chain workload (256 x 16, V=151,936, rank 256) with token-major base
+    logits: every request against the oracle, and identical to the row-major outputs."""
+    c = workloads.markov_chain()
+    y = _check_chain(c, want_logq=True, token_major=True)
+    Lr, Ug, Wtg, ag = _gpu_inputs(c)
+    a = dsp.draft_markov_step(Lr, Ug, Wtg, ag)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(a["y"]), y)
+
+
+def _padded_l(bits, vp):
+    """[R, B, V] base logits in a buffer whose rows are vp >= V entries apart (vp a
+    multiple of 8: the persistent chain's alignment)."""
+    R, B, V = bits.shape
+    buf = np.zeros((R, B, vp), np.uint16)
+    buf[..., :V] = bits
+    return to_gpu_bf16(buf)[..., :V]
+
+
+def _chain_both_paths(c, Lg, want_logq=True):
+    """The chain on both launch paths; checks that the persistent one ran, that the tokens
+    are identical and that log q agrees to fp32 rounding (the paths split the vocabulary
+    into different partial sums)."""
+    _, Ug, Wtg, ag = _gpu_inputs(c)
+    dsp.prof_reset()
+    dsp.prof_enable(kernels=["CHAIN_PERSIST"])
+    dsp.set_option("chain_persistent", 1)
+    try:
+        p = dsp.draft_markov_step(Lg, Ug, Wtg, ag, want_logq=want_logq)
+        torch.cuda.synchronize()
+        assert dsp.prof_query("CHAIN_PERSIST")[1] == 1, "the persistent chain did not run"
+    finally:
+        dsp.set_option("chain_persistent", 0)
+        dsp.prof_enable(False)
+        dsp.prof_reset()
+    q = dsp.draft_markov_step(Lg, Ug, Wtg, ag, want_logq=want_logq)
+    torch.cuda.synchronize()
+    assert int(host(p["status"])[0]) == 0 and int(host(q["status"])[0]) == 0
+    np.testing.assert_array_equal(host(p["y"]), host(q["y"]))
+    return p, q
+
+
+@pytest.mark.parametrize("R,B,V", [(1, 3, 100), (5, 4, 1000), (33, 2, 4099), (100, 3, 30011), (256, 2, 9000),
+                                   (64, 3, 151936), (256, 2, 155000)])
+def test_chain_persistent(R, B, V):
+    """Rank 256, aligned row-major L: the whole chain in one persistent launch, against the
+    oracle (every request, counted near-ties) and against the per-step launches.
+    Covers one row, ragged column blocks, few vocabulary tiles (idle waves and workgroups)
+    and the largest vocabulary the path takes (19 tiles per workgroup)."""
+    c = workloads.markov_case(R, B, V, rank=256, seed=R + V + 11)
+    c = dict(c, W=workloads.f32_to_bf16_bits(_f32(c)[2] * np.float32(300.0)))  # choices the head changes
+    vp = (V + 7) // 8 * 8
+    Lg = _padded_l(c["L"], vp)
+    print(f"persistent chain R={R} B={B} V={V}", flush=True)
+    p, q = _chain_both_paths(c, Lg)
+    L, U, W = _f32(c)
+    y = host(p["y"]).astype(np.int64)
+    orc = om.chain(L, U, W, c["anchors"], forced=y)
+    ties = TieCounter()
+    ties.decisions += y.size
+    for i, d in np.argwhere(orc["y"] != y):
+        prev = c["anchors"][i] if d == 0 else y[i, d - 1]
+        z = om.markov_logits(L[i, d][None], U, W, [prev])[0]
+        assert z[orc["y"][i, d]] - z[y[i, d]] < ARGMAX_BAND * max(1.0, abs(z[orc["y"][i, d]])), (i, d)
+        ties.near += 1
+    ties.check()
+    for name, g in (("persistent", p), ("per step", q)):
+        lq = host(g["logq"]).astype(np.float64)
+        err = np.abs(lq - orc["logq_forced"])
+        bad = np.argwhere(err > 1e-5 + 1e-5 * np.abs(orc["logq_forced"]))
+        assert not len(bad), (name, [(int(i), int(d), lq[i, d], orc["logq_forced"][i, d]) for i, d in bad[:5]])
+
+
+def test_chain_persistent_c4_matches_per_step():
+    """The Markov-chain workload (256 x 16, V=151,936): persistent and per-step launches
+    give identical tokens and matching log q (oracle parity of this shape: test_chain_c4_full)."""
+    c = workloads.markov_chain()
+    Lg, _, _, _ = _gpu_inputs(c)
+    _chain_both_paths(c, Lg, want_logq=True)
+    _chain_both_paths(c, Lg, want_logq=False)
+
+
+def test_chain_persistent_barrier_timeout_is_reported():
+    """A grid barrier that gives up (forced from the host with a spin limit of 0 polls)
+    sets DSP_STATUS_TIMEOUT and the launch still drains; the next call, with the default
+    limit, is correct."""
+    c = workloads.markov_case(64, 3, 9000, rank=256, seed=77)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    dsp.set_option("spin_limit", 0)
+    dsp.set_option("chain_persistent", 1)
+    try:
+        g = dsp.draft_markov_step(Lg, Ug, Wtg, ag)
+        torch.cuda.synchronize()
+    finally:
+        dsp.set_option("spin_limit", 1 << 20)
+        dsp.set_option("chain_persistent", 0)
+    assert int(host(g["status"])[0]) & dsp.DSP_STATUS_TIMEOUT
+    _chain_both_paths(c, Lg)
 
 
 def _check_tree(c, topk, F, N, requests=None, w_boost=1.0, status=0):
@@ -187,7 +305,7 @@ def test_tree_verify_c5_shape_planted_paths():
 
 # ---------------------------------------------------------------- sampled chain
 
-def _check_sampled(c, T, seed=0, rnd=0, requests=None, w_boost=1.0):
+def _check_sampled(c, T, seed=0, rnd=0, requests=None, w_boost=1.0, token_major=False):
     """Sampled chain against the oracle with replay of the GPU's draws: the emitted bf16 rows
     bit-exact except entries the oracle marks as rounding near-ties (then within one bf16
     unit), the draws exact except counted near-ties, logq within 1e-5."""
@@ -195,8 +313,9 @@ def _check_sampled(c, T, seed=0, rnd=0, requests=None, w_boost=1.0):
     if w_boost != 1.0:
         c = dict(c, W=workloads.f32_to_bf16_bits(W * np.float32(w_boost)))
         L, U, W = _f32(c)
-    Lg, Ug, Wtg, ag = _gpu_inputs(c)
-    print(f"sampled chain R={c['R']} B={c['B']} V={c['V']} rank={c['rank']} T={T}", flush=True)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c, token_major)
+    print(f"sampled chain R={c['R']} B={c['B']} V={c['V']} rank={c['rank']} T={T} token_major={token_major}",
+          flush=True)
     g = dsp.draft_markov_sample(Lg, Ug, Wtg, ag, T, seed=seed, round=rnd)
     torch.cuda.synchronize()
     assert int(host(g["status"])[0]) == 0
@@ -239,6 +358,19 @@ def test_chain_sampled_small(R, B, V, rank, T):
     c = workloads.markov_case(R, B, V, rank=rank, seed=R + V + 1)
     _check_sampled(c, T, seed=3, rnd=1, w_boost=100.0)
     _check_sampled(c, T, seed=4, rnd=2)
+
+
+def test_chain_sampled_token_major_layout():
+    """Sampled chain from token-major base logits: oracle parity, and the draws, logq and
+    emitted rows bit-identical to the row-major call's."""
+    c = workloads.markov_case(40, 3, 9001, rank=256, seed=41)
+    g, y = _check_sampled(c, 0.8, seed=5, rnd=3, w_boost=100.0, token_major=True)
+    Lr, Ug, Wtg, ag = _gpu_inputs(dict(c, W=workloads.f32_to_bf16_bits(_f32(c)[2] * np.float32(100.0))))
+    a = dsp.draft_markov_sample(Lr, Ug, Wtg, ag, 0.8, seed=5, round=3)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(a["y"]), y)
+    np.testing.assert_array_equal(host(a["logq"]).view(np.uint32), host(g["logq"]).view(np.uint32))
+    np.testing.assert_array_equal(host(a["z"].contiguous().view(torch.int16)), host(g["z"].contiguous().view(torch.int16)))
 
 
 def test_chain_sampled_round_dev_and_req_id():
