@@ -50,16 +50,13 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* wsum) {
   }
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t run = 0;
-    for (int j = 0; j < kSchedThreads / 64; ++j) {
-      const uint64_t t = wsum[j];
-      wsum[j] = run;
-      run += t;
-    }
-  }
-  __syncthreads();
-  return wsum[w] + inc - v;
+  // every thread adds up the waves before its own (16 independent LDS reads, no serial
+  // pass by one thread)
+  uint64_t pre = 0;
+#pragma unroll
+  for (int j = 0; j < kSchedThreads / 64; ++j) pre += j < w ? wsum[j] : 0ull;
+  __syncthreads();  // wsum may be reused by the next scan
+  return pre + inc - v;
 }
 
 // conf [n] into LDS: eight loads per thread in flight per round (clamped, stored only
@@ -221,6 +218,90 @@ __device__ void pack_body(const int32_t* __restrict__ windows, int R, int K, con
   }
 }
 
+// The pack inside the selection workgroup (R*K <= kMaxCand): every token it may copy is
+// loaded up front (pack_prefetch, issued at the start of the selection so the loads
+// overlap it), the windows come from LDS and the offsets stay in LDS, so the copy needs
+// no further round trip to memory. Thread t holds items t, t + 1024, ... of the
+// (request, position) grid R x (K+1), position 0 being the anchor.
+constexpr int kPackPre = 2 * kMaxCand / kSchedThreads;  // R*(K+1) <= 2*R*K
+// (request, position) of item j of the R x (K+1) grid without an integer division:
+// (j + 1/2) / (K+1) is at least 1/(2(K+1)) >= 1/258 away from an integer, and the float
+// quotient of j < 2^15 errs by less than 2^-8, so truncation gives the exact quotient.
+__device__ __forceinline__ void pack_item(int j, int K1, float inv_k1, int& i, int& k) {
+  i = (int)(((float)j + 0.5f) * inv_k1);
+  k = j - i * K1;
+}
+__device__ void pack_prefetch(int R, int K, const PackArgs& pa, int32_t (&tok)[kPackPre]) {
+  const int K1 = K + 1, n = R * K1, tid = threadIdx.x;
+  const float inv_k1 = 1.0f / (float)K1;
+#pragma unroll
+  for (int q = 0; q < kPackPre; ++q) {  // clamped items (masked at use): all loads in flight at once
+    const int j = min(tid + q * kSchedThreads, n - 1);
+    int i, k;
+    pack_item(j, K1, inv_k1, i, k);
+    tok[q] = k == 0 ? pa.anchors[i] : pa.drafts[(size_t)i * pa.ld + k - 1];
+  }
+}
+__device__ void pack_body_lds(const int* s_win, int R, int K, const PackArgs& pa, uint64_t* wsum, int* s_cu,
+                              const int32_t (&tok)[kPackPre]) {
+  const int tid = threadIdx.x;
+  const int C = (R + kSchedThreads - 1) / kSchedThreads;
+  const int i0 = min(R, tid * C), i1 = min(R, i0 + C);
+  uint64_t local = 0;
+  bool bad = false;
+  for (int i = i0; i < i1; ++i) {
+    int w = s_win[i];
+    if (w < 0 || w > K) {
+      bad = true;
+      w = w < 0 ? 0 : K;
+    }
+    local += (uint64_t)(w + 1);
+  }
+  if (bad) atomicOr(pa.status, DSP_STATUS_WINDOW_RANGE);
+  const uint64_t ex = block_exclusive_scan_u64(local, wsum);
+  int pos = (int)ex;
+  if (tid == 0) {
+    pa.cu[0] = 0;
+    s_cu[0] = 0;
+  }
+  for (int i = i0; i < i1; ++i) {
+    int w = s_win[i];
+    w = w < 0 ? 0 : (w > K ? K : w);
+    pos += w + 1;
+    pa.cu[i + 1] = pos;
+    s_cu[i + 1] = pos;
+  }
+  if (i1 == R && i0 < i1) {
+    const int T = pos;
+    int tier = T;
+    if (pa.tiers.n > 0) {
+      tier = -1;
+      for (int t = 0; t < pa.tiers.n; ++t)
+        if (pa.tiers.v[t] >= T) {
+          tier = pa.tiers.v[t];
+          break;
+        }
+    }
+    pa.total_and_tier[0] = T;
+    pa.total_and_tier[1] = tier;
+  }
+  __syncthreads();
+  const int K1 = K + 1, n = R * K1;
+  const float inv_k1 = 1.0f / (float)K1;
+#pragma unroll
+  for (int q = 0; q < kPackPre; ++q) {
+    const int j = tid + q * kSchedThreads;
+    if (j >= n) break;
+    int i, k;
+    pack_item(j, K1, inv_k1, i, k);
+    const int start = s_cu[i];
+    if (start + k >= s_cu[i + 1]) continue;  // beyond this request's window
+    pa.tokens[start + k] = tok[q];
+    pa.row_req[start + k] = i;
+    pa.row_pos[start + k] = k;
+  }
+}
+
 __global__ __launch_bounds__(1024) void pack_kernel(const int32_t* __restrict__ windows, int R, int K,
                                                     PackArgs pa) {
   __shared__ uint64_t wsum[16];
@@ -234,7 +315,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     const float* __restrict__ conf, int R, int K, const double* __restrict__ cost, int mode, int M,
     double threshold, int Q, const uint64_t* __restrict__ sorted, int32_t* __restrict__ windows,
     double* __restrict__ survival, double* __restrict__ stats, PackArgs pa) {
-  __shared__ float s_conf[kMaxCand];  // threshold mode
+  __shared__ float s_conf[kMaxCand + 1];  // threshold mode; then the pack's R + 1 offsets
   __shared__ int cnt[kMaxCand];
   __shared__ uint64_t wsum[kSchedThreads / 64];
   __shared__ double smd[kSchedThreads / 64];
@@ -243,6 +324,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
   const int tid = threadIdx.x;
   const int n = R * K;
   const double scale = ldexp(1.0, Q);
+  int32_t tok[kPackPre];
+  if (pa.cu) pack_prefetch(R, K, pa, tok);  // in flight during the selection
+  int* s_cu = (int*)s_conf;                  // the pack's offsets (s_conf is free by then)
 
   if (mode == DSP_SCHED_THRESHOLD) {
     // n_i = #{k : S_{i,k} >= threshold} on the fp64 survival; no ranking needed
@@ -262,6 +346,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
         }
       }
       windows[i] = c;
+      cnt[i] = c;
       cnt_all += c;
     }
     const int Nt = block_sum<kSchedThreads / 64>(cnt_all, smi);
@@ -274,9 +359,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
       stats[3] = (double)Q;
     }
     if (pa.cu) {  // the pack of these windows, in this workgroup
-      __threadfence_block();
       __syncthreads();
-      pack_body(windows, R, K, pa, wsum);
+      pack_body_lds(cnt, R, K, pa, wsum, s_cu, tok);
     }
     return;
   }
@@ -365,10 +449,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     stats[2] = cost[N] != 0.0 ? __ddiv_rn(E, cost[N]) : (E == 0.0 ? 0.0 : INFINITY);
     stats[3] = (double)Q;
   }
-  if (pa.cu) {  // the pack of these windows, in this workgroup
-    __threadfence_block();
+  if (pa.cu) {  // the pack of these windows, in this workgroup (windows from LDS)
     __syncthreads();
-    pack_body(windows, R, K, pa, wsum);
+    pack_body_lds(cnt, R, K, pa, wsum, s_cu, tok);
   }
 }
 
