@@ -59,15 +59,15 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* wsum) {
   return pre + inc - v;
 }
 
-// conf [n] into LDS: eight loads per thread in flight per round (clamped, stored only
-// in range), instead of one round trip per element.
+// conf [n] into LDS: 32 loads per thread in flight per round (clamped, stored only in
+// range), so a whole table of up to 32 x blockDim entries takes one round trip.
 __device__ __forceinline__ void stage_conf(const float* __restrict__ conf, int n, float* s_conf) {
-  for (int j0 = threadIdx.x; j0 < n; j0 += 8 * blockDim.x) {
-    float v[8];
+  for (int j0 = threadIdx.x; j0 < n; j0 += 32 * blockDim.x) {
+    float v[32];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = conf[min(j0 + q * (int)blockDim.x, n - 1)];
+    for (int q = 0; q < 32; ++q) v[q] = conf[min(j0 + q * (int)blockDim.x, n - 1)];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < 32; ++q)
       if (j0 + q * (int)blockDim.x < n) s_conf[j0 + q * blockDim.x] = v[q];
   }
 }
@@ -97,8 +97,8 @@ __device__ void candidate_keys(const float* __restrict__ conf, int R, int K, dou
       }
     }
   }
-  // padding keys (never below a real key) up to a whole number of 128-key strips
-  for (int j = n + threadIdx.x; j < ((n + 127) & ~127); j += blockDim.x) keys[j] = ~0ull;
+  // padding keys (never below a real key) up to a whole number of 256-key strips
+  for (int j = n + threadIdx.x; j < ((n + 255) & ~255); j += blockDim.x) keys[j] = ~0ull;
   __syncthreads();
 }
 
@@ -126,14 +126,14 @@ __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(const float
   const int c = blockIdx.x * kRankCand + cl;
   const uint64_t x = c < n ? keys[c] : 0ull;
   int cnt = 0;
-  const int np = (n + 127) & ~127;  // padded with keys above every real one
+  const int np = (n + 255) & ~255;  // padded with keys above every real one
   typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-  for (int j = 2 * sl; j < np; j += 128) {
-    u64x2 v[4];
+  for (int j = 2 * sl; j < np; j += 256) {  // eight reads in flight per round
+    u64x2 v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = *(const u64x2*)&keys[j + 32 * q];
+    for (int q = 0; q < 8; ++q) v[q] = *(const u64x2*)&keys[j + 32 * q];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) cnt += (v[q].x < x ? 1 : 0) + (v[q].y < x ? 1 : 0);
+    for (int q = 0; q < 8; ++q) cnt += (v[q].x < x ? 1 : 0) + (v[q].y < x ? 1 : 0);
   }
   part[tid] = cnt;
   __syncthreads();
