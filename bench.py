@@ -302,11 +302,17 @@ def bench_verify(args, which, c, cpu):
     w0 = c["w0"]
     conf, cost, anchors, x = _gpu(dev, c["conf"]), _gpu(dev, c["cost"]), _gpu(dev, c["anchors"]), _gpu(dev, c["x"])
     drf = _bf16(dev, c["d"])
+    # the packed target rows at the front of a buffer sized for the largest batch, R x (K+1)
+    # rows: the step is captured once with max_rows = R x (K+1), as a caller that learns the
+    # packed total only on the device would (its kernels skip the rows past that total)
+    max_rows = R * (K + 1)
     if which == "dense-verify":
-        tgt = _bf16(dev, c["t"].reshape(R * (K + 1), V))
+        tgt = _bf16(dev, c["t"].reshape(max_rows, V))
     else:
-        tgt = _bf16(dev, np.concatenate([c["t"][i, :w0[i] + 1] for i in range(R)]))
-    max_rows = tgt.shape[0]
+        tgt = torch.zeros(max_rows, V, dtype=torch.bfloat16, device=dev)
+        packed = _bf16(dev, np.concatenate([c["t"][i, :w0[i] + 1] for i in range(R)]))
+        tgt[:packed.shape[0]].copy_(packed)
+        del packed
     rnd = torch.zeros(1, dtype=torch.int64, device=dev)
     ops = {}
 
@@ -345,7 +351,8 @@ def bench_verify(args, which, c, cpu):
         data="synthetic (seeded N(0,3) logits with 1% +8 boosts; draft = target + Gaussian noise)",
         config=dict(workload=wl, requests=R, block=K, vocab=V, logits_dtype="bf16",
                     arithmetic="fp32 per element (exp2), fp64 sums and decisions",
-                    verified_drafts_per_step=N, packed_rows=T_rows, mean_accepted=float(acc.mean()),
+                    verified_drafts_per_step=N, packed_rows=T_rows, captured_rows=max_rows,
+                    mean_accepted=float(acc.mean()),
                     window_histogram=np.bincount(win, minlength=K + 1).tolist()),
         roofline=hbm_roofline("verify_stats", bytes_stats, kern["VERIFY_STATS"]["avg_us"],
                               traffic_from_profiles("verify.hip", "verify_stats", which)),
@@ -353,9 +360,90 @@ def bench_verify(args, which, c, cpu):
     res["roofline"]["read_ref"] = read_reference(tgt, drf)
     if which == "scheduled-verify":
         res["static"] = bench_static(args, c, dev, drf, x)
+        res["known_total"] = bench_tiering(args, c, dev, tgt, drf, x, conf, cost, anchors)
     if cpu is not None:
         res["cpu_baseline"] = cpu
     return res
+
+
+ROW_TIERS = [256, 320, 384, 512, 640, 768, 1024, 1536, 2048, 3072, 4352]
+
+
+def bench_tiering(args, c, dev, tgt, drf, x, conf, cost, anchors):
+    """The same step when the host learns the packed total before the verify, two ways:
+    one graph captured with max_rows = the packed total (an upper bound on what a host
+    that knows it gets), and one verify graph per row tier replayed by the tier the pack
+    wrote (SGLang article, "Ragged verify"), which costs a read-back of that tier and a
+    wait before the replay. tgt holds the packed rows at its front."""
+    import torch
+    import block_drafting_verification_amd as dsp
+    R = c["R"]
+    w0 = c["w0"]
+    T = int(w0.sum()) + R
+    N = int(w0.sum())
+    out = {}
+
+    # (a) one graph sized to the packed total
+    rnd = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def make_step(stream):
+        sch = dsp.schedule_pack(conf, cost, anchors, x, want_survival=False, stream=stream, prepare=True)
+        ver = dsp.verify_rejection(tgt, sch.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=0,
+                                   round_dev=rnd, max_rows=T, row_req=sch.outputs["row_req"],
+                                   row_pos=sch.outputs["row_pos"], stream=stream, prepare=True)
+
+        def step():
+            sch()
+            ver()
+        return step
+
+    ph = run_phases(make_step, args.steps, args.warmup, ["VERIFY_STATS"], not args.no_flush)
+    out["exact_size_graph"] = dict(ms_per_step=1000.0 * ph["graph_s"] / args.steps,
+                                   value=N * args.steps / ph["graph_s"], max_rows=T,
+                                   verify_stats_us=ph["kernels"]["VERIFY_STATS"]["avg_us"])
+
+    # (b) one verify graph per tier, chosen from the pack's tier
+    s = torch.cuda.Stream()
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    rnd2 = torch.zeros(1, dtype=torch.int64, device=dev)
+    with torch.cuda.stream(s):
+        sch = dsp.schedule_pack(conf, cost, anchors, x, want_survival=False, tiers=ROW_TIERS, stream=s,
+                                prepare=True)
+        shared = {"status": torch.zeros(1, dtype=torch.int32, device=dev)}
+
+        def make(tier):
+            v = dsp.verify_rejection(tgt, sch.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=0,
+                                     round_dev=rnd2, max_rows=tier, row_req=sch.outputs["row_req"],
+                                     row_pos=sch.outputs["row_pos"], out=shared, status=shared["status"],
+                                     stream=s, prepare=True)
+            shared.update({k: t for k, t in v.outputs.items() if t is not None})
+            return v
+
+        g_sch = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_sch, stream=s):
+            sch()
+        tg = dsp.TierGraphs(ROW_TIERS, make, stream=s)
+        tt = sch.outputs["total_and_tier"]
+        for _ in range(args.warmup):
+            g_sch.replay()
+            tg.replay(tt)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        tier = None
+        for i, (a, b) in enumerate(ev):
+            if not args.no_flush:
+                scratch.fill_(i + 1)
+            a.record(s)
+            g_sch.replay()
+            tier = tg.replay(tt)
+            b.record(s)
+        torch.cuda.synchronize()
+        sec = sum(a.elapsed_time(b) for a, b in ev) / 1e3
+    assert int(shared["status"].item()) == 0 and tier == min(t for t in ROW_TIERS if t >= T)
+    out["tier_graphs"] = dict(ms_per_step=1000.0 * sec / args.steps, value=N * args.steps / sec, tier=tier,
+                              packed_rows=T, tiers=ROW_TIERS,
+                              note="schedule+pack graph, read-back of the tier, then that tier's verify graph")
+    return out
 
 
 def bench_static(args, c, dev, drf, x):
@@ -644,7 +732,10 @@ def bench_cycle(args, c, cpu):
     conf0 = dsp.confidence_head(hh, hw, hd["bias"], temps)["conf"]
     w0 = dsp.schedule_windows(conf0, cost)["windows"].cpu().numpy()
     assert np.array_equal(w0, c["w0"]), "the head's confidences give other windows than the workload's"
-    tgt = _bf16(dev, c["tp"])
+    # packed target rows at the front of a buffer for the largest batch (the step is captured
+    # once with max_rows = R x (K+1); its kernels skip the rows past the device-side total)
+    tgt = torch.zeros(R * (K + 1), V, dtype=torch.bfloat16, device=dev)
+    tgt[:c["tp"].shape[0]].copy_(_bf16(dev, c["tp"]))
     rd = torch.zeros(1, dtype=torch.int64, device=dev)
     ops = {}
 

@@ -19,6 +19,7 @@ Calls (same names as the C entry points without the ``dsp_`` prefix):
   draft_rnn_step     -- greedy chain with the RNN sequential head
   tree_expand        -- PCTree expansion
   philox_uniforms    -- the counter-based uniforms the verify step draws
+  TierGraphs         -- one captured verify graph per packed-row tier, replayed by the pack's tier
 """
 import ctypes
 
@@ -29,8 +30,9 @@ from ._abi import (DSP_BF16, DSP_BF16_TOKEN_MAJOR, DSP_F32, DSP_SCHED_ARGMAX, DS
                    DSP_SCHED_TOP_M, DSP_STATUS_NONFINITE, DSP_STATUS_TIMEOUT, DSP_STATUS_TOKEN_RANGE,
                    DSP_STATUS_WINDOW_RANGE,
                    DspError, KERNELS)
+from .tiers import TierGraphs
 
-__all__ = ["PreparedCall", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection",
+__all__ = ["PreparedCall", "TierGraphs", "confidence_head", "schedule_windows", "pack_ragged", "verify_rejection",
            "verify_rejection_noalloc", "verify_calibration", "draft_markov_step", "draft_rnn_step",
            "draft_markov_sample", "tree_expand", "schedule_pack",
            "philox_uniforms", "stream_read", "set_option", "prof_enable", "prof_reset", "prof_query", "DspError", "lib",

@@ -588,10 +588,13 @@ __device__ __forceinline__ int find_request(const int32_t* cu, int R, int p) {
 constexpr int kCuLds = 2048;  // requests whose offsets are staged in LDS for the row search
 
 // Statistics pass (T > 0): every packed target row, and the draft row of every packed
-// row that is not an anchor (so windows shorter than K cost no work). One workgroup
-// item is one (row, chunk): target items first, then draft items in packed-row order.
-// A draft item finds its (request, position) in the pack's row maps when the caller
-// passes them, else by a binary search of cu_seqlens staged in LDS.
+// row that is not an anchor (so windows shorter than K cost no work). Items are numbered
+// row by row, each row's target chunks before its draft chunks, so the items of rows at
+// or past the device-side packed total form one tail: a workgroup stops at its first
+// such item, and a grid capped below the item count (the caller's max_rows may be far
+// above the packed total) costs no dispatch of idle workgroups past the cap. A draft
+// item finds its (request, position) in the pack's row maps when the caller passes
+// them, else by a binary search of cu_seqlens staged in LDS.
 template <typename TT, typename TD>
 __global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a, const int32_t* __restrict__ cu_,
                                                                  const int32_t* __restrict__ rq_,
@@ -603,24 +606,21 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a, con
   __shared__ int32_t s_cu[kCuLds + 1];
   int phase = 0;
   if (a.round_dev && blockIdx.x == 0 && threadIdx.x == 0) *a.round_dev += 1;
-  // items are numbered against max_rows, so a workgroup knows its row before cu_seqlens
-  // arrives; rows at or past the packed total are skipped. The packed total is read in
-  // each item together with the item's other metadata (one memory round trip).
-  const long items_t = (long)a.max_rows * a.ncht;
-  const long items = items_t + (long)a.max_rows * a.nchd;
+  // an item's row and chunk follow from its number alone, so its metadata loads (the
+  // packed total, the row maps) go out together, in one memory round trip
+  const int nch = a.ncht + a.nchd;
   const int max_packed = (int)min((long)a.max_rows, (long)a.R * (a.K + 1));
+  const long items = (long)max_packed * nch;
   bool staged = false;
   for (long it = blockIdx.x; it < items; it += gridDim.x) {
-    if (it < items_t) {
-      const int row = (int)(it / a.ncht), c = (int)(it % a.ncht);
-      if (row >= min(cu_[a.R], a.max_rows)) continue;  // uniform over the workgroup
+    const int row = (int)(it / nch), c = (int)(it % nch);
+    if (c < a.ncht) {
+      if (row >= cu_[a.R]) break;  // uniform over the workgroup; later items lie further on
       const TT* p = (const TT*)a.tgt + (size_t)row * a.ld_t;
-      chunk_stats<TT>(p, a.V, a.ncht, c, a.cl, a.tstats + it, sml, &phase);
+      chunk_stats<TT>(p, a.V, a.ncht, c, a.cl, a.tstats + (size_t)row * a.ncht + c, sml, &phase);
       continue;
     }
-    const long j = it - items_t;
-    const int row = (int)(j / a.nchd), c = (int)(j % a.nchd);
-    if (row >= max_packed) continue;
+    const int cd = c - a.ncht;
     if (rq_) {
       // the maps are read together with the packed total; their agreement with
       // cu_seqlens is checked while the row streams in, and a disagreeing pair falls
@@ -632,10 +632,10 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a, con
       asm volatile("" ::"v"(i), "v"(k0), "v"(tot));  // keep the three loads ahead of any branch
       const bool in_req = (i >= 0) & (i < a.R);
       const bool drafted = in_req & (k0 >= 0) & (k0 < a.K);
-      if (row >= tot) continue;
+      if (row >= tot) break;
       if (drafted) {
         const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
-        if (chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + c, sml,
+        if (chunk_stats<TD>(p, a.V, a.nchd, cd, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + cd, sml,
                             &phase, cu_ + i, row - k0 - 1))
           continue;
       } else if (in_req && k0 == -1 && cu_[i] == row) {
@@ -645,11 +645,11 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a, con
       const int k2 = row - cu_[i2] - 1;
       if (k2 < 0 || k2 >= a.K) continue;
       const TD* p = (const TD*)a.drf + (size_t)i2 * a.ld_d_r + (size_t)k2 * a.ld_d_k;
-      chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i2 * a.K + k2) * a.nchd + c, sml,
+      chunk_stats<TD>(p, a.V, a.nchd, cd, a.cl, a.dstats + ((size_t)i2 * a.K + k2) * a.nchd + cd, sml,
                       &phase);
       continue;
     }
-    if (row >= cu_[a.R]) continue;
+    if (row >= cu_[a.R]) break;
     const bool cu_lds = a.R <= kCuLds;
     if (cu_lds && !staged) {
       for (int q = threadIdx.x; q <= a.R; q += kThreads) s_cu[q] = cu_[q];
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(StatsArgs a, con
     const int k0 = row - cu[i] - 1;  // draft position - 1 (-1: the anchor row)
     if (k0 < 0 || k0 >= a.K) continue;  // uniform over the workgroup
     const TD* p = (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)k0 * a.ld_d_k;
-    chunk_stats<TD>(p, a.V, a.nchd, c, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + c, sml,
+    chunk_stats<TD>(p, a.V, a.nchd, cd, a.cl, a.dstats + ((size_t)i * a.K + k0) * a.nchd + cd, sml,
                     &phase);
   }
 }
@@ -1411,11 +1411,17 @@ VerifyLayout verify_layout(int R, int K, int V, int max_rows, int t_dtype, int d
   return L;
 }
 
-// One item per workgroup (a persistent grid looping over items measured slower: the
-// hardware's workgroup dispatch overlaps items better), capped for very large batches.
+// Workgroups of the statistics pass. Up to kStatsOneEach items, one item each: when
+// every item is live that is the fastest shape (measured: a workgroup looping over ~10
+// items costs ~8% on the 256 x 16 full-window run). Larger launches get kStatsGridCap
+// workgroups that loop: max_rows is then often far above the device-side packed total
+// (one graph captured for the largest batch), and a workgroup left without a live item
+// still costs its dispatch (~0.7 ns each: 98 us instead of 37 for 472 live rows under
+// max_rows = 4,352 at V = 151,936).
+constexpr long kStatsOneEach = 16384;
+constexpr long kStatsGridCap = 8192;
 long stats_grid(long max_items) {
-  const long cap = 1l << 20;
-  long g = max_items < cap ? max_items : cap;
+  long g = max_items <= kStatsOneEach ? max_items : kStatsGridCap;
   return g < 1 ? 1 : g;
 }
 

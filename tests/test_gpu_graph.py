@@ -192,3 +192,65 @@ def test_graph_tree_expand_replays_match_eager():
             assert torch.equal(t.outputs[k], ref[k]), (r, k)
         _unrelated_eager_work(dev)
     assert int(t.outputs["status"].item()) == 0
+
+
+def test_tier_graph_replays_match_eager():
+    """Per-tier graph replay (SGLang article, "Ragged verify"): one verify graph captured per
+    packed-row tier, chosen each step by the tier the pack wrote; every step's outputs
+    equal an eager verify of the same packing over the full row range, bit for bit.
+    48 requests x K=8, V=20,000, windows moving from short to long across the steps."""
+    dev = torch.device("cuda", 0)
+    R, K, V = 48, 8, 20000
+    c = workloads.verify_case(R, K, V, dtype="bf16", seed=77, boost_p=0.01, d_sigma=0.8)
+    rng = np.random.default_rng(78)
+    tiers = [64, 96, 160, 288, R * (K + 1)]
+    drf = logits_to_gpu(c["d"], "bf16")
+    x = to_gpu(c["x"].astype(np.int32))
+    anchors = to_gpu(np.arange(R, dtype=np.int32))
+    cost = to_gpu(1.0 + 0.05 * np.arange(R * K + 1))
+    conf = torch.zeros(R, K, dtype=torch.float32, device=dev)
+    tgt = torch.zeros(R * (K + 1), V, dtype=torch.bfloat16, device=dev)
+    rd = torch.zeros(1, dtype=torch.int64, device=dev)
+    rd_ref = torch.zeros(1, dtype=torch.int64, device=dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sch = dsp.schedule_pack(conf, cost, anchors, x, tiers=tiers, stream=s, prepare=True)
+    shared = {"status": torch.zeros(1, dtype=torch.int32, device=dev)}
+
+    def make(tier):  # every tier's call writes the same output buffers
+        v = dsp.verify_rejection(tgt, sch.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=5,
+                                 round_dev=rd, max_rows=tier, row_req=sch.outputs["row_req"],
+                                 row_pos=sch.outputs["row_pos"], out=shared, status=shared["status"],
+                                 stream=s, prepare=True)
+        shared.update({k: t for k, t in v.outputs.items() if t is not None})
+        return v
+
+    tg = dsp.TierGraphs(tiers, make, stream=s)
+    used = set()
+    for step, mu in enumerate([-1.5, 0.5, 2.5, 5.0, 0.0]):
+        c_s = (1.0 / (1.0 + np.exp(-(mu + rng.standard_normal((R, K)))))).astype(np.float32)
+        conf.copy_(to_gpu(c_s))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            sch()
+        s.synchronize()
+        win = sch.outputs["windows"].cpu().numpy()
+        T = int(win.sum()) + R
+        tgt[:T].copy_(logits_to_gpu(packed_from_dense(c["t"], win), "bf16"))
+        torch.cuda.synchronize()
+        print(f"tier step {step}: packed rows {T}", flush=True)
+        tier = tg.replay(sch.outputs["total_and_tier"])
+        assert tier == min(t for t in tiers if t >= T)
+        assert sch.outputs["total_and_tier"].cpu().tolist() == [T, tier]
+        used.add(tier)
+        s.synchronize()
+        got = {k: shared[k].clone() for k in ("accepted_len", "out_tokens", "stop_pos", "p_x", "q_x", "status")}
+        ref = dsp.verify_rejection(tgt, sch.outputs["cu_seqlens"], x, drf=drf, temperature=1.0, seed=5,
+                                   round_dev=rd_ref, row_req=sch.outputs["row_req"], row_pos=sch.outputs["row_pos"])
+        torch.cuda.synchronize()
+        for k, t in got.items():
+            assert torch.equal(t, ref[k]), (step, k)
+        assert int(got["status"].item()) == 0
+        _unrelated_eager_work(dev)
+    assert len(used) >= 3, used
+    assert int(rd.item()) == int(rd_ref.item()) == 5
