@@ -1094,17 +1094,104 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(SampleArgs a)
   }
 }
 
-// Inverse-CDF draw of request i's job, one workgroup: s_csum (LDS) holds the job's
-// weight per chunk of a.ce elements; locate the chunk holding u' * total, rescan it
-// with contiguous per-thread ranges and an fp64 exclusive scan, and let the owning
-// thread walk its range to the first element past the target.
-template <typename TT, typename TD>
+// Inverse-CDF draw of request i's job, one workgroup of NT threads: s_csum (LDS) holds
+// the job's weight per chunk; locate the chunk holding u' * total, rescan it with
+// contiguous per-thread ranges and an fp64 exclusive scan, and let the owning thread walk
+// its range to the first element past the target. A thread's range is taken in batches
+// of kDrawVecs vectors (8 elements each), one memory round trip per batch; a range of
+// one batch keeps its weights in registers for the walk, a longer one is reloaded batch
+// by batch by its owner.
+constexpr int kDrawVecs = 4;
+// The job's weights of the kDrawVecs vectors from element eb, masked to [.., r1): every
+// load issued before any is used (bounded buffer loads; a vector past the range reads
+// zeros and is masked, the row's ragged last vector takes the guarded element path).
+template <typename TT, typename TD, int NV>
+__device__ __forceinline__ void draw_batch(const JobFrame& f, const TT* tp, const TD* dp,
+                                           __amdgpu_buffer_rsrc_t trs, __amdgpu_buffer_rsrc_t drs, bool al,
+                                           int eb, int r1, float (&wv)[8 * NV]) {
+  Raw8<TT> rt[NV];
+  Raw8<TD> rd[NV];
+  bool fast[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int e = eb + 8 * v;
+    fast[v] = al && e + 8 <= r1;
+    rt[v].load_buf(trs, fast[v] ? (uint32_t)(e * sizeof(TT)) : kRowOOB);
+    rd[v].load_buf(drs, fast[v] && f.resid ? (uint32_t)(e * sizeof(TD)) : kRowOOB);
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int e = eb + 8 * v;
+    float t[8], d[8];
+    rt[v].unpack(t);
+    rd[v].unpack(d);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float wq = job_weight(f, t[q], f.resid ? d[q] : 0.f);
+      wv[8 * v + q] = fast[v] ? wq : 0.f;
+    }
+    if (!fast[v] && e < r1) {
+      float w8[8];
+      job_weights8<TT, TD>(f, tp, dp, false, false, e, r1, w8);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[8 * v + q] = w8[q];
+    }
+  }
+}
+
+// The rescan of a draw's chunk: each thread's range [r0, r1) (per elements) summed in
+// batches of NV vectors, an fp64 exclusive scan over the workgroup, and the walk of the
+// range holding tau by its owner, which records the first element past it in *found.
+template <typename TT, typename TD, int NV, int NW>
+__device__ __forceinline__ void draw_rescan(const JobFrame& f, const TT* tp, const TD* dp,
+                                            __amdgpu_buffer_rsrc_t trs, __amdgpu_buffer_rsrc_t drs, bool al,
+                                            int r0, int r1, int per, double tau, double* s_wtot, int* found) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int BE = 8 * NV;  // elements per batch
+  const int nb = (per + BE - 1) / BE;  // batches per thread (uniform)
+  float wv[BE];
+  double s = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    draw_batch<TT, TD, NV>(f, tp, dp, trs, drs, al, r0 + b * BE, r1, wv);
+#pragma unroll
+    for (int q = 0; q < BE; ++q) s += (double)wv[q];
+  }
+  double inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_wtot[w] = inc;
+  __syncthreads();
+  double off = 0.0;
+  for (int q = 0; q < w; ++q) off += s_wtot[q];
+  const double E = off + inc - s;
+  if (E <= tau && tau < E + s) {
+    // the owner walks its range again batch by batch (a single batch is still in registers)
+    double run = E;
+    int hit = -1;
+    for (int b = 0; b < nb && hit < 0; ++b) {
+      if (nb > 1) draw_batch<TT, TD, NV>(f, tp, dp, trs, drs, al, r0 + b * BE, r1, wv);
+#pragma unroll
+      for (int q = 0; q < BE; ++q) {
+        run += (double)wv[q];
+        if (hit < 0 && r0 + b * BE + q < r1 && run > tau) hit = r0 + b * BE + q;
+      }
+    }
+    if (hit >= 0) atomicMin(found, hit);
+  }
+}
+
+template <typename TT, typename TD, int NT>
 __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s_csum, const DrawChunks& dc) {
-  __shared__ double s_wtot[kSampleThreads / 64];
+  constexpr int NW = NT / 64;
+  constexpr int kGrain = NT * 8;
+  __shared__ double s_wtot[NW];
   __shared__ int s_chunk;
   __shared__ double s_tau;
   __shared__ int s_found;
-  __shared__ int s_lastp[kSampleThreads / 64];
+  __shared__ int s_lastp[NW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   bool resid = jb.mode == JOB_RESID;
   const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
@@ -1119,9 +1206,9 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
       double s0 = 0.0;
       const int c0 = dc.begin(c), c1 = dc.begin(c + 1);
       const bool t_al0 = (((uintptr_t)(tp + c0)) & 15u) == 0;
-      for (int e = c0 + tid * 8; e < c1; e += kSampleThreads * 8)
+      for (int e = c0 + tid * 8; e < c1; e += NT * 8)
         s0 += (double)job_weight8<TT, TD>(fp, tp, nullptr, t_al0, true, e, c1);
-      const double S = block_sum<kSampleThreads / 64>(s0, s_wtot);
+      const double S = block_sum<NW>(s0, s_wtot);
       __syncthreads();
       if (tid == 0) s_csum[c] = S;
       __syncthreads();
@@ -1163,82 +1250,31 @@ __device__ void sample_draw(const SampleArgs& a, int i, const Job& jb, double* s
     return;
   }
   const int e0 = dc.begin(cs), e1 = dc.begin(cs + 1);
-  // contiguous per-thread ranges, a multiple of 8 elements each (8 for the uniform chunks)
-  const int per = (e1 - e0 + kSampleGrain - 1) / kSampleGrain * 8;
+  // contiguous per-thread ranges, a multiple of 8 elements each
+  const int per = (e1 - e0 + kGrain - 1) / kGrain * 8;
   const int r0 = min(e1, e0 + tid * per), r1 = min(e1, r0 + per);
   // vector loads need 16-byte aligned ranges: the uniform chunks start at multiples of 8
   // elements; a statistics chunk of an unaligned row may not
   const bool t_al = (((uintptr_t)(tp + e0)) & 15u) == 0 && (e0 % 8) == 0;
   const bool d_al = !resid || ((((uintptr_t)dp) & 15u) == 0 && (e0 % 8) == 0);
-  // the thread's weights; with 8 elements per thread (chunks of 8192) they stay in
-  // registers for the walk below
-  // the thread's weights: up to 16 elements (chunks of at most 16384) stay in registers
-  // for the walk below
-  double s = 0.0;
-  float wv[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) wv[q] = 0.f;
-  if (per <= 16) {
-    if (r0 < r1) job_weights8<TT, TD>(f, tp, dp, t_al, d_al, r0, r1, wv);
-    if (r0 + 8 < r1) job_weights8<TT, TD>(f, tp, dp, t_al, d_al, r0 + 8, r1, wv + 8);
-    float ws = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) ws += wv[q];
-    s = (double)ws;
-  } else {
-    for (int e = r0; e < r1; e += 8) {
-      job_weights8<TT, TD>(f, tp, dp, t_al, d_al, e, r1, wv);
-      float ws = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) ws += wv[q];
-      s += (double)ws;
-    }
-  }
-  double inc = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += t;
-  }
-  if (lane == 63) s_wtot[w] = inc;
-  __syncthreads();
-  double off = 0.0;
-  for (int q = 0; q < w; ++q) off += s_wtot[q];
-  const double E = off + inc - s;
-  if (E <= tau && tau < E + s) {
-    double run = E;
-    if (per <= 16) {
-      int hit = -1;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        run += (double)wv[q];
-        if (hit < 0 && r0 + q < r1 && run > tau) hit = r0 + q;
-      }
-      if (hit >= 0) atomicMin(&s_found, hit);
-    } else {
-      for (int e = r0; e < r1; e += 8) {
-        float w8[8];
-        job_weights8<TT, TD>(f, tp, dp, t_al, d_al, e, r1, w8);
-        int hit = -1;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          run += (double)w8[q];
-          if (hit < 0 && run > tau) hit = e + q;
-        }
-        if (hit >= 0) {
-          atomicMin(&s_found, hit);
-          break;
-        }
-      }
-    }
-  }
+  // the range in batches of kDrawVecs vectors, each batch's loads issued together
+  const __amdgpu_buffer_rsrc_t trs = row_rsrc(tp, (uint32_t)((size_t)a.V * sizeof(TT)));
+  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dp, resid ? (uint32_t)((size_t)a.V * sizeof(TD)) : 0u);
+  // batches as long as the range, up to kDrawVecs vectors (unused vectors measured
+  // slower on short ranges)
+  const int nv = min(kDrawVecs, max(1, per / 8));  // uniform
+  const bool al = t_al && d_al;
+  if (nv == 1) draw_rescan<TT, TD, 1, NW>(f, tp, dp, trs, drs, al, r0, r1, per, tau, s_wtot, &s_found);
+  else if (nv == 2) draw_rescan<TT, TD, 2, NW>(f, tp, dp, trs, drs, al, r0, r1, per, tau, s_wtot, &s_found);
+  else if (nv == 3) draw_rescan<TT, TD, 3, NW>(f, tp, dp, trs, drs, al, r0, r1, per, tau, s_wtot, &s_found);
+  else draw_rescan<TT, TD, 4, NW>(f, tp, dp, trs, drs, al, r0, r1, per, tau, s_wtot, &s_found);
   __syncthreads();
   if (s_found == 0x7fffffff) {
     // rounding put the target past the rescanned total: last token with weight in the chunk
     int last_pos = -1;
     for (int e = r1 - 1; e >= r0 && last_pos < 0; --e)
       if (job_weight(f, Elem<TT>::val(tp, e), resid ? Elem<TD>::val(dp, e) : 0.f) > 0.f) last_pos = e;
-    const int lp = block_max<kSampleThreads / 64>(last_pos, s_lastp);
+    const int lp = block_max<NW>(last_pos, s_lastp);
     if (tid == 0) s_found = lp;
     __syncthreads();
   }
@@ -1258,132 +1294,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample_kernel(SampleArg
   }
   __syncthreads();
   const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
-  sample_draw<TT, TD>(a, i, jb, s_csum, st ? stats_chunks<TT>(a, tp) : uniform_chunks(a));
-}
-
-// Decisions, residual / bonus mass and the draw of one request in one workgroup of
-// kSampleThreads: the first wavefront decides (accepted prefix, outputs, the job of
-// the draw); all waves then stream the job's row(s) once -- a 16-byte vector of each
-// row per thread per block of kSampleGrain elements, kFinBatch blocks (half for fp32) of loads in
-// flight -- adding each thread's weights per chunk of a.ce elements (a multiple of
-// the block, so blocks never straddle chunks); a wavefront sum per chunk goes to LDS,
-// and the draw proceeds from those chunk masses. No other workgroup is involved, so
-// the request needs no hand-off through memory.
-constexpr int kFinBatch = 4;
-template <typename TT, typename TD>
-__global__ __launch_bounds__(kSampleThreads) void verify_finish_kernel(DecideArgs da, SampleArgs a) {
-  __shared__ Job s_job;
-  __shared__ double s_part[64][kSampleThreads / 64];
-  __shared__ double s_csum[64];
-  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid < 64) {
-    const int base = da.cu[i], end = da.cu[i + 1];
-    const int n = end - base - 1;
-    if (n < 0 || n > da.K || base < 0 || end > da.max_rows) {
-      fault_request(da, i, DSP_STATUS_WINDOW_RANGE);
-      if (tid == 0) s_job.mode = JOB_NONE;
-    } else {
-      decide_sampled<TT, TD>(da, i, &s_job);
-    }
-  }
-  __syncthreads();
-  const Job jb = s_job;
-  if (jb.mode == JOB_NONE) return;  // uniform over the workgroup
-  const TT* tp = (const TT*)a.tgt + (size_t)jb.trow * a.ld_t;
-  if (bonus_from_stats(jb, a)) {  // uniform: the masses are known, no pass over the row
-    if (tid < 64) bonus_masses(a, jb, s_csum);
-    __syncthreads();
-    sample_draw<TT, TD>(a, i, jb, s_csum, stats_chunks<TT>(a, tp));
-    return;
-  }
-  const bool resid = jb.mode == JOB_RESID;
-  const JobFrame f = job_frame(jb, a.cl, resid);
-  const TD* dp = resid ? (const TD*)a.drf + (size_t)i * a.ld_d_r + (size_t)jb.drow * a.ld_d_k : nullptr;
-  const bool al = (((uintptr_t)tp) & 15u) == 0 && (!resid || (((uintptr_t)dp) & 15u) == 0);
-  const int nblk = (a.V + kSampleGrain - 1) / kSampleGrain;
-  const int bpc = a.ce / kSampleGrain;  // blocks per chunk
-  double run = 0.0;
-  // batches of FB blocks, every load of a batch issued before any is used (double
-  // buffering the batches measured no faster)
-  constexpr int FB = (sizeof(TT) == 2 && sizeof(TD) == 2) ? kFinBatch : kFinBatch / 2;  // fp32: twice the bytes
-  Raw8<TT> rt[FB];
-  Raw8<TD> rd[FB];
-  bool fast[FB];
-  const __amdgpu_buffer_rsrc_t trs = row_rsrc(tp, (uint32_t)((size_t)a.V * sizeof(TT)));
-  const __amdgpu_buffer_rsrc_t drs = row_rsrc(dp, resid ? (uint32_t)((size_t)a.V * sizeof(TD)) : 0u);
-  auto issue = [&](int j0) {
-#pragma unroll
-    for (int b = 0; b < FB; ++b) {
-      const int e = (j0 + b) * kSampleGrain + tid * 8;
-      fast[b] = al && e + 8 <= a.V;
-      rt[b].load_buf(trs, fast[b] ? (uint32_t)(e * sizeof(TT)) : kRowOOB);
-      rd[b].load_buf(drs, fast[b] && resid ? (uint32_t)(e * sizeof(TD)) : kRowOOB);
-    }
-  };
-  auto weigh = [&](int j0) {
-#pragma unroll
-    for (int b = 0; b < FB; ++b) {
-      const int j = j0 + b;
-      if (j >= nblk) break;  // uniform
-      const int e = j * kSampleGrain + tid * 8;
-      // unconditional fast-path weights, selected after (see job_chunk_sum)
-      float t[8], d[8];
-      rt[b].unpack(t);
-      rd[b].unpack(d);
-      float wf = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) wf += job_weight(f, t[q], resid ? d[q] : 0.f);
-      float wsum = fast[b] ? wf : 0.f;
-      if (!fast[b] && e < a.V) wsum = job_weight8<TT, TD>(f, tp, dp, false, false, e, a.V);
-      run += (double)wsum;
-      if ((j + 1) % bpc == 0 || j + 1 == nblk) {  // the chunk ends with this block (uniform)
-        double s = run;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) s_part[j / bpc][w] = s;
-        run = 0.0;
-      }
-    }
-  };
-  for (int j0 = 0; j0 < nblk; j0 += FB) {
-    issue(j0);
-    weigh(j0);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    double c = 0.0;
-    if (tid < a.nch2)
-#pragma unroll
-      for (int q = 0; q < kSampleThreads / 64; ++q) c += s_part[tid][q];
-    s_csum[tid] = c;
-  }
-  __syncthreads();
-  sample_draw<TT, TD>(a, i, jb, s_csum, uniform_chunks(a));
-}
-
-int g_cus = 0;
-int num_cus() {
-  if (g_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_cus = n;
-    else
-      g_cus = 256;
-  }
-  return g_cus;
-}
-
-// Chunking of the one-workgroup finish: at most 64 chunks of a multiple of kSampleGrain.
-__host__ __device__ inline SampleGeom finish_geom(int V) {
-  int n = (V + kSampleGrain - 1) / kSampleGrain;
-  if (n > 64) n = 64;
-  int ce = (V + n - 1) / n;
-  ce = (ce + kSampleGrain - 1) / kSampleGrain * kSampleGrain;
-  SampleGeom g;
-  g.ce = ce;
-  g.nch2 = (V + ce - 1) / ce;
-  return g;
+  sample_draw<TT, TD, kSampleThreads>(a, i, jb, s_csum, st ? stats_chunks<TT>(a, tp) : uniform_chunks(a));
 }
 
 struct VerifyLayout {
@@ -1428,30 +1339,20 @@ long stats_grid(long max_items) {
 template <typename TT, typename TD>
 void launch_sampled(const StatsArgs& sa, const DecideArgs& da, const SampleArgs& pa, hipStream_t s,
                     long max_items) {
-  const int cus = num_cus();
   const long g = stats_grid(max_items);
   launch(DSP_K_VERIFY_STATS, verify_stats_kernel<TT, TD>, dim3((unsigned)g), dim3(kThreads), 0, s, sa, sa.cu,
          sa.row_req, sa.row_pos);
-  if (4l * pa.R >= 3l * cus && pa.ncht > 64) {
-    // enough requests to give nearly every CU one: decide, stream and draw each request
-    // in its own workgroup (no hand-off between launches)
-    SampleArgs fa = pa;
-    const SampleGeom fg = finish_geom(pa.V);
-    fa.nch2 = fg.nch2;
-    fa.ce = fg.ce;
-    launch(DSP_K_VERIFY_SAMPLE, verify_finish_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, da, fa);
-  } else {
-    // few requests: one CU per request would leave most of the chip idle on the residual
-    // rows (two exponentials per element), so the rows are spread over every CU
-    launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
-    // one workgroup per (request, chunk) item: most items belong to bonus jobs (masses from
-    // the statistics pass) and exit at once, so a grid-stride loop would only chain their
-    // job loads one after another
-    const long ri = (long)pa.R * pa.nch2;
-    const long g2 = ri < (1l << 20) ? ri : (1l << 20);
-    launch(DSP_K_VERIFY_RESIDUAL, verify_residual_kernel<TT, TD>, dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
-    launch(DSP_K_VERIFY_SAMPLE, verify_sample_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
-  }
+  // decisions, then the residual / bonus masses spread over every CU (one workgroup per
+  // (request, chunk) item: most items belong to bonus jobs, whose masses the statistics
+  // pass holds, and exit at once, so a grid-stride loop would only chain their job loads
+  // one after another), then one draw per request. (One workgroup per request doing all
+  // three measured slower even with a request for nearly every CU: 36.6 against 31 us at
+  // 256 requests, V = 151,936.)
+  launch(DSP_K_VERIFY_DECIDE, verify_decide_kernel<TT, TD>, dim3(da.R), dim3(64), 0, s, da, (Job*)pa.jobs);
+  const long ri = (long)pa.R * pa.nch2;
+  const long g2 = ri < (1l << 20) ? ri : (1l << 20);
+  launch(DSP_K_VERIFY_RESIDUAL, verify_residual_kernel<TT, TD>, dim3((unsigned)g2), dim3(kThreads), 0, s, pa);
+  launch(DSP_K_VERIFY_SAMPLE, verify_sample_kernel<TT, TD>, dim3(pa.R), dim3(kSampleThreads), 0, s, pa);
 }
 
 template <typename TT>
