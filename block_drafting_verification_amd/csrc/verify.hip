@@ -712,45 +712,6 @@ __global__ __launch_bounds__(64) void verify_decide_greedy(DecideArgs a) {
   }
 }
 
-// Greedy walk of a draft tree; lane j holds node j.
-__global__ __launch_bounds__(64) void verify_decide_tree(DecideArgs a) {
-  const int i = blockIdx.x, lane = threadIdx.x;
-  const int base = a.cu[i], end = a.cu[i + 1];
-  const int nn = end - base - 1;
-  if (nn < 0 || nn > a.K || base < 0 || end > a.max_rows) {
-    fault_request(a, i, DSP_STATUS_WINDOW_RANGE);
-    return;
-  }
-  int tok = -1, par = -2;
-  if (lane < nn) {
-    tok = a.x[(size_t)i * a.ld_x + lane];
-    par = a.parent[(size_t)i * a.ld_x + lane];
-  }
-  if (__ballot(lane < nn && (tok < 0 || tok >= a.V))) {
-    fault_request(a, i, DSP_STATUS_TOKEN_RANGE);
-    return;
-  }
-  int32_t* orow = a.out + (size_t)i * (a.K + 1);
-  int cur = -1, depth = 0;
-  int am = 0;
-  while (true) {
-    am = (int)merge_argmax(a.tstats + (size_t)(base + 1 + cur) * a.ncht, a.ncht);
-    const uint64_t m = __ballot(lane < nn && par == cur && tok == am);
-    if (!m || depth >= a.K) break;
-    const int j = __ffsll((unsigned long long)m) - 1;
-    const int tj = __shfl(tok, j, 64);
-    if (lane == 0) orow[depth] = tj;
-    cur = j;
-    ++depth;
-  }
-  for (int j = depth + 1 + lane; j <= a.K; j += 64) orow[j] = -1;
-  if (lane == 0) {
-    orow[depth] = am;
-    a.acc_len[i] = depth;
-    a.stop[i] = cur;
-  }
-}
-
 // Greedy tree walk, one workgroup of kWalkThreads per request: from the root, the
 // arg-max of the current node's target row (largest value, lowest token id) selects
 // the child carrying that token, until no child does. Only the rows on the walked
@@ -1368,7 +1329,7 @@ void launch_greedy(const StatsArgs& sa, const DecideArgs& da, hipStream_t s, lon
   }
   const long g = stats_grid(max_items);
   launch(DSP_K_VERIFY_STATS, verify_argmax_kernel<TT>, dim3((unsigned)g), dim3(kThreads), 0, s, sa);
-  launch(DSP_K_VERIFY_DECIDE, tree ? verify_decide_tree : verify_decide_greedy, dim3(da.R), dim3(64), 0, s,
+  launch(DSP_K_VERIFY_DECIDE, verify_decide_greedy, dim3(da.R), dim3(64), 0, s,
          da);
 }
 
