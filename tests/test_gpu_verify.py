@@ -337,6 +337,38 @@ def test_scheduled_ragged_verify_full():
     ties.check()
 
 
+def test_scheduled_verify_captured_at_full_size():
+    """The same scheduled batch verified with max_rows = R x (K+1) = 4,352 rows while only the
+    packed rows at the front are live (one graph captured for the largest batch): past 16,384
+    items the statistics pass runs a capped grid of workgroups that loop over the items and
+    stop at the device-side packed total. Outputs must equal the exact-size call bit for bit,
+    with the pack's row maps and with the binary search of cu_seqlens."""
+    c = workloads.scheduled_verify()
+    R, K, V = c["R"], c["K"], c["V"]
+    sch = dsp.schedule_windows(to_gpu(c["conf"]), to_gpu(c["cost"]))
+    xg = to_gpu(c["x"].astype(np.int32))
+    pk = dsp.pack_ragged(sch["windows"], to_gpu(c["anchors"]), xg)
+    w = host(sch["windows"])
+    tp = packed_from_dense(c["t"], w)
+    T = tp.shape[0]
+    full = R * (K + 1)
+    tg_exact = logits_to_gpu(tp, "bf16")
+    tg_full = torch.zeros(full, V, dtype=torch.bfloat16, device=tg_exact.device)
+    tg_full[:T].copy_(tg_exact)
+    dg = logits_to_gpu(c["d"], "bf16")
+    print(f"full-size capture: packed rows {T} of {full}, items {full * 20}", flush=True)
+    keys = ("accepted_len", "out_tokens", "stop_pos", "p_x", "q_x")
+    for maps in (True, False):
+        extra = dict(row_req=pk["row_req"], row_pos=pk["row_pos"]) if maps else {}
+        ref = dsp.verify_rejection(tg_exact, pk["cu_seqlens"], xg, drf=dg, temperature=1.0, seed=0, round=5, **extra)
+        got = dsp.verify_rejection(tg_full, pk["cu_seqlens"], xg, drf=dg, temperature=1.0, seed=0, round=5,
+                                   max_rows=full, **extra)
+        torch.cuda.synchronize()
+        assert int(host(got["status"])[0]) == 0 and int(host(ref["status"])[0]) == 0
+        for k in keys:
+            assert torch.equal(got[k], ref[k]), (maps, k)
+
+
 def test_masked_vocabulary_entries():
     """Rows with -inf entries (a masked or padded vocabulary, same mask for target and draft):
     the masked tokens carry no probability mass on either side and are never drawn."""
