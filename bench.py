@@ -45,7 +45,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-FLUSH_BYTES = 512 << 20     # store pass between timed steps (2x the Infinity Cache)
+FLUSH_BYTES = 512 << 20     # cache flush between timed steps (2x the Infinity Cache)
+
+
+def flush_caches(scratch, i):
+    """Outside the timed interval: a plain store pass over a buffer twice the Infinity
+    Cache's size evicts what the step left there, then a read pass over the same buffer
+    writes the store pass's dirty lines back, so the next step starts from cold caches
+    holding clean lines only (otherwise the step's first kernels pay for writing back up
+    to the whole cache of the flush's own data)."""
+    scratch.fill_(i + 1)  # elementwise store kernel (nonzero: no memset path)
+    scratch.sum()         # reduction: reads the buffer
 MAX_CPU_WORKERS = 16        # host cores given to one GPU
 
 
@@ -158,7 +168,7 @@ def run_phases(make_step, steps, warmup, dominant, do_flush=True):
 
     def flush(i):
         if do_flush:
-            scratch.fill_(i + 1)  # a plain elementwise store kernel (nonzero: no memset path)
+            flush_caches(scratch, i)
 
     def timed(body):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -209,7 +219,8 @@ def timing_record(ph, steps):
                          eager_ms_per_step=1000.0 * ph["eager_s"] / steps,
                          warm_graph_ms_per_step=1000.0 * ph["warm_graph_s"] / steps,
                          value_from="graph" if ph["graph_s"] <= ph["eager_s"] else "eager",
-                         cache_flush=f"{FLUSH_BYTES >> 20} MiB store pass before each timed step")
+                         cache_flush=f"{FLUSH_BYTES >> 20} MiB store pass, then a read pass over it, before each "
+                                     "timed step")
 
 
 def hbm_roofline(kernel, algo_bytes, avg_us, traffic):
@@ -432,7 +443,7 @@ def bench_tiering(args, c, dev, tgt, drf, x, conf, cost, anchors):
         tier = None
         for i, (a, b) in enumerate(ev):
             if not args.no_flush:
-                scratch.fill_(i + 1)
+                flush_caches(scratch, i)
             a.record(s)
             g_sch.replay()
             tier = tg.replay(tt)
