@@ -64,8 +64,8 @@ def _replay_matches_eager(make_step, ops, keys, rd, dev):
 
 
 def test_graph_cycle_replays_match_eager():
-    """Sampled draft -> confidence head -> schedule -> pack -> verify, 256 requests x 16
-    (the one-workgroup-per-request decision and draw), V=30,011."""
+    """Sampled draft -> confidence head -> schedule -> pack -> verify, 256 requests x 16,
+    V=30,011."""
     dev = torch.device("cuda", 0)
     c = workloads.cycle_case(256, 16, 30011, 64, seed=2024)
     L, U = to_gpu_bf16(c["L"]), to_gpu_bf16(c["U"])

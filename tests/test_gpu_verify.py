@@ -311,8 +311,7 @@ def test_cap_accept(T, dt, V):
 
 def test_scheduled_ragged_verify_full():
     """The confidence-scheduled ragged verify workload: 256 requests x K=16, V=151,936 bf16;
-    scheduler -> pack -> compact verify on the GPU, every request checked against the oracle
-    (256 requests take the one-workgroup-per-request decision and draw)."""
+    scheduler -> pack -> compact verify on the GPU, every request checked against the oracle."""
     c = workloads.scheduled_verify()
     R, K, V = c["R"], c["K"], c["V"]
     sch = dsp.schedule_windows(to_gpu(c["conf"]), to_gpu(c["cost"]))
