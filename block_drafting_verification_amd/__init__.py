@@ -544,9 +544,13 @@ def stream_read(t, sink=None, stream=None):
 
 def set_option(option, value):
     """Set a library option: "chain_persistent" (1 = the greedy chain may run all steps in
-    one persistent launch, 0 = one launch per step, the default) or "spin_limit" (polls of a
-    persistent launch's grid barrier before it gives up with DSP_STATUS_TIMEOUT)."""
-    code = {"chain_persistent": _abi.DSP_OPT_CHAIN_PERSISTENT, "spin_limit": _abi.DSP_OPT_SPIN_LIMIT}[option]
+    one persistent launch, 0 = one launch per step, the default), "spin_limit" (polls of a
+    persistent launch's grid barrier before it gives up with DSP_STATUS_TIMEOUT) or
+    "tree_split" (1 = the tree's GEMM runs its depths whose row blocks span at most 16
+    requests on the kernel with direct-to-LDS stages and a fixed issue order, the default;
+    0 = the general GEMM everywhere; outputs are bit-identical)."""
+    code = {"chain_persistent": _abi.DSP_OPT_CHAIN_PERSISTENT, "spin_limit": _abi.DSP_OPT_SPIN_LIMIT,
+            "tree_split": _abi.DSP_OPT_TREE_SPLIT}[option]
     _abi.check(lib().dsp_set_option(code, int(value)))
 
 

@@ -215,6 +215,81 @@ __device__ __forceinline__ void merge_top4(float* va, int* ia, const float* vb, 
   }
 }
 
+// Tree epilogue of one stage for this lane's parent row: z holds 16 tokens of the row
+// (value q is token v0 + 8*(q>>2) + 4*(lane>>5) + (q&3)), tm is their maximum and ts the
+// sum of exp2(z log2e - lref) against the reference of the stages before. The reference
+// is raised only when the stage could exceed it by more than 2^64 (each term stays finite
+// in fp32), which recomputes the stage's sum (always on a lane's first non-empty stage).
+// Then the top-4 insertion, skipped unless the stage has an entry above the threshold
+// thr = max(4th kept value, row bound th_row). Split in two: the branch-free part that
+// adds the stage's sum (returns whether it did), and the rest.
+__device__ __forceinline__ bool tree_stage_sum(float tm, float ts, float lref, double& lsum) {
+  // the sum is selected, not branched on, so that the exponentials stay between the
+  // MFMAs (a branch lets the compiler sink them past the whole stage)
+  const bool fast = lref != -INFINITY && tm * kLog2e <= lref + 64.f;
+  lsum += fast ? (double)ts : 0.0;
+  return fast;
+}
+__device__ __forceinline__ void tree_stage_rest(bool fast, int v0, int lane, const f32x16& z, float tm, float& lref,
+                                                double& lsum, float (&tv)[kTopK], int (&ti)[kTopK], float& thr,
+                                                float th_row) {
+  if (!fast && tm != -INFINITY) {
+    const float nref = fmaxf(lref, tm * kLog2e);
+    float t2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t2 += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));
+    const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
+    lsum = lsum * scale + (double)t2;
+    lref = nref;
+  }
+  if (tm > thr) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (z[q] > thr) {
+        tv[kTopK - 1] = z[q];
+        ti[kTopK - 1] = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+#pragma unroll
+        for (int p2 = kTopK - 1; p2 > 0; --p2) {
+          if (tv[p2] > tv[p2 - 1]) {
+            const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
+            const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
+          }
+        }
+        thr = fmaxf(tv[kTopK - 1], th_row);
+      }
+    }
+  }
+}
+__device__ __forceinline__ void tree_stage_end(int v0, int lane, const f32x16& z, float tm, float ts, float& lref,
+                                               double& lsum, float (&tv)[kTopK], int (&ti)[kTopK], float& thr,
+                                               float th_row) {
+  const bool fast = tree_stage_sum(tm, ts, lref, lsum);
+  tree_stage_rest(fast, v0, lane, z, tm, lref, lsum, tv, ti, thr, th_row);
+}
+
+// Lanes l and l ^ 32 hold the same parent row: merge their top-4 lists, and their
+// log-sum-exp pairs (reference, sum) on a common reference.
+__device__ __forceinline__ void merge_pair_top4(float (&tv)[kTopK], int (&ti)[kTopK]) {
+  float ov[kTopK];
+  int oi[kTopK];
+#pragma unroll
+  for (int q = 0; q < kTopK; ++q) {
+    ov[q] = __shfl_xor(tv[q], 32, 64);
+    oi[q] = __shfl_xor(ti[q], 32, 64);
+  }
+  merge_top4(tv, ti, ov, oi);
+}
+__device__ __forceinline__ void merge_pair_lse(float& lref, double& lsum) {
+  const float oref = __shfl_xor(lref, 32, 64);
+  const double osum = __shfl_xor(lsum, 32, 64);
+  const float nref = fmaxf(lref, oref);
+  double s = 0.0;
+  if (lref != -INFINITY) s += lsum * exp2((double)lref - (double)nref);
+  if (oref != -INFINITY) s += osum * exp2((double)oref - (double)nref);
+  lref = nref;
+  lsum = s;
+}
+
 template <int MODE, int KS, bool LAL, bool LTM = false>
 __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   constexpr int NV = 2 * KS;                  // 16-byte vectors per staged Wt row (rank padded to 16*KS)
@@ -571,43 +646,10 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
   };
 
   // Tree: the stage maximum tm and ts = sum of exp2(z log2e - lref) are accumulated one
-  // value per MFMA of the next stage, against the reference of the stages before; the
-  // reference is raised only when the stage could exceed it by more than 2^64 (each term
-  // stays finite in fp32), which recomputes the stage's sum (always on a lane's first
-  // non-empty stage). Then the top-4 insertion, skipped unless the stage has an entry
-  // above the threshold.
-  auto tree_stage_end = [&](int s, const f32x16& z, float tm, float ts) {
-    const int v0 = (s_begin + s) * kTS;
-    // the fast path's sum is selected, not branched on, so that the exponentials stay
-    // between the MFMAs (a branch lets the compiler sink them past the whole stage)
-    const bool fast = lref != -INFINITY && tm * kLog2e <= lref + 64.f;
-    lsum += fast ? (double)ts : 0.0;
-    if (!fast && tm != -INFINITY) {
-      const float nref = fmaxf(lref, tm * kLog2e);
-      float t2 = 0.f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) t2 += fast_exp2(__builtin_fmaf(z[q], kLog2e, -nref));
-      const double scale = lref == -INFINITY ? 0.0 : (double)fast_exp2(lref - nref);
-      lsum = lsum * scale + (double)t2;
-      lref = nref;
-    }
-    if (tm > thr) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (z[q] > thr) {
-          tv[kTopK - 1] = z[q];
-          ti[kTopK - 1] = v0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-#pragma unroll
-          for (int p2 = kTopK - 1; p2 > 0; --p2) {
-            if (tv[p2] > tv[p2 - 1]) {
-              const float fv = tv[p2]; tv[p2] = tv[p2 - 1]; tv[p2 - 1] = fv;
-              const int iv = ti[p2]; ti[p2] = ti[p2 - 1]; ti[p2 - 1] = iv;
-            }
-          }
-          thr = fmaxf(tv[kTopK - 1], th_row);
-        }
-      }
-    }
+  // value per MFMA of the next stage, against the reference of the stages before; then
+  // the stage's end (reference update, top-4 insertion).
+  auto tree_stage_end_s = [&](int s, const f32x16& z, float tm, float ts) {
+    tree_stage_end((s_begin + s) * kTS, lane, z, tm, ts, lref, lsum, tv, ti, thr, th_row);
   };
 
   // Stages are software-pipelined inside each wave: the MFMAs of stage s are issued
@@ -686,7 +728,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         }
         // s = 0: the stage before is the -inf sentinel, which changes nothing (its sum is
         // not selected, its maximum is -inf)
-        tree_stage_end(s - 1, acc[b ^ 1], tm, ts);
+        tree_stage_end_s(s - 1, acc[b ^ 1], tm, ts);
       } else if (MODE == MODE_ARGMAX) {
 #pragma unroll
         for (int q = KS; q < 16; ++q)  // ranks below 256: the remaining values
@@ -721,7 +763,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
         tm = fmaxf(tm, last[q]);
         ts += fast_exp2(__builtin_fmaf(last[q], kLog2e, -lref));
       }
-      tree_stage_end(nst - 1, last, tm, ts);
+      tree_stage_end_s(nst - 1, last, tm, ts);
     } else {
       epilogue(nst - 1, last);
     }
@@ -737,14 +779,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
 
   // merge lane pairs (lane, lane ^ 32 hold the same parent row), then lanes < 32 write
   if (MODE == MODE_TREE) {
-    float ov[kTopK];
-    int oi[kTopK];
-#pragma unroll
-    for (int q = 0; q < kTopK; ++q) {
-      ov[q] = __shfl_xor(tv[q], 32, 64);
-      oi[q] = __shfl_xor(ti[q], 32, 64);
-    }
-    merge_top4(tv, ti, ov, oi);
+    merge_pair_top4(tv, ti);
   } else {
     const float ob = __shfl_xor(best, 32, 64);
     const int oi = __shfl_xor(bidx, 32, 64);
@@ -753,16 +788,7 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
       bidx = oi;
     }
   }
-  if (MODE != MODE_ARGMAX) {
-    const float oref = __shfl_xor(lref, 32, 64);
-    const double osum = __shfl_xor(lsum, 32, 64);
-    const float nref = fmaxf(lref, oref);
-    double s = 0.0;
-    if (lref != -INFINITY) s += lsum * exp2((double)lref - (double)nref);
-    if (oref != -INFINITY) s += osum * exp2((double)oref - (double)nref);
-    lref = nref;
-    lsum = s;
-  }
+  if (MODE != MODE_ARGMAX) merge_pair_lse(lref, lsum);
   if (lane >= 32 || !rvalid) return;
   if (MODE == MODE_TREE) {
     TreePart p;
@@ -783,6 +809,300 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
     p.sum = MODE == MODE_ARGMAX ? 0.0 : lsum;
     ((ChainPart*)a.part)[(size_t)row * a.G + g] = p;
   }
+}
+
+// ---------------------------------------------------------------- tree GEMM, scheduled stages
+// The tree's GEMM for row blocks spanning at most 16 requests (the PCTree's depths with
+// a full frontier), at rank up to 256. Same workgroup shape, vocabulary slices, XCD
+// grouping, partial results and arithmetic as markov_gemm_kernel's tree mode, with the
+// base logits entering as the first k-step (A = the stage's 32 tokens x 16 requests of
+// L, B = each row's one-hot request) and the k-steps summed in the same order, so z and
+// every output are bit-identical to it. What differs is how a stage is issued:
+//  - Wt stages go straight from memory into LDS (buffer loads with the lds modifier,
+//    issued from inline assembly so that no compiler-inserted wait drains them), six
+//    stage slots with three stages in flight; the L tile takes one 2-byte entry per
+//    thread through a register and is transposed into LDS a stage ahead of its use.
+//    No register ring holds Wt, which leaves room for
+//  - a fixed issue order per stage (scheduling barriers): Wt fragments read three
+//    k-steps ahead of their MFMA, the previous stage's exp2 sums and maximum placed
+//    between the MFMAs so they run while the matrix cores work, the stage's sum added
+//    before the last MFMAs, and the next stages' loads spread over the k-steps instead
+//    of issued by every wave at once after the barrier.
+// A direct-to-LDS load of 16 bytes writes lane l's data at M0 + 16*l, so the swizzled
+// tile layout is made by choosing each lane's source address: slot t of a stage holds
+// token row m = t / NV, swizzled vector p = t % NV, i.e. rank vector kv = swz(m, p)
+// (the swizzle is an XOR, its own inverse).
+__device__ __forceinline__ void dma_load_x4(uint32_t lds_addr, const s32x4& d, uint32_t off) {
+  // s_nop 4: M0 is read by the load one instruction after it is written, and the
+  // descriptor may come from a VALU write of an SGPR (5 wait states)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(off),
+               "s"(d)
+               : "memory");
+}
+
+template <int KS>
+__global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
+  static_assert(KS >= 2 && KS <= 16 && (KS & (KS - 1)) == 0, "rank up to 256");
+  constexpr int NV = 2 * KS;                          // 16-byte vectors per staged Wt row
+  constexpr int WST = kTS * NV;                       // Wt vectors per stage
+  constexpr int WSLOT = WST > kGT ? WST : kGT;        // LDS vectors per stage slot
+  constexpr int WD = WSLOT / kGT;                     // direct-to-LDS loads per thread per stage
+  constexpr int NR = 3;                               // stages in flight
+  constexpr int NWS = 6;                              // Wt stage slots (stage s in slot s % 6: static per unrolled
+                                                      // stage; the slot refilled, s + 3's, was read at stage s - 3)
+  constexpr int LPS = WD + 1;                         // loads per stage per thread (Wt, one L entry)
+  constexpr int LTV = kTS * 16 * 2 / 16;              // L tile vectors (32 tokens x 16 requests, bf16)
+  extern __shared__ u32x4 lds[];                      // [NWS][WSLOT] Wt slots, then [2][LTV] L tiles
+  static_assert(NWS == 6, "the stage loop unrolls six stages");
+  u32x4* const wbuf = lds;
+  u32x4* const ltbuf = lds + NWS * WSLOT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  int g, rb;
+  {
+    const int id = blockIdx.x;
+    if (a.xcd_map) {
+      const int j = id >> 3;
+      g = (j / a.nrb) * 8 + (id & 7);
+      rb = j % a.nrb;
+    } else {
+      g = id % a.G;
+      rb = id / a.G;
+    }
+  }
+  const int r0 = rb * kTR;
+  const int nst_all = (a.V + kTS - 1) / kTS;
+  const int s_begin = (int)(((long)g * nst_all) / a.G);
+  const int nst = (int)(((long)(g + 1) * nst_all) / a.G) - s_begin;
+
+  const int nloc = wave * 32 + (lane & 31);
+  const int row = r0 + nloc;
+  const bool rvalid = row < a.rows;
+  const bool all_rows = r0 + kTR <= a.rows;
+  int tok = 0;
+  if (rvalid) {
+    tok = a.row_tok[(size_t)row * a.ld_tok];
+    if (tok < 0 || tok >= (a.u_rows > 0 ? a.u_rows : a.V)) {
+      if (g == 0 && lane < 32) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+      tok = 0;
+    }
+  }
+  u32x4 ufr[KS] = {};
+  u32x4 onehot = {0u, 0u, 0u, 0u};
+  if (rvalid) {
+    const int j = row / a.rows_per_req - r0 / a.rows_per_req - 8 * (lane >> 5);
+    if (j >= 0 && j < 8) onehot[j >> 1] = 0x3f80u << (16 * (j & 1));
+  }
+
+  const s32x4 wdesc = make_desc(a.Wt, (uint32_t)((size_t)a.V * a.rank * 2));
+  const int req0 = r0 / a.rows_per_req;
+  const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
+  const int nreq = rlast / a.rows_per_req - req0 + 1;  // at most 16 (checked on the host)
+  const s32x4 ldesc = make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
+                                (uint32_t)(((size_t)(nreq - 1) * a.ldL_r + a.V) * 2));
+  // this thread's Wt source offsets (less the stage term) and LDS destinations
+  uint32_t wofs[WD];
+#pragma unroll
+  for (int q = 0; q < WD; ++q) {
+    const int t = q * kGT + tid;
+    const int m = t / NV, p = t % NV;
+    constexpr int W = NV < 16 ? NV : 16, RW = 16 / W;
+    const int kv = (p & ~(W - 1)) | ((p ^ (m / RW)) & (W - 1));
+    wofs[q] = t < WST && kv * 8 < a.rank ? (uint32_t)((m * a.rank + kv * 8) * 2) : kOOB;
+  }
+  const uint32_t lds_w = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)wbuf;
+  // L: one entry per thread, token tid % 32 of request tid / 32 of the block (zero past
+  // the block's requests; a token past V reads another row or zero and is masked at use)
+  const int lj = tid >> 5, lt = tid & 31;
+  const uint32_t lofs = lj < nreq ? (uint32_t)(((size_t)lj * a.ldL_r + lt) * 2) : kOOB;
+
+  auto load_stage = [&](int s, uint32_t& rl) {
+    const bool live = s < nst;
+    const uint32_t tw = live ? (uint32_t)((size_t)(s_begin + s) * kTS * a.rank * 2) : kOOB;
+    const uint32_t tl = live ? (uint32_t)((size_t)(s_begin + s) * kTS * 2) : kOOB;
+    const uint32_t slot = lds_w + (uint32_t)((s % NWS) * WSLOT * 16);
+    buf_load_u16<true>(rl, ldesc, lofs + tl);  // first: the wait one stage earlier covers it
+#pragma unroll
+    for (int q = 0; q < WD; ++q)
+      dma_load_x4(__builtin_amdgcn_readfirstlane(slot + (uint32_t)((q * kGT + wave * 64) * 16)), wdesc, wofs[q] + tw);
+  };
+  // the L tile, transposed: token t of request j at Lt[t * 16 + j], one entry per thread;
+  // every request column is written (zeros past the block's requests). A non-finite
+  // entry is staged as -max (a zero weight times an infinity would make NaN in every
+  // other request's sum): for a masked -inf that ranks and weighs the same; +inf and NaN
+  // are faults, noted here and reported once at the end (no branch in the stage loop).
+  bool lfault = false;
+  auto store_lt = [&](int b, uint32_t w) {
+    const uint32_t h = w & 0xffffu;
+    const bool nonfinite = (h & 0x7f80u) == 0x7f80u;
+    lfault |= nonfinite & ((h & 0x807fu) != 0x8000u);  // +inf or NaN
+    ((uint16_t*)(ltbuf + b * LTV))[lt * 16 + lj] = (uint16_t)(nonfinite ? 0xff7fu : h);
+  };
+
+  float tv[kTopK];
+  int ti[kTopK];
+#pragma unroll
+  for (int q = 0; q < kTopK; ++q) {
+    tv[q] = -INFINITY;
+    ti[q] = 0x7fffffff;
+  }
+  float lref = -INFINITY;
+  double lsum = 0.0;
+  float th_row = -INFINITY;
+  if (a.theta && rvalid) th_row = a.theta[row];
+  float thr = th_row;
+
+  uint32_t ringl[NR] = {};
+  load_stage(0, ringl[0]);
+  {
+    const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)(a.u_rows > 0 ? a.u_rows : a.V) * a.rank * 2));
+    const uint32_t ubase = (uint32_t)(((size_t)tok * a.rank + 8 * (lane >> 5)) * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool ok = rvalid && 16 * ks + 8 * (lane >> 5) < a.rank;
+      buf_load_x4<true>(ufr[ks], udesc, ok ? ubase + 32 * ks : kOOB);
+    }
+  }
+#pragma unroll
+  for (int p = 1; p < NR; ++p) load_stage(p, ringl[p]);
+  // stage 0's L tile goes to LDS before the loop; stage s + 1's is stored during stage s
+  vm_wait<WD + KS + (NR - 1) * LPS>();
+  landed(ringl[0]);
+  store_lt(0, ringl[0]);
+
+  // tokens past V and rows past the block are -inf (their L entries may hold another
+  // request's logits); the masked values replace the stage's sums, which were taken
+  // before the mask
+  auto mask_stage = [&](int s, f32x16& z, float& tm, float& ts) {
+    const int v0 = (s_begin + s) * kTS;
+    if (v0 + kTS <= a.V && all_rows) return;  // uniform
+    const int vb = v0 + 4 * (lane >> 5);
+    tm = -INFINITY;
+    ts = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (!(rvalid & (vb + 8 * (q >> 2) + (q & 3) < a.V))) z[q] = -INFINITY;
+      tm = fmaxf(tm, z[q]);
+      ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -lref));
+    }
+  };
+
+  // acc[b]: stage s (b = s & 1), the L k-step first and then every k-step in order, so z
+  // is summed exactly as in markov_gemm_kernel; acc[b ^ 1] holds stage s - 1 for the epilogue
+  f32x16 acc[2];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[1][q] = -INFINITY;  // "stage -1": updates nothing
+  constexpr int NU = 6;  // L ring slot (s % 3), accumulator parity (s % 2) and Wt slot (s % 6) static
+  for (int base = 0; base < nst; base += NU) {
+#pragma unroll
+    for (int p = 0; p < NU; ++p) {
+      const int s = base + p;
+      if (s >= nst) break;  // uniform over the workgroup
+      const int b = p & 1, rp = p % NR;
+      // stage s's Wt (and, at s = 0, the U rows) and stage s + 1's L entry landed
+      vm_wait<(NR - 2) * LPS + WD>();
+      landed(ringl[(p + 1) % NR]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) landed(ufr[ks]);
+      __syncthreads();
+
+      const u32x4* Ws = wbuf + p * WSLOT;  // s % NWS: base is a multiple of NU = NWS
+      const bf16x8 al = __builtin_bit_cast(
+          bf16x8, *((const u32x4*)((const uint16_t*)(ltbuf + b * LTV) + (lane & 31) * 16) + (lane >> 5)));
+      auto wfrag = [&](int ks) {
+        const int m = lane & 31, kv = 2 * ks + (lane >> 5);
+        constexpr int W = NV < 16 ? NV : 16, RW = 16 / W;
+        return __builtin_bit_cast(bf16x8, Ws[m * NV + ((kv & ~(W - 1)) | ((kv ^ (m / RW)) & (W - 1)))]);
+      };
+      const f32x16 zero = {};
+      f32x16& z = acc[b ^ 1];  // stage s - 1 (masked in place: dead after its epilogue)
+      // stage s - 1 needs the mask (tokens past V, rows past the block): then its sums
+      // are taken again after the mask, and the in-section sum is not added
+      const int v0p = (s_begin + s - 1) * kTS;
+      const bool masked = !(v0p + kTS <= a.V && all_rows);  // uniform
+      float tm = -INFINITY, ts = 0.f;
+      bool fast = false;
+      // Issue order, fixed by scheduling barriers, one group per k-step after its MFMA:
+      // the Wt fragments are read three k-steps ahead (an MFMA never waits for its own
+      // read); the 16 values of stage s - 1's epilogue run in the first VS groups and its
+      // sum is added in the next, so no dependent chain trails the last MFMA; stage
+      // s + 3's loads and stage s + 1's L store are spread over the groups rather than
+      // queued by all waves at once after the barrier.
+      constexpr int VS = KS >= 8 ? KS * 3 / 4 : KS;  // groups carrying the values
+      auto values = [&](int j) {
+#pragma unroll
+        for (int q = 16 * j / VS; q < 16 * (j + 1) / VS; ++q) {
+          tm = fmaxf(tm, z[q]);
+          ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -lref));
+        }
+      };
+      const bool live = s + NR < nst;
+      const uint32_t tw = live ? (uint32_t)((size_t)(s_begin + s + NR) * kTS * a.rank * 2) : kOOB;
+      const uint32_t tl = live ? (uint32_t)((size_t)(s_begin + s + NR) * kTS * 2) : kOOB;
+      const uint32_t slot = lds_w + (uint32_t)(((p + NR) % NWS) * WSLOT * 16);  // stage s - 3's slot
+      bf16x8 fr[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < KS) fr[j] = wfrag(j);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, __builtin_bit_cast(bf16x8, onehot), zero, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks % 3], __builtin_bit_cast(bf16x8, ufr[ks]), acc[b], 0,
+                                                         0, 0);
+        if (ks + 3 < KS) fr[ks % 3] = wfrag(ks + 3);
+        if (ks < VS) values(ks);
+        // (a stage to be masked adds nothing here: a -inf reference selects no sum)
+        if (VS < KS && ks == VS) fast = tree_stage_sum(tm, ts, masked ? -INFINITY : lref, lsum);
+        if (ks == 0) buf_load_u16<true>(ringl[rp], ldesc, lofs + tl);  // L first: the counted waits rely on it
+        if (ks == 1) store_lt(b ^ 1, ringl[(p + 1) % NR]);              // L tile b ^ 1 was last read at s - 1
+#pragma unroll
+        for (int q = 0; q < WD; ++q)
+          if (ks == (KS * (q + 1)) / (WD + 1))
+            dma_load_x4(__builtin_amdgcn_readfirstlane(slot + (uint32_t)((q * kGT + wave * 64) * 16)), wdesc,
+                        wofs[q] + tw);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (VS == KS) fast = tree_stage_sum(tm, ts, masked ? -INFINITY : lref, lsum);
+      // s = 0: the -inf sentinel, which changes nothing
+      if (masked) {
+        mask_stage(s - 1, z, tm, ts);
+        tree_stage_end(v0p, lane, z, tm, ts, lref, lsum, tv, ti, thr, th_row);
+      } else {
+        tree_stage_rest(fast, v0p, lane, z, tm, lref, lsum, tv, ti, thr, th_row);
+      }
+    }
+  }
+  vm_wait<0>();  // the ring's trailing loads (past the range) land before the LDS is left
+  auto finish = [&](const f32x16& last) {
+    f32x16 z = last;
+    float tm = -INFINITY, ts = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      tm = fmaxf(tm, z[q]);
+      ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -lref));
+    }
+    mask_stage(nst - 1, z, tm, ts);
+    tree_stage_end((s_begin + nst - 1) * kTS, lane, z, tm, ts, lref, lsum, tv, ti, thr, th_row);
+  };
+  if (nst > 0) {
+    if ((nst - 1) & 1) finish(acc[1]);
+    else finish(acc[0]);
+  }
+  if (lfault) atomicOr(a.status, DSP_STATUS_NONFINITE);
+  merge_pair_top4(tv, ti);
+  merge_pair_lse(lref, lsum);
+  if (lane >= 32 || !rvalid) return;
+  TreePart p;
+#pragma unroll
+  for (int q = 0; q < kTopK; ++q) {
+    p.val[q] = tv[q];
+    p.idx[q] = ti[q];
+  }
+  p.ref = lref;
+  p.pad = 0.f;
+  p.sum = lsum;
+  ((TreePart*)a.part)[(size_t)row * a.G + g] = p;
 }
 
 // ---------------------------------------------------------------- chain merge
@@ -2159,6 +2479,44 @@ int32_t launch_gemm_al(int kid, const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// Every row block of kTR parent rows spans at most 16 requests (tree_gemm_kernel's L tile).
+bool blocks_span_16(const GemmArgs& a) {
+  for (int r0 = 0; r0 < a.rows; r0 += kTR) {
+    const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
+    if (rlast / a.rows_per_req - r0 / a.rows_per_req >= 16) return false;
+  }
+  return true;
+}
+
+size_t tree_split_lds_bytes(int ks) {
+  const int wslot = kTS * 2 * ks > kGT ? kTS * 2 * ks : kGT;
+  return ((size_t)6 * wslot + 2 * 64) * 16;  // six Wt stage slots, two 1 KB L tiles
+}
+
+template <int KS>
+int32_t launch_tree_split_ks(int kid, GemmArgs a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)tree_gemm_kernel<KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    attr_set = true;
+  }
+  a.nrb = (a.rows + kTR - 1) / kTR;
+  a.xcd_map = a.nrb > 1 && a.G % 8 == 0;
+  launch(kid, tree_gemm_kernel<KS>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT), (uint32_t)tree_split_lds_bytes(KS), s,
+         a);
+  return hip_check(hipGetLastError(), "tree gemm launch");
+}
+
+int32_t launch_tree_split(int kid, const GemmArgs& a, hipStream_t s) {
+  switch (ksteps(a.rank)) {
+    case 2: return launch_tree_split_ks<2>(kid, a, s);
+    case 4: return launch_tree_split_ks<4>(kid, a, s);
+    case 8: return launch_tree_split_ks<8>(kid, a, s);
+    default: return launch_tree_split_ks<16>(kid, a, s);
+  }
+}
+
 // L rows 16-byte aligned (base and both strides) take the vector-load kernel
 template <int MODE>
 int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
@@ -2170,6 +2528,8 @@ int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
   if ((reqs * (size_t)a.ldL_r + (size_t)a.V) * 2 >= kOOB)
     return fail(DSP_ERR_SHAPE, "the L rows of %d parent rows must span less than 2 GiB", kTR);
   const bool al = ((uintptr_t)a.L) % 16 == 0 && a.ldL_r % 8 == 0 && a.ldL_d % 8 == 0;
+  if (MODE == MODE_TREE && al && ksteps(a.rank) <= 16 && option(DSP_OPT_TREE_SPLIT) && blocks_span_16(a))
+    return launch_tree_split(kid, a, s);
   return al ? launch_gemm_al<MODE, true>(kid, a, s) : launch_gemm_al<MODE, false>(kid, a, s);
 }
 

@@ -484,11 +484,17 @@ int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);
 /* DSP_OPT_SPIN_LIMIT: polls a persistent launch's grid barrier makes before */
 /*   it gives up and sets DSP_STATUS_TIMEOUT (default 2^20, about a second); */
 /*   0 makes every wait that is not already satisfied give up at once.       */
+/* DSP_OPT_TREE_SPLIT: 1 (default) lets dsp_tree_expand run its depths whose */
+/*   row blocks of 256 parents span at most 16 requests (rank <= 256,        */
+/*   16-byte aligned L) on the GEMM with direct-to-LDS stages and a fixed    */
+/*   issue order; 0 keeps the general GEMM for every depth. Both compute the */
+/*   same sums in the same order: outputs are bit-identical.                 */
 /* Returns DSP_ERR_SHAPE for an unknown option or a negative value. Not      */
 /* thread safe; set before issuing work.                                     */
 /* ------------------------------------------------------------------------ */
 #define DSP_OPT_CHAIN_PERSISTENT  0
 #define DSP_OPT_SPIN_LIMIT        1
+#define DSP_OPT_TREE_SPLIT        2
 int32_t dsp_set_option(int32_t option, int64_t value);
 
 #ifdef __cplusplus

@@ -547,3 +547,39 @@ def test_tree_nonfinite_base_logit_is_a_fault(R, depth, bits):
     L[0, depth, 17] = bits
     c = dict(c, L=L)
     _check_tree(c, 4, 16, 24, requests=range(1, R), status=dsp.DSP_STATUS_NONFINITE)
+
+
+@pytest.mark.parametrize("R,D,V,rank,k,F,N,mask,bits", [
+    (128, 5, 151936, 256, 4, 16, 64, False, 0),  # the PCTree shape (shorter), full row blocks
+    (37, 4, 40001, 256, 4, 16, 40, True, 0),     # partial row blocks, ragged vocabulary, masked entries
+    (9, 4, 5003, 64, 4, 16, 30, False, 0x7F80),  # rank 64, a +inf base logit (fault)
+    (21, 3, 3001, 32, 3, 12, 20, True, 0),       # rank 32, 12 parents per request
+    (16, 4, 20000, 128, 4, 16, 40, False, 0),    # rank 128
+])
+def test_tree_scheduled_gemm_matches_general_gemm(R, D, V, rank, k, F, N, mask, bits):
+    """The tree's depths whose row blocks span at most 16 requests run on the GEMM with
+    direct-to-LDS stages and a fixed issue order; it sums the same products in the same
+    order as the general GEMM, so every output (tokens, parents, depths, scores, masks,
+    status) must be bit-identical to a run with that kernel switched off."""
+    c = workloads.markov_case(R, D, V, rank=rank, seed=300 + R + V)
+    L = c["L"].copy()
+    if mask:
+        rng = np.random.default_rng(R)
+        L[..., rng.random(V) < 0.1] = 0xFF80
+    if bits:
+        L[0, D - 1, 17] = bits
+    c = dict(c, L=L)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    out = {}
+    try:
+        for opt_on in (0, 1):
+            dsp.set_option("tree_split", opt_on)
+            print(f"tree R={R} D={D} V={V} rank={rank} tree_split={opt_on}", flush=True)
+            g = dsp.tree_expand(Lg, Ug, Wtg, ag, k, F, N, want_mask=True)
+            torch.cuda.synchronize()
+            out[opt_on] = {n: host(t).copy() for n, t in g.items() if torch.is_tensor(t)}
+    finally:
+        dsp.set_option("tree_split", 1)
+    assert (out[1]["status"][0] != 0) == bool(bits)
+    for n in out[0]:
+        np.testing.assert_array_equal(out[1][n].view(np.uint8), out[0][n].view(np.uint8), err_msg=n)
