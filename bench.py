@@ -674,7 +674,7 @@ def bench_tree(args, c, cpu):
                              "k=4, F=16, N=64", parent_rows=parents),
         roofline=dict(kernel="tree_gemm (all depths)", bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=tflops / PEAK_BF16_TFLOPS,
-                      traffic=traffic_from_profiles("markov.hip", "markov_gemm_tree", "pctree"),
+                      traffic=traffic_from_profiles("markov.hip", "tree_gemm", "pctree"),
                       gemm_us_per_step=gemm_total_us, flops_per_step=flops),
         kernels=kern, timing=timing)
     # the walk reads the target rows of the visited nodes only (accepted + 1 per request)
