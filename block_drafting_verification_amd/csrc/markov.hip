@@ -818,20 +818,22 @@ __global__ __launch_bounds__(kGT, 1) void markov_gemm_kernel(GemmArgs a) {
 // base logits entering as the first k-step (A = the stage's 32 tokens x 16 requests of
 // L, B = each row's one-hot request) and the k-steps summed in the same order, so z and
 // every output are bit-identical to it. What differs is how a stage is issued:
-//  - Wt stages go straight from memory into LDS (buffer loads with the lds modifier,
-//    issued from inline assembly so that no compiler-inserted wait drains them), six
-//    stage slots with three stages in flight; the L tile takes one 2-byte entry per
-//    thread through a register and is transposed into LDS a stage ahead of its use.
-//    No register ring holds Wt, which leaves room for
+//  - every streaming load goes straight from memory into LDS (buffer loads with the
+//    lds modifier, issued from inline assembly so that no compiler-inserted wait drains
+//    them): Wt stages and the L tile as stored, six stage slots, stages issued four
+//    ahead. No register is the destination of a load in flight in the stage loop, so
+//    the compiler cannot copy one before its wait; the stages go in pairs with one
+//    barrier per pair. Each lane gathers its L fragment (8 requests of one token) from
+//    the stored tile during the stage before.
 //  - a fixed issue order per stage (scheduling barriers): Wt fragments read three
 //    k-steps ahead of their MFMA, the previous stage's exp2 sums and maximum placed
 //    between the MFMAs so they run while the matrix cores work, the stage's sum added
 //    before the last MFMAs, and the next stages' loads spread over the k-steps instead
 //    of issued by every wave at once after the barrier.
 // A direct-to-LDS load of 16 bytes writes lane l's data at M0 + 16*l, so the swizzled
-// tile layout is made by choosing each lane's source address: slot t of a stage holds
-// token row m = t / NV, swizzled vector p = t % NV, i.e. rank vector kv = swz(m, p)
-// (the swizzle is an XOR, its own inverse).
+// Wt tile layout is made by choosing each lane's source address: slot t of a stage
+// holds token row m = t / NV, swizzled vector p = t % NV, i.e. rank vector
+// kv = swz(m, p) (the swizzle is an XOR, its own inverse).
 __device__ __forceinline__ void dma_load_x4(uint32_t lds_addr, const s32x4& d, uint32_t off) {
   // s_nop 4: M0 is read by the load one instruction after it is written, and the
   // descriptor may come from a VALU write of an SGPR (5 wait states)
@@ -843,19 +845,15 @@ __device__ __forceinline__ void dma_load_x4(uint32_t lds_addr, const s32x4& d, u
 template <int KS>
 __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
   static_assert(KS >= 2 && KS <= 16 && (KS & (KS - 1)) == 0, "rank up to 256");
-  constexpr int NV = 2 * KS;                          // 16-byte vectors per staged Wt row
-  constexpr int WST = kTS * NV;                       // Wt vectors per stage
-  constexpr int WSLOT = WST > kGT ? WST : kGT;        // LDS vectors per stage slot
-  constexpr int WD = WSLOT / kGT;                     // direct-to-LDS loads per thread per stage
-  constexpr int NR = 3;                               // stages in flight
-  constexpr int NWS = 6;                              // Wt stage slots (stage s in slot s % 6: static per unrolled
-                                                      // stage; the slot refilled, s + 3's, was read at stage s - 3)
-  constexpr int LPS = WD + 1;                         // loads per stage per thread (Wt, one L entry)
-  constexpr int LTV = kTS * 16 * 2 / 16;              // L tile vectors (32 tokens x 16 requests, bf16)
-  extern __shared__ u32x4 lds[];                      // [NWS][WSLOT] Wt slots, then [2][LTV] L tiles
-  static_assert(NWS == 6, "the stage loop unrolls six stages");
+  constexpr int NV = 2 * KS;                    // 16-byte vectors per staged Wt row
+  constexpr int WST = kTS * NV;                 // Wt vectors per stage
+  constexpr int WSLOT = WST > kGT ? WST : kGT;  // LDS vectors per Wt stage slot
+  constexpr int WD = WSLOT / kGT;               // Wt direct-to-LDS loads per thread per stage
+  constexpr int NS = 6;                         // stage slots (Wt and L): stage s in slot s % 6
+  constexpr int LTV = kTS * 16 * 2 / 16;        // L tile vectors (16 requests x 32 tokens, bf16)
+  extern __shared__ u32x4 lds[];                // [NS][WSLOT] Wt, then [NS][LTV] L tiles
   u32x4* const wbuf = lds;
-  u32x4* const ltbuf = lds + NWS * WSLOT;
+  u32x4* const lbuf = lds + NS * WSLOT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   int g, rb;
@@ -898,9 +896,11 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
   const int req0 = r0 / a.rows_per_req;
   const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
   const int nreq = rlast / a.rows_per_req - req0 + 1;  // at most 16 (checked on the host)
+  // the L rows of the block's requests (a 16-byte load ending past V reads the dword
+  // holding V-1 whole: the extent is rounded up to it, still inside the row's storage)
   const s32x4 ldesc = make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
-                                (uint32_t)(((size_t)(nreq - 1) * a.ldL_r + a.V) * 2));
-  // this thread's Wt source offsets (less the stage term) and LDS destinations
+                                (uint32_t)((((size_t)(nreq - 1) * a.ldL_r + a.V) * 2 + 3) & ~(size_t)3));
+  // Wt: this thread's source offsets, less the stage term
   uint32_t wofs[WD];
 #pragma unroll
   for (int q = 0; q < WD; ++q) {
@@ -911,32 +911,53 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
     wofs[q] = t < WST && kv * 8 < a.rank ? (uint32_t)((m * a.rank + kv * 8) * 2) : kOOB;
   }
   const uint32_t lds_w = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)wbuf;
-  // L: one entry per thread, token tid % 32 of request tid / 32 of the block (zero past
-  // the block's requests; a token past V reads another row or zero and is masked at use)
-  const int lj = tid >> 5, lt = tid & 31;
-  const uint32_t lofs = lj < nreq ? (uint32_t)(((size_t)lj * a.ldL_r + lt) * 2) : kOOB;
-
-  auto load_stage = [&](int s, uint32_t& rl) {
-    const bool live = s < nst;
-    const uint32_t tw = live ? (uint32_t)((size_t)(s_begin + s) * kTS * a.rank * 2) : kOOB;
-    const uint32_t tl = live ? (uint32_t)((size_t)(s_begin + s) * kTS * 2) : kOOB;
-    const uint32_t slot = lds_w + (uint32_t)((s % NWS) * WSLOT * 16);
-    buf_load_u16<true>(rl, ldesc, lofs + tl);  // first: the wait one stage earlier covers it
-#pragma unroll
-    for (int q = 0; q < WD; ++q)
-      dma_load_x4(__builtin_amdgcn_readfirstlane(slot + (uint32_t)((q * kGT + wave * 64) * 16)), wdesc, wofs[q] + tw);
+  const uint32_t lds_l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)lbuf;
+  // L (the first wave): lane l loads 8 tokens (16 bytes) of request l / 4, column l % 4,
+  // into the tile [request][32 tokens] as stored (zero past the block's requests)
+  const uint32_t lofs =
+      lane >> 2 < nreq ? (uint32_t)(((size_t)(lane >> 2) * a.ldL_r + 8 * (lane & 3)) * 2) : kOOB;
+  auto load_l = [&](int s) {
+    if (wave == 0)  // uniform; the other waves' counted waits leave this load out
+      dma_load_x4(lds_l + (uint32_t)((s % NS) * LTV * 16), ldesc,
+                  lofs + (s < nst ? (uint32_t)((size_t)(s_begin + s) * kTS * 2) : kOOB));
   };
-  // the L tile, transposed: token t of request j at Lt[t * 16 + j], one entry per thread;
-  // every request column is written (zeros past the block's requests). A non-finite
-  // entry is staged as -max (a zero weight times an infinity would make NaN in every
-  // other request's sum): for a masked -inf that ranks and weighs the same; +inf and NaN
-  // are faults, noted here and reported once at the end (no branch in the stage loop).
+  auto load_w = [&](int s, int q) {
+    const uint32_t tw = s < nst ? (uint32_t)((size_t)(s_begin + s) * kTS * a.rank * 2) : kOOB;
+    const uint32_t slot = lds_w + (uint32_t)((s % NS) * WSLOT * 16);
+    dma_load_x4(__builtin_amdgcn_readfirstlane(slot + (uint32_t)((q * kGT + wave * 64) * 16)), wdesc, wofs[q] + tw);
+  };
+  // the L k-step's A fragment of stage s: lane l holds token l % 32 of requests
+  // 8*(l/32) .. +8, gathered from the stored tile. A non-finite entry is taken as -max
+  // (a zero weight times an infinity would make NaN in every other request's sum): for a
+  // masked -inf that ranks and weighs the same; +inf and NaN are faults, noted here and
+  // reported once at the end (no branch in the stage loop).
   bool lfault = false;
-  auto store_lt = [&](int b, uint32_t w) {
-    const uint32_t h = w & 0xffffu;
-    const bool nonfinite = (h & 0x7f80u) == 0x7f80u;
-    lfault |= nonfinite & ((h & 0x807fu) != 0x8000u);  // +inf or NaN
-    ((uint16_t*)(ltbuf + b * LTV))[lt * 16 + lj] = (uint16_t)(nonfinite ? 0xff7fu : h);
+  auto l_frag = [&](int s) {
+    const uint16_t* t = (const uint16_t*)(lbuf + (s % NS) * LTV) + 8 * (lane >> 5) * kTS + (lane & 31);
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = t[e * kTS];
+    u32x4 v;
+    // any non-finite entry: adding 0x80 to a bf16 exponent field (bits 7..14) carries into
+    // bit 15 only when the field is all ones, and with both halves of a pair at once no
+    // carry crosses into the upper half
+    uint32_t any = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = h[2 * c] | (h[2 * c + 1] << 16);
+      any |= (v[c] & 0x7f807f80u) + 0x00800080u;
+    }
+    if (any & 0x80008000u) {  // rare: stage the non-finite entries
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool nonfinite = (h[e] & 0x7f80u) == 0x7f80u;
+        lfault |= nonfinite & ((h[e] & 0x807fu) != 0x8000u);  // +inf or NaN
+        h[e] = nonfinite ? 0xff7fu : h[e];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = h[2 * c] | (h[2 * c + 1] << 16);
+    }
+    return v;
   };
 
   float tv[kTopK];
@@ -952,8 +973,19 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
   if (a.theta && rvalid) th_row = a.theta[row];
   float thr = th_row;
 
-  uint32_t ringl[NR] = {};
-  load_stage(0, ringl[0]);
+  // Stages go in pairs (s, s + 1), s even, with one barrier per pair; every load goes
+  // straight to LDS, so no register is written by a load in flight. Loads per pair, in
+  // this order: the L tiles of stages s + 4 and s + 5 (first wave), then their Wt parts.
+  // The wait at a pair's start leaves only the previous pair's Wt parts in flight, so
+  // stages s and s + 1 (and the U rows) and the L tiles of s + 2 and s + 3 have landed.
+  // A stage's slot is refilled (s + 4, s + 5) once its reads are before the barrier
+  // (s - 2, s - 1); stage t's L fragment is gathered during stage t - 1.
+  load_l(0);
+  load_l(1);
+#pragma unroll
+  for (int q = 0; q < WD; ++q) load_w(0, q);
+#pragma unroll
+  for (int q = 0; q < WD; ++q) load_w(1, q);
   {
     const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)(a.u_rows > 0 ? a.u_rows : a.V) * a.rank * 2));
     const uint32_t ubase = (uint32_t)(((size_t)tok * a.rank + 8 * (lane >> 5)) * 2);
@@ -963,19 +995,21 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
       buf_load_x4<true>(ufr[ks], udesc, ok ? ubase + 32 * ks : kOOB);
     }
   }
+  load_l(2);
+  load_l(3);
 #pragma unroll
-  for (int p = 1; p < NR; ++p) load_stage(p, ringl[p]);
-  // stage 0's L tile goes to LDS before the loop; stage s + 1's is stored during stage s
-  vm_wait<WD + KS + (NR - 1) * LPS>();
-  landed(ringl[0]);
-  store_lt(0, ringl[0]);
+  for (int q = 0; q < WD; ++q) load_w(2, q);
+#pragma unroll
+  for (int q = 0; q < WD; ++q) load_w(3, q);
+  // stage 0's L tile, for its fragment
+  if (wave == 0) vm_wait<2 * WD + KS + 2 + 2 * WD>();
+  __syncthreads();
+  u32x4 alf = l_frag(0);
 
   // tokens past V and rows past the block are -inf (their L entries may hold another
-  // request's logits); the masked values replace the stage's sums, which were taken
-  // before the mask
+  // request's logits); the masked values replace the stage's sums
   auto mask_stage = [&](int s, f32x16& z, float& tm, float& ts) {
     const int v0 = (s_begin + s) * kTS;
-    if (v0 + kTS <= a.V && all_rows) return;  // uniform
     const int vb = v0 + 4 * (lane >> 5);
     tm = -INFINITY;
     ts = 0.f;
@@ -992,88 +1026,90 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
   f32x16 acc[2];
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[1][q] = -INFINITY;  // "stage -1": updates nothing
-  constexpr int NU = 6;  // L ring slot (s % 3), accumulator parity (s % 2) and Wt slot (s % 6) static
-  for (int base = 0; base < nst; base += NU) {
+  auto stage = [&](const int p, const int s) {
+    const int b = p & 1;
+    const u32x4* Ws = wbuf + p * WSLOT;  // s % NS (base is a multiple of NS)
+    auto wfrag = [&](int ks) {
+      const int m = lane & 31, kv = 2 * ks + (lane >> 5);
+      constexpr int W = NV < 16 ? NV : 16, RW = 16 / W;
+      return __builtin_bit_cast(bf16x8, Ws[m * NV + ((kv & ~(W - 1)) | ((kv ^ (m / RW)) & (W - 1)))]);
+    };
+    const f32x16 zero = {};
+    const f32x16& z = acc[b ^ 1];  // stage s - 1
+    const int v0p = (s_begin + s - 1) * kTS;
+    // stage s - 1 needs the mask (tokens past V, rows past the block): then its sums are
+    // taken again after the mask, and the in-section sum is not added
+    const bool masked = !(v0p + kTS <= a.V && all_rows);  // uniform
+    float tm = -INFINITY, ts = 0.f;
+    bool fast = false;
+    // Issue order, fixed by scheduling barriers, one group per k-step after its MFMA:
+    // the Wt fragments are read three k-steps ahead (an MFMA never waits for its own
+    // read); the 16 values of stage s - 1's epilogue run in the first VS groups and its
+    // sum is added in the next, so no dependent chain trails the last MFMA; the next
+    // stage's L fragment is gathered and stage s + 4's loads issued, spread over the
+    // groups rather than queued by all waves at once after the barrier.
+    constexpr int VS = KS >= 8 ? KS * 3 / 4 : KS;
+    auto values = [&](int j) {
 #pragma unroll
-    for (int p = 0; p < NU; ++p) {
+      for (int q = 16 * j / VS; q < 16 * (j + 1) / VS; ++q) {
+        tm = fmaxf(tm, z[q]);
+        ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -lref));
+      }
+    };
+    bf16x8 fr[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < KS) fr[j] = wfrag(j);
+    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, alf), __builtin_bit_cast(bf16x8, onehot),
+                                                     zero, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks % 3], __builtin_bit_cast(bf16x8, ufr[ks]), acc[b], 0, 0,
+                                                       0);
+      if (ks + 3 < KS) fr[ks % 3] = wfrag(ks + 3);
+      if (ks < VS) values(ks);
+      // (a stage to be masked adds nothing here: a -inf reference selects no sum)
+      if (VS < KS && ks == VS) fast = tree_stage_sum(tm, ts, masked ? -INFINITY : lref, lsum);
+      if (ks == 1) alf = l_frag(s + 1);  // stage s + 1's tile: landed before this pair's barrier or the last
+      if (b == 0 && ks == 0) {
+        load_l(s + 4);
+        load_l(s + 5);
+      }
+#pragma unroll
+      for (int q = 0; q < WD; ++q)
+        if (ks == (KS * (q + 1)) / (WD + 1)) load_w(s + 4, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (VS == KS) fast = tree_stage_sum(tm, ts, masked ? -INFINITY : lref, lsum);
+    // s = 0: the -inf sentinel, which changes nothing
+    if (masked) {
+      f32x16 zm = z;
+      mask_stage(s - 1, zm, tm, ts);
+      tree_stage_end(v0p, lane, zm, tm, ts, lref, lsum, tv, ti, thr, th_row);
+    } else {
+      tree_stage_rest(fast, v0p, lane, z, tm, lref, lsum, tv, ti, thr, th_row);
+    }
+  };
+  for (int base = 0; base < nst; base += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; p += 2) {
       const int s = base + p;
       if (s >= nst) break;  // uniform over the workgroup
-      const int b = p & 1, rp = p % NR;
-      // stage s's Wt (and, at s = 0, the U rows) and stage s + 1's L entry landed
-      vm_wait<(NR - 2) * LPS + WD>();
-      landed(ringl[(p + 1) % NR]);
+      vm_wait<2 * WD>();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) landed(ufr[ks]);
       __syncthreads();
-
-      const u32x4* Ws = wbuf + p * WSLOT;  // s % NWS: base is a multiple of NU = NWS
-      const bf16x8 al = __builtin_bit_cast(
-          bf16x8, *((const u32x4*)((const uint16_t*)(ltbuf + b * LTV) + (lane & 31) * 16) + (lane >> 5)));
-      auto wfrag = [&](int ks) {
-        const int m = lane & 31, kv = 2 * ks + (lane >> 5);
-        constexpr int W = NV < 16 ? NV : 16, RW = 16 / W;
-        return __builtin_bit_cast(bf16x8, Ws[m * NV + ((kv & ~(W - 1)) | ((kv ^ (m / RW)) & (W - 1)))]);
-      };
-      const f32x16 zero = {};
-      f32x16& z = acc[b ^ 1];  // stage s - 1 (masked in place: dead after its epilogue)
-      // stage s - 1 needs the mask (tokens past V, rows past the block): then its sums
-      // are taken again after the mask, and the in-section sum is not added
-      const int v0p = (s_begin + s - 1) * kTS;
-      const bool masked = !(v0p + kTS <= a.V && all_rows);  // uniform
-      float tm = -INFINITY, ts = 0.f;
-      bool fast = false;
-      // Issue order, fixed by scheduling barriers, one group per k-step after its MFMA:
-      // the Wt fragments are read three k-steps ahead (an MFMA never waits for its own
-      // read); the 16 values of stage s - 1's epilogue run in the first VS groups and its
-      // sum is added in the next, so no dependent chain trails the last MFMA; stage
-      // s + 3's loads and stage s + 1's L store are spread over the groups rather than
-      // queued by all waves at once after the barrier.
-      constexpr int VS = KS >= 8 ? KS * 3 / 4 : KS;  // groups carrying the values
-      auto values = [&](int j) {
+      stage(p, s);
+      if (s + 1 < nst) {
+        stage(p + 1, s + 1);
+      } else {  // the pair's load count: stage s + 5's Wt parts (past the range)
 #pragma unroll
-        for (int q = 16 * j / VS; q < 16 * (j + 1) / VS; ++q) {
-          tm = fmaxf(tm, z[q]);
-          ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -lref));
-        }
-      };
-      const bool live = s + NR < nst;
-      const uint32_t tw = live ? (uint32_t)((size_t)(s_begin + s + NR) * kTS * a.rank * 2) : kOOB;
-      const uint32_t tl = live ? (uint32_t)((size_t)(s_begin + s + NR) * kTS * 2) : kOOB;
-      const uint32_t slot = lds_w + (uint32_t)(((p + NR) % NWS) * WSLOT * 16);  // stage s - 3's slot
-      bf16x8 fr[3];
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < KS) fr[j] = wfrag(j);
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, __builtin_bit_cast(bf16x8, onehot), zero, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks % 3], __builtin_bit_cast(bf16x8, ufr[ks]), acc[b], 0,
-                                                         0, 0);
-        if (ks + 3 < KS) fr[ks % 3] = wfrag(ks + 3);
-        if (ks < VS) values(ks);
-        // (a stage to be masked adds nothing here: a -inf reference selects no sum)
-        if (VS < KS && ks == VS) fast = tree_stage_sum(tm, ts, masked ? -INFINITY : lref, lsum);
-        if (ks == 0) buf_load_u16<true>(ringl[rp], ldesc, lofs + tl);  // L first: the counted waits rely on it
-        if (ks == 1) store_lt(b ^ 1, ringl[(p + 1) % NR]);              // L tile b ^ 1 was last read at s - 1
-#pragma unroll
-        for (int q = 0; q < WD; ++q)
-          if (ks == (KS * (q + 1)) / (WD + 1))
-            dma_load_x4(__builtin_amdgcn_readfirstlane(slot + (uint32_t)((q * kGT + wave * 64) * 16)), wdesc,
-                        wofs[q] + tw);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (VS == KS) fast = tree_stage_sum(tm, ts, masked ? -INFINITY : lref, lsum);
-      // s = 0: the -inf sentinel, which changes nothing
-      if (masked) {
-        mask_stage(s - 1, z, tm, ts);
-        tree_stage_end(v0p, lane, z, tm, ts, lref, lsum, tv, ti, thr, th_row);
-      } else {
-        tree_stage_rest(fast, v0p, lane, z, tm, lref, lsum, tv, ti, thr, th_row);
+        for (int q = 0; q < WD; ++q) load_w(s + 5, q);
       }
     }
   }
-  vm_wait<0>();  // the ring's trailing loads (past the range) land before the LDS is left
+  vm_wait<0>();  // the trailing loads (past the range) land before the LDS is left
   auto finish = [&](const f32x16& last) {
     f32x16 z = last;
     float tm = -INFINITY, ts = 0.f;
@@ -1082,8 +1118,9 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
       tm = fmaxf(tm, z[q]);
       ts += fast_exp2(__builtin_fmaf(z[q], kLog2e, -lref));
     }
-    mask_stage(nst - 1, z, tm, ts);
-    tree_stage_end((s_begin + nst - 1) * kTS, lane, z, tm, ts, lref, lsum, tv, ti, thr, th_row);
+    const int v0 = (s_begin + nst - 1) * kTS;
+    if (!(v0 + kTS <= a.V && all_rows)) mask_stage(nst - 1, z, tm, ts);
+    tree_stage_end(v0, lane, z, tm, ts, lref, lsum, tv, ti, thr, th_row);
   };
   if (nst > 0) {
     if ((nst - 1) & 1) finish(acc[1]);
@@ -2490,7 +2527,7 @@ bool blocks_span_16(const GemmArgs& a) {
 
 size_t tree_split_lds_bytes(int ks) {
   const int wslot = kTS * 2 * ks > kGT ? kTS * 2 * ks : kGT;
-  return ((size_t)6 * wslot + 2 * 64) * 16;  // six Wt stage slots, two 1 KB L tiles
+  return ((size_t)6 * wslot + 6 * 64) * 16;  // six stage slots: Wt and the 1 KB L tile
 }
 
 template <int KS>
