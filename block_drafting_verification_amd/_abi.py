@@ -15,6 +15,7 @@ DSP_STATUS_TIMEOUT = 8
 DSP_OPT_CHAIN_PERSISTENT = 0
 DSP_OPT_SPIN_LIMIT = 1
 DSP_OPT_TREE_SPLIT = 2
+DSP_OPT_CHAIN_SCHED = 3
 DSP_SCHED_EARLY_STOP = 0
 DSP_SCHED_ARGMAX = 1
 DSP_SCHED_TOP_M = 2

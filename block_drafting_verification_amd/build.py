@@ -33,8 +33,8 @@ FLAGS = [
 
 # Kernels whose streaming loads are issued asynchronously from inline assembly must not
 # spill registers (a spill could copy a register before its load lands): the Markov GEMM
-# instantiations with rank up to 256 (k-steps 2..16) and the tree's split GEMM.
-ASYNC_KERNELS = re.compile(r"markov_gemm_kernelILi\dELi(2|4|8|16)ELb[01]E|tree_gemm_kernelILi(2|4|8|16)E")
+# instantiations with rank up to 256 (k-steps 2..16) and the scheduled tree and chain GEMMs.
+ASYNC_KERNELS = re.compile(r"markov_gemm_kernelILi\dELi(2|4|8|16)ELb[01]E|(?:tree|chain)_gemm_kernelILi(2|4|8|16)E")
 
 
 def _spills(stderr):

@@ -64,9 +64,9 @@ bool prof_events(int kernel, hipEvent_t* start, hipEvent_t* stop) {
 void prof_commit(int kernel, hipEvent_t start, hipEvent_t stop) { g_prof_recs.push_back({kernel, start, stop}); }
 
 // ---------------------------------------------------------------- options
-static int64_t g_options[3] = {0, 1 << 20, 1};
+static int64_t g_options[4] = {0, 1 << 20, 1, 1};
 
-int64_t option(int32_t opt) { return opt >= 0 && opt < 3 ? g_options[opt] : 0; }
+int64_t option(int32_t opt) { return opt >= 0 && opt < 4 ? g_options[opt] : 0; }
 
 // ---------------------------------------------------------------- philox utility
 __global__ void philox_uniforms_kernel(const uint64_t* __restrict__ ctr, int64_t n, uint64_t seed,
@@ -102,7 +102,7 @@ extern "C" int32_t dsp_philox_uniforms(const uint64_t* ctr, int64_t n, uint64_t 
 
 extern "C" int32_t dsp_set_option(int32_t opt, int64_t value) {
   clear_error();
-  if (opt < 0 || opt >= 3) return fail(DSP_ERR_SHAPE, "unknown option %d", opt);
+  if (opt < 0 || opt >= 4) return fail(DSP_ERR_SHAPE, "unknown option %d", opt);
   if (value < 0 || (opt == DSP_OPT_SPIN_LIMIT && value > 0xffffffffll))
     return fail(DSP_ERR_SHAPE, "option %d: value out of range", opt);
   g_options[opt] = value;

@@ -1142,6 +1142,241 @@ __global__ __launch_bounds__(kGT, 1) void tree_gemm_kernel(GemmArgs a) {
   ((TreePart*)a.part)[(size_t)row * a.G + g] = p;
 }
 
+// ---------------------------------------------------------------- chain GEMM, scheduled stages
+// The greedy chain's GEMM (arg-max only) for 16-byte aligned row-major L, at rank up to
+// 256: the same workgroup shape, vocabulary slices, accumulators started from L and
+// k-steps summed in order as markov_gemm_kernel's arg-max mode, so z, the arg-max and
+// the partial results are bit-identical to it. The stage issue follows tree_gemm_kernel:
+// Wt and L stages go straight from memory into LDS (direct-to-LDS buffer loads from
+// inline assembly: no load in flight into a register inside the stage loop), four stage
+// slots with three stages in flight, a stage's data waited one stage before its use so
+// each lane reads its L entries for the next stage ahead of time; per k-step, fixed by
+// scheduling barriers, the MFMA, the fragment read three k-steps ahead, one value of the
+// previous stage's arg-max, and the next stages' loads spread over the k-steps.
+template <int KS>
+__global__ __launch_bounds__(kGT, 1) void chain_gemm_kernel(GemmArgs a) {
+  static_assert(KS >= 2 && KS <= 16 && (KS & (KS - 1)) == 0, "rank up to 256");
+  constexpr int NV = 2 * KS;                    // 16-byte vectors per staged Wt row
+  constexpr int WST = kTS * NV;                 // Wt vectors per stage
+  constexpr int WSLOT = WST > kGT ? WST : kGT;  // LDS vectors per Wt stage slot
+  constexpr int WD = WSLOT / kGT;               // Wt loads per thread per stage
+  constexpr int LST = kTR * 4;                  // L vectors per stage: 256 rows x 32 tokens
+  constexpr int LD = LST / kGT;                 // L loads per thread per stage
+  constexpr int LPS = WD + LD;                  // loads per stage per thread
+  constexpr int NS = 4;                         // stage slots: stage s in slot s % 4
+  extern __shared__ u32x4 lds[];                // [NS][WSLOT] Wt, then [NS][LST] L
+  u32x4* const wbuf = lds;
+  u32x4* const lbuf = lds + NS * WSLOT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  int g, rb;
+  {
+    const int id = blockIdx.x;
+    if (a.xcd_map) {
+      const int j = id >> 3;
+      g = (j / a.nrb) * 8 + (id & 7);
+      rb = j % a.nrb;
+    } else {
+      g = id % a.G;
+      rb = id / a.G;
+    }
+  }
+  const int r0 = rb * kTR;
+  const int nst_all = (a.V + kTS - 1) / kTS;
+  const int s_begin = (int)(((long)g * nst_all) / a.G);
+  const int nst = (int)(((long)(g + 1) * nst_all) / a.G) - s_begin;
+
+  const int nloc = wave * 32 + (lane & 31);
+  const int row = r0 + nloc;
+  const bool rvalid = row < a.rows;
+  const bool all_rows = r0 + kTR <= a.rows;
+  int tok = 0;
+  if (rvalid) {
+    tok = a.row_tok[(size_t)row * a.ld_tok];
+    if (tok < 0 || tok >= (a.u_rows > 0 ? a.u_rows : a.V)) {
+      if (g == 0 && lane < 32) atomicOr(a.status, DSP_STATUS_TOKEN_RANGE);
+      tok = 0;
+    }
+  }
+  u32x4 ufr[KS] = {};
+
+  const s32x4 wdesc = make_desc(a.Wt, (uint32_t)((size_t)a.V * a.rank * 2));
+  const int req0 = r0 / a.rows_per_req;
+  const int rlast = (r0 + kTR < a.rows ? r0 + kTR : a.rows) - 1;
+  // up to the block's last row's token V-1; a 16-byte load ending past it reads the dword
+  // holding V-1 whole (the extent is rounded up to it, inside the row's storage)
+  const s32x4 ldesc = make_desc(a.L + (size_t)req0 * a.ldL_r + (size_t)a.d * a.ldL_d,
+                                (uint32_t)((((size_t)(rlast / a.rows_per_req - req0) * a.ldL_r + a.V) * 2 + 3) &
+                                           ~(size_t)3));
+  constexpr int W = NV < 16 ? NV : 16, RW = 16 / W;  // Wt tile swizzle (an XOR: its own inverse)
+  uint32_t wofs[WD], lofs[LD];
+#pragma unroll
+  for (int q = 0; q < WD; ++q) {
+    const int t = q * kGT + tid;
+    const int m = t / NV, p = t % NV;
+    const int kv = (p & ~(W - 1)) | ((p ^ (m / RW)) & (W - 1));
+    wofs[q] = t < WST && kv * 8 < a.rank ? (uint32_t)((m * a.rank + kv * 8) * 2) : kOOB;
+  }
+  // L tile: row n holds 4 vectors of 8 tokens, vector c at n*4 + (c ^ ((n >> 2) & 3)), so the
+  // 8-byte reads of 16 consecutive rows hit 16 distinct slots; slot t = n*4 + c' holds
+  // vector c = c' ^ ((n >> 2) & 3) of row n
+#pragma unroll
+  for (int q = 0; q < LD; ++q) {
+    const int t = q * kGT + tid;
+    const int n = t >> 2, c = (t & 3) ^ ((n >> 2) & 3);
+    lofs[q] = r0 + n < a.rows ? (uint32_t)((((size_t)(r0 + n) / a.rows_per_req - req0) * a.ldL_r + 8 * c) * 2) : kOOB;
+  }
+  const uint32_t lds_w = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)wbuf;
+  const uint32_t lds_l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)lbuf;
+  auto load_w = [&](int s, int q) {
+    const uint32_t tw = s < nst ? (uint32_t)((size_t)(s_begin + s) * kTS * a.rank * 2) : kOOB;
+    dma_load_x4(__builtin_amdgcn_readfirstlane(lds_w + (uint32_t)(((s % NS) * WSLOT + q * kGT + wave * 64) * 16)), wdesc,
+                wofs[q] + tw);
+  };
+  auto load_l = [&](int s, int q) {
+    const uint32_t tl = s < nst ? (uint32_t)((size_t)(s_begin + s) * kTS * 2) : kOOB;
+    dma_load_x4(__builtin_amdgcn_readfirstlane(lds_l + (uint32_t)(((s % NS) * LST + q * kGT + wave * 64) * 16)), ldesc,
+                lofs[q] + tl);
+  };
+  auto load_stage = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < WD; ++q) load_w(s, q);
+#pragma unroll
+    for (int q = 0; q < LD; ++q) load_l(s, q);
+  };
+  // this lane's 16 L entries of stage s (token v0 + 8*(q>>2) + 4*(lane>>5) + (q&3) at value q)
+  auto read_l = [&](int s, uint2 (&w)[4]) {
+    const char* lb = (const char*)(lbuf + (s % NS) * LST + nloc * 4) + 8 * (lane >> 5);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[h] = *(const uint2*)(lb + 16 * (h ^ ((nloc >> 2) & 3)));
+  };
+
+  float best = -INFINITY;
+  int bcode = -1;  // 16 * stage + value index of best
+
+  // Prologue: stage 0, the U rows, stages 1 and 2; stage 0's L entries once it landed.
+  load_stage(0);
+  {
+    const s32x4 udesc = make_desc(a.U, (uint32_t)((size_t)(a.u_rows > 0 ? a.u_rows : a.V) * a.rank * 2));
+    const uint32_t ubase = (uint32_t)(((size_t)tok * a.rank + 8 * (lane >> 5)) * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool ok = rvalid && 16 * ks + 8 * (lane >> 5) < a.rank;
+      buf_load_x4<true>(ufr[ks], udesc, ok ? ubase + 32 * ks : kOOB);
+    }
+  }
+  load_stage(1);
+  load_stage(2);
+  vm_wait<KS + 2 * LPS>();
+  __syncthreads();
+  uint2 lw[4];
+  read_l(0, lw);
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[1][q] = -INFINITY;  // "stage -1": updates nothing
+  // stage s: at its start stage s + 1 has landed (each thread its own loads, then the
+  // barrier), so its L entries are read during stage s; stage s + 3's loads go into the
+  // slot of stage s - 1, read before this stage's barrier
+  auto stage = [&](const int p, const int s) {
+    const int b = p & 1;
+    const u32x4* Ws = wbuf + p * WSLOT;  // s % NS (base is a multiple of NS)
+    auto wfrag = [&](int ks) {
+      const int m = lane & 31, kv = 2 * ks + (lane >> 5);
+      return __builtin_bit_cast(bf16x8, Ws[m * NV + ((kv & ~(W - 1)) | ((kv ^ (m / RW)) & (W - 1)))]);
+    };
+    // the accumulators start from L (-inf for a token past V or a row past the block)
+    const int v0 = (s_begin + s) * kTS;
+    if (v0 + kTS <= a.V && all_rows) {  // uniform: nothing to mask
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t ww = (q & 3) < 2 ? lw[q >> 2].x : lw[q >> 2].y;
+        acc[b][q] = (q & 1) ? bf16_hi(ww) : bf16_lo(ww);
+      }
+    } else {
+      const int vb = v0 + 4 * (lane >> 5);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t ww = (q & 3) < 2 ? lw[q >> 2].x : lw[q >> 2].y;
+        const bool ok = rvalid & (vb + 8 * (q >> 2) + (q & 3) < a.V);
+        acc[b][q] = ok ? ((q & 1) ? bf16_hi(ww) : bf16_lo(ww)) : -INFINITY;
+      }
+    }
+    const f32x16& z = acc[b ^ 1];  // stage s - 1
+    const int code0 = 16 * (s - 1);
+    constexpr int VPM = 16 / KS;
+    bf16x8 fr[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < KS) fr[j] = wfrag(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks % 3], __builtin_bit_cast(bf16x8, ufr[ks]), acc[b], 0, 0,
+                                                       0);
+      if (ks + 3 < KS) fr[ks % 3] = wfrag(ks + 3);
+#pragma unroll
+      for (int q = ks * VPM; q < (ks + 1) * VPM; ++q) {  // values in token order: ties keep the first
+        const bool gt = z[q] > best;
+        best = gt ? z[q] : best;
+        bcode = gt ? code0 + q : bcode;
+      }
+      if (ks == 1) read_l(s + 1, lw);
+#pragma unroll
+      for (int q = 0; q < WD; ++q)
+        if (ks == (KS * (q + 1)) / (LPS + 1)) load_w(s + 3, q);
+#pragma unroll
+      for (int q = 0; q < LD; ++q)
+        if (ks == (KS * (WD + q + 1)) / (LPS + 1)) load_l(s + 3, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int base = 0; base < nst; base += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      const int s = base + p;
+      if (s >= nst) break;  // uniform over the workgroup
+      vm_wait<LPS>();       // stage s + 1 landed: stage s + 2's loads may still be in flight
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) landed(ufr[ks]);
+      __syncthreads();
+      stage(p, s);
+    }
+  }
+  vm_wait<0>();  // the trailing loads (past the range) land before the LDS is left
+  auto finish = [&](const f32x16& last) {
+    const int code0 = 16 * (nst - 1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (last[q] > best) {
+        best = last[q];
+        bcode = code0 + q;
+      }
+  };
+  if (nst > 0) {
+    if ((nst - 1) & 1) finish(acc[1]);
+    else finish(acc[0]);
+  }
+  int bidx = 0x7fffffff;
+  if (bcode >= 0) {
+    const int q = bcode & 15;
+    bidx = (s_begin + (bcode >> 4)) * kTS + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+  }
+  const float ob = __shfl_xor(best, 32, 64);
+  const int oi = __shfl_xor(bidx, 32, 64);
+  if (ob > best || (ob == best && oi < bidx)) {
+    best = ob;
+    bidx = oi;
+  }
+  if (lane >= 32 || !rvalid) return;
+  ChainPart pp;
+  pp.key = bidx == 0x7fffffff ? 0ull : amax_key(best, (uint32_t)bidx);
+  pp.ref = -INFINITY;
+  pp.pad = 0.f;
+  pp.sum = 0.0;
+  ((ChainPart*)a.part)[(size_t)row * a.G + g] = pp;
+}
+
 // ---------------------------------------------------------------- chain merge
 struct ChainMergeArgs {
   const ChainPart* part;
@@ -2554,6 +2789,35 @@ int32_t launch_tree_split(int kid, const GemmArgs& a, hipStream_t s) {
   }
 }
 
+size_t chain_sched_lds_bytes(int ks) {
+  const int wslot = kTS * 2 * ks > kGT ? kTS * 2 * ks : kGT;
+  return ((size_t)4 * wslot + 4 * kTR * 4) * 16;  // four stage slots: Wt and the 16 KB L tile
+}
+
+template <int KS>
+int32_t launch_chain_sched_ks(int kid, GemmArgs a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)chain_gemm_kernel<KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    attr_set = true;
+  }
+  a.nrb = (a.rows + kTR - 1) / kTR;
+  a.xcd_map = a.nrb > 1 && a.G % 8 == 0;
+  launch(kid, chain_gemm_kernel<KS>, dim3((unsigned)(a.G * a.nrb)), dim3(kGT), (uint32_t)chain_sched_lds_bytes(KS), s,
+         a);
+  return hip_check(hipGetLastError(), "chain gemm launch");
+}
+
+int32_t launch_chain_sched(int kid, const GemmArgs& a, hipStream_t s) {
+  switch (ksteps(a.rank)) {
+    case 2: return launch_chain_sched_ks<2>(kid, a, s);
+    case 4: return launch_chain_sched_ks<4>(kid, a, s);
+    case 8: return launch_chain_sched_ks<8>(kid, a, s);
+    default: return launch_chain_sched_ks<16>(kid, a, s);
+  }
+}
+
 // L rows 16-byte aligned (base and both strides) take the vector-load kernel
 template <int MODE>
 int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
@@ -2567,6 +2831,7 @@ int32_t launch_gemm(int kid, const GemmArgs& a, hipStream_t s) {
   const bool al = ((uintptr_t)a.L) % 16 == 0 && a.ldL_r % 8 == 0 && a.ldL_d % 8 == 0;
   if (MODE == MODE_TREE && al && ksteps(a.rank) <= 16 && option(DSP_OPT_TREE_SPLIT) && blocks_span_16(a))
     return launch_tree_split(kid, a, s);
+  if (MODE == MODE_ARGMAX && al && ksteps(a.rank) <= 16 && option(DSP_OPT_CHAIN_SCHED)) return launch_chain_sched(kid, a, s);
   return al ? launch_gemm_al<MODE, true>(kid, a, s) : launch_gemm_al<MODE, false>(kid, a, s);
 }
 

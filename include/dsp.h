@@ -489,12 +489,17 @@ int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);
 /*   16-byte aligned L) on the GEMM with direct-to-LDS stages and a fixed    */
 /*   issue order; 0 keeps the general GEMM for every depth. Both compute the */
 /*   same sums in the same order: outputs are bit-identical.                 */
+/* DSP_OPT_CHAIN_SCHED: 1 (default) lets the greedy chain's and the RNN      */
+/*   head's arg-max steps (no log q, rank <= 256, 16-byte aligned row-major  */
+/*   L) run on the GEMM with direct-to-LDS stages and a fixed issue order;   */
+/*   0 keeps the general GEMM. Outputs are bit-identical.                    */
 /* Returns DSP_ERR_SHAPE for an unknown option or a negative value. Not      */
 /* thread safe; set before issuing work.                                     */
 /* ------------------------------------------------------------------------ */
 #define DSP_OPT_CHAIN_PERSISTENT  0
 #define DSP_OPT_SPIN_LIMIT        1
 #define DSP_OPT_TREE_SPLIT        2
+#define DSP_OPT_CHAIN_SCHED       3
 int32_t dsp_set_option(int32_t option, int64_t value);
 
 #ifdef __cplusplus

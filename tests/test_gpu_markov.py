@@ -61,6 +61,7 @@ def test_chain_small(R, B, V, rank):
     c = workloads.markov_case(R, B, V, rank=rank, seed=R + V)
     _check_chain(c, w_boost=300.0)  # a Markov term large enough to change choices
     _check_chain(c)
+    _check_chain(c, want_logq=False, w_boost=300.0)  # arg-max only (the scheduled GEMM up to rank 256)
 
 
 def test_chain_of_course_fixture():
@@ -583,3 +584,36 @@ def test_tree_scheduled_gemm_matches_general_gemm(R, D, V, rank, k, F, N, mask, 
     assert (out[1]["status"][0] != 0) == bool(bits)
     for n in out[0]:
         np.testing.assert_array_equal(out[1][n].view(np.uint8), out[0][n].view(np.uint8), err_msg=n)
+
+
+@pytest.mark.parametrize("R,B,V,rank,mask", [
+    (256, 4, 151936, 256, False),  # the chain workload's shape (fewer steps)
+    (37, 3, 40001, 256, True),     # a partial row block, ragged vocabulary, masked entries
+    (300, 3, 5003, 64, False),     # two row blocks, rank 64
+    (21, 3, 3001, 32, True),       # rank 32
+    (16, 4, 20000, 128, False),    # rank 128
+])
+def test_chain_scheduled_gemm_matches_general_gemm(R, B, V, rank, mask):
+    """The greedy chain's arg-max steps (no log q) run on the GEMM with direct-to-LDS stages
+    and a fixed issue order; it starts the accumulators from L and sums the k-steps in the
+    same order as the general GEMM, so the tokens must be identical to a run with that
+    kernel switched off, and to the oracle up to counted near-ties."""
+    c = workloads.markov_case(R, B, V, rank=rank, seed=400 + R + V)
+    if mask:
+        L = c["L"].copy()
+        L[..., np.random.default_rng(R).random(V) < 0.1] = 0xFF80
+        c = dict(c, L=L)
+    Lg, Ug, Wtg, ag = _gpu_inputs(c)
+    out = {}
+    try:
+        for opt_on in (0, 1):
+            dsp.set_option("chain_sched", opt_on)
+            print(f"chain R={R} B={B} V={V} rank={rank} chain_sched={opt_on}", flush=True)
+            g = dsp.draft_markov_step(Lg, Ug, Wtg, ag)
+            torch.cuda.synchronize()
+            assert int(host(g["status"])[0]) == 0
+            out[opt_on] = host(g["y"]).copy()
+    finally:
+        dsp.set_option("chain_sched", 1)
+    np.testing.assert_array_equal(out[1], out[0])
+    _check_chain(c, want_logq=False, requests=range(0, R, max(1, R // 24)))
