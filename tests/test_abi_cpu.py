@@ -136,3 +136,23 @@ def test_workspace_queries_are_pure_functions():
     assert lib.dsp_verify_rejection_workspace_size(0, 7, 10, 0, 1, 1) == 0
     assert lib.dsp_tree_expand_workspace_size(128, 16, 129280, 256, 4, 16, 64) > 0
     assert lib.dsp_draft_markov_step_workspace_size(256, 151936, 256, 16, 0) > 0
+
+
+def test_options_match_the_header_and_are_checked():
+    """The binding's option codes are the header's, every declared option is accepted and
+    restored, and an undeclared code or a negative value is rejected (host only)."""
+    src = open(HEADER).read()
+    declared = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(DSP_OPT_[A-Z_]+)\s+(\d+)", src)}
+    assert declared
+    for name, code in declared.items():
+        assert getattr(_abi, name) == code, name
+    lib = _abi.load()
+    defaults = {"DSP_OPT_CHAIN_PERSISTENT": 0, "DSP_OPT_SPIN_LIMIT": 1 << 20, "DSP_OPT_TREE_SPLIT": 1,
+                "DSP_OPT_CHAIN_SCHED": 1}
+    assert set(defaults) == set(declared)
+    for name, code in declared.items():
+        assert lib.dsp_set_option(code, 0) == 0
+        assert lib.dsp_set_option(code, -1) == _abi.DSP_ERR_SHAPE
+        assert lib.dsp_set_option(code, defaults[name]) == 0
+    assert lib.dsp_set_option(max(declared.values()) + 1, 0) == _abi.DSP_ERR_SHAPE
+    assert lib.dsp_set_option(-1, 0) == _abi.DSP_ERR_SHAPE
