@@ -173,15 +173,6 @@ struct GemmArgs {
   int32_t l_tm;
 };
 
-// 16-byte slot of (row, vector) in a swizzled LDS tile whose rows hold `nv` vectors
-// (nv a multiple of 4): the vector index is XOR-ed with the low row bits inside
-// aligned groups of 8 (or 4), so consecutive rows start on different banks.
-__device__ __forceinline__ int swz(int row, int kv, int nv) {
-  const int m = (nv & 7) == 0 ? 7 : 3;
-  return row * nv + ((kv & ~m) | ((kv ^ row) & m));
-}
-
-
 // (value desc, id asc) order of top-k entries
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
