@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="diagnostic: no cache flush between timed steps")
     ap.add_argument("--chain-persistent", action="store_true",
                     help="markov-chain: all 16 steps in one persistent launch (default: one launch per step)")
+    ap.add_argument("--general-gemm", action="store_true",
+                    help="diagnostic: the general GEMM kernel for every tree depth (default: the scheduled kernel "
+                         "where it applies; outputs are bit-identical)")
     ap.add_argument("--l-layout", default="row-major", choices=["row-major", "token-major"],
                     help="chain workloads: base logits [R, B, V] (row-major) or [B, V, R] (token-major)")
     return ap.parse_args()
@@ -846,6 +849,10 @@ def main():
         cpu = cycle_cpu(c, args) if want_cpu else None
     import torch
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.general_gemm:
+        import block_drafting_verification_amd as dsp
+        dsp.set_option("chain_sched", 0)
+        dsp.set_option("tree_split", 0)
     if w == "copy":
         res = bench_copy(args)
     elif w in ("dense-verify", "scheduled-verify"):
@@ -858,6 +865,8 @@ def main():
         res = bench_cycle(args, c, cpu)
     else:
         res = bench_tree(args, c, cpu)
+    if args.general_gemm:
+        res["config"]["gemm"] = "general (diagnostic)"
     print(json.dumps(res))
 
 

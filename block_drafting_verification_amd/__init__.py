@@ -549,8 +549,8 @@ def set_option(option, value):
     "tree_split" (1 = the tree's GEMM runs its depths whose row blocks span at most 16
     requests on the kernel with direct-to-LDS stages and a fixed issue order, the default;
     0 = the general GEMM everywhere; outputs are bit-identical) or "chain_sched" (1 = the
-    greedy chain's arg-max steps run on the GEMM with direct-to-LDS stages, the default;
-    0 = the general GEMM; outputs are bit-identical)."""
+    greedy chain's arg-max steps run on the GEMM with direct-to-LDS stages; 0 = the general
+    GEMM, the default; outputs are bit-identical)."""
     code = {"chain_persistent": _abi.DSP_OPT_CHAIN_PERSISTENT, "spin_limit": _abi.DSP_OPT_SPIN_LIMIT,
             "tree_split": _abi.DSP_OPT_TREE_SPLIT, "chain_sched": _abi.DSP_OPT_CHAIN_SCHED}[option]
     _abi.check(lib().dsp_set_option(code, int(value)))

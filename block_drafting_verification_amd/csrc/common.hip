@@ -64,7 +64,7 @@ bool prof_events(int kernel, hipEvent_t* start, hipEvent_t* stop) {
 void prof_commit(int kernel, hipEvent_t start, hipEvent_t stop) { g_prof_recs.push_back({kernel, start, stop}); }
 
 // ---------------------------------------------------------------- options
-static int64_t g_options[4] = {0, 1 << 20, 1, 1};
+static int64_t g_options[4] = {0, 1 << 20, 1, 0};
 
 int64_t option(int32_t opt) { return opt >= 0 && opt < 4 ? g_options[opt] : 0; }
 

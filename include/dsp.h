@@ -489,10 +489,11 @@ int32_t dsp_prof_query(int32_t kernel, double* total_ms, int64_t* launches);
 /*   16-byte aligned L) on the GEMM with direct-to-LDS stages and a fixed    */
 /*   issue order; 0 keeps the general GEMM for every depth. Both compute the */
 /*   same sums in the same order: outputs are bit-identical.                 */
-/* DSP_OPT_CHAIN_SCHED: 1 (default) lets the greedy chain's and the RNN      */
-/*   head's arg-max steps (no log q, rank <= 256, 16-byte aligned row-major  */
-/*   L) run on the GEMM with direct-to-LDS stages and a fixed issue order;   */
-/*   0 keeps the general GEMM. Outputs are bit-identical.                    */
+/* DSP_OPT_CHAIN_SCHED: 1 lets the greedy chain's and the RNN head's       */
+/*   arg-max steps (no log q, rank <= 256, 16-byte aligned row-major L) run  */
+/*   on the GEMM with direct-to-LDS stages and a fixed issue order; 0        */
+/*   (default) keeps the general GEMM, which measures as fast or faster on   */
+/*   gfx950. Outputs are bit-identical.                                      */
 /* Returns DSP_ERR_SHAPE for an unknown option or a negative value. Not      */
 /* thread safe; set before issuing work.                                     */
 /* ------------------------------------------------------------------------ */

@@ -149,7 +149,7 @@ def test_options_match_the_header_and_are_checked():
     err_shape = int(re.search(r"#define\s+DSP_ERR_SHAPE\s+(-?\d+)", src).group(1))
     lib = _abi.load()
     defaults = {"DSP_OPT_CHAIN_PERSISTENT": 0, "DSP_OPT_SPIN_LIMIT": 1 << 20, "DSP_OPT_TREE_SPLIT": 1,
-                "DSP_OPT_CHAIN_SCHED": 1}
+                "DSP_OPT_CHAIN_SCHED": 0}
     assert set(defaults) == set(declared)
     for name, code in declared.items():
         assert lib.dsp_set_option(code, 0) == 0

@@ -61,7 +61,12 @@ def test_chain_small(R, B, V, rank):
     c = workloads.markov_case(R, B, V, rank=rank, seed=R + V)
     _check_chain(c, w_boost=300.0)  # a Markov term large enough to change choices
     _check_chain(c)
-    _check_chain(c, want_logq=False, w_boost=300.0)  # arg-max only (the scheduled GEMM up to rank 256)
+    _check_chain(c, want_logq=False, w_boost=300.0)  # arg-max only
+    dsp.set_option("chain_sched", 1)  # the opt-in scheduled GEMM (rank up to 256)
+    try:
+        _check_chain(c, want_logq=False, w_boost=300.0)
+    finally:
+        dsp.set_option("chain_sched", 0)
 
 
 def test_chain_of_course_fixture():
@@ -594,10 +599,10 @@ def test_tree_scheduled_gemm_matches_general_gemm(R, D, V, rank, k, F, N, mask, 
     (16, 4, 20000, 128, False),    # rank 128
 ])
 def test_chain_scheduled_gemm_matches_general_gemm(R, B, V, rank, mask):
-    """The greedy chain's arg-max steps (no log q) run on the GEMM with direct-to-LDS stages
-    and a fixed issue order; it starts the accumulators from L and sums the k-steps in the
-    same order as the general GEMM, so the tokens must be identical to a run with that
-    kernel switched off, and to the oracle up to counted near-ties."""
+    """With the opt-in scheduled GEMM, the greedy chain's arg-max steps (no log q) run on the
+    kernel with direct-to-LDS stages and a fixed issue order; it starts the accumulators
+    from L and sums the k-steps in the same order as the general GEMM, so the tokens must be
+    identical to the general kernel's, and to the oracle up to counted near-ties."""
     c = workloads.markov_case(R, B, V, rank=rank, seed=400 + R + V)
     if mask:
         L = c["L"].copy()
@@ -613,7 +618,8 @@ def test_chain_scheduled_gemm_matches_general_gemm(R, B, V, rank, mask):
             torch.cuda.synchronize()
             assert int(host(g["status"])[0]) == 0
             out[opt_on] = host(g["y"]).copy()
-    finally:
         dsp.set_option("chain_sched", 1)
+        _check_chain(c, want_logq=False, requests=range(0, R, max(1, R // 24)))
+    finally:
+        dsp.set_option("chain_sched", 0)
     np.testing.assert_array_equal(out[1], out[0])
-    _check_chain(c, want_logq=False, requests=range(0, R, max(1, R // 24)))
