@@ -2250,6 +2250,19 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
   __shared__ int32_t s_ntok[64];
   const int i = blockIdx.x, tid = threadIdx.x;
   const int nc = a.fp * a.topk;
+  const int qn = a.rank / 4;  // a multiple of 8
+  // With one batch of candidates and of their rank quarters (nc <= 64, rank <= 256), the
+  // parents' U rows that the candidates' dot products read are known from the start:
+  // their loads are issued here, ahead of the partials, instead of after the merge.
+  const bool upre_on = nc <= 64 && qn / 8 <= 8;
+  u32x4 upre[8];
+  if (upre_on) {
+    const int c = tid >> 2, r = tid & 3;
+    const int ptoken = a.ptok[i * a.fp + (c < nc ? c / a.topk : 0)];
+    const u32x4* ur = (const u32x4*)(a.U + (size_t)ptoken * a.rank + r * qn);
+#pragma unroll
+    for (int t2 = 0; t2 < 8; ++t2) upre[t2] = ur[min(t2, qn / 8 - 1)];
+  }
   // parents: 16 lanes each (aligned groups inside a wavefront), 16 parents per pass
   for (int pb = 0; pb < a.fp; pb += 16) {
     const int p = pb + (tid >> 4), j = tid & 15;
@@ -2263,6 +2276,8 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
       ti[q] = 0x7fffffff;
     }
     float H = -INFINITY;
+    float rf1[4];  // the first batch's (reference, sum) pairs, reused below when G <= 64
+    double sm1[4];
     // four partials per lane per batch, loaded unconditionally (clamped, masked after:
     // a load under a branch is waited for on the spot)
     for (int g0 = j; g0 < a.G; g0 += 64) {
@@ -2270,11 +2285,16 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) tp[q] = pr[min(g0 + 16 * q, a.G - 1)];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q) {
         if (pv && g0 + 16 * q < a.G) {
           merge_top4(tv, ti, tp[q].val, tp[q].idx);
           H = fmaxf(H, tp[q].ref);
         }
+        if (g0 == j) {
+          rf1[q] = tp[q].ref;
+          sm1[q] = tp[q].sum;
+        }
+      }
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) {
@@ -2289,7 +2309,12 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
       H = fmaxf(H, __shfl_xor(H, o, 64));
     }
     double S = 0.0;
-    for (int g0 = j; g0 < a.G; g0 += 64) {
+    if (a.G <= 64) {  // one batch: the pairs are still in registers (same terms, same order)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (pv && j + 16 * q < a.G && rf1[q] != -INFINITY) S += sm1[q] * exp2((double)rf1[q] - (double)H);
+    }
+    for (int g0 = j; a.G > 64 && g0 < a.G; g0 += 64) {
       float rf[4];
       double sm[4];
 #pragma unroll
@@ -2326,7 +2351,6 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
     }
     if (v < 0 || v >= a.V) v = 0;
     const int ptoken = a.ptok[i * a.fp + p];
-    const int qn = a.rank / 4;  // a multiple of 8
     const u32x4* ur = (const u32x4*)(a.U + (size_t)ptoken * a.rank + r * qn);
     const u32x4* wr = (const u32x4*)(a.Wt + (size_t)v * a.rank + r * qn);
     double m = 0.0;
@@ -2335,7 +2359,7 @@ __global__ __launch_bounds__(256) void tree_merge_kernel(TreeMergeArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int tt = min(j0 + t, qn / 8 - 1);
-        uu[t] = ur[tt];
+        uu[t] = upre_on ? upre[t] : ur[tt];  // the same vectors (one batch: j0 = 0)
         ww[t] = wr[tt];
       }
 #pragma unroll
