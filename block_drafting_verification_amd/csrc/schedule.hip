@@ -74,25 +74,37 @@ __device__ __forceinline__ void stage_conf(const float* __restrict__ conf, int n
 
 // Candidate keys of every (request, position): survival in fp64, one thread per
 // request multiplying left to right, quantised and packed (optionally also written
-// out as the survival table).
-__device__ void candidate_keys(const float* __restrict__ conf, int R, int K, double scale,
-                               float* s_conf, uint64_t* keys, double* survival) {
+// out as the survival table). Each thread reads its own request's confidences straight
+// from global memory, sixteen in flight per round (as four 16-byte loads when the rows
+// are 16-byte aligned), and the keys are stored position-major, keys[k * R + i], so the
+// lanes of a wave write consecutive words; the ranking counts over all keys, so their
+// order in LDS does not matter.
+__device__ void candidate_keys(const float* __restrict__ conf, int R, int K, double scale, uint64_t* keys,
+                               double* survival) {
   const int n = R * K;
-  stage_conf(conf, n, s_conf);
-  __syncthreads();
+  const bool v4 = (K & 3) == 0 && ((uintptr_t)conf & 15) == 0;
   for (int i = threadIdx.x; i < R; i += blockDim.x) {
+    const float* row = conf + (size_t)i * K;
     double s = 1.0;
-    for (int k0 = 0; k0 < K; k0 += 8) {
-      float cf[8];  // eight reads in flight, then the products in order
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      float cf[16];
+      if (v4 && k0 + 16 <= K) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) cf[q] = k0 + q < K ? s_conf[i * K + k0 + q] : 1.0f;
+        for (int q = 0; q < 4; ++q) {
+          const float4 t = *(const float4*)(row + k0 + 4 * q);
+          cf[4 * q] = t.x, cf[4 * q + 1] = t.y, cf[4 * q + 2] = t.z, cf[4 * q + 3] = t.w;
+        }
+      } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 16; ++q) cf[q] = k0 + q < K ? row[k0 + q] : 1.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
         const int k = k0 + q;
         if (k < K) {
           s = __dmul_rn(s, (double)cf[q]);
           if (survival) survival[(size_t)i * K + k] = s;
-          keys[i * K + k] = sched_key(quantise(s, scale), i, k);
+          keys[k * R + i] = sched_key(quantise(s, scale), i, k);
         }
       }
     }
@@ -117,11 +129,10 @@ __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(const float
                                                                      int K, int Q, double* __restrict__ survival,
                                                                      uint64_t* __restrict__ sorted) {
   __shared__ __align__(16) uint64_t keys[kMaxCand];
-  __shared__ float s_conf[kMaxCand];
   __shared__ int part[kRankThreads];
   const int tid = threadIdx.x;
   const int n = R * K;
-  candidate_keys(conf, R, K, ldexp(1.0, Q), s_conf, keys, blockIdx.x == 0 ? survival : nullptr);
+  candidate_keys(conf, R, K, ldexp(1.0, Q), keys, blockIdx.x == 0 ? survival : nullptr);
   const int cl = tid % kRankCand, sl = tid / kRankCand;
   const int c = blockIdx.x * kRankCand + cl;
   const uint64_t x = c < n ? keys[c] : 0ull;
