@@ -245,12 +245,17 @@ __device__ __forceinline__ void pack_item(int j, int K1, float inv_k1, int& i, i
 __device__ void pack_prefetch(int R, int K, const PackArgs& pa, int32_t (&tok)[kPackPre]) {
   const int K1 = K + 1, n = R * K1, tid = threadIdx.x;
   const float inv_k1 = 1.0f / (float)K1;
+  const int rounds = (n + kSchedThreads - 1) / kSchedThreads;  // the same in every thread
 #pragma unroll
   for (int q = 0; q < kPackPre; ++q) {  // clamped items (masked at use): all loads in flight at once
-    const int j = min(tid + q * kSchedThreads, n - 1);
-    int i, k;
-    pack_item(j, K1, inv_k1, i, k);
-    tok[q] = k == 0 ? pa.anchors[i] : pa.drafts[(size_t)i * pa.ld + k - 1];
+    if (q < rounds) {
+      const int j = min(tid + q * kSchedThreads, n - 1);
+      int i, k;
+      pack_item(j, K1, inv_k1, i, k);
+      // the source picked by address, so every item costs one load and no branch
+      const int32_t* src = k == 0 ? pa.anchors + i : pa.drafts + ((size_t)i * pa.ld + (k > 0 ? k - 1 : 0));
+      tok[q] = *src;
+    }
   }
 }
 __device__ void pack_body_lds(const int* s_win, int R, int K, const PackArgs& pa, uint64_t* wsum, int* s_cu,
@@ -377,15 +382,17 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
   }
 
   // thread t owns ranks [t*C, t*C + C) of the first M (C <= kSelPer): its keys and the
-  // cost entries it needs are loaded straight into registers, all in one round trip
+  // cost entries it needs are loaded straight into registers, all in one round trip.
+  // The trip count C is the same in every thread and the indices are clamped, so no
+  // load sits under a per-lane branch; entries past p1 are masked at every use.
   const int C = (M + kSchedThreads - 1) / kSchedThreads;
   const int p0 = min(M, tid * C), p1 = min(M, p0 + C);
   uint64_t kq[kSelPer];
   double cq[kSelPer + 1];
 #pragma unroll
-  for (int q = 0; q < kSelPer; ++q) kq[q] = p0 + q < p1 ? sorted[p0 + q] : 0ull;
+  for (int q = 0; q < kSelPer; ++q) kq[q] = q < C ? sorted[min(p0 + q, M - 1)] : 0ull;
 #pragma unroll
-  for (int q = 0; q <= kSelPer; ++q) cq[q] = p0 + q <= p1 ? cost[p0 + q] : 0.0;
+  for (int q = 0; q <= kSelPer; ++q) cq[q] = q <= C ? cost[min(p0 + q, M)] : 0.0;
   for (int i = tid; i < R; i += kSchedThreads) cnt[i] = 0;
 
   // exact prefix sums of the quantised survivals in rank order
@@ -420,17 +427,22 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
       best = __ddiv_rn(0.0, cq[0]);
       bj = 0;
     }
+    // the C quotients first (independent, so their division sequences overlap), then
+    // the comparisons in rank order over the valid ones
     uint64_t run = ex;
+    double Jq[kSelPer];
 #pragma unroll
     for (int q = 0; q < kSelPer; ++q) {
-      if (p0 + q < p1) {
-        const int j = p0 + q + 1;
+      if (q < C) {
         run += key_sq(kq[q]);
-        const double J = __ddiv_rn((double)run, cq[q + 1]);
-        if (J > best) {
-          best = J;
-          bj = j;
-        }
+        Jq[q] = __ddiv_rn((double)run, cq[q + 1]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kSelPer; ++q) {
+      if (q < C && p0 + q < p1 && Jq[q] > best) {
+        best = Jq[q];
+        bj = p0 + q + 1;
       }
     }
     const double Jm = block_max<kSchedThreads / 64>(best, smd);
