@@ -72,6 +72,10 @@ __device__ __forceinline__ void stage_conf(const float* __restrict__ conf, int n
   }
 }
 
+// The ranking reads the keys kKeyBlock at a time; kMaxCand is a multiple of it.
+constexpr int kKeyBlock = 512;
+static_assert(kMaxCand % kKeyBlock == 0, "padded keys must fit the key table");
+
 // Candidate keys of every (request, position): survival in fp64, one thread per
 // request multiplying left to right, quantised and packed (optionally also written
 // out as the survival table). Each thread reads its own request's confidences straight
@@ -109,27 +113,31 @@ __device__ void candidate_keys(const float* __restrict__ conf, int R, int K, dou
       }
     }
   }
-  // padding keys (never below a real key) up to a whole number of 256-key strips
-  for (int j = n + threadIdx.x; j < ((n + 255) & ~255); j += blockDim.x) keys[j] = ~0ull;
+  // padding keys (never below a real key) up to a whole number of kKeyBlock-key blocks
+  for (int j = n + threadIdx.x; j < ((n + kKeyBlock - 1) & ~(kKeyBlock - 1)); j += blockDim.x) keys[j] = ~0ull;
   __syncthreads();
 }
 
 // Ranking, spread over many workgroups: each workgroup builds every key in LDS and
 // ranks kRankCand of them by counting the keys below each (keys are unique, so the
-// counts are a permutation of 0..n-1), 16 lanes per candidate over interleaved
-// slices of the keys: slice s reads key pairs (2s, 2s+1) of every 32-key strip
-// (lanes of one slice read the same LDS words: a broadcast), four strips per step.
-// The sorted keys go to sorted[rank].
-constexpr int kRankThreads = 256;
+// counts are a permutation of 0..n-1), kRankSlices lanes per candidate over
+// interleaved slices of the keys: slice s reads key pairs (2s, 2s+1) of every strip of
+// 2*kRankSlices keys (lanes of one slice read the same LDS words: a broadcast), the
+// kRankReads strips of a kKeyBlock-key block per step. 1024 threads give every SIMD
+// four waves, so one wave's compares run while another waits on its LDS reads. The
+// sorted keys go to sorted[rank].
+constexpr int kRankThreads = 1024;
 constexpr int kSelPer = kMaxCand / kSchedThreads;  // ranks per thread in the selection
 constexpr int kRankCand = 16;
 constexpr int kRankSlices = kRankThreads / kRankCand;
+constexpr int kRankReads = kKeyBlock / (2 * kRankSlices);
+static_assert(kRankReads * 2 * kRankSlices == kKeyBlock, "slices must tile a key block");
 
 __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(const float* __restrict__ conf, int R,
                                                                      int K, int Q, double* __restrict__ survival,
                                                                      uint64_t* __restrict__ sorted) {
   __shared__ __align__(16) uint64_t keys[kMaxCand];
-  __shared__ int part[kRankThreads];
+  __shared__ __align__(16) int part[kRankThreads];
   const int tid = threadIdx.x;
   const int n = R * K;
   candidate_keys(conf, R, K, ldexp(1.0, Q), keys, blockIdx.x == 0 ? survival : nullptr);
@@ -137,21 +145,21 @@ __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(const float
   const int c = blockIdx.x * kRankCand + cl;
   const uint64_t x = c < n ? keys[c] : 0ull;
   int cnt = 0;
-  const int np = (n + 255) & ~255;  // padded with keys above every real one
+  const int np = (n + kKeyBlock - 1) & ~(kKeyBlock - 1);  // padded with keys above every real one
   typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-  for (int j = 2 * sl; j < np; j += 256) {  // eight reads in flight per round
-    u64x2 v[8];
+  for (int j = 2 * sl; j < np; j += kKeyBlock) {  // kRankReads reads in flight per round
+    u64x2 v[kRankReads];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = *(const u64x2*)&keys[j + 32 * q];
+    for (int q = 0; q < kRankReads; ++q) v[q] = *(const u64x2*)&keys[j + 2 * kRankSlices * q];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cnt += (v[q].x < x ? 1 : 0) + (v[q].y < x ? 1 : 0);
+    for (int q = 0; q < kRankReads; ++q) cnt += (v[q].x < x ? 1 : 0) + (v[q].y < x ? 1 : 0);
   }
-  part[tid] = cnt;
+  part[cl * kRankSlices + sl] = cnt;  // a candidate's partial counts side by side
   __syncthreads();
   if (sl == 0 && c < n) {
     int r = 0;
 #pragma unroll
-    for (int q = 0; q < kRankSlices; ++q) r += part[q * kRankCand + cl];
+    for (int q = 0; q < kRankSlices; ++q) r += part[cl * kRankSlices + q];
     sorted[r] = x;
   }
 }
