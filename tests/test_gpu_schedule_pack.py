@@ -42,6 +42,32 @@ def test_schedule_random(R, K):
     _sched(conf, cost, 1)
 
 
+@pytest.mark.parametrize("R,K", [(64, 16), (256, 16), (32, 128)])
+def test_schedule_misaligned_inputs(R, K):
+    """conf one float and cost one double past a 16-byte boundary: the ranking reads the
+    confidence rows with scalar loads instead of 16-byte ones; the result is the same."""
+    rng = np.random.Generator(np.random.PCG64(R * 7 + K))
+    conf = rng.uniform(0.0, 1.0, size=(R, K)).astype(np.float32)
+    conf[rng.random((R, K)) < 0.05] = 1.0
+    cost = osch.additive_cost(1.0, 0.05, R * K)
+    cbuf = torch.zeros(R * K + 1, dtype=torch.float32, device="cuda")
+    cbuf[1:] = to_gpu(conf).reshape(-1)
+    conf_v = cbuf[1:].view(R, K)
+    kbuf = torch.zeros(cost.size + 1, dtype=torch.float64, device="cuda")
+    kbuf[1:] = to_gpu(cost)
+    cost_v = kbuf[1:]
+    assert conf_v.data_ptr() % 16 == 4 and cost_v.data_ptr() % 16 == 8
+    for mode in (osch.MODE_EARLY_STOP, osch.MODE_ARGMAX):
+        print(f"schedule misaligned R={R} K={K} mode={mode}", flush=True)
+        g = dsp.schedule_windows(conf_v, cost_v, mode=mode)
+        torch.cuda.synchronize()
+        o = osch.schedule_windows(conf, cost, mode=mode)
+        np.testing.assert_array_equal(host(g["windows"]), o["windows"])
+        np.testing.assert_array_equal(host(g["survival"]), o["survival"])
+        st = host(g["stats"])
+        assert st[0] == o["N"] and st[1] == o["E"] and st[2] == o["J"] and st[3] == o["Q"]
+
+
 @pytest.mark.parametrize("R,K", [(3, 5), (64, 7), (256, 16)])
 def test_schedule_nonmonotone_survival(R, K):
     """Confidences above 1 let a survival grow along k, so a request's candidates are no
