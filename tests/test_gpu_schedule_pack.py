@@ -93,6 +93,23 @@ def test_schedule_special_cases():
     assert np.all(o["windows"] == 0)
 
 
+@pytest.mark.parametrize("R,K", [(256, 16), (512, 16), (8192, 1)])
+def test_schedule_ties_across_requests(R, K):
+    """Survivals that tie across many requests (a constant confidence; rows repeated
+    request to request) at up to the largest candidate count: the order falls back to
+    (request, position), so a capacity cut through a tied run must take the lower
+    requests first, exactly as the oracle does."""
+    rng = np.random.Generator(np.random.PCG64(R * 11 + K))
+    row = rng.uniform(0.3, 1.0, size=(1, K)).astype(np.float32)
+    for conf in (np.full((R, K), 0.5, np.float32), np.repeat(row, R, axis=0)):
+        cost = osch.additive_cost(1.0, 0.01, R * K)
+        for mode in (osch.MODE_EARLY_STOP, osch.MODE_ARGMAX):
+            _sched(conf, cost, mode)
+        for cap in (1, R // 3, R * K // 2 + 1):
+            o = _sched(conf, cost, osch.MODE_TOP_M, cap=cap)
+            assert o["windows"].sum() == cap
+
+
 @pytest.mark.parametrize("R,K", [(1, 1), (7, 16), (64, 7), (256, 16), (8192, 1), (64, 128)])
 def test_schedule_top_m_and_threshold(R, K):
     rng = np.random.Generator(np.random.PCG64(R * 7 + K))
